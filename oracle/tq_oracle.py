@@ -1,0 +1,390 @@
+"""Plain CPU oracle for the TurboQuant KV-cache hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import this module.  The product path (the
+HIP library and its Python binding) never calls it and shares no code with it.
+
+Everything is computed in float64 from the given inputs, one step after another
+in the order the pages describe, with numpy primitives (matmul, sort, packbits)
+as the only library steps.  Sources, cited as page title + section:
+
+  [P1] "TurboQuant KV 캐시 압축 for llama.cpp" (stig.sh, AmesianX README_KO)
+  [P2] "윈도우용 터보퀀트(TurboQuant) 구현을 개선하다" (idea.jsleekr.com)
+  [P3] "[GitHub 탐방] TurboQuant 3-bit KV 캐시 압축 — 단일 GPU 재현 기록" (velog.io)
+
+Readings where the pages are silent (each one is listed with its reason in the
+design notes of the repository):
+  * H is the unnormalised Sylvester Hadamard matrix, H[i][j] = (-1)^popcount(i&j);
+    the rotated unit coordinate is z = H (D x) / ||x||, which has unit variance,
+    so the codebook is the Lloyd-Max quantiser of N(0,1).
+  * Sign i of D is -1 when bit 63 of the (i+1)-th SplitMix64 output for the
+    seed is set.
+  * idx_i = #{j : z_i > t_j} (a value exactly on a threshold goes to the lower
+    cell); indices are packed as an LSB-first bit stream, index i at bits
+    [b*i, b*i+b).
+  * The norm is stored as IEEE half (round to nearest even, clamped to 65504).
+  * QJL: residual in the rotated unit domain r = (z - c[idx]) / sqrt(d),
+    gamma = ||r|| stored as half, bit_j = [(S r)_j >= 0] with S ~ N(0,1) [m][d]
+    passed in by the caller; the inner-product estimator uses sqrt(pi/2)/m.
+
+Every function here is pinned by tests/test_oracle_pins.py against values the
+pages print, closed forms, textbook routines or brute force.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+_MASK64 = (1 << 64) - 1
+_GOLDEN = 0x9E3779B97F4A7C15
+
+
+# --------------------------------------------------------------------------
+# Codebook: Lloyd-Max scalar quantiser of N(0,1)
+# --------------------------------------------------------------------------
+def _phi(x: float) -> float:
+    """Standard normal density."""
+    if math.isinf(x):
+        return 0.0
+    return math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def _upper_tail(x: float) -> float:
+    """P(X > x) for X ~ N(0,1), accurate in the tail."""
+    if math.isinf(x):
+        return 0.0 if x > 0 else 1.0
+    return 0.5 * math.erfc(x / math.sqrt(2.0))
+
+
+def lloyd_max_gaussian(bits: int, tol: float = 1e-15, max_iter: int = 1_000_000):
+    """Lloyd-Max quantiser for N(0,1) with 2^bits levels, in float64.
+
+    [P1] names the scalar stage "Lloyd-Max 양자화" (page header); [P3] "GPU 세대가
+    바뀌면 결과가 달라질까" describes it as mapping each coordinate to one of 2^bits
+    centroids.  The quantiser is the fixed point of the two Lloyd conditions:
+    every centroid is the conditional mean of its cell, and every threshold is
+    the midpoint of its two neighbouring centroids.  The positive half is solved
+    and mirrored, so the codebook is exactly symmetric and the middle threshold
+    is exactly 0.  Start: thresholds at the uniform quantiles of N(0,1).
+
+    Returns (centroids[L], thresholds[L-1]) in float64, ascending.
+    """
+    if not 1 <= bits <= 4:
+        raise ValueError("bits must be 1..4")
+    L = 1 << bits
+    half = L // 2
+    # positive-half cell edges tau[0]=0 < tau[1] < ... < tau[half-1] < tau[half]=inf
+    from statistics import NormalDist
+
+    nd = NormalDist()
+    tau = [0.0] + [nd.inv_cdf(0.5 + k / L) for k in range(1, half)] + [math.inf]
+    cent = [0.0] * half
+    for _ in range(max_iter):
+        for k in range(half):
+            a, b = tau[k], tau[k + 1]
+            mass = _upper_tail(a) - _upper_tail(b)
+            cent[k] = (_phi(a) - _phi(b)) / mass
+        new_tau = [0.0] + [0.5 * (cent[k - 1] + cent[k]) for k in range(1, half)] + [math.inf]
+        delta = max((abs(new_tau[k] - tau[k]) for k in range(1, half)), default=0.0)
+        tau = new_tau
+        if delta < tol:
+            break
+    # final centroids for the final thresholds
+    for k in range(half):
+        a, b = tau[k], tau[k + 1]
+        cent[k] = (_phi(a) - _phi(b)) / (_upper_tail(a) - _upper_tail(b))
+    pos_c = np.array(cent, dtype=np.float64)
+    centroids = np.concatenate([-pos_c[::-1], pos_c])
+    pos_t = np.array([0.5 * (cent[k - 1] + cent[k]) for k in range(1, half)], dtype=np.float64)
+    thresholds = np.concatenate([-pos_t[::-1], [0.0], pos_t])
+    return centroids, thresholds
+
+
+def lloyd_max_mse(centroids: np.ndarray, thresholds: np.ndarray) -> float:
+    """E[(X - Q(X))^2] for X ~ N(0,1) and the quantiser (closed form per cell)."""
+    edges = np.concatenate([[-np.inf], thresholds, [np.inf]])
+    mse = 0.0
+    for k, c in enumerate(centroids):
+        a, b = float(edges[k]), float(edges[k + 1])
+        mass = _upper_tail(a) - _upper_tail(b)
+        # E[X^2 1_cell] = mass + a phi(a) - b phi(b);  E[X 1_cell] = phi(a) - phi(b)
+        ax = 0.0 if math.isinf(a) else a * _phi(a)
+        bx = 0.0 if math.isinf(b) else b * _phi(b)
+        ex2 = mass + ax - bx
+        ex1 = _phi(a) - _phi(b)
+        mse += ex2 - 2.0 * c * ex1 + c * c * mass
+    return mse
+
+
+# --------------------------------------------------------------------------
+# Random signs and the Hadamard matrix
+# --------------------------------------------------------------------------
+def splitmix64(seed: int, count: int) -> list[int]:
+    """The first ``count`` outputs of SplitMix64 (Steele, Lea & Flood 2014;
+    Vigna's public-domain reference) started from state ``seed``."""
+    state = seed & _MASK64
+    out = []
+    for _ in range(count):
+        state = (state + _GOLDEN) & _MASK64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+        out.append(z ^ (z >> 31))
+    return out
+
+
+def sign_vector(seed: int, d: int) -> np.ndarray:
+    """Diagonal of D: the seeded +-1 sign flip ("tbq_signs", [P1] v1.7.0
+    "핵심 설계 결정" item 4).  Sign i is -1 when bit 63 of output i+1 is set."""
+    return np.array([-1.0 if (v >> 63) & 1 else 1.0 for v in splitmix64(seed, d)])
+
+
+def hadamard(d: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order d from its definition (-1)^popcount(i&j)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    i = np.arange(d)
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+# --------------------------------------------------------------------------
+# Codec
+# --------------------------------------------------------------------------
+class Codec:
+    """What one encoder/decoder needs: d, bits, QJL width, signs, codebook.
+
+    The float64 Lloyd-Max values are rounded to float32 once; those float32
+    centroids and thresholds define the quantiser.
+    """
+
+    def __init__(self, bits: int, d: int, seed: int, qjl_m: int = 0):
+        self.bits = int(bits)
+        self.d = int(d)
+        self.seed = int(seed)
+        self.qjl_m = int(qjl_m)
+        c64, t64 = lloyd_max_gaussian(self.bits)
+        self.centroid = c64.astype(np.float32)
+        self.threshold = t64.astype(np.float32)
+        self.signs = sign_vector(self.seed, self.d)
+        self.H = hadamard(self.d)
+
+    @property
+    def code_bytes(self) -> int:
+        return self.d * self.bits // 8
+
+    @property
+    def qjl_bytes(self) -> int:
+        return self.qjl_m // 8
+
+
+def packed_bytes(d: int, bits: int, qjl_m: int = 0) -> int:
+    """Stored bytes per vector: d*bits/8 of codes + 2 B norm (+ m/8 + 2 B for QJL).
+
+    [P1] "약간의 비하인드": a 3-bit head_dim-128 block is 50 B (48 B codes + norm);
+    [P2] "핵심 발견 3": bit shifting packs several indices per byte.
+    """
+    total = d * bits // 8 + 2
+    if qjl_m:
+        total += qjl_m // 8 + 2
+    return total
+
+
+def to_half(x: np.ndarray) -> np.ndarray:
+    """float64 -> IEEE half, round to nearest even, finite values clamped to 65504."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.clip(x, -65504.0, 65504.0).astype(np.float16)
+
+
+def pack_indices(idx: np.ndarray, bits: int) -> np.ndarray:
+    """LSB-first bit stream: index i of a row occupies bits [bits*i, bits*i+bits)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    n, d = idx.shape
+    shifts = np.arange(bits)
+    bitplanes = (idx[:, :, None] >> shifts[None, None, :]) & 1  # [n][d][bits], bit b' of index i
+    stream = bitplanes.reshape(n, d * bits).astype(np.uint8)
+    return np.packbits(stream, axis=1, bitorder="little")
+
+
+def unpack_indices(codes: np.ndarray, d: int, bits: int) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    stream = np.unpackbits(codes, axis=1, bitorder="little")[:, : d * bits]
+    planes = stream.reshape(codes.shape[0], d, bits).astype(np.int64)
+    return np.sum(planes << np.arange(bits)[None, None, :], axis=2)
+
+
+def pack_signs(bits01: np.ndarray) -> np.ndarray:
+    """m sign bits per row, bit j of the row stream = bits01[:, j]."""
+    return np.packbits(np.asarray(bits01, dtype=np.uint8), axis=1, bitorder="little")
+
+
+def unpack_signs(packed: np.ndarray, m: int) -> np.ndarray:
+    return np.unpackbits(np.asarray(packed, dtype=np.uint8), axis=1, bitorder="little")[:, :m]
+
+
+def rotate(x: np.ndarray, codec: Codec) -> np.ndarray:
+    """H (D x) per row: sign flip then Walsh-Hadamard transform ([P1] v1.7.0
+    "핵심 설계 결정" item 4: internal sign flip + butterfly WHT), as a dense product."""
+    x = np.asarray(x, dtype=np.float64)
+    return (x * codec.signs[None, :]) @ codec.H.T
+
+
+def quantize(z: np.ndarray, codec: Codec) -> np.ndarray:
+    """idx = #{j : z > t_j} with the float32 thresholds (nearest centroid)."""
+    t = codec.threshold.astype(np.float64)
+    return np.sum(z[..., None] > t, axis=-1)
+
+
+def encode(x: np.ndarray, codec: Codec, S: np.ndarray | None = None):
+    """Encode rows of x (any float dtype, promoted to float64).
+
+    Steps: norm; z = H(Dx)/norm (z = 0 for a zero vector); nearest Lloyd-Max
+    index; LSB-first pack; half norm.  With QJL (codec.qjl_m > 0, S [m][d]):
+    r = (z - c[idx]) / sqrt(d); gamma = ||r|| as half; bit_j = [(S r)_j >= 0].
+    QJL is "the paper's TurboQuant_prod: a 1-bit residual correction on K"
+    ([P1] "QJL 보정 효과"; [P1] v1.4.2 item 2 for sign bits + scalar per block).
+
+    Returns dict(codes [n][d*b/8] u8, norms [n] f16, qjl [n][m/8] u8, gamma [n] f16,
+    z [n][d] f64, idx [n][d] i64, u [n][m] f64).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n_rows = x.shape[0]
+    norm = np.sqrt(np.sum(x * x, axis=1))
+    y = rotate(x, codec)
+    safe = np.where(norm > 0, norm, 1.0)
+    z = np.where(norm[:, None] > 0, y / safe[:, None], 0.0)
+    idx = quantize(z, codec)
+    out = {
+        "codes": pack_indices(idx, codec.bits),
+        "norms": to_half(norm),
+        "z": z,
+        "idx": idx,
+        "norm": norm,
+    }
+    if codec.qjl_m:
+        if S is None or S.shape != (codec.qjl_m, codec.d):
+            raise ValueError("QJL needs S of shape [m][d]")
+        c = codec.centroid.astype(np.float64)
+        r = (z - c[idx]) / math.sqrt(codec.d)
+        gamma = np.sqrt(np.sum(r * r, axis=1))
+        u = r @ np.asarray(S, dtype=np.float64).T
+        out["qjl"] = pack_signs(u >= 0.0)
+        out["gamma"] = to_half(gamma)
+        out["gamma64"] = gamma
+        out["u"] = u
+        out["r"] = r
+    else:
+        out["qjl"] = np.zeros((n_rows, 0), dtype=np.uint8)
+        out["gamma"] = np.zeros((n_rows,), dtype=np.float16)
+    return out
+
+
+def decode(codes: np.ndarray, norms16: np.ndarray, codec: Codec) -> np.ndarray:
+    """x_hat = n16 * D * H(c[idx]) / d (H H = d I, D D = I)."""
+    idx = unpack_indices(codes, codec.d, codec.bits)
+    c = codec.centroid.astype(np.float64)[idx]
+    w = c @ codec.H.T / codec.d
+    return np.asarray(norms16, dtype=np.float64)[:, None] * w * codec.signs[None, :]
+
+
+def qjl_term(q: np.ndarray, qjl_packed: np.ndarray, norms16: np.ndarray,
+             gamma16: np.ndarray, S: np.ndarray, codec: Codec) -> np.ndarray:
+    """QJL estimate of <q, x - x_hat> for every (query, row) pair.
+
+    With a = H(Dq): <q, x> = n/d <a, z> and the residual part n/d <a, rho> is
+    estimated by n * gamma * sqrt(pi/2)/m * <S a / sqrt(d), sign(S r)>, which is
+    unbiased over S because E[sign(s.r) (s.a)] = sqrt(2/pi) <a, r>/||r|| for
+    s ~ N(0, I).  ([P1] "Attention Sharpening" describes the same scalar
+    correction d_qjl * sum(Q_wht2[i] * sign[i]).)  Returns [n_q][n_rows].
+    """
+    m = codec.qjl_m
+    a = rotate(np.atleast_2d(q), codec)
+    qhat = (a / math.sqrt(codec.d)) @ np.asarray(S, dtype=np.float64).T  # [n_q][m]
+    sgn = 2.0 * unpack_signs(qjl_packed, m).astype(np.float64) - 1.0  # [n][m]
+    coef = np.asarray(norms16, np.float64) * np.asarray(gamma16, np.float64) * math.sqrt(math.pi / 2) / m
+    return (qhat @ sgn.T) * coef[None, :]
+
+
+def attention(q: np.ndarray, k_codes, k_norms, v_codes, v_norms, kc: Codec, vc: Codec,
+              scale: float, k_qjl=None, k_gamma=None, S=None) -> np.ndarray:
+    """Exact softmax attention of one query group over one decoded cache.
+
+    Decompress-then-attend ([P3] "결과 — 피크 VRAM" describes the reference
+    implementation materialising the full fp16 K/V each step): K_hat, V_hat are
+    decoded, s_t = scale <q, K_hat_t> (+ the QJL estimate of the residual part),
+    p = softmax(s) (max-subtracted), o = sum_t p_t V_hat_t.
+
+    q [n_q][d]; caches [ctx][...]; returns [n_q][d] float64.  An empty context
+    gives a zero output.
+    """
+    q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+    ctx = k_codes.shape[0]
+    if ctx == 0:
+        return np.zeros((q.shape[0], vc.d))
+    K = decode(k_codes, k_norms, kc)
+    V = decode(v_codes, v_norms, vc)
+    s = scale * (q @ K.T)
+    if kc.qjl_m:
+        s = s + scale * qjl_term(q, k_qjl, k_norms, k_gamma, S, kc)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ V
+
+
+def gqa_attention(q, ctx_len, k_codes, k_norms, v_codes, v_norms, kc, vc, scale,
+                  k_qjl=None, k_gamma=None, S=None, heads=None):
+    """Batched grouped-query attention: q [B][Hq][d], caches [B][Hkv][cap][...].
+
+    Query head h reads kv head h // (Hq/Hkv).  ``heads`` optionally restricts the
+    computation to a list of (b, h) pairs; the result then has one row per pair.
+    """
+    B, Hq, d = q.shape
+    Hkv = k_codes.shape[1]
+    g = Hq // Hkv
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    out = np.zeros((len(pairs), vc.d))
+    for row, (b, h) in enumerate(pairs):
+        kh = h // g
+        n = int(ctx_len[b])
+        args = {}
+        if kc.qjl_m:
+            args = dict(k_qjl=k_qjl[b, kh, :n], k_gamma=k_gamma[b, kh, :n], S=S)
+        out[row] = attention(q[b, h][None, :], k_codes[b, kh, :n], k_norms[b, kh, :n],
+                             v_codes[b, kh, :n], v_norms[b, kh, :n], kc, vc, scale, **args)[0]
+    return out
+
+
+def ip_scores(q: np.ndarray, codes, norms16, qjl_packed, gamma16, S, codec: Codec) -> np.ndarray:
+    """Unbiased inner-product estimates <q, x_t> for all (query, database row) pairs.
+
+    est = n16 (<H(Dq), c[idx]>/d + gamma16 sqrt(pi/2)/m <S H(Dq)/sqrt(d), 2 bit - 1>);
+    the vector-search use case for which the QJL term is unbiased and helps
+    ([P2] "핵심 발견 1 — QJL 레이어를 제거하라": no softmax in vector search).
+    """
+    q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+    X = decode(codes, norms16, codec)
+    est = q @ X.T
+    if codec.qjl_m:
+        est = est + qjl_term(q, qjl_packed, norms16, gamma16, S, codec)
+    return est
+
+
+def topk(scores: np.ndarray, k: int):
+    """Per row, the k largest scores ordered by (score desc, id asc)."""
+    scores = np.atleast_2d(scores)
+    n_q, n = scores.shape
+    ids = np.zeros((n_q, k), dtype=np.int64)
+    vals = np.zeros((n_q, k))
+    ar = np.arange(n)
+    for i in range(n_q):
+        order = np.lexsort((ar, -scores[i]))[:k]
+        ids[i] = order
+        vals[i] = scores[i, order]
+    return vals, ids
+
+
+def ip_search(q, codes, norms16, qjl_packed, gamma16, S, codec: Codec, k: int):
+    """Estimator over every database row, then exact top-k per query."""
+    return topk(ip_scores(q, codes, norms16, qjl_packed, gamma16, S, codec), k)
