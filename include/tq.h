@@ -1,0 +1,215 @@
+/*
+ * tq.h -- C ABI of the TurboQuant KV-cache hot path for AMD MI355X (gfx950).
+ *
+ * The operations follow three public pages about TurboQuant:
+ *   [P1] "TurboQuant KV 캐시 압축 for llama.cpp" (AmesianX README_KO on stig.sh)
+ *   [P2] "윈도우용 터보퀀트(TurboQuant) 구현을 개선하다" (idea.jsleekr.com)
+ *   [P3] "[GitHub 탐방] TurboQuant 3-bit KV 캐시 압축 — 단일 GPU 재현 기록" (velog.io)
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless marked "host".  The library never
+ *     allocates, frees or synchronises inside tq_encode, tq_decode,
+ *     tq_attn_decode or tq_ip_search: the caller owns every buffer.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous on that stream; results are valid once the
+ *     stream has been synchronised.
+ *   - Return value: TQ_OK (0) or a negative TQ_E* code.  All argument checks
+ *     happen on the host before any launch; on an error nothing is launched
+ *     and no output is touched.  TQ_EDEVICE reports a failed launch
+ *     (hipGetLastError after the launch).
+ *   - The library keeps no mutable global state: calls on different streams
+ *     may run concurrently.
+ *   - Non-finite inputs give unspecified (but in-bounds) results.
+ *
+ * Packed formats (all little-endian):
+ *   codes  : one row of d*bits/8 bytes per vector; index i occupies bits
+ *            [bits*i, bits*i + bits) of the row read as an LSB-first bit stream;
+ *            index 0 is the most negative centroid.
+ *   norms  : IEEE half (uint16) per vector, round to nearest even, clamped to 65504.
+ *   qjl    : one row of m/8 bytes per vector; bit j (LSB-first) is 1 when the
+ *            j-th projection of the residual is >= 0.
+ *   gamma  : IEEE half per vector, the norm of the residual r (see tq_encode).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    TQ_OK = 0,
+    TQ_EINVAL = -1,        /* null pointer, bad size, stride or alignment      */
+    TQ_EUNSUPPORTED = -2,  /* d, bits, qjl_m, k or head ratio outside support  */
+    TQ_EWORKSPACE = -3,    /* workspace missing or smaller than required       */
+    TQ_EDEVICE = -4        /* the HIP runtime reported a launch failure        */
+};
+
+enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 };
+
+/*
+ * One quantiser: what the encoder and decoder of one cache (K or V) share.
+ * Host struct, filled by tq_codebook and passed by pointer; the library copies
+ * it by value into kernel arguments.
+ *
+ *   d           head dimension: 32, 64, 128 or 256 (attention: 128 or 256).
+ *   bits        1..4 bits per coordinate (L = 2^bits centroids).
+ *   qjl_m       0, or the number of QJL projections (multiple of 32, <= 256).
+ *   sign_mask   bit i (word i/32, bit i%32) set means D_ii = -1: the seeded
+ *               random sign flip applied before the Walsh-Hadamard transform
+ *               ([P1] v1.7.0 "핵심 설계 결정" item 4, "tbq_signs").
+ *   centroid    L float32 Lloyd-Max centroids of N(0,1), ascending, exactly
+ *               symmetric; entries >= L are 0.
+ *   threshold   L-1 float32 midpoints; the middle one is exactly 0.
+ */
+typedef struct {
+    int32_t d;
+    int32_t bits;
+    int32_t qjl_m;
+    int32_t reserved;
+    uint64_t seed;
+    uint32_t sign_mask[8];
+    float centroid[16];
+    float threshold[15];
+} tq_codec;
+
+/*
+ * tq_codebook -- fill a codec (host only, deterministic, no device access).
+ *
+ * The scalar stage is the Lloyd-Max quantiser ([P1] page header "Walsh-Hadamard
+ * Transform + Lloyd-Max 양자화"; [P3] "GPU 세대가 바뀌면": each coordinate maps to
+ * one of 2^bits centroids) of the rotated unit coordinate z = H(Dx)/||x||, which
+ * has unit variance, so the codebook is that of N(0,1).  It is solved in
+ * double precision by the Lloyd fixed-point iteration (centroid = conditional
+ * mean of its cell, threshold = midpoint) on the positive half, mirrored, then
+ * rounded to float32.  Signs: D_ii = -1 when bit 63 of the (i+1)-th SplitMix64
+ * output from state `seed` is set.
+ *
+ * Errors: TQ_EINVAL if out is NULL; TQ_EUNSUPPORTED for d not in {32,64,128,256},
+ * bits not in 1..4, qjl_m not a multiple of 32 in 0..256.
+ */
+int tq_codebook(int bits, int d, uint64_t seed, int qjl_m, tq_codec *out);
+
+/*
+ * tq_encode -- quantise n vectors ([P1] v1.7.0 "핵심 설계 결정" item 4: sign flip +
+ * butterfly WHT inside the encoder; [P2] "핵심 발견 3": bit-packed indices; [P1]
+ * "약간의 비하인드": a 3-bit d=128 block is 48 B of codes + a 2 B norm).
+ *
+ * For each row x (d values of x_dtype, row i at x + i*x_row_stride elements):
+ *   n = ||x||_2;  z = H(D x)/n (z = 0 when n = 0);  idx_i = #{j : z_i > t_j};
+ *   codes = packed idx;  norms = half(n).
+ * With codec->qjl_m = m > 0 (the paper's TurboQuant_prod residual correction,
+ * [P1] "QJL 보정 효과", K caches only):
+ *   r = (z - c[idx]) / sqrt(d);  gamma = half(||r||);  qjl bit j = [(S r)_j >= 0].
+ *
+ *   c              codec (host pointer).
+ *   x              [n][x_row_stride] elements; 16-byte aligned; x_row_stride*elem
+ *                  must be a multiple of 16 bytes and x_row_stride >= d.
+ *   codes          row i at codes + i*code_row_stride; code_row_stride >= d*bits/8,
+ *                  multiple of 4; codes 4-byte aligned.
+ *   norms_f16      [n] halves.
+ *   qjl_S          [m][d] float32 row-major (N(0,1) draws made by the caller);
+ *                  NULL when m = 0.
+ *   qjl_bits       [n][m/8] bytes, 4-byte aligned; NULL when m = 0.
+ *   qjl_gamma_f16  [n] halves; NULL when m = 0.
+ * n = 0 is valid and launches nothing.  Vectors whose squared norm underflows
+ * float32 are encoded as the zero vector.
+ */
+int tq_encode(const tq_codec *c, const void *x, int x_dtype, int64_t n, int64_t x_row_stride,
+              uint8_t *codes, int64_t code_row_stride, uint16_t *norms_f16,
+              const float *qjl_S, uint8_t *qjl_bits, uint16_t *qjl_gamma_f16, void *stream);
+
+/*
+ * tq_decode -- reconstruct x_hat = half_norm * D H(c[idx]) / d for n rows
+ * (the inverse rotation; used to check reconstructions, not on the hot path).
+ *   codes: row i at codes + i*code_row_stride (4-byte aligned stride and base);
+ *   norms_f16 [n]; x_hat [n][d] float32 (16-byte aligned).
+ */
+int tq_decode(const tq_codec *c, const uint8_t *codes, int64_t code_row_stride,
+              const uint16_t *norms_f16, int64_t n, float *x_hat, void *stream);
+
+/*
+ * tq_attn_decode -- one decode step of grouped-query attention read straight
+ * from the packed cache (compressed-domain attention, [P3] "결과 — 피크 VRAM"
+ * contrasts it with decompress-then-attend).
+ *
+ * For batch b and query head h (kv head kh = h / (n_q_heads/n_kv_heads)):
+ *   q_rot = H(D_K q) (the query is rotated once, [P1] v1.7.0 item 4: the same WHT
+ *           on the Q side, so the rotation cancels by Parseval);
+ *   s_t   = scale * n_t/d * <q_rot, c_K[idx_t]>
+ *           (+ with QJL: scale * n_t * gamma_t * sqrt(pi/2)/m * <S q_rot/sqrt(d), 2 bit_t - 1>,
+ *            [P1] "Attention Sharpening": d_qjl * sum(Q_wht2[i] * sign[i]));
+ *   p     = softmax(s) over t < ctx_len[b] (exact, float32 accumulation,
+ *           [P1] v1.5.2 "핵심 변경" item 1: float, not half2);
+ *   o     = D_V H( sum_t p_t nV_t c_V[vidx_t] ) / d  (V accumulated in the rotated
+ *           domain, one inverse WHT per output, [P1] v1.5.1 item 2).
+ *
+ *   kc, vc          K and V codecs (host); independent bit widths ([P2] "핵심 발견 2":
+ *                   asymmetric K/V).  kc->d == vc->d in {128, 256}; vc->qjl_m must
+ *                   be 0 (QJL is K-only, [P1] "지원 K/V 조합").
+ *   q               [batch][n_q_heads][d] of q_dtype, 16-byte aligned, contiguous.
+ *   ctx_len         [batch] int32 on the device; values are clamped to [0, ctx_cap].
+ *   k_codes         [batch][n_kv_heads][ctx_cap][d*kbits/8]   contiguous, 16-B aligned
+ *   k_norms         [batch][n_kv_heads][ctx_cap] halves
+ *   k_qjl, k_gamma  [batch][n_kv_heads][ctx_cap][m/8], [..][ctx_cap] halves; NULL if m = 0
+ *   qjl_S           [m][d] float32; NULL if m = 0
+ *   v_codes, v_norms as k_codes / k_norms with vbits
+ *   out             [batch][n_q_heads][d] float32; a sequence with ctx_len 0 gives 0.
+ *   workspace       device scratch of at least tq_attn_workspace_bytes(...) bytes,
+ *                   16-byte aligned (query rotations and split-K partials).
+ * Supported: n_q_heads % n_kv_heads == 0, group size g = n_q_heads/n_kv_heads
+ * with g <= 8 or g a multiple of a divisor in 1..8 (heads are processed in
+ * chunks of at most 8).  ctx_cap >= 1.
+ */
+int tq_attn_decode(const tq_codec *kc, const tq_codec *vc,
+                   const void *q, int q_dtype, int batch, int n_q_heads, int n_kv_heads,
+                   const int32_t *ctx_len, int64_t ctx_cap,
+                   const uint8_t *k_codes, const uint16_t *k_norms,
+                   const uint8_t *k_qjl, const uint16_t *k_gamma, const float *qjl_S,
+                   const uint8_t *v_codes, const uint16_t *v_norms,
+                   float scale, float *out, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/* Bytes of workspace tq_attn_decode needs for these sizes (0 on bad arguments). */
+size_t tq_attn_workspace_bytes(const tq_codec *kc, const tq_codec *vc, int batch,
+                               int n_q_heads, int n_kv_heads, int64_t ctx_cap);
+
+/*
+ * tq_ip_search -- inner-product search over QJL-encoded database vectors, the
+ * non-softmax use case for which the QJL estimator is unbiased and helps
+ * ([P2] "핵심 발견 1 — QJL 레이어를 제거하라": vector search has no softmax).
+ *
+ *   est(q, t) = n_t ( <H(Dq), c[idx_t]>/d
+ *                     + gamma_t sqrt(pi/2)/m <S H(Dq)/sqrt(d), 2 bit_t - 1> )
+ * then the k largest estimates per query, ordered by (estimate desc, id asc).
+ *
+ *   c            codec (host) with qjl_m = m (0 = MSE-only estimate).
+ *   q            [n_q][d] float32, 16-byte aligned.
+ *   codes, norms [n_db][d*bits/8], [n_db]; qjl_bits [n_db][m/8]; qjl_gamma [n_db].
+ *   out_scores   [n_q][k] float32;  out_ids [n_q][k] int64.  If n_db < k the tail
+ *                is filled with -inf and id -1.
+ *   workspace    >= tq_search_workspace_bytes(...) bytes, 16-byte aligned.
+ * Supported: d in {128, 256}, 1 <= k <= 32, n_db < 2^31.
+ */
+int tq_ip_search(const tq_codec *c, const float *q, int n_q,
+                 const uint8_t *codes, const uint16_t *norms,
+                 const uint8_t *qjl_bits, const uint16_t *qjl_gamma, const float *qjl_S,
+                 int64_t n_db, int k, float *out_scores, int64_t *out_ids,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+size_t tq_search_workspace_bytes(const tq_codec *c, int n_q, int64_t n_db, int k);
+
+/* Stored bytes per vector: d*bits/8 codes + 2 B norm (+ m/8 + 2 B with QJL). */
+size_t tq_packed_bytes(int d, int bits, int qjl_m);
+
+/* Static description of an error code (never NULL). */
+const char *tq_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,324 @@
+// Host side of the C ABI declared in include/tq.h: codebook construction,
+// argument validation, workspace sizing and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <string.h>
+
+#include "tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+// ------------------------------------------------------------ codebook ----
+double normal_pdf(double x) {
+    if (isinf(x)) return 0.0;
+    return exp(-0.5 * x * x) * 0.3989422804014327;  // 1/sqrt(2 pi)
+}
+
+// P(X > x) for X ~ N(0,1); erfc keeps the tail accurate.
+double normal_tail(double x) {
+    if (isinf(x)) return x > 0 ? 0.0 : 1.0;
+    return 0.5 * erfc(x * 0.7071067811865476);
+}
+
+// x with P(X > x) = p, 0 < p <= 0.5, by bisection (x >= 0).
+double tail_inverse(double p) {
+    double lo = 0.0, hi = 40.0;
+    for (int i = 0; i < 200; ++i) {
+        const double mid = 0.5 * (lo + hi);
+        if (normal_tail(mid) > p) lo = mid; else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+// Lloyd-Max quantiser of N(0,1) with 2^bits levels: the fixed point of
+// "centroid = conditional mean of its cell" and "threshold = midpoint of the
+// neighbouring centroids", solved on the positive half (cells [tau_k, tau_k+1)
+// with tau_0 = 0, tau_half = inf) and mirrored.
+void lloyd_max(int bits, double* cent, double* thr) {
+    const int L = 1 << bits, half = L / 2;
+    double tau[9], c[8];
+    tau[0] = 0.0;
+    for (int k = 1; k < half; ++k) tau[k] = tail_inverse(0.5 - (double)k / L);
+    tau[half] = INFINITY;
+    for (int it = 0; it < 1000000; ++it) {
+        for (int k = 0; k < half; ++k)
+            c[k] = (normal_pdf(tau[k]) - normal_pdf(tau[k + 1])) / (normal_tail(tau[k]) - normal_tail(tau[k + 1]));
+        double delta = 0.0;
+        for (int k = 1; k < half; ++k) {
+            const double nt = 0.5 * (c[k - 1] + c[k]);
+            delta = fmax(delta, fabs(nt - tau[k]));
+            tau[k] = nt;
+        }
+        if (delta < 1e-15) break;
+    }
+    for (int k = 0; k < half; ++k)
+        c[k] = (normal_pdf(tau[k]) - normal_pdf(tau[k + 1])) / (normal_tail(tau[k]) - normal_tail(tau[k + 1]));
+    for (int k = 0; k < half; ++k) {
+        cent[half + k] = c[k];
+        cent[half - 1 - k] = -c[k];
+    }
+    thr[half - 1] = 0.0;
+    for (int k = 1; k < half; ++k) {
+        const double t = 0.5 * (c[k - 1] + c[k]);
+        thr[half - 1 + k] = t;
+        thr[half - 1 - k] = -t;
+    }
+}
+
+// SplitMix64 output number `index` (1-based) from state `seed`.
+uint64_t splitmix64_at(uint64_t seed, uint64_t index) {
+    uint64_t z = seed + index * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+bool valid_d(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+bool valid_codec(const tq_codec* c) {
+    return c && valid_d(c->d) && c->bits >= 1 && c->bits <= 4 && c->qjl_m >= 0 && c->qjl_m <= 256 &&
+           c->qjl_m % 32 == 0;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int finish(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EDEVICE; }
+
+}  // namespace
+
+namespace tqi {
+void fill_codec_args(const tq_codec* c, CodecArgs* a) {
+    memcpy(a->sign_mask, c->sign_mask, sizeof(a->sign_mask));
+    memcpy(a->centroid, c->centroid, sizeof(a->centroid));
+    memcpy(a->threshold, c->threshold, sizeof(a->threshold));
+    a->d = c->d;
+    a->bits = c->bits;
+    a->qjl_m = c->qjl_m;
+}
+}  // namespace tqi
+
+extern "C" {
+
+int tq_codebook(int bits, int d, uint64_t seed, int qjl_m, tq_codec* out) {
+    if (!out) return TQ_EINVAL;
+    if (!valid_d(d) || bits < 1 || bits > 4 || qjl_m < 0 || qjl_m > 256 || qjl_m % 32 != 0)
+        return TQ_EUNSUPPORTED;
+    memset(out, 0, sizeof(*out));
+    out->d = d;
+    out->bits = bits;
+    out->qjl_m = qjl_m;
+    out->seed = seed;
+    for (int i = 0; i < d; ++i)
+        if (splitmix64_at(seed, (uint64_t)i + 1) >> 63) out->sign_mask[i >> 5] |= 1u << (i & 31);
+    double c[16], t[15];
+    lloyd_max(bits, c, t);
+    const int L = 1 << bits;
+    for (int k = 0; k < L; ++k) out->centroid[k] = (float)c[k];
+    for (int k = 0; k < L - 1; ++k) out->threshold[k] = (float)t[k];
+    return TQ_OK;
+}
+
+size_t tq_packed_bytes(int d, int bits, int qjl_m) {
+    if (d <= 0 || bits < 1 || bits > 4 || qjl_m < 0) return 0;
+    size_t n = (size_t)d * bits / 8 + 2;
+    if (qjl_m) n += (size_t)qjl_m / 8 + 2;
+    return n;
+}
+
+const char* tq_strerror(int code) {
+    switch (code) {
+        case TQ_OK: return "ok";
+        case TQ_EINVAL: return "invalid argument (null pointer, size, stride or alignment)";
+        case TQ_EUNSUPPORTED: return "unsupported configuration (d, bits, qjl_m, k or head ratio)";
+        case TQ_EWORKSPACE: return "workspace missing or too small";
+        case TQ_EDEVICE: return "HIP launch failed";
+        default: return "unknown error code";
+    }
+}
+
+int tq_encode(const tq_codec* c, const void* x, int x_dtype, int64_t n, int64_t x_row_stride, uint8_t* codes,
+              int64_t code_row_stride, uint16_t* norms_f16, const float* qjl_S, uint8_t* qjl_bits,
+              uint16_t* qjl_gamma_f16, void* stream) {
+    if (!c) return TQ_EINVAL;
+    if (!valid_codec(c)) return TQ_EUNSUPPORTED;
+    if (x_dtype != TQ_F32 && x_dtype != TQ_F16 && x_dtype != TQ_BF16) return TQ_EINVAL;
+    if (n < 0) return TQ_EINVAL;
+    if (n == 0) return TQ_OK;
+    const int esz = x_dtype == TQ_F32 ? 4 : 2;
+    if (!x || !codes || !norms_f16 || !aligned(x, 16) || !aligned(codes, 4) || !aligned(norms_f16, 2))
+        return TQ_EINVAL;
+    if (x_row_stride < c->d || (x_row_stride * esz) % 16 != 0) return TQ_EINVAL;
+    if (code_row_stride < c->d * c->bits / 8 || code_row_stride % 4 != 0) return TQ_EINVAL;
+    if (c->qjl_m > 0) {
+        if (!qjl_S || !qjl_bits || !qjl_gamma_f16 || !aligned(qjl_bits, 4) || !aligned(qjl_gamma_f16, 2) ||
+            !aligned(qjl_S, 4))
+            return TQ_EINVAL;
+    }
+    tqi::EncodeArgs a;
+    tqi::fill_codec_args(c, &a.c);
+    a.x = x;
+    a.n = n;
+    a.x_stride = x_row_stride;
+    a.codes = codes;
+    a.code_stride = code_row_stride;
+    a.norms = norms_f16;
+    a.S = qjl_S;
+    a.qjl = qjl_bits;
+    a.gamma = qjl_gamma_f16;
+    return finish(tqi::launch_encode(a, x_dtype, (hipStream_t)stream));
+}
+
+int tq_decode(const tq_codec* c, const uint8_t* codes, int64_t code_row_stride, const uint16_t* norms_f16,
+              int64_t n, float* x_hat, void* stream) {
+    if (!c) return TQ_EINVAL;
+    if (!valid_codec(c)) return TQ_EUNSUPPORTED;
+    if (n < 0) return TQ_EINVAL;
+    if (n == 0) return TQ_OK;
+    if (!codes || !norms_f16 || !x_hat || !aligned(x_hat, 16) || !aligned(norms_f16, 2)) return TQ_EINVAL;
+    if (code_row_stride < c->d * c->bits / 8) return TQ_EINVAL;
+    tqi::DecodeArgs a;
+    tqi::fill_codec_args(c, &a.c);
+    a.codes = codes;
+    a.code_stride = code_row_stride;
+    a.norms = norms_f16;
+    a.n = n;
+    a.out = x_hat;
+    return finish(tqi::launch_decode(a, (hipStream_t)stream));
+}
+
+static int attn_check(const tq_codec* kc, const tq_codec* vc, int batch, int n_q_heads, int n_kv_heads,
+                      int64_t ctx_cap, int* splits, int64_t* split_tokens, int* G) {
+    if (!kc || !vc) return TQ_EINVAL;
+    if (!valid_codec(kc) || !valid_codec(vc)) return TQ_EUNSUPPORTED;
+    if (kc->d != vc->d || (kc->d != 128 && kc->d != 256) || vc->qjl_m != 0) return TQ_EUNSUPPORTED;
+    if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || ctx_cap <= 0 || batch > 65535) return TQ_EINVAL;
+    if (n_q_heads % n_kv_heads != 0) return TQ_EUNSUPPORTED;
+    const int g = n_q_heads / n_kv_heads;
+    tqi::attn_plan(batch, n_kv_heads, g, ctx_cap, splits, split_tokens, G);
+    if ((int64_t)n_kv_heads * (g / *G) > 65535) return TQ_EUNSUPPORTED;
+    return TQ_OK;
+}
+
+size_t tq_attn_workspace_bytes(const tq_codec* kc, const tq_codec* vc, int batch, int n_q_heads, int n_kv_heads,
+                               int64_t ctx_cap) {
+    int splits, G;
+    int64_t per;
+    if (attn_check(kc, vc, batch, n_q_heads, n_kv_heads, ctx_cap, &splits, &per, &G) != TQ_OK) return 0;
+    return tqi::attn_workspace(batch, n_q_heads, kc->d, kc->qjl_m, splits);
+}
+
+int tq_attn_decode(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch, int n_q_heads,
+                   int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap, const uint8_t* k_codes,
+                   const uint16_t* k_norms, const uint8_t* k_qjl, const uint16_t* k_gamma, const float* qjl_S,
+                   const uint8_t* v_codes, const uint16_t* v_norms, float scale, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    int splits, G;
+    int64_t per;
+    const int rc = attn_check(kc, vc, batch, n_q_heads, n_kv_heads, ctx_cap, &splits, &per, &G);
+    if (rc != TQ_OK) return rc;
+    if (q_dtype != TQ_F32 && q_dtype != TQ_F16 && q_dtype != TQ_BF16) return TQ_EINVAL;
+    if (!q || !ctx_len || !k_codes || !k_norms || !v_codes || !v_norms || !out) return TQ_EINVAL;
+    if (!aligned(q, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(out, 16) ||
+        !aligned(k_norms, 2) || !aligned(v_norms, 2) || !aligned(ctx_len, 4))
+        return TQ_EINVAL;
+    if (kc->qjl_m > 0 && (!k_qjl || !k_gamma || !qjl_S || !aligned(k_qjl, 4) || !aligned(k_gamma, 2)))
+        return TQ_EINVAL;
+    if (!isfinite(scale)) return TQ_EINVAL;
+    const int d = kc->d, m = kc->qjl_m;
+    const size_t need = tqi::attn_workspace(batch, n_q_heads, d, m, splits);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return TQ_EWORKSPACE;
+
+    tqi::AttnArgs a;
+    tqi::fill_codec_args(kc, &a.kc);
+    tqi::fill_codec_args(vc, &a.vc);
+    a.q = q;
+    a.q_dtype = q_dtype;
+    a.batch = batch;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.g = n_q_heads / n_kv_heads;
+    a.heads_per_chunk = G;
+    a.chunks = a.g / G;
+    a.ctx_len = ctx_len;
+    a.ctx_cap = ctx_cap;
+    a.k_codes = k_codes;
+    a.k_norms = k_norms;
+    a.k_qjl = k_qjl;
+    a.k_gamma = k_gamma;
+    a.S = qjl_S;
+    a.v_codes = v_codes;
+    a.v_norms = v_norms;
+    a.scale = scale;
+    a.out = out;
+    const size_t heads = (size_t)batch * n_q_heads;
+    float* ws = (float*)workspace;
+    auto al = [](size_t n) { return (n + 63) & ~(size_t)63; };
+    a.qrot = ws;
+    a.qproj = ws + al(heads * d);
+    a.part = a.qproj + al(heads * (size_t)m);
+    a.splits = splits;
+    a.split_tokens = per;
+    return finish(tqi::launch_attn(a, (hipStream_t)stream));
+}
+
+static int search_check(const tq_codec* c, int n_q, int64_t n_db, int k) {
+    if (!c) return TQ_EINVAL;
+    if (!valid_codec(c)) return TQ_EUNSUPPORTED;
+    if (c->d != 128 && c->d != 256) return TQ_EUNSUPPORTED;
+    if (k < 1 || k > 32) return TQ_EUNSUPPORTED;
+    if (n_q <= 0 || n_db < 0 || n_q > 65535 * 64) return TQ_EINVAL;
+    if (n_db > ((int64_t)1 << 31) - 1) return TQ_EUNSUPPORTED;
+    return TQ_OK;
+}
+
+size_t tq_search_workspace_bytes(const tq_codec* c, int n_q, int64_t n_db, int k) {
+    if (search_check(c, n_q, n_db, k) != TQ_OK) return 0;
+    int nb;
+    int64_t rows;
+    tqi::search_plan(n_q, n_db, k, &nb, &rows);
+    return tqi::search_workspace(n_q, c->d, c->qjl_m, k, nb);
+}
+
+int tq_ip_search(const tq_codec* c, const float* q, int n_q, const uint8_t* codes, const uint16_t* norms,
+                 const uint8_t* qjl_bits, const uint16_t* qjl_gamma, const float* qjl_S, int64_t n_db, int k,
+                 float* out_scores, int64_t* out_ids, void* workspace, size_t workspace_bytes, void* stream) {
+    const int rc = search_check(c, n_q, n_db, k);
+    if (rc != TQ_OK) return rc;
+    if (!q || !out_scores || !out_ids || !aligned(q, 16)) return TQ_EINVAL;
+    if (n_db > 0 && (!codes || !norms || !aligned(codes, 4) || !aligned(norms, 2))) return TQ_EINVAL;
+    if (c->qjl_m > 0 && n_db > 0 && (!qjl_bits || !qjl_gamma || !qjl_S || !aligned(qjl_bits, 4)))
+        return TQ_EINVAL;
+    if (c->qjl_m > 0 && !qjl_S) return TQ_EINVAL;
+    int nb;
+    int64_t rows;
+    tqi::search_plan(n_q, n_db, k, &nb, &rows);
+    const size_t need = tqi::search_workspace(n_q, c->d, c->qjl_m, k, nb);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return TQ_EWORKSPACE;
+    tqi::SearchArgs a;
+    tqi::fill_codec_args(c, &a.c);
+    a.q = q;
+    a.n_q = n_q;
+    a.codes = codes;
+    a.norms = norms;
+    a.qjl = qjl_bits;
+    a.gamma = qjl_gamma;
+    a.S = qjl_S;
+    a.n_db = n_db;
+    a.k = k;
+    a.out_scores = out_scores;
+    a.out_ids = out_ids;
+    float* ws = (float*)workspace;
+    const size_t qa = ((size_t)n_q * (c->d + c->qjl_m) + 63) & ~(size_t)63;
+    const size_t cand = (((size_t)n_q * nb * k) + 63) & ~(size_t)63;
+    a.qrot = ws;
+    a.qproj = nullptr;
+    a.cand_s = ws + qa;
+    a.cand_i = (int32_t*)(ws + qa + cand);
+    a.n_blocks = nb;
+    a.block_rows = rows;
+    return finish(tqi::launch_search(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

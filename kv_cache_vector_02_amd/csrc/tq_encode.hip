@@ -1,0 +1,332 @@
+// Encode and decode kernels for gfx950.
+//
+// Encode one vector per group of LPV = d/8 lanes: 16-byte loads, float32 norm
+// by a group reduction, sign flip, register/DPP Walsh-Hadamard transform,
+// Lloyd-Max index by counting scaled thresholds, bit packing with the quad's
+// bytes assembled into whole dwords, half norm.  The QJL variant additionally
+// stages the residual r of a 32-vector tile in LDS and forms the sign bits of
+// S r with a register-tiled product against S streamed through LDS.
+//
+// The method steps follow "TurboQuant KV 캐시 압축 for llama.cpp" (v1.7.0
+// "핵심 설계 결정" item 4: internal sign flip + butterfly WHT in the encoder;
+// "약간의 비하인드": 50 B per 3-bit d=128 block) and the TurboQuant PyTorch
+// write-up on idea.jsleekr.com ("핵심 발견 3": bit-shift packing).
+#include <hip/hip_runtime.h>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tqi {
+namespace {
+
+using namespace tqd;
+
+// Index of z = w/n with the float32 thresholds t_j: idx = #{j : z > t_j}.
+// The comparison uses w against t_j*n (n > 0); the codebook is symmetric with
+// t_{L/2-1} = 0, so for w > 0 idx = L/2 + #{k : w > T_k} and for w <= 0
+// idx = L/2 - 1 - #{k : |w| >= T_k}, over the positive scaled thresholds T_k.
+// Both counts compare non-negative floats, done exactly on their bit patterns:
+// a >= T  <=>  bits(a) + 1 > bits(T).
+template <int BITS>
+__device__ __forceinline__ uint32_t quantize(float w, const uint32_t (&T)[(1 << BITS) / 2]) {
+    constexpr int HALF = (1 << BITS) / 2;
+    const uint32_t wb = as_u(w);
+    const bool pos = (int32_t)wb > 0;  // w > +0 (sign clear, not zero)
+    const uint32_t key = (wb & 0x7FFFFFFFu) + (pos ? 0u : 1u);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int k = 0; k < HALF - 1; ++k) cnt += key > T[k] ? 1u : 0u;
+    return pos ? (uint32_t)HALF + cnt : (uint32_t)(HALF - 1) - cnt;
+}
+
+// Write the packed codes of one vector: each lane owns BITS bytes (8 indices);
+// lane j of each quad stores dword j of the quad's 4*BITS bytes.
+template <int BITS>
+__device__ __forceinline__ void store_codes(uint32_t* rowp, int gl, uint32_t packed, bool valid) {
+    const uint32_t p0 = quad_bcast<0>(packed), p1 = quad_bcast<1>(packed);
+    const uint32_t p2 = quad_bcast<2>(packed), p3 = quad_bcast<3>(packed);
+    const int j = gl & 3;
+    uint32_t word = 0;
+    if constexpr (BITS == 4) {
+        word = packed;
+    } else if constexpr (BITS == 3) {
+        word = j == 0 ? (p0 | (p1 << 24)) : j == 1 ? ((p1 >> 8) | (p2 << 16)) : ((p2 >> 16) | (p3 << 8));
+    } else if constexpr (BITS == 2) {
+        word = j == 0 ? (p0 | (p1 << 16)) : (p2 | (p3 << 16));
+    } else {
+        word = p0 | (p1 << 8) | (p2 << 16) | (p3 << 24);
+    }
+    if (valid && j < BITS) rowp[(gl >> 2) * BITS + j] = word;
+}
+
+struct VecState {
+    float v[8];
+    float nrm;
+};
+
+// Load row `row` (or zeros), compute the norm, sign flip and transform.
+template <int D, int DT>
+__device__ __forceinline__ void load_rotate(const EncodeArgs& a, int64_t row, bool valid, int gl,
+                                            uint32_t sbits, VecState& st) {
+    constexpr int LPV = D / 8;
+    if (valid) {
+        const char* base = static_cast<const char*>(a.x) + (row * a.x_stride + gl * 8) * elem_bytes<DT>();
+        load8<DT>(base, st.v);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.v[e] = 0.0f;
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(st.v[e], st.v[e], ss);
+    ss = group_sum<LPV>(ss);
+    st.nrm = sqrtf(ss);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.v[e] = as_f(as_u(st.v[e]) ^ (((sbits >> e) & 1u) << 31));
+    fwht<LPV>(st.v, gl);
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t pack_lane(const VecState& st, const CodecArgs& c, uint32_t (&idx)[8]) {
+    constexpr int HALF = (1 << BITS) / 2;
+    const float sc = st.nrm > 0.0f ? st.nrm : 1.0f;
+    uint32_t T[HALF];
+#pragma unroll
+    for (int k = 0; k < HALF - 1; ++k) T[k] = as_u(c.threshold[HALF + k] * sc);
+    T[HALF - 1] = 0;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        idx[e] = quantize<BITS>(st.v[e], T);
+        packed |= idx[e] << (BITS * e);
+    }
+    return packed;
+}
+
+template <int D, int BITS, int DT>
+__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+    constexpr int LPV = D / 8;
+    constexpr int VPW = 64 / LPV;
+    const int lane = threadIdx.x & 63;
+    const int gl = lane & (LPV - 1);
+    const uint32_t sbits = (a.c.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t base = wave * VPW; base < a.n; base += nwaves * VPW) {
+        const int64_t row = base + lane / LPV;
+        const bool valid = row < a.n;
+        VecState st;
+        load_rotate<D, DT>(a, row, valid, gl, sbits, st);
+        uint32_t idx[8];
+        const uint32_t packed = pack_lane<BITS>(st, a.c, idx);
+        uint32_t* rowp = reinterpret_cast<uint32_t*>(a.codes + (valid ? row : 0) * a.code_stride);
+        store_codes<BITS>(rowp, gl, packed, valid);
+        if (valid && gl == 0) a.norms[row] = norm_to_half(st.nrm);
+    }
+}
+
+// QJL variant: a block of 256 threads encodes a tile of 32 vectors.
+constexpr int QJL_TILE = 32;
+constexpr int QJL_ICHUNK = 16;
+
+template <int D, int BITS, int DT>
+__global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
+    constexpr int LPV = D / 8;
+    constexpr int VPW = 64 / LPV;
+    constexpr int RS = D + 1;  // padded row of r in LDS
+    __shared__ float r_lds[QJL_TILE * RS];
+    __shared__ float s_lds[QJL_ICHUNK * 256];
+    __shared__ float cent[16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int gl = lane & (LPV - 1);
+    const uint32_t sbits = (a.c.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+    const int m = a.c.qjl_m;
+    const float rsd = 1.0f / sqrtf((float)D);
+    if (tid < 16) cent[tid] = a.c.centroid[tid];
+    __syncthreads();
+
+    for (int64_t tile0 = (int64_t)blockIdx.x * QJL_TILE; tile0 < a.n; tile0 += (int64_t)gridDim.x * QJL_TILE) {
+        // phase 1: codes, norm, residual -> LDS, gamma
+        for (int vb = wave * VPW; vb < QJL_TILE; vb += 4 * VPW) {
+            const int vloc = vb + lane / LPV;
+            const int64_t row = tile0 + vloc;
+            const bool valid = row < a.n;
+            VecState st;
+            load_rotate<D, DT>(a, row, valid, gl, sbits, st);
+            uint32_t idx[8];
+            const uint32_t packed = pack_lane<BITS>(st, a.c, idx);
+            uint32_t* rowp = reinterpret_cast<uint32_t*>(a.codes + (valid ? row : 0) * a.code_stride);
+            store_codes<BITS>(rowp, gl, packed, valid);
+            const float inv = st.nrm > 0.0f ? 1.0f / st.nrm : 0.0f;
+            float g2 = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float z = st.v[e] * inv;
+                const float r = (z - cent[idx[e]]) * rsd;
+                r_lds[vloc * RS + gl * 8 + e] = r;
+                g2 = fmaf(r, r, g2);
+            }
+            g2 = group_sum<LPV>(g2);
+            if (valid && gl == 0) {
+                a.norms[row] = norm_to_half(st.nrm);
+                a.gamma[row] = norm_to_half(sqrtf(g2));
+            }
+        }
+        __syncthreads();
+        // phase 2: U = R S^T, thread (tv, tj): vectors tv + 8*vv, projections tj + 32*jj
+        const int tv = tid >> 5, tj = tid & 31;
+        float acc[4][8];
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) acc[vv][jj] = 0.0f;
+        const int nj = m >> 5;
+        for (int i0 = 0; i0 < D; i0 += QJL_ICHUNK) {
+            // stage S[:, i0:i0+16] transposed: s_lds[ii][j]
+            for (int e = tid; e < QJL_ICHUNK * m; e += 256) {
+                const int j = e / QJL_ICHUNK, ii = e % QJL_ICHUNK;
+                s_lds[ii * 256 + j] = a.S[(int64_t)j * D + i0 + ii];
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int ii = 0; ii < QJL_ICHUNK; ++ii) {
+                float rv[4];
+#pragma unroll
+                for (int vv = 0; vv < 4; ++vv) rv[vv] = r_lds[(tv + 8 * vv) * RS + i0 + ii];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    if (jj < nj) {
+                        const float sv = s_lds[ii * 256 + tj + 32 * jj];
+#pragma unroll
+                        for (int vv = 0; vv < 4; ++vv) acc[vv][jj] = fmaf(rv[vv], sv, acc[vv][jj]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        // sign bits: one ballot per (vector, 32 projections); lanes 0..31 and
+        // 32..63 of a wave hold two different vectors.
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+            const int vloc = tv + 8 * vv;
+            const int64_t row = tile0 + vloc;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                if (jj < nj) {
+                    const uint64_t mask = __ballot(acc[vv][jj] >= 0.0f);
+                    const uint32_t word = (lane < 32) ? (uint32_t)mask : (uint32_t)(mask >> 32);
+                    if ((lane & 31) == 0 && row < a.n)
+                        reinterpret_cast<uint32_t*>(a.qjl + row * (m >> 3))[jj] = word;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+    constexpr int LPV = D / 8;
+    constexpr int VPW = 64 / LPV;
+    __shared__ float cent[16];
+    if (threadIdx.x < 16) cent[threadIdx.x] = a.c.centroid[threadIdx.x];
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int gl = lane & (LPV - 1);
+    const uint32_t sbits = (a.c.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t base = wave * VPW; base < a.n; base += nwaves * VPW) {
+        const int64_t row = base + lane / LPV;
+        const bool valid = row < a.n;
+        const int64_t r = valid ? row : 0;
+        const uint8_t* rp = a.codes + r * a.code_stride + gl * BITS;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) packed |= (uint32_t)rp[k] << (8 * k);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = cent[(packed >> (BITS * e)) & ((1u << BITS) - 1u)];
+        fwht<LPV>(v, gl);
+        const float sc = half_bits_to_float(a.norms[r]) * (1.0f / (float)D);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = as_f(as_u(v[e] * sc) ^ (((sbits >> e) & 1u) << 31));
+        if (valid) {
+            float4* o = reinterpret_cast<float4*>(a.out + row * D + gl * 8);
+            o[0] = make_float4(v[0], v[1], v[2], v[3]);
+            o[1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
+    }
+}
+
+template <int D, int BITS, int DT>
+hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t s) {
+    if (a.c.qjl_m > 0) {
+        const int64_t tiles = (a.n + QJL_TILE - 1) / QJL_TILE;
+        const int grid = (int)(tiles < 8192 ? tiles : 8192);
+        hipLaunchKernelGGL((encode_qjl_kernel<D, BITS, DT>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+        constexpr int VPB = 4 * (64 / (D / 8));  // vectors per block per iteration
+        const int64_t need = (a.n + VPB - 1) / VPB;
+        const int grid = (int)(need < 16384 ? need : 16384);
+        hipLaunchKernelGGL((encode_kernel<D, BITS, DT>), dim3(grid), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <int D, int DT>
+hipError_t launch_encode_b(const EncodeArgs& a, hipStream_t s) {
+    switch (a.c.bits) {
+        case 1: return launch_encode_t<D, 1, DT>(a, s);
+        case 2: return launch_encode_t<D, 2, DT>(a, s);
+        case 3: return launch_encode_t<D, 3, DT>(a, s);
+        default: return launch_encode_t<D, 4, DT>(a, s);
+    }
+}
+
+template <int DT>
+hipError_t launch_encode_d(const EncodeArgs& a, hipStream_t s) {
+    switch (a.c.d) {
+        case 32: return launch_encode_b<32, DT>(a, s);
+        case 64: return launch_encode_b<64, DT>(a, s);
+        case 128: return launch_encode_b<128, DT>(a, s);
+        default: return launch_encode_b<256, DT>(a, s);
+    }
+}
+
+template <int D>
+hipError_t launch_decode_b(const DecodeArgs& a, hipStream_t s) {
+    constexpr int VPB = 4 * (64 / (D / 8));
+    const int64_t need = (a.n + VPB - 1) / VPB;
+    const int grid = (int)(need < 16384 ? need : 16384);
+    switch (a.c.bits) {
+        case 1: hipLaunchKernelGGL((decode_kernel<D, 1>), dim3(grid), dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), dim3(grid), dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<D, 3>), dim3(grid), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((decode_kernel<D, 4>), dim3(grid), dim3(256), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode(const EncodeArgs& a, int dtype, hipStream_t s) {
+    switch (dtype) {
+        case TQ_F32: return launch_encode_d<0>(a, s);
+        case TQ_F16: return launch_encode_d<1>(a, s);
+        default: return launch_encode_d<2>(a, s);
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+    switch (a.c.d) {
+        case 32: return launch_decode_b<32>(a, s);
+        case 64: return launch_decode_b<64>(a, s);
+        case 128: return launch_decode_b<128>(a, s);
+        default: return launch_decode_b<256>(a, s);
+    }
+}
+
+}  // namespace tqi

@@ -1,0 +1,102 @@
+// Internal declarations shared by the host API and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tqi {
+
+// Everything one encode/decode launch needs, passed by value as a kernel argument.
+struct CodecArgs {
+    uint32_t sign_mask[8];
+    float centroid[16];
+    float threshold[15];
+    int32_t d, bits, qjl_m;
+};
+
+struct EncodeArgs {
+    CodecArgs c;
+    const void* x;
+    int64_t n;
+    int64_t x_stride;  // elements
+    uint8_t* codes;
+    int64_t code_stride;  // bytes
+    uint16_t* norms;
+    const float* S;  // [m][d] or null
+    uint8_t* qjl;    // [n][m/8]
+    uint16_t* gamma;
+};
+
+struct DecodeArgs {
+    CodecArgs c;
+    const uint8_t* codes;
+    int64_t code_stride;
+    const uint16_t* norms;
+    int64_t n;
+    float* out;
+};
+
+// Decode-attention launch description (see tq_attn.hip).
+struct AttnArgs {
+    CodecArgs kc, vc;
+    const void* q;
+    int q_dtype;
+    int batch, hq, hkv, g;   // g = hq / hkv
+    int heads_per_chunk;     // G: query heads handled by one block
+    int chunks;              // g / G
+    const int32_t* ctx_len;
+    int64_t ctx_cap;
+    const uint8_t* k_codes;
+    const uint16_t* k_norms;
+    const uint8_t* k_qjl;
+    const uint16_t* k_gamma;
+    const float* S;
+    const uint8_t* v_codes;
+    const uint16_t* v_norms;
+    float scale;
+    float* out;
+    float* qrot;      // [batch][hq][d]  (scale*log2e/d) * H(D_K q)
+    float* qproj;     // [batch][hq][m]  scale*log2e*sqrt(pi/2)/m * S H(D_K q)/sqrt(d)
+    float* part;      // [batch][hq][splits][d + 2]
+    int splits;
+    int64_t split_tokens;  // tokens per split (multiple of 64)
+};
+
+// Host-side helpers.
+void fill_codec_args(const tq_codec* c, CodecArgs* a);
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_encode(const EncodeArgs& a, int dtype, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t* split_tokens,
+               int* heads_per_chunk);
+size_t attn_workspace(int batch, int hq, int d, int m, int splits);
+
+struct SearchArgs {
+    CodecArgs c;
+    const float* q;
+    int n_q;
+    const uint8_t* codes;
+    const uint16_t* norms;
+    const uint8_t* qjl;
+    const uint16_t* gamma;
+    const float* S;
+    int64_t n_db;
+    int k;
+    float* out_scores;
+    int64_t* out_ids;
+    float* qrot;   // [n_q][d]
+    float* qproj;  // [n_q][m]
+    float* cand_s;  // [n_q][n_blocks][k]
+    int32_t* cand_i;
+    int n_blocks;
+    int64_t block_rows;
+};
+hipError_t launch_search(const SearchArgs& a, hipStream_t s);
+void search_plan(int n_q, int64_t n_db, int k, int* n_blocks, int64_t* block_rows);
+size_t search_workspace(int n_q, int d, int m, int k, int n_blocks);
+
+}  // namespace tqi
