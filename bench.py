@@ -1,0 +1,405 @@
+#!/usr/bin/env python3
+"""Benchmark of the TurboQuant KV-cache hot path on one MI355X.
+
+Headline step (the `value`): one decode-attention call over a packed K4/V2
+cache -- batch 16, 28 query heads over 4 kv heads, d=128, 32768 tokens, fp16
+queries -- i.e. query prep + split-K scan + combine/inverse transform.  The
+timed steps rotate over 4 replicas of the 210 MB cache (a decode step reads a
+different layer's cache each time), so the 256 MB Infinity Cache cannot serve
+them.  `value` is algorithmic bytes per step (packed cache + queries + output)
+divided by the step time.
+
+Further legs in the same JSON line: tq_encode throughput (4 kv heads x 8192
+tokens, fp16, K 4-bit + V 2-bit per step, over a 1 GiB rotating input pool),
+long-context decode (8 kv heads x 2^20 tokens, K3/V3, 64 bf16 query heads) and
+inner-product search (2^20 x 256 database, 3-bit + QJL m=256, 1024 queries,
+top-10).  `roofline` is the scan kernel's algorithmic bytes per launch over its
+mean launch time measured with HIP events on the launch stream.
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same decode
+workload.  Inputs are synthetic and seeded (synth.py).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs decode,encode,long,search]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (counts packed FMA)
+
+METRIC = "packed-KV decode attn GB/s & % HBM peak (1 GPU); tq_encode Mvectors/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--legs", default="decode,encode,long,search")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration for --pmc runs)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def timed_loop(fn, steps, warmup, torch):
+    """Runs fn(i) for warmup + steps iterations; returns ms per timed step."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        fn(warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+# ------------------------------------------------------------------ decode ----
+def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
+    B, Hkv, g, ctx, d, kb, vb = 16, 4, 7, 32768, 128, 4, 2
+    Hq = Hkv * g
+    kc, vc = tq.tq_codebook(kb, d, 42), tq.tq_codebook(vb, d, 42)
+    K, V = synth.decode_cache_inputs(B, Hkv, ctx, d, device="cuda")
+    caches = []
+    for _ in range(replicas):
+        c = {
+            "k_codes": torch.empty(B, Hkv, ctx, kc.code_bytes, dtype=torch.uint8, device="cuda"),
+            "k_norms": torch.empty(B, Hkv, ctx, dtype=torch.float16, device="cuda"),
+            "v_codes": torch.empty(B, Hkv, ctx, vc.code_bytes, dtype=torch.uint8, device="cuda"),
+            "v_norms": torch.empty(B, Hkv, ctx, dtype=torch.float16, device="cuda"),
+        }
+        tq.tq_encode(kc, K.view(-1, d), c["k_codes"].view(-1, kc.code_bytes), c["k_norms"].view(-1))
+        tq.tq_encode(vc, V.view(-1, d), c["v_codes"].view(-1, vc.code_bytes), c["v_norms"].view(-1))
+        caches.append(c)
+    del K, V
+    q = synth.decode_queries(B, Hq, d, device="cuda")
+    ctx_len = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, Hq, d, device="cuda")
+    ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, B, Hq, Hkv, ctx))
+    scale = 1.0 / math.sqrt(d)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps + warmup)]
+
+    def step(i):
+        c = caches[i % replicas]
+        args = (kc, vc, q, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], scale, out, ws)
+        tq.tq_attn_prepare(*args)
+        ev[i][0].record()
+        tq.tq_attn_scan(*args)
+        ev[i][1].record()
+        tq.tq_attn_combine(*args)
+
+    ms = timed_loop(step, steps, warmup, torch)
+    scan_ms = sum(ev[warmup + i][0].elapsed_time(ev[warmup + i][1]) for i in range(steps)) / steps
+    token_heads = B * Hkv * ctx
+    per_token_head = (kc.code_bytes + 2) + (vc.code_bytes + 2)  # 100 B
+    cache_bytes = token_heads * per_token_head
+    step_bytes = cache_bytes + q.numel() * 2 + out.numel() * 4
+    return {
+        "ms_per_step": ms,
+        "gbs": step_bytes / (ms * 1e-3) / 1e9,
+        "scan_ms": scan_ms,
+        "scan_gbs": cache_bytes / (scan_ms * 1e-3) / 1e9,
+        "cache_bytes": cache_bytes,
+        "step_bytes": step_bytes,
+        "bytes_per_token_head": per_token_head,
+        "token_heads": token_heads,
+        "replicas": replicas,
+        "fma_per_token_head": 2 * g * d,
+    }, (kc, vc, caches[0], q)
+
+
+# ------------------------------------------------------------------ encode ----
+def encode_leg(tq, torch, synth, steps, warmup):
+    H, T, d = 4, 8192, 128
+    kc, vc = tq.tq_codebook(4, d, 11), tq.tq_codebook(2, d, 11)
+    n = H * T
+    layers = 64  # 64 x 16 MiB = 1 GiB of fp16 input
+    pool_k = torch.empty(layers, n, d, dtype=torch.float16, device="cuda")
+    pool_v = torch.empty(layers, n, d, dtype=torch.float16, device="cuda")
+    for li in range(layers):
+        k, v = synth.kv_block(H, T, d, synth.SEED_ENCODE + li, device="cuda", dtype=torch.float16)
+        pool_k[li] = k.view(n, d)
+        pool_v[li] = v.view(n, d)
+    out_k = torch.empty(layers, n, kc.code_bytes, dtype=torch.uint8, device="cuda")
+    out_v = torch.empty(layers, n, vc.code_bytes, dtype=torch.uint8, device="cuda")
+    nk = torch.empty(layers, n, dtype=torch.float16, device="cuda")
+    nv = torch.empty(layers, n, dtype=torch.float16, device="cuda")
+
+    def step(i):
+        li = i % layers
+        tq.tq_encode(kc, pool_k[li], out_k[li], nk[li])
+        tq.tq_encode(vc, pool_v[li], out_v[li], nv[li])
+
+    ms = timed_loop(step, max(steps, 512), warmup, torch)
+    # single-call latency (one K+V layer), median of 20
+    lat = []
+    for i in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step(i)
+        b.record()
+        torch.cuda.synchronize()
+        lat.append(a.elapsed_time(b))
+    lat.sort()
+    vecs = 2 * n
+    bytes_step = vecs * d * 2 + n * (kc.code_bytes + 2) + n * (vc.code_bytes + 2)
+    return {
+        "workload": "4 kv heads x 8192 tokens x d=128 fp16, K 4-bit + V 2-bit per step, 1 GiB rotating input pool",
+        "mvectors_per_s": vecs / (ms * 1e-3) / 1e6,
+        "ms_per_step": ms,
+        "gbs": bytes_step / (ms * 1e-3) / 1e9,
+        "bytes_per_step": bytes_step,
+        "latency_ms_median": lat[len(lat) // 2],
+        "steps": max(steps, 512),
+    }
+
+
+# -------------------------------------------------------------------- long ----
+def long_leg(tq, torch, synth, steps, warmup):
+    Hkv, g, d, chunk, n_chunks = 8, 8, 128, 4096, 256
+    cap = chunk * n_chunks
+    kc, vc = tq.tq_codebook(3, d, 77), tq.tq_codebook(3, d, 77)
+    c = {
+        "k_codes": torch.empty(1, Hkv, cap, kc.code_bytes, dtype=torch.uint8, device="cuda"),
+        "k_norms": torch.empty(1, Hkv, cap, dtype=torch.float16, device="cuda"),
+        "v_codes": torch.empty(1, Hkv, cap, vc.code_bytes, dtype=torch.uint8, device="cuda"),
+        "v_norms": torch.empty(1, Hkv, cap, dtype=torch.float16, device="cuda"),
+    }
+    enc_ms = 0.0
+    for ci in range(n_chunks):
+        k, v = synth.long_chunk(ci, kv_heads=Hkv, tokens=chunk, d=d, device="cuda")
+        sl = slice(ci * chunk, (ci + 1) * chunk)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for h in range(Hkv):
+            tq.tq_encode(kc, k[h], c["k_codes"][0, h, sl], c["k_norms"][0, h, sl])
+            tq.tq_encode(vc, v[h], c["v_codes"][0, h, sl], c["v_norms"][0, h, sl])
+        b.record()
+        torch.cuda.synchronize()
+        enc_ms += a.elapsed_time(b)
+    q = synth.long_queries(Hkv * g, d, device="cuda")[None].contiguous()
+    ctx_len = torch.full((1,), cap, dtype=torch.int32, device="cuda")
+    out = torch.empty(1, Hkv * g, d, device="cuda")
+    ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, 1, Hkv * g, Hkv, cap))
+    scale = 1.0 / math.sqrt(d)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps + warmup)]
+
+    def step(i):
+        args = (kc, vc, q, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], scale, out, ws)
+        tq.tq_attn_prepare(*args)
+        ev[i][0].record()
+        tq.tq_attn_scan(*args)
+        ev[i][1].record()
+        tq.tq_attn_combine(*args)
+
+    ms = timed_loop(step, steps, warmup, torch)
+    scan_ms = sum(ev[warmup + i][0].elapsed_time(ev[warmup + i][1]) for i in range(steps)) / steps
+    cache_bytes = Hkv * cap * ((kc.code_bytes + 2) + (vc.code_bytes + 2))
+    return {
+        "workload": "1 sequence, 8 kv heads x 2^20 tokens, d=128, K3/V3, 64 bf16 query heads (8:1)",
+        "ms_per_step": ms,
+        "gbs": cache_bytes / (ms * 1e-3) / 1e9,
+        "scan_ms": scan_ms,
+        "scan_gbs": cache_bytes / (scan_ms * 1e-3) / 1e9,
+        "pct_hbm_peak": 100.0 * cache_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "cache_bytes": cache_bytes,
+        "prefill_encode_ms": enc_ms,
+        "prefill_encode_mvectors_per_s": 2 * Hkv * cap / (enc_ms * 1e-3) / 1e6,
+    }
+
+
+# ------------------------------------------------------------------ search ----
+def search_leg(tq, torch, synth, steps, warmup):
+    n_db, n_q, d, m, k = 1 << 20, 1024, 256, 256, 10
+    db, q, S = synth.search_inputs(n_db, n_q, d, m, device="cuda")
+    codec = tq.tq_codebook(3, d, 99, m)
+    codes = torch.empty(n_db, codec.code_bytes, dtype=torch.uint8, device="cuda")
+    norms = torch.empty(n_db, dtype=torch.float16, device="cuda")
+    bits = torch.empty(n_db, m // 8, dtype=torch.uint8, device="cuda")
+    gamma = torch.empty(n_db, dtype=torch.float16, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    tq.tq_encode(codec, db, codes, norms, S, bits, gamma)
+    b.record()
+    torch.cuda.synchronize()
+    enc_ms = a.elapsed_time(b)
+    del db
+    ws = tq.workspace(tq.tq_search_workspace_bytes(codec, n_q, n_db, k))
+    scores = torch.empty(n_q, k, device="cuda")
+    ids = torch.empty(n_q, k, dtype=torch.int64, device="cuda")
+
+    def step(i):
+        tq.tq_ip_search(codec, q, codes, norms, bits, gamma, S, k, scores, ids, ws)
+
+    st = max(2, min(steps, 5))
+    ms = timed_loop(step, st, min(warmup, 2), torch)
+    flops = 2.0 * n_q * n_db * (d + m)
+    db_bytes = n_db * (codec.code_bytes + 2 + m // 8 + 2)
+    return {
+        "workload": "2^20 x 256 unit vectors, 3-bit + QJL m=256, 1024 unit queries, exact top-10",
+        "ms_per_call": ms,
+        "queries_per_s": n_q / (ms * 1e-3),
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "pct_fp32_valu_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+        "db_bytes": db_bytes,
+        "db_encode_ms": enc_ms,
+        "db_encode_mvectors_per_s": n_db / (enc_ms * 1e-3) / 1e6,
+        "steps": st,
+    }
+
+
+# -------------------------------------------------------------- CPU oracle ----
+def cpu_baseline(torch, synth, target_s):
+    """The oracle, untouched, on a bounded sample of the decode workload: the
+    K4/V2 caches of sample (batch, kv head) units are encoded by the oracle
+    (timed as the encode baseline), then the oracle's decompress-then-attend
+    runs for the 7 query heads of each unit, repeated until target_s elapsed."""
+    import numpy as np
+    from oracle import tq_oracle as o
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    d, ctx, g = 128, 32768, 7
+    kc, vc = o.Codec(4, d, 42), o.Codec(2, d, 42)
+    units = [(0, 0), (5, 1), (10, 2), (15, 3)]
+    t0 = time.perf_counter()
+    caches = []
+    for b, kh in units:
+        k, v = synth.kv_block(4, ctx, d, synth.SEED_DECODE_BASE + b, dtype=torch.float16)
+        ek = o.encode(k[kh].float().numpy().astype(np.float64), kc)
+        ev = o.encode(v[kh].float().numpy().astype(np.float64), vc)
+        caches.append((ek, ev))
+    enc_s = time.perf_counter() - t0
+    q = synth.decode_queries(16, 28, d).float().numpy().astype(np.float64)
+    done, t1 = 0, time.perf_counter()
+    while True:
+        for (b, kh), (ek, ev) in zip(units, caches):
+            o.attention(q[b, kh * g:(kh + 1) * g], ek["codes"], ek["norms"], ev["codes"], ev["norms"], kc, vc,
+                        1 / math.sqrt(d))
+            done += 1
+        if time.perf_counter() - t1 >= target_s:
+            break
+    att_s = time.perf_counter() - t1
+    bytes_done = done * ctx * 100
+    return {
+        "value": bytes_done / att_s / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(units)} (batch, kv head) units of the decode workload (32768 tokens, 7 query heads each), "
+                   f"oracle-encoded, then decompress-then-attend repeated {done // len(units)}x in {att_s:.1f} s"),
+        "encode_mvectors_per_s": 2 * len(units) * ctx / enc_s / 1e6,
+        "encode_sample": f"{2 * len(units) * ctx} vectors (K 4-bit + V 2-bit) in {enc_s:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1",
+                          "requested_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    import synth
+    import kv_cache_vector_02_amd as tq
+
+    legs = set(args.legs.split(","))
+    torch.cuda.init()
+    res = {}
+    if args.calib_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x 256 MiB read + 256 MiB written")
+    if "decode" in legs:
+        log("decode leg: batch 16, 28/4 heads, 32768 tokens, K4/V2")
+        res["decode"], _ = decode_leg(tq, torch, synth, args.steps, args.warmup)
+        log(f"decode: {res['decode']['ms_per_step']:.3f} ms/step, {res['decode']['gbs']:.0f} GB/s")
+    if "encode" in legs:
+        log("encode leg")
+        res["encode"] = encode_leg(tq, torch, synth, args.steps, args.warmup)
+        log(f"encode: {res['encode']['mvectors_per_s']:.0f} Mvectors/s")
+    if "long" in legs:
+        log("long-context leg (2^20 tokens)")
+        res["long"] = long_leg(tq, torch, synth, max(5, args.steps // 5), max(2, args.warmup // 5))
+        log(f"long: {res['long']['ms_per_step']:.3f} ms/step, {res['long']['gbs']:.0f} GB/s")
+    if "search" in legs:
+        log("search leg (2^20 x 256, 1024 queries)")
+        res["search"] = search_leg(tq, torch, synth, args.steps, args.warmup)
+        log(f"search: {res['search']['ms_per_call']:.2f} ms/call, {res['search']['tflops']:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(torch, synth, args.cpu_seconds)
+        log(f"cpu: {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+
+    dec = res.get("decode")
+    line = {
+        "metric": METRIC,
+        "value": dec["gbs"] if dec else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"] if dec else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode attention over a packed K4/V2 cache: batch 16, 28 query heads / 4 kv heads (7:1), "
+                        "d=128, context 32768, fp16 queries, scale 1/sqrt(128)",
+            "batch": 16, "q_heads": 28, "kv_heads": 4, "ctx": 32768, "d": 128, "k_bits": 4, "v_bits": 2,
+        },
+    }
+    if dec:
+        line["pct_hbm_peak"] = 100.0 * dec["gbs"] / HBM_PEAK_GBS
+        line["roofline"] = {
+            "bound": "hbm",
+            "kernel": "split-K scan (tq_attn_scan)",
+            "achieved": dec["scan_gbs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": dec["scan_gbs"] / HBM_PEAK_GBS,
+            "traffic": None,
+            "scan_ms": dec["scan_ms"],
+            "algorithmic_bytes_per_launch": dec["cache_bytes"],
+        }
+        line["decode"] = dec
+    if cpu:
+        line["cpu_baseline"] = cpu
+    for k in ("encode", "long", "search"):
+        if k in res:
+            line[k] = res[k]
+    if "encode" in res:
+        line["tq_encode_mvectors_per_s"] = res["encode"]["mvectors_per_s"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -173,6 +173,44 @@ int tq_attn_decode(const tq_codec *kc, const tq_codec *vc,
                    float scale, float *out, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/*
+ * The three launches of tq_attn_decode as separate calls (same arguments, same
+ * checks, same workspace, which carries the state between them), for callers
+ * that time or schedule the stages themselves:
+ *   tq_attn_prepare  rotate the queries once (q_rot, and S q_rot/sqrt(d) with
+ *                    QJL) into the workspace -- the Q-side WHT of [P1] v1.7.0
+ *                    item 4 and the fused Q_wht1/Q_wht2 pass of [P1] v1.4.2 item 5;
+ *   tq_attn_scan     stream the packed cache: scores, online softmax and rotated
+ *                    V sums per context split, into the workspace;
+ *   tq_attn_combine  merge the splits and apply one inverse transform per head
+ *                    into `out` ([P1] v1.5.1 item 2).
+ * tq_attn_decode == prepare, scan, combine on one stream.
+ */
+int tq_attn_prepare(const tq_codec *kc, const tq_codec *vc,
+                    const void *q, int q_dtype, int batch, int n_q_heads, int n_kv_heads,
+                    const int32_t *ctx_len, int64_t ctx_cap,
+                    const uint8_t *k_codes, const uint16_t *k_norms,
+                    const uint8_t *k_qjl, const uint16_t *k_gamma, const float *qjl_S,
+                    const uint8_t *v_codes, const uint16_t *v_norms,
+                    float scale, float *out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+int tq_attn_scan(const tq_codec *kc, const tq_codec *vc,
+                 const void *q, int q_dtype, int batch, int n_q_heads, int n_kv_heads,
+                 const int32_t *ctx_len, int64_t ctx_cap,
+                 const uint8_t *k_codes, const uint16_t *k_norms,
+                 const uint8_t *k_qjl, const uint16_t *k_gamma, const float *qjl_S,
+                 const uint8_t *v_codes, const uint16_t *v_norms,
+                 float scale, float *out, void *workspace, size_t workspace_bytes,
+                 void *stream);
+int tq_attn_combine(const tq_codec *kc, const tq_codec *vc,
+                    const void *q, int q_dtype, int batch, int n_q_heads, int n_kv_heads,
+                    const int32_t *ctx_len, int64_t ctx_cap,
+                    const uint8_t *k_codes, const uint16_t *k_norms,
+                    const uint8_t *k_qjl, const uint16_t *k_gamma, const float *qjl_S,
+                    const uint8_t *v_codes, const uint16_t *v_norms,
+                    float scale, float *out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
 /* Bytes of workspace tq_attn_decode needs for these sizes (0 on bad arguments). */
 size_t tq_attn_workspace_bytes(const tq_codec *kc, const tq_codec *vc, int batch,
                                int n_q_heads, int n_kv_heads, int64_t ctx_cap);

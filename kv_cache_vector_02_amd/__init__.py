@@ -22,7 +22,8 @@ TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 _DTYPES = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16}
 
 EXPORTS = (
-    "tq_codebook", "tq_encode", "tq_decode", "tq_attn_decode", "tq_attn_workspace_bytes",
+    "tq_codebook", "tq_encode", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
+    "tq_attn_combine", "tq_attn_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror",
 )
 
@@ -75,6 +76,9 @@ def _load():
         "tq_encode": (I, [CP, P, I, I64, I64, P, I64, P, P, P, P, P]),
         "tq_decode": (I, [CP, P, I64, P, I64, P, P]),
         "tq_attn_decode": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
+        "tq_attn_prepare": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
+        "tq_attn_scan": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
+        "tq_attn_combine": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
         "tq_attn_workspace_bytes": (SZ, [CP, CP, I, I, I, I64]),
         "tq_ip_search": (I, [CP, P, I, P, P, P, P, P, I64, I, P, P, P, SZ, P]),
         "tq_search_workspace_bytes": (SZ, [CP, I, I64, I]),
@@ -152,22 +156,49 @@ def tq_attn_workspace_bytes(kc: tq_codec, vc: tq_codec, batch: int, n_q_heads: i
     return _lib.tq_attn_workspace_bytes(ctypes.byref(kc), ctypes.byref(vc), batch, n_q_heads, n_kv_heads, ctx_cap)
 
 
+def _attn(name, kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, scale, out, workspace,
+          k_qjl, k_gamma, qjl_S, stream):
+    B, Hq, _ = q.shape
+    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
+    for t in (q, k_codes, k_norms, v_codes, v_norms, out, ctx_len):
+        if not t.is_contiguous():
+            raise ValueError("attention tensors must be contiguous")
+    fn = getattr(_lib, name)
+    _check(fn(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _DTYPES[q.dtype], B, Hq, Hkv,
+              _ptr(ctx_len), cap, _ptr(k_codes), _ptr(k_norms), _ptr(k_qjl), _ptr(k_gamma),
+              _ptr(qjl_S), _ptr(v_codes), _ptr(v_norms), ctypes.c_float(scale), _ptr(out),
+              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)), name)
+
+
 def tq_attn_decode(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.Tensor,
                    k_codes: torch.Tensor, k_norms: torch.Tensor, v_codes: torch.Tensor, v_norms: torch.Tensor,
                    scale: float, out: torch.Tensor, workspace: torch.Tensor,
                    k_qjl: torch.Tensor | None = None, k_gamma: torch.Tensor | None = None,
                    qjl_S: torch.Tensor | None = None, stream=None) -> None:
     """q [B][Hq][d]; caches [B][Hkv][ctx_cap][...] contiguous; out [B][Hq][d] fp32."""
-    B, Hq, _ = q.shape
-    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
-    for t in (q, k_codes, k_norms, v_codes, v_norms, out, ctx_len):
-        if not t.is_contiguous():
-            raise ValueError("attention tensors must be contiguous")
-    _check(_lib.tq_attn_decode(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _DTYPES[q.dtype], B, Hq, Hkv,
-                               _ptr(ctx_len), cap, _ptr(k_codes), _ptr(k_norms), _ptr(k_qjl), _ptr(k_gamma),
-                               _ptr(qjl_S), _ptr(v_codes), _ptr(v_norms), ctypes.c_float(scale), _ptr(out),
-                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
-           "tq_attn_decode")
+    _attn("tq_attn_decode", kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, scale, out, workspace,
+          k_qjl, k_gamma, qjl_S, stream)
+
+
+def tq_attn_prepare(*args, **kw) -> None:
+    """Stage 1 of tq_attn_decode (same arguments)."""
+    _attn_stage("tq_attn_prepare", *args, **kw)
+
+
+def tq_attn_scan(*args, **kw) -> None:
+    """Stage 2 of tq_attn_decode (same arguments)."""
+    _attn_stage("tq_attn_scan", *args, **kw)
+
+
+def tq_attn_combine(*args, **kw) -> None:
+    """Stage 3 of tq_attn_decode (same arguments)."""
+    _attn_stage("tq_attn_combine", *args, **kw)
+
+
+def _attn_stage(name, kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, scale, out, workspace,
+                k_qjl=None, k_gamma=None, qjl_S=None, stream=None):
+    _attn(name, kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, scale, out, workspace,
+          k_qjl, k_gamma, qjl_S, stream)
 
 
 def tq_search_workspace_bytes(codec: tq_codec, n_q: int, n_db: int, k: int) -> int:

@@ -209,11 +209,13 @@ size_t tq_attn_workspace_bytes(const tq_codec* kc, const tq_codec* vc, int batch
     return tqi::attn_workspace(batch, n_q_heads, kc->d, kc->qjl_m, splits);
 }
 
-int tq_attn_decode(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch, int n_q_heads,
-                   int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap, const uint8_t* k_codes,
-                   const uint16_t* k_norms, const uint8_t* k_qjl, const uint16_t* k_gamma, const float* qjl_S,
-                   const uint8_t* v_codes, const uint16_t* v_norms, float scale, float* out, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+// Validates every argument of the decode-attention entry points and fills the
+// launch description; nothing is launched here.
+static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch,
+                      int n_q_heads, int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap,
+                      const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl, const uint16_t* k_gamma,
+                      const float* qjl_S, const uint8_t* v_codes, const uint16_t* v_norms, float scale, float* out,
+                      void* workspace, size_t workspace_bytes, tqi::AttnArgs* a) {
     int splits, G;
     int64_t per;
     const int rc = attn_check(kc, vc, batch, n_q_heads, n_kv_heads, ctx_cap, &splits, &per, &G);
@@ -230,38 +232,56 @@ int tq_attn_decode(const tq_codec* kc, const tq_codec* vc, const void* q, int q_
     const size_t need = tqi::attn_workspace(batch, n_q_heads, d, m, splits);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return TQ_EWORKSPACE;
 
-    tqi::AttnArgs a;
-    tqi::fill_codec_args(kc, &a.kc);
-    tqi::fill_codec_args(vc, &a.vc);
-    a.q = q;
-    a.q_dtype = q_dtype;
-    a.batch = batch;
-    a.hq = n_q_heads;
-    a.hkv = n_kv_heads;
-    a.g = n_q_heads / n_kv_heads;
-    a.heads_per_chunk = G;
-    a.chunks = a.g / G;
-    a.ctx_len = ctx_len;
-    a.ctx_cap = ctx_cap;
-    a.k_codes = k_codes;
-    a.k_norms = k_norms;
-    a.k_qjl = k_qjl;
-    a.k_gamma = k_gamma;
-    a.S = qjl_S;
-    a.v_codes = v_codes;
-    a.v_norms = v_norms;
-    a.scale = scale;
-    a.out = out;
+    tqi::fill_codec_args(kc, &a->kc);
+    tqi::fill_codec_args(vc, &a->vc);
+    a->q = q;
+    a->q_dtype = q_dtype;
+    a->batch = batch;
+    a->hq = n_q_heads;
+    a->hkv = n_kv_heads;
+    a->g = n_q_heads / n_kv_heads;
+    a->heads_per_chunk = G;
+    a->chunks = a->g / G;
+    a->ctx_len = ctx_len;
+    a->ctx_cap = ctx_cap;
+    a->k_codes = k_codes;
+    a->k_norms = k_norms;
+    a->k_qjl = k_qjl;
+    a->k_gamma = k_gamma;
+    a->S = qjl_S;
+    a->v_codes = v_codes;
+    a->v_norms = v_norms;
+    a->scale = scale;
+    a->out = out;
     const size_t heads = (size_t)batch * n_q_heads;
     float* ws = (float*)workspace;
     auto al = [](size_t n) { return (n + 63) & ~(size_t)63; };
-    a.qrot = ws;
-    a.qproj = ws + al(heads * d);
-    a.part = a.qproj + al(heads * (size_t)m);
-    a.splits = splits;
-    a.split_tokens = per;
-    return finish(tqi::launch_attn(a, (hipStream_t)stream));
+    a->qrot = ws;
+    a->qproj = ws + al(heads * d);
+    a->part = a->qproj + al(heads * (size_t)m);
+    a->splits = splits;
+    a->split_tokens = per;
+    return TQ_OK;
 }
+
+#define TQ_ATTN_ENTRY(NAME, STAGE)                                                                            \
+    int NAME(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch, int n_q_heads,     \
+             int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap, const uint8_t* k_codes,                 \
+             const uint16_t* k_norms, const uint8_t* k_qjl, const uint16_t* k_gamma, const float* qjl_S,       \
+             const uint8_t* v_codes, const uint16_t* v_norms, float scale, float* out, void* workspace,        \
+             size_t workspace_bytes, void* stream) {                                                          \
+        tqi::AttnArgs a;                                                                                      \
+        const int rc = attn_setup(kc, vc, q, q_dtype, batch, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes, \
+                                  k_norms, k_qjl, k_gamma, qjl_S, v_codes, v_norms, scale, out, workspace,     \
+                                  workspace_bytes, &a);                                                       \
+        if (rc != TQ_OK) return rc;                                                                           \
+        return finish(tqi::launch_attn(a, STAGE, (hipStream_t)stream));                                      \
+    }
+
+TQ_ATTN_ENTRY(tq_attn_decode, tqi::ATTN_ALL)
+TQ_ATTN_ENTRY(tq_attn_prepare, tqi::ATTN_PREPARE)
+TQ_ATTN_ENTRY(tq_attn_scan, tqi::ATTN_SCAN)
+TQ_ATTN_ENTRY(tq_attn_combine, tqi::ATTN_COMBINE)
 
 static int search_check(const tq_codec* c, int n_q, int64_t n_db, int k) {
     if (!c) return TQ_EINVAL;

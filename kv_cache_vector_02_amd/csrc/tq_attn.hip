@@ -77,13 +77,19 @@ static hipError_t launch_split_any(const AttnArgs& a, hipStream_t s) {
     }
 }
 
-hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s) {
     const bool d128 = a.kc.d == 128;
-    hipError_t e = d128 ? launch_qprep_combine<128>(a, s, true) : launch_qprep_combine<256>(a, s, true);
-    if (e != hipSuccess) return e;
-    e = launch_split_any(a, s);
-    if (e != hipSuccess) return e;
-    return d128 ? launch_qprep_combine<128>(a, s, false) : launch_qprep_combine<256>(a, s, false);
+    hipError_t e = hipSuccess;
+    if (stages & ATTN_PREPARE) {
+        e = d128 ? launch_qprep_combine<128>(a, s, true) : launch_qprep_combine<256>(a, s, true);
+        if (e != hipSuccess) return e;
+    }
+    if (stages & ATTN_SCAN) {
+        e = launch_split_any(a, s);
+        if (e != hipSuccess) return e;
+    }
+    if (stages & ATTN_COMBINE) e = d128 ? launch_qprep_combine<128>(a, s, false) : launch_qprep_combine<256>(a, s, false);
+    return e;
 }
 
 }  // namespace tqi

@@ -70,7 +70,8 @@ void fill_codec_args(const tq_codec* c, CodecArgs* a);
 // Launchers (return hipError_t of the launch).
 hipError_t launch_encode(const EncodeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+enum AttnStage { ATTN_PREPARE = 1, ATTN_SCAN = 2, ATTN_COMBINE = 4, ATTN_ALL = 7 };
+hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s);
 void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t* split_tokens,
                int* heads_per_chunk);
 size_t attn_workspace(int batch, int hq, int d, int m, int splits);
