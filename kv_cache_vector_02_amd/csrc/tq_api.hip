@@ -195,6 +195,9 @@ static int attn_check(const tq_codec* kc, const tq_codec* vc, int batch, int n_q
     if (kc->d != vc->d || (kc->d != 128 && kc->d != 256) || vc->qjl_m != 0) return TQ_EUNSUPPORTED;
     if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || ctx_cap <= 0 || batch > 65535) return TQ_EINVAL;
     if (n_q_heads % n_kv_heads != 0) return TQ_EUNSUPPORTED;
+    // one (batch, kv head) plane of any cache array must be addressable with 31-bit offsets
+    const int64_t row_max = kc->d * (kc->bits > vc->bits ? kc->bits : vc->bits) / 8 + kc->qjl_m / 8;
+    if (ctx_cap > (((int64_t)1 << 31) - 1) / (row_max > 2 ? row_max : 2)) return TQ_EUNSUPPORTED;
     const int g = n_q_heads / n_kv_heads;
     tqi::attn_plan(batch, n_kv_heads, g, ctx_cap, splits, split_tokens, G);
     if ((int64_t)n_kv_heads * (g / *G) > 65535) return TQ_EUNSUPPORTED;
