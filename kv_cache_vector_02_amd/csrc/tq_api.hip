@@ -199,7 +199,7 @@ static int attn_check(const tq_codec* kc, const tq_codec* vc, int batch, int n_q
     const int64_t row_max = kc->d * (kc->bits > vc->bits ? kc->bits : vc->bits) / 8 + kc->qjl_m / 8;
     if (ctx_cap > (((int64_t)1 << 31) - 1) / (row_max > 2 ? row_max : 2)) return TQ_EUNSUPPORTED;
     const int g = n_q_heads / n_kv_heads;
-    tqi::attn_plan(batch, n_kv_heads, g, ctx_cap, splits, split_tokens, G);
+    tqi::attn_plan(batch, n_kv_heads, g, ctx_cap, kc->d, kc->bits, vc->bits, kc->qjl_m > 0, splits, split_tokens, G);
     if ((int64_t)n_kv_heads * (g / *G) > 65535) return TQ_EUNSUPPORTED;
     return TQ_OK;
 }

@@ -2,17 +2,62 @@
 // three launches (query prep, split-K scan, combine + inverse transform).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "tq_attn_kernels.h"
 #include "tq_internal.h"
 
 namespace tqi {
 
+// Resident split blocks per compute unit for this variant (cached).
+static int split_blocks_any(int d, int kb, int vb, int G, bool qjl) {
+    static std::atomic<int> cache[2][4][4][8][2];
+    std::atomic<int>& c = cache[d == 128 ? 0 : 1][kb - 1][vb - 1][G - 1][qjl ? 1 : 0];
+    int nb = c.load(std::memory_order_relaxed);
+    if (nb > 0) return nb;
+    if (d == 128) {
+        switch (kb) {
+            case 1: nb = split_blocks_dk<128, 1>(vb, G, qjl); break;
+            case 2: nb = split_blocks_dk<128, 2>(vb, G, qjl); break;
+            case 3: nb = split_blocks_dk<128, 3>(vb, G, qjl); break;
+            default: nb = split_blocks_dk<128, 4>(vb, G, qjl); break;
+        }
+    } else {
+        switch (kb) {
+            case 1: nb = split_blocks_dk<256, 1>(vb, G, qjl); break;
+            case 2: nb = split_blocks_dk<256, 2>(vb, G, qjl); break;
+            case 3: nb = split_blocks_dk<256, 3>(vb, G, qjl); break;
+            default: nb = split_blocks_dk<256, 4>(vb, G, qjl); break;
+        }
+    }
+    if (nb <= 0) return 1;  // occupancy unknown (no device): not cached
+    c.store(nb, std::memory_order_relaxed);
+    return nb;
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    std::atomic<int>* c = dev < 64 ? &cache[dev] : nullptr;
+    int n = c ? c->load(std::memory_order_relaxed) : 0;
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 1;
+    if (c) c->store(n, std::memory_order_relaxed);
+    return n;
+}
+
 // Query heads of one kv group are processed in chunks of G <= 8 heads (the
-// largest divisor of g not above 8); splits cut the context so that roughly
-// 1024 blocks of 256 threads cover the GPU, each split a multiple of 64 tokens
-// and at least 256 tokens (one tile per wave).
-void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t* split_tokens,
-               int* heads_per_chunk) {
+// largest divisor of g not above 8).  The context is cut into splits of a
+// multiple of 64 tokens.  With S resident block slots on the device (compute
+// units x blocks per unit for this variant), a grid of B blocks runs in
+// ceil(B / S) rounds and a block costs about (tiles per wave + 2) tile times
+// (the 2 covers its table setup and merge); the split count minimising
+// rounds x block cost is taken, among the largest split counts that fit 1..8
+// rounds.  The plan depends on the current device.
+void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int d, int kb, int vb, bool qjl, int* splits,
+               int64_t* split_tokens, int* heads_per_chunk) {
     int G = 1;
     for (int c = 8; c >= 1; --c) {
         if (g % c == 0) {
@@ -20,18 +65,31 @@ void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t*
             break;
         }
     }
-    const int64_t units = (int64_t)batch * hkv * (g / G);
-    const int64_t target = 1024;
-    const int64_t max_splits = ctx_cap > 0 ? (ctx_cap + 255) / 256 : 1;
-    int64_t sp = (target + units - 1) / units;
-    if (sp > max_splits) sp = max_splits;
-    if (sp < 1) sp = 1;
-    int64_t per = ctx_cap > 0 ? (ctx_cap + sp - 1) / sp : 64;
-    per = (per + 63) & ~(int64_t)63;
-    sp = ctx_cap > 0 ? (ctx_cap + per - 1) / per : 1;
-    *splits = (int)sp;
-    *split_tokens = per;
     *heads_per_chunk = G;
+    const int64_t units = (int64_t)batch * hkv * (g / G);
+    const int64_t slots = (int64_t)device_cus() * split_blocks_any(d, kb, vb, G, qjl);
+    const int64_t max_splits = ctx_cap > 0 ? (ctx_cap + 63) / 64 : 1;
+    int64_t best_sp = 1, best_per = ((ctx_cap > 0 ? ctx_cap : 1) + 63) & ~(int64_t)63;
+    double best_cost = -1.0;
+    for (int r = 1; r <= 8; ++r) {
+        int64_t sp = r * slots / units;
+        if (sp < 1) sp = 1;
+        if (sp > max_splits) sp = max_splits;
+        int64_t per = ctx_cap > 0 ? (ctx_cap + sp - 1) / sp : 64;
+        per = (per + 63) & ~(int64_t)63;
+        sp = ctx_cap > 0 ? (ctx_cap + per - 1) / per : 1;
+        const int64_t rounds = (units * sp + slots - 1) / slots;
+        const int64_t nw = attn::split_waves(d);
+        const int64_t wave_tiles = (per / 64 + nw - 1) / nw;
+        const double cost = (double)rounds * (double)(wave_tiles + 2);
+        if (best_cost < 0.0 || cost < best_cost || (cost == best_cost && sp < best_sp)) {
+            best_cost = cost;
+            best_sp = sp;
+            best_per = per;
+        }
+    }
+    *splits = (int)best_sp;
+    *split_tokens = best_per;
 }
 
 static size_t align_floats(size_t n) { return (n + 63) & ~(size_t)63; }

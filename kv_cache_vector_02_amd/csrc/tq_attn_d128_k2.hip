@@ -8,4 +8,8 @@ template <>
 hipError_t launch_split_dk<128, 2>(const AttnArgs& a, hipStream_t s) {
     return attn::launch_split_dk<128, 2>(a, s);
 }
+template <>
+int split_blocks_dk<128, 2>(int vb, int G, bool qjl) {
+    return attn::split_blocks_dk<128, 2>(vb, G, qjl);
+}
 }  // namespace tqi

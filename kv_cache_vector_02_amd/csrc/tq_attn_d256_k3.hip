@@ -8,4 +8,8 @@ template <>
 hipError_t launch_split_dk<256, 3>(const AttnArgs& a, hipStream_t s) {
     return attn::launch_split_dk<256, 3>(a, s);
 }
+template <>
+int split_blocks_dk<256, 3>(int vb, int G, bool qjl) {
+    return attn::split_blocks_dk<256, 3>(vb, G, qjl);
+}
 }  // namespace tqi

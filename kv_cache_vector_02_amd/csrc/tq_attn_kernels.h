@@ -46,10 +46,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Waves per SIMD the split kernel is compiled for (caps its VGPRs at 512/N).
-#ifndef TQ_SPLIT_WAVES
-#define TQ_SPLIT_WAVES(D) ((D) == 128 ? 3 : 2)
-#endif
 
 // ----------------------------------------------------------------- qprep ----
 // q_rot is stored dim-major inside each chunk of G query heads, so the 2*G
@@ -101,51 +97,102 @@ __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
 }
 
 // ----------------------------------------------------------------- split ----
-// K side on matrix cores.  For one wave and 16 tokens, the scores of the 16
-// query-head columns (G used) are D[token][head] = sum_dim C[token][dim] Q[dim][head]
-// with v_mfma_f32_16x16x32_f16: lane l holds A = 8 dims of token l%16 and
-// B = the same 8 dims of head l%16, for dims (l/16)*d/4 + 8*ks + [0, 8) in K
-// step ks (each lane group owns a contiguous quarter of the dims, so its code
-// bytes are one contiguous load).  Float32 accuracy comes from splitting both
-// operands into half hi + lo parts: q_hi c_hi + q_lo c_hi + q_hi c_lo (the
-// c_lo q_lo term is below float32 rounding).  The query is scaled per head by a
-// power of two into [2^14, 2^15) and the centroids by 16 so every lo part is a
-// normal half; the scale is removed exactly on the float32 result.
+// Both contractions of a 64-token tile run on v_mfma_f32_16x16x32_f16.  For
+// this MFMA lane l holds A[l%16][8(l/16) + e] and B[8(l/16) + e][l%16]
+// (e = 0..7) and receives D[4(l/16) + i][l%16] (i = 0..3).
+//
+// Scores, per 16-token sub-tile j: D[token][head] = sum_dim C_K[token][dim]
+// Q[dim][head].  Lane (n, grp) = (l%16, l/16) takes the K codes of token 16j + n
+// straight from memory, dims grp*d/4 + [0, d/4) (one contiguous load), and in K
+// step ks the dims grp*d/4 + 8ks + e.  Float32 accuracy comes from splitting
+// both operands into half hi + lo parts: c_hi q_hi + c_hi q_lo + c_lo q_hi (the
+// c_lo q_lo term is below float32 rounding).  The query chunk is scaled by one
+// power of two into [2^14, 2^15) and the centroids by 16, so every lo part is a
+// normal half; the scale is removed exactly on the float32 result.  Lane
+// (n, grp) then holds the scores of tokens 16j + 4grp + i for head n.
+//
+// V sums, per K step s2 of 32 tokens: D[head][col] = sum_token W[head][token]
+// C_V[token][dim(col)], with the softmax weights of the lane's own registers as
+// A (k slot 8grp + e <-> token 32 s2 + 16(e/4) + 4grp + e%4) and column n' of
+// N-block nb standing for dim NB*n' + nb, so a lane's codes of one token are one
+// contiguous NB*VB-bit piece of the token's row.  Centroids come from an LDS
+// table indexed by VT codes of one token; v_perm pairs the halves of two tokens
+// into one B dword.
+//
+// Softmax: the log2-domain scores are exponentiated against a reference max
+// that is only raised when a score exceeds it by more than 2^kTauLog2 (lazy
+// rescaling), and the V weights p * |v| are scaled by a power of two taken
+// from a reference V norm that is only raised when a larger norm shows up.
+// Both keep the half weights below 2^15; the rare raise rescales the running
+// sums of the wave.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-template <int D, int KB, int VB, int G>
+constexpr float kTauLog2 = 8.0f;  // scores may exceed the reference max by this much (log2 units)
+constexpr int kVHeadroom = 1;     // binades of headroom above the largest V norm seen
+
+// Waves of one split block: the block owns a compute unit (one resident block
+// per CU) and its waves share the lookup tables.
+constexpr int split_waves(int d) { return d == 128 ? 12 : 8; }
+
+template <int D, int KB, int VB, int G, bool QJL>
 struct Cfg {
-    // K side: scores on matrix cores (see above)
+    static constexpr int NW = split_waves(D);       // waves per block
+    static constexpr int NT = 64 * NW;              // threads per block
+    // K side
     static constexpr int RBK = D * KB / 8;          // K code bytes per token
-    static constexpr int CPT = RBK / 16;            // 16-byte chunks per K row
-    static constexpr int RBKP = RBK % 64 == 0 ? RBK + 16 : RBK;  // LDS K row stride (bank spread)
     static constexpr int DG = D / 4;                // dims per lane group
     static constexpr int KSTEPS = DG / 8;           // MFMA K steps (32 dims each)
     static constexpr int GB = DG * KB / 8;          // K code bytes per lane group per token
+    static constexpr int GW = GB / 4;               // ... in dwords
     static constexpr int KLU = (KB == 3) ? 6 : 8;   // bits per K table lookup
     static constexpr int KCPL = KLU / KB;           // codes per lookup
     static constexpr int LPS = 8 / KCPL;            // lookups per K step
-    static constexpr int KENT = 4 * KCPL;           // bytes per K table entry: hi[KCPL], lo[KCPL] halves
-    static constexpr int KTABB = (1 << KLU) * KENT;
-    // V side: weighted sums on matrix cores.  Output column n' of N-block nb is
-    // dim NB*n' + nb, so a lane's codes for all N-blocks are one contiguous
-    // PIECE-bit field of the token's row.
+    static constexpr int KHB = 2 * KCPL;            // bytes per hi (or lo) entry
+    // V side
     static constexpr int RBV = D * VB / 8;          // V code bytes per token
     static constexpr int VTW = RBV / 4;             // dwords per V row
     static constexpr int NB = D / 16;               // N-blocks of 16 columns
     static constexpr int PIECE = VB * NB;           // bits per lane per token
-    static constexpr int PL = VB <= 2 ? 2 : 1;      // N-blocks per V table lookup
-    static constexpr int VIDXB = 2 * PL * VB;       // V table index bits (two tokens x PL codes)
-    static constexpr int VENT = 4 * PL;             // bytes per V table entry (PL half2)
-    static constexpr int VTABB = (1 << VIDXB) * VENT;
-    // per wave: K tile [64][RBKP] bytes, V tile dword-major [VTW + 1][64],
-    // head factors [16], K norm / V norm / gamma [64] floats each
-    static constexpr int KT_DW = 64 * RBKP / 4;
-    static constexpr int WAVE_DW = KT_DW + (VTW + 1) * 64 + 16 + 3 * 64;
-    static constexpr int MAIN = 4 * WAVE_DW;
-    static constexpr int MERGE = 4 * G * (D + 2);
-    static constexpr int UNION = MAIN > MERGE ? MAIN : MERGE;
+    static constexpr int VT = VB == 1 ? 8 : (VB == 2 ? 4 : 2);  // codes per V lookup
+    static constexpr int VLB = VT * VB;             // V index bits
+    static constexpr int VENT = 2 * VT;             // bytes per V entry
+    static constexpr int VENTW = VENT / 4;          // ... in dwords
+    static constexpr int VLK = NB / VT;             // V lookups per token
+    // per wave: V tile dword-major [VTW + 1][VSTR] (last row zero; VSTR pads the
+    // rows across banks), head factors [16], K norm * query scale [64], scaled
+    // V norm [64], QJL gamma [64]
+    static constexpr int VSTR = 68;
+    static constexpr int WAVE_DW = (VTW + 1) * VSTR + 16 + 3 * 64;
+    static constexpr int QJL_DW = QJL ? 8 * 64 * 8 + 256 * 4 : 0;  // QJL B operands + sign table
+    // Bank-sliced tables: the hi entries of K table row u sit in the first half
+    // of a KROW-byte row at u*KROW, one copy per slice; lane l reads slice
+    // l % (KROW / 2 / KHB), so the lanes of one LDS pass touch distinct banks
+    // whatever their indices.  The lo entries of row u sit in the second half of
+    // row u + KLO_SHIFT: that offset is neither below 1 KiB nor a multiple of
+    // 256 bytes, so the hi and lo reads stay two instructions with their results
+    // in place (a merged pair read would need register moves).  The V table is
+    // sliced the same way with VROW bytes per row.
+    static constexpr int FIXED_B = 4 * (NW * WAVE_DW + QJL_DW);
+    static constexpr int LDS_CAP = 160 * 1024 - 1024;
+    static constexpr int KLO_SHIFT = 5;
+    static constexpr bool fits(int kr, int vr) {
+        return ((1 << KLU) + KLO_SHIFT) * kr + (1 << VLB) * vr + FIXED_B <= LDS_CAP;
+    }
+    static constexpr int KROW = fits(256, 128) ? 256 : fits(256, 64) ? 256 : fits(128, 64) ? 128 : 64;
+    static constexpr int VROW = fits(KROW, 128) ? 128 : fits(KROW, 64) ? 64 : 32;
+    static constexpr int KSL = KROW / 2 / KHB;      // K slices
+    static constexpr int VSL = VROW / VENT;         // V slices
+    static constexpr int KLO = KLO_SHIFT * KROW + KROW / 2;  // lo entry offset from its hi entry
+    static constexpr int KTABB = ((1 << KLU) + KLO_SHIFT) * KROW;
+    static constexpr int VTABB = (1 << VLB) * VROW;
+    static constexpr int LOOP_DW = KTABB / 4 + VTABB / 4 + NW * WAVE_DW + QJL_DW;
+    static constexpr int MERGE_DW = NW * G * (D + 2);
+    static constexpr int SMEM_DW = LOOP_DW > MERGE_DW ? LOOP_DW : MERGE_DW;
+    static_assert(KSL >= 1 && VSL >= 1, "table rows too small");
+    static_assert(4 * SMEM_DW <= 160 * 1024, "split kernel exceeds LDS");
 };
 
 __device__ __forceinline__ half8_t as_half8(uint4 u) { return __builtin_bit_cast(half8_t, u); }
@@ -158,16 +205,6 @@ __device__ __forceinline__ uint32_t field_at(const uint32_t* w, int bit0) {
     return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & ((1u << BITS) - 1u);
 }
 
-// Power of two mapping max|v| of a head (its four lane groups) into [2^14, 2^15).
-__device__ __forceinline__ float head_scale(float local_absmax) {
-    float mx = fmaxf(local_absmax, xor_lane<16>(local_absmax));
-    mx = fmaxf(mx, xor_lane<32>(mx));
-    if (!(mx > 0.0f) || !isfinite(mx)) return 1.0f;
-    int e;
-    frexpf(mx, &e);
-    return ldexpf(1.0f, 15 - e);
-}
-
 __device__ __forceinline__ float bcast_lane(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
@@ -175,56 +212,89 @@ __device__ __forceinline__ float bcast_lane(float v, int l) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){a, b}, half2_t));
 }
 
-// Loads of one 64-token tile into registers: the K tile as 16-byte chunks
-// (chunk 64*j + lane of the tile), the V row of token t0 + lane and its norms.
-// Token indices are clamped into [t0, t_end) so every address is valid; values
-// of clamped tokens are masked by the caller.
-template <int D, int KB, int VB, bool QJL>
-__device__ __forceinline__ void fetch_tile(uint32_t (&rk)[D * KB / 32], uint32_t (&rv)[D * VB / 32], uint32_t& rn,
-                                           uint32_t& rg, const AttnArgs& a, const uint8_t* kcodes,
-                                           const uint8_t* vcodes, int64_t kvrow, int64_t t0, int64_t t_end,
-                                           int lane) {
-    constexpr int RBK = D * KB / 8, RBV = D * VB / 8, CPT = RBK / 16;
-    // token indices fit 32 bits (ctx_cap * row bytes < 2^31 is checked on the host)
-    const uint32_t last = (uint32_t)(t_end - 1), tb = (uint32_t)t0;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const uint32_t c = 64 * j + lane;
-        uint32_t t = tb + c / CPT;
-        t = t < last ? t : last;
-        const uint4 v = *reinterpret_cast<const uint4*>(kcodes + (t * RBK + (c % CPT) * 16));
-        rk[4 * j] = v.x; rk[4 * j + 1] = v.y; rk[4 * j + 2] = v.z; rk[4 * j + 3] = v.w;
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, xor_lane<1>(v));
+    v = fmaxf(v, xor_lane<2>(v));
+    v = fmaxf(v, xor_lane<4>(v));
+    v = fmaxf(v, xor_lane<8>(v));
+    v = fmaxf(v, xor_lane<16>(v));
+    return fmaxf(v, xor_lane<32>(v));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_read(uint32_t* dst, const uint8_t* p) {
+    if constexpr (N == 1) {
+        dst[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (N == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        dst[0] = v.x; dst[1] = v.y;
+    } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
     }
-    uint32_t tl = tb + lane;
-    tl = tl < last ? tl : last;
-    const uint4* vp = reinterpret_cast<const uint4*>(vcodes + tl * RBV);
+}
+
+// K codes of sub-tiles 0..3 in MFMA A layout: token t0 + 16j + n, bytes grp*GB.
+// Token indices are clamped into [t0, t_end) so every address is valid.
+template <class C>
+__device__ __forceinline__ void fetch_k(uint32_t (&rk)[4 * C::GW], const uint8_t* kcodes, uint32_t t0, uint32_t last,
+                                        int n, int grp) {
 #pragma unroll
-    for (int w = 0; w < RBV / 16; ++w) {
+    for (int j = 0; j < 4; ++j) {
+        uint32_t t = t0 + 16 * j + n;
+        t = t < last ? t : last;
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(kcodes + (t * C::RBK + grp * C::GB));
+        if constexpr (C::GW % 4 == 0) {
+#pragma unroll
+            for (int w = 0; w < C::GW / 4; ++w) {
+                const uint4 v = reinterpret_cast<const uint4*>(p)[w];
+                rk[j * C::GW + 4 * w] = v.x; rk[j * C::GW + 4 * w + 1] = v.y;
+                rk[j * C::GW + 4 * w + 2] = v.z; rk[j * C::GW + 4 * w + 3] = v.w;
+            }
+        } else if constexpr (C::GW % 2 == 0) {
+#pragma unroll
+            for (int w = 0; w < C::GW / 2; ++w) {
+                const uint2 v = reinterpret_cast<const uint2*>(p)[w];
+                rk[j * C::GW + 2 * w] = v.x; rk[j * C::GW + 2 * w + 1] = v.y;
+            }
+        } else {
+#pragma unroll
+            for (int w = 0; w < C::GW; ++w) rk[j * C::GW + w] = p[w];
+        }
+    }
+}
+
+// V row, norms (and QJL gamma) of token t0 + lane (clamped like fetch_k).
+template <class C, bool QJL>
+__device__ __forceinline__ void fetch_v(uint32_t (&rv)[C::VTW], uint32_t& rn, uint32_t& rg, const uint8_t* vcodes,
+                                        const uint8_t* knb, const uint8_t* vnb, const uint8_t* gmb, uint32_t t0,
+                                        uint32_t last, int lane) {
+    uint32_t tl = t0 + lane;
+    tl = tl < last ? tl : last;
+    const uint4* vp = reinterpret_cast<const uint4*>(vcodes + tl * C::RBV);
+#pragma unroll
+    for (int w = 0; w < C::RBV / 16; ++w) {
         const uint4 v = vp[w];
         rv[4 * w] = v.x; rv[4 * w + 1] = v.y; rv[4 * w + 2] = v.z; rv[4 * w + 3] = v.w;
     }
-    const uint16_t* kn = a.k_norms + kvrow;
-    const uint16_t* vn = a.v_norms + kvrow;
-    rn = (uint32_t)kn[tl] | ((uint32_t)vn[tl] << 16);
-    if constexpr (QJL) rg = (a.k_gamma + kvrow)[tl];
+    rn = (uint32_t)*reinterpret_cast<const uint16_t*>(knb + 2u * tl) |
+         ((uint32_t)*reinterpret_cast<const uint16_t*>(vnb + 2u * tl) << 16);
+    if constexpr (QJL) rg = *reinterpret_cast<const uint16_t*>(gmb + 2u * tl);
 }
 
 template <int D, int KB, int VB, int G, bool QJL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WAVES(D)))) void split_kernel(AttnArgs a) {
-    using C = Cfg<D, KB, VB, G>;
-    constexpr int QJLB = QJL ? 8 * 64 * 8 : 0;   // dwords: QJL B operands (<= 8 K steps x 64 lanes x hi,lo)
-    constexpr int SIGB = QJL ? 256 * 4 : 0;      // dwords: sign table 256 x 8 halves
-    constexpr int SMEM = C::KTABB / 4 + C::VTABB / 4 + C::UNION + QJLB + SIGB;
-    __shared__ __attribute__((aligned(16))) uint32_t smem[SMEM];
+__global__ __launch_bounds__(64 * split_waves(D)) __attribute__((amdgpu_waves_per_eu(split_waves(D) / 4)))
+void split_kernel(AttnArgs a) {
+    using C = Cfg<D, KB, VB, G, QJL>;
+    __shared__ __attribute__((aligned(16))) uint32_t smem[C::SMEM_DW];
     uint8_t* ktab = reinterpret_cast<uint8_t*>(smem);
     uint8_t* vtab = reinterpret_cast<uint8_t*>(smem + C::KTABB / 4);
-    uint32_t* uni = smem + C::KTABB / 4 + C::VTABB / 4;
-    uint4* qjlb = reinterpret_cast<uint4*>(uni + C::UNION);
-    uint4* sigt = reinterpret_cast<uint4*>(uni + C::UNION + QJLB);
+    uint32_t* waves_lds = smem + C::KTABB / 4 + C::VTABB / 4;
+    uint4* qjlb = reinterpret_cast<uint4*>(waves_lds + C::NW * C::WAVE_DW);
+    uint4* sigt = qjlb + 8 * 64 * 2;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, grp = lane >> 4;
@@ -232,41 +302,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WA
     const int kvh = blockIdx.y / a.chunks, chunk = blockIdx.y - kvh * a.chunks;
     const int b = blockIdx.z;
     const int m = QJL ? a.kc.qjl_m : 0;
-    int64_t ctx = a.ctx_len[b];
-    ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
-    const int64_t t_beg = (int64_t)split * a.split_tokens;
-    const int64_t t_end = (t_beg + a.split_tokens < ctx) ? t_beg + a.split_tokens : ctx;
+    // token indices fit 31 bits (ctx_cap * row bytes < 2^31 is checked on the host)
+    const int cap = (int)a.ctx_cap;
+    int ctx = a.ctx_len[b];
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    const int t_beg = split * (int)a.split_tokens;
+    const int t_end = (t_beg + (int)a.split_tokens < ctx) ? t_beg + (int)a.split_tokens : ctx;
     const int h0 = kvh * a.g + chunk * G;
+    const int64_t kvrow = ((int64_t)b * a.hkv + kvh) * a.ctx_cap;
+    const uint8_t* kcodes = a.k_codes + kvrow * C::RBK;
+    const uint8_t* vcodes = a.v_codes + kvrow * C::RBV;
+    const uint8_t* knb = reinterpret_cast<const uint8_t*>(a.k_norms + kvrow);
+    const uint8_t* vnb = reinterpret_cast<const uint8_t*>(a.v_norms + kvrow);
+    const uint8_t* gmb = QJL ? reinterpret_cast<const uint8_t*>(a.k_gamma + kvrow) : nullptr;
+    const uint32_t last = t_end > 0 ? (uint32_t)(t_end - 1) : 0u;
 
-    // K table: entry u -> 16*c_K of its KCPL codes, half hi parts then lo parts
-    for (int u = tid; u < (1 << C::KLU); u += 256) {
-        _Float16* e = reinterpret_cast<_Float16*>(ktab + u * C::KENT);
+    // first tile's loads go out before the tables are built
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int t0 = t_beg + wave_u * 64;
+    uint32_t rk[4 * C::GW];
+    uint32_t rv[C::VTW], rn = 0, rg = 0;
+    if (t0 < t_end) {
+        fetch_k<C>(rk, kcodes, (uint32_t)t0, last, n, grp);
+        fetch_v<C, QJL>(rv, rn, rg, vcodes, knb, vnb, gmb, (uint32_t)t0, last, lane);
+    }
+
+    // K table: row u, slice sl -> hi halves of 16*c_K of the KCPL codes of u at
+    // u*KROW + sl*KHB, lo halves KLO bytes further
+    for (int i = tid; i < (1 << C::KLU) * C::KSL; i += C::NT) {
+        const int u = i / C::KSL, sl = i - u * C::KSL;
+        _Float16* eh = reinterpret_cast<_Float16*>(ktab + u * C::KROW + sl * C::KHB);
+        _Float16* el = reinterpret_cast<_Float16*>(ktab + u * C::KROW + C::KLO + sl * C::KHB);
 #pragma unroll
         for (int p = 0; p < C::KCPL; ++p) {
             const float c = 16.0f * a.kc.centroid[(u >> (KB * p)) & ((1 << KB) - 1)];
             const _Float16 hi = (_Float16)c;
-            e[p] = hi;
-            e[C::KCPL + p] = (_Float16)(c - (float)hi);
+            eh[p] = hi;
+            el[p] = (_Float16)(c - (float)hi);
         }
     }
-    // V table: index = (PL codes of token a) | (PL codes of token b) << PL*VB;
-    // entry dword q = half2(c_V[code_q of a], c_V[code_q of b])
-    for (int u = tid; u < (1 << C::VIDXB); u += 256) {
-        _Float16* e = reinterpret_cast<_Float16*>(vtab + u * C::VENT);
-        constexpr int VM = (1 << VB) - 1;
+    // V table: row u, slice sl -> half c_V of the VT codes of u (code p = bits [VB p, VB p + VB))
+    for (int i = tid; i < (1 << C::VLB) * C::VSL; i += C::NT) {
+        const int u = i / C::VSL, sl = i - u * C::VSL;
+        _Float16* e = reinterpret_cast<_Float16*>(vtab + u * C::VROW + sl * C::VENT);
 #pragma unroll
-        for (int q = 0; q < C::PL; ++q) {
-            e[2 * q] = (_Float16)a.vc.centroid[(u >> (q * VB)) & VM];
-            e[2 * q + 1] = (_Float16)a.vc.centroid[(u >> (C::PL * VB + q * VB)) & VM];
-        }
+        for (int p = 0; p < C::VT; ++p) e[p] = (_Float16)a.vc.centroid[(u >> (VB * p)) & ((1 << VB) - 1)];
     }
     if constexpr (QJL) {
         _Float16* st = reinterpret_cast<_Float16*>(sigt);
-        for (int e = tid; e < 256 * 8; e += 256) st[e] = ((e >> 3) >> (e & 7)) & 1 ? (_Float16)1.0f : (_Float16)(-1.0f);
+        for (int e = tid; e < 256 * 8; e += C::NT) st[e] = ((e >> 3) >> (e & 7)) & 1 ? (_Float16)1.0f : (_Float16)(-1.0f);
     }
 
-    // K-side B operands: rotated query (and QJL projection) of head n, scaled
-    // by one power of two per head; zero for n >= G
+    // K-side B operands: rotated query (and QJL projection) of head n, all G
+    // heads scaled by one power of two; zero for n >= G
     const float* qrot = a.qrot + ((int64_t)b * a.hq + h0) * D;  // [dim][G] inside this chunk
     half8_t qhi[C::KSTEPS], qlo[C::KSTEPS];
     float qinv;
@@ -278,7 +366,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WA
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int dim = grp * C::DG + 8 * ks + j;
-                qv[ks][j] = n < G ? qrot[dim * G + n] : 0.0f;
+                const float x = qrot[dim * G + (n < G ? n : G - 1)];
+                qv[ks][j] = n < G ? x : 0.0f;
                 amax = fmaxf(amax, fabsf(qv[ks][j]));
             }
         const float* qp = a.qproj + ((int64_t)b * a.hq + h0) * m;
@@ -287,7 +376,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WA
                 for (int j = 0; j < 8; ++j)
                     amax = fmaxf(amax, n < G ? fabsf(qp[n * m + grp * (m >> 2) + 8 * ks + j]) : 0.0f);
         }
-        const float sc = head_scale(amax);
+        amax = wave_max(amax);
+        float sc = 1.0f;
+        if (amax > 0.0f && isfinite(amax)) {
+            int e;
+            frexpf(amax, &e);
+            sc = ldexpf(1.0f, 15 - e);
+        }
         qinv = 1.0f / (16.0f * sc);
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks)
@@ -315,65 +410,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WA
             }
         }
     }
+    uint32_t* vt = waves_lds + wave * C::WAVE_DW;                      // [VTW + 1][VSTR] dword-major V tile
+    float* hfac = reinterpret_cast<float*>(vt + (C::VTW + 1) * C::VSTR);  // [16] per-head rescale factors
+    float* knq = hfac + 16;                                             // [64] K norm * query scale
+    float* vnl = knq + 64;                                              // [64] V norm * weight scale
+    float* gml = vnl + 64;                                              // [64] QJL gamma
+    vt[C::VTW * C::VSTR + lane] = 0u;
     __syncthreads();
+    // this lane's table slices (byte offsets inside a row)
+    const uint32_t koff = (uint32_t)(lane % C::KSL) * C::KHB;
+    const uint32_t voff = (uint32_t)(lane % C::VSL) * C::VENT;
 
-    const int64_t kvrow = ((int64_t)b * a.hkv + kvh) * a.ctx_cap;
-    const uint8_t* kcodes = a.k_codes + kvrow * C::RBK;
-    const uint8_t* vcodes = a.v_codes + kvrow * (C::RBV);
-    uint32_t* wv = uni + wave * C::WAVE_DW;
-    uint8_t* kt = reinterpret_cast<uint8_t*>(wv);       // [64][RBKP] K tile
-    uint32_t* vt = wv + C::KT_DW;                       // [VTW + 1][64] dword-major V tile
-    float* hfac = reinterpret_cast<float*>(vt + (C::VTW + 1) * 64);  // [16] per-head V factors
-    float* knl = hfac + 16;                             // [64] K norms
-    float* vnl = knl + 64;                              // [64] V norms * weight scale
-    float* gml = vnl + 64;                              // [64] QJL gamma
-
-    float m_run = -INFINITY, l_lane = 0.0f;  // head n's running max / this lane's partial sum
-    // V sums D[nb][i]: head 4*grp + i, dim NB*n + nb, in units of the current weight scale
+    float m_ref = -INFINITY, l_lane = 0.0f;  // head n's reference max / this lane's partial sum
+    // V sums D[nb][i]: head 4*grp + i, dim NB*n + nb, in units of 2^wsh
     floatx4_t vacc[C::NB];
 #pragma unroll
     for (int q = 0; q < C::NB; ++q) vacc[q] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    int wexp_prev = 0;
-    bool first = true;
-    constexpr int PB0 = 0;
-    const int pbit = C::PIECE * n;               // this lane's V field inside a row
-    const int pw0 = pbit >> 5, psh = pbit & 31;  // first dword and shift
-    (void)PB0;
+    int vref = -200;                 // reference V-norm exponent: norms < 2^vref
+    float vlim = 0.0f, vsc = 0.0f;   // 2^vref, 2^wsh with wsh = 15 - kTauLog2 - vref
+    const int pbit = C::PIECE * n;   // this lane's V field inside a row
+    const int pw0 = pbit >> 5, psh = pbit & 31;
 
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    int64_t t0 = t_beg + wave_u * 64;
-    uint32_t rk[4 * C::CPT];
-    uint32_t rv[C::VTW], rn = 0, rg = 0;
-    if (t0 < t_end) fetch_tile<D, KB, VB, QJL>(rk, rv, rn, rg, a, kcodes, vcodes, kvrow, t0, t_end, lane);
-    for (; t0 < t_end; t0 += 256) {
-        const int rem = (int)(t_end - t0);  // tokens left in this split (> 0)
+    while (t0 < t_end) {
+        const int rem = t_end - t0;  // tokens left in this split (> 0)
         const bool lane_valid = lane < rem;
-        // ---- stage this tile: K chunks (row-major, padded rows), V (dword-major), norms
+        // ---- stage V codes and norms of this tile (lane <-> token)
 #pragma unroll
-        for (int j = 0; j < C::CPT; ++j) {
-            const int c = 64 * j + lane;
-            *reinterpret_cast<uint4*>(kt + (c / C::CPT) * C::RBKP + (c % C::CPT) * 16) =
-                make_uint4(rk[4 * j], rk[4 * j + 1], rk[4 * j + 2], rk[4 * j + 3]);
-        }
-#pragma unroll
-        for (int w = 0; w < C::VTW; ++w) vt[w * 64 + lane] = rv[w];
-        vt[C::VTW * 64 + lane] = 0u;
-        const float vnf = lane_valid ? half_bits_to_float(rn >> 16) : 0.0f;
-        knl[lane] = lane_valid ? half_bits_to_float(rn & 0xFFFFu) : 0.0f;
+        for (int w = 0; w < C::VTW; ++w) vt[w * C::VSTR + lane] = rv[w];
+        const float vnf = half_bits_to_float(rn >> 16);
+        knq[lane] = half_bits_to_float(rn & 0xFFFFu) * qinv;
         if constexpr (QJL) gml[lane] = half_bits_to_float(rg);
-        // power of two bringing this tile's largest V norm into [2^14, 2^15)
-        float vmax = vnf;
-        vmax = fmaxf(vmax, xor_lane<1>(vmax));
-        vmax = fmaxf(vmax, xor_lane<2>(vmax));
-        vmax = fmaxf(vmax, xor_lane<4>(vmax));
-        vmax = fmaxf(vmax, xor_lane<8>(vmax));
-        vmax = fmaxf(vmax, xor_lane<16>(vmax));
-        vmax = fmaxf(vmax, xor_lane<32>(vmax));
-        int wexp = 0;
-        if (vmax > 0.0f && isfinite(vmax)) frexpf(vmax, &wexp);
-        vnl[lane] = vnf * ldexpf(1.0f, 15 - wexp);  // weights are p * vn * 2^(15 - wexp)
-        // ---- fetch the next tile while this one computes (clamped: always valid)
-        fetch_tile<D, KB, VB, QJL>(rk, rv, rn, rg, a, kcodes, vcodes, kvrow, t0 + 256, t_end, lane);
+        float vfac = 1.0f;
+        bool pend = false;
+        if (__builtin_amdgcn_ballot_w64(lane_valid && vnf >= vlim)) {
+            // a V norm at or above the reference: raise it (rare)
+            const float vm = wave_max(lane_valid ? vnf : 0.0f);
+            int e;
+            frexpf(vm, &e);
+            const int vnew = e + kVHeadroom;
+            vfac = ldexpf(1.0f, vref - vnew);
+            vref = vnew;
+            vlim = ldexpf(1.0f, vref);
+            vsc = ldexpf(1.0f, 15 - (int)kTauLog2 - vref);
+            pend = true;
+        }
+        vnl[lane] = vnf * vsc;
+        // ---- next tile's loads (clamped; skipped past the end of the split)
+        const int tn = t0 + 64 * C::NW;
+        if (tn < t_end) fetch_v<C, QJL>(rv, rn, rg, vcodes, knb, vnb, gmb, (uint32_t)tn, last, lane);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -384,45 +468,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WA
         for (int j = 0; j < 4; ++j) sacc[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint32_t kg[C::GB / 4];
-            const uint8_t* src = kt + (16 * j + n) * C::RBKP + grp * C::GB;
-            if constexpr (C::GB % 16 == 0) {
-#pragma unroll
-                for (int w = 0; w < C::GB / 16; ++w) {
-                    const uint4 v = reinterpret_cast<const uint4*>(src)[w];
-                    kg[4 * w] = v.x; kg[4 * w + 1] = v.y; kg[4 * w + 2] = v.z; kg[4 * w + 3] = v.w;
-                }
-            } else if constexpr (C::GB % 8 == 0) {
-#pragma unroll
-                for (int w = 0; w < C::GB / 8; ++w) {
-                    const uint2 v = reinterpret_cast<const uint2*>(src)[w];
-                    kg[2 * w] = v.x; kg[2 * w + 1] = v.y;
-                }
-            } else {
-#pragma unroll
-                for (int w = 0; w < C::GB / 4; ++w) kg[w] = reinterpret_cast<const uint32_t*>(src)[w];
-            }
 #pragma unroll
             for (int ks = 0; ks < C::KSTEPS; ++ks) {
                 uint32_t hw[4], lw[4];
 #pragma unroll
                 for (int u = 0; u < C::LPS; ++u) {
-                    const uint32_t f = field_at<C::KLU>(kg, ks * 8 * KB + u * C::KLU);
-                    const uint8_t* ent = ktab + f * C::KENT;
-                    if constexpr (C::KCPL == 2) {
-                        const uint2 e = *reinterpret_cast<const uint2*>(ent);
-                        hw[u] = e.x;
-                        lw[u] = e.y;
-                    } else if constexpr (C::KCPL == 4) {
-                        const uint4 e = *reinterpret_cast<const uint4*>(ent);
-                        hw[2 * u] = e.x; hw[2 * u + 1] = e.y;
-                        lw[2 * u] = e.z; lw[2 * u + 1] = e.w;
+                    const int bit = ks * 8 * KB + u * C::KLU;
+                    uint32_t addr;
+                    if constexpr (C::KLU == 8 && C::KROW == 256) {
+                        // row byte offset = field * 256 + koff: one byte permute
+                        const uint32_t w = rk[j * C::GW + (bit >> 5)];
+                        addr = __builtin_amdgcn_perm(w, koff, 0x0C0C0000u | ((uint32_t)(4 + ((bit >> 3) & 3)) << 8));
                     } else {
-                        const uint4 eh = reinterpret_cast<const uint4*>(ent)[0];
-                        const uint4 el = reinterpret_cast<const uint4*>(ent)[1];
-                        hw[0] = eh.x; hw[1] = eh.y; hw[2] = eh.z; hw[3] = eh.w;
-                        lw[0] = el.x; lw[1] = el.y; lw[2] = el.z; lw[3] = el.w;
+                        addr = field_at<C::KLU>(rk + j * C::GW, bit) * C::KROW + koff;
                     }
+                    lds_read<C::KHB / 4>(hw + u * (C::KHB / 4), ktab + addr);
+                    lds_read<C::KHB / 4>(lw + u * (C::KHB / 4), ktab + addr + C::KLO);
                 }
                 const half8_t ahi = as_half8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
                 const half8_t alo = as_half8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
@@ -431,11 +492,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WA
                 sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, qhi[ks], sacc[j], 0, 0, 0);
             }
         }
+        if (tn < t_end) fetch_k<C>(rk, kcodes, (uint32_t)tn, last, n, grp);
         if constexpr (QJL) {
             // A = 16*gamma*(+-1) of token 16j + n (exact in half); same accumulators
             const int gbytes = m >> 5;
             for (int j = 0; j < 4; ++j) {
-                int64_t t = t0 + 16 * j + n;
+                int t = t0 + 16 * j + n;
                 t = t < t_end - 1 ? t : t_end - 1;
                 const _Float16 g16 = (_Float16)(16.0f * gml[16 * j + n]);
                 const uint8_t* sp = a.k_qjl + (kvrow + t) * (m >> 3) + grp * gbytes;
@@ -446,48 +508,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WA
                 }
             }
         }
-        // ---- scores of tokens 16j + 4*grp + v for head n; online softmax (log2 domain)
-        float tmax = -INFINITY;
+        // ---- scores of tokens 16j + 4grp + v for head n, relative to the reference max
+        float dsc[4][4];
+        float lmax = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float4 kn4 = *reinterpret_cast<const float4*>(knl + 16 * j + 4 * grp);
-            const float knv[4] = {kn4.x, kn4.y, kn4.z, kn4.w};
+            const float4 kq = *reinterpret_cast<const float4*>(knq + 16 * j + 4 * grp);
+            dsc[j][0] = fmaf(sacc[j][0], kq.x, -m_ref);
+            dsc[j][1] = fmaf(sacc[j][1], kq.y, -m_ref);
+            dsc[j][2] = fmaf(sacc[j][2], kq.z, -m_ref);
+            dsc[j][3] = fmaf(sacc[j][3], kq.w, -m_ref);
+        }
+        const int lim = rem - 4 * grp;  // token 16j + 4grp + v is valid iff 16j + v < lim
+        if (rem < 64) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const bool ok = 16 * j + 4 * grp + v < rem;
-                const float sv = ok ? sacc[j][v] * qinv * knv[v] : -INFINITY;
-                sacc[j][v] = sv;
-                tmax = fmaxf(tmax, sv);
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (16 * j + v >= lim) dsc[j][v] = -INFINITY;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) lmax = fmaxf(lmax, dsc[j][v]);
+        if (__builtin_amdgcn_ballot_w64(lmax > kTauLog2) || pend) {
+            // raise the reference max of every head to its tile max (rare)
+            float s[4][4], tmax = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 kq = *reinterpret_cast<const float4*>(knq + 16 * j + 4 * grp);
+                const float kv[4] = {kq.x, kq.y, kq.z, kq.w};
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    s[j][v] = (16 * j + v < lim) ? sacc[j][v] * kv[v] : -INFINITY;
+                    tmax = fmaxf(tmax, s[j][v]);
+                }
             }
-        }
-        tmax = fmaxf(tmax, xor_lane<16>(tmax));
-        tmax = fmaxf(tmax, xor_lane<32>(tmax));
-        const float mnew = fmaxf(m_run, tmax);
-        const float alpha = fast_exp2(m_run - mnew);
-        m_run = mnew;
-        // V-side A operands: half weights of this lane's tokens (K order: sub-tile
-        // pairs (2s, 2s+1), tokens 4*grp + v), head n = row
-        uint32_t wa[2][4];
-        float psum = 0.0f;
+            tmax = fmaxf(tmax, xor_lane<16>(tmax));
+            tmax = fmaxf(tmax, xor_lane<32>(tmax));
+            const float mnew = fmaxf(m_ref, tmax);
+            const float alpha = fast_exp2(m_ref - mnew);
+            m_ref = mnew;
+            l_lane *= alpha;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 vn4 = *reinterpret_cast<const float4*>(vnl + 16 * j + 4 * grp);
-            const float p0 = fast_exp2(sacc[j][0] - mnew), p1 = fast_exp2(sacc[j][1] - mnew);
-            const float p2 = fast_exp2(sacc[j][2] - mnew), p3 = fast_exp2(sacc[j][3] - mnew);
-            psum += (p0 + p1) + (p2 + p3);
-            wa[j >> 1][2 * (j & 1)] = pack_half2(p0 * vn4.x, p1 * vn4.y);
-            wa[j >> 1][2 * (j & 1) + 1] = pack_half2(p2 * vn4.z, p3 * vn4.w);
-        }
-        l_lane = fmaf(l_lane, alpha, psum);
-        // per-head factor for the V sums: softmax correction x change of weight scale
-        const float rescale = first ? 1.0f : ldexpf(1.0f, wexp_prev - wexp);  // exact power of two
-        wexp_prev = wexp;
-        first = false;
-        if (grp == 0) hfac[n] = alpha * rescale;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        {
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dsc[j][v] = s[j][v] - mnew;
+            if (grp == 0) hfac[n] = alpha * vfac;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             const float4 f4 = *reinterpret_cast<const float4*>(hfac + 4 * grp);
 #pragma unroll
             for (int q = 0; q < C::NB; ++q) {
@@ -497,79 +567,87 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WA
                 vacc[q][3] *= f4.w;
             }
         }
+        // ---- V-side A operands: half weights p * |v| * 2^wsh (K order: sub-tile
+        // pairs (2 s2, 2 s2 + 1), tokens 4grp + v), row = head n
+        uint32_t wa[2][4];
+        float psum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 vq = *reinterpret_cast<const float4*>(vnl + 16 * j + 4 * grp);
+            const float p0 = fast_exp2(dsc[j][0]), p1 = fast_exp2(dsc[j][1]);
+            const float p2 = fast_exp2(dsc[j][2]), p3 = fast_exp2(dsc[j][3]);
+            psum += (p0 + p1) + (p2 + p3);
+            wa[j >> 1][2 * (j & 1)] = pack_half2(p0 * vq.x, p1 * vq.y);
+            wa[j >> 1][2 * (j & 1) + 1] = pack_half2(p2 * vq.z, p3 * vq.w);
+        }
+        l_lane += psum;
 
-        // ---- V sums on matrix cores: for K step s (sub-tiles 2s, 2s+1), this
-        // lane's 8 tokens, its PIECE-bit field of each token's V row
+        // ---- V sums on matrix cores
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            uint32_t pc[8];  // PIECE <= 32: the field; else its low 32 bits (high part in ph)
-            uint32_t ph[8];
+            // this lane's PIECE-bit field of its 8 tokens (e = 4 jj + v)
+            uint32_t pc[8], ph[8];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                const int tok = 16 * (2 * s2 + jj) + 4 * grp;
-                const uint4 x = *reinterpret_cast<const uint4*>(vt + pw0 * 64 + tok);
-                uint32_t lo[4] = {x.x, x.y, x.z, x.w};
-                if constexpr (C::PIECE <= 32 && (32 % C::PIECE == 0)) {
+                const int tok = 32 * s2 + 16 * jj + 4 * grp;
+                const uint4 x = *reinterpret_cast<const uint4*>(vt + pw0 * C::VSTR + tok);
+                const uint32_t lo[4] = {x.x, x.y, x.z, x.w};
+                if constexpr (C::PIECE <= 32 && 32 % C::PIECE == 0) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) pc[4 * jj + v] = lo[v] >> psh;
                 } else {
-                    const uint4 y = *reinterpret_cast<const uint4*>(vt + (pw0 + 1) * 64 + tok);
+                    const uint4 y = *reinterpret_cast<const uint4*>(vt + (pw0 + 1) * C::VSTR + tok);
                     const uint32_t hi[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         pc[4 * jj + v] = __builtin_amdgcn_alignbit(hi[v], lo[v], psh);
-                        ph[4 * jj + v] = psh == 0 ? hi[v] : (hi[v] >> psh);
+                        ph[4 * jj + v] = hi[v] >> psh;  // psh < 32; only read when PIECE > 32
                     }
                 }
             }
             const half8_t aw = as_half8(make_uint4(wa[s2][0], wa[s2][1], wa[s2][2], wa[s2][3]));
 #pragma unroll
-            for (int k = 0; k < C::NB / C::PL; ++k) {
-                constexpr int FB = C::PL * VB;  // bits per token per lookup
-                uint32_t bw[C::PL][4];
+            for (int k = 0; k < C::VLK; ++k) {
+                const int bit = k * C::VLB;
+                uint32_t ent[8][C::VENTW];
 #pragma unroll
-                for (int pp = 0; pp < 4; ++pp) {
-                    const int bit = k * FB;
-                    uint32_t fa, fb;
+                for (int e = 0; e < 8; ++e) {
+                    uint32_t idx;
                     if constexpr (C::PIECE <= 32) {
-                        fa = (pc[2 * pp] >> bit) & ((1u << FB) - 1u);
-                        fb = (pc[2 * pp + 1] >> bit) & ((1u << FB) - 1u);
+                        idx = (pc[e] >> bit) & ((1u << C::VLB) - 1u);
                     } else {
-                        const uint64_t xa = ((uint64_t)ph[2 * pp] << 32) | pc[2 * pp];
-                        const uint64_t xb = ((uint64_t)ph[2 * pp + 1] << 32) | pc[2 * pp + 1];
-                        fa = (uint32_t)(xa >> bit) & ((1u << FB) - 1u);
-                        fb = (uint32_t)(xb >> bit) & ((1u << FB) - 1u);
+                        const uint64_t x = ((uint64_t)ph[e] << 32) | pc[e];
+                        idx = (uint32_t)(x >> bit) & ((1u << C::VLB) - 1u);
                     }
-                    const uint32_t idx = fa | (fb << FB);
-                    if constexpr (C::PL == 2) {
-                        const uint2 e = *reinterpret_cast<const uint2*>(vtab + idx * 8);
-                        bw[0][pp] = e.x;
-                        bw[1][pp] = e.y;
-                    } else {
-                        bw[0][pp] = *reinterpret_cast<const uint32_t*>(vtab + idx * 4);
-                    }
+                    lds_read<C::VENTW>(ent[e], vtab + idx * C::VROW + voff);
                 }
 #pragma unroll
-                for (int q = 0; q < C::PL; ++q) {
-                    const half8_t bv = as_half8(make_uint4(bw[q][0], bw[q][1], bw[q][2], bw[q][3]));
-                    vacc[k * C::PL + q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, bv, vacc[k * C::PL + q], 0, 0, 0);
+                for (int h = 0; h < C::VT; ++h) {
+                    const uint32_t sel = (h & 1) ? 0x07060302u : 0x05040100u;
+                    const uint4 bq = make_uint4(__builtin_amdgcn_perm(ent[1][h >> 1], ent[0][h >> 1], sel),
+                                                __builtin_amdgcn_perm(ent[3][h >> 1], ent[2][h >> 1], sel),
+                                                __builtin_amdgcn_perm(ent[5][h >> 1], ent[4][h >> 1], sel),
+                                                __builtin_amdgcn_perm(ent[7][h >> 1], ent[6][h >> 1], sel));
+                    const int nb = k * C::VT + h;
+                    vacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(bq), vacc[nb], 0, 0, 0);
                 }
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        t0 += 64 * C::NW;
     }
 
-    // block merge of the four waves (V sums back to true units)
-    const float wunit = ldexpf(1.0f, wexp_prev - 15);
+    // block merge of the waves (V sums back to true units)
+    const float wunit = ldexpf(1.0f, vref - 15 + (int)kTauLog2);
     float l_head = l_lane + xor_lane<16>(l_lane);
     l_head += xor_lane<32>(l_head);
     __syncthreads();
-    float* mrg = reinterpret_cast<float*>(uni);  // [4][G][D + 2]
+    float* mrg = reinterpret_cast<float*>(smem);  // [NW][G][D + 2]
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const float mh = bcast_lane(m_run, h);
+        const float mh = bcast_lane(m_ref, h);
         const float lh = bcast_lane(l_head, h);
         if (lane == 0) {
             mrg[(wave * G + h) * (D + 2)] = mh;
@@ -588,14 +666,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WA
     __syncthreads();
     float* part = a.part + (((int64_t)b * a.hq + h0) * a.splits + split) * (D + 2);
     const int64_t hstride = (int64_t)a.splits * (D + 2);
-    for (int e = tid; e < G * (D + 2); e += 256) {
+    for (int e = tid; e < G * (D + 2); e += C::NT) {
         const int h = e / (D + 2), i = e - h * (D + 2);
-        float mw[4], mx = -INFINITY;
+        float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            mw[w] = mrg[(w * G + h) * (D + 2)];
-            mx = fmaxf(mx, mw[w]);
-        }
+        for (int w = 0; w < C::NW; ++w) mx = fmaxf(mx, mrg[(w * G + h) * (D + 2)]);
         float val;
         if (i == 0) {
             val = mx;
@@ -604,7 +679,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ_SPLIT_WA
         } else {
             val = 0.0f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) val = fmaf(mrg[(w * G + h) * (D + 2) + i], exp2f(mw[w] - mx), val);
+            for (int w = 0; w < C::NW; ++w) {
+                const float mw = mrg[(w * G + h) * (D + 2)];
+                val = fmaf(mrg[(w * G + h) * (D + 2) + i], exp2f(mw - mx), val);
+            }
         }
         part[h * hstride + i] = val;
     }
@@ -677,10 +755,20 @@ template <int D, int KB, int VB, int G>
 hipError_t launch_split(const AttnArgs& a, hipStream_t s) {
     dim3 grid(a.splits, a.hkv * a.chunks, a.batch);
     if (a.kc.qjl_m > 0)
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, G, true>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, G, true>), grid, dim3(64 * split_waves(D)), 0, s, a);
     else
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, G, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, G, false>), grid, dim3(64 * split_waves(D)), 0, s, a);
     return hipGetLastError();
+}
+
+// Resident split blocks per compute unit for one split-kernel variant.
+template <int D, int KB, int VB, int G>
+int split_blocks(bool qjl) {
+    int nb = 0;
+    const hipError_t e =
+        qjl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, G, true>, 64 * split_waves(D), 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, G, false>, 64 * split_waves(D), 0);
+    return e == hipSuccess && nb > 0 ? nb : 0;
 }
 
 template <int D, int KB, int VB>
@@ -697,6 +785,20 @@ hipError_t launch_split_g(const AttnArgs& a, hipStream_t s) {
     }
 }
 
+template <int D, int KB, int VB>
+int split_blocks_g(int G, bool qjl) {
+    switch (G) {
+        case 1: return split_blocks<D, KB, VB, 1>(qjl);
+        case 2: return split_blocks<D, KB, VB, 2>(qjl);
+        case 3: return split_blocks<D, KB, VB, 3>(qjl);
+        case 4: return split_blocks<D, KB, VB, 4>(qjl);
+        case 5: return split_blocks<D, KB, VB, 5>(qjl);
+        case 6: return split_blocks<D, KB, VB, 6>(qjl);
+        case 7: return split_blocks<D, KB, VB, 7>(qjl);
+        default: return split_blocks<D, KB, VB, 8>(qjl);
+    }
+}
+
 template <int D, int KB>
 hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s) {
     switch (a.vc.bits) {
@@ -707,10 +809,22 @@ hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s) {
     }
 }
 
+template <int D, int KB>
+int split_blocks_dk(int vb, int G, bool qjl) {
+    switch (vb) {
+        case 1: return split_blocks_g<D, KB, 1>(G, qjl);
+        case 2: return split_blocks_g<D, KB, 2>(G, qjl);
+        case 3: return split_blocks_g<D, KB, 3>(G, qjl);
+        default: return split_blocks_g<D, KB, 4>(G, qjl);
+    }
+}
+
 }  // namespace attn
 
-// One explicit instantiation per (D, KB) lives in its own translation unit.
+// One explicit specialization per (D, KB) lives in its own translation unit.
 template <int D, int KB>
 hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s);
+template <int D, int KB>
+int split_blocks_dk(int vb, int G, bool qjl);
 
 }  // namespace tqi

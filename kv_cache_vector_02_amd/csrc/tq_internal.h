@@ -72,8 +72,12 @@ hipError_t launch_encode(const EncodeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 enum AttnStage { ATTN_PREPARE = 1, ATTN_SCAN = 2, ATTN_COMBINE = 4, ATTN_ALL = 7 };
 hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s);
-void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t* split_tokens,
-               int* heads_per_chunk);
+void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int d, int kb, int vb, bool qjl, int* splits,
+               int64_t* split_tokens, int* heads_per_chunk);
+template <int D, int KB>
+hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s);
+template <int D, int KB>
+int split_blocks_dk(int vb, int G, bool qjl);
 size_t attn_workspace(int batch, int hq, int d, int m, int splits);
 
 struct SearchArgs {
