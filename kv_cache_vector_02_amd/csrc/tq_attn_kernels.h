@@ -431,39 +431,32 @@ void split_kernel(AttnArgs a) {
     const int pbit = C::PIECE * n;   // this lane's V field inside a row
     const int pw0 = pbit >> 5, psh = pbit & 31;
 
-    while (t0 < t_end) {
-        const int rem = t_end - t0;  // tokens left in this split (> 0)
-        const bool lane_valid = lane < rem;
-        // ---- stage V codes and norms of this tile (lane <-> token)
-#pragma unroll
-        for (int w = 0; w < C::VTW; ++w) vt[w * C::VSTR + lane] = rv[w];
-        const float vnf = half_bits_to_float(rn >> 16);
-        knq[lane] = half_bits_to_float(rn & 0xFFFFu) * qinv;
-        if constexpr (QJL) gml[lane] = half_bits_to_float(rg);
-        float vfac = 1.0f;
-        bool pend = false;
-        if (__builtin_amdgcn_ballot_w64(lane_valid && vnf >= vlim)) {
-            // a V norm at or above the reference: raise it (rare)
-            const float vm = wave_max(lane_valid ? vnf : 0.0f);
-            int e;
-            frexpf(vm, &e);
-            const int vnew = e + kVHeadroom;
-            vfac = ldexpf(1.0f, vref - vnew);
-            vref = vnew;
-            vlim = ldexpf(1.0f, vref);
-            vsc = ldexpf(1.0f, 15 - (int)kTauLog2 - vref);
-            pend = true;
-        }
-        vnl[lane] = vnf * vsc;
-        // ---- next tile's loads (clamped; skipped past the end of the split)
-        const int tn = t0 + 64 * C::NW;
-        if (tn < t_end) fetch_v<C, QJL>(rv, rn, rg, vcodes, knb, vnb, gmb, (uint32_t)tn, last, lane);
+    // Software pipeline over this wave's tiles: iteration i stages tile i, runs
+    // its K scores on the matrix cores in the same basic block as the V sums of
+    // tile i-1 (so the matrix-core and VALU/LDS work of the two overlap), then
+    // exponentiates tile i.  Every stage below is inlined at each use.
+    auto wave_sync = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // ---- K scores on matrix cores: 4 sub-tiles of 16 tokens
-        floatx4_t sacc[4];
+    };
+    // stage tile t0 (lane <-> token) and prefetch the next tile's V row and norms
+    auto stage = [&](float& vnf) __attribute__((always_inline)) -> bool {
+        const int rem = t_end - t0;
+        const bool lane_valid = lane < rem;
+#pragma unroll
+        for (int w = 0; w < C::VTW; ++w) vt[w * C::VSTR + lane] = rv[w];
+        vnf = half_bits_to_float(rn >> 16);
+        knq[lane] = half_bits_to_float(rn & 0xFFFFu) * qinv;
+        if constexpr (QJL) gml[lane] = half_bits_to_float(rg);
+        vnl[lane] = vnf * vsc;
+        // prefetch (clamped to the split: past its end this re-reads the last token)
+        fetch_v<C, QJL>(rv, rn, rg, vcodes, knb, vnb, gmb, (uint32_t)(t0 + 64 * C::NW), last, lane);
+        // a V norm at or above the reference is handled by the rare rescale
+        return __builtin_amdgcn_ballot_w64(lane_valid && vnf >= vlim) != 0;
+    };
+    // K scores of tile t0 (16 tokens x 16 heads per sub-tile), then prefetch the next tile's K codes
+    auto kphase = [&](floatx4_t (&sacc)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) sacc[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -492,7 +485,7 @@ void split_kernel(AttnArgs a) {
                 sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, qhi[ks], sacc[j], 0, 0, 0);
             }
         }
-        if (tn < t_end) fetch_k<C>(rk, kcodes, (uint32_t)tn, last, n, grp);
+        fetch_k<C>(rk, kcodes, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
         if constexpr (QJL) {
             // A = 16*gamma*(+-1) of token 16j + n (exact in half); same accumulators
             const int gbytes = m >> 5;
@@ -508,7 +501,13 @@ void split_kernel(AttnArgs a) {
                 }
             }
         }
-        // ---- scores of tokens 16j + 4grp + v for head n, relative to the reference max
+    };
+    // scores of tile t0 relative to the reference max, the rare rescale, and the
+    // V-side A operands: half weights p * |v| * 2^wsh (K order: sub-tile pairs
+    // (2 s2, 2 s2 + 1), tokens 4grp + v), row = head n
+    auto softmax = [&](const floatx4_t (&sacc)[4], bool vraise, float vnf, uint32_t (&wa)[2][4])
+        __attribute__((always_inline)) {
+        const int rem = t_end - t0;
         float dsc[4][4];
         float lmax = -INFINITY;
 #pragma unroll
@@ -519,8 +518,10 @@ void split_kernel(AttnArgs a) {
             dsc[j][2] = fmaf(sacc[j][2], kq.z, -m_ref);
             dsc[j][3] = fmaf(sacc[j][3], kq.w, -m_ref);
         }
-        const int lim = rem - 4 * grp;  // token 16j + 4grp + v is valid iff 16j + v < lim
+        int lim = rem - 4 * grp;  // token 16j + 4grp + v is valid iff 16j + v < lim
         if (rem < 64) {
+            // keeps the compares inside this (last-tile) branch
+            asm volatile("" : "+v"(lim));
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -531,17 +532,30 @@ void split_kernel(AttnArgs a) {
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) lmax = fmaxf(lmax, dsc[j][v]);
-        if (__builtin_amdgcn_ballot_w64(lmax > kTauLog2) || pend) {
-            // raise the reference max of every head to its tile max (rare)
-            float s[4][4], tmax = -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(lmax > kTauLog2) || vraise) {
+            // rare: raise the V-norm reference and/or the reference max of every
+            // head (to its tile max), rescaling the running sums
+            float vfac = 1.0f;
+            if (vraise) {
+                const float vm = wave_max(lane < rem ? vnf : 0.0f);
+                int e;
+                frexpf(vm, &e);
+                const int vnew = e + kVHeadroom;
+                vfac = ldexpf(1.0f, vref - vnew);
+                vref = vnew;
+                vlim = ldexpf(1.0f, vref);
+                vsc = ldexpf(1.0f, 15 - (int)kTauLog2 - vref);
+                vnl[lane] = vnf * vsc;
+            }
+            float sv[4][4], tmax = -INFINITY;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float4 kq = *reinterpret_cast<const float4*>(knq + 16 * j + 4 * grp);
                 const float kv[4] = {kq.x, kq.y, kq.z, kq.w};
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    s[j][v] = (16 * j + v < lim) ? sacc[j][v] * kv[v] : -INFINITY;
-                    tmax = fmaxf(tmax, s[j][v]);
+                    sv[j][v] = (16 * j + v < lim) ? sacc[j][v] * kv[v] : -INFINITY;
+                    tmax = fmaxf(tmax, sv[j][v]);
                 }
             }
             tmax = fmaxf(tmax, xor_lane<16>(tmax));
@@ -553,11 +567,9 @@ void split_kernel(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) dsc[j][v] = s[j][v] - mnew;
+                for (int v = 0; v < 4; ++v) dsc[j][v] = sv[j][v] - mnew;
             if (grp == 0) hfac[n] = alpha * vfac;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            wave_sync();
             const float4 f4 = *reinterpret_cast<const float4*>(hfac + 4 * grp);
 #pragma unroll
             for (int q = 0; q < C::NB; ++q) {
@@ -567,9 +579,6 @@ void split_kernel(AttnArgs a) {
                 vacc[q][3] *= f4.w;
             }
         }
-        // ---- V-side A operands: half weights p * |v| * 2^wsh (K order: sub-tile
-        // pairs (2 s2, 2 s2 + 1), tokens 4grp + v), row = head n
-        uint32_t wa[2][4];
         float psum = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -581,30 +590,48 @@ void split_kernel(AttnArgs a) {
             wa[j >> 1][2 * (j & 1) + 1] = pack_half2(p2 * vq.z, p3 * vq.w);
         }
         l_lane += psum;
-
-        // ---- V sums on matrix cores
+    };
+    // this lane's PIECE-bit field of the staged tile's tokens e = 4 jj + v (token
+    // 32 s2 + 16 jj + 4 grp + v): fields of PK consecutive tokens share one word
+    // when PIECE <= 16; otherwise pc holds the low 32 bits and ph the rest
+    constexpr int PK = C::PIECE == 16 ? 2 : (C::PIECE == 8 ? 4 : 1);
+    const uint32_t psel = C::PIECE == 16 ? (psh ? 0x07060302u : 0x05040100u)
+                                         : (0x0C0C0400u | (uint32_t)(psh >> 3) | ((uint32_t)(4 + (psh >> 3)) << 8));
+    auto vread = [&](uint32_t (&pc)[2][8], uint32_t (&ph)[2][8]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            // this lane's PIECE-bit field of its 8 tokens (e = 4 jj + v)
-            uint32_t pc[8], ph[8];
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const int tok = 32 * s2 + 16 * jj + 4 * grp;
                 const uint4 x = *reinterpret_cast<const uint4*>(vt + pw0 * C::VSTR + tok);
                 const uint32_t lo[4] = {x.x, x.y, x.z, x.w};
-                if constexpr (C::PIECE <= 32 && 32 % C::PIECE == 0) {
+                if constexpr (PK == 2) {
+                    // the lane's halves of tokens (v, v + 1) side by side
+                    pc[s2][2 * jj] = __builtin_amdgcn_perm(lo[1], lo[0], psel);
+                    pc[s2][2 * jj + 1] = __builtin_amdgcn_perm(lo[3], lo[2], psel);
+                } else if constexpr (PK == 4) {
+                    // the lane's bytes of tokens v = 0..3
+                    pc[s2][jj] = __builtin_amdgcn_perm(lo[1], lo[0], psel) |
+                                 (__builtin_amdgcn_perm(lo[3], lo[2], psel) << 16);
+                } else if constexpr (C::PIECE <= 32 && 32 % C::PIECE == 0) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) pc[4 * jj + v] = lo[v] >> psh;
+                    for (int v = 0; v < 4; ++v) pc[s2][4 * jj + v] = lo[v] >> psh;
                 } else {
                     const uint4 y = *reinterpret_cast<const uint4*>(vt + (pw0 + 1) * C::VSTR + tok);
                     const uint32_t hi[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        pc[4 * jj + v] = __builtin_amdgcn_alignbit(hi[v], lo[v], psh);
-                        ph[4 * jj + v] = hi[v] >> psh;  // psh < 32; only read when PIECE > 32
+                        pc[s2][4 * jj + v] = __builtin_amdgcn_alignbit(hi[v], lo[v], psh);
+                        ph[s2][4 * jj + v] = hi[v] >> psh;  // psh < 32; only read when PIECE > 32
                     }
                 }
             }
+    };
+    // V sums of one tile on matrix cores from its pieces and weights
+    auto vphase = [&](const uint32_t (&pc)[2][8], const uint32_t (&ph)[2][8], const uint32_t (&wa)[2][4])
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
             const half8_t aw = as_half8(make_uint4(wa[s2][0], wa[s2][1], wa[s2][2], wa[s2][3]));
 #pragma unroll
             for (int k = 0; k < C::VLK; ++k) {
@@ -613,10 +640,12 @@ void split_kernel(AttnArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     uint32_t idx;
-                    if constexpr (C::PIECE <= 32) {
-                        idx = (pc[e] >> bit) & ((1u << C::VLB) - 1u);
+                    if constexpr (PK > 1) {
+                        idx = (pc[s2][e / PK] >> ((e % PK) * C::PIECE + bit)) & ((1u << C::VLB) - 1u);
+                    } else if constexpr (C::PIECE <= 32) {
+                        idx = (pc[s2][e] >> bit) & ((1u << C::VLB) - 1u);
                     } else {
-                        const uint64_t x = ((uint64_t)ph[e] << 32) | pc[e];
+                        const uint64_t x = ((uint64_t)ph[s2][e] << 32) | pc[s2][e];
                         idx = (uint32_t)(x >> bit) & ((1u << C::VLB) - 1u);
                     }
                     lds_read<C::VENTW>(ent[e], vtab + idx * C::VROW + voff);
@@ -633,10 +662,29 @@ void split_kernel(AttnArgs a) {
                 }
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    if (t0 < t_end) {
+        uint32_t wa[2][4], pc[2][8], ph[2][8];
+        floatx4_t sacc[4];
+        float vnf;
+        bool vraise = stage(vnf);
+        wave_sync();
+        kphase(sacc);
+        softmax(sacc, vraise, vnf, wa);
         t0 += 64 * C::NW;
+        while (t0 < t_end) {
+            vread(pc, ph);  // previous tile, before this tile overwrites the staging area
+            wave_sync();
+            vraise = stage(vnf);
+            wave_sync();
+            kphase(sacc);
+            vphase(pc, ph, wa);  // previous tile's V sums, before this tile's rescale
+            softmax(sacc, vraise, vnf, wa);
+            t0 += 64 * C::NW;
+        }
+        vread(pc, ph);
+        vphase(pc, ph, wa);
     }
 
     // block merge of the waves (V sums back to true units)
