@@ -101,15 +101,20 @@ __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
 // this MFMA lane l holds A[l%16][8(l/16) + e] and B[8(l/16) + e][l%16]
 // (e = 0..7) and receives D[4(l/16) + i][l%16] (i = 0..3).
 //
-// Scores, per 16-token sub-tile j: D[token][head] = sum_dim C_K[token][dim]
-// Q[dim][head].  Lane (n, grp) = (l%16, l/16) takes the K codes of token 16j + n
-// straight from memory, dims grp*d/4 + [0, d/4) (one contiguous load), and in K
-// step ks the dims grp*d/4 + 8ks + e.  Float32 accuracy comes from splitting
-// both operands into half hi + lo parts: c_hi q_hi + c_hi q_lo + c_lo q_hi (the
-// c_lo q_lo term is below float32 rounding).  The query chunk is scaled by one
-// power of two into [2^14, 2^15) and the centroids by 16, so every lo part is a
-// normal half; the scale is removed exactly on the float32 result.  Lane
-// (n, grp) then holds the scores of tokens 16j + 4grp + i for head n.
+// Scores, per 16-token sub-tile j: D[token][col] = sum_k A[token][k] B[k][col].
+// Lane (n, grp) = (l%16, l/16) takes the K codes of token 16j + n straight from
+// memory, dims grp*d/4 + [0, d/4) (one contiguous load); K step ks covers dims
+// grp*d/4 + 4ks + [0, 4).  Float32 accuracy comes from splitting both operands
+// into half hi + lo parts, folded into the two MFMA dimensions that have room:
+// the eight k slots of a lane hold c_hi and c_lo of its four dims, and columns
+// 0..7 hold q_hi of the (at most eight) query heads while columns 8..15 hold
+// q_lo, so that D[t][h] + D[t][h + 8] = sum_dim (c_hi + c_lo)(q_hi + q_lo) over
+// the centroid and query of every dim, a float32-exact product up to the
+// rounding of the accumulation.  The query chunk is scaled by one power of two
+// into [2^14, 2^15) and the centroids by 16 so every lo part is a normal half;
+// the scale is removed exactly on the float32 result.  After adding the two
+// column halves (a DPP row rotate), lane (n, grp) holds the scores of tokens
+// 16j + 4grp + i for head n % 8.
 //
 // V sums, per K step s2 of 32 tokens: D[head][col] = sum_token W[head][token]
 // C_V[token][dim(col)], with the softmax weights of the lane's own registers as
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
 // N-block nb standing for dim NB*n' + nb, so a lane's codes of one token are one
 // contiguous NB*VB-bit piece of the token's row.  Centroids come from an LDS
 // table indexed by VT codes of one token; v_perm pairs the halves of two tokens
-// into one B dword.
+// into one B dword.  Rows 8..15 repeat heads 0..7 and are not used.
 //
 // Softmax: the log2-domain scores are exponentiated against a reference max
 // that is only raised when a score exceeds it by more than 2^kTauLog2 (lazy
@@ -139,18 +144,19 @@ constexpr int split_waves(int d) { return d == 128 ? 12 : 8; }
 
 template <int D, int KB, int VB, int G, bool QJL>
 struct Cfg {
+    static_assert(G >= 1 && G <= 8, "at most eight query heads per block");
     static constexpr int NW = split_waves(D);       // waves per block
     static constexpr int NT = 64 * NW;              // threads per block
     // K side
     static constexpr int RBK = D * KB / 8;          // K code bytes per token
     static constexpr int DG = D / 4;                // dims per lane group
-    static constexpr int KSTEPS = DG / 8;           // MFMA K steps (32 dims each)
+    static constexpr int KSTEPS = DG / 4;           // MFMA K steps (4 dims per lane each)
     static constexpr int GB = DG * KB / 8;          // K code bytes per lane group per token
     static constexpr int GW = GB / 4;               // ... in dwords
-    static constexpr int KLU = (KB == 3) ? 6 : 8;   // bits per K table lookup
-    static constexpr int KCPL = KLU / KB;           // codes per lookup
-    static constexpr int LPS = 8 / KCPL;            // lookups per K step
-    static constexpr int KHB = 2 * KCPL;            // bytes per hi (or lo) entry
+    static constexpr int KE = KB >= 3 ? 2 : 4;      // codes per K lookup
+    static constexpr int KLU = KE * KB;             // K index bits
+    static constexpr int KENT = 4 * KE;             // bytes per K entry: hi halves then lo halves
+    static constexpr int LPS = 4 / KE;              // K lookups per step
     // V side
     static constexpr int RBV = D * VB / 8;          // V code bytes per token
     static constexpr int VTW = RBV / 4;             // dwords per V row
@@ -161,37 +167,24 @@ struct Cfg {
     static constexpr int VENT = 2 * VT;             // bytes per V entry
     static constexpr int VENTW = VENT / 4;          // ... in dwords
     static constexpr int VLK = NB / VT;             // V lookups per token
+    // Bank-sliced table: 256-byte rows; row u holds the K entry of index u once
+    // per K slice in its first 128 bytes and the V entry of index u once per V
+    // slice in its last 128 bytes.  Lane l reads slice l % (128 / entry size),
+    // so the lanes of one LDS pass touch distinct banks whatever their indices,
+    // and a row offset is one byte permute of an 8-bit index.
+    static constexpr int KSL = 128 / KENT;          // K slices
+    static constexpr int VSL = 128 / VENT;          // V slices
+    static constexpr int ROWS = (1 << KLU) > (1 << VLB) ? (1 << KLU) : (1 << VLB);
+    static constexpr int TABB = ROWS * 256;
     // per wave: V tile dword-major [VTW + 1][VSTR] (last row zero; VSTR pads the
     // rows across banks), head factors [16], K norm * query scale [64], scaled
     // V norm [64], QJL gamma [64]
     static constexpr int VSTR = 68;
     static constexpr int WAVE_DW = (VTW + 1) * VSTR + 16 + 3 * 64;
-    static constexpr int QJL_DW = QJL ? 8 * 64 * 8 + 256 * 4 : 0;  // QJL B operands + sign table
-    // Bank-sliced tables: the hi entries of K table row u sit in the first half
-    // of a KROW-byte row at u*KROW, one copy per slice; lane l reads slice
-    // l % (KROW / 2 / KHB), so the lanes of one LDS pass touch distinct banks
-    // whatever their indices.  The lo entries of row u sit in the second half of
-    // row u + KLO_SHIFT: that offset is neither below 1 KiB nor a multiple of
-    // 256 bytes, so the hi and lo reads stay two instructions with their results
-    // in place (a merged pair read would need register moves).  The V table is
-    // sliced the same way with VROW bytes per row.
-    static constexpr int FIXED_B = 4 * (NW * WAVE_DW + QJL_DW);
-    static constexpr int LDS_CAP = 160 * 1024 - 1024;
-    static constexpr int KLO_SHIFT = 5;
-    static constexpr bool fits(int kr, int vr) {
-        return ((1 << KLU) + KLO_SHIFT) * kr + (1 << VLB) * vr + FIXED_B <= LDS_CAP;
-    }
-    static constexpr int KROW = fits(256, 128) ? 256 : fits(256, 64) ? 256 : fits(128, 64) ? 128 : 64;
-    static constexpr int VROW = fits(KROW, 128) ? 128 : fits(KROW, 64) ? 64 : 32;
-    static constexpr int KSL = KROW / 2 / KHB;      // K slices
-    static constexpr int VSL = VROW / VENT;         // V slices
-    static constexpr int KLO = KLO_SHIFT * KROW + KROW / 2;  // lo entry offset from its hi entry
-    static constexpr int KTABB = ((1 << KLU) + KLO_SHIFT) * KROW;
-    static constexpr int VTABB = (1 << VLB) * VROW;
-    static constexpr int LOOP_DW = KTABB / 4 + VTABB / 4 + NW * WAVE_DW + QJL_DW;
+    static constexpr int QJL_DW = QJL ? 8 * 64 * 4 + 256 * 4 : 0;  // QJL B operands + sign table
+    static constexpr int LOOP_DW = TABB / 4 + NW * WAVE_DW + QJL_DW;
     static constexpr int MERGE_DW = NW * G * (D + 2);
     static constexpr int SMEM_DW = LOOP_DW > MERGE_DW ? LOOP_DW : MERGE_DW;
-    static_assert(KSL >= 1 && VSL >= 1, "table rows too small");
     static_assert(4 * SMEM_DW <= 160 * 1024, "split kernel exceeds LDS");
 };
 
@@ -290,11 +283,10 @@ __global__ __launch_bounds__(64 * split_waves(D)) __attribute__((amdgpu_waves_pe
 void split_kernel(AttnArgs a) {
     using C = Cfg<D, KB, VB, G, QJL>;
     __shared__ __attribute__((aligned(16))) uint32_t smem[C::SMEM_DW];
-    uint8_t* ktab = reinterpret_cast<uint8_t*>(smem);
-    uint8_t* vtab = reinterpret_cast<uint8_t*>(smem + C::KTABB / 4);
-    uint32_t* waves_lds = smem + C::KTABB / 4 + C::VTABB / 4;
+    uint8_t* tab = reinterpret_cast<uint8_t*>(smem);
+    uint32_t* waves_lds = smem + C::TABB / 4;
     uint4* qjlb = reinterpret_cast<uint4*>(waves_lds + C::NW * C::WAVE_DW);
-    uint4* sigt = qjlb + 8 * 64 * 2;
+    uint4* sigt = qjlb + 8 * 64;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, grp = lane >> 4;
@@ -327,54 +319,72 @@ void split_kernel(AttnArgs a) {
         fetch_v<C, QJL>(rv, rn, rg, vcodes, knb, vnb, gmb, (uint32_t)t0, last, lane);
     }
 
-    // K table: row u, slice sl -> hi halves of 16*c_K of the KCPL codes of u at
-    // u*KROW + sl*KHB, lo halves KLO bytes further
-    for (int i = tid; i < (1 << C::KLU) * C::KSL; i += C::NT) {
-        const int u = i / C::KSL, sl = i - u * C::KSL;
-        _Float16* eh = reinterpret_cast<_Float16*>(ktab + u * C::KROW + sl * C::KHB);
-        _Float16* el = reinterpret_cast<_Float16*>(ktab + u * C::KROW + C::KLO + sl * C::KHB);
+    // centroids once into LDS, then every table row is written as 16-byte
+    // chunks that repeat one entry (one chunk covers 16 / entry-size slices)
+    __shared__ float cent[32];  // [0, 16): 16 * c_K, [16, 32): c_V
+    if (tid < (1 << KB)) cent[tid] = 16.0f * a.kc.centroid[tid];
+    if (tid >= 16 && tid < 16 + (1 << VB)) cent[tid] = a.vc.centroid[tid - 16];
+    __syncthreads();
+    for (int i = tid; i < C::ROWS * 16; i += C::NT) {
+        // row u, 16-byte chunk c: chunks 0..7 repeat the K entry of u, 8..15 the V entry
+        const int u = i >> 4, c = i & 15;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};  // one entry (K: hi halves then lo halves; V: halves)
+        bool live;
+        if (c < 8) {
+            live = u < (1 << C::KLU);
 #pragma unroll
-        for (int p = 0; p < C::KCPL; ++p) {
-            const float c = 16.0f * a.kc.centroid[(u >> (KB * p)) & ((1 << KB) - 1)];
-            const _Float16 hi = (_Float16)c;
-            eh[p] = hi;
-            el[p] = (_Float16)(c - (float)hi);
+            for (int p = 0; p < C::KE; p += 2) {
+                const float c0 = cent[(u >> (KB * p)) & ((1 << KB) - 1)];
+                const float c1 = cent[(u >> (KB * (p + 1))) & ((1 << KB) - 1)];
+                const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+                w[p / 2] = pack_half2((float)h0, (float)h1);
+                w[C::KE / 2 + p / 2] = pack_half2(c0 - (float)h0, c1 - (float)h1);
+            }
+        } else {
+            live = u < (1 << C::VLB);
+#pragma unroll
+            for (int p = 0; p < C::VT; p += 2)
+                w[p / 2] = pack_half2(cent[16 + ((u >> (VB * p)) & ((1 << VB) - 1))],
+                                      cent[16 + ((u >> (VB * (p + 1))) & ((1 << VB) - 1))]);
         }
-    }
-    // V table: row u, slice sl -> half c_V of the VT codes of u (code p = bits [VB p, VB p + VB))
-    for (int i = tid; i < (1 << C::VLB) * C::VSL; i += C::NT) {
-        const int u = i / C::VSL, sl = i - u * C::VSL;
-        _Float16* e = reinterpret_cast<_Float16*>(vtab + u * C::VROW + sl * C::VENT);
-#pragma unroll
-        for (int p = 0; p < C::VT; ++p) e[p] = (_Float16)a.vc.centroid[(u >> (VB * p)) & ((1 << VB) - 1)];
+        const int eb = c < 8 ? C::KENT : C::VENT;  // entry bytes
+        uint4 v;
+        if (eb == 4) v = make_uint4(w[0], w[0], w[0], w[0]);
+        else if (eb == 8) v = make_uint4(w[0], w[1], w[0], w[1]);
+        else v = make_uint4(w[0], w[1], w[2], w[3]);
+        if (live) *reinterpret_cast<uint4*>(tab + u * 256 + 16 * c) = v;
     }
     if constexpr (QJL) {
         _Float16* st = reinterpret_cast<_Float16*>(sigt);
         for (int e = tid; e < 256 * 8; e += C::NT) st[e] = ((e >> 3) >> (e & 7)) & 1 ? (_Float16)1.0f : (_Float16)(-1.0f);
     }
 
-    // K-side B operands: rotated query (and QJL projection) of head n, all G
-    // heads scaled by one power of two; zero for n >= G
+    // K-side B operands: column n holds q_hi (n < 8) or q_lo (n >= 8) of head
+    // n % 8 (zero beyond G), all heads scaled by one power of two, with the dims
+    // of K step ks in the order of the A entries (KE = 2: d0 d1 d0 d1 d2 d3 d2 d3;
+    // KE = 4: d0 d1 d2 d3 d0 d1 d2 d3); likewise the QJL projection
     const float* qrot = a.qrot + ((int64_t)b * a.hq + h0) * D;  // [dim][G] inside this chunk
-    half8_t qhi[C::KSTEPS], qlo[C::KSTEPS];
+    const int hh = n & 7;
+    const bool lo_col = n >= 8, head_ok = hh < G;
+    half8_t bq[C::KSTEPS];
     float qinv;
     {
-        float qv[C::KSTEPS][8];
+        float qv[C::KSTEPS][4];
         float amax = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int dim = grp * C::DG + 8 * ks + j;
-                const float x = qrot[dim * G + (n < G ? n : G - 1)];
-                qv[ks][j] = n < G ? x : 0.0f;
-                amax = fmaxf(amax, fabsf(qv[ks][j]));
+            for (int i = 0; i < 4; ++i) {
+                const int dim = grp * C::DG + 4 * ks + i;
+                const float x = qrot[dim * G + (head_ok ? hh : 0)];
+                qv[ks][i] = head_ok ? x : 0.0f;
+                amax = fmaxf(amax, fabsf(qv[ks][i]));
             }
         const float* qp = a.qproj + ((int64_t)b * a.hq + h0) * m;
         if constexpr (QJL) {
             for (int ks = 0; ks < (m >> 5); ++ks)
                 for (int j = 0; j < 8; ++j)
-                    amax = fmaxf(amax, n < G ? fabsf(qp[n * m + grp * (m >> 2) + 8 * ks + j]) : 0.0f);
+                    amax = fmaxf(amax, head_ok ? fabsf(qp[hh * m + grp * (m >> 2) + 8 * ks + j]) : 0.0f);
         }
         amax = wave_max(amax);
         float sc = 1.0f;
@@ -385,27 +395,28 @@ void split_kernel(AttnArgs a) {
         }
         qinv = 1.0f / (16.0f * sc);
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks)
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+            _Float16 x[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float v = qv[ks][j] * sc;
+            for (int i = 0; i < 4; ++i) {
+                const float v = qv[ks][i] * sc;
                 const _Float16 hi = (_Float16)v;
-                qhi[ks][j] = hi;
-                qlo[ks][j] = (_Float16)(v - (float)hi);
+                x[i] = lo_col ? (_Float16)(v - (float)hi) : hi;
             }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bq[ks][e] = C::KE == 2 ? x[(e >> 2) * 2 + (e & 1)] : x[e & 3];
+        }
         if constexpr (QJL) {
             if (wave == 0) {
                 for (int ks = 0; ks < (m >> 5); ++ks) {
-                    half8_t hi8, lo8;
+                    half8_t x8;
                     for (int j = 0; j < 8; ++j) {
                         // the sign operand carries 16*gamma, so scale by sc only
-                        const float v = (n < G ? qp[n * m + grp * (m >> 2) + 8 * ks + j] : 0.0f) * sc;
+                        const float v = (head_ok ? qp[hh * m + grp * (m >> 2) + 8 * ks + j] : 0.0f) * sc;
                         const _Float16 hi = (_Float16)v;
-                        hi8[j] = hi;
-                        lo8[j] = (_Float16)(v - (float)hi);
+                        x8[j] = lo_col ? (_Float16)(v - (float)hi) : hi;
                     }
-                    qjlb[(ks * 64 + lane) * 2] = __builtin_bit_cast(uint4, hi8);
-                    qjlb[(ks * 64 + lane) * 2 + 1] = __builtin_bit_cast(uint4, lo8);
+                    qjlb[ks * 64 + lane] = __builtin_bit_cast(uint4, x8);
                 }
             }
         }
@@ -418,8 +429,8 @@ void split_kernel(AttnArgs a) {
     vt[C::VTW * C::VSTR + lane] = 0u;
     __syncthreads();
     // this lane's table slices (byte offsets inside a row)
-    const uint32_t koff = (uint32_t)(lane % C::KSL) * C::KHB;
-    const uint32_t voff = (uint32_t)(lane % C::VSL) * C::VENT;
+    const uint32_t koff = (uint32_t)(lane % C::KSL) * C::KENT;
+    const uint32_t voff = 128u + (uint32_t)(lane % C::VSL) * C::VENT;
 
     float m_ref = -INFINITY, l_lane = 0.0f;  // head n's reference max / this lane's partial sum
     // V sums D[nb][i]: head 4*grp + i, dim NB*n + nb, in units of 2^wsh
@@ -455,7 +466,7 @@ void split_kernel(AttnArgs a) {
         // a V norm at or above the reference is handled by the rare rescale
         return __builtin_amdgcn_ballot_w64(lane_valid && vnf >= vlim) != 0;
     };
-    // K scores of tile t0 (16 tokens x 16 heads per sub-tile), then prefetch the next tile's K codes
+    // K scores of tile t0 (16 tokens x 16 columns per sub-tile), then prefetch the next tile's K codes
     auto kphase = [&](floatx4_t (&sacc)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) sacc[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -463,26 +474,22 @@ void split_kernel(AttnArgs a) {
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int ks = 0; ks < C::KSTEPS; ++ks) {
-                uint32_t hw[4], lw[4];
+                uint32_t aw[4];
 #pragma unroll
                 for (int u = 0; u < C::LPS; ++u) {
-                    const int bit = ks * 8 * KB + u * C::KLU;
+                    const int bit = (4 * ks + u * C::KE) * KB;
                     uint32_t addr;
-                    if constexpr (C::KLU == 8 && C::KROW == 256) {
-                        // row byte offset = field * 256 + koff: one byte permute
+                    if constexpr (C::KLU == 8) {
+                        // row offset = index * 256 + koff: one byte permute
                         const uint32_t w = rk[j * C::GW + (bit >> 5)];
                         addr = __builtin_amdgcn_perm(w, koff, 0x0C0C0000u | ((uint32_t)(4 + ((bit >> 3) & 3)) << 8));
                     } else {
-                        addr = field_at<C::KLU>(rk + j * C::GW, bit) * C::KROW + koff;
+                        addr = field_at<C::KLU>(rk + j * C::GW, bit) * 256u + koff;
                     }
-                    lds_read<C::KHB / 4>(hw + u * (C::KHB / 4), ktab + addr);
-                    lds_read<C::KHB / 4>(lw + u * (C::KHB / 4), ktab + addr + C::KLO);
+                    lds_read<C::KENT / 4>(aw + u * (C::KENT / 4), tab + addr);
                 }
-                const half8_t ahi = as_half8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-                const half8_t alo = as_half8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-                sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, qhi[ks], sacc[j], 0, 0, 0);
-                sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, qlo[ks], sacc[j], 0, 0, 0);
-                sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, qhi[ks], sacc[j], 0, 0, 0);
+                sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(make_uint4(aw[0], aw[1], aw[2], aw[3])),
+                                                                 bq[ks], sacc[j], 0, 0, 0);
             }
         }
         fetch_k<C>(rk, kcodes, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
@@ -496,11 +503,15 @@ void split_kernel(AttnArgs a) {
                 const uint8_t* sp = a.k_qjl + (kvrow + t) * (m >> 3) + grp * gbytes;
                 for (int ks = 0; ks < (m >> 5); ++ks) {
                     const half8_t asg = as_half8(sigt[sp[ks]]) * g16;
-                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asg, as_half8(qjlb[(ks * 64 + lane) * 2]), sacc[j], 0, 0, 0);
-                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asg, as_half8(qjlb[(ks * 64 + lane) * 2 + 1]), sacc[j], 0, 0, 0);
+                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asg, as_half8(qjlb[ks * 64 + lane]), sacc[j], 0, 0, 0);
                 }
             }
         }
+        // column h + 8 holds the q_lo part of head h: add the two halves of each row
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sacc[j][v] += xor_lane<8>(sacc[j][v]);
     };
     // scores of tile t0 relative to the reference max, the rare rescale, and the
     // V-side A operands: half weights p * |v| * 2^wsh (K order: sub-tile pairs
@@ -639,16 +650,25 @@ void split_kernel(AttnArgs a) {
                 uint32_t ent[8][C::VENTW];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    uint32_t idx;
-                    if constexpr (PK > 1) {
-                        idx = (pc[s2][e / PK] >> ((e % PK) * C::PIECE + bit)) & ((1u << C::VLB) - 1u);
-                    } else if constexpr (C::PIECE <= 32) {
-                        idx = (pc[s2][e] >> bit) & ((1u << C::VLB) - 1u);
+                    uint32_t addr;
+                    if constexpr (C::VLB == 8) {
+                        // byte-aligned index: row offset = index * 256 + voff by one byte permute
+                        const int pos = (PK > 1 ? (e % PK) * C::PIECE : 0) + bit;  // bit position in its word
+                        const uint32_t w = PK > 1 ? pc[s2][e / PK] : (pos < 32 ? pc[s2][e] : ph[s2][e]);
+                        addr = __builtin_amdgcn_perm(w, voff, 0x0C0C0000u | ((uint32_t)(4 + ((pos >> 3) & 3)) << 8));
                     } else {
-                        const uint64_t x = ((uint64_t)ph[s2][e] << 32) | pc[s2][e];
-                        idx = (uint32_t)(x >> bit) & ((1u << C::VLB) - 1u);
+                        uint32_t idx;
+                        if constexpr (PK > 1) {
+                            idx = (pc[s2][e / PK] >> ((e % PK) * C::PIECE + bit)) & ((1u << C::VLB) - 1u);
+                        } else if constexpr (C::PIECE <= 32) {
+                            idx = (pc[s2][e] >> bit) & ((1u << C::VLB) - 1u);
+                        } else {
+                            const uint64_t x = ((uint64_t)ph[s2][e] << 32) | pc[s2][e];
+                            idx = (uint32_t)(x >> bit) & ((1u << C::VLB) - 1u);
+                        }
+                        addr = idx * 256u + voff;
                     }
-                    lds_read<C::VENTW>(ent[e], vtab + idx * C::VROW + voff);
+                    lds_read<C::VENTW>(ent[e], tab + addr);
                 }
 #pragma unroll
                 for (int h = 0; h < C::VT; ++h) {
