@@ -14,7 +14,10 @@ tokens, fp16, K 4-bit + V 2-bit per step, over a 1 GiB rotating input pool),
 long-context decode (8 kv heads x 2^20 tokens, K3/V3, 64 bf16 query heads) and
 inner-product search (2^20 x 256 database, 3-bit + QJL m=256, 1024 queries,
 top-10).  `roofline` is the scan kernel's algorithmic bytes per launch over its
-mean launch time measured with HIP events on the launch stream.
+mean launch time, measured with HIP events on the launch stream around
+back-to-back scan launches; `traffic` is the HBM bytes per scan launch from the
+committed FETCH_SIZE / WRITE_SIZE summary under profiles/ (null once the scan
+sources differ from the ones measured).
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same decode
 workload.  Inputs are synthetic and seeded (synth.py).
 
@@ -30,6 +33,11 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_scan_traffic_b16_h28x4_ctx32768_k4v2.txt")
+# sources of the scan kernel: a stored traffic measurement is used only while these are unchanged
+SCAN_SOURCES = ("kv_cache_vector_02_amd/csrc/tq_attn_kernels.h", "kv_cache_vector_02_amd/csrc/tq_attn.hip",
+                "kv_cache_vector_02_amd/csrc/tq_device.h", "kv_cache_vector_02_amd/csrc/tq_internal.h")
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (counts packed FMA)
 
 METRIC = "packed-KV decode attn GB/s & % HBM peak (1 GPU); tq_encode Mvectors/s"
@@ -52,6 +60,39 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def scan_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in SCAN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per scan launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary, each counter scaled by its reading on a copy of known size; None
+    when the summary is missing or the kernel sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if kv.get("scan_source_sha256") != scan_source_hash():
+            return None
+        fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["fetch_scale"])
+        write = float(kv["write_kib_per_dispatch"]) * 1024 * float(kv["write_scale"])
+    except (KeyError, ValueError, OSError):
+        return None
+    return {"bytes": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+            "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+
+
 def timed_loop(fn, steps, warmup, torch):
     """Runs fn(i) for warmup + steps iterations; returns ms per timed step."""
     for i in range(warmup):
@@ -65,6 +106,22 @@ def timed_loop(fn, steps, warmup, torch):
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
+
+
+def scan_launch_ms(tq, torch, args_of, launches):
+    """Mean duration of one tq_attn_scan launch: HIP events on the launch stream
+    around `launches` back-to-back scans (query prep done once before; the scan
+    is idempotent), so launch gaps overlap the previous kernel."""
+    tq.tq_attn_prepare(*args_of(0))
+    tq.tq_attn_scan(*args_of(0))
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(launches):
+        tq.tq_attn_scan(*args_of(i))
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / launches
 
 
 # ------------------------------------------------------------------ decode ----
@@ -90,20 +147,18 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
     out = torch.empty(B, Hq, d, device="cuda")
     ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, B, Hq, Hkv, ctx))
     scale = 1.0 / math.sqrt(d)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps + warmup)]
+    def args_of(i):
+        c = caches[i % replicas]
+        return (kc, vc, q, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], scale, out, ws)
 
     def step(i):
-        c = caches[i % replicas]
-        args = (kc, vc, q, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], scale, out, ws)
+        args = args_of(i)
         tq.tq_attn_prepare(*args)
-        ev[i][0].record()
         tq.tq_attn_scan(*args)
-        ev[i][1].record()
         tq.tq_attn_combine(*args)
 
     ms = timed_loop(step, steps, warmup, torch)
-    scan_ms = sum(ev[warmup + i][0].elapsed_time(ev[warmup + i][1]) for i in range(steps)) / steps
+    scan_ms = scan_launch_ms(tq, torch, args_of, steps)
     token_heads = B * Hkv * ctx
     per_token_head = (kc.code_bytes + 2) + (vc.code_bytes + 2)  # 100 B
     cache_bytes = token_heads * per_token_head
@@ -196,19 +251,17 @@ def long_leg(tq, torch, synth, steps, warmup):
     out = torch.empty(1, Hkv * g, d, device="cuda")
     ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, 1, Hkv * g, Hkv, cap))
     scale = 1.0 / math.sqrt(d)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps + warmup)]
+    def args_of(i):
+        return (kc, vc, q, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], scale, out, ws)
 
     def step(i):
-        args = (kc, vc, q, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], scale, out, ws)
+        args = args_of(i)
         tq.tq_attn_prepare(*args)
-        ev[i][0].record()
         tq.tq_attn_scan(*args)
-        ev[i][1].record()
         tq.tq_attn_combine(*args)
 
     ms = timed_loop(step, steps, warmup, torch)
-    scan_ms = sum(ev[warmup + i][0].elapsed_time(ev[warmup + i][1]) for i in range(steps)) / steps
+    scan_ms = scan_launch_ms(tq, torch, args_of, steps)
     cache_bytes = Hkv * cap * ((kc.code_bytes + 2) + (vc.code_bytes + 2))
     return {
         "workload": "1 sequence, 8 kv heads x 2^20 tokens, d=128, K3/V3, 64 bf16 query heads (8:1)",
@@ -320,8 +373,7 @@ def main():
         sys.exit(2)
     import torch
 
-    root = os.path.dirname(os.path.abspath(__file__))
-    sys.path.insert(0, root)
+    sys.path.insert(0, ROOT)
     import synth
     import kv_cache_vector_02_amd as tq
 
@@ -331,10 +383,11 @@ def main():
     if args.calib_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        log("calibration copy: 3 x 256 MiB read + 256 MiB written")
+        log("calibration copy: 3 launches, each 256 MiB read + 256 MiB written")
     if "decode" in legs:
         log("decode leg: batch 16, 28/4 heads, 32768 tokens, K4/V2")
         res["decode"], _ = decode_leg(tq, torch, synth, args.steps, args.warmup)
@@ -390,6 +443,10 @@ def main():
             "scan_ms": dec["scan_ms"],
             "algorithmic_bytes_per_launch": dec["cache_bytes"],
         }
+        tr = stored_traffic()
+        if tr:
+            line["roofline"]["traffic"] = tr["bytes"]
+            line["roofline"]["traffic_detail"] = tr
         line["decode"] = dec
     if cpu:
         line["cpu_baseline"] = cpu
