@@ -135,7 +135,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr float kTauLog2 = 8.0f;  // scores may exceed the reference max by this much (log2 units)
+constexpr float kTauLog2 = 12.0f;  // scores may exceed the reference max by this much (log2 units)
 constexpr int kVHeadroom = 1;     // binades of headroom above the largest V norm seen
 
 // Waves of one split block: the block owns a compute unit (one resident block
