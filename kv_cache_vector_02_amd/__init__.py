@@ -106,18 +106,24 @@ def _check(code: int, where: str):
 
 
 def _ptr(t):
+    """Device address of a torch tensor (None passes through as NULL)."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError("expected a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("device tensor expected")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
-def _stream(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+_raw_stream = torch._C._cuda_getCurrentRawStream
+
+
+def _stream(stream=None, like=None):
+    """hipStream_t of `stream`, else of the current stream of `like`'s device."""
+    if stream is not None:
+        return stream.cuda_stream
+    return _raw_stream(like.get_device() if like is not None else torch.cuda.current_device())
 
 
 def tq_codebook(bits: int, d: int, seed: int, qjl_m: int = 0) -> tq_codec:
@@ -141,14 +147,14 @@ def tq_encode(codec: tq_codec, x: torch.Tensor, codes: torch.Tensor, norms: torc
     n = x.shape[0]
     _check(_lib.tq_encode(ctypes.byref(codec), _ptr(x), _DTYPES[x.dtype], n, x.stride(0), _ptr(codes),
                           codes.stride(0), _ptr(norms), _ptr(qjl_S), _ptr(qjl_bits), _ptr(qjl_gamma),
-                          _stream(stream)), "tq_encode")
+                          _stream(stream, x)), "tq_encode")
 
 
 def tq_decode(codec: tq_codec, codes: torch.Tensor, norms: torch.Tensor, x_hat: torch.Tensor, stream=None) -> None:
     if codes.dim() != 2 or codes.stride(1) != 1:
         raise ValueError("codes must be 2-D with contiguous rows")
     _check(_lib.tq_decode(ctypes.byref(codec), _ptr(codes), codes.stride(0), _ptr(norms), codes.shape[0],
-                          _ptr(x_hat), _stream(stream)), "tq_decode")
+                          _ptr(x_hat), _stream(stream, codes)), "tq_decode")
 
 
 def tq_attn_workspace_bytes(kc: tq_codec, vc: tq_codec, batch: int, n_q_heads: int, n_kv_heads: int,
@@ -167,7 +173,7 @@ def _attn(name, kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, scale, o
     _check(fn(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _DTYPES[q.dtype], B, Hq, Hkv,
               _ptr(ctx_len), cap, _ptr(k_codes), _ptr(k_norms), _ptr(k_qjl), _ptr(k_gamma),
               _ptr(qjl_S), _ptr(v_codes), _ptr(v_norms), ctypes.c_float(scale), _ptr(out),
-              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)), name)
+              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q)), name)
 
 
 def tq_attn_decode(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.Tensor,
@@ -213,7 +219,7 @@ def tq_ip_search(codec: tq_codec, q: torch.Tensor, codes: torch.Tensor, norms: t
     n_db = codes.shape[0]
     _check(_lib.tq_ip_search(ctypes.byref(codec), _ptr(q), n_q, _ptr(codes), _ptr(norms), _ptr(qjl_bits),
                              _ptr(qjl_gamma), _ptr(qjl_S), n_db, k, _ptr(out_scores), _ptr(out_ids),
-                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q)),
            "tq_ip_search")
 
 
