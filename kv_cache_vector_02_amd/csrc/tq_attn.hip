@@ -79,7 +79,7 @@ void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int d, int kb, int vb
         per = (per + 63) & ~(int64_t)63;
         sp = ctx_cap > 0 ? (ctx_cap + per - 1) / per : 1;
         const int64_t rounds = (units * sp + slots - 1) / slots;
-        const int64_t nw = attn::split_waves(d);
+        const int64_t nw = attn::split_waves(d, kb, vb, qjl);
         const int64_t wave_tiles = (per / 64 + nw - 1) / nw;
         const double cost = (double)rounds * (double)(wave_tiles + 2);
         if (best_cost < 0.0 || cost < best_cost || (cost == best_cost && sp < best_sp)) {

@@ -1,15 +1,16 @@
-// Decode attention over the packed cache, gfx950, float32 VALU.
+// Decode attention over the packed cache, gfx950.
 //
 // Three launches per call:
 //   1. qprep: q_rot = H(D_K q) per query head (register/DPP transform), stored
 //      pre-scaled by scale*log2(e)/d; with QJL also S q_rot/sqrt(d).
-//   2. split: grid (splits, kv_head x head_chunk, batch).  Each wave streams
-//      64-token tiles of its split: lane <-> token for the K side (codes in
-//      registers, centroid pairs from an LDS table, rotated query from scalar
-//      registers), a wave-wide online softmax in the log2 domain, then lane <->
-//      dimension pairs for the V side (codes staged in LDS, softmax weights
-//      broadcast from LDS), accumulating V in the rotated domain.  The four
-//      waves of a block merge their (max, sum, acc) and write one partial.
+//   2. split: grid (splits, kv_head x head_chunk, batch), one block per compute
+//      unit.  Each wave streams 64-token tiles of its split: K scores on the
+//      matrix cores from centroid pairs looked up in LDS tables by the K codes
+//      (loaded straight into the operand layout), a wave-wide online softmax in
+//      the log2 domain, then the V sums on the matrix cores with the softmax
+//      weights as one operand and V centroids looked up by the V codes (staged
+//      through LDS) as the other, accumulated in the rotated domain.  The waves
+//      of a block merge their (max, sum, acc) and write one partial.
 //   3. combine: log-sum-exp merge of the partials of each (batch, head), one
 //      inverse transform D_V H(.)/d per output head.
 //
@@ -110,7 +111,8 @@ __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
 // 0..7 hold q_hi of the (at most eight) query heads while columns 8..15 hold
 // q_lo, so that D[t][h] + D[t][h + 8] = sum_dim (c_hi + c_lo)(q_hi + q_lo) over
 // the centroid and query of every dim, a float32-exact product up to the
-// rounding of the accumulation.  The query chunk is scaled by one power of two
+// rounding of the accumulation (the c_lo * q_lo term, below 2^-22 of the
+// score, is zeroed out of the q_lo columns).  The query chunk is scaled by one power of two
 // into [2^14, 2^15) and the centroids by 16 so every lo part is a normal half;
 // the scale is removed exactly on the float32 result.  After adding the two
 // column halves (a DPP row rotate), lane (n, grp) holds the scores of tokens
@@ -137,15 +139,51 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kTauLog2 = 12.0f;  // scores may exceed the reference max by this much (log2 units)
 constexpr int kVHeadroom = 1;     // binades of headroom above the largest V norm seen
+constexpr int kKLookahead = 2;    // K table lookups issued this many matrix-core steps ahead
 
-// Waves of one split block: the block owns a compute unit (one resident block
-// per CU) and its waves share the lookup tables.
-constexpr int split_waves(int d) { return d == 128 ? 12 : 8; }
+// LDS of one split block: the lookup tables, one staging area per wave and,
+// with QJL, the sign-side operands.  gfx950 reads 256 bytes per clock from 64
+// four-byte banks (32 lanes per pass for 8-byte reads, 16 for 16-byte reads).
+//
+// Split tables: a K table and a V table of 256-byte rows, row u holding the
+// entry of index u repeated across the whole row (256 / entry-size slices).
+// Lane l reads slice l % slices, so the lanes of one pass touch distinct banks
+// whatever their indices.  When the two tables and the wave areas do not fit,
+// one shared table of 256-byte rows holds the K entry in its first and the V
+// entry in its last 128 bytes (half the slices: two lanes of a pass may share a
+// bank).  Either way a row offset is index * 256 (one byte permute of an 8-bit
+// index).
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kVStride = 68;                        // padded dword stride of the V staging rows
+constexpr int k_codes(int kb) { return kb >= 3 ? 2 : 4; }  // codes per K lookup
+constexpr int v_codes(int vb) { return vb == 1 ? 8 : (vb == 2 ? 4 : 2); }  // codes per V lookup
+constexpr int wave_dw(int d, int vb) { return (d * vb / 32 + 1) * kVStride + 16 + 3 * 64; }
+constexpr int qjl_dw(bool qjl) { return qjl ? 8 * 64 * 4 + 256 * 4 : 0; }
+constexpr int k_rows(int kb) { return 1 << (k_codes(kb) * kb); }
+constexpr int v_rows(int vb) { return 1 << (v_codes(vb) * vb); }
+constexpr int split_tab_bytes(int kb, int vb) { return (k_rows(kb) + v_rows(vb)) * 256; }
+constexpr int shared_tab_bytes(int kb, int vb) { return (k_rows(kb) > v_rows(vb) ? k_rows(kb) : v_rows(vb)) * 256; }
+constexpr bool split_fits(int d, int kb, int vb, bool qjl, int nw) {
+    return split_tab_bytes(kb, vb) + 4 * (nw * wave_dw(d, vb) + qjl_dw(qjl)) <= kLdsBytes;
+}
+// Waves of one split block (the block owns a compute unit: one resident block
+// per CU, its waves sharing the tables): split tables with the most waves that
+// fit (12 or 8 at d = 128, 8 at d = 256), else the shared table.  The QJL
+// variant, whose extra operands already press on the registers, keeps the
+// shared table.
+constexpr int split_waves(int d, int kb, int vb, bool qjl) {
+    if (!qjl && d == 128 && split_fits(d, kb, vb, qjl, 12)) return 12;
+    if (!qjl && split_fits(d, kb, vb, qjl, 8)) return 8;
+    return d == 128 ? 12 : 8;
+}
+constexpr bool split_tables(int d, int kb, int vb, bool qjl) {
+    return !qjl && split_fits(d, kb, vb, qjl, split_waves(d, kb, vb, qjl));
+}
 
 template <int D, int KB, int VB, int G, bool QJL>
 struct Cfg {
     static_assert(G >= 1 && G <= 8, "at most eight query heads per block");
-    static constexpr int NW = split_waves(D);       // waves per block
+    static constexpr int NW = split_waves(D, KB, VB, QJL);  // waves per block
     static constexpr int NT = 64 * NW;              // threads per block
     // K side
     static constexpr int RBK = D * KB / 8;          // K code bytes per token
@@ -153,7 +191,7 @@ struct Cfg {
     static constexpr int KSTEPS = DG / 4;           // MFMA K steps (4 dims per lane each)
     static constexpr int GB = DG * KB / 8;          // K code bytes per lane group per token
     static constexpr int GW = GB / 4;               // ... in dwords
-    static constexpr int KE = KB >= 3 ? 2 : 4;      // codes per K lookup
+    static constexpr int KE = k_codes(KB);          // codes per K lookup
     static constexpr int KLU = KE * KB;             // K index bits
     static constexpr int KENT = 4 * KE;             // bytes per K entry: hi halves then lo halves
     static constexpr int LPS = 4 / KE;              // K lookups per step
@@ -162,30 +200,35 @@ struct Cfg {
     static constexpr int VTW = RBV / 4;             // dwords per V row
     static constexpr int NB = D / 16;               // N-blocks of 16 columns
     static constexpr int PIECE = VB * NB;           // bits per lane per token
-    static constexpr int VT = VB == 1 ? 8 : (VB == 2 ? 4 : 2);  // codes per V lookup
+    static constexpr int VT = v_codes(VB);          // codes per V lookup
     static constexpr int VLB = VT * VB;             // V index bits
     static constexpr int VENT = 2 * VT;             // bytes per V entry
     static constexpr int VENTW = VENT / 4;          // ... in dwords
     static constexpr int VLK = NB / VT;             // V lookups per token
-    // Bank-sliced table: 256-byte rows; row u holds the K entry of index u once
-    // per K slice in its first 128 bytes and the V entry of index u once per V
-    // slice in its last 128 bytes.  Lane l reads slice l % (128 / entry size),
-    // so the lanes of one LDS pass touch distinct banks whatever their indices,
-    // and a row offset is one byte permute of an 8-bit index.
-    static constexpr int KSL = 128 / KENT;          // K slices
-    static constexpr int VSL = 128 / VENT;          // V slices
-    static constexpr int ROWS = (1 << KLU) > (1 << VLB) ? (1 << KLU) : (1 << VLB);
-    static constexpr int TABB = ROWS * 256;
+    // tables (see above): slices per row, table bytes, byte offset of V row 0
+    // split into the part above 64 KiB (carried by the lane offset) and the
+    // rest (an instruction offset)
+    static constexpr bool SPLIT = split_tables(D, KB, VB, QJL);
+    static constexpr int KROWS = k_rows(KB), VROWS = v_rows(VB);
+    static constexpr int KSL = (SPLIT ? 256 : 128) / KENT;  // K slices
+    static constexpr int VSL = (SPLIT ? 256 : 128) / VENT;  // V slices
+    static constexpr int TABB = SPLIT ? split_tab_bytes(KB, VB) : shared_tab_bytes(KB, VB);
+    static constexpr int VBASE = SPLIT ? KROWS * 256 : 128;
+    static constexpr uint32_t VOFF0 = SPLIT ? (uint32_t)VBASE & ~0xFFFFu : (uint32_t)VBASE;
+    static constexpr int VIMM = SPLIT ? VBASE & 0xFFFF : 0;
     // per wave: V tile dword-major [VTW + 1][VSTR] (last row zero; VSTR pads the
     // rows across banks), head factors [16], K norm * query scale [64], scaled
     // V norm [64], QJL gamma [64]
-    static constexpr int VSTR = 68;
-    static constexpr int WAVE_DW = (VTW + 1) * VSTR + 16 + 3 * 64;
-    static constexpr int QJL_DW = QJL ? 8 * 64 * 4 + 256 * 4 : 0;  // QJL B operands + sign table
+    static constexpr int VSTR = kVStride;
+    static constexpr int WAVE_DW = wave_dw(D, VB);
+    static constexpr int QJL_DW = qjl_dw(QJL);      // QJL B operands + sign table
     static constexpr int LOOP_DW = TABB / 4 + NW * WAVE_DW + QJL_DW;
     static constexpr int MERGE_DW = NW * G * (D + 2);
     static constexpr int SMEM_DW = LOOP_DW > MERGE_DW ? LOOP_DW : MERGE_DW;
-    static_assert(4 * SMEM_DW <= 160 * 1024, "split kernel exceeds LDS");
+    static_assert(4 * SMEM_DW <= kLdsBytes, "split kernel exceeds LDS");
+    // K codes double-buffered (loaded a whole tile ahead) where the register
+    // budget of two waves per SIMD leaves room
+    static constexpr bool KDB = NW <= 8 && !QJL;
 };
 
 __device__ __forceinline__ half8_t as_half8(uint4 u) { return __builtin_bit_cast(half8_t, u); }
@@ -279,7 +322,8 @@ __device__ __forceinline__ void fetch_v(uint32_t (&rv)[C::VTW], uint32_t& rn, ui
 }
 
 template <int D, int KB, int VB, int G, bool QJL>
-__global__ __launch_bounds__(64 * split_waves(D)) __attribute__((amdgpu_waves_per_eu(split_waves(D) / 4)))
+__global__ __launch_bounds__(64 * split_waves(D, KB, VB, QJL))
+__attribute__((amdgpu_waves_per_eu(split_waves(D, KB, VB, QJL) / 4)))
 void split_kernel(AttnArgs a) {
     using C = Cfg<D, KB, VB, G, QJL>;
     __shared__ __attribute__((aligned(16))) uint32_t smem[C::SMEM_DW];
@@ -312,10 +356,12 @@ void split_kernel(AttnArgs a) {
     // first tile's loads go out before the tables are built
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     int t0 = t_beg + wave_u * 64;
-    uint32_t rk[4 * C::GW];
+    constexpr bool KDB = C::KDB;
+    constexpr int KBUF = KDB ? 2 : 1;  // K code buffers: with two, a tile's K codes are loaded one tile ahead
+    uint32_t rk[KBUF][4 * C::GW];
     uint32_t rv[C::VTW], rn = 0, rg = 0;
     if (t0 < t_end) {
-        fetch_k<C>(rk, kcodes, (uint32_t)t0, last, n, grp);
+        fetch_k<C>(rk[0], kcodes, (uint32_t)t0, last, n, grp);
         fetch_v<C, QJL>(rv, rn, rg, vcodes, knb, vnb, gmb, (uint32_t)t0, last, lane);
     }
 
@@ -325,13 +371,26 @@ void split_kernel(AttnArgs a) {
     if (tid < (1 << KB)) cent[tid] = 16.0f * a.kc.centroid[tid];
     if (tid >= 16 && tid < 16 + (1 << VB)) cent[tid] = a.vc.centroid[tid - 16];
     __syncthreads();
-    for (int i = tid; i < C::ROWS * 16; i += C::NT) {
-        // row u, 16-byte chunk c: chunks 0..7 repeat the K entry of u, 8..15 the V entry
-        const int u = i >> 4, c = i & 15;
+    constexpr int NCH = C::SPLIT ? (C::KROWS + C::VROWS) * 16 : C::TABB / 16;  // 16-byte chunks
+    for (int i = tid; i < NCH; i += C::NT) {
+        // split: K rows then V rows, 16 chunks each; shared: row u, chunks 0..7
+        // repeat the K entry of u and chunks 8..15 the V entry
+        bool is_k;
+        int u, dst;
+        if constexpr (C::SPLIT) {
+            is_k = i < C::KROWS * 16;
+            const int r = is_k ? i : i - C::KROWS * 16;
+            u = r >> 4;
+            dst = (is_k ? 0 : C::VBASE) + 16 * r;
+        } else {
+            u = i >> 4;
+            is_k = (i & 15) < 8;
+            dst = 16 * i;
+        }
         uint32_t w[4] = {0u, 0u, 0u, 0u};  // one entry (K: hi halves then lo halves; V: halves)
         bool live;
-        if (c < 8) {
-            live = u < (1 << C::KLU);
+        if (is_k) {
+            live = u < C::KROWS;
 #pragma unroll
             for (int p = 0; p < C::KE; p += 2) {
                 const float c0 = cent[(u >> (KB * p)) & ((1 << KB) - 1)];
@@ -341,18 +400,18 @@ void split_kernel(AttnArgs a) {
                 w[C::KE / 2 + p / 2] = pack_half2(c0 - (float)h0, c1 - (float)h1);
             }
         } else {
-            live = u < (1 << C::VLB);
+            live = u < C::VROWS;
 #pragma unroll
             for (int p = 0; p < C::VT; p += 2)
                 w[p / 2] = pack_half2(cent[16 + ((u >> (VB * p)) & ((1 << VB) - 1))],
                                       cent[16 + ((u >> (VB * (p + 1))) & ((1 << VB) - 1))]);
         }
-        const int eb = c < 8 ? C::KENT : C::VENT;  // entry bytes
+        const int eb = is_k ? C::KENT : C::VENT;  // entry bytes
         uint4 v;
         if (eb == 4) v = make_uint4(w[0], w[0], w[0], w[0]);
         else if (eb == 8) v = make_uint4(w[0], w[1], w[0], w[1]);
         else v = make_uint4(w[0], w[1], w[2], w[3]);
-        if (live) *reinterpret_cast<uint4*>(tab + u * 256 + 16 * c) = v;
+        if (live) *reinterpret_cast<uint4*>(tab + dst) = v;
     }
     if constexpr (QJL) {
         _Float16* st = reinterpret_cast<_Float16*>(sigt);
@@ -404,7 +463,13 @@ void split_kernel(AttnArgs a) {
                 x[i] = lo_col ? (_Float16)(v - (float)hi) : hi;
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bq[ks][e] = C::KE == 2 ? x[(e >> 2) * 2 + (e & 1)] : x[e & 3];
+            // the q_lo columns are zero on the c_lo slots: the c_lo * q_lo product
+            // (below 2^-22 of the score) is left out, and zero operands cost the
+            // matrix cores less energy
+            for (int e = 0; e < 8; ++e) {
+                const bool lo_slot = C::KE == 2 ? (e & 2) != 0 : (e & 4) != 0;
+                bq[ks][e] = (lo_col && lo_slot) ? (_Float16)0.0f : (C::KE == 2 ? x[(e >> 2) * 2 + (e & 1)] : x[e & 3]);
+            }
         }
         if constexpr (QJL) {
             if (wave == 0) {
@@ -430,7 +495,7 @@ void split_kernel(AttnArgs a) {
     __syncthreads();
     // this lane's table slices (byte offsets inside a row)
     const uint32_t koff = (uint32_t)(lane % C::KSL) * C::KENT;
-    const uint32_t voff = 128u + (uint32_t)(lane % C::VSL) * C::VENT;
+    const uint32_t voff = C::VOFF0 + (uint32_t)(lane % C::VSL) * C::VENT;
 
     float m_ref = -INFINITY, l_lane = 0.0f;  // head n's reference max / this lane's partial sum
     // V sums D[nb][i]: head 4*grp + i, dim NB*n + nb, in units of 2^wsh
@@ -451,8 +516,10 @@ void split_kernel(AttnArgs a) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
-    // stage tile t0 (lane <-> token) and prefetch the next tile's V row and norms
-    auto stage = [&](float& vnf) __attribute__((always_inline)) -> bool {
+    // stage tile t0 (lane <-> token) and prefetch the next tile's V row and
+    // norms (and, with two K buffers, its K codes into buffer nxt)
+    auto stage = [&](float& vnf, auto nxtc) __attribute__((always_inline)) -> bool {
+        constexpr int nxt = decltype(nxtc)::value % KBUF;
         const int rem = t_end - t0;
         const bool lane_valid = lane < rem;
 #pragma unroll
@@ -463,36 +530,47 @@ void split_kernel(AttnArgs a) {
         vnl[lane] = vnf * vsc;
         // prefetch (clamped to the split: past its end this re-reads the last token)
         fetch_v<C, QJL>(rv, rn, rg, vcodes, knb, vnb, gmb, (uint32_t)(t0 + 64 * C::NW), last, lane);
+        if constexpr (KDB) fetch_k<C>(rk[nxt], kcodes, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
         // a V norm at or above the reference is handled by the rare rescale
         return __builtin_amdgcn_ballot_w64(lane_valid && vnf >= vlim) != 0;
     };
     // K scores of tile t0 (16 tokens x 16 columns per sub-tile), then prefetch the next tile's K codes
-    auto kphase = [&](floatx4_t (&sacc)[4]) __attribute__((always_inline)) {
+    // (K codes from buffer cur; with one buffer the next tile's codes are loaded after the lookups)
+    auto kphase = [&](floatx4_t (&sacc)[4], auto curc) __attribute__((always_inline)) {
+        constexpr int cur = decltype(curc)::value % KBUF;
 #pragma unroll
         for (int j = 0; j < 4; ++j) sacc[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        // step s = (sub-tile j, K step ks); the table lookups of step
+        // s + kKLookahead are issued before the matrix-core op of step s, and
+        // scheduling barriers keep that order
+        constexpr int NS = 4 * C::KSTEPS;
+        uint32_t aw[NS][4];
+        auto look = [&](auto sc) __attribute__((always_inline)) {
+            constexpr int s = decltype(sc)::value, j = s / C::KSTEPS, ks = s % C::KSTEPS;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int ks = 0; ks < C::KSTEPS; ++ks) {
-                uint32_t aw[4];
-#pragma unroll
-                for (int u = 0; u < C::LPS; ++u) {
-                    const int bit = (4 * ks + u * C::KE) * KB;
-                    uint32_t addr;
-                    if constexpr (C::KLU == 8) {
-                        // row offset = index * 256 + koff: one byte permute
-                        const uint32_t w = rk[j * C::GW + (bit >> 5)];
-                        addr = __builtin_amdgcn_perm(w, koff, 0x0C0C0000u | ((uint32_t)(4 + ((bit >> 3) & 3)) << 8));
-                    } else {
-                        addr = field_at<C::KLU>(rk + j * C::GW, bit) * 256u + koff;
-                    }
-                    lds_read<C::KENT / 4>(aw + u * (C::KENT / 4), tab + addr);
+            for (int u = 0; u < C::LPS; ++u) {
+                const int bit = (4 * ks + u * C::KE) * KB;
+                uint32_t addr;
+                if constexpr (C::KLU == 8) {
+                    // row offset = index * 256 + koff: one byte permute
+                    const uint32_t w = rk[cur][j * C::GW + (bit >> 5)];
+                    addr = __builtin_amdgcn_perm(w, koff, 0x0C020000u | ((uint32_t)(4 + ((bit >> 3) & 3)) << 8));
+                } else {
+                    addr = field_at<C::KLU>(rk[cur] + j * C::GW, bit) * 256u + koff;
                 }
-                sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(make_uint4(aw[0], aw[1], aw[2], aw[3])),
-                                                                 bq[ks], sacc[j], 0, 0, 0);
+                lds_read<C::KENT / 4>(aw[s] + u * (C::KENT / 4), tab + addr);
             }
-        }
-        fetch_k<C>(rk, kcodes, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
+        };
+        static_for<kKLookahead>(look);
+        static_for<NS>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int s = decltype(sc)::value, j = s / C::KSTEPS, ks = s % C::KSTEPS;
+            if constexpr (s + kKLookahead < NS) look(std::integral_constant<int, s + kKLookahead>{});
+            __builtin_amdgcn_sched_barrier(0);
+            sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(make_uint4(aw[s][0], aw[s][1], aw[s][2], aw[s][3])),
+                                                             bq[ks], sacc[j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr (!KDB) fetch_k<C>(rk[cur], kcodes, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
         if constexpr (QJL) {
             // A = 16*gamma*(+-1) of token 16j + n (exact in half); same accumulators
             const int gbytes = m >> 5;
@@ -601,6 +679,14 @@ void split_kernel(AttnArgs a) {
             wa[j >> 1][2 * (j & 1) + 1] = pack_half2(p2 * vq.z, p3 * vq.w);
         }
         l_lane += psum;
+        // rows of heads >= G and the repeated rows 8..15 carry zero weights (they
+        // are never read; zero operands cost the matrix cores less energy)
+        if (n >= G) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) wa[s2][w] = 0u;
+        }
     };
     // this lane's PIECE-bit field of the staged tile's tokens e = 4 jj + v (token
     // 32 s2 + 16 jj + 4 grp + v): fields of PK consecutive tokens share one word
@@ -655,7 +741,7 @@ void split_kernel(AttnArgs a) {
                         // byte-aligned index: row offset = index * 256 + voff by one byte permute
                         const int pos = (PK > 1 ? (e % PK) * C::PIECE : 0) + bit;  // bit position in its word
                         const uint32_t w = PK > 1 ? pc[s2][e / PK] : (pos < 32 ? pc[s2][e] : ph[s2][e]);
-                        addr = __builtin_amdgcn_perm(w, voff, 0x0C0C0000u | ((uint32_t)(4 + ((pos >> 3) & 3)) << 8));
+                        addr = __builtin_amdgcn_perm(w, voff, 0x0C020000u | ((uint32_t)(4 + ((pos >> 3) & 3)) << 8));
                     } else {
                         uint32_t idx;
                         if constexpr (PK > 1) {
@@ -668,7 +754,7 @@ void split_kernel(AttnArgs a) {
                         }
                         addr = idx * 256u + voff;
                     }
-                    lds_read<C::VENTW>(ent[e], tab + addr);
+                    lds_read<C::VENTW>(ent[e], tab + C::VIMM + addr);
                 }
 #pragma unroll
                 for (int h = 0; h < C::VT; ++h) {
@@ -685,23 +771,35 @@ void split_kernel(AttnArgs a) {
     };
 
     if (t0 < t_end) {
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
         uint32_t wa[2][4], pc[2][8], ph[2][8];
         floatx4_t sacc[4];
         float vnf;
-        bool vraise = stage(vnf);
+        bool vraise = stage(vnf, I1{});
         wave_sync();
-        kphase(sacc);
+        kphase(sacc, I0{});
         softmax(sacc, vraise, vnf, wa);
         t0 += 64 * C::NW;
-        while (t0 < t_end) {
+        // one tile: its K codes are in buffer cur, the next tile's go to the other
+        auto tile = [&](auto curc) __attribute__((always_inline)) {
             vread(pc, ph);  // previous tile, before this tile overwrites the staging area
             wave_sync();
-            vraise = stage(vnf);
+            vraise = stage(vnf, std::integral_constant<int, 1 - decltype(curc)::value>{});
             wave_sync();
-            kphase(sacc);
+            kphase(sacc, curc);
             vphase(pc, ph, wa);  // previous tile's V sums, before this tile's rescale
             softmax(sacc, vraise, vnf, wa);
             t0 += 64 * C::NW;
+        };
+        if constexpr (KDB) {
+            while (t0 < t_end) {
+                tile(I1{});
+                if (t0 >= t_end) break;
+                tile(I0{});
+            }
+        } else {
+            while (t0 < t_end) tile(I0{});
         }
         vread(pc, ph);
         vphase(pc, ph, wa);
@@ -823,9 +921,9 @@ template <int D, int KB, int VB, int G>
 hipError_t launch_split(const AttnArgs& a, hipStream_t s) {
     dim3 grid(a.splits, a.hkv * a.chunks, a.batch);
     if (a.kc.qjl_m > 0)
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, G, true>), grid, dim3(64 * split_waves(D)), 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, G, true>), grid, dim3(64 * split_waves(D, KB, VB, true)), 0, s, a);
     else
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, G, false>), grid, dim3(64 * split_waves(D)), 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, G, false>), grid, dim3(64 * split_waves(D, KB, VB, false)), 0, s, a);
     return hipGetLastError();
 }
 
@@ -834,8 +932,8 @@ template <int D, int KB, int VB, int G>
 int split_blocks(bool qjl) {
     int nb = 0;
     const hipError_t e =
-        qjl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, G, true>, 64 * split_waves(D), 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, G, false>, 64 * split_waves(D), 0);
+        qjl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, G, true>, 64 * split_waves(D, KB, VB, true), 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, G, false>, 64 * split_waves(D, KB, VB, false), 0);
     return e == hipSuccess && nb > 0 ? nb : 0;
 }
 
