@@ -159,7 +159,7 @@ int tq_decode(const tq_codec *c, const uint8_t *codes, int64_t code_row_stride,
  *   v_codes, v_norms as k_codes / k_norms with vbits
  *   out             [batch][n_q_heads][d] float32; a sequence with ctx_len 0 gives 0.
  *   workspace       device scratch of at least tq_attn_workspace_bytes(...) bytes,
- *                   16-byte aligned (query rotations and split-K partials).
+ *                   16-byte aligned (QJL query projections and split-K partials).
  * Supported: n_q_heads % n_kv_heads == 0, group size g = n_q_heads/n_kv_heads
  * with g <= 8 or g a multiple of a divisor in 1..8 (heads are processed in
  * chunks of at most 8).  ctx_cap >= 1.
@@ -177,11 +177,14 @@ int tq_attn_decode(const tq_codec *kc, const tq_codec *vc,
  * The three launches of tq_attn_decode as separate calls (same arguments, same
  * checks, same workspace, which carries the state between them), for callers
  * that time or schedule the stages themselves:
- *   tq_attn_prepare  rotate the queries once (q_rot, and S q_rot/sqrt(d) with
- *                    QJL) into the workspace -- the Q-side WHT of [P1] v1.7.0
- *                    item 4 and the fused Q_wht1/Q_wht2 pass of [P1] v1.4.2 item 5;
- *   tq_attn_scan     stream the packed cache: scores, online softmax and rotated
- *                    V sums per context split, into the workspace;
+ *   tq_attn_prepare  with QJL keys: the projection S q_rot/sqrt(d) of every
+ *                    rotated query into the workspace (the Q_wht2 half of the
+ *                    fused Q_wht1/Q_wht2 pass of [P1] v1.4.2 item 5); without
+ *                    QJL it launches nothing;
+ *   tq_attn_scan     rotate the queries (q_rot = H(D_K q), the Q-side WHT of
+ *                    [P1] v1.7.0 item 4), then stream the packed cache: scores,
+ *                    online softmax and rotated V sums per context split, into
+ *                    the workspace;
  *   tq_attn_combine  merge the splits and apply one inverse transform per head
  *                    into `out` ([P1] v1.5.1 item 2).
  * tq_attn_decode == prepare, scan, combine on one stream.

@@ -259,9 +259,8 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
     const size_t heads = (size_t)batch * n_q_heads;
     float* ws = (float*)workspace;
     auto al = [](size_t n) { return (n + 63) & ~(size_t)63; };
-    a->qrot = ws;
-    a->qproj = ws + al(heads * d);
-    a->part = a->qproj + al(heads * (size_t)m);
+    a->qproj = ws;
+    a->part = ws + al(heads * (size_t)m);
     a->splits = splits;
     a->split_tokens = per;
     return TQ_OK;

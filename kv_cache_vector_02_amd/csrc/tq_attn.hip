@@ -1,5 +1,6 @@
 // Host side of decode attention: launch planning, workspace layout and the
-// three launches (query prep, split-K scan, combine + inverse transform).
+// launches (QJL query projection when the keys carry QJL bits, split-K scan,
+// combine + inverse transform).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -96,8 +97,7 @@ static size_t align_floats(size_t n) { return (n + 63) & ~(size_t)63; }
 
 size_t attn_workspace(int batch, int hq, int d, int m, int splits) {
     const size_t heads = (size_t)batch * hq;
-    const size_t floats = align_floats(heads * d) + align_floats(heads * (size_t)m) +
-                          align_floats(heads * (size_t)splits * (d + 2));
+    const size_t floats = align_floats(heads * (size_t)m) + align_floats(heads * (size_t)splits * (d + 2));
     return floats * sizeof(float);
 }
 
@@ -138,7 +138,8 @@ static hipError_t launch_split_any(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s) {
     const bool d128 = a.kc.d == 128;
     hipError_t e = hipSuccess;
-    if (stages & ATTN_PREPARE) {
+    // without QJL the scan rotates its queries itself and there is nothing to prepare
+    if ((stages & ATTN_PREPARE) && a.kc.qjl_m > 0) {
         e = d128 ? launch_qprep_combine<128>(a, s, true) : launch_qprep_combine<256>(a, s, true);
         if (e != hipSuccess) return e;
     }

@@ -1,10 +1,11 @@
 // Decode attention over the packed cache, gfx950.
 //
-// Three launches per call:
-//   1. qprep: q_rot = H(D_K q) per query head (register/DPP transform), stored
-//      pre-scaled by scale*log2(e)/d; with QJL also S q_rot/sqrt(d).
+// Launches per call (two without QJL):
+//   1. qprep (QJL keys only): S q_rot / sqrt(d) per query head, with
+//      q_rot = H(D_K q) from the register/DPP transform.
 //   2. split: grid (splits, kv_head x head_chunk, batch), one block per compute
-//      unit.  Each wave streams 64-token tiles of its split: K scores on the
+//      unit.  The block first rotates its chunk's queries (q_rot = H(D_K q),
+//      pre-scaled by scale * log2(e) / d).  Each wave then streams 64-token tiles of its split: K scores on the
 //      matrix cores from centroid pairs looked up in LDS tables by the K codes
 //      (loaded straight into the operand layout), a wave-wide online softmax in
 //      the log2 domain, then the V sums on the matrix cores with the softmax
@@ -49,8 +50,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 
 // ----------------------------------------------------------------- qprep ----
-// q_rot is stored dim-major inside each chunk of G query heads, so the 2*G
-// values one K lookup needs are contiguous for the scalar loads.
+// QJL keys only: per query head, the projection S H(D_K q) / sqrt(d) of the
+// rotated query (the Q_wht2 side of the fused query pass), pre-scaled by
+// scale * log2(e) * sqrt(pi/2) / m.  The scan rotates its queries itself.
 template <int D, int DT>
 __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
     constexpr int LPV = D / 8;
@@ -73,27 +75,16 @@ __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = as_f(as_u(v[e]) ^ (((sbits >> e) & 1u) << 31));
     fwht<LPV>(v, gl);
-    const float qs = a.scale * kLog2e / (float)D;
-    if (valid) {
-        // dim-major inside each chunk of G heads: [head - hh][dim][hh]
-        const int G = a.heads_per_chunk;
-        const int hh = head % G;
-        float* o = a.qrot + (int64_t)(head - hh) * D + hh;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[(gl * 8 + e) * G] = v[e] * qs;
-    }
     const int m = a.kc.qjl_m;
-    if (m > 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rot[grp][gl * 8 + e] = v[e];
-        __syncthreads();
-        const float ps = a.scale * kLog2e * sqrtf(1.57079632679489662f) / ((float)m * sqrtf((float)D));
-        for (int j = gl; j < m; j += LPV) {
-            const float* srow = a.S + (int64_t)j * D;
-            float acc = 0.0f;
-            for (int i = 0; i < D; ++i) acc = fmaf(srow[i], rot[grp][i], acc);
-            if (valid) a.qproj[(int64_t)head * m + j] = acc * ps;
-        }
+    for (int e = 0; e < 8; ++e) rot[grp][gl * 8 + e] = v[e];
+    __syncthreads();
+    const float ps = a.scale * kLog2e * sqrtf(1.57079632679489662f) / ((float)m * sqrtf((float)D));
+    for (int j = gl; j < m; j += LPV) {
+        const float* srow = a.S + (int64_t)j * D;
+        float acc = 0.0f;
+        for (int i = 0; i < D; ++i) acc = fmaf(srow[i], rot[grp][i], acc);
+        if (valid) a.qproj[(int64_t)head * m + j] = acc * ps;
     }
 }
 
@@ -226,6 +217,7 @@ struct Cfg {
     static constexpr int MERGE_DW = NW * G * (D + 2);
     static constexpr int SMEM_DW = LOOP_DW > MERGE_DW ? LOOP_DW : MERGE_DW;
     static_assert(4 * SMEM_DW <= kLdsBytes, "split kernel exceeds LDS");
+    static_assert(G * D <= NW * WAVE_DW, "rotated queries exceed the wave areas");
     // K codes double-buffered (loaded a whole tile ahead) where the register
     // budget of two waves per SIMD leaves room
     static constexpr bool KDB = NW <= 8 && !QJL;
@@ -353,8 +345,27 @@ void split_kernel(AttnArgs a) {
     const uint8_t* gmb = QJL ? reinterpret_cast<const uint8_t*>(a.k_gamma + kvrow) : nullptr;
     const uint32_t last = t_end > 0 ? (uint32_t)(t_end - 1) : 0u;
 
-    // first tile's loads go out before the tables are built
+    // This chunk's query heads are rotated here (the Q-side transform): lane
+    // group hl = wave * QVPW + lane / QLPV of the first waves holds dims
+    // [8 gl, 8 gl + 8) of head h0 + hl.  Their loads go out first, so the
+    // transform waits for them alone, then the first tile's loads.
+    constexpr int QLPV = D / 8, QVPW = 64 / QLPV;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const bool qwave = wave_u * QVPW < G;
+    const int qgl = lane & (QLPV - 1), qhl = wave_u * QVPW + lane / QLPV;
+    float qx[8];
+    if (qwave) {
+        if (qhl < G) {
+            const int64_t e0 = ((int64_t)b * a.hq + h0 + qhl) * D + qgl * 8;
+            if (a.q_dtype == TQ_F32) load8<0>(static_cast<const float*>(a.q) + e0, qx);
+            else if (a.q_dtype == TQ_F16) load8<1>(static_cast<const uint16_t*>(a.q) + e0, qx);
+            else load8<2>(static_cast<const uint16_t*>(a.q) + e0, qx);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qx[e] = 0.0f;
+        }
+    }
+    // first tile's loads go out before the tables are built
     int t0 = t_beg + wave_u * 64;
     constexpr bool KDB = C::KDB;
     constexpr int KBUF = KDB ? 2 : 1;  // K code buffers: with two, a tile's K codes are loaded one tile ahead
@@ -370,6 +381,20 @@ void split_kernel(AttnArgs a) {
     __shared__ float cent[32];  // [0, 16): 16 * c_K, [16, 32): c_V
     if (tid < (1 << KB)) cent[tid] = 16.0f * a.kc.centroid[tid];
     if (tid >= 16 && tid < 16 + (1 << VB)) cent[tid] = a.vc.centroid[tid - 16];
+    // rotated queries qr[hl][dim] = (scale log2(e) / d) H(D_K q), in the wave
+    // areas (free until the tile loop)
+    float* qr = reinterpret_cast<float*>(waves_lds);
+    if (qwave) {
+        const uint32_t sbits = (a.kc.sign_mask[qgl >> 2] >> ((qgl & 3) * 8)) & 0xFFu;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qx[e] = as_f(as_u(qx[e]) ^ (((sbits >> e) & 1u) << 31));
+        fwht<QLPV>(qx, qgl);
+        const float qs = a.scale * kLog2e / (float)D;
+        if (qhl < G) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qr[qhl * D + qgl * 8 + e] = qx[e] * qs;
+        }
+    }
     __syncthreads();
     constexpr int NCH = C::SPLIT ? (C::KROWS + C::VROWS) * 16 : C::TABB / 16;  // 16-byte chunks
     for (int i = tid; i < NCH; i += C::NT) {
@@ -422,7 +447,6 @@ void split_kernel(AttnArgs a) {
     // n % 8 (zero beyond G), all heads scaled by one power of two, with the dims
     // of K step ks in the order of the A entries (KE = 2: d0 d1 d0 d1 d2 d3 d2 d3;
     // KE = 4: d0 d1 d2 d3 d0 d1 d2 d3); likewise the QJL projection
-    const float* qrot = a.qrot + ((int64_t)b * a.hq + h0) * D;  // [dim][G] inside this chunk
     const int hh = n & 7;
     const bool lo_col = n >= 8, head_ok = hh < G;
     half8_t bq[C::KSTEPS];
@@ -435,7 +459,7 @@ void split_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int dim = grp * C::DG + 4 * ks + i;
-                const float x = qrot[dim * G + (head_ok ? hh : 0)];
+                const float x = qr[(head_ok ? hh : 0) * D + dim];
                 qv[ks][i] = head_ok ? x : 0.0f;
                 amax = fmaxf(amax, fabsf(qv[ks][i]));
             }
@@ -491,6 +515,7 @@ void split_kernel(AttnArgs a) {
     float* knq = hfac + 16;                                             // [64] K norm * query scale
     float* vnl = knq + 64;                                              // [64] V norm * weight scale
     float* gml = vnl + 64;                                              // [64] QJL gamma
+    __syncthreads();  // every wave has read qr before the wave areas are reused
     vt[C::VTW * C::VSTR + lane] = 0u;
     __syncthreads();
     // this lane's table slices (byte offsets inside a row)

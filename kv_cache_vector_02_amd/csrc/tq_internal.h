@@ -57,7 +57,6 @@ struct AttnArgs {
     const uint16_t* v_norms;
     float scale;
     float* out;
-    float* qrot;      // [batch][hq][d]  (scale*log2e/d) * H(D_K q)
     float* qproj;     // [batch][hq][m]  scale*log2e*sqrt(pi/2)/m * S H(D_K q)/sqrt(d)
     float* part;      // [batch][hq][splits][d + 2]
     int splits;
