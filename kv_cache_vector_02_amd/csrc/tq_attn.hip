@@ -113,7 +113,8 @@ static hipError_t launch_qprep_combine(const AttnArgs& a, hipStream_t s, bool pr
             default: hipLaunchKernelGGL((attn::qprep_kernel<D, 2>), dim3(grid), dim3(64), 0, s, a); break;
         }
     } else {
-        hipLaunchKernelGGL((attn::combine_kernel<D>), dim3(a.batch * a.hq), dim3(256), 0, s, a);
+        constexpr int HPB = 256 / (D / 8);  // heads per combine block
+        hipLaunchKernelGGL((attn::combine_kernel<D>), dim3((a.batch * a.hq + HPB - 1) / HPB), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

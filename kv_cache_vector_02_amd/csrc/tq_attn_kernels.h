@@ -880,65 +880,70 @@ void split_kernel(AttnArgs a) {
 }
 
 // --------------------------------------------------------------- combine ----
-// One block of 256 threads per (batch, query head): 256/D split groups reduce
-// disjoint subsets of the splits with independent (unrolled) loads, the
-// groups are merged through LDS, then one inverse transform.
+// One lane group of D/8 lanes per (batch, query head), lane gl holding dims
+// [8 gl, 8 gl + 8) as in the encoder's transform layout: the log-sum-exp merge
+// of the head's split partials runs in registers, then the inverse transform
+// D_V H(.) / d through lane exchanges.  No LDS and no barriers.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
-    constexpr int NG = 256 / D;  // split groups
-    __shared__ float x[NG][D];
-    __shared__ float red[256];
-    __shared__ float lsum[NG];
-    const int bh = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int i = tid % D, grp = tid / D;
-    const float* p = a.part + (int64_t)bh * a.splits * (D + 2);
+    constexpr int LPV = D / 8, HPB = 256 / LPV;  // lanes per head, heads per block
+    const int tid = threadIdx.x, gl = tid & (LPV - 1);
+    const int heads = a.batch * a.hq;
+    const int bh = blockIdx.x * HPB + tid / LPV;
+    const bool valid = bh < heads;  // uniform inside a lane group
     const int S = a.splits;
-
-    float mx = -INFINITY;
-    for (int s = tid; s < S; s += 256) mx = fmaxf(mx, p[(int64_t)s * (D + 2)]);
-    red[tid] = mx;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-        __syncthreads();
-    }
-    mx = red[0];
-    float L = 0.0f, acc = 0.0f;
-    if (mx != -INFINITY) {
-#pragma unroll 8
-        for (int s = grp; s < S; s += NG) {
-            const float* ps = p + (int64_t)s * (D + 2);
-            const float f = exp2f(ps[0] - mx);
-            L = fmaf(ps[1], f, L);
-            acc = fmaf(ps[2 + i], f, acc);
-        }
-    }
-    x[grp][i] = acc;
-    if (i == 0) lsum[grp] = L;
-    __syncthreads();
-    if (grp == 0) {
-        float at = 0.0f, lt = 0.0f;
+    const float* p = a.part + (int64_t)(valid ? bh : 0) * S * (D + 2);
+    // online merge over chunks of four splits: the loads of a chunk go out
+    // together, its max raises the running one and rescales the sums
+    float mx = -INFINITY, L = 0.0f, x[8];
 #pragma unroll
-        for (int g2 = 0; g2 < NG; ++g2) {
-            at += x[g2][i];
-            lt += lsum[g2];
+    for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += 4) {
+        float mc[4], lc[4], vc[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool live = s0 + u < S;
+            const float* ps = p + (int64_t)(live ? s0 + u : S - 1) * (D + 2);
+            mc[u] = ps[0];
+            lc[u] = ps[1];
+            // dims 8 gl .. 8 gl + 7 of the split's sums (8-byte aligned: D + 2 is even)
+            const float2* v2 = reinterpret_cast<const float2*>(ps + 2 + 8 * gl);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float2 v = v2[k];
+                vc[u][2 * k] = v.x;
+                vc[u][2 * k + 1] = v.y;
+            }
+            if (!live) mc[u] = -INFINITY;  // a repeated split weighs zero
         }
-        x[0][i] = lt > 0.0f ? at / lt : 0.0f;
+        const float nm = fmaxf(fmaxf(mx, fmaxf(mc[0], mc[1])), fmaxf(mc[2], mc[3]));
+        if (nm != -INFINITY) {
+            // a split with max -inf (no tokens) has zero sums and weighs exp2(-inf) = 0
+            const float f0 = exp2f(mx - nm);
+            L *= f0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= f0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float f = exp2f(mc[u] - nm);
+                L = fmaf(lc[u], f, L);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = fmaf(vc[u][e], f, x[e]);
+            }
+            mx = nm;
+        }
     }
-    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = L > 0.0f ? x[e] / L : 0.0f;
     // inverse rotation: D_V H(x) / d
+    fwht<LPV>(x, gl);
+    const uint32_t sbits = (a.vc.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
 #pragma unroll
-    for (int h = 1; h < D; h <<= 1) {
-        float nv = 0.0f;
-        if (grp == 0) nv = ((i & h) == 0) ? x[0][i] + x[0][i + h] : x[0][i - h] - x[0][i];
-        __syncthreads();
-        if (grp == 0) x[0][i] = nv;
-        __syncthreads();
-    }
-    if (grp == 0) {
-        const uint32_t neg = ((a.vc.sign_mask[i >> 5] >> (i & 31)) & 1u) << 31;
-        a.out[(int64_t)bh * D + i] = as_f(as_u(x[0][i] * (1.0f / (float)D)) ^ neg);
+    for (int e = 0; e < 8; ++e) x[e] = as_f(as_u(x[e] * (1.0f / (float)D)) ^ (((sbits >> e) & 1u) << 31));
+    if (valid) {
+        float4* o = reinterpret_cast<float4*>(a.out + (int64_t)bh * D + 8 * gl);
+        o[0] = make_float4(x[0], x[1], x[2], x[3]);
+        o[1] = make_float4(x[4], x[5], x[6], x[7]);
     }
 }
 
