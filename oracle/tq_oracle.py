@@ -307,7 +307,7 @@ def qjl_term(q: np.ndarray, qjl_packed: np.ndarray, norms16: np.ndarray,
 
 
 def attention(q: np.ndarray, k_codes, k_norms, v_codes, v_norms, kc: Codec, vc: Codec,
-              scale: float, k_qjl=None, k_gamma=None, S=None) -> np.ndarray:
+              scale: float, k_qjl=None, k_gamma=None, S=None, k_win=None, v_win=None) -> np.ndarray:
     """Exact softmax attention of one query group over one decoded cache.
 
     Decompress-then-attend ([P3] "결과 — 피크 VRAM" describes the reference
@@ -315,18 +315,32 @@ def attention(q: np.ndarray, k_codes, k_norms, v_codes, v_norms, kc: Codec, vc: 
     decoded, s_t = scale <q, K_hat_t> (+ the QJL estimate of the residual part),
     p = softmax(s) (max-subtracted), o = sum_t p_t V_hat_t.
 
-    q [n_q][d]; caches [ctx][...]; returns [n_q][d] float64.  An empty context
-    gives a zero output.
+    Residual window ([P3] "실험 설계" and "결과 — 피크 VRAM": the most recent
+    tokens are kept uncompressed and appended to the decompressed ones before
+    attention): k_win, v_win [w][d] are exact keys and values that join the
+    softmax after the decoded tokens, with s = scale <q, k_win_t> (no QJL term).
+
+    q [n_q][d]; caches [ctx][...]; returns [n_q][d] float64.  With no token at
+    all the output is zero.
     """
     q = np.atleast_2d(np.asarray(q, dtype=np.float64))
     ctx = k_codes.shape[0]
-    if ctx == 0:
+    w = 0 if k_win is None else np.asarray(k_win).shape[0]
+    if ctx + w == 0:
         return np.zeros((q.shape[0], vc.d))
-    K = decode(k_codes, k_norms, kc)
-    V = decode(v_codes, v_norms, vc)
-    s = scale * (q @ K.T)
-    if kc.qjl_m:
-        s = s + scale * qjl_term(q, k_qjl, k_norms, k_gamma, S, kc)
+    parts_s, parts_v = [], []
+    if ctx:
+        K = decode(k_codes, k_norms, kc)
+        s = scale * (q @ K.T)
+        if kc.qjl_m:
+            s = s + scale * qjl_term(q, k_qjl, k_norms, k_gamma, S, kc)
+        parts_s.append(s)
+        parts_v.append(decode(v_codes, v_norms, vc))
+    if w:
+        parts_s.append(scale * (q @ np.asarray(k_win, dtype=np.float64).T))
+        parts_v.append(np.asarray(v_win, dtype=np.float64))
+    s = np.concatenate(parts_s, axis=1)
+    V = np.concatenate(parts_v, axis=0)
     s = s - s.max(axis=1, keepdims=True)
     p = np.exp(s)
     p /= p.sum(axis=1, keepdims=True)
@@ -334,11 +348,13 @@ def attention(q: np.ndarray, k_codes, k_norms, v_codes, v_norms, kc: Codec, vc: 
 
 
 def gqa_attention(q, ctx_len, k_codes, k_norms, v_codes, v_norms, kc, vc, scale,
-                  k_qjl=None, k_gamma=None, S=None, heads=None):
+                  k_qjl=None, k_gamma=None, S=None, heads=None, k_win=None, v_win=None, win_len=None):
     """Batched grouped-query attention: q [B][Hq][d], caches [B][Hkv][cap][...].
 
     Query head h reads kv head h // (Hq/Hkv).  ``heads`` optionally restricts the
     computation to a list of (b, h) pairs; the result then has one row per pair.
+    Optional residual windows k_win, v_win [B][Hkv][win_cap][d] hold win_len[b]
+    exact tokens of sequence b.
     """
     B, Hq, d = q.shape
     Hkv = k_codes.shape[1]
@@ -351,6 +367,9 @@ def gqa_attention(q, ctx_len, k_codes, k_norms, v_codes, v_norms, kc, vc, scale,
         args = {}
         if kc.qjl_m:
             args = dict(k_qjl=k_qjl[b, kh, :n], k_gamma=k_gamma[b, kh, :n], S=S)
+        if k_win is not None:
+            wl = int(win_len[b])
+            args.update(k_win=k_win[b, kh, :wl], v_win=v_win[b, kh, :wl])
         out[row] = attention(q[b, h][None, :], k_codes[b, kh, :n], k_norms[b, kh, :n],
                              v_codes[b, kh, :n], v_norms[b, kh, :n], kc, vc, scale, **args)[0]
     return out

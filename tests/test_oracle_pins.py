@@ -339,6 +339,69 @@ def test_gqa_head_mapping():
         np.testing.assert_allclose(out[row], want, rtol=1e-14)
 
 
+def test_window_is_concatenation():
+    """Tokens moved from the packed cache into the residual window (as their
+    decoded values) leave the output unchanged: the window joins the same softmax."""
+    d = 128
+    kc, vc = o.Codec(4, d, 3), o.Codec(2, d, 3)
+    rng = np.random.default_rng(21)
+    ek = o.encode(rng.standard_normal((40, d)) * 20, kc)
+    ev = o.encode(rng.standard_normal((40, d)), vc)
+    K = o.decode(ek["codes"], ek["norms"], kc)
+    V = o.decode(ev["codes"], ev["norms"], vc)
+    q = rng.standard_normal((3, d))
+    full = o.attention(q, ek["codes"], ek["norms"], ev["codes"], ev["norms"], kc, vc, 0.09)
+    for j in (1, 7, 40):
+        split = o.attention(q, ek["codes"][:40 - j], ek["norms"][:40 - j], ev["codes"][:40 - j],
+                            ev["norms"][:40 - j], kc, vc, 0.09, k_win=K[40 - j:], v_win=V[40 - j:])
+        np.testing.assert_allclose(split, full, rtol=1e-12, atol=1e-14)
+
+
+def test_window_closed_forms():
+    """Window-only attention: two tokens give the logistic weight in closed form,
+    one token gives its value, and a dominating key selects its value."""
+    d = 64
+    kc, vc = o.Codec(3, d, 1), o.Codec(3, d, 1)
+    empty_k = np.zeros((0, d * 3 // 8), np.uint8)
+    empty_n = np.zeros(0, np.float16)
+    rng = np.random.default_rng(22)
+    q = np.zeros((1, d)); q[0, 5] = 2.0
+    kw = np.zeros((2, d)); kw[0, 5] = 1.5; kw[1, 5] = -0.5; kw[1, 7] = 9.0
+    vw = rng.standard_normal((2, d))
+    scale = 0.3
+    out = o.attention(q, empty_k, empty_n, empty_k, empty_n, kc, vc, scale, k_win=kw, v_win=vw)
+    # s = scale * (3.0, -1.0): p_0 = 1 / (1 + e^{-scale * 4})
+    p0 = 1.0 / (1.0 + math.exp(-scale * 4.0))
+    np.testing.assert_allclose(out[0], p0 * vw[0] + (1 - p0) * vw[1], rtol=1e-13)
+    one = o.attention(q, empty_k, empty_n, empty_k, empty_n, kc, vc, scale, k_win=kw[1:], v_win=vw[1:])
+    np.testing.assert_allclose(one[0], vw[1], rtol=1e-14)
+    # a window key 200 score units above every decoded key takes all the weight
+    ek = o.encode(rng.standard_normal((16, d)), kc)
+    ev = o.encode(rng.standard_normal((16, d)), vc)
+    kbig = np.zeros((1, d)); kbig[0, 5] = 200.0 / (scale * 2.0)
+    dom = o.attention(q, ek["codes"], ek["norms"], ev["codes"], ev["norms"], kc, vc, scale, k_win=kbig, v_win=vw[:1])
+    np.testing.assert_allclose(dom[0], vw[0], rtol=1e-12)
+
+
+def test_gqa_window_mapping():
+    d, B, Hq, Hkv, ctx, wcap = 64, 2, 4, 2, 5, 3
+    kc, vc = o.Codec(2, d, 1), o.Codec(2, d, 1)
+    rng = np.random.default_rng(23)
+    ek = o.encode(rng.standard_normal((B * Hkv * ctx, d)), kc)
+    ev = o.encode(rng.standard_normal((B * Hkv * ctx, d)), vc)
+    kcodes, kn = ek["codes"].reshape(B, Hkv, ctx, -1), ek["norms"].reshape(B, Hkv, ctx)
+    vcodes, vn = ev["codes"].reshape(B, Hkv, ctx, -1), ev["norms"].reshape(B, Hkv, ctx)
+    kw, vw = rng.standard_normal((B, Hkv, wcap, d)), rng.standard_normal((B, Hkv, wcap, d))
+    q = rng.standard_normal((B, Hq, d))
+    ctx_len, win_len = np.array([5, 0]), np.array([2, 3])
+    out = o.gqa_attention(q, ctx_len, kcodes, kn, vcodes, vn, kc, vc, 0.2, k_win=kw, v_win=vw, win_len=win_len)
+    for row, (b, h) in enumerate([(b, h) for b in range(B) for h in range(Hq)]):
+        kh, n, w = h // 2, ctx_len[b], win_len[b]
+        want = o.attention(q[b, h][None], kcodes[b, kh, :n], kn[b, kh, :n], vcodes[b, kh, :n], vn[b, kh, :n],
+                           kc, vc, 0.2, k_win=kw[b, kh, :w], v_win=vw[b, kh, :w])[0]
+        np.testing.assert_allclose(out[row], want, rtol=1e-14)
+
+
 # -------------------------------------------------------------------- QJL ----
 def test_qjl_sign_projection_closed_form():
     """E[sign(s.r) (s.a)] = sqrt(2/pi) <a, r>/||r|| for s ~ N(0, I)."""
