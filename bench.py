@@ -9,7 +9,9 @@ different layer's cache each time), so the 256 MB Infinity Cache cannot serve
 them.  `value` is algorithmic bytes per step (packed cache + queries + output)
 divided by the step time.
 
-Further legs in the same JSON line: tq_encode throughput (4 kv heads x 8192
+The decode leg also times the same step with a 128-token fp16 residual window
+per sequence (tq_attn_decode_rw).  Further legs in the same JSON line:
+tq_encode throughput (4 kv heads x 8192
 tokens, fp16, K 4-bit + V 2-bit per step, over a 1 GiB rotating input pool),
 long-context decode (8 kv heads x 2^20 tokens, K3/V3, 64 bf16 query heads) and
 inner-product search (2^20 x 256 database, 3-bit + QJL m=256, 1024 queries,
@@ -164,6 +166,21 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
 
     ms = timed_loop(step, steps, warmup, torch)
     scan_ms = scan_launch_ms(tq, torch, args_of, steps)
+
+    # the same step with a residual window of 128 exact fp16 tokens per
+    # sequence (the pages' rw = 128) joining the softmax: tq_attn_decode_rw
+    rw = 128
+    wins = [synth.kv_block(Hkv * B, rw, d, 9000 + r, device="cuda", dtype=torch.float16) for r in range(replicas)]
+    wins = [(k.view(B, Hkv, rw, d).contiguous(), v.view(B, Hkv, rw, d).contiguous()) for k, v in wins]
+    win_len = torch.full((B,), rw, dtype=torch.int32, device="cuda")
+
+    def step_rw(i):
+        c, (kw, vw) = caches[i % replicas], wins[i % replicas]
+        tq.tq_attn_decode_rw(kc, vc, q, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"],
+                             kw, vw, win_len, scale, out, ws)
+
+    ms_rw = timed_loop(step_rw, steps, max(warmup // 4, 1), torch)
+    win_bytes = 2 * B * Hkv * rw * d * 2
     token_heads = B * Hkv * ctx
     per_token_head = (kc.code_bytes + 2) + (vc.code_bytes + 2)  # 100 B
     cache_bytes = token_heads * per_token_head
@@ -179,6 +196,14 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
         "token_heads": token_heads,
         "replicas": replicas,
         "fma_per_token_head": 2 * g * d,
+        "window": {
+            "workload": "the same step plus a residual window of 128 exact fp16 tokens per sequence (tq_attn_decode_rw)",
+            "win_tokens": rw,
+            "ms_per_step": ms_rw,
+            "gbs": (cache_bytes + win_bytes + q.numel() * 2 + out.numel() * 4) / (ms_rw * 1e-3) / 1e9,
+            "window_bytes": win_bytes,
+            "extra_ms_vs_packed_only": ms_rw - ms,
+        },
     }, (kc, vc, caches[0], q)
 
 

@@ -214,7 +214,39 @@ int tq_attn_combine(const tq_codec *kc, const tq_codec *vc,
                     float scale, float *out, void *workspace, size_t workspace_bytes,
                     void *stream);
 
-/* Bytes of workspace tq_attn_decode needs for these sizes (0 on bad arguments). */
+/*
+ * tq_attn_decode_rw -- decode attention over the packed cache plus a residual
+ * window of exact recent tokens.  [P3] ("실험 설계", "결과 — 피크 VRAM")
+ * describes the V3 cache: the most recent rw tokens stay uncompressed and are
+ * appended to the decompressed ones before attention.  Here the window tokens
+ * join the same softmax as the ctx_len[b] packed tokens, with score
+ * scale <q, k_win_t> (exact keys, no QJL term) and value v_win_t:
+ *   o = sum over packed and window tokens of softmax(s)_t * value_t.
+ *
+ *   k_win, v_win  [batch][n_kv_heads][win_cap][d] in win_dtype (TQ_F32, TQ_F16
+ *                 or TQ_BF16), 16-byte aligned; caller-owned, read only.
+ *   win_len       [batch] int32 on the device: tokens used in each sequence's
+ *                 window, clamped to [0, win_cap].
+ *   win_cap       window capacity; 0 means no window (then k_win, v_win and
+ *                 win_len may be NULL and the call equals tq_attn_decode).
+ * Every other argument, the workspace (tq_attn_workspace_bytes covers both
+ * calls) and the error behaviour are those of tq_attn_decode; additionally
+ * win_cap < 0, a bad win_dtype, or NULL/misaligned window pointers with
+ * win_cap > 0 give TQ_EINVAL.  A sequence with no packed and no window token
+ * gives a zero output row.
+ */
+int tq_attn_decode_rw(const tq_codec *kc, const tq_codec *vc,
+                      const void *q, int q_dtype, int batch, int n_q_heads, int n_kv_heads,
+                      const int32_t *ctx_len, int64_t ctx_cap,
+                      const uint8_t *k_codes, const uint16_t *k_norms,
+                      const uint8_t *k_qjl, const uint16_t *k_gamma, const float *qjl_S,
+                      const uint8_t *v_codes, const uint16_t *v_norms,
+                      const void *k_win, const void *v_win, int win_dtype,
+                      const int32_t *win_len, int win_cap,
+                      float scale, float *out, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Bytes of workspace tq_attn_decode (and tq_attn_decode_rw) needs for these sizes (0 on bad arguments). */
 size_t tq_attn_workspace_bytes(const tq_codec *kc, const tq_codec *vc, int batch,
                                int n_q_heads, int n_kv_heads, int64_t ctx_cap);
 

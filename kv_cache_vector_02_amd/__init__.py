@@ -23,7 +23,7 @@ _DTYPES = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16
 
 EXPORTS = (
     "tq_codebook", "tq_encode", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
-    "tq_attn_combine", "tq_attn_workspace_bytes",
+    "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror",
 )
 
@@ -79,6 +79,7 @@ def _load():
         "tq_attn_prepare": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
         "tq_attn_scan": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
         "tq_attn_combine": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
+        "tq_attn_decode_rw": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, P, P, I, P, I, F, P, P, SZ, P]),
         "tq_attn_workspace_bytes": (SZ, [CP, CP, I, I, I, I64]),
         "tq_ip_search": (I, [CP, P, I, P, P, P, P, P, I64, I, P, P, P, SZ, P]),
         "tq_search_workspace_bytes": (SZ, [CP, I, I64, I]),
@@ -184,6 +185,29 @@ def tq_attn_decode(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.T
     """q [B][Hq][d]; caches [B][Hkv][ctx_cap][...] contiguous; out [B][Hq][d] fp32."""
     _attn("tq_attn_decode", kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, scale, out, workspace,
           k_qjl, k_gamma, qjl_S, stream)
+
+
+def tq_attn_decode_rw(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.Tensor,
+                      k_codes: torch.Tensor, k_norms: torch.Tensor, v_codes: torch.Tensor, v_norms: torch.Tensor,
+                      k_win: torch.Tensor, v_win: torch.Tensor, win_len: torch.Tensor,
+                      scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                      k_qjl: torch.Tensor | None = None, k_gamma: torch.Tensor | None = None,
+                      qjl_S: torch.Tensor | None = None, stream=None) -> None:
+    """tq_attn_decode plus a residual window: k_win, v_win [B][Hkv][win_cap][d]
+    (fp32/fp16/bf16, contiguous) holding win_len[b] exact recent tokens."""
+    B, Hq, _ = q.shape
+    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
+    for t in (q, k_codes, k_norms, v_codes, v_norms, out, ctx_len, k_win, v_win, win_len):
+        if not t.is_contiguous():
+            raise ValueError("attention tensors must be contiguous")
+    if k_win.dim() != 4 or k_win.shape != v_win.shape or k_win.dtype != v_win.dtype:
+        raise ValueError("k_win and v_win must be [B][Hkv][win_cap][d] of one dtype")
+    _check(_lib.tq_attn_decode_rw(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _DTYPES[q.dtype], B, Hq, Hkv,
+                                  _ptr(ctx_len), cap, _ptr(k_codes), _ptr(k_norms), _ptr(k_qjl), _ptr(k_gamma),
+                                  _ptr(qjl_S), _ptr(v_codes), _ptr(v_norms), _ptr(k_win), _ptr(v_win),
+                                  _DTYPES[k_win.dtype], _ptr(win_len), k_win.shape[2], ctypes.c_float(scale),
+                                  _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream, q)), "tq_attn_decode_rw")
 
 
 def tq_attn_prepare(*args, **kw) -> None:

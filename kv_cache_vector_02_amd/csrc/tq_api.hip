@@ -217,7 +217,8 @@ size_t tq_attn_workspace_bytes(const tq_codec* kc, const tq_codec* vc, int batch
 static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch,
                       int n_q_heads, int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap,
                       const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl, const uint16_t* k_gamma,
-                      const float* qjl_S, const uint8_t* v_codes, const uint16_t* v_norms, float scale, float* out,
+                      const float* qjl_S, const uint8_t* v_codes, const uint16_t* v_norms, const void* k_win,
+                      const void* v_win, int win_dtype, const int32_t* win_len, int win_cap, float scale, float* out,
                       void* workspace, size_t workspace_bytes, tqi::AttnArgs* a) {
     int splits, G;
     int64_t per;
@@ -231,6 +232,12 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
     if (kc->qjl_m > 0 && (!k_qjl || !k_gamma || !qjl_S || !aligned(k_qjl, 4) || !aligned(k_gamma, 2)))
         return TQ_EINVAL;
     if (!isfinite(scale)) return TQ_EINVAL;
+    if (win_cap < 0) return TQ_EINVAL;
+    if (win_cap > 0) {
+        if (win_dtype != TQ_F32 && win_dtype != TQ_F16 && win_dtype != TQ_BF16) return TQ_EINVAL;
+        if (!k_win || !v_win || !win_len || !aligned(k_win, 16) || !aligned(v_win, 16) || !aligned(win_len, 4))
+            return TQ_EINVAL;
+    }
     const int d = kc->d, m = kc->qjl_m;
     const size_t need = tqi::attn_workspace(batch, n_q_heads, d, m, splits);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return TQ_EWORKSPACE;
@@ -263,6 +270,11 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
     a->part = ws + al(heads * (size_t)m);
     a->splits = splits;
     a->split_tokens = per;
+    a->k_win = k_win;
+    a->v_win = v_win;
+    a->win_dtype = win_dtype;
+    a->win_len = win_len;
+    a->win_cap = win_cap;
     return TQ_OK;
 }
 
@@ -274,8 +286,8 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
              size_t workspace_bytes, void* stream) {                                                          \
         tqi::AttnArgs a;                                                                                      \
         const int rc = attn_setup(kc, vc, q, q_dtype, batch, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes, \
-                                  k_norms, k_qjl, k_gamma, qjl_S, v_codes, v_norms, scale, out, workspace,     \
-                                  workspace_bytes, &a);                                                       \
+                                  k_norms, k_qjl, k_gamma, qjl_S, v_codes, v_norms, nullptr, nullptr, 0,       \
+                                  nullptr, 0, scale, out, workspace, workspace_bytes, &a);                   \
         if (rc != TQ_OK) return rc;                                                                           \
         return finish(tqi::launch_attn(a, STAGE, (hipStream_t)stream));                                      \
     }
@@ -284,6 +296,20 @@ TQ_ATTN_ENTRY(tq_attn_decode, tqi::ATTN_ALL)
 TQ_ATTN_ENTRY(tq_attn_prepare, tqi::ATTN_PREPARE)
 TQ_ATTN_ENTRY(tq_attn_scan, tqi::ATTN_SCAN)
 TQ_ATTN_ENTRY(tq_attn_combine, tqi::ATTN_COMBINE)
+
+int tq_attn_decode_rw(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch, int n_q_heads,
+                      int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap, const uint8_t* k_codes,
+                      const uint16_t* k_norms, const uint8_t* k_qjl, const uint16_t* k_gamma, const float* qjl_S,
+                      const uint8_t* v_codes, const uint16_t* v_norms, const void* k_win, const void* v_win,
+                      int win_dtype, const int32_t* win_len, int win_cap, float scale, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    tqi::AttnArgs a;
+    const int rc = attn_setup(kc, vc, q, q_dtype, batch, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes, k_norms,
+                              k_qjl, k_gamma, qjl_S, v_codes, v_norms, k_win, v_win, win_dtype, win_len, win_cap,
+                              scale, out, workspace, workspace_bytes, &a);
+    if (rc != TQ_OK) return rc;
+    return finish(tqi::launch_attn(a, tqi::ATTN_ALL | tqi::ATTN_WINDOW, (hipStream_t)stream));
+}
 
 static int search_check(const tq_codec* c, int n_q, int64_t n_db, int k) {
     if (!c) return TQ_EINVAL;

@@ -1,6 +1,7 @@
 // Host side of decode attention: launch planning, workspace layout and the
 // launches (QJL query projection when the keys carry QJL bits, split-K scan,
-// combine + inverse transform).
+// combine + inverse transform, or with a residual window the window kernel,
+// which also combines).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -119,6 +120,15 @@ static hipError_t launch_qprep_combine(const AttnArgs& a, hipStream_t s, bool pr
     return hipGetLastError();
 }
 
+template <int D>
+static void launch_window(const AttnArgs& a, int grid, hipStream_t s) {
+    switch (a.win_dtype) {
+        case TQ_F32: hipLaunchKernelGGL((attn::window_kernel<D, 0>), dim3(grid), dim3(256), 0, s, a); break;
+        case TQ_F16: hipLaunchKernelGGL((attn::window_kernel<D, 1>), dim3(grid), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((attn::window_kernel<D, 2>), dim3(grid), dim3(256), 0, s, a); break;
+    }
+}
+
 static hipError_t launch_split_any(const AttnArgs& a, hipStream_t s) {
     if (a.kc.d == 128) {
         switch (a.kc.bits) {
@@ -147,6 +157,14 @@ hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s) {
     if (stages & ATTN_SCAN) {
         e = launch_split_any(a, s);
         if (e != hipSuccess) return e;
+    }
+    if ((stages & ATTN_WINDOW) && a.win_cap > 0) {
+        // the window kernel also merges the splits and writes the output:
+        // one block per (batch, query head), heads of one kv head on one XCD
+        const int grid = ((a.batch * a.hkv + 7) & ~7) * a.g;
+        if (d128) launch_window<128>(a, grid, s);
+        else launch_window<256>(a, grid, s);
+        return hipGetLastError();
     }
     if (stages & ATTN_COMBINE) e = d128 ? launch_qprep_combine<128>(a, s, false) : launch_qprep_combine<256>(a, s, false);
     return e;

@@ -884,20 +884,17 @@ void split_kernel(AttnArgs a) {
 // [8 gl, 8 gl + 8) as in the encoder's transform layout: the log-sum-exp merge
 // of the head's split partials runs in registers, then the inverse transform
 // D_V H(.) / d through lane exchanges.  No LDS and no barriers.
+//
+// combine_head merges the splits of head bh into the running state (mx, L, x)
+// (rotated domain, log2 units) and writes the output row when `store`.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
-    constexpr int LPV = D / 8, HPB = 256 / LPV;  // lanes per head, heads per block
-    const int tid = threadIdx.x, gl = tid & (LPV - 1);
-    const int heads = a.batch * a.hq;
-    const int bh = blockIdx.x * HPB + tid / LPV;
-    const bool valid = bh < heads;  // uniform inside a lane group
+__device__ __forceinline__ void combine_head(const AttnArgs& a, int64_t bh, int gl, bool store, float mx, float L,
+                                             float (&x)[8]) {
+    constexpr int LPV = D / 8;
     const int S = a.splits;
-    const float* p = a.part + (int64_t)(valid ? bh : 0) * S * (D + 2);
+    const float* p = a.part + bh * S * (D + 2);
     // online merge over chunks of four splits: the loads of a chunk go out
     // together, its max raises the running one and rescales the sums
-    float mx = -INFINITY, L = 0.0f, x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = 0.0f;
     for (int s0 = 0; s0 < S; s0 += 4) {
         float mc[4], lc[4], vc[4][8];
 #pragma unroll
@@ -940,11 +937,179 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     const uint32_t sbits = (a.vc.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = as_f(as_u(x[e] * (1.0f / (float)D)) ^ (((sbits >> e) & 1u) << 31));
-    if (valid) {
-        float4* o = reinterpret_cast<float4*>(a.out + (int64_t)bh * D + 8 * gl);
+    if (store) {
+        float4* o = reinterpret_cast<float4*>(a.out + bh * D + 8 * gl);
         o[0] = make_float4(x[0], x[1], x[2], x[3]);
         o[1] = make_float4(x[4], x[5], x[6], x[7]);
     }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+    constexpr int LPV = D / 8, HPB = 256 / LPV;  // lanes per head, heads per block
+    const int tid = threadIdx.x, gl = tid & (LPV - 1);
+    const int heads = a.batch * a.hq;
+    const int bh = blockIdx.x * HPB + tid / LPV;
+    const bool valid = bh < heads;  // uniform inside a lane group
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+    combine_head<D>(a, valid ? bh : 0, gl, valid, -INFINITY, 0.0f, x);
+}
+
+// ---------------------------------------------------------------- window ----
+// Residual window: the most recent tokens of a sequence kept exact, which join
+// the softmax after the packed ones (the V3 cache of the PyTorch reproduction,
+// "[GitHub 탐방] TurboQuant 3-bit KV 캐시 압축", "실험 설계" and "결과 — 피크
+// VRAM").  One block of 4 waves per (batch, query head), XCD-aware; a lane group of D/8
+// lanes takes one token at a time, lane gl holding dims [8 gl, 8 gl + 8), and
+// loads U tokens' rows before using any of them.  Each group runs an online
+// softmax in the scan's log2 units; groups merge by lane exchanges, waves
+// through LDS.  The window's weighted value sum y enters the merge with the
+// head's split partials as x = H(D_V y), so that the final D_V H(.) / d returns
+// y; this kernel then writes the output (it replaces the combine launch).
+template <int D, int WDT>
+__global__ __launch_bounds__(256) void window_kernel(AttnArgs a) {
+    constexpr int LPV = D / 8, TPW = 64 / LPV;  // lanes per token, tokens per wave
+    constexpr int U = 8;                        // tokens per lane group per round, loaded together
+    constexpr int STEP = 4 * TPW;               // tokens per block pass (4 waves)
+    __shared__ float mrg[4][D + 2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gl = lane & (LPV - 1), tg = lane / LPV;
+    // One block per (batch, query head).  Workgroups are dealt round-robin to
+    // the 8 XCDs, each with its own L2: block i serves (batch, kv head) unit
+    // i mod U8 (U8 = units rounded up to a multiple of 8) and query head
+    // i / U8 of its group, so the g heads that read one window share an XCD
+    // and its L2.
+    const int units = a.batch * a.hkv, u8 = (units + 7) & ~7;
+    const int unit = blockIdx.x % u8, hl = blockIdx.x / u8;
+    if (unit >= units) return;  // whole block: before any barrier
+    const int b = unit / a.hkv, kvh = unit - b * a.hkv;
+    const int h = kvh * a.g + hl;
+    const int bh = b * a.hq + h;
+    const int wl_raw = a.win_len[b];
+    // the query's raw words now, converted after the first window loads are out
+    uint4 qw0 = make_uint4(0u, 0u, 0u, 0u), qw1 = qw0;
+    if (a.q_dtype == TQ_F32) {
+        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + (int64_t)bh * D + 8 * gl);
+        qw0 = qp[0];
+        qw1 = qp[1];
+    } else {
+        qw0 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + (int64_t)bh * D + 8 * gl);
+    }
+    float q[8];
+    bool qready = false;
+    const float qs = a.scale * kLog2e;
+    const int64_t wrow = ((int64_t)b * a.hkv + kvh) * a.win_cap;
+    const char* kw = static_cast<const char*>(a.k_win);
+    const char* vw = static_cast<const char*>(a.v_win);
+    float m = -INFINITY, l = 0.0f, y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+    // Token of (round r, slot u) for this lane group: t0 + u * STEP with
+    // t0 = r * U * STEP + wave * TPW + tg.  Row indices are clamped to the
+    // capacity, so the first round's loads go out together with the window
+    // length's and the query's; tokens at or past the length are masked.  The
+    // lanes of one group share t0 and so their trip count: the in-group
+    // reduction only reads active lanes.
+    int wl = -1;
+    for (int t0 = wave * TPW + tg;; t0 += U * STEP) {
+        float k[U][8], v[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int t = t0 + u * STEP;
+            t = t < a.win_cap ? t : a.win_cap - 1;
+            // the window dtype is a template argument: no branch between the
+            // loads, so all 2U of them are in flight before the first use
+            const int64_t off = ((wrow + t) * D + 8 * gl) * elem_bytes<WDT>();
+            load8<WDT>(kw + off, k[u]);
+            load8<WDT>(vw + off, v[u]);
+        }
+        if (wl < 0) wl = wl_raw < 0 ? 0 : (wl_raw > a.win_cap ? a.win_cap : wl_raw);
+        if (!qready) {
+            const uint32_t w[8] = {qw0.x, qw0.y, qw0.z, qw0.w, qw1.x, qw1.y, qw1.z, qw1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t hw = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                q[e] = a.q_dtype == TQ_F32 ? as_f(w[e]) : (a.q_dtype == TQ_F16 ? half_bits_to_float(hw) : as_f(hw << 16));
+            }
+            qready = true;
+        }
+        float sc[U], cm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = fmaf(q[e], k[u][e], dot);
+            const float su = group_sum<LPV>(dot) * qs;  // every lane, then masked: no branch
+            sc[u] = t0 + u * STEP < wl ? su : -INFINITY;
+            cm = fmaxf(cm, sc[u]);
+        }
+        const float mn = fmaxf(m, cm);
+        if (mn != -INFINITY) {
+            const float f = exp2f(m - mn);
+            l *= f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float p = exp2f(sc[u] - mn);
+                l += p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = fmaf(p, v[u][e], y[e]);
+            }
+            m = mn;
+        }
+        if (t0 + U * STEP >= wl) break;
+    }
+    // merge (m, l, y) of two states; an empty state has m = -inf and zeros
+    auto join = [&](float mo, float lo, const float (&yo)[8]) __attribute__((always_inline)) {
+        const float mn = fmaxf(m, mo);
+        if (mn != -INFINITY) {
+            const float f = exp2f(m - mn), fo = exp2f(mo - mn);
+            l = l * f + lo * fo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = y[e] * f + yo[e] * fo;
+            m = mn;
+        }
+    };
+    // the TPW lane groups of the wave (lane bits above the group)
+    auto merge_lanes = [&](auto mc) __attribute__((always_inline)) {
+        constexpr int M = decltype(mc)::value;
+        const float mo = xor_lane<M>(m), lo = xor_lane<M>(l);
+        float yo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yo[e] = xor_lane<M>(y[e]);
+        join(mo, lo, yo);
+    };
+    if constexpr (TPW >= 4) merge_lanes(std::integral_constant<int, 16>{});
+    merge_lanes(std::integral_constant<int, 32>{});
+    // the 4 waves, through LDS
+    if (tg == 0) {
+        if (gl == 0) {
+            mrg[wave][0] = m;
+            mrg[wave][1] = l;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mrg[wave][2 + 8 * gl + e] = y[e];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+        float yo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yo[e] = mrg[w][2 + 8 * gl + e];
+        join(mrg[w][0], mrg[w][1], yo);
+    }
+    // the window's share in the rotated domain, x = H(D_V y), then the merge
+    // with the head's split partials and the output (every group of wave 0
+    // holds the same state; group 0 stores)
+    const uint32_t sbits = (a.vc.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = as_f(as_u(y[e]) ^ (((sbits >> e) & 1u) << 31));
+    fwht<LPV>(y, gl);
+    combine_head<D>(a, bh, gl, tg == 0, m, l, y);
 }
 
 template <int D, int KB, int VB, int G>

@@ -61,6 +61,12 @@ struct AttnArgs {
     float* part;      // [batch][hq][splits][d + 2]
     int splits;
     int64_t split_tokens;  // tokens per split (multiple of 64)
+    // residual window of exact tokens: [batch][hkv][win_cap][d] in win_dtype
+    const void* k_win;
+    const void* v_win;
+    int win_dtype;
+    const int32_t* win_len;  // [batch]
+    int win_cap;             // 0: no window
 };
 
 // Host-side helpers.
@@ -69,7 +75,7 @@ void fill_codec_args(const tq_codec* c, CodecArgs* a);
 // Launchers (return hipError_t of the launch).
 hipError_t launch_encode(const EncodeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
-enum AttnStage { ATTN_PREPARE = 1, ATTN_SCAN = 2, ATTN_COMBINE = 4, ATTN_ALL = 7 };
+enum AttnStage { ATTN_PREPARE = 1, ATTN_SCAN = 2, ATTN_COMBINE = 4, ATTN_ALL = 7, ATTN_WINDOW = 8 };
 hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s);
 void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int d, int kb, int vb, bool qjl, int* splits,
                int64_t* split_tokens, int* heads_per_chunk);

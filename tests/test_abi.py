@@ -106,6 +106,25 @@ def test_attention_argument_errors():
     assert call(kq, vc, wsb=tq.tq_attn_workspace_bytes(kq, vc, 2, 14, 2, 1000)) == tq.TQ_EINVAL
 
 
+def test_attention_window_argument_errors():
+    kc = tq.tq_codebook(4, 128, 0)
+    vc = tq.tq_codebook(2, 128, 0)
+    P = FAKE
+    ws = tq.tq_attn_workspace_bytes(kc, vc, 2, 14, 2, 1000)
+
+    def call(kw=P, vw=P, wdt=1, wl=P, wcap=128, wsb=ws):
+        return tq.raw_call("tq_attn_decode_rw", ctypes.byref(kc), ctypes.byref(vc), P, 1, 2, 14, 2, P, 1000,
+                           P, P, None, None, None, P, P, kw, vw, wdt, wl, wcap, ctypes.c_float(0.1), P, P, wsb, None)
+
+    assert call(wcap=-1) == tq.TQ_EINVAL
+    assert call(kw=None) == tq.TQ_EINVAL
+    assert call(vw=None) == tq.TQ_EINVAL
+    assert call(wl=None) == tq.TQ_EINVAL
+    assert call(wdt=7) == tq.TQ_EINVAL
+    assert call(kw=ctypes.c_void_p((1 << 20) + 8)) == tq.TQ_EINVAL  # not 16-byte aligned
+    assert call(wsb=ws - 1) == tq.TQ_EWORKSPACE
+
+
 def test_search_argument_errors():
     c = tq.tq_codebook(3, 256, 0, 256)
     P = FAKE
