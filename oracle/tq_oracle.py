@@ -288,6 +288,32 @@ def decode(codes: np.ndarray, norms16: np.ndarray, codec: Codec) -> np.ndarray:
     return np.asarray(norms16, dtype=np.float64)[:, None] * w * codec.signs[None, :]
 
 
+def append(codes, norms16, x_new, pos, codec: Codec, S=None, qjl=None, gamma16=None):
+    """Decode-step append into a packed cache ([P3] "결과 — 피크 VRAM": every
+    step the new K/V enters the cache before attention).
+
+    codes [B][H][cap][row], norms16 [B][H][cap] (and with QJL qjl [B][H][cap][m/8],
+    gamma16 [B][H][cap]) are updated in place: the new vector x_new[b][h] of every
+    (sequence, head) is encoded and written at token pos[b]; a position outside
+    [0, cap) writes nothing.  Returns the encode() result of all new vectors.
+    """
+    B, H, cap = norms16.shape
+    flat = np.asarray(x_new, dtype=np.float64).reshape(B * H, -1)
+    enc = encode(flat, codec, S)
+    for b in range(B):
+        p = int(pos[b])
+        if not 0 <= p < cap:
+            continue
+        for h in range(H):
+            r = b * H + h
+            codes[b, h, p] = enc["codes"][r]
+            norms16[b, h, p] = enc["norms"][r]
+            if codec.qjl_m:
+                qjl[b, h, p] = enc["qjl"][r]
+                gamma16[b, h, p] = enc["gamma"][r]
+    return enc
+
+
 def qjl_term(q: np.ndarray, qjl_packed: np.ndarray, norms16: np.ndarray,
              gamma16: np.ndarray, S: np.ndarray, codec: Codec) -> np.ndarray:
     """QJL estimate of <q, x - x_hat> for every (query, row) pair.

@@ -402,6 +402,41 @@ def test_gqa_window_mapping():
         np.testing.assert_allclose(out[row], want, rtol=1e-14)
 
 
+def test_append_token_by_token_equals_whole_encode():
+    """Appending a sequence one token per step (each sequence at its own
+    position) gives the bytes of encoding every token at once; positions
+    outside the cache write nothing."""
+    d, B, H, cap, steps = 64, 3, 2, 6, 4
+    rng = np.random.default_rng(24)
+    for m in (0, 32):
+        codec = o.Codec(3, d, 4, m)
+        S = rng.standard_normal((m, d)) if m else None
+        X = rng.standard_normal((B, H, steps, d)) * 5
+        start = np.array([0, 2, 4])  # sequence 2 runs past the end at step 2
+        rowb = d * 3 // 8
+        codes = np.full((B, H, cap, rowb), 0xAB, np.uint8)
+        norms = np.full((B, H, cap), 0x1234, np.uint16).view(np.float16)
+        qjl = np.full((B, H, cap, max(m // 8, 1)), 0xCD, np.uint8)
+        gamma = np.full((B, H, cap), 0x4321, np.uint16).view(np.float16)
+        for t in range(steps):
+            o.append(codes, norms, X[:, :, t], start + t, codec, S, qjl, gamma)
+        whole = o.encode(X.reshape(-1, d), codec, S)
+        for b in range(B):
+            for h in range(H):
+                for t in range(steps):
+                    p = start[b] + t
+                    r = (b * H + h) * steps + t
+                    if p < cap:
+                        assert np.array_equal(codes[b, h, p], whole["codes"][r])
+                        assert norms[b, h, p] == whole["norms"][r]
+                        if m:
+                            assert np.array_equal(qjl[b, h, p], whole["qjl"][r])
+                            assert gamma[b, h, p] == whole["gamma"][r]
+                untouched = [p for p in range(cap) if not start[b] <= p < start[b] + steps]
+                assert np.all(codes[b, h, untouched] == 0xAB)
+                assert np.all(norms[b, h, untouched].view(np.uint16) == 0x1234)
+
+
 # -------------------------------------------------------------------- QJL ----
 def test_qjl_sign_projection_closed_form():
     """E[sign(s.r) (s.a)] = sqrt(2/pi) <a, r>/||r|| for s ~ N(0, I)."""
