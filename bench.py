@@ -181,6 +181,25 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
 
     ms_rw = timed_loop(step_rw, steps, max(warmup // 4, 1), torch)
     win_bytes = 2 * B * Hkv * rw * d * 2
+
+    # the decode-step append: the new token's K and V of every (sequence, kv
+    # head) encoded into the packed cache at ctx_len[b] (tq_append), alone and
+    # followed by the attention call
+    pos = torch.full((B,), ctx - 1, dtype=torch.int32, device="cuda")
+    k_new, v_new = synth.kv_block(B * Hkv, 1, d, 9100, device="cuda", dtype=torch.float16)
+    k_new, v_new = k_new.view(B, Hkv, d).contiguous(), v_new.view(B, Hkv, d).contiguous()
+
+    def append(i):
+        c = caches[i % replicas]
+        tq.tq_append(kc, k_new, pos, c["k_codes"], c["k_norms"])
+        tq.tq_append(vc, v_new, pos, c["v_codes"], c["v_norms"])
+
+    def append_attend(i):
+        append(i)
+        tq.tq_attn_decode(*args_of(i))
+
+    ms_append = timed_loop(append, steps, max(warmup // 4, 1), torch)
+    ms_append_attend = timed_loop(append_attend, steps, max(warmup // 4, 1), torch)
     token_heads = B * Hkv * ctx
     per_token_head = (kc.code_bytes + 2) + (vc.code_bytes + 2)  # 100 B
     cache_bytes = token_heads * per_token_head
@@ -203,6 +222,12 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
             "gbs": (cache_bytes + win_bytes + q.numel() * 2 + out.numel() * 4) / (ms_rw * 1e-3) / 1e9,
             "window_bytes": win_bytes,
             "extra_ms_vs_packed_only": ms_rw - ms,
+        },
+        "append": {
+            "workload": "one new token per (sequence, kv head) appended to the K4 and V2 caches (tq_append x 2)",
+            "vectors": 2 * B * Hkv,
+            "ms_per_append": ms_append,
+            "ms_per_append_and_attend": ms_append_attend,
         },
     }, (kc, vc, caches[0], q)
 

@@ -123,6 +123,29 @@ int tq_encode(const tq_codec *c, const void *x, int x_dtype, int64_t n, int64_t 
               const float *qjl_S, uint8_t *qjl_bits, uint16_t *qjl_gamma_f16, void *stream);
 
 /*
+ * tq_append -- the decode-step append: encode the new token of every
+ * (sequence, head) into the packed cache at that sequence's position.  [P3]
+ * ("결과 — 피크 VRAM") describes each decode step adding the new K/V to the
+ * cache before attention; with a residual window ([P3] "실험 설계") the token
+ * leaving the window is the one appended.  Same arithmetic as tq_encode.
+ *
+ *   x         [batch][n_heads][d] elements of x_dtype, contiguous, 16-byte aligned.
+ *   pos       [batch] int32 on the device: token slot written for sequence b
+ *             (read by the kernel, not updated); a slot outside [0, ctx_cap)
+ *             writes nothing for that sequence.
+ *   codes     cache plane [batch][n_heads][ctx_cap][d*bits/8] (the layout the
+ *             attention calls read), 4-byte aligned; norms_f16 [batch][n_heads][ctx_cap].
+ *   qjl_S, qjl_bits [batch][n_heads][ctx_cap][m/8], qjl_gamma_f16
+ *             [batch][n_heads][ctx_cap]: as in tq_encode, NULL when m = 0.
+ * Only the addressed slots are written.  Errors: TQ_EINVAL for NULL or
+ * misaligned pointers, a bad x_dtype, or batch, n_heads or ctx_cap <= 0;
+ * TQ_EUNSUPPORTED for an unsupported codec.
+ */
+int tq_append(const tq_codec *c, const void *x, int x_dtype, int batch, int n_heads,
+              const int32_t *pos, int64_t ctx_cap, uint8_t *codes, uint16_t *norms_f16,
+              const float *qjl_S, uint8_t *qjl_bits, uint16_t *qjl_gamma_f16, void *stream);
+
+/*
  * tq_decode -- reconstruct x_hat = half_norm * D H(c[idx]) / d for n rows
  * (the inverse rotation; used to check reconstructions, not on the hot path).
  *   codes: row i at codes + i*code_row_stride (4-byte aligned stride and base);

@@ -22,7 +22,7 @@ TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 _DTYPES = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16}
 
 EXPORTS = (
-    "tq_codebook", "tq_encode", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
+    "tq_codebook", "tq_encode", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
     "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror",
 )
@@ -74,6 +74,7 @@ def _load():
     sig = {
         "tq_codebook": (I, [I, I, ctypes.c_uint64, I, CP]),
         "tq_encode": (I, [CP, P, I, I64, I64, P, I64, P, P, P, P, P]),
+        "tq_append": (I, [CP, P, I, I, I, P, I64, P, P, P, P, P, P]),
         "tq_decode": (I, [CP, P, I64, P, I64, P, P]),
         "tq_attn_decode": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
         "tq_attn_prepare": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
@@ -149,6 +150,22 @@ def tq_encode(codec: tq_codec, x: torch.Tensor, codes: torch.Tensor, norms: torc
     _check(_lib.tq_encode(ctypes.byref(codec), _ptr(x), _DTYPES[x.dtype], n, x.stride(0), _ptr(codes),
                           codes.stride(0), _ptr(norms), _ptr(qjl_S), _ptr(qjl_bits), _ptr(qjl_gamma),
                           _stream(stream, x)), "tq_encode")
+
+
+def tq_append(codec: tq_codec, x: torch.Tensor, pos: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor,
+              qjl_S: torch.Tensor | None = None, qjl_bits: torch.Tensor | None = None,
+              qjl_gamma: torch.Tensor | None = None, stream=None) -> None:
+    """x [B][H][d] (fp32/fp16/bf16) contiguous; pos [B] int32 (device); codes
+    [B][H][cap][d*bits/8] uint8 and norms [B][H][cap] (2-byte dtype) contiguous."""
+    for t in (x, pos, codes, norms):
+        if not t.is_contiguous():
+            raise ValueError("append tensors must be contiguous")
+    if x.dim() != 3 or codes.dim() != 4 or codes.shape[:2] != x.shape[:2]:
+        raise ValueError("x [B][H][d] and codes [B][H][cap][row] must agree")
+    B, H = x.shape[0], x.shape[1]
+    _check(_lib.tq_append(ctypes.byref(codec), _ptr(x), _DTYPES[x.dtype], B, H, _ptr(pos), codes.shape[2],
+                          _ptr(codes), _ptr(norms), _ptr(qjl_S), _ptr(qjl_bits), _ptr(qjl_gamma),
+                          _stream(stream, x)), "tq_append")
 
 
 def tq_decode(codec: tq_codec, codes: torch.Tensor, norms: torch.Tensor, x_hat: torch.Tensor, stream=None) -> None:

@@ -167,6 +167,43 @@ int tq_encode(const tq_codec* c, const void* x, int x_dtype, int64_t n, int64_t 
     a.S = qjl_S;
     a.qjl = qjl_bits;
     a.gamma = qjl_gamma_f16;
+    a.pos = nullptr;
+    a.cap = 0;
+    a.seq_heads = 1;
+    return finish(tqi::launch_encode(a, x_dtype, (hipStream_t)stream));
+}
+
+int tq_append(const tq_codec* c, const void* x, int x_dtype, int batch, int n_heads, const int32_t* pos,
+              int64_t ctx_cap, uint8_t* codes, uint16_t* norms_f16, const float* qjl_S, uint8_t* qjl_bits,
+              uint16_t* qjl_gamma_f16, void* stream) {
+    if (!c) return TQ_EINVAL;
+    if (!valid_codec(c)) return TQ_EUNSUPPORTED;
+    if (x_dtype != TQ_F32 && x_dtype != TQ_F16 && x_dtype != TQ_BF16) return TQ_EINVAL;
+    if (batch <= 0 || n_heads <= 0 || ctx_cap <= 0) return TQ_EINVAL;
+    if (!x || !pos || !codes || !norms_f16 || !aligned(x, 16) || !aligned(pos, 4) || !aligned(codes, 4) ||
+        !aligned(norms_f16, 2))
+        return TQ_EINVAL;
+    const int64_t row_bytes = c->d * c->bits / 8;
+    if (row_bytes % 4 != 0) return TQ_EUNSUPPORTED;  // cache rows hold whole dwords (d >= 32)
+    if (c->qjl_m > 0) {
+        if (!qjl_S || !qjl_bits || !qjl_gamma_f16 || !aligned(qjl_bits, 4) || !aligned(qjl_gamma_f16, 2) ||
+            !aligned(qjl_S, 4))
+            return TQ_EINVAL;
+    }
+    tqi::EncodeArgs a;
+    tqi::fill_codec_args(c, &a.c);
+    a.x = x;
+    a.n = (int64_t)batch * n_heads;
+    a.x_stride = c->d;
+    a.codes = codes;
+    a.code_stride = row_bytes;
+    a.norms = norms_f16;
+    a.S = qjl_S;
+    a.qjl = qjl_bits;
+    a.gamma = qjl_gamma_f16;
+    a.pos = pos;
+    a.cap = ctx_cap;
+    a.seq_heads = n_heads;
     return finish(tqi::launch_encode(a, x_dtype, (hipStream_t)stream));
 }
 

@@ -86,6 +86,16 @@ __device__ __forceinline__ void load_rotate(const EncodeArgs& a, int64_t row, bo
     fwht<LPV>(st.v, gl);
 }
 
+// Output row of input row `row` (see EncodeArgs); keep = false when an append
+// position lies outside the cache.
+__device__ __forceinline__ int64_t out_row(const EncodeArgs& a, int64_t row, bool& keep) {
+    keep = true;
+    if (!a.pos) return row;
+    const int p = a.pos[row / a.seq_heads];
+    keep = p >= 0 && (int64_t)p < a.cap;
+    return row * a.cap + (keep ? p : 0);
+}
+
 template <int BITS>
 __device__ __forceinline__ uint32_t pack_lane(const VecState& st, const CodecArgs& c, uint32_t (&idx)[8]) {
     constexpr int HALF = (1 << BITS) / 2;
@@ -119,9 +129,11 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
         load_rotate<D, DT>(a, row, valid, gl, sbits, st);
         uint32_t idx[8];
         const uint32_t packed = pack_lane<BITS>(st, a.c, idx);
-        uint32_t* rowp = reinterpret_cast<uint32_t*>(a.codes + (valid ? row : 0) * a.code_stride);
-        store_codes<BITS>(rowp, gl, packed, valid);
-        if (valid && gl == 0) a.norms[row] = norm_to_half(st.nrm);
+        bool keep = true;
+        const int64_t orow = valid ? out_row(a, row, keep) : 0;
+        uint32_t* rowp = reinterpret_cast<uint32_t*>(a.codes + orow * a.code_stride);
+        store_codes<BITS>(rowp, gl, packed, valid && keep);
+        if (valid && keep && gl == 0) a.norms[orow] = norm_to_half(st.nrm);
     }
 }
 
@@ -157,8 +169,10 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
             load_rotate<D, DT>(a, row, valid, gl, sbits, st);
             uint32_t idx[8];
             const uint32_t packed = pack_lane<BITS>(st, a.c, idx);
-            uint32_t* rowp = reinterpret_cast<uint32_t*>(a.codes + (valid ? row : 0) * a.code_stride);
-            store_codes<BITS>(rowp, gl, packed, valid);
+            bool keep = true;
+            const int64_t orow = valid ? out_row(a, row, keep) : 0;
+            uint32_t* rowp = reinterpret_cast<uint32_t*>(a.codes + orow * a.code_stride);
+            store_codes<BITS>(rowp, gl, packed, valid && keep);
             const float inv = st.nrm > 0.0f ? 1.0f / st.nrm : 0.0f;
             float g2 = 0.0f;
 #pragma unroll
@@ -169,9 +183,9 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
                 g2 = fmaf(r, r, g2);
             }
             g2 = group_sum<LPV>(g2);
-            if (valid && gl == 0) {
-                a.norms[row] = norm_to_half(st.nrm);
-                a.gamma[row] = norm_to_half(sqrtf(g2));
+            if (valid && keep && gl == 0) {
+                a.norms[orow] = norm_to_half(st.nrm);
+                a.gamma[orow] = norm_to_half(sqrtf(g2));
             }
         }
         __syncthreads();
@@ -212,13 +226,15 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
         for (int vv = 0; vv < 4; ++vv) {
             const int vloc = tv + 8 * vv;
             const int64_t row = tile0 + vloc;
+            bool keep = true;
+            const int64_t orow = row < a.n ? out_row(a, row, keep) : 0;
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 if (jj < nj) {
                     const uint64_t mask = __ballot(acc[vv][jj] >= 0.0f);
                     const uint32_t word = (lane < 32) ? (uint32_t)mask : (uint32_t)(mask >> 32);
-                    if ((lane & 31) == 0 && row < a.n)
-                        reinterpret_cast<uint32_t*>(a.qjl + row * (m >> 3))[jj] = word;
+                    if ((lane & 31) == 0 && row < a.n && keep)
+                        reinterpret_cast<uint32_t*>(a.qjl + orow * (m >> 3))[jj] = word;
                 }
             }
         }

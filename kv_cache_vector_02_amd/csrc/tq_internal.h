@@ -27,6 +27,12 @@ struct EncodeArgs {
     const float* S;  // [m][d] or null
     uint8_t* qjl;    // [n][m/8]
     uint16_t* gamma;
+    // decode-step append: with pos set, input row r = b * seq_heads + h goes to
+    // output row r * cap + pos[b], and nothing is stored when pos[b] is outside
+    // [0, cap)
+    const int32_t* pos;
+    int64_t cap;
+    int seq_heads;
 };
 
 struct DecodeArgs {

@@ -125,6 +125,24 @@ def test_attention_window_argument_errors():
     assert call(wsb=ws - 1) == tq.TQ_EWORKSPACE
 
 
+def test_append_argument_errors():
+    c = tq.tq_codebook(3, 128, 0)
+    cq = tq.tq_codebook(3, 128, 0, 128)
+    P = FAKE
+
+    def call(codec=c, x=P, dt=1, b=2, h=4, pos=P, cap=100, codes=P, norms=P):
+        return tq.raw_call("tq_append", ctypes.byref(codec), x, dt, b, h, pos, cap, codes, norms, None, None, None,
+                           None)
+
+    assert call(b=0) == tq.TQ_EINVAL
+    assert call(h=0) == tq.TQ_EINVAL
+    assert call(cap=0) == tq.TQ_EINVAL
+    assert call(pos=None) == tq.TQ_EINVAL
+    assert call(x=ctypes.c_void_p((1 << 20) + 4)) == tq.TQ_EINVAL
+    assert call(dt=9) == tq.TQ_EINVAL
+    assert call(codec=cq) == tq.TQ_EINVAL  # QJL codec without its buffers
+
+
 def test_search_argument_errors():
     c = tq.tq_codebook(3, 256, 0, 256)
     P = FAKE
