@@ -191,8 +191,7 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
 
     def append(i):
         c = caches[i % replicas]
-        tq.tq_append(kc, k_new, pos, c["k_codes"], c["k_norms"])
-        tq.tq_append(vc, v_new, pos, c["v_codes"], c["v_norms"])
+        tq.tq_append(kc, vc, k_new, v_new, pos, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"])
 
     def append_attend(i):
         append(i)
@@ -224,7 +223,7 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
             "extra_ms_vs_packed_only": ms_rw - ms,
         },
         "append": {
-            "workload": "one new token per (sequence, kv head) appended to the K4 and V2 caches (tq_append x 2)",
+            "workload": "one new token per (sequence, kv head) appended to the K4 and V2 caches (one tq_append call)",
             "vectors": 2 * B * Hkv,
             "ms_per_append": ms_append,
             "ms_per_append_and_attend": ms_append_attend,
@@ -255,6 +254,12 @@ def encode_leg(tq, torch, synth, steps, warmup):
         tq.tq_encode(vc, pool_v[li], out_v[li], nv[li])
 
     ms = timed_loop(step, max(steps, 512), warmup, torch)
+
+    def step_kv(i):  # the same K and V through tq_encode_kv (one launch)
+        li = i % layers
+        tq.tq_encode_kv(kc, vc, pool_k[li], pool_v[li], out_k[li], nk[li], out_v[li], nv[li])
+
+    ms_kv = timed_loop(step_kv, max(steps, 512), max(warmup // 4, 1), torch)
     # single-call latency (one K+V layer), median of 20
     lat = []
     for i in range(20):
@@ -275,6 +280,12 @@ def encode_leg(tq, torch, synth, steps, warmup):
         "bytes_per_step": bytes_step,
         "latency_ms_median": lat[len(lat) // 2],
         "steps": max(steps, 512),
+        "encode_kv": {
+            "call": "tq_encode_kv (K and V in one launch), same inputs and outputs",
+            "mvectors_per_s": vecs / (ms_kv * 1e-3) / 1e6,
+            "ms_per_step": ms_kv,
+            "gbs": bytes_step / (ms_kv * 1e-3) / 1e9,
+        },
     }
 
 
@@ -296,8 +307,8 @@ def long_leg(tq, torch, synth, steps, warmup):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for h in range(Hkv):
-            tq.tq_encode(kc, k[h], c["k_codes"][0, h, sl], c["k_norms"][0, h, sl])
-            tq.tq_encode(vc, v[h], c["v_codes"][0, h, sl], c["v_norms"][0, h, sl])
+            tq.tq_encode_kv(kc, vc, k[h], v[h], c["k_codes"][0, h, sl], c["k_norms"][0, h, sl],
+                            c["v_codes"][0, h, sl], c["v_norms"][0, h, sl])
         b.record()
         torch.cuda.synchronize()
         enc_ms += a.elapsed_time(b)

@@ -123,27 +123,45 @@ int tq_encode(const tq_codec *c, const void *x, int x_dtype, int64_t n, int64_t 
               const float *qjl_S, uint8_t *qjl_bits, uint16_t *qjl_gamma_f16, void *stream);
 
 /*
- * tq_append -- the decode-step append: encode the new token of every
+ * tq_encode_kv -- tq_encode of a layer's keys and values in one call (one
+ * launch when the K codec has no QJL; the per-call cost dominates at the sizes
+ * of a prefill chunk).  Both rows sets have n rows of the same d, dtype and
+ * x_row_stride; every K argument means what it means for tq_encode with kc,
+ * every V argument what it means with vc.  vc must not use QJL (QJL is K-only,
+ * [P1] "QJL 보정 효과"): TQ_EUNSUPPORTED, as are codecs of different d.
+ */
+int tq_encode_kv(const tq_codec *kc, const tq_codec *vc, const void *k, const void *v, int x_dtype,
+                 int64_t n, int64_t x_row_stride,
+                 uint8_t *k_codes, int64_t k_code_row_stride, uint16_t *k_norms_f16,
+                 uint8_t *v_codes, int64_t v_code_row_stride, uint16_t *v_norms_f16,
+                 const float *qjl_S, uint8_t *k_qjl_bits, uint16_t *k_qjl_gamma_f16, void *stream);
+
+/*
+ * tq_append -- the decode-step append: encode the new key and value of every
  * (sequence, head) into the packed cache at that sequence's position.  [P3]
  * ("결과 — 피크 VRAM") describes each decode step adding the new K/V to the
  * cache before attention; with a residual window ([P3] "실험 설계") the token
- * leaving the window is the one appended.  Same arithmetic as tq_encode.
+ * leaving the window is the one appended.  Same arithmetic as tq_encode; one
+ * launch for K and V unless kc uses QJL.
  *
- *   x         [batch][n_heads][d] elements of x_dtype, contiguous, 16-byte aligned.
+ *   k, v      [batch][n_heads][d] elements of x_dtype, contiguous, 16-byte aligned.
  *   pos       [batch] int32 on the device: token slot written for sequence b
  *             (read by the kernel, not updated); a slot outside [0, ctx_cap)
  *             writes nothing for that sequence.
- *   codes     cache plane [batch][n_heads][ctx_cap][d*bits/8] (the layout the
- *             attention calls read), 4-byte aligned; norms_f16 [batch][n_heads][ctx_cap].
- *   qjl_S, qjl_bits [batch][n_heads][ctx_cap][m/8], qjl_gamma_f16
- *             [batch][n_heads][ctx_cap]: as in tq_encode, NULL when m = 0.
+ *   k_codes, v_codes    cache planes [batch][n_heads][ctx_cap][d*bits/8] (the
+ *             layout the attention calls read), 4-byte aligned; k_norms_f16,
+ *             v_norms_f16 [batch][n_heads][ctx_cap].
+ *   qjl_S, k_qjl_bits [batch][n_heads][ctx_cap][m/8], k_qjl_gamma_f16
+ *             [batch][n_heads][ctx_cap]: as in tq_encode for kc, NULL when kc
+ *             has no QJL.
  * Only the addressed slots are written.  Errors: TQ_EINVAL for NULL or
  * misaligned pointers, a bad x_dtype, or batch, n_heads or ctx_cap <= 0;
- * TQ_EUNSUPPORTED for an unsupported codec.
+ * TQ_EUNSUPPORTED for an unsupported codec, codecs of different d, or QJL on vc.
  */
-int tq_append(const tq_codec *c, const void *x, int x_dtype, int batch, int n_heads,
-              const int32_t *pos, int64_t ctx_cap, uint8_t *codes, uint16_t *norms_f16,
-              const float *qjl_S, uint8_t *qjl_bits, uint16_t *qjl_gamma_f16, void *stream);
+int tq_append(const tq_codec *kc, const tq_codec *vc, const void *k, const void *v, int x_dtype,
+              int batch, int n_heads, const int32_t *pos, int64_t ctx_cap,
+              uint8_t *k_codes, uint16_t *k_norms_f16, uint8_t *v_codes, uint16_t *v_norms_f16,
+              const float *qjl_S, uint8_t *k_qjl_bits, uint16_t *k_qjl_gamma_f16, void *stream);
 
 /*
  * tq_decode -- reconstruct x_hat = half_norm * D H(c[idx]) / d for n rows

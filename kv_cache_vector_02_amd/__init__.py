@@ -22,7 +22,7 @@ TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 _DTYPES = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16}
 
 EXPORTS = (
-    "tq_codebook", "tq_encode", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
+    "tq_codebook", "tq_encode", "tq_encode_kv", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
     "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror",
 )
@@ -74,7 +74,8 @@ def _load():
     sig = {
         "tq_codebook": (I, [I, I, ctypes.c_uint64, I, CP]),
         "tq_encode": (I, [CP, P, I, I64, I64, P, I64, P, P, P, P, P]),
-        "tq_append": (I, [CP, P, I, I, I, P, I64, P, P, P, P, P, P]),
+        "tq_encode_kv": (I, [CP, CP, P, P, I, I64, I64, P, I64, P, P, I64, P, P, P, P, P]),
+        "tq_append": (I, [CP, CP, P, P, I, I, I, P, I64, P, P, P, P, P, P, P, P]),
         "tq_decode": (I, [CP, P, I64, P, I64, P, P]),
         "tq_attn_decode": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
         "tq_attn_prepare": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
@@ -152,20 +153,41 @@ def tq_encode(codec: tq_codec, x: torch.Tensor, codes: torch.Tensor, norms: torc
                           _stream(stream, x)), "tq_encode")
 
 
-def tq_append(codec: tq_codec, x: torch.Tensor, pos: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor,
-              qjl_S: torch.Tensor | None = None, qjl_bits: torch.Tensor | None = None,
-              qjl_gamma: torch.Tensor | None = None, stream=None) -> None:
-    """x [B][H][d] (fp32/fp16/bf16) contiguous; pos [B] int32 (device); codes
-    [B][H][cap][d*bits/8] uint8 and norms [B][H][cap] (2-byte dtype) contiguous."""
-    for t in (x, pos, codes, norms):
+def tq_encode_kv(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, k_codes: torch.Tensor,
+                 k_norms: torch.Tensor, v_codes: torch.Tensor, v_norms: torch.Tensor,
+                 qjl_S: torch.Tensor | None = None, k_qjl_bits: torch.Tensor | None = None,
+                 k_qjl_gamma: torch.Tensor | None = None, stream=None) -> None:
+    """tq_encode of keys and values in one call: k, v [n][>=d] of one dtype and
+    row stride (last dim contiguous); codes [n][>= d*bits/8] uint8; norms [n]."""
+    for t in (k, v, k_codes, v_codes):
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("k, v and the code planes must be 2-D with contiguous rows")
+    if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("k and v must share shape, strides and dtype")
+    _check(_lib.tq_encode_kv(ctypes.byref(kc), ctypes.byref(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], k.shape[0],
+                             k.stride(0), _ptr(k_codes), k_codes.stride(0), _ptr(k_norms), _ptr(v_codes),
+                             v_codes.stride(0), _ptr(v_norms), _ptr(qjl_S), _ptr(k_qjl_bits), _ptr(k_qjl_gamma),
+                             _stream(stream, k)), "tq_encode_kv")
+
+
+def tq_append(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor,
+              k_codes: torch.Tensor, k_norms: torch.Tensor, v_codes: torch.Tensor, v_norms: torch.Tensor,
+              qjl_S: torch.Tensor | None = None, k_qjl_bits: torch.Tensor | None = None,
+              k_qjl_gamma: torch.Tensor | None = None, stream=None) -> None:
+    """k, v [B][H][d] (fp32/fp16/bf16, one dtype) contiguous; pos [B] int32
+    (device); cache planes [B][H][cap][d*bits/8] uint8 and norms [B][H][cap]
+    (2-byte dtype), contiguous."""
+    for t in (k, v, pos, k_codes, k_norms, v_codes, v_norms):
         if not t.is_contiguous():
             raise ValueError("append tensors must be contiguous")
-    if x.dim() != 3 or codes.dim() != 4 or codes.shape[:2] != x.shape[:2]:
-        raise ValueError("x [B][H][d] and codes [B][H][cap][row] must agree")
-    B, H = x.shape[0], x.shape[1]
-    _check(_lib.tq_append(ctypes.byref(codec), _ptr(x), _DTYPES[x.dtype], B, H, _ptr(pos), codes.shape[2],
-                          _ptr(codes), _ptr(norms), _ptr(qjl_S), _ptr(qjl_bits), _ptr(qjl_gamma),
-                          _stream(stream, x)), "tq_append")
+    if k.dim() != 3 or k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must be [B][H][d] of one dtype")
+    if k_codes.dim() != 4 or k_codes.shape[:2] != k.shape[:2] or v_codes.shape[:3] != k_codes.shape[:3]:
+        raise ValueError("cache planes must be [B][H][cap][row] matching k")
+    B, H = k.shape[0], k.shape[1]
+    _check(_lib.tq_append(ctypes.byref(kc), ctypes.byref(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], B, H, _ptr(pos),
+                          k_codes.shape[2], _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), _ptr(qjl_S),
+                          _ptr(k_qjl_bits), _ptr(k_qjl_gamma), _stream(stream, k)), "tq_append")
 
 
 def tq_decode(codec: tq_codec, codes: torch.Tensor, norms: torch.Tensor, x_hat: torch.Tensor, stream=None) -> None:

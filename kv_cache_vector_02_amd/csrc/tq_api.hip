@@ -138,73 +138,90 @@ const char* tq_strerror(int code) {
     }
 }
 
-int tq_encode(const tq_codec* c, const void* x, int x_dtype, int64_t n, int64_t x_row_stride, uint8_t* codes,
-              int64_t code_row_stride, uint16_t* norms_f16, const float* qjl_S, uint8_t* qjl_bits,
-              uint16_t* qjl_gamma_f16, void* stream) {
+// Validates one encode job and fills its launch arguments (nothing is launched).
+static int encode_setup(const tq_codec* c, const void* x, int x_dtype, int64_t n, int64_t x_row_stride,
+                        uint8_t* codes, int64_t code_row_stride, uint16_t* norms_f16, const float* qjl_S,
+                        uint8_t* qjl_bits, uint16_t* qjl_gamma_f16, tqi::EncodeArgs* a) {
     if (!c) return TQ_EINVAL;
     if (!valid_codec(c)) return TQ_EUNSUPPORTED;
     if (x_dtype != TQ_F32 && x_dtype != TQ_F16 && x_dtype != TQ_BF16) return TQ_EINVAL;
     if (n < 0) return TQ_EINVAL;
-    if (n == 0) return TQ_OK;
     const int esz = x_dtype == TQ_F32 ? 4 : 2;
-    if (!x || !codes || !norms_f16 || !aligned(x, 16) || !aligned(codes, 4) || !aligned(norms_f16, 2))
-        return TQ_EINVAL;
-    if (x_row_stride < c->d || (x_row_stride * esz) % 16 != 0) return TQ_EINVAL;
-    if (code_row_stride < c->d * c->bits / 8 || code_row_stride % 4 != 0) return TQ_EINVAL;
-    if (c->qjl_m > 0) {
-        if (!qjl_S || !qjl_bits || !qjl_gamma_f16 || !aligned(qjl_bits, 4) || !aligned(qjl_gamma_f16, 2) ||
-            !aligned(qjl_S, 4))
+    if (n > 0) {
+        if (!x || !codes || !norms_f16 || !aligned(x, 16) || !aligned(codes, 4) || !aligned(norms_f16, 2))
             return TQ_EINVAL;
+        if (x_row_stride < c->d || (x_row_stride * esz) % 16 != 0) return TQ_EINVAL;
+        if (code_row_stride < c->d * c->bits / 8 || code_row_stride % 4 != 0) return TQ_EINVAL;
+        if (c->qjl_m > 0) {
+            if (!qjl_S || !qjl_bits || !qjl_gamma_f16 || !aligned(qjl_bits, 4) || !aligned(qjl_gamma_f16, 2) ||
+                !aligned(qjl_S, 4))
+                return TQ_EINVAL;
+        }
     }
+    tqi::fill_codec_args(c, &a->c);
+    a->x = x;
+    a->n = n;
+    a->x_stride = x_row_stride;
+    a->codes = codes;
+    a->code_stride = code_row_stride;
+    a->norms = norms_f16;
+    a->S = qjl_S;
+    a->qjl = qjl_bits;
+    a->gamma = qjl_gamma_f16;
+    a->pos = nullptr;
+    a->cap = 0;
+    a->seq_heads = 1;
+    return TQ_OK;
+}
+
+int tq_encode(const tq_codec* c, const void* x, int x_dtype, int64_t n, int64_t x_row_stride, uint8_t* codes,
+              int64_t code_row_stride, uint16_t* norms_f16, const float* qjl_S, uint8_t* qjl_bits,
+              uint16_t* qjl_gamma_f16, void* stream) {
     tqi::EncodeArgs a;
-    tqi::fill_codec_args(c, &a.c);
-    a.x = x;
-    a.n = n;
-    a.x_stride = x_row_stride;
-    a.codes = codes;
-    a.code_stride = code_row_stride;
-    a.norms = norms_f16;
-    a.S = qjl_S;
-    a.qjl = qjl_bits;
-    a.gamma = qjl_gamma_f16;
-    a.pos = nullptr;
-    a.cap = 0;
-    a.seq_heads = 1;
+    const int rc = encode_setup(c, x, x_dtype, n, x_row_stride, codes, code_row_stride, norms_f16, qjl_S, qjl_bits,
+                                qjl_gamma_f16, &a);
+    if (rc != TQ_OK || n == 0) return rc;
     return finish(tqi::launch_encode(a, x_dtype, (hipStream_t)stream));
 }
 
-int tq_append(const tq_codec* c, const void* x, int x_dtype, int batch, int n_heads, const int32_t* pos,
-              int64_t ctx_cap, uint8_t* codes, uint16_t* norms_f16, const float* qjl_S, uint8_t* qjl_bits,
-              uint16_t* qjl_gamma_f16, void* stream) {
-    if (!c) return TQ_EINVAL;
-    if (!valid_codec(c)) return TQ_EUNSUPPORTED;
-    if (x_dtype != TQ_F32 && x_dtype != TQ_F16 && x_dtype != TQ_BF16) return TQ_EINVAL;
-    if (batch <= 0 || n_heads <= 0 || ctx_cap <= 0) return TQ_EINVAL;
-    if (!x || !pos || !codes || !norms_f16 || !aligned(x, 16) || !aligned(pos, 4) || !aligned(codes, 4) ||
-        !aligned(norms_f16, 2))
-        return TQ_EINVAL;
-    const int64_t row_bytes = c->d * c->bits / 8;
-    if (row_bytes % 4 != 0) return TQ_EUNSUPPORTED;  // cache rows hold whole dwords (d >= 32)
-    if (c->qjl_m > 0) {
-        if (!qjl_S || !qjl_bits || !qjl_gamma_f16 || !aligned(qjl_bits, 4) || !aligned(qjl_gamma_f16, 2) ||
-            !aligned(qjl_S, 4))
-            return TQ_EINVAL;
+int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k, const void* v, int x_dtype, int64_t n,
+                 int64_t x_row_stride, uint8_t* k_codes, int64_t k_code_row_stride, uint16_t* k_norms_f16,
+                 uint8_t* v_codes, int64_t v_code_row_stride, uint16_t* v_norms_f16, const float* qjl_S,
+                 uint8_t* k_qjl_bits, uint16_t* k_qjl_gamma_f16, void* stream) {
+    if (!kc || !vc) return TQ_EINVAL;
+    if (kc->d != vc->d || vc->qjl_m != 0) return TQ_EUNSUPPORTED;
+    tqi::EncodeArgs ka, va;
+    int rc = encode_setup(kc, k, x_dtype, n, x_row_stride, k_codes, k_code_row_stride, k_norms_f16, qjl_S, k_qjl_bits,
+                          k_qjl_gamma_f16, &ka);
+    if (rc == TQ_OK)
+        rc = encode_setup(vc, v, x_dtype, n, x_row_stride, v_codes, v_code_row_stride, v_norms_f16, nullptr, nullptr,
+                          nullptr, &va);
+    if (rc != TQ_OK || n == 0) return rc;
+    return finish(tqi::launch_encode_pair(ka, va, x_dtype, (hipStream_t)stream));
+}
+
+int tq_append(const tq_codec* kc, const tq_codec* vc, const void* k, const void* v, int x_dtype, int batch,
+              int n_heads, const int32_t* pos, int64_t ctx_cap, uint8_t* k_codes, uint16_t* k_norms_f16,
+              uint8_t* v_codes, uint16_t* v_norms_f16, const float* qjl_S, uint8_t* k_qjl_bits,
+              uint16_t* k_qjl_gamma_f16, void* stream) {
+    if (!kc || !vc) return TQ_EINVAL;
+    if (kc->d != vc->d || vc->qjl_m != 0) return TQ_EUNSUPPORTED;
+    if (batch <= 0 || n_heads <= 0 || ctx_cap <= 0 || !pos || !aligned(pos, 4)) return TQ_EINVAL;
+    const int64_t n = (int64_t)batch * n_heads;
+    tqi::EncodeArgs ka, va;
+    // cache rows are exactly d*bits/8 bytes (the layout the attention calls read)
+    int rc = encode_setup(kc, k, x_dtype, n, kc->d, k_codes, kc->d * kc->bits / 8, k_norms_f16, qjl_S, k_qjl_bits,
+                          k_qjl_gamma_f16, &ka);
+    if (rc == TQ_OK)
+        rc = encode_setup(vc, v, x_dtype, n, vc->d, v_codes, vc->d * vc->bits / 8, v_norms_f16, nullptr, nullptr,
+                          nullptr, &va);
+    if (rc != TQ_OK) return rc;
+    for (tqi::EncodeArgs* a : {&ka, &va}) {
+        a->pos = pos;
+        a->cap = ctx_cap;
+        a->seq_heads = n_heads;
     }
-    tqi::EncodeArgs a;
-    tqi::fill_codec_args(c, &a.c);
-    a.x = x;
-    a.n = (int64_t)batch * n_heads;
-    a.x_stride = c->d;
-    a.codes = codes;
-    a.code_stride = row_bytes;
-    a.norms = norms_f16;
-    a.S = qjl_S;
-    a.qjl = qjl_bits;
-    a.gamma = qjl_gamma_f16;
-    a.pos = pos;
-    a.cap = ctx_cap;
-    a.seq_heads = n_heads;
-    return finish(tqi::launch_encode(a, x_dtype, (hipStream_t)stream));
+    return finish(tqi::launch_encode_pair(ka, va, x_dtype, (hipStream_t)stream));
 }
 
 int tq_decode(const tq_codec* c, const uint8_t* codes, int64_t code_row_stride, const uint16_t* norms_f16,

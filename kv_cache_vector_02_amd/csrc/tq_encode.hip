@@ -114,14 +114,14 @@ __device__ __forceinline__ uint32_t pack_lane(const VecState& st, const CodecArg
 }
 
 template <int D, int BITS, int DT>
-__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+__device__ __forceinline__ void encode_rows(const EncodeArgs& a, int64_t block, int64_t nblocks) {
     constexpr int LPV = D / 8;
     constexpr int VPW = 64 / LPV;
     const int lane = threadIdx.x & 63;
     const int gl = lane & (LPV - 1);
     const uint32_t sbits = (a.c.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
-    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int64_t wave = (block * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = (nblocks * blockDim.x) >> 6;
     for (int64_t base = wave * VPW; base < a.n; base += nwaves * VPW) {
         const int64_t row = base + lane / LPV;
         const bool valid = row < a.n;
@@ -135,6 +135,30 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
         store_codes<BITS>(rowp, gl, packed, valid && keep);
         if (valid && keep && gl == 0) a.norms[orow] = norm_to_half(st.nrm);
     }
+}
+
+template <int D, int BITS, int DT>
+__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+    encode_rows<D, BITS, DT>(a, blockIdx.x, gridDim.x);
+}
+
+// Two encodes in one launch (a layer's K and V): blocks [0, kblocks) run job
+// k, the rest job v; each block switches on its codec's bit width (uniform
+// per block).  Neither job uses QJL.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void encode_pair_kernel(EncodeArgs k, EncodeArgs v, int kblocks) {
+    // each branch reads its own argument directly (selecting a reference to
+    // one of the two would copy them to scratch)
+    auto run = [](const EncodeArgs& a, int64_t block, int64_t nblocks) __attribute__((always_inline)) {
+        switch (a.c.bits) {
+            case 1: encode_rows<D, 1, DT>(a, block, nblocks); break;
+            case 2: encode_rows<D, 2, DT>(a, block, nblocks); break;
+            case 3: encode_rows<D, 3, DT>(a, block, nblocks); break;
+            default: encode_rows<D, 4, DT>(a, block, nblocks); break;
+        }
+    };
+    if ((int)blockIdx.x < kblocks) run(k, blockIdx.x, kblocks);
+    else run(v, (int64_t)blockIdx.x - kblocks, (int64_t)gridDim.x - kblocks);
 }
 
 // QJL variant: a block of 256 threads encodes a tile of 32 vectors.
@@ -327,6 +351,45 @@ hipError_t launch_decode_b(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Blocks of the plain encoder for n rows at d (4 waves of 64/(d/8) vectors per
+// iteration, at most 16384 blocks; the rows loop inside).
+static int encode_blocks(int64_t n, int d) {
+    const int64_t vpb = 4 * (64 / (d / 8));
+    const int64_t need = (n + vpb - 1) / vpb;
+    return (int)(need < 16384 ? need : 16384);
+}
+
+template <int D, int DT>
+static hipError_t launch_pair_d(const EncodeArgs& k, const EncodeArgs& v, hipStream_t s) {
+    const int kb = encode_blocks(k.n, D), vb = encode_blocks(v.n, D);
+    hipLaunchKernelGGL((encode_pair_kernel<D, DT>), dim3(kb + vb), dim3(256), 0, s, k, v, kb);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_pair_t(const EncodeArgs& k, const EncodeArgs& v, hipStream_t s) {
+    switch (k.c.d) {
+        case 32: return launch_pair_d<32, DT>(k, v, s);
+        case 64: return launch_pair_d<64, DT>(k, v, s);
+        case 128: return launch_pair_d<128, DT>(k, v, s);
+        default: return launch_pair_d<256, DT>(k, v, s);
+    }
+}
+
+hipError_t launch_encode_pair(const EncodeArgs& k, const EncodeArgs& v, int dtype, hipStream_t s) {
+    // a QJL key codec keeps its own kernel: two launches then
+    if (k.c.qjl_m > 0 || v.c.qjl_m > 0 || k.n == 0 || v.n == 0) {
+        hipError_t e = k.n > 0 ? launch_encode(k, dtype, s) : hipSuccess;
+        if (e == hipSuccess && v.n > 0) e = launch_encode(v, dtype, s);
+        return e;
+    }
+    switch (dtype) {
+        case TQ_F32: return launch_pair_t<0>(k, v, s);
+        case TQ_F16: return launch_pair_t<1>(k, v, s);
+        default: return launch_pair_t<2>(k, v, s);
+    }
+}
 
 hipError_t launch_encode(const EncodeArgs& a, int dtype, hipStream_t s) {
     switch (dtype) {

@@ -80,6 +80,8 @@ void fill_codec_args(const tq_codec* c, CodecArgs* a);
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_encode(const EncodeArgs& a, int dtype, hipStream_t s);
+// a layer's K and V encodes (same d and dtype) in one launch when neither uses QJL
+hipError_t launch_encode_pair(const EncodeArgs& k, const EncodeArgs& v, int dtype, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 enum AttnStage { ATTN_PREPARE = 1, ATTN_SCAN = 2, ATTN_COMBINE = 4, ATTN_ALL = 7, ATTN_WINDOW = 8 };
 hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s);

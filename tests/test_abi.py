@@ -128,11 +128,12 @@ def test_attention_window_argument_errors():
 def test_append_argument_errors():
     c = tq.tq_codebook(3, 128, 0)
     cq = tq.tq_codebook(3, 128, 0, 128)
+    c64 = tq.tq_codebook(3, 64, 0)
     P = FAKE
 
-    def call(codec=c, x=P, dt=1, b=2, h=4, pos=P, cap=100, codes=P, norms=P):
-        return tq.raw_call("tq_append", ctypes.byref(codec), x, dt, b, h, pos, cap, codes, norms, None, None, None,
-                           None)
+    def call(kc=c, vc=c, x=P, dt=1, b=2, h=4, pos=P, cap=100):
+        return tq.raw_call("tq_append", ctypes.byref(kc), ctypes.byref(vc), x, P, dt, b, h, pos, cap, P, P, P, P,
+                           None, None, None, None)
 
     assert call(b=0) == tq.TQ_EINVAL
     assert call(h=0) == tq.TQ_EINVAL
@@ -140,7 +141,27 @@ def test_append_argument_errors():
     assert call(pos=None) == tq.TQ_EINVAL
     assert call(x=ctypes.c_void_p((1 << 20) + 4)) == tq.TQ_EINVAL
     assert call(dt=9) == tq.TQ_EINVAL
-    assert call(codec=cq) == tq.TQ_EINVAL  # QJL codec without its buffers
+    assert call(kc=cq) == tq.TQ_EINVAL  # QJL key codec without its buffers
+    assert call(vc=cq) == tq.TQ_EUNSUPPORTED  # QJL is K-only
+    assert call(vc=c64) == tq.TQ_EUNSUPPORTED  # different d
+
+
+def test_encode_kv_argument_errors():
+    c = tq.tq_codebook(4, 128, 0)
+    cq = tq.tq_codebook(3, 128, 0, 128)
+    P = FAKE
+
+    def call(kc=c, vc=c, n=10, stride=128, kcs=64, vcs=64, x=P):
+        return tq.raw_call("tq_encode_kv", ctypes.byref(kc), ctypes.byref(vc), x, P, 1, n, stride, P, kcs, P, P, vcs,
+                           P, None, None, None, None)
+
+    assert call(n=-1) == tq.TQ_EINVAL
+    assert call(n=0) == tq.TQ_OK  # nothing to do
+    assert call(stride=100) == tq.TQ_EINVAL  # 200 B rows are not a multiple of 16 B
+    assert call(kcs=60) == tq.TQ_EINVAL
+    assert call(x=None) == tq.TQ_EINVAL
+    assert call(vc=cq) == tq.TQ_EUNSUPPORTED
+    assert call(kc=cq, kcs=48) == tq.TQ_EINVAL  # QJL key codec without its buffers
 
 
 def test_search_argument_errors():

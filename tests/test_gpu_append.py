@@ -62,32 +62,38 @@ def _check_step(g, r, enc, pos, codec_r, S):
             r[key][b, :, p] = g[key][b, :, p]
 
 
-@pytest.mark.parametrize("bits,m,dtype", [(4, 0, torch.float16), (2, 0, torch.bfloat16), (3, 128, torch.float32)])
-def test_append_steps(tq, bits, m, dtype):
+@pytest.mark.parametrize("kbits,m,dtype", [(4, 0, torch.float16), (2, 0, torch.bfloat16), (3, 128, torch.float32)])
+def test_append_steps(tq, kbits, m, dtype):
     """Five sequences at different positions (one runs past the end, one is
-    negative), four decode steps, poisoned planes: only the addressed slots change."""
-    B, H, cap, d, steps = 5, 3, 50, 128, 4
-    codec, codec_r = tq.tq_codebook(bits, d, 17, m), o.Codec(bits, d, 17, m)
+    negative), four decode steps, K and V appended together into poisoned
+    planes: only the addressed slots change."""
+    B, H, cap, d, steps, vbits = 5, 3, 50, 128, 4, 2
+    kc, kc_r = tq.tq_codebook(kbits, d, 17, m), o.Codec(kbits, d, 17, m)
+    vc, vc_r = tq.tq_codebook(vbits, d, 18), o.Codec(vbits, d, 18)
     S = synth.qjl_projection(m, d, seed=7) if m else None
     S64 = S.numpy().astype(np.float64) if m else None
-    ref = _planes(B, H, cap, codec_r)
-    dev = {k: torch.from_numpy(v.copy()).cuda() for k, v in ref.items()}
+    ref = {"k": _planes(B, H, cap, kc_r), "v": _planes(B, H, cap, vc_r)}
+    dev = {side: {k: torch.from_numpy(v.copy()).cuda() for k, v in planes.items()} for side, planes in ref.items()}
     start = np.array([0, 10, 48, 50, -3])
     for t in range(steps):
-        k, _ = synth.kv_block(B * H, 1, d, seed=100 + t, dtype=dtype)
-        x = k.view(B, H, d).contiguous()
+        kx, vx = synth.kv_block(B * H, 1, d, seed=100 + t, dtype=dtype)
+        kx, vx = kx.view(B, H, d).contiguous(), vx.view(B, H, d).contiguous()
         pos = start + t
-        tq.tq_append(codec, x.cuda(), torch.tensor(pos, dtype=torch.int32, device="cuda"), dev["codes"],
-                     dev["norms"], None if S is None else S.cuda(), dev.get("qjl"), dev.get("gamma"))
+        dk, dv = dev["k"], dev["v"]
+        tq.tq_append(kc, vc, kx.cuda(), vx.cuda(), torch.tensor(pos, dtype=torch.int32, device="cuda"),
+                     dk["codes"], dk["norms"], dv["codes"], dv["norms"], None if S is None else S.cuda(),
+                     dk.get("qjl"), dk.get("gamma"))
         torch.cuda.synchronize()
-        g = {kk: vv.cpu().numpy() for kk, vv in dev.items()}
-        before = {kk: vv.copy() for kk, vv in ref.items()}
-        enc = o.append(ref["codes"], ref["norms"], x.float().numpy().astype(np.float64), pos, codec_r, S64,
-                       ref.get("qjl"), ref.get("gamma"))
-        # compare against the oracle step applied to the previous state
-        for kk in ref:
-            ref[kk][...] = before[kk]
-        _check_step(g, ref, enc, pos, codec_r, S64)
+        for side, x, codec_r, S_side in (("k", kx, kc_r, S64), ("v", vx, vc_r, None)):
+            r = ref[side]
+            g = {kk: vv.cpu().numpy() for kk, vv in dev[side].items()}
+            before = {kk: vv.copy() for kk, vv in r.items()}
+            enc = o.append(r["codes"], r["norms"], x.float().numpy().astype(np.float64), pos, codec_r, S_side,
+                           r.get("qjl"), r.get("gamma"))
+            # compare against the oracle step applied to the previous state
+            for kk in r:
+                r[kk][...] = before[kk]
+            _check_step(g, r, enc, pos, codec_r, S_side)
 
 
 def test_decode_loop(tq):
@@ -111,8 +117,8 @@ def test_decode_loop(tq):
         kn, vn = synth.kv_block(B * Hkv, 1, d, seed=200 + step, dtype=torch.float16)
         kn, vn = kn.view(B, Hkv, d).contiguous(), vn.view(B, Hkv, d).contiguous()
         pos = torch.tensor(ctx, dtype=torch.int32, device="cuda")
-        tq.tq_append(kc, kn.cuda(), pos, dev["k_codes"], dev["k_norms"])
-        tq.tq_append(vc, vn.cuda(), pos, dev["v_codes"], dev["v_norms"])
+        tq.tq_append(kc, vc, kn.cuda(), vn.cuda(), pos, dev["k_codes"], dev["k_norms"], dev["v_codes"],
+                     dev["v_norms"])
         o.append(ref["k_codes"], ref["k_norms"], kn.float().numpy().astype(np.float64), ctx, kc_r)
         o.append(ref["v_codes"], ref["v_norms"], vn.float().numpy().astype(np.float64), ctx, vc_r)
         ctx = np.minimum(ctx + 1, cap)

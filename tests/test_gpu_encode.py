@@ -143,3 +143,45 @@ def test_decode_on_oracle_bytes(tq, d, bits):
     want = o.decode(ref["codes"], ref["norms"], ref_codec)
     tol = parity.RECON_TOL * ref["norms"].astype(np.float64)[:, None]
     assert np.all(np.abs(out.cpu().numpy() - want) <= tol)
+
+
+@pytest.mark.parametrize("kbits,vbits,m,dtype,n", [(4, 2, 0, torch.float16, 32768), (3, 3, 0, torch.bfloat16, 1000),
+                                                   (3, 2, 128, torch.float32, 777), (1, 4, 0, torch.float32, 5)])
+def test_encode_kv_matches_two_encodes_and_oracle(tq, kbits, vbits, m, dtype, n):
+    """tq_encode_kv gives the bytes of tq_encode on K and on V (one launch
+    without QJL, the QJL kernel plus the plain one with it), and both match
+    the oracle under the band rule."""
+    d = 128
+    k, v = synth.kv_block(1, n, d, seed=31, dtype=dtype)
+    k, v = k[0].contiguous(), v[0].contiguous()
+    kc, vc = tq.tq_codebook(kbits, d, 3, m), tq.tq_codebook(vbits, d, 3)
+    S = synth.qjl_projection(m, d, seed=8) if m else None
+
+    def planes(codec):
+        p = {"codes": torch.full((n, codec.d * codec.bits // 8), 0xA5, dtype=torch.uint8, device="cuda"),
+             "norms": torch.empty(n, dtype=torch.float16, device="cuda")}
+        if codec.qjl_m:
+            p["qjl"] = torch.empty(n, codec.qjl_m // 8, dtype=torch.uint8, device="cuda")
+            p["gamma"] = torch.empty(n, dtype=torch.float16, device="cuda")
+        return p
+
+    fk, fv, sk, sv = planes(kc), planes(vc), planes(kc), planes(vc)
+    kd, vd, Sd = k.cuda(), v.cuda(), (S.cuda() if m else None)
+    tq.tq_encode_kv(kc, vc, kd, vd, fk["codes"], fk["norms"], fv["codes"], fv["norms"], Sd, fk.get("qjl"),
+                    fk.get("gamma"))
+    tq.tq_encode(kc, kd, sk["codes"], sk["norms"], Sd, sk.get("qjl"), sk.get("gamma"))
+    tq.tq_encode(vc, vd, sv["codes"], sv["norms"])
+    torch.cuda.synchronize()
+    for a, b in ((fk, sk), (fv, sv)):
+        for key in a:
+            assert torch.equal(a[key].view(torch.uint8), b[key].view(torch.uint8)), key
+    for x, codec, pl, S_side in ((k, kc, fk, S), (v, vc, fv, None)):
+        ref_codec = o.Codec(codec.bits, d, 3, codec.qjl_m)
+        ref = o.encode(x.float().numpy().astype(np.float64), ref_codec,
+                       None if S_side is None else S_side.numpy().astype(np.float64))
+        _, bad_rows = parity.compare_codes(pl["codes"].cpu().numpy(), ref, ref_codec)
+        parity.compare_halves(pl["norms"].cpu().numpy().view(np.uint16), ref["norm"], ref["norms"])
+        if codec.qjl_m:
+            parity.compare_halves(pl["gamma"].cpu().numpy().view(np.uint16), ref["gamma64"], ref["gamma"],
+                                  skip=bad_rows)
+            parity.compare_qjl(pl["qjl"].cpu().numpy(), ref, S_side.numpy(), ref_codec, bad_rows)
