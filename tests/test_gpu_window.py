@@ -29,7 +29,7 @@ def tq():
 
 
 def run_window_case(tq, B, Hkv, g, cap, ctx_len, win_cap, win_len, kbits=4, vbits=2, d=128,
-                    qdtype=torch.float16, wdtype=torch.float16, seed=0):
+                    qdtype=torch.float16, wdtype=torch.float16, seed=0, m=0):
     Hq = Hkv * g
     kk = torch.stack([synth.kv_block(Hkv, cap, d, seed + b, dtype=torch.float32)[0] for b in range(B)])
     vv = torch.stack([synth.kv_block(Hkv, cap, d, seed + b, dtype=torch.float32)[1] for b in range(B)])
@@ -37,9 +37,11 @@ def run_window_case(tq, B, Hkv, g, cap, ctx_len, win_cap, win_len, kbits=4, vbit
     vw = torch.stack([synth.kv_block(Hkv, max(win_cap, 1), d, seed + 50 + b, dtype=wdtype)[1] for b in range(B)])
     kw, vw = kw[:, :, :win_cap].contiguous(), vw[:, :, :win_cap].contiguous()
     q = synth.normal((B, Hq, d), seed=seed + 99, dtype=qdtype)
-    kc_r, vc_r = o.Codec(kbits, d, seed + 1), o.Codec(vbits, d, seed + 1)
-    kc, vc = tq.tq_codebook(kbits, d, seed + 1), tq.tq_codebook(vbits, d, seed + 1)
-    cache = oracle_cache(kk.numpy().astype(np.float64), vv.numpy().astype(np.float64), kc_r, vc_r)
+    kc_r, vc_r = o.Codec(kbits, d, seed + 1, m), o.Codec(vbits, d, seed + 1)
+    kc, vc = tq.tq_codebook(kbits, d, seed + 1, m), tq.tq_codebook(vbits, d, seed + 1)
+    S = synth.qjl_projection(m, d, seed=seed + 7) if m else None
+    S64 = S.numpy().astype(np.float64) if m else None
+    cache = oracle_cache(kk.numpy().astype(np.float64), vv.numpy().astype(np.float64), kc_r, vc_r, S64)
     dev = to_dev(cache)
     scale = 1.0 / math.sqrt(d)
     ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, B, Hq, Hkv, cap))
@@ -47,12 +49,14 @@ def run_window_case(tq, B, Hkv, g, cap, ctx_len, win_cap, win_len, kbits=4, vbit
     out = torch.full((B, Hq, d), float("nan"), device="cuda")
     tq.tq_attn_decode_rw(kc, vc, q.cuda(), torch.tensor(ctx_len, dtype=torch.int32, device="cuda"),
                          dev["k_codes"], dev["k_norms"], dev["v_codes"], dev["v_norms"], kw.cuda(), vw.cuda(),
-                         torch.tensor(win_len, dtype=torch.int32, device="cuda"), scale, out, ws)
+                         torch.tensor(win_len, dtype=torch.int32, device="cuda"), scale, out, ws,
+                         dev.get("k_qjl"), dev.get("k_gamma"), None if S is None else S.cuda())
     torch.cuda.synchronize()
     got = out.cpu().numpy().reshape(-1, d)
     wl = [min(max(w, 0), win_cap) for w in win_len]
     ref = o.gqa_attention(q.float().numpy().astype(np.float64), ctx_len, cache["k_codes"], cache["k_norms"],
-                          cache["v_codes"], cache["v_norms"], kc_r, vc_r, scale,
+                          cache["v_codes"], cache["v_norms"], kc_r, vc_r, scale, cache.get("k_qjl"),
+                          cache.get("k_gamma"), S64,
                           k_win=kw.float().numpy().astype(np.float64), v_win=vw.float().numpy().astype(np.float64),
                           win_len=wl)
     assert np.all(np.isfinite(got))
@@ -80,6 +84,13 @@ def test_window_edges(tq):
 def test_window_dtypes_d256(tq, wdtype):
     run_window_case(tq, B=2, Hkv=2, g=4, cap=900, ctx_len=[900, 450], win_cap=96, win_len=[96, 33], d=256,
                     qdtype=torch.bfloat16, wdtype=wdtype, kbits=3, vbits=3, seed=5)
+
+
+@pytest.mark.parametrize("d,m", [(128, 128), (256, 256)])
+def test_window_with_qjl_keys(tq, d, m):
+    """QJL keys (the prepare launch, the scan's sign term) with a residual window."""
+    run_window_case(tq, B=2, Hkv=1, g=4, cap=700, ctx_len=[700, 333], win_cap=64, win_len=[64, 9], kbits=3,
+                    vbits=2, d=d, m=m, qdtype=torch.float32, seed=3)
 
 
 def test_window_large_and_dominant(tq):
