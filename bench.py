@@ -15,7 +15,8 @@ tq_encode throughput (4 kv heads x 8192
 tokens, fp16, K 4-bit + V 2-bit per step, over a 1 GiB rotating input pool),
 long-context decode (8 kv heads x 2^20 tokens, K3/V3, 64 bf16 query heads) and
 inner-product search (2^20 x 256 database, 3-bit + QJL m=256, 1024 queries,
-top-10).  `roofline` is the scan kernel's algorithmic bytes per launch over its
+top-10; useful estimator TFLOP/s, and the matrix-core work issued against the
+dense fp16 peak).  `roofline` is the scan kernel's algorithmic bytes per launch over its
 mean launch time, measured with HIP events on the launch stream around
 back-to-back scan launches; `traffic` is the HBM bytes per scan launch from the
 committed FETCH_SIZE / WRITE_SIZE summary under profiles/ (null once the scan
@@ -45,7 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_scan_traffic_b16_h28x4_ctx32
 # sources of the scan kernel: a stored traffic measurement is used only while these are unchanged
 SCAN_SOURCES = ("kv_cache_vector_02_amd/csrc/tq_attn_kernels.h", "kv_cache_vector_02_amd/csrc/tq_attn.hip",
                 "kv_cache_vector_02_amd/csrc/tq_device.h", "kv_cache_vector_02_amd/csrc/tq_internal.h")
-FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (counts packed FMA)
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores, published
 
 METRIC = "packed-KV decode attn GB/s & % HBM peak (1 GPU); tq_encode Mvectors/s"
 
@@ -368,13 +369,17 @@ def search_leg(tq, torch, synth, steps, warmup):
     st = max(2, min(steps, 5))
     ms = timed_loop(step, st, min(warmup, 2), torch)
     flops = 2.0 * n_q * n_db * (d + m)
+    # matrix-core work actually issued: per 16 rows x 8 queries, d/16 + m/32
+    # v_mfma_f32_16x16x32_f16 (2*16*16*32 flops each; the hi/lo operand fold)
+    mfma_flops = n_q * n_db / 128.0 * (d // 16 + m // 32) * 2 * 16 * 16 * 32
     db_bytes = n_db * (codec.code_bytes + 2 + m // 8 + 2)
     return {
         "workload": "2^20 x 256 unit vectors, 3-bit + QJL m=256, 1024 unit queries, exact top-10",
         "ms_per_call": ms,
         "queries_per_s": n_q / (ms * 1e-3),
         "tflops": flops / (ms * 1e-3) / 1e12,
-        "pct_fp32_valu_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+        "mfma_tflops": mfma_flops / (ms * 1e-3) / 1e12,
+        "pct_fp16_mfma_peak": 100.0 * mfma_flops / (ms * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
         "db_bytes": db_bytes,
         "db_encode_ms": enc_ms,
         "db_encode_mvectors_per_s": n_db / (enc_ms * 1e-3) / 1e6,

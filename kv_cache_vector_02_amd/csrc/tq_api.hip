@@ -370,7 +370,7 @@ static int search_check(const tq_codec* c, int n_q, int64_t n_db, int k) {
     if (!valid_codec(c)) return TQ_EUNSUPPORTED;
     if (c->d != 128 && c->d != 256) return TQ_EUNSUPPORTED;
     if (k < 1 || k > 32) return TQ_EUNSUPPORTED;
-    if (n_q <= 0 || n_db < 0 || n_q > 65535 * 64) return TQ_EINVAL;
+    if (n_q <= 0 || n_db < 0 || n_q > 65535 * 32) return TQ_EINVAL;  // 32 queries per block row of the grid
     if (n_db > ((int64_t)1 << 31) - 1) return TQ_EUNSUPPORTED;
     return TQ_OK;
 }

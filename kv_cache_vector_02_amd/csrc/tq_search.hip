@@ -8,10 +8,10 @@
 // unbiasedness pays off (the TurboQuant PyTorch write-up on idea.jsleekr.com,
 // "핵심 발견 1 — QJL 레이어를 제거하라": no softmax in vector search).
 //
-// Launches: qprep (A, stored k-major [d+m][n_q]), scan (grid = DB chunks x 64-query tiles; 64x64
-// tiles of est through LDS, 4x4 register tiles per thread, exact per-block
-// top-k lists in LDS), merge (per query, exact top-k over the block lists,
-// ordered by estimate descending then id ascending).
+// Launches: qprep (A, stored k-major [d+m][n_q]), scan (grid = DB chunks x
+// 32-query tiles; the estimates on the matrix cores, see below, and exact
+// per-block top-k lists in LDS), merge (per query, exact top-k over the block
+// lists, ordered by estimate descending then id ascending).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -23,9 +23,6 @@ namespace {
 
 using namespace tqd;
 
-constexpr int BQ = 64;     // queries per block
-constexpr int BT = 64;     // database rows per tile
-constexpr int KC = 32;     // K chunk
 constexpr int KMAX = 32;   // largest k
 
 template <int D>
@@ -67,137 +64,248 @@ __global__ __launch_bounds__(64) void search_qprep_kernel(SearchArgs a) {
     }
 }
 
-template <int D, int BITS>
-__global__ __launch_bounds__(256) void search_scan_kernel(SearchArgs a) {
-    constexpr int RB = D * BITS / 8;  // code bytes per row
-    const int m = a.c.qjl_m;
-    const int KD = D + m;
-    const int k = a.k;
-    __shared__ __attribute__((aligned(16))) float As[KC][BQ];
-    __shared__ __attribute__((aligned(16))) float Bs[KC][BT];
-    __shared__ float Es[BQ][BT + 1];
-    __shared__ float lst_s[BQ][KMAX];
-    __shared__ int32_t lst_i[BQ][KMAX];
-    __shared__ __attribute__((aligned(16))) uint32_t rcode[BT * RB / 4];
-    __shared__ __attribute__((aligned(16))) uint32_t rbits[BT * 8];  // m <= 256 -> 8 dwords per row
-    __shared__ float rn[BT], rg[BT];
-    __shared__ float cent[16];
+// --------------------------------------------------------- matrix cores ----
+// The same estimator as one matrix-core contraction per (16 rows, 8 queries):
+// v_mfma_f32_16x16x32_f16, lane l holding A[l%16][8(l/16) + e], B[8(l/16) + e][l%16]
+// and receiving D[4(l/16) + i][l%16].  Rows of A are database rows, columns of
+// B are queries.  Float32-exact products come from splitting both operands into
+// half hi + lo parts folded into the two MFMA dimensions with room (the decode
+// scan's scheme): the eight k slots of a lane hold (c_hi, c_hi, c_lo, c_lo) of
+// two dims twice, columns 0..7 hold q_hi and 8..15 q_lo of the wave's 8 queries
+// (zero on the c_lo slots), so D[row][n] + D[row][n + 8] is the product
+// sum over (c_hi + c_lo)(q_hi + q_lo) without the c_lo q_lo term (below 2^-22).
+// Lane group g = l/16 covers dims g*d/4 + [0, d/4): k step ks takes dims
+// g*d/4 + 4ks + [0, 4).  The QJL part takes A = 16 gamma (+-1), exact in half,
+// with projections j = g*m/4 + 8js + [0, 8) per k step.  Centroids are scaled by
+// 16 and each wave's queries by one power of two into [2^14, 2^15) so every lo
+// part is a normal half; the scale comes off the float32 result.
+//
+// A block of 4 waves takes 32 queries (8 per wave, their operands kept in
+// registers) and a range of database rows in tiles of 64 staged through LDS;
+// each wave scores all 64 rows of a tile for its queries and inserts them into
+// its queries' exact top-k lists, so after staging the waves run independently.
+typedef _Float16 sh8_t __attribute__((ext_vector_type(8)));
+typedef float sf4_t __attribute__((ext_vector_type(4)));
 
-    const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;
-    const int q0 = blockIdx.y * BQ;
+constexpr int MQ = 32;  // queries per block
+constexpr int MT = 64;  // database rows per tile
+
+__device__ __forceinline__ sh8_t as_sh8(uint4 u) { return __builtin_bit_cast(sh8_t, u); }
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    const _Float16 x = (_Float16)a, y = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// bits [bit0, bit0 + NB) of a little-endian dword array (bit0 compile-time after unrolling)
+template <int NB>
+__device__ __forceinline__ uint32_t bits_at(const uint32_t* w, int bit0) {
+    const int wi = bit0 >> 5, sh = bit0 & 31;
+    if (sh + NB <= 32) return (w[wi] >> sh) & ((1u << NB) - 1u);
+    return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & ((1u << NB) - 1u);
+}
+
+__device__ __forceinline__ float wmax64(float v) {
+    v = fmaxf(v, xor_lane<1>(v));
+    v = fmaxf(v, xor_lane<2>(v));
+    v = fmaxf(v, xor_lane<4>(v));
+    v = fmaxf(v, xor_lane<8>(v));
+    v = fmaxf(v, xor_lane<16>(v));
+    return fmaxf(v, xor_lane<32>(v));
+}
+
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void search_mfma_kernel(SearchArgs a) {
+    constexpr int RB = D * BITS / 8;   // code bytes per row
+    constexpr int RW = RB / 4;         // ... dwords
+    constexpr int DG = D / 4;          // dims per lane group
+    constexpr int KS = DG / 4;         // centroid k steps
+    constexpr int GW = DG * BITS / 32; // code dwords per lane group and row
+    constexpr int TE = 1 << (2 * BITS);
+    // bank-sliced tables: entry e occupies a row of TS copies, lane l reads copy
+    // l % TS, so the 32 lanes of a pass hit distinct banks whatever their
+    // entries (at 4 bits 8 copies keep the table at 16 KB)
+    constexpr int TS = BITS <= 3 ? 32 : 8;
+    const int m = a.c.qjl_m;
+    const int JS = m >> 5;             // QJL k steps (<= 8)
+    const int MW = m >> 5;             // sign dwords per row
+    const int k = a.k;
+    __shared__ __attribute__((aligned(16))) uint2 tab[TE * TS];  // two codes: hi a, hi b | lo a, lo b (of 16 c)
+    __shared__ __attribute__((aligned(16))) uint2 sgn[16 * 32];  // nibble -> 4 halves of +-1, 32 copies
+    __shared__ __attribute__((aligned(16))) uint32_t rcode[MT * RW];
+    __shared__ __attribute__((aligned(16))) uint32_t rbits[MT * 8];
+    __shared__ float rn[MT], rg[MT];
+    __shared__ float es[MQ][MT + 1];
+    __shared__ float lst_s[MQ][KMAX];
+    __shared__ int32_t lst_i[MQ][KMAX];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, grp = lane >> 4;
+    const int q0 = blockIdx.y * MQ;
     const int64_t r_beg = (int64_t)blockIdx.x * a.block_rows;
     const int64_t r_end = (r_beg + a.block_rows < a.n_db) ? r_beg + a.block_rows : a.n_db;
 
-    if (tid < 16) cent[tid] = a.c.centroid[tid];
-    for (int e = tid; e < BQ * KMAX; e += 256) {
+    for (int i = tid; i < TE * TS; i += 256) {
+        const int e = i / TS;
+        const float fa = 16.0f * a.c.centroid[e & ((1 << BITS) - 1)];
+        const float fb = 16.0f * a.c.centroid[e >> BITS];
+        const float ha = (float)(_Float16)fa, hb = (float)(_Float16)fb;
+        tab[i] = make_uint2(pack_h2(ha, hb), pack_h2(fa - ha, fb - hb));
+    }
+    for (int i = tid; i < 16 * 32; i += 256) {
+        const int x = i >> 5;
+        auto sg = [&](int b) { return ((x >> b) & 1) ? 1.0f : -1.0f; };
+        sgn[i] = make_uint2(pack_h2(sg(0), sg(1)), pack_h2(sg(2), sg(3)));
+    }
+    const int tsl = lane % TS, ssl = lane & 31;  // this lane's table copies
+    for (int e = tid; e < MQ * KMAX; e += 256) {
         lst_s[e / KMAX][e % KMAX] = -INFINITY;
         lst_i[e / KMAX][e % KMAX] = -1;
     }
-    __syncthreads();
 
-    for (int64_t t0 = r_beg; t0 < r_end; t0 += BT) {
-        const int nt = (int)((r_end - t0) < BT ? (r_end - t0) : BT);
-        // stage the row tile: codes, sign bits, norm, gamma
-        for (int e = tid; e < BT * RB / 4; e += 256) {
-            const int r = e / (RB / 4);
-            rcode[e] = r < nt ? reinterpret_cast<const uint32_t*>(a.codes + (t0 + r) * RB)[e % (RB / 4)] : 0u;
+    // this wave's query operands: column n <-> query q0 + 8 wave + (n & 7), hi (n < 8) or lo
+    const int qi = q0 + 8 * wave + (n & 7);
+    const bool qok = qi < a.n_q;
+    const bool lo_col = n >= 8;
+    sh8_t bq[KS], bj[8];
+    float qinv;
+    {
+        float amax = 0.0f;
+        for (int t = 0; t < DG; ++t) amax = fmaxf(amax, qok ? fabsf(a.qrot[(int64_t)(grp * DG + t) * a.n_q + qi]) : 0.0f);
+        for (int t = 0; t < (m >> 2); ++t)
+            amax = fmaxf(amax, qok ? fabsf(a.qrot[(int64_t)(D + grp * (m >> 2) + t) * a.n_q + qi]) : 0.0f);
+        amax = wmax64(amax);
+        float sc = 1.0f;
+        if (amax > 0.0f && isfinite(amax)) {
+            int ex;
+            frexpf(amax, &ex);
+            sc = ldexpf(1.0f, 15 - ex);
         }
-        if (m > 0) {
-            const int mw = m >> 5;
-            for (int e = tid; e < BT * mw; e += 256) {
-                const int r = e / mw;
-                rbits[r * 8 + e % mw] = r < nt ? reinterpret_cast<const uint32_t*>(a.qjl + (t0 + r) * (m >> 3))[e % mw] : 0u;
+        qinv = 1.0f / (16.0f * sc);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = qok ? a.qrot[(int64_t)(grp * DG + 4 * ks + i) * a.n_q + qi] * sc : 0.0f;
+                const float h = (float)(_Float16)v;
+                x[i] = lo_col ? v - h : h;
+            }
+            // slots (hi d0, hi d1, lo d0, lo d1, hi d2, hi d3, lo d2, lo d3) of the A side
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bool lo_slot = (e & 2) != 0;
+                bq[ks][e] = (lo_col && lo_slot) ? (_Float16)0.0f : (_Float16)x[(e >> 2) * 2 + (e & 1)];
             }
         }
-        if (tid < BT) {
+#pragma unroll
+        for (int js = 0; js < 8; ++js) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = 0.0f;
+                if (js < JS && qok) v = a.qrot[(int64_t)(D + grp * (m >> 2) + 8 * js + e) * a.n_q + qi] * sc;
+                const float h = (float)(_Float16)v;
+                bj[js][e] = (_Float16)(lo_col ? v - h : h);
+            }
+        }
+    }
+
+    for (int64_t t0 = r_beg; t0 < r_end; t0 += MT) {
+        const int nt = (int)((r_end - t0) < MT ? (r_end - t0) : MT);
+        __syncthreads();  // the previous tile's rows are no longer read
+        for (int e = tid; e < MT * RW; e += 256) {
+            const int r = e / RW;
+            rcode[e] = r < nt ? reinterpret_cast<const uint32_t*>(a.codes + (t0 + r) * RB)[e % RW] : 0u;
+        }
+        for (int e = tid; e < MT * MW; e += 256) {
+            const int r = e / MW;
+            rbits[r * 8 + e % MW] = r < nt ? reinterpret_cast<const uint32_t*>(a.qjl + (t0 + r) * (m >> 3))[e % MW] : 0u;
+        }
+        if (tid < MT) {
             rn[tid] = tid < nt ? half_bits_to_float(a.norms[t0 + tid]) : 0.0f;
             rg[tid] = (tid < nt && m > 0) ? half_bits_to_float(a.gamma[t0 + tid]) : 0.0f;
         }
-        float acc[4][4];
+        __syncthreads();
+#pragma unroll 1
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * j + n;  // this lane's row of the A side
+            uint32_t cw[GW];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int w = 0; w < GW; ++w) cw[w] = rcode[r * RW + grp * GW + w];
+            sf4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-
-        for (int k0 = 0; k0 < KD; k0 += KC) {
-            __syncthreads();
-            // A chunk: As[kk][q] = A[q0+q][k0+kk] (A is stored k-major: [d+m][n_q])
-            for (int e = tid; e < KC * BQ; e += 256) {
-                const int kk = e / BQ, q = e % BQ;
-                As[kk][q] = (q0 + q < a.n_q) ? a.qrot[(int64_t)(k0 + kk) * a.n_q + q0 + q] : 0.0f;
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint2 e0 = tab[bits_at<2 * BITS>(cw, 4 * ks * BITS) * TS + tsl];
+                const uint2 e1 = tab[bits_at<2 * BITS>(cw, (4 * ks + 2) * BITS) * TS + tsl];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_sh8(make_uint4(e0.x, e0.y, e1.x, e1.y)), bq[ks], acc, 0, 0, 0);
             }
-            // B chunk: 8 consecutive k of one row per thread
-            {
-                const int r = tid >> 2, kb = (tid & 3) * 8;
-                float vals[8];
-                if (k0 < D) {
-                    const int bit0 = (k0 + kb) * BITS;  // 8 codes = BITS bytes
-                    const uint8_t* rp = reinterpret_cast<const uint8_t*>(rcode) + r * RB + bit0 / 8;
-                    uint32_t packed = 0;
+            if (JS > 0) {
+                const _Float16 g16 = (_Float16)(16.0f * rg[r]);
 #pragma unroll
-                    for (int x = 0; x < BITS; ++x) packed |= (uint32_t)rp[x] << (8 * x);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) vals[e] = cent[(packed >> (BITS * e)) & ((1u << BITS) - 1u)];
-                } else {
-                    const int j0 = k0 - D + kb;
-                    const uint32_t w = rbits[r * 8 + (j0 >> 5)] >> (j0 & 31);
-                    const float gm = rg[r];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) vals[e] = ((w >> e) & 1u) ? gm : -gm;
+                for (int js = 0; js < 8; ++js) {
+                    if (js < JS) {
+                        const int j0 = grp * (m >> 2) + 8 * js;
+                        const uint32_t byte = (rbits[r * 8 + (j0 >> 5)] >> (j0 & 31)) & 0xFFu;
+                        const uint2 lo = sgn[(byte & 15u) * 32 + ssl], hi = sgn[(byte >> 4) * 32 + ssl];
+                        const sh8_t av = as_sh8(make_uint4(lo.x, lo.y, hi.x, hi.y)) * g16;
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bj[js], acc, 0, 0, 0);
+                    }
                 }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) Bs[kb + e][r] = vals[e];
             }
-            __syncthreads();
-#pragma unroll 8
-            for (int kk = 0; kk < KC; ++kk) {
-                const float4 av = *reinterpret_cast<const float4*>(&As[kk][ty * 4]);
-                const float4 bv = *reinterpret_cast<const float4*>(&Bs[kk][tx * 4]);
-                const float ar[4] = {av.x, av.y, av.z, av.w};
-                const float br[4] = {bv.x, bv.y, bv.z, bv.w};
+            // column n + 8 holds the q_lo part of query n: add the two halves
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int v = 0; v < 4; ++v) acc[v] += xor_lane<8>(acc[v]);
+            if (n < 8) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ar[i], br[j], acc[i][j]);
+                for (int v = 0; v < 4; ++v) {
+                    const int row = 16 * j + 4 * grp + v;
+                    es[8 * wave + n][row] = row < nt ? rn[row] * (acc[v] * qinv) : -INFINITY;
+                }
             }
         }
+        // this wave's queries: exact top-k insertion (score desc, id asc; ids
+        // grow along the scan, so an equal score never displaces an entry)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < 8) {
+            const int ql = 8 * wave + lane;
+            float* ls = lst_s[ql];
+            int32_t* li = lst_i[ql];
+            float thr = ls[k - 1];  // the list's k-th score: only larger scores enter
+            for (int tb = 0; tb < nt; tb += 8) {
+                float sv[8], mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = tx * 4 + j;
-                Es[ty * 4 + i][t] = t < nt ? rn[t] * acc[i][j] : -INFINITY;
-            }
-        __syncthreads();
-        // per-query insertion into the exact top-k list (score desc, id asc;
-        // ids grow along the scan, so an equal score never displaces an entry)
-        if (tid < BQ) {
-            float* ls = lst_s[tid];
-            int32_t* li = lst_i[tid];
-            for (int t = 0; t < nt; ++t) {
-                const float sc = Es[tid][t];
-                if (sc > ls[k - 1]) {
-                    int pos = k - 1;
-                    while (pos > 0 && ls[pos - 1] < sc) {
-                        ls[pos] = ls[pos - 1];
-                        li[pos] = li[pos - 1];
-                        --pos;
+                for (int u = 0; u < 8; ++u) {  // 8 independent loads, then one compare in the common case
+                    sv[u] = tb + u < nt ? es[ql][tb + u] : -INFINITY;
+                    mx = fmaxf(mx, sv[u]);
+                }
+                if (mx > thr) {
+                    for (int u = 0; u < 8; ++u) {
+                        const float sc = sv[u];
+                        if (sc > ls[k - 1]) {
+                            int pos = k - 1;
+                            while (pos > 0 && ls[pos - 1] < sc) {
+                                ls[pos] = ls[pos - 1];
+                                li[pos] = li[pos - 1];
+                                --pos;
+                            }
+                            ls[pos] = sc;
+                            li[pos] = (int32_t)(t0 + tb + u);
+                        }
                     }
-                    ls[pos] = sc;
-                    li[pos] = (int32_t)(t0 + t);
+                    thr = ls[k - 1];
                 }
             }
         }
     }
     __syncthreads();
-    // block candidates -> workspace [n_q][n_blocks][k]
-    for (int e = tid; e < BQ * k; e += 256) {
-        const int q = e / k, j = e % k;
+    for (int e = tid; e < MQ * k; e += 256) {
+        const int q = e / k, jj = e % k;
         if (q0 + q < a.n_q) {
-            const int64_t o = ((int64_t)(q0 + q) * a.n_blocks + blockIdx.x) * k + j;
-            a.cand_s[o] = lst_s[q][j];
-            a.cand_i[o] = lst_i[q][j];
+            const int64_t o = ((int64_t)(q0 + q) * a.n_blocks + blockIdx.x) * k + jj;
+            a.cand_s[o] = lst_s[q][jj];
+            a.cand_i[o] = lst_i[q][jj];
         }
     }
 }
@@ -257,12 +365,12 @@ __global__ __launch_bounds__(256) void search_merge_kernel(SearchArgs a) {
 
 template <int D>
 hipError_t launch_scan_b(const SearchArgs& a, hipStream_t s) {
-    const dim3 grid(a.n_blocks, (a.n_q + BQ - 1) / BQ);
+    const dim3 grid(a.n_blocks, (a.n_q + MQ - 1) / MQ);
     switch (a.c.bits) {
-        case 1: hipLaunchKernelGGL((search_scan_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((search_scan_kernel<D, 2>), grid, dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((search_scan_kernel<D, 3>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((search_scan_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((search_mfma_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((search_mfma_kernel<D, 2>), grid, dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((search_mfma_kernel<D, 3>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((search_mfma_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
     }
     return hipGetLastError();
 }
