@@ -75,8 +75,9 @@ __global__ __launch_bounds__(64) void search_qprep_kernel(SearchArgs a) {
 // (zero on the c_lo slots), so D[row][n] + D[row][n + 8] is the product
 // sum over (c_hi + c_lo)(q_hi + q_lo) without the c_lo q_lo term (below 2^-22).
 // Lane group g = l/16 covers dims g*d/4 + [0, d/4): k step ks takes dims
-// g*d/4 + 4ks + [0, 4).  The QJL part takes A = 16 gamma (+-1), exact in half,
-// with projections j = g*m/4 + 8js + [0, 8) per k step.  Centroids are scaled by
+// g*d/4 + 4ks + [0, 4).  The QJL part takes A = 16 (+-1), exact in half,
+// with projections j = g*m/4 + 8js + [0, 8) per k step, accumulated apart
+// from the centroid part; the row's gamma multiplies that float32 sum.  Centroids are scaled by
 // 16 and each wave's queries by one power of two into [2^14, 2^15) so every lo
 // part is a normal half; the scale comes off the float32 result.
 //
@@ -115,7 +116,7 @@ __device__ __forceinline__ float wmax64(float v) {
 }
 
 template <int D, int BITS>
-__global__ __launch_bounds__(256) void search_mfma_kernel(SearchArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void search_mfma_kernel(SearchArgs a) {
     constexpr int RB = D * BITS / 8;   // code bytes per row
     constexpr int RW = RB / 4;         // ... dwords
     constexpr int DG = D / 4;          // dims per lane group
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(256) void search_mfma_kernel(SearchArgs a) {
     const int MW = m >> 5;             // sign dwords per row
     const int k = a.k;
     __shared__ __attribute__((aligned(16))) uint2 tab[TE * TS];  // two codes: hi a, hi b | lo a, lo b (of 16 c)
-    __shared__ __attribute__((aligned(16))) uint2 sgn[16 * 32];  // nibble -> 4 halves of +-1, 32 copies
+    __shared__ __attribute__((aligned(16))) uint2 sgn[16 * 32];  // nibble -> 4 halves of +-16, 32 copies
     __shared__ __attribute__((aligned(16))) uint32_t rcode[MT * RW];
     __shared__ __attribute__((aligned(16))) uint32_t rbits[MT * 8];
     __shared__ float rn[MT], rg[MT];
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(256) void search_mfma_kernel(SearchArgs a) {
     }
     for (int i = tid; i < 16 * 32; i += 256) {
         const int x = i >> 5;
-        auto sg = [&](int b) { return ((x >> b) & 1) ? 1.0f : -1.0f; };
+        auto sg = [&](int b) { return ((x >> b) & 1) ? 16.0f : -16.0f; };
         sgn[i] = make_uint2(pack_h2(sg(0), sg(1)), pack_h2(sg(2), sg(3)));
     }
     const int tsl = lane % TS, ssl = lane & 31;  // this lane's table copies
@@ -239,27 +240,30 @@ __global__ __launch_bounds__(256) void search_mfma_kernel(SearchArgs a) {
                 const uint2 e1 = tab[bits_at<2 * BITS>(cw, (4 * ks + 2) * BITS) * TS + tsl];
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_sh8(make_uint4(e0.x, e0.y, e1.x, e1.y)), bq[ks], acc, 0, 0, 0);
             }
-            if (JS > 0) {
-                const _Float16 g16 = (_Float16)(16.0f * rg[r]);
+            // the QJL part in its own accumulator with A = 16 (+-1): the row's
+            // gamma multiplies the float32 result instead of the operands
+            sf4_t accq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int js = 0; js < 8; ++js) {
-                    if (js < JS) {
-                        const int j0 = grp * (m >> 2) + 8 * js;
-                        const uint32_t byte = (rbits[r * 8 + (j0 >> 5)] >> (j0 & 31)) & 0xFFu;
-                        const uint2 lo = sgn[(byte & 15u) * 32 + ssl], hi = sgn[(byte >> 4) * 32 + ssl];
-                        const sh8_t av = as_sh8(make_uint4(lo.x, lo.y, hi.x, hi.y)) * g16;
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bj[js], acc, 0, 0, 0);
-                    }
+            for (int js = 0; js < 8; ++js) {
+                if (js < JS) {
+                    const int j0 = grp * (m >> 2) + 8 * js;
+                    const uint32_t byte = (rbits[r * 8 + (j0 >> 5)] >> (j0 & 31)) & 0xFFu;
+                    const uint2 lo = sgn[(byte & 15u) * 32 + ssl], hi = sgn[(byte >> 4) * 32 + ssl];
+                    accq = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_sh8(make_uint4(lo.x, lo.y, hi.x, hi.y)), bj[js],
+                                                                 accq, 0, 0, 0);
                 }
             }
             // column n + 8 holds the q_lo part of query n: add the two halves
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] += xor_lane<8>(acc[v]);
+            for (int v = 0; v < 4; ++v) {
+                acc[v] += xor_lane<8>(acc[v]);
+                accq[v] += xor_lane<8>(accq[v]);
+            }
             if (n < 8) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int row = 16 * j + 4 * grp + v;
-                    es[8 * wave + n][row] = row < nt ? rn[row] * (acc[v] * qinv) : -INFINITY;
+                    es[8 * wave + n][row] = row < nt ? rn[row] * (fmaf(rg[row], accq[v], acc[v]) * qinv) : -INFINITY;
                 }
             }
         }
