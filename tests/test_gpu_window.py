@@ -119,3 +119,44 @@ def test_zero_capacity_equals_decode(tq):
                          empty, torch.zeros(B, dtype=torch.int32, device="cuda"), 0.088, b, ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_window_full_size_sampled_heads(tq):
+    """The decode workload with its residual window, in the launch
+    configuration the benchmark times: batch 16, 28 query heads over 4 kv heads,
+    32768 packed tokens (GPU-encoded, sampled slices carry oracle bytes) plus a
+    128-token fp16 window per sequence; the 7 query heads of three (batch, kv
+    head) slices are checked."""
+    from tests.test_gpu_attn import _fill_gpu_cache, _overwrite_slice
+    B, Hkv, g, cap, d, rw = 16, 4, 7, 32768, 128, 128
+    K, V = synth.decode_cache_inputs(B, Hkv, cap, d, device="cuda")
+    q = synth.decode_queries(B, Hkv * g, d, device="cuda")
+    kc, vc = tq.tq_codebook(4, d, 42), tq.tq_codebook(2, d, 42)
+    kc_r, vc_r = o.Codec(4, d, 42), o.Codec(2, d, 42)
+    dev = _fill_gpu_cache(tq, kc, vc, K, V)
+    samples = [(0, 0), (15, 3), (9, 2)]
+    for b, kh in samples:
+        _overwrite_slice(dev, b, kh, K[b, kh].float().cpu().numpy(), V[b, kh].float().cpu().numpy(), kc_r, vc_r)
+    del K, V
+    kw, vw = synth.kv_block(B * Hkv, rw, d, 9000, device="cuda", dtype=torch.float16)
+    kw, vw = kw.view(B, Hkv, rw, d).contiguous(), vw.view(B, Hkv, rw, d).contiguous()
+    win_len = [rw] * B
+    win_len[9] = 77
+    ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, B, Hkv * g, Hkv, cap))
+    out = torch.empty(B, Hkv * g, d, device="cuda")
+    tq.tq_attn_decode_rw(kc, vc, q, torch.full((B,), cap, dtype=torch.int32, device="cuda"), dev["k_codes"],
+                         dev["k_norms"], dev["v_codes"], dev["v_norms"], kw, vw,
+                         torch.tensor(win_len, dtype=torch.int32, device="cuda"), 1 / math.sqrt(d), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    qn = q.float().cpu().numpy().astype(np.float64)
+    for b, kh in samples:
+        w = win_len[b]
+        ref = o.attention(qn[b, kh * g:(kh + 1) * g], dev["k_codes"][b, kh].cpu().numpy(),
+                          dev["k_norms"][b, kh].cpu().numpy(), dev["v_codes"][b, kh].cpu().numpy(),
+                          dev["v_norms"][b, kh].cpu().numpy(), kc_r, vc_r, 1 / math.sqrt(d),
+                          k_win=kw[b, kh, :w].float().cpu().numpy().astype(np.float64),
+                          v_win=vw[b, kh, :w].float().cpu().numpy().astype(np.float64))
+        rel = parity.rel_rows(got[b, kh * g:(kh + 1) * g], ref)
+        assert rel.max() <= parity.ATTN_TOL, (b, kh, rel.max())
+    assert np.all(np.isfinite(got))
