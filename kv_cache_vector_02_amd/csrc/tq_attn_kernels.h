@@ -1103,8 +1103,9 @@ __global__ __launch_bounds__(256) void window_kernel(AttnArgs a) {
         join(mrg[w][0], mrg[w][1], yo);
     }
     // the window's share in the rotated domain, x = H(D_V y), then the merge
-    // with the head's split partials and the output (every group of wave 0
-    // holds the same state; group 0 stores)
+    // with the head's split partials and the output (every lane group of wave
+    // 0 holds the merged state, up to the rounding order of its merges; group
+    // 0's is the one stored)
     const uint32_t sbits = (a.vc.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = as_f(as_u(y[e]) ^ (((sbits >> e) & 1u) << 31));
