@@ -64,7 +64,8 @@ def check_search(tq, n_db, n_q, d, bits, m, k, seed):
     return g_s, g_i, est
 
 
-@pytest.mark.parametrize("d,bits,m", [(256, 3, 256), (128, 3, 128), (256, 2, 0), (128, 4, 64)])
+@pytest.mark.parametrize("d,bits,m", [(256, 3, 256), (128, 3, 128), (256, 2, 0), (128, 4, 64), (256, 4, 32),
+                                        (128, 2, 256)])
 def test_search_small(tq, d, bits, m):
     check_search(tq, n_db=5000, n_q=100, d=d, bits=bits, m=m, k=10, seed=d + bits + m)
 
