@@ -137,3 +137,37 @@ def test_decode_loop(tq):
         want = o.gqa_attention(q.float().numpy().astype(np.float64), ctx, host["k_codes"], host["k_norms"],
                                host["v_codes"], host["v_norms"], kc_r, vc_r, scale)
         assert parity.rel_rows(out.cpu().numpy().reshape(-1, d), want).max() <= parity.ATTN_TOL
+
+
+def test_append_full_size_decode_cache(tq):
+    """The decode-step append the benchmark times: the new K4/V2 token of 16
+    sequences x 4 kv heads written at the last slot of a 32768-token cache
+    (one sequence at an out-of-range position); the appended rows match the
+    oracle and no other slot of the sampled planes changes."""
+    B, Hkv, cap, d = 16, 4, 32768, 128
+    kc, vc = tq.tq_codebook(4, d, 42), tq.tq_codebook(2, d, 42)
+    kc_r, vc_r = o.Codec(4, d, 42), o.Codec(2, d, 42)
+    planes = {
+        "k_codes": torch.full((B, Hkv, cap, kc.code_bytes), 0x5A, dtype=torch.uint8, device="cuda"),
+        "k_norms": torch.full((B, Hkv, cap), 0.5, dtype=torch.float16, device="cuda"),
+        "v_codes": torch.full((B, Hkv, cap, vc.code_bytes), 0x5A, dtype=torch.uint8, device="cuda"),
+        "v_norms": torch.full((B, Hkv, cap), 0.5, dtype=torch.float16, device="cuda"),
+    }
+    kn, vn = synth.kv_block(B * Hkv, 1, d, 9100, device="cuda", dtype=torch.float16)
+    kn, vn = kn.view(B, Hkv, d).contiguous(), vn.view(B, Hkv, d).contiguous()
+    pos = torch.full((B,), cap - 1, dtype=torch.int32, device="cuda")
+    pos[5] = cap  # past the end: nothing written for sequence 5
+    tq.tq_append(kc, vc, kn, vn, pos, planes["k_codes"], planes["k_norms"], planes["v_codes"], planes["v_norms"])
+    torch.cuda.synchronize()
+    for x, codec_r, ck, nk in ((kn, kc_r, "k_codes", "k_norms"), (vn, vc_r, "v_codes", "v_norms")):
+        ref = o.encode(x.float().cpu().numpy().reshape(-1, d).astype(np.float64), codec_r)
+        got_codes = planes[ck][:, :, cap - 1].cpu().numpy().reshape(B * Hkv, -1)
+        got_norms = planes[nk][:, :, cap - 1].cpu().numpy().reshape(-1)
+        live = np.array([b != 5 for b in range(B) for _ in range(Hkv)])
+        sub = {k: v[live] for k, v in ref.items() if isinstance(v, np.ndarray) and v.shape[:1] == (B * Hkv,)}
+        parity.compare_codes(got_codes[live], sub, codec_r)
+        parity.compare_halves(got_norms[live].view(np.uint16), sub["norm"], sub["norms"])
+        assert np.all(got_codes[~live] == 0x5A)
+        for b in (0, 5, 15):  # untouched slots of sampled planes
+            assert torch.all(planes[ck][b, :, : cap - 1] == 0x5A)
+            assert torch.all(planes[nk][b, :, : cap - 1] == 0.5)
