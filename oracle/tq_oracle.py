@@ -314,6 +314,30 @@ def append(codes, norms16, x_new, pos, codec: Codec, S=None, qjl=None, gamma16=N
     return enc
 
 
+def prefill(codes, norms16, x_chunk, t0: int, codec: Codec, S=None, qjl=None, gamma16=None):
+    """Chunked prefill into one sequence's packed cache ([P3] "실험 설계": the
+    prompt's K/V enter the compressed cache chunk by chunk before decoding).
+
+    codes [H][cap][row], norms16 [H][cap] (with QJL qjl [H][cap][m/8], gamma16
+    [H][cap]) are updated in place: token t of head h in x_chunk [H][T][d] is
+    encoded and written at slot t0 + t.  Requires 0 <= t0 and t0 + T <= cap.
+    Returns the encode() result of the chunk's rows (head-major).
+    """
+    H, T, d = np.asarray(x_chunk).shape
+    cap = norms16.shape[1]
+    if t0 < 0 or t0 + T > cap:
+        raise ValueError("chunk outside the cache")
+    enc = encode(np.asarray(x_chunk, dtype=np.float64).reshape(H * T, d), codec, S)
+    for h in range(H):
+        rows = slice(h * T, (h + 1) * T)
+        codes[h, t0:t0 + T] = enc["codes"][rows]
+        norms16[h, t0:t0 + T] = enc["norms"][rows]
+        if codec.qjl_m:
+            qjl[h, t0:t0 + T] = enc["qjl"][rows]
+            gamma16[h, t0:t0 + T] = enc["gamma"][rows]
+    return enc
+
+
 def qjl_term(q: np.ndarray, qjl_packed: np.ndarray, norms16: np.ndarray,
              gamma16: np.ndarray, S: np.ndarray, codec: Codec) -> np.ndarray:
     """QJL estimate of <q, x - x_hat> for every (query, row) pair.

@@ -437,6 +437,28 @@ def test_append_token_by_token_equals_whole_encode():
                 assert np.all(norms[b, h, untouched].view(np.uint16) == 0x1234)
 
 
+def test_prefill_chunks_equal_whole_encode():
+    """Prefilling a sequence chunk by chunk gives the bytes of encoding every
+    token at once, at the right slots; slots past the prefill stay untouched
+    and a chunk outside the cache is rejected."""
+    d, H, cap, T = 64, 3, 20, 4
+    rng = np.random.default_rng(25)
+    codec = o.Codec(3, d, 6)
+    X = rng.standard_normal((H, 3 * T, d)) * 3
+    codes = np.full((H, cap, d * 3 // 8), 0xAB, np.uint8)
+    norms = np.full((H, cap), 0x1234, np.uint16).view(np.float16)
+    for c in range(3):
+        o.prefill(codes, norms, X[:, c * T:(c + 1) * T], 2 + c * T, codec)
+    whole = o.encode(X.reshape(-1, d), codec)
+    for h in range(H):
+        for t in range(3 * T):
+            r = h * 3 * T + t
+            assert np.array_equal(codes[h, 2 + t], whole["codes"][r]) and norms[h, 2 + t] == whole["norms"][r]
+        assert np.all(codes[h, :2] == 0xAB) and np.all(codes[h, 2 + 3 * T:] == 0xAB)
+    with pytest.raises(ValueError):
+        o.prefill(codes, norms, X[:, :T], cap - T + 1, codec)
+
+
 # -------------------------------------------------------------------- QJL ----
 def test_qjl_sign_projection_closed_form():
     """E[sign(s.r) (s.a)] = sqrt(2/pi) <a, r>/||r|| for s ~ N(0, I)."""
