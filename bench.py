@@ -304,12 +304,9 @@ def long_leg(tq, torch, synth, steps, warmup):
     enc_ms = 0.0
     for ci in range(n_chunks):
         k, v = synth.long_chunk(ci, kv_heads=Hkv, tokens=chunk, d=d, device="cuda")
-        sl = slice(ci * chunk, (ci + 1) * chunk)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for h in range(Hkv):
-            tq.tq_encode_kv(kc, vc, k[h], v[h], c["k_codes"][0, h, sl], c["k_norms"][0, h, sl],
-                            c["v_codes"][0, h, sl], c["v_norms"][0, h, sl])
+        tq.tq_prefill(kc, vc, k, v, ci * chunk, c["k_codes"][0], c["k_norms"][0], c["v_codes"][0], c["v_norms"][0])
         b.record()
         torch.cuda.synchronize()
         enc_ms += a.elapsed_time(b)

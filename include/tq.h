@@ -137,6 +137,31 @@ int tq_encode_kv(const tq_codec *kc, const tq_codec *vc, const void *k, const vo
                  const float *qjl_S, uint8_t *k_qjl_bits, uint16_t *k_qjl_gamma_f16, void *stream);
 
 /*
+ * tq_prefill -- chunked prefill: encode one sequence's chunk of `tokens` new
+ * keys and values per head into its packed cache at token slots
+ * [t0, t0 + tokens), all heads in one call (one launch unless kc uses QJL).
+ * [P3] ("실험 설계") describes the prompt's K/V entering the compressed cache
+ * before decoding; the chunk size is the caller's.  Same arithmetic as tq_encode.
+ *
+ *   k, v      [n_heads][tokens][d] elements of x_dtype, contiguous, 16-byte aligned.
+ *   k_codes, v_codes    one sequence's cache planes [n_heads][ctx_cap][d*bits/8]
+ *             (for sequence b of a batched cache, pass the plane pointers offset
+ *             by b * n_heads * ctx_cap rows), 4-byte aligned; k_norms_f16,
+ *             v_norms_f16 [n_heads][ctx_cap].
+ *   qjl_S, k_qjl_bits [n_heads][ctx_cap][m/8], k_qjl_gamma_f16 [n_heads][ctx_cap]:
+ *             as in tq_encode for kc, NULL when kc has no QJL.
+ * Only the slots [t0, t0 + tokens) of every head are written; tokens = 0 is
+ * valid and launches nothing.  Errors: TQ_EINVAL for NULL or misaligned
+ * pointers, a bad x_dtype, n_heads or ctx_cap <= 0, t0 < 0, tokens < 0 or
+ * t0 + tokens > ctx_cap; TQ_EUNSUPPORTED for an unsupported codec, codecs of
+ * different d, or QJL on vc.
+ */
+int tq_prefill(const tq_codec *kc, const tq_codec *vc, const void *k, const void *v, int x_dtype,
+               int n_heads, int64_t tokens, int64_t t0, int64_t ctx_cap,
+               uint8_t *k_codes, uint16_t *k_norms_f16, uint8_t *v_codes, uint16_t *v_norms_f16,
+               const float *qjl_S, uint8_t *k_qjl_bits, uint16_t *k_qjl_gamma_f16, void *stream);
+
+/*
  * tq_append -- the decode-step append: encode the new key and value of every
  * (sequence, head) into the packed cache at that sequence's position.  [P3]
  * ("결과 — 피크 VRAM") describes each decode step adding the new K/V to the

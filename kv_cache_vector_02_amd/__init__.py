@@ -22,7 +22,7 @@ TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 _DTYPES = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16}
 
 EXPORTS = (
-    "tq_codebook", "tq_encode", "tq_encode_kv", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
+    "tq_codebook", "tq_encode", "tq_encode_kv", "tq_prefill", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
     "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror",
 )
@@ -75,6 +75,7 @@ def _load():
         "tq_codebook": (I, [I, I, ctypes.c_uint64, I, CP]),
         "tq_encode": (I, [CP, P, I, I64, I64, P, I64, P, P, P, P, P]),
         "tq_encode_kv": (I, [CP, CP, P, P, I, I64, I64, P, I64, P, P, I64, P, P, P, P, P]),
+        "tq_prefill": (I, [CP, CP, P, P, I, I, I64, I64, I64, P, P, P, P, P, P, P, P]),
         "tq_append": (I, [CP, CP, P, P, I, I, I, P, I64, P, P, P, P, P, P, P, P]),
         "tq_decode": (I, [CP, P, I64, P, I64, P, P]),
         "tq_attn_decode": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
@@ -168,6 +169,26 @@ def tq_encode_kv(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, k
                              k.stride(0), _ptr(k_codes), k_codes.stride(0), _ptr(k_norms), _ptr(v_codes),
                              v_codes.stride(0), _ptr(v_norms), _ptr(qjl_S), _ptr(k_qjl_bits), _ptr(k_qjl_gamma),
                              _stream(stream, k)), "tq_encode_kv")
+
+
+def tq_prefill(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, t0: int, k_codes: torch.Tensor,
+               k_norms: torch.Tensor, v_codes: torch.Tensor, v_norms: torch.Tensor,
+               qjl_S: torch.Tensor | None = None, k_qjl_bits: torch.Tensor | None = None,
+               k_qjl_gamma: torch.Tensor | None = None, stream=None) -> None:
+    """k, v [H][T][d] (one dtype) contiguous; one sequence's cache planes
+    [H][cap][d*bits/8] uint8 and norms [H][cap] (2-byte dtype), contiguous (a
+    slice [b] of a batched cache is); writes slots [t0, t0 + T) of every head."""
+    for t in (k, v, k_codes, k_norms, v_codes, v_norms):
+        if not t.is_contiguous():
+            raise ValueError("prefill tensors must be contiguous")
+    if k.dim() != 3 or k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must be [H][T][d] of one dtype")
+    if k_codes.dim() != 3 or k_codes.shape[0] != k.shape[0] or v_codes.shape[:2] != k_codes.shape[:2]:
+        raise ValueError("cache planes must be [H][cap][row] matching k")
+    H, T = k.shape[0], k.shape[1]
+    _check(_lib.tq_prefill(ctypes.byref(kc), ctypes.byref(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], H, T, t0,
+                           k_codes.shape[1], _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), _ptr(qjl_S),
+                           _ptr(k_qjl_bits), _ptr(k_qjl_gamma), _stream(stream, k)), "tq_prefill")
 
 
 def tq_append(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor,

@@ -171,6 +171,8 @@ static int encode_setup(const tq_codec* c, const void* x, int x_dtype, int64_t n
     a->pos = nullptr;
     a->cap = 0;
     a->seq_heads = 1;
+    a->grp_rows = 0;
+    a->grp_off = 0;
     return TQ_OK;
 }
 
@@ -197,6 +199,30 @@ int tq_encode_kv(const tq_codec* kc, const tq_codec* vc, const void* k, const vo
         rc = encode_setup(vc, v, x_dtype, n, x_row_stride, v_codes, v_code_row_stride, v_norms_f16, nullptr, nullptr,
                           nullptr, &va);
     if (rc != TQ_OK || n == 0) return rc;
+    return finish(tqi::launch_encode_pair(ka, va, x_dtype, (hipStream_t)stream));
+}
+
+int tq_prefill(const tq_codec* kc, const tq_codec* vc, const void* k, const void* v, int x_dtype, int n_heads,
+               int64_t tokens, int64_t t0, int64_t ctx_cap, uint8_t* k_codes, uint16_t* k_norms_f16, uint8_t* v_codes,
+               uint16_t* v_norms_f16, const float* qjl_S, uint8_t* k_qjl_bits, uint16_t* k_qjl_gamma_f16,
+               void* stream) {
+    if (!kc || !vc) return TQ_EINVAL;
+    if (kc->d != vc->d || vc->qjl_m != 0) return TQ_EUNSUPPORTED;
+    if (n_heads <= 0 || tokens < 0 || t0 < 0 || ctx_cap <= 0 || t0 + tokens > ctx_cap) return TQ_EINVAL;
+    const int64_t n = (int64_t)n_heads * tokens;
+    tqi::EncodeArgs ka, va;
+    // cache rows are exactly d*bits/8 bytes (the layout the attention calls read)
+    int rc = encode_setup(kc, k, x_dtype, n, kc->d, k_codes, kc->d * kc->bits / 8, k_norms_f16, qjl_S, k_qjl_bits,
+                          k_qjl_gamma_f16, &ka);
+    if (rc == TQ_OK)
+        rc = encode_setup(vc, v, x_dtype, n, vc->d, v_codes, vc->d * vc->bits / 8, v_norms_f16, nullptr, nullptr,
+                          nullptr, &va);
+    if (rc != TQ_OK || n == 0) return rc;
+    for (tqi::EncodeArgs* a : {&ka, &va}) {
+        a->cap = ctx_cap;
+        a->grp_rows = tokens;
+        a->grp_off = t0;
+    }
     return finish(tqi::launch_encode_pair(ka, va, x_dtype, (hipStream_t)stream));
 }
 

@@ -86,11 +86,15 @@ __device__ __forceinline__ void load_rotate(const EncodeArgs& a, int64_t row, bo
     fwht<LPV>(st.v, gl);
 }
 
-// Output row of input row `row` (see EncodeArgs); keep = false when an append
-// position lies outside the cache.
+// Output row of input row `row` (see EncodeArgs: plain, append or prefill
+// mapping); keep = false when an append position lies outside the cache.
 __device__ __forceinline__ int64_t out_row(const EncodeArgs& a, int64_t row, bool& keep) {
     keep = true;
-    if (!a.pos) return row;
+    if (!a.pos) {
+        if (a.grp_rows <= 0) return row;
+        const int64_t g = row / a.grp_rows;
+        return g * a.cap + a.grp_off + (row - g * a.grp_rows);
+    }
     const int p = a.pos[row / a.seq_heads];
     keep = p >= 0 && (int64_t)p < a.cap;
     return row * a.cap + (keep ? p : 0);

@@ -33,6 +33,10 @@ struct EncodeArgs {
     const int32_t* pos;
     int64_t cap;
     int seq_heads;
+    // chunked prefill (pos unset, grp_rows > 0): input row r goes to output row
+    // (r / grp_rows) * cap + grp_off + r % grp_rows
+    int64_t grp_rows;
+    int64_t grp_off;
 };
 
 struct DecodeArgs {

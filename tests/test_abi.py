@@ -164,6 +164,25 @@ def test_encode_kv_argument_errors():
     assert call(kc=cq, kcs=48) == tq.TQ_EINVAL  # QJL key codec without its buffers
 
 
+def test_prefill_argument_errors():
+    c = tq.tq_codebook(3, 128, 0)
+    cq = tq.tq_codebook(3, 128, 0, 128)
+    P = FAKE
+
+    def call(kc=c, vc=c, h=8, tokens=4096, t0=0, cap=1 << 20, x=P):
+        return tq.raw_call("tq_prefill", ctypes.byref(kc), ctypes.byref(vc), x, P, 2, h, tokens, t0, cap, P, P, P,
+                           P, None, None, None, None)
+
+    assert call(tokens=0) == tq.TQ_OK  # nothing to do
+    assert call(h=0) == tq.TQ_EINVAL
+    assert call(t0=-1) == tq.TQ_EINVAL
+    assert call(tokens=-5) == tq.TQ_EINVAL
+    assert call(t0=(1 << 20) - 4095) == tq.TQ_EINVAL  # past the capacity
+    assert call(x=None) == tq.TQ_EINVAL
+    assert call(vc=cq) == tq.TQ_EUNSUPPORTED
+    assert call(kc=cq) == tq.TQ_EINVAL  # QJL key codec without its buffers
+
+
 def test_search_argument_errors():
     c = tq.tq_codebook(3, 256, 0, 256)
     P = FAKE

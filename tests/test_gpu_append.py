@@ -171,3 +171,59 @@ def test_append_full_size_decode_cache(tq):
         for b in (0, 5, 15):  # untouched slots of sampled planes
             assert torch.all(planes[ck][b, :, : cap - 1] == 0x5A)
             assert torch.all(planes[nk][b, :, : cap - 1] == 0.5)
+
+
+@pytest.mark.parametrize("kbits,m,dtype", [(3, 0, torch.bfloat16), (3, 128, torch.float32)])
+def test_prefill_chunks(tq, kbits, m, dtype):
+    """Chunked prefill of sequence 1 of a two-sequence cache (4096-token chunks
+    and a ragged last one, K and V of 8 heads per call): the written slots match
+    the oracle's prefill and the bytes of per-head tq_encode_kv calls; sequence 0
+    and the slots past the prefill are untouched."""
+    H, cap, d, chunk, total = 8, 10000, 128, 4096, 9000
+    kc, vc = tq.tq_codebook(kbits, d, 77, m), tq.tq_codebook(3, d, 77)
+    kc_r, vc_r = o.Codec(kbits, d, 77, m), o.Codec(3, d, 77)
+    S = synth.qjl_projection(m, d, seed=9) if m else None
+    S64 = S.numpy().astype(np.float64) if m else None
+
+    def cache():
+        c = {"k_codes": torch.full((2, H, cap, kc.code_bytes), 0xA5, dtype=torch.uint8, device="cuda"),
+             "k_norms": torch.full((2, H, cap), 2.0, dtype=torch.float16, device="cuda"),
+             "v_codes": torch.full((2, H, cap, vc.code_bytes), 0xA5, dtype=torch.uint8, device="cuda"),
+             "v_norms": torch.full((2, H, cap), 2.0, dtype=torch.float16, device="cuda")}
+        if m:
+            c["k_qjl"] = torch.full((2, H, cap, m // 8), 0xA5, dtype=torch.uint8, device="cuda")
+            c["k_gamma"] = torch.full((2, H, cap), 2.0, dtype=torch.float16, device="cuda")
+        return c
+
+    a, b = cache(), cache()
+    ref = {key: v[1].cpu().numpy().copy() for key, v in a.items()}
+    for t0 in range(0, total, chunk):
+        T = min(chunk, total - t0)
+        k, v = synth.long_chunk(t0 // chunk, kv_heads=H, tokens=T, d=d, device="cuda")
+        k, v = k.to(dtype).contiguous(), v.to(dtype).contiguous()
+        tq.tq_prefill(kc, vc, k, v, t0, a["k_codes"][1], a["k_norms"][1], a["v_codes"][1], a["v_norms"][1],
+                      None if S is None else S.cuda(), a["k_qjl"][1] if m else None, a["k_gamma"][1] if m else None)
+        for h in range(H):  # the same rows head by head through tq_encode_kv
+            sl = slice(t0, t0 + T)
+            tq.tq_encode_kv(kc, vc, k[h], v[h], b["k_codes"][1, h, sl], b["k_norms"][1, h, sl],
+                            b["v_codes"][1, h, sl], b["v_norms"][1, h, sl], None if S is None else S.cuda(),
+                            b["k_qjl"][1, h, sl] if m else None, b["k_gamma"][1, h, sl] if m else None)
+        kx, vx = k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64)
+        enc_k = o.prefill(ref["k_codes"], ref["k_norms"], kx, t0, kc_r, S64, ref.get("k_qjl"), ref.get("k_gamma"))
+        enc_v = o.prefill(ref["v_codes"], ref["v_norms"], vx, t0, vc_r)
+        torch.cuda.synchronize()
+        for enc, codec_r, ck, nk in ((enc_k, kc_r, "k_codes", "k_norms"), (enc_v, vc_r, "v_codes", "v_norms")):
+            got = a[ck][1, :, t0:t0 + T].cpu().numpy().reshape(H * T, -1)
+            _, bad_rows = parity.compare_codes(got, enc, codec_r)
+            parity.compare_halves(a[nk][1, :, t0:t0 + T].cpu().numpy().reshape(-1).view(np.uint16), enc["norm"],
+                                  enc["norms"])
+            if codec_r.qjl_m:
+                parity.compare_halves(a["k_gamma"][1, :, t0:t0 + T].cpu().numpy().reshape(-1).view(np.uint16),
+                                      enc["gamma64"], enc["gamma"], skip=bad_rows)
+                parity.compare_qjl(a["k_qjl"][1, :, t0:t0 + T].cpu().numpy().reshape(H * T, -1), enc, S64, codec_r,
+                                   bad_rows)
+    for key in a:
+        assert torch.equal(a[key].view(torch.uint8), b[key].view(torch.uint8)), key  # same bytes as per-head calls
+        assert torch.all(a[key][0].view(torch.uint8) == b[key][0].view(torch.uint8))
+    assert torch.all(a["k_codes"][0] == 0xA5) and torch.all(a["k_codes"][1, :, total:] == 0xA5)
+    assert torch.all(a["v_norms"][1, :, total:] == 2.0)
