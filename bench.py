@@ -29,7 +29,7 @@ the GPU reach its sustained clock: a decode loop run straight from idle is
 timed while the clocks still ramp, which reads about 20% slower than the steady
 state a serving loop runs in.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs decode,encode,long,search]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs decode,encode,long,search,quality]
 """
 from __future__ import annotations
 
@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=2000)
-    ap.add_argument("--legs", default="decode,encode,long,search")
+    ap.add_argument("--legs", default="decode,encode,long,search,quality")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
@@ -384,6 +384,65 @@ def search_leg(tq, torch, synth, steps, warmup):
     }
 
 
+# ----------------------------------------------------------------- quality ----
+def quality_leg(tq, torch, synth):
+    """Context, not parity: the tiny workload (1 kv head, d=128, 512 keys and
+    values, 8 queries, 3-bit codecs) through the GPU path against exact
+    uncompressed attention computed in float64 on the host -- the analogue of
+    the pages' attention-score similarity and top-1 agreement figures.  MSE-only
+    keys and keys with QJL (m=128): output cosine of tq_attn_decode, key-score
+    cosine of q.K_hat (tq_decode), and top-1 agreement of the key scores
+    (tq_ip_search with k=1, which ranks by the QJL-corrected estimate)."""
+    k, v, q, S = synth.tiny()
+    n, d = k.shape
+    scale = 1.0 / math.sqrt(d)
+    k64, v64, q64 = (t.double() for t in (k, v, q))
+    s_exact = (q64 @ k64.T) * scale
+    o_exact = torch.softmax(s_exact, dim=1) @ v64
+    top_exact = s_exact.argmax(dim=1)
+    kd, vd, qd, Sd = k.cuda(), v.cuda(), q.cuda(), S.cuda()
+    vc = tq.tq_codebook(3, d, 0)
+    v_codes = torch.empty(n, vc.code_bytes, dtype=torch.uint8, device="cuda")
+    v_norms = torch.empty(n, dtype=torch.float16, device="cuda")
+    tq.tq_encode(vc, vd, v_codes, v_norms)
+
+    def cos_rows(a, b):
+        return float((torch.nn.functional.cosine_similarity(a, b, dim=1)).mean())
+
+    out = {"workload": "tiny: 1 kv head, d=128, 512 keys/values and 8 queries fp32 N(0,1), 3-bit K and V"}
+    for name, m in (("mse", 0), ("qjl", 128)):
+        kc = tq.tq_codebook(3, d, 0, m)
+        k_codes = torch.empty(n, kc.code_bytes, dtype=torch.uint8, device="cuda")
+        k_norms = torch.empty(n, dtype=torch.float16, device="cuda")
+        bits = torch.empty(n, max(m // 8, 1), dtype=torch.uint8, device="cuda") if m else None
+        gamma = torch.empty(n, dtype=torch.float16, device="cuda") if m else None
+        tq.tq_encode(kc, kd, k_codes, k_norms, Sd if m else None, bits, gamma)
+        o_gpu = torch.empty(1, q.shape[0], d, device="cuda")
+        ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, 1, q.shape[0], 1, n))
+        ctx = torch.tensor([n], dtype=torch.int32, device="cuda")
+        tq.tq_attn_decode(kc, vc, qd[None].contiguous(), ctx, k_codes[None, None].contiguous(),
+                          k_norms[None, None].contiguous(), v_codes[None, None].contiguous(),
+                          v_norms[None, None].contiguous(), scale, o_gpu, ws,
+                          bits[None, None].contiguous() if m else None, gamma[None, None].contiguous() if m else None,
+                          Sd if m else None)
+        sws = tq.workspace(tq.tq_search_workspace_bytes(kc, q.shape[0], n, 1))
+        top_s = torch.empty(q.shape[0], 1, device="cuda")
+        top_i = torch.empty(q.shape[0], 1, dtype=torch.int64, device="cuda")
+        tq.tq_ip_search(kc, qd, k_codes, k_norms, bits, gamma, Sd if m else None, 1, top_s, top_i, sws)
+        torch.cuda.synchronize()
+        entry = {
+            "output_cosine": cos_rows(o_gpu[0].double().cpu(), o_exact),
+            "top1_agreement": float((top_i[:, 0].cpu() == top_exact).double().mean()),
+        }
+        if m == 0:
+            k_hat = torch.empty(n, d, device="cuda")
+            tq.tq_decode(kc, k_codes, k_norms, k_hat)
+            torch.cuda.synchronize()
+            entry["score_cosine"] = cos_rows((q64 @ k_hat.double().cpu().T) * scale, s_exact)
+        out[name] = entry
+    return out
+
+
 # -------------------------------------------------------------- CPU oracle ----
 def cpu_baseline(torch, synth, target_s):
     """The oracle, untouched, on a bounded sample of the decode workload: the
@@ -504,6 +563,9 @@ def main():
         log("search leg (2^20 x 256, 1024 queries)")
         res["search"] = search_leg(tq, torch, synth, args.steps, args.warmup)
         log(f"search: {res['search']['ms_per_call']:.2f} ms/call, {res['search']['tflops']:.1f} TFLOP/s")
+    if "quality" in legs:
+        res["quality"] = quality_leg(tq, torch, synth)
+        log(f"quality: {res['quality']}")
     if "decode" in legs and not args.calib_copy:  # counter runs keep the calibration copies the only large ones
         res["read_ceiling"] = read_ceiling(torch)
         log(f"streaming-read reference: {res['read_ceiling']['gbs']:.0f} GB/s")
@@ -558,7 +620,7 @@ def main():
             line["read_ceiling"] = rc
     if cpu:
         line["cpu_baseline"] = cpu
-    for k in ("encode", "long", "search"):
+    for k in ("encode", "long", "search", "quality"):
         if k in res:
             line[k] = res[k]
     if "encode" in res:
