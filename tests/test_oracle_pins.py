@@ -500,6 +500,101 @@ def test_qjl_estimator_unbiased():
     assert abs(zs.mean()) < 4 / math.sqrt(len(zs))
 
 
+def test_pack_signs_bit_order():
+    """QJL sign bits use the same LSB-first stream as 1-bit indices: projection
+    j sits in bit j % 8 of byte j // 8 (the layout the library documents)."""
+    rng = np.random.default_rng(16)
+    bits = rng.integers(0, 2, size=(5, 64)).astype(np.uint8)
+    packed = o.pack_signs(bits)
+    assert np.array_equal(packed, o.pack_indices(bits, 1))
+    assert np.array_equal(packed, _naive_pack(bits, 1))
+    assert np.array_equal(o.unpack_signs(packed, 64), bits)
+    one = np.zeros((1, 16), dtype=np.uint8)
+    one[0, 0] = 1
+    one[0, 9] = 1
+    assert o.pack_signs(one).tolist() == [[0x01, 0x02]]
+
+
+def _qjl_case(seed, d=64, m=64, n=40, kscale=3.0):
+    rng = np.random.default_rng(seed)
+    S = rng.standard_normal((m, d))
+    kc, vc = o.Codec(3, d, seed=5, qjl_m=m), o.Codec(2, d, seed=6)
+    ek = o.encode(kscale * rng.standard_normal((n, d)), kc, S)
+    ev = o.encode(rng.standard_normal((n, d)), vc)
+    q = rng.standard_normal((3, d))
+    return S, kc, vc, ek, ev, q
+
+
+def test_qjl_attention_is_softmax_of_scaled_estimates():
+    """With QJL keys, attention() is softmax(scale * est) V_hat where est is the
+    inner-product estimator ip_scores() (pinned by its unbiasedness): the whole
+    estimate, QJL term included, carries the softmax scale."""
+    from scipy.special import softmax
+
+    S, kc, vc, ek, ev, q = _qjl_case(17)
+    scale = 0.37
+    got = o.attention(q, ek["codes"], ek["norms"], ev["codes"], ev["norms"], kc, vc, scale,
+                      k_qjl=ek["qjl"], k_gamma=ek["gamma"], S=S)
+    est = o.ip_scores(q, ek["codes"], ek["norms"], ek["qjl"], ek["gamma"], S, kc)
+    V = o.decode(ev["codes"], ev["norms"], vc)
+    want = softmax(scale * est, axis=1) @ V
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-13)
+    # the check has teeth: the QJL term moves the output, and an unscaled QJL
+    # term would move it far more than the tolerance above
+    mse_only = o.ip_scores(q, ek["codes"], ek["norms"], None, None, None, o.Codec(3, kc.d, seed=5))
+    corr = est - mse_only
+    assert np.abs(corr).max() > 0.1
+    unscaled = softmax(scale * mse_only + corr, axis=1) @ V
+    assert np.abs(unscaled - want).max() > 1e-3
+    assert np.abs(softmax(scale * mse_only, axis=1) @ V - want).max() > 1e-4
+
+
+def test_qjl_attention_logit_unbiased():
+    """Through attention outputs alone: with two keys, the logit difference
+    s_0 - s_1 recovered from the output averages over S draws to its closed-form
+    expectation scale * (<q, x0_hat - x1_hat> + residual parts), where
+    E[sign(s.r)(s.a)] = sqrt(2/pi) <a, r>/||r|| makes the QJL term's mean
+    n16 * (gamma16/||r||) * <H(Dq), rho>/d for residual rho = z - c[idx]."""
+    d = m = 32
+    rng = np.random.default_rng(18)
+    kc, vc = o.Codec(2, d, seed=7, qjl_m=m), o.Codec(3, d, seed=8)
+    x = rng.standard_normal((2, d))
+    # a query leaning on key 0's quantisation residual, so the QJL part of the
+    # logit is large
+    e0 = o.encode(x, o.Codec(2, d, seed=7))
+    q = 2.0 * (x[:1] - o.decode(e0["codes"][:1], e0["norms"][:1], o.Codec(2, d, seed=7))) \
+        + 0.3 * rng.standard_normal((1, d))
+    ev = o.encode(rng.standard_normal((2, d)), vc)
+    V = o.decode(ev["codes"], ev["norms"], vc)
+    dv = V[0] - V[1]
+    scale = 0.1
+    draws = 3000
+    diffs = np.empty(draws)
+    for i in range(draws):
+        S = rng.standard_normal((m, d))
+        ek = o.encode(x, kc, S)
+        out = o.attention(q, ek["codes"], ek["norms"], ev["codes"], ev["norms"], kc, vc, scale,
+                          k_qjl=ek["qjl"], k_gamma=ek["gamma"], S=S)[0]
+        p0 = float((out - V[1]) @ dv / (dv @ dv))
+        diffs[i] = math.log(p0 / (1.0 - p0))
+    ek = o.encode(x, kc, rng.standard_normal((m, d)))  # S-independent parts
+    a = o.rotate(q, kc)[0]
+    c = kc.centroid.astype(np.float64)
+    K = o.decode(ek["codes"], ek["norms"], kc)
+    mean = []
+    for t in range(2):
+        rho = ek["z"][t] - c[ek["idx"][t]]
+        n16, g16 = float(ek["norms"][t]), float(ek["gamma"][t])
+        mean.append(scale * (q[0] @ K[t] + n16 * g16 / float(ek["gamma64"][t]) * (a @ rho) / d))
+    want = mean[0] - mean[1]
+    se = diffs.std() / math.sqrt(draws)
+    assert abs(diffs.mean() - want) < 4 * se, (diffs.mean(), want, se)
+    # the residual part is many standard errors away from zero: dropping the
+    # QJL term, its scale or its sign would fail the check above
+    resid = want - scale * (q[0] @ (K[0] - K[1]))
+    assert abs(resid) > 10 * se
+
+
 def test_qjl_bits_and_gamma():
     d, m = 128, 128
     rng = np.random.default_rng(14)
