@@ -189,10 +189,17 @@ int tq_append(const tq_codec *kc, const tq_codec *vc, const void *k, const void 
               const float *qjl_S, uint8_t *k_qjl_bits, uint16_t *k_qjl_gamma_f16, void *stream);
 
 /*
- * tq_decode -- reconstruct x_hat = half_norm * D H(c[idx]) / d for n rows
- * (the inverse rotation; used to check reconstructions, not on the hot path).
- *   codes: row i at codes + i*code_row_stride (4-byte aligned stride and base);
- *   norms_f16 [n]; x_hat [n][d] float32 (16-byte aligned).
+ * tq_decode -- reconstruct x_hat = half_norm * D H(c[idx]) / d for n rows: the
+ * dequantise step of decompress-then-attend ([P3] "결과 — 피크 VRAM": the
+ * reference reconstructs the full K/V each step) with the inverse transform
+ * applied per vector ([P1] v1.5.1 "핵심 기술" item 2: V WHT on encode, IWHT on
+ * read).  Used to check reconstructions; decode attention never calls it.
+ *   codes: row i at codes + i*code_row_stride (code_row_stride >= d*bits/8,
+ *          any byte stride, so rows of a cache with padding can be read in
+ *          place); norms_f16 [n]; x_hat [n][d] float32 (16-byte aligned).
+ * n = 0 is valid and launches nothing.  Errors: TQ_EINVAL for NULL or
+ * misaligned pointers, n < 0 or a short row stride; TQ_EUNSUPPORTED for an
+ * unsupported codec.
  */
 int tq_decode(const tq_codec *c, const uint8_t *codes, int64_t code_row_stride,
               const uint16_t *norms_f16, int64_t n, float *x_hat, void *stream);
@@ -229,6 +236,11 @@ int tq_decode(const tq_codec *c, const uint8_t *codes, int64_t code_row_stride,
  * Supported: n_q_heads % n_kv_heads == 0, group size g = n_q_heads/n_kv_heads
  * with g <= 8 or g a multiple of a divisor in 1..8 (heads are processed in
  * chunks of at most 8).  ctx_cap >= 1.
+ * The context is cut into splits whose count is planned per call from the
+ * device; a positive integer in the environment variable TQ_ATTN_SPLITS
+ * replaces that count (clamped to the capacity's 64-token tiles), which tests
+ * use to show the result does not depend on it.  Query the workspace size
+ * under the same setting.
  */
 int tq_attn_decode(const tq_codec *kc, const tq_codec *vc,
                    const void *q, int q_dtype, int batch, int n_q_heads, int n_kv_heads,
@@ -312,7 +324,31 @@ int tq_attn_decode_rw(const tq_codec *kc, const tq_codec *vc,
                       float scale, float *out, void *workspace, size_t workspace_bytes,
                       void *stream);
 
-/* Bytes of workspace tq_attn_decode (and tq_attn_decode_rw) needs for these sizes (0 on bad arguments). */
+/*
+ * Workspace sizes.  The workspace holds float32 staging of the rotated-domain
+ * partial sums (max, sum, acc[d]) of every (query head, context split) before
+ * the one inverse transform per head (the float staging of [P1] v1.5.2 "핵심
+ * 변경" item 2), and with QJL keys the projected queries (Q_wht2 of [P1] v1.4.2
+ * item 5); for search, the rotated queries and per-block candidate lists.  The
+ * caller allocates it ([P3] "결과 — 피크 VRAM" counts the reference's peak
+ * memory; here nothing is allocated inside a call).
+ *
+ * tq_workspace_bytes(op, ...) -- bytes needed by operation `op` (0 on bad
+ * arguments or an unknown op):
+ *   TQ_OP_ATTN_DECODE, TQ_OP_ATTN_DECODE_RW: kc, vc, batch, n_q_heads,
+ *       n_kv_heads, ctx_cap as for tq_attn_decode (n_q, n_db, k unused);
+ *   TQ_OP_IP_SEARCH: kc is the search codec (vc may be NULL), n_q, n_db, k as
+ *       for tq_ip_search (batch, heads and ctx_cap unused).
+ * The codecs are arguments because the sizes depend on d, the bit widths
+ * (through the split plan) and the QJL width m.  The size depends on the
+ * current device (its compute-unit count sets the split count).
+ * tq_attn_workspace_bytes and tq_search_workspace_bytes are the same sizes for
+ * one operation each.
+ */
+enum { TQ_OP_ATTN_DECODE = 1, TQ_OP_ATTN_DECODE_RW = 2, TQ_OP_IP_SEARCH = 3 };
+size_t tq_workspace_bytes(int op, const tq_codec *kc, const tq_codec *vc, int batch, int n_q_heads,
+                          int n_kv_heads, int64_t ctx_cap, int n_q, int64_t n_db, int k);
+
 size_t tq_attn_workspace_bytes(const tq_codec *kc, const tq_codec *vc, int batch,
                                int n_q_heads, int n_kv_heads, int64_t ctx_cap);
 
@@ -331,7 +367,7 @@ size_t tq_attn_workspace_bytes(const tq_codec *kc, const tq_codec *vc, int batch
  *   out_scores   [n_q][k] float32;  out_ids [n_q][k] int64.  If n_db < k the tail
  *                is filled with -inf and id -1.
  *   workspace    >= tq_search_workspace_bytes(...) bytes, 16-byte aligned.
- * Supported: d in {128, 256}, 1 <= k <= 32, n_db < 2^31.
+ * Supported: d in {128, 256}, 1 <= k <= 64, n_db < 2^31.
  */
 int tq_ip_search(const tq_codec *c, const float *q, int n_q,
                  const uint8_t *codes, const uint16_t *norms,
@@ -341,10 +377,20 @@ int tq_ip_search(const tq_codec *c, const float *q, int n_q,
 
 size_t tq_search_workspace_bytes(const tq_codec *c, int n_q, int64_t n_db, int k);
 
-/* Stored bytes per vector: d*bits/8 codes + 2 B norm (+ m/8 + 2 B with QJL). */
+/*
+ * Stored bytes per vector: d*bits/8 codes + 2 B norm (+ m/8 + 2 B with QJL).
+ * [P1] "약간의 비하인드": a 3-bit head_dim-128 block is 50 B (48 B codes + a
+ * 2 B norm); [P3] "결과 — 피크 VRAM" gives the theoretical compression the
+ * reference's memory_bytes() reports (K4/V2 5.12x against fp16).  Returns 0
+ * for d <= 0, bits outside 1..4 or qjl_m < 0.
+ */
 size_t tq_packed_bytes(int d, int bits, int qjl_m);
 
-/* Static description of an error code (never NULL). */
+/*
+ * Static description of an error code (never NULL).  [P1] v1.2.0 ("입력 검증")
+ * handles invalid K/V type combinations by silently falling back; this
+ * library reports them as TQ_EUNSUPPORTED and leaves the policy to the caller.
+ */
 const char *tq_strerror(int code);
 
 #ifdef __cplusplus

@@ -23,9 +23,10 @@ _DTYPES = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16
 
 EXPORTS = (
     "tq_codebook", "tq_encode", "tq_encode_kv", "tq_prefill", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
-    "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes",
+    "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes", "tq_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror",
 )
+TQ_OP_ATTN_DECODE, TQ_OP_ATTN_DECODE_RW, TQ_OP_IP_SEARCH = 1, 2, 3
 
 
 class tq_codec(ctypes.Structure):
@@ -84,6 +85,7 @@ def _load():
         "tq_attn_combine": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
         "tq_attn_decode_rw": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, P, P, I, P, I, F, P, P, SZ, P]),
         "tq_attn_workspace_bytes": (SZ, [CP, CP, I, I, I, I64]),
+        "tq_workspace_bytes": (SZ, [I, CP, CP, I, I, I, I64, I, I64, I]),
         "tq_ip_search": (I, [CP, P, I, P, P, P, P, P, I64, I, P, P, P, SZ, P]),
         "tq_search_workspace_bytes": (SZ, [CP, I, I64, I]),
         "tq_packed_bytes": (SZ, [I, I, I]),
@@ -120,6 +122,49 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _shape(t, shape, name, dtype=None, elem=None):
+    """Raises ValueError unless t has exactly `shape` (and dtype / element size):
+    the C side trusts these sizes, so a mismatched plane would be read or
+    written out of bounds on the device."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if elem is not None and t.element_size() != elem:
+        raise ValueError(f"{name} must have {elem}-byte elements")
+
+
+def _rows(t, n, min_width, name, dtype=None):
+    """2-D tensor with n rows of at least min_width elements, contiguous rows."""
+    if t is None or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    if t.shape[0] != n or t.shape[1] < min_width:
+        raise ValueError(f"{name} must be [{n}][>= {min_width}], got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _vec(t, n, name):
+    """n half values (any 2-byte dtype), contiguous."""
+    if t is None or t.numel() != n or t.element_size() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must hold {n} contiguous 2-byte values")
+
+
+def _qjl_rows(codec, n, qjl_S, qjl_bits, qjl_gamma, names=("qjl_S", "qjl_bits", "qjl_gamma")):
+    """QJL planes of n rows for a QJL codec: S [m][d] float32, bits [n][m/8]
+    uint8 contiguous, gamma [n] halves."""
+    m = codec.qjl_m
+    if not m:
+        return
+    _shape(qjl_S, (m, codec.d), names[0], torch.float32)
+    if qjl_bits is None or qjl_bits.numel() != n * (m // 8) or qjl_bits.dtype != torch.uint8 \
+            or not qjl_bits.is_contiguous() or qjl_bits.shape[-1] != m // 8:
+        raise ValueError(f"{names[1]} must be contiguous uint8 [{n}][{m // 8}]")
+    _vec(qjl_gamma, n, names[2])
+
+
 _raw_stream = torch._C._cuda_getCurrentRawStream
 
 
@@ -149,6 +194,10 @@ def tq_encode(codec: tq_codec, x: torch.Tensor, codes: torch.Tensor, norms: torc
     if x.dim() != 2 or x.stride(1) != 1 or codes.dim() != 2 or codes.stride(1) != 1:
         raise ValueError("x and codes must be 2-D with contiguous rows")
     n = x.shape[0]
+    _rows(x, n, codec.d, "x")
+    _rows(codes, n, codec.code_bytes, "codes", torch.uint8)
+    _vec(norms, n, "norms")
+    _qjl_rows(codec, n, qjl_S, qjl_bits, qjl_gamma)
     _check(_lib.tq_encode(ctypes.byref(codec), _ptr(x), _DTYPES[x.dtype], n, x.stride(0), _ptr(codes),
                           codes.stride(0), _ptr(norms), _ptr(qjl_S), _ptr(qjl_bits), _ptr(qjl_gamma),
                           _stream(stream, x)), "tq_encode")
@@ -165,6 +214,13 @@ def tq_encode_kv(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, k
             raise ValueError("k, v and the code planes must be 2-D with contiguous rows")
     if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
         raise ValueError("k and v must share shape, strides and dtype")
+    n = k.shape[0]
+    _rows(k, n, kc.d, "k")
+    _rows(k_codes, n, kc.code_bytes, "k_codes", torch.uint8)
+    _rows(v_codes, n, vc.code_bytes, "v_codes", torch.uint8)
+    _vec(k_norms, n, "k_norms")
+    _vec(v_norms, n, "v_norms")
+    _qjl_rows(kc, n, qjl_S, k_qjl_bits, k_qjl_gamma, ("qjl_S", "k_qjl_bits", "k_qjl_gamma"))
     _check(_lib.tq_encode_kv(ctypes.byref(kc), ctypes.byref(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], k.shape[0],
                              k.stride(0), _ptr(k_codes), k_codes.stride(0), _ptr(k_norms), _ptr(v_codes),
                              v_codes.stride(0), _ptr(v_norms), _ptr(qjl_S), _ptr(k_qjl_bits), _ptr(k_qjl_gamma),
@@ -186,6 +242,15 @@ def tq_prefill(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, t0:
     if k_codes.dim() != 3 or k_codes.shape[0] != k.shape[0] or v_codes.shape[:2] != k_codes.shape[:2]:
         raise ValueError("cache planes must be [H][cap][row] matching k")
     H, T = k.shape[0], k.shape[1]
+    cap = k_codes.shape[1]
+    _shape(k, (H, T, kc.d), "k")
+    _shape(k_codes, (H, cap, kc.code_bytes), "k_codes", torch.uint8)
+    _shape(v_codes, (H, cap, vc.code_bytes), "v_codes", torch.uint8)
+    _shape(k_norms, (H, cap), "k_norms", elem=2)
+    _shape(v_norms, (H, cap), "v_norms", elem=2)
+    if kc.qjl_m:
+        _qjl_rows(kc, H * cap, qjl_S, k_qjl_bits, k_qjl_gamma, ("qjl_S", "k_qjl_bits", "k_qjl_gamma"))
+        _shape(k_qjl_bits, (H, cap, kc.qjl_m // 8), "k_qjl_bits", torch.uint8)
     _check(_lib.tq_prefill(ctypes.byref(kc), ctypes.byref(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], H, T, t0,
                            k_codes.shape[1], _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), _ptr(qjl_S),
                            _ptr(k_qjl_bits), _ptr(k_qjl_gamma), _stream(stream, k)), "tq_prefill")
@@ -206,6 +271,16 @@ def tq_append(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, pos:
     if k_codes.dim() != 4 or k_codes.shape[:2] != k.shape[:2] or v_codes.shape[:3] != k_codes.shape[:3]:
         raise ValueError("cache planes must be [B][H][cap][row] matching k")
     B, H = k.shape[0], k.shape[1]
+    cap = k_codes.shape[2]
+    _shape(k, (B, H, kc.d), "k")
+    _shape(pos, (B,), "pos", torch.int32)
+    _shape(k_codes, (B, H, cap, kc.code_bytes), "k_codes", torch.uint8)
+    _shape(v_codes, (B, H, cap, vc.code_bytes), "v_codes", torch.uint8)
+    _shape(k_norms, (B, H, cap), "k_norms", elem=2)
+    _shape(v_norms, (B, H, cap), "v_norms", elem=2)
+    if kc.qjl_m:
+        _qjl_rows(kc, B * H * cap, qjl_S, k_qjl_bits, k_qjl_gamma, ("qjl_S", "k_qjl_bits", "k_qjl_gamma"))
+        _shape(k_qjl_bits, (B, H, cap, kc.qjl_m // 8), "k_qjl_bits", torch.uint8)
     _check(_lib.tq_append(ctypes.byref(kc), ctypes.byref(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], B, H, _ptr(pos),
                           k_codes.shape[2], _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), _ptr(qjl_S),
                           _ptr(k_qjl_bits), _ptr(k_qjl_gamma), _stream(stream, k)), "tq_append")
@@ -214,6 +289,12 @@ def tq_append(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, pos:
 def tq_decode(codec: tq_codec, codes: torch.Tensor, norms: torch.Tensor, x_hat: torch.Tensor, stream=None) -> None:
     if codes.dim() != 2 or codes.stride(1) != 1:
         raise ValueError("codes must be 2-D with contiguous rows")
+    n = codes.shape[0]
+    _rows(codes, n, codec.code_bytes, "codes", torch.uint8)
+    _vec(norms, n, "norms")
+    _shape(x_hat, (n, codec.d), "x_hat", torch.float32)
+    if not x_hat.is_contiguous():
+        raise ValueError("x_hat must be contiguous")
     _check(_lib.tq_decode(ctypes.byref(codec), _ptr(codes), codes.stride(0), _ptr(norms), codes.shape[0],
                           _ptr(x_hat), _stream(stream, codes)), "tq_decode")
 
@@ -223,13 +304,34 @@ def tq_attn_workspace_bytes(kc: tq_codec, vc: tq_codec, batch: int, n_q_heads: i
     return _lib.tq_attn_workspace_bytes(ctypes.byref(kc), ctypes.byref(vc), batch, n_q_heads, n_kv_heads, ctx_cap)
 
 
-def _attn(name, kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, scale, out, workspace,
-          k_qjl, k_gamma, qjl_S, stream):
+def _check_cache(kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, out, k_qjl, k_gamma, qjl_S):
+    """Shapes of a decode-attention call: q [B][Hq][d], ctx_len [B] int32,
+    planes [B][Hkv][cap][row] with rows of exactly d*bits/8 bytes, norms
+    [B][Hkv][cap], out [B][Hq][d] float32, QJL planes for a QJL key codec."""
+    if q.dim() != 3 or k_codes.dim() != 4:
+        raise ValueError("q must be [B][Hq][d] and k_codes [B][Hkv][cap][row]")
     B, Hq, _ = q.shape
     Hkv, cap = k_codes.shape[1], k_codes.shape[2]
     for t in (q, k_codes, k_norms, v_codes, v_norms, out, ctx_len):
         if not t.is_contiguous():
             raise ValueError("attention tensors must be contiguous")
+    _shape(q, (B, Hq, kc.d), "q")
+    _shape(ctx_len, (B,), "ctx_len", torch.int32)
+    _shape(k_codes, (B, Hkv, cap, kc.code_bytes), "k_codes", torch.uint8)
+    _shape(v_codes, (B, Hkv, cap, vc.code_bytes), "v_codes", torch.uint8)
+    _shape(k_norms, (B, Hkv, cap), "k_norms", elem=2)
+    _shape(v_norms, (B, Hkv, cap), "v_norms", elem=2)
+    _shape(out, (B, Hq, vc.d), "out", torch.float32)
+    if kc.qjl_m:
+        _qjl_rows(kc, B * Hkv * cap, qjl_S, k_qjl, k_gamma, ("qjl_S", "k_qjl", "k_gamma"))
+        _shape(k_qjl, (B, Hkv, cap, kc.qjl_m // 8), "k_qjl", torch.uint8)
+    return B, Hq, Hkv, cap
+
+
+def _attn(name, kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, scale, out, workspace,
+          k_qjl, k_gamma, qjl_S, stream):
+    B, Hq, Hkv, cap = _check_cache(kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, out, k_qjl, k_gamma,
+                                   qjl_S)
     fn = getattr(_lib, name)
     _check(fn(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _DTYPES[q.dtype], B, Hq, Hkv,
               _ptr(ctx_len), cap, _ptr(k_codes), _ptr(k_norms), _ptr(k_qjl), _ptr(k_gamma),
@@ -255,13 +357,15 @@ def tq_attn_decode_rw(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torc
                       qjl_S: torch.Tensor | None = None, stream=None) -> None:
     """tq_attn_decode plus a residual window: k_win, v_win [B][Hkv][win_cap][d]
     (fp32/fp16/bf16, contiguous) holding win_len[b] exact recent tokens."""
-    B, Hq, _ = q.shape
-    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
-    for t in (q, k_codes, k_norms, v_codes, v_norms, out, ctx_len, k_win, v_win, win_len):
+    B, Hq, Hkv, cap = _check_cache(kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, out, k_qjl, k_gamma,
+                                   qjl_S)
+    for t in (k_win, v_win, win_len):
         if not t.is_contiguous():
             raise ValueError("attention tensors must be contiguous")
     if k_win.dim() != 4 or k_win.shape != v_win.shape or k_win.dtype != v_win.dtype:
         raise ValueError("k_win and v_win must be [B][Hkv][win_cap][d] of one dtype")
+    _shape(k_win, (B, Hkv, k_win.shape[2], kc.d), "k_win")
+    _shape(win_len, (B,), "win_len", torch.int32)
     _check(_lib.tq_attn_decode_rw(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _DTYPES[q.dtype], B, Hq, Hkv,
                                   _ptr(ctx_len), cap, _ptr(k_codes), _ptr(k_norms), _ptr(k_qjl), _ptr(k_gamma),
                                   _ptr(qjl_S), _ptr(v_codes), _ptr(v_norms), _ptr(k_win), _ptr(v_win),
@@ -295,12 +399,27 @@ def tq_search_workspace_bytes(codec: tq_codec, n_q: int, n_db: int, k: int) -> i
     return _lib.tq_search_workspace_bytes(ctypes.byref(codec), n_q, n_db, k)
 
 
+def tq_workspace_bytes(op: int, kc: tq_codec, vc: tq_codec | None = None, batch: int = 0, n_q_heads: int = 0,
+                       n_kv_heads: int = 0, ctx_cap: int = 0, n_q: int = 0, n_db: int = 0, k: int = 0) -> int:
+    """Workspace bytes of operation `op` (TQ_OP_*); 0 on bad arguments."""
+    return _lib.tq_workspace_bytes(op, ctypes.byref(kc), ctypes.byref(vc) if vc is not None else None, batch,
+                                   n_q_heads, n_kv_heads, ctx_cap, n_q, n_db, k)
+
+
 def tq_ip_search(codec: tq_codec, q: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor,
                  qjl_bits: torch.Tensor | None, qjl_gamma: torch.Tensor | None, qjl_S: torch.Tensor | None,
                  k: int, out_scores: torch.Tensor, out_ids: torch.Tensor, workspace: torch.Tensor,
                  stream=None) -> None:
     n_q = q.shape[0]
     n_db = codes.shape[0]
+    _shape(q, (n_q, codec.d), "q", torch.float32)
+    if not q.is_contiguous() or not codes.is_contiguous():
+        raise ValueError("q and codes must be contiguous")
+    _shape(codes, (n_db, codec.code_bytes), "codes", torch.uint8)
+    _vec(norms, n_db, "norms")
+    _qjl_rows(codec, n_db, qjl_S, qjl_bits, qjl_gamma)
+    _shape(out_scores, (n_q, k), "out_scores", torch.float32)
+    _shape(out_ids, (n_q, k), "out_ids", torch.int64)
     _check(_lib.tq_ip_search(ctypes.byref(codec), _ptr(q), n_q, _ptr(codes), _ptr(norms), _ptr(qjl_bits),
                              _ptr(qjl_gamma), _ptr(qjl_S), n_db, k, _ptr(out_scores), _ptr(out_ids),
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q)),

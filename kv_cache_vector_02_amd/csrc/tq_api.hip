@@ -395,7 +395,7 @@ static int search_check(const tq_codec* c, int n_q, int64_t n_db, int k) {
     if (!c) return TQ_EINVAL;
     if (!valid_codec(c)) return TQ_EUNSUPPORTED;
     if (c->d != 128 && c->d != 256) return TQ_EUNSUPPORTED;
-    if (k < 1 || k > 32) return TQ_EUNSUPPORTED;
+    if (k < 1 || k > 64) return TQ_EUNSUPPORTED;
     if (n_q <= 0 || n_db < 0 || n_q > 65535 * 32) return TQ_EINVAL;  // 32 queries per block row of the grid
     if (n_db > ((int64_t)1 << 31) - 1) return TQ_EUNSUPPORTED;
     return TQ_OK;
@@ -407,6 +407,16 @@ size_t tq_search_workspace_bytes(const tq_codec* c, int n_q, int64_t n_db, int k
     int64_t rows;
     tqi::search_plan(n_q, n_db, k, &nb, &rows);
     return tqi::search_workspace(n_q, c->d, c->qjl_m, k, nb);
+}
+
+size_t tq_workspace_bytes(int op, const tq_codec* kc, const tq_codec* vc, int batch, int n_q_heads, int n_kv_heads,
+                          int64_t ctx_cap, int n_q, int64_t n_db, int k) {
+    switch (op) {
+        case TQ_OP_ATTN_DECODE:
+        case TQ_OP_ATTN_DECODE_RW: return tq_attn_workspace_bytes(kc, vc, batch, n_q_heads, n_kv_heads, ctx_cap);
+        case TQ_OP_IP_SEARCH: return tq_search_workspace_bytes(kc, n_q, n_db, k);
+        default: return 0;
+    }
 }
 
 int tq_ip_search(const tq_codec* c, const float* q, int n_q, const uint8_t* codes, const uint16_t* norms,

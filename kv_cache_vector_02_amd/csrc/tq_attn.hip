@@ -4,6 +4,8 @@
 // which also combines).
 #include <hip/hip_runtime.h>
 
+#include <stdlib.h>
+
 #include <atomic>
 
 #include "tq_attn_kernels.h"
@@ -88,6 +90,19 @@ void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int d, int kb, int vb
             best_cost = cost;
             best_sp = sp;
             best_per = per;
+        }
+    }
+    // A positive TQ_ATTN_SPLITS in the environment replaces the chosen split
+    // count (clamped to [1, 64-token tiles of the capacity]); tests use it to
+    // check that the result does not depend on the split.  Read per call, so
+    // the workspace query and the call that follows agree.
+    if (const char* env = getenv("TQ_ATTN_SPLITS")) {
+        const long want = strtol(env, nullptr, 10);
+        if (want > 0 && ctx_cap > 0) {
+            int64_t sp = want < max_splits ? (int64_t)want : max_splits;
+            int64_t per = ((ctx_cap + sp - 1) / sp + 63) & ~(int64_t)63;
+            best_per = per;
+            best_sp = (ctx_cap + per - 1) / per;
         }
     }
     *splits = (int)best_sp;

@@ -23,7 +23,7 @@ namespace {
 
 using namespace tqd;
 
-constexpr int KMAX = 32;   // largest k
+constexpr int KMAX = 64;   // largest k (per-block lists hold 32 or 64 entries)
 
 template <int D>
 __global__ __launch_bounds__(64) void search_qprep_kernel(SearchArgs a) {
@@ -115,7 +115,7 @@ __device__ __forceinline__ float wmax64(float v) {
     return fmaxf(v, xor_lane<32>(v));
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int KM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void search_mfma_kernel(SearchArgs a) {
     constexpr int RB = D * BITS / 8;   // code bytes per row
     constexpr int RW = RB / 4;         // ... dwords
@@ -137,8 +137,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     __shared__ __attribute__((aligned(16))) uint32_t rbits[MT * 8];
     __shared__ float rn[MT], rg[MT];
     __shared__ float es[MQ][MT + 1];
-    __shared__ float lst_s[MQ][KMAX];
-    __shared__ int32_t lst_i[MQ][KMAX];
+    __shared__ float lst_s[MQ][KM];
+    __shared__ int32_t lst_i[MQ][KM];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, grp = lane >> 4;
@@ -159,9 +159,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
         sgn[i] = make_uint2(pack_h2(sg(0), sg(1)), pack_h2(sg(2), sg(3)));
     }
     const int tsl = lane % TS, ssl = lane & 31;  // this lane's table copies
-    for (int e = tid; e < MQ * KMAX; e += 256) {
-        lst_s[e / KMAX][e % KMAX] = -INFINITY;
-        lst_i[e / KMAX][e % KMAX] = -1;
+    for (int e = tid; e < MQ * KM; e += 256) {
+        lst_s[e / KM][e % KM] = -INFINITY;
+        lst_i[e / KM][e % KM] = -1;
     }
 
     // this wave's query operands: column n <-> query q0 + 8 wave + (n & 7), hi (n < 8) or lo
@@ -367,16 +367,22 @@ __global__ __launch_bounds__(256) void search_merge_kernel(SearchArgs a) {
     }
 }
 
-template <int D>
-hipError_t launch_scan_b(const SearchArgs& a, hipStream_t s) {
+template <int D, int KM>
+hipError_t launch_scan_k(const SearchArgs& a, hipStream_t s) {
     const dim3 grid(a.n_blocks, (a.n_q + MQ - 1) / MQ);
     switch (a.c.bits) {
-        case 1: hipLaunchKernelGGL((search_mfma_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((search_mfma_kernel<D, 2>), grid, dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((search_mfma_kernel<D, 3>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((search_mfma_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((search_mfma_kernel<D, 1, KM>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((search_mfma_kernel<D, 2, KM>), grid, dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((search_mfma_kernel<D, 3, KM>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((search_mfma_kernel<D, 4, KM>), grid, dim3(256), 0, s, a); break;
     }
     return hipGetLastError();
+}
+
+// per-block lists of 32 entries for k <= 32 (less LDS per block), else 64
+template <int D>
+hipError_t launch_scan_b(const SearchArgs& a, hipStream_t s) {
+    return a.k <= 32 ? launch_scan_k<D, 32>(a, s) : launch_scan_k<D, KMAX>(a, s);
 }
 
 }  // namespace

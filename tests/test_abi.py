@@ -188,14 +188,123 @@ def test_search_argument_errors():
     P = FAKE
     ws = tq.tq_search_workspace_bytes(c, 16, 1000, 10)
     assert ws > 0
-    assert tq.tq_search_workspace_bytes(c, 16, 1000, 33) == 0
+    assert tq.tq_search_workspace_bytes(c, 16, 1000, 64) > 0
+    assert tq.tq_search_workspace_bytes(c, 16, 1000, 65) == 0
     assert tq.tq_search_workspace_bytes(tq.tq_codebook(3, 64, 0), 16, 1000, 10) == 0
 
     def call(k=10, wsb=ws, S=P, nq=16):
         return tq.raw_call("tq_ip_search", ctypes.byref(c), P, nq, P, P, P, P, S, 1000, k, P, P, P, wsb, None)
 
     assert call(k=0) == tq.TQ_EUNSUPPORTED
-    assert call(k=33) == tq.TQ_EUNSUPPORTED
+    assert call(k=65) == tq.TQ_EUNSUPPORTED
     assert call(wsb=ws - 16) == tq.TQ_EWORKSPACE
     assert call(S=None) == tq.TQ_EINVAL
     assert call(nq=0) == tq.TQ_EINVAL
+
+
+def test_workspace_bytes_by_operation():
+    """tq_workspace_bytes(op, ...) through ctypes equals the per-operation sizes."""
+    kc, vc = tq.tq_codebook(4, 128, 0), tq.tq_codebook(2, 128, 0)
+    sc = tq.tq_codebook(3, 256, 0, 256)
+    ws = lambda *a: tq.raw_call("tq_workspace_bytes", *a)  # noqa: E731
+    att = tq.tq_attn_workspace_bytes(kc, vc, 16, 28, 4, 32768)
+    assert att > 0
+    for op in (tq.TQ_OP_ATTN_DECODE, tq.TQ_OP_ATTN_DECODE_RW):
+        assert ws(op, ctypes.byref(kc), ctypes.byref(vc), 16, 28, 4, 32768, 0, 0, 0) == att
+    srch = tq.tq_search_workspace_bytes(sc, 1024, 1 << 20, 10)
+    assert srch > 0
+    assert ws(tq.TQ_OP_IP_SEARCH, ctypes.byref(sc), None, 0, 0, 0, 0, 1024, 1 << 20, 10) == srch
+    assert ws(99, ctypes.byref(kc), ctypes.byref(vc), 16, 28, 4, 32768, 0, 0, 0) == 0
+    assert ws(tq.TQ_OP_ATTN_DECODE, None, ctypes.byref(vc), 16, 28, 4, 32768, 0, 0, 0) == 0
+    assert tq.tq_workspace_bytes(tq.TQ_OP_ATTN_DECODE, kc, vc, 16, 28, 4, 32768) == att
+
+
+def test_split_override_sizes_the_workspace(monkeypatch):
+    """TQ_ATTN_SPLITS replaces the planned split count; the workspace follows it
+    (partials are [B*Hq][splits][d+2] floats, QJL-free keys need no projections)."""
+    kc, vc = tq.tq_codebook(4, 128, 0), tq.tq_codebook(2, 128, 0)
+    B, Hq, Hkv, cap, d = 2, 14, 2, 1000, 128
+    align = lambda n: (n + 63) // 64 * 64  # noqa: E731
+    for splits, want in ((1, 1), (3, 3), (16, 16), (1000, 16)):  # 16 = 64-token tiles of 1000
+        monkeypatch.setenv("TQ_ATTN_SPLITS", str(splits))
+        assert tq.tq_attn_workspace_bytes(kc, vc, B, Hq, Hkv, cap) == 4 * align(B * Hq * want * (d + 2))
+    monkeypatch.setenv("TQ_ATTN_SPLITS", "7")
+    per = (-(-cap // 7) + 63) // 64 * 64  # 192 tokens per split -> 6 splits
+    assert tq.tq_attn_workspace_bytes(kc, vc, B, Hq, Hkv, cap) == 4 * align(B * Hq * (-(-cap // per)) * (d + 2))
+
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.uint8)
+
+
+def test_binding_rejects_mismatched_planes():
+    """The binding checks every plane's shape before anything reaches the C side
+    (which trusts rows of exactly d*bits/8 bytes): wrong shapes raise ValueError
+    naming the plane, on CPU tensors, before any device pointer is taken."""
+    import torch
+
+    kc, vc = tq.tq_codebook(4, 128, 0), tq.tq_codebook(2, 128, 0)
+    B, Hq, Hkv, cap, d = 2, 14, 2, 64, 128
+    good = dict(q=_cpu(B, Hq, d, dtype=torch.float16), ctx=_cpu(B, dtype=torch.int32),
+                kcodes=_cpu(B, Hkv, cap, 64), knorms=_cpu(B, Hkv, cap, dtype=torch.float16),
+                vcodes=_cpu(B, Hkv, cap, 32), vnorms=_cpu(B, Hkv, cap, dtype=torch.float16),
+                out=_cpu(B, Hq, d, dtype=torch.float32), ws=_cpu(1 << 20))
+
+    def attn(**over):
+        a = dict(good, **over)
+        tq.tq_attn_decode(kc, vc, a["q"], a["ctx"], a["kcodes"], a["knorms"], a["vcodes"], a["vnorms"], 0.1,
+                          a["out"], a["ws"])
+
+    for over, name in ((dict(vcodes=_cpu(B, Hkv, cap, 64)), "v_codes"),  # a 4-bit plane with a 2-bit codec
+                       (dict(kcodes=_cpu(B, Hkv, cap, 48)), "k_codes"),
+                       (dict(q=_cpu(B, Hq, 64, dtype=torch.float16)), "q"),
+                       (dict(knorms=_cpu(B, Hkv, cap - 1, dtype=torch.float16)), "k_norms"),
+                       (dict(out=_cpu(B, Hq, d, dtype=torch.float16)), "out"),
+                       (dict(ctx=_cpu(B + 1, dtype=torch.int32)), "ctx_len")):
+        with pytest.raises(ValueError, match=name):
+            attn(**over)
+    kq = tq.tq_codebook(4, 128, 0, 128)
+    with pytest.raises(ValueError, match="qjl_S"):  # QJL keys without their planes
+        tq.tq_attn_decode(kq, vc, good["q"], good["ctx"], good["kcodes"], good["knorms"], good["vcodes"],
+                          good["vnorms"], 0.1, good["out"], good["ws"])
+    with pytest.raises(ValueError, match="k_win"):
+        tq.tq_attn_decode_rw(kc, vc, good["q"], good["ctx"], good["kcodes"], good["knorms"], good["vcodes"],
+                             good["vnorms"], _cpu(B, Hkv, 8, 64, dtype=torch.float16),
+                             _cpu(B, Hkv, 8, 64, dtype=torch.float16), _cpu(B, dtype=torch.int32), 0.1,
+                             good["out"], good["ws"])
+    # encode / decode
+    with pytest.raises(ValueError, match="codes"):
+        tq.tq_encode(kc, _cpu(10, d, dtype=torch.float16), _cpu(10, 32), _cpu(10, dtype=torch.float16))
+    with pytest.raises(ValueError, match="x"):
+        tq.tq_encode(kc, _cpu(10, 64, dtype=torch.float16), _cpu(10, 64), _cpu(10, dtype=torch.float16))
+    with pytest.raises(ValueError, match="norms"):
+        tq.tq_encode(kc, _cpu(10, d, dtype=torch.float16), _cpu(10, 64), _cpu(9, dtype=torch.float16))
+    with pytest.raises(ValueError, match="x_hat"):
+        tq.tq_decode(kc, _cpu(10, 64), _cpu(10, dtype=torch.float16), _cpu(10, 64, dtype=torch.float32))
+    # prefill / append
+    with pytest.raises(ValueError, match="v_codes"):
+        tq.tq_prefill(kc, vc, _cpu(2, 16, d, dtype=torch.float16), _cpu(2, 16, d, dtype=torch.float16), 0,
+                      _cpu(2, 64, 64), _cpu(2, 64, dtype=torch.float16), _cpu(2, 64, 64),
+                      _cpu(2, 64, dtype=torch.float16))
+    with pytest.raises(ValueError, match="k"):
+        tq.tq_prefill(kc, vc, _cpu(2, 16, 64, dtype=torch.float16), _cpu(2, 16, 64, dtype=torch.float16), 0,
+                      _cpu(2, 64, 64), _cpu(2, 64, dtype=torch.float16), _cpu(2, 64, 32),
+                      _cpu(2, 64, dtype=torch.float16))
+    with pytest.raises(ValueError, match="pos"):
+        tq.tq_append(kc, vc, _cpu(B, Hkv, d, dtype=torch.float16), _cpu(B, Hkv, d, dtype=torch.float16),
+                     _cpu(B + 1, dtype=torch.int32), good["kcodes"], good["knorms"], good["vcodes"], good["vnorms"])
+    with pytest.raises(ValueError, match="v_norms"):
+        tq.tq_append(kc, vc, _cpu(B, Hkv, d, dtype=torch.float16), _cpu(B, Hkv, d, dtype=torch.float16),
+                     _cpu(B, dtype=torch.int32), good["kcodes"], good["knorms"], good["vcodes"],
+                     _cpu(B, Hkv, cap, dtype=torch.float32))
+    # search
+    sc = tq.tq_codebook(3, 256, 0, 256)
+    with pytest.raises(ValueError, match="qjl_bits"):
+        tq.tq_ip_search(sc, _cpu(4, 256, dtype=torch.float32), _cpu(100, 96), _cpu(100, dtype=torch.float16),
+                        _cpu(100, 16), _cpu(100, dtype=torch.float16), _cpu(256, 256, dtype=torch.float32), 10,
+                        _cpu(4, 10, dtype=torch.float32), _cpu(4, 10, dtype=torch.int64), _cpu(1 << 16))
+    with pytest.raises(ValueError, match="out_ids"):
+        tq.tq_ip_search(sc, _cpu(4, 256, dtype=torch.float32), _cpu(100, 96), _cpu(100, dtype=torch.float16),
+                        _cpu(100, 32), _cpu(100, dtype=torch.float16), _cpu(256, 256, dtype=torch.float32), 10,
+                        _cpu(4, 10, dtype=torch.float32), _cpu(4, 10, dtype=torch.int32), _cpu(1 << 16))
