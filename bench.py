@@ -17,12 +17,16 @@ long-context decode (8 kv heads x 2^20 tokens, K3/V3, 64 bf16 query heads) and
 inner-product search (2^20 x 256 database, 3-bit + QJL m=256, 1024 queries,
 top-10; useful estimator TFLOP/s, and the matrix-core work issued against the
 dense fp16 peak).  `roofline` is the scan kernel's algorithmic bytes per launch over its
-mean launch time, measured with HIP events on the launch stream around
-back-to-back scan launches; `traffic` is the HBM bytes per scan launch from the
+mean launch time, measured with HIP events recorded on the launch stream around
+the scan launch of every timed step (so the scan time is part of, and never
+longer than, the step time); `traffic` is the HBM bytes per scan launch from the
 committed FETCH_SIZE / WRITE_SIZE summary under profiles/ (null once the scan
-sources differ from the ones measured).
-`cpu_baseline` is the CPU oracle timed on a bounded sample of the same decode
-workload.  Inputs are synthetic and seeded (synth.py).
+sources differ from the ones measured).  `read_ceiling` is the library's
+read-only streaming kernel (tq_stream_read: 16-byte loads over 1 GiB, beyond
+the 256 MB Infinity Cache) timed the same way.
+`cpu_baseline` is the CPU oracle timed on bounded samples of the workloads
+(decode, encode, tiny, search, long context).  Inputs are synthetic and seeded
+(synth.py).
 
 The default warmup (2000 untimed steps, about 0.15 s of back-to-back decode) lets
 the GPU reach its sustained clock: a decode loop run straight from idle is
@@ -47,6 +51,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_scan_traffic_b16_h28x4_ctx32
 SCAN_SOURCES = ("kv_cache_vector_02_amd/csrc/tq_attn_kernels.h", "kv_cache_vector_02_amd/csrc/tq_attn.hip",
                 "kv_cache_vector_02_amd/csrc/tq_device.h", "kv_cache_vector_02_amd/csrc/tq_internal.h")
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores, published
+PROBE_EVERY = 8                 # timed steps between two carrying kernel-timing events
 
 METRIC = "packed-KV decode attn GB/s & % HBM peak (1 GPU); tq_encode Mvectors/s"
 
@@ -101,35 +106,43 @@ def stored_traffic():
             "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
 
 
-def timed_loop(fn, steps, warmup, torch):
-    """Runs fn(i) for warmup + steps iterations; returns ms per timed step."""
+def timed_loop(fn, steps, warmup, torch, probe=False):
+    """Runs fn(i, ev) for warmup + steps iterations; returns ms per timed step.
+
+    With probe=True every PROBE_EVERY-th timed step (from the first) gets a
+    pair of timing events `ev` that fn records around the kernel it wants timed
+    (on the launch stream, which is torch's current stream); the mean probed
+    duration is returned as well.  Event markers between the launches of every
+    step would add about 8 us per 55 us decode step on MI355X, so only a sample
+    of the steps carries them."""
     for i in range(warmup):
-        fn(i)
+        fn(i, None)
     torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           if probe and i % PROBE_EVERY == 0 else None for i in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(steps):
-        fn(warmup + i)
+        fn(warmup + i, evs[i])
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    ms = t0.elapsed_time(t1) / steps
+    if not probe:
+        return ms
+    probed = [a.elapsed_time(b) for a, b in (e for e in evs if e is not None)]
+    return ms, sum(probed) / len(probed)
 
 
-def scan_launch_ms(tq, torch, args_of, launches):
-    """Mean duration of one tq_attn_scan launch: HIP events on the launch stream
-    around `launches` back-to-back scans (query prep done once before; the scan
-    is idempotent), so launch gaps overlap the previous kernel."""
-    tq.tq_attn_prepare(*args_of(0))
-    tq.tq_attn_scan(*args_of(0))
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(launches):
-        tq.tq_attn_scan(*args_of(i))
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / launches
+def attn_step(tq, args, ev):
+    """One decode step as its three launches; the scan between the events."""
+    tq.tq_attn_prepare(*args)
+    if ev is not None:
+        ev[0].record()
+    tq.tq_attn_scan(*args)
+    if ev is not None:
+        ev[1].record()
+    tq.tq_attn_combine(*args)
 
 
 # ------------------------------------------------------------------ decode ----
@@ -159,14 +172,7 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
         c = caches[i % replicas]
         return (kc, vc, q, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], scale, out, ws)
 
-    def step(i):
-        args = args_of(i)
-        tq.tq_attn_prepare(*args)
-        tq.tq_attn_scan(*args)
-        tq.tq_attn_combine(*args)
-
-    ms = timed_loop(step, steps, warmup, torch)
-    scan_ms = scan_launch_ms(tq, torch, args_of, steps)
+    ms, scan_ms = timed_loop(lambda i, ev: attn_step(tq, args_of(i), ev), steps, warmup, torch, probe=True)
 
     # the same step with a residual window of 128 exact fp16 tokens per
     # sequence (the pages' rw = 128) joining the softmax: tq_attn_decode_rw
@@ -175,7 +181,7 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
     wins = [(k.view(B, Hkv, rw, d).contiguous(), v.view(B, Hkv, rw, d).contiguous()) for k, v in wins]
     win_len = torch.full((B,), rw, dtype=torch.int32, device="cuda")
 
-    def step_rw(i):
+    def step_rw(i, ev=None):
         c, (kw, vw) = caches[i % replicas], wins[i % replicas]
         tq.tq_attn_decode_rw(kc, vc, q, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"],
                              kw, vw, win_len, scale, out, ws)
@@ -190,11 +196,11 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
     k_new, v_new = synth.kv_block(B * Hkv, 1, d, 9100, device="cuda", dtype=torch.float16)
     k_new, v_new = k_new.view(B, Hkv, d).contiguous(), v_new.view(B, Hkv, d).contiguous()
 
-    def append(i):
+    def append(i, ev=None):
         c = caches[i % replicas]
         tq.tq_append(kc, vc, k_new, v_new, pos, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"])
 
-    def append_attend(i):
+    def append_attend(i, ev=None):
         append(i)
         tq.tq_attn_decode(*args_of(i))
 
@@ -249,14 +255,14 @@ def encode_leg(tq, torch, synth, steps, warmup):
     nk = torch.empty(layers, n, dtype=torch.float16, device="cuda")
     nv = torch.empty(layers, n, dtype=torch.float16, device="cuda")
 
-    def step(i):
+    def step(i, ev=None):
         li = i % layers
         tq.tq_encode(kc, pool_k[li], out_k[li], nk[li])
         tq.tq_encode(vc, pool_v[li], out_v[li], nv[li])
 
     ms = timed_loop(step, max(steps, 512), warmup, torch)
 
-    def step_kv(i):  # the same K and V through tq_encode_kv (one launch)
+    def step_kv(i, ev=None):  # the same K and V through tq_encode_kv (one launch)
         li = i % layers
         tq.tq_encode_kv(kc, vc, pool_k[li], pool_v[li], out_k[li], nk[li], out_v[li], nv[li])
 
@@ -318,14 +324,7 @@ def long_leg(tq, torch, synth, steps, warmup):
     def args_of(i):
         return (kc, vc, q, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], scale, out, ws)
 
-    def step(i):
-        args = args_of(i)
-        tq.tq_attn_prepare(*args)
-        tq.tq_attn_scan(*args)
-        tq.tq_attn_combine(*args)
-
-    ms = timed_loop(step, steps, warmup, torch)
-    scan_ms = scan_launch_ms(tq, torch, args_of, steps)
+    ms, scan_ms = timed_loop(lambda i, ev: attn_step(tq, args_of(i), ev), steps, warmup, torch, probe=True)
     cache_bytes = Hkv * cap * ((kc.code_bytes + 2) + (vc.code_bytes + 2))
     return {
         "workload": "1 sequence, 8 kv heads x 2^20 tokens, d=128, K3/V3, 64 bf16 query heads (8:1)",
@@ -360,7 +359,7 @@ def search_leg(tq, torch, synth, steps, warmup):
     scores = torch.empty(n_q, k, device="cuda")
     ids = torch.empty(n_q, k, dtype=torch.int64, device="cuda")
 
-    def step(i):
+    def step(i, ev=None):
         tq.tq_ip_search(codec, q, codes, norms, bits, gamma, S, k, scores, ids, ws)
 
     st = max(2, min(steps, 5))
@@ -444,31 +443,57 @@ def quality_leg(tq, torch, synth):
 
 
 # -------------------------------------------------------------- CPU oracle ----
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(torch, synth, target_s):
-    """The oracle, untouched, on a bounded sample of the decode workload: the
-    K4/V2 caches of sample (batch, kv head) units are encoded by the oracle
-    (timed as the encode baseline), then the oracle's decompress-then-attend
-    runs for the 7 query heads of each unit, repeated until target_s elapsed."""
+    """The oracle, untouched, on bounded samples of the workloads, on this
+    host's cores (numpy's BLAS threads; single-thread runs under a thread limit):
+
+    * decode (the headline unit, GB/s of packed cache): 4 (batch, kv head)
+      units of the decode workload, oracle-encoded, then decompress-then-attend
+      for the 7 query heads of each unit, repeated until target_s elapsed;
+    * encode: the whole 4 heads x 8192 tokens fp16 K4 + V2 step (65,536
+      vectors), all threads and one thread;
+    * tiny: the 512-key workload (3-bit K with and without QJL m=128, 3-bit V,
+      8 queries), one thread;
+    * search: 64 of the 1024 queries over 2^16 of the 2^20 database rows
+      (3-bit + QJL m=256, d=256, top-10), extrapolated linearly in queries x rows
+      to the full call and labelled so;
+    * long context: one kv head x 2^15 tokens of the K3/V3 cache with its 8
+      query heads, GB/s of packed cache."""
     import numpy as np
     from oracle import tq_oracle as o
 
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        threads = 1
+        threads, threadpool_limits = 1, None
+
+    def one_thread():
+        return threadpool_limits(limits=1) if threadpool_limits else _Null()
+
+    def f64(t):
+        return t.float().numpy().astype(np.float64)
+
     d, ctx, g = 128, 32768, 7
+    # decode sample
     kc, vc = o.Codec(4, d, 42), o.Codec(2, d, 42)
     units = [(0, 0), (5, 1), (10, 2), (15, 3)]
-    t0 = time.perf_counter()
     caches = []
     for b, kh in units:
         k, v = synth.kv_block(4, ctx, d, synth.SEED_DECODE_BASE + b, dtype=torch.float16)
-        ek = o.encode(k[kh].float().numpy().astype(np.float64), kc)
-        ev = o.encode(v[kh].float().numpy().astype(np.float64), vc)
-        caches.append((ek, ev))
-    enc_s = time.perf_counter() - t0
-    q = synth.decode_queries(16, 28, d).float().numpy().astype(np.float64)
+        caches.append((o.encode(f64(k[kh]), kc), o.encode(f64(v[kh]), vc)))
+    q = f64(synth.decode_queries(16, 28, d))
     done, t1 = 0, time.perf_counter()
     while True:
         for (b, kh), (ek, ev) in zip(units, caches):
@@ -478,49 +503,122 @@ def cpu_baseline(torch, synth, target_s):
         if time.perf_counter() - t1 >= target_s:
             break
     att_s = time.perf_counter() - t1
-    bytes_done = done * ctx * 100
+    del caches
+
+    # encode: the whole 4 x 8192 fp16 K4 + V2 step, all threads and one thread
+    k, v = synth.kv_block(4, 8192, d, synth.SEED_ENCODE, dtype=torch.float16)
+    k, v = f64(k).reshape(-1, d), f64(v).reshape(-1, d)
+    ek4, ev2 = o.Codec(4, d, 11), o.Codec(2, d, 11)
+
+    def enc_step():
+        t = time.perf_counter()
+        o.encode(k, ek4)
+        o.encode(v, ev2)
+        return time.perf_counter() - t
+
+    enc_s = enc_step()
+    with one_thread():
+        enc_1t_s = enc_step()
+    n_enc = 2 * k.shape[0]
+
+    # tiny workload, one thread
+    kt, vt, qt, St = (x.numpy().astype(np.float64) for x in synth.tiny())
+    with one_thread():
+        t = time.perf_counter()
+        c3, cq, cv = o.Codec(3, d, 0), o.Codec(3, d, 0, 128), o.Codec(3, d, 0)
+        e_k, e_kq, e_v = o.encode(kt, c3), o.encode(kt, cq, St), o.encode(vt, cv)
+        o.attention(qt, e_k["codes"], e_k["norms"], e_v["codes"], e_v["norms"], c3, cv, 1 / math.sqrt(d))
+        o.attention(qt, e_kq["codes"], e_kq["norms"], e_v["codes"], e_v["norms"], cq, cv, 1 / math.sqrt(d),
+                    k_qjl=e_kq["qjl"], k_gamma=e_kq["gamma"], S=St)
+        tiny_s = time.perf_counter() - t
+
+    # search sample: 64 queries x 2^16 rows, extrapolated
+    n_rows, n_qs = 1 << 16, 64
+    db, qs, S = synth.search_inputs(1 << 20, 1024, 256, 256)
+    db, qs, S = db[:n_rows].numpy().astype(np.float64), qs[:n_qs].numpy().astype(np.float64), S.numpy()
+    sc = o.Codec(3, 256, 99, 256)
+    t = time.perf_counter()
+    es = o.encode(db, sc, S)
+    s_enc = time.perf_counter() - t
+    t = time.perf_counter()
+    o.ip_search(qs, es["codes"], es["norms"], es["qjl"], es["gamma"], S, sc, 10)
+    s_search = time.perf_counter() - t
+    del db, es
+    full = s_search * (1024 / n_qs) * ((1 << 20) / n_rows)
+
+    # long-context sample: one kv head x 2^15 tokens, 8 query heads
+    lt = 1 << 15
+    lk, lv = synth.long_chunk(0, kv_heads=1, tokens=lt, d=d)
+    lq = f64(synth.long_queries(8, d))
+    l3 = o.Codec(3, d, 77)
+    elk, elv = o.encode(f64(lk[0]), l3), o.encode(f64(lv[0]), l3)
+    t = time.perf_counter()
+    o.attention(lq, elk["codes"], elk["norms"], elv["codes"], elv["norms"], l3, l3, 1 / math.sqrt(d))
+    long_s = time.perf_counter() - t
+
     return {
-        "value": bytes_done / att_s / 1e9,
+        "value": done * ctx * 100 / att_s / 1e9,
         "unit": "GB/s",
         "cores": threads,
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": (f"{len(units)} (batch, kv head) units of the decode workload (32768 tokens, 7 query heads each), "
                    f"oracle-encoded, then decompress-then-attend repeated {done // len(units)}x in {att_s:.1f} s"),
-        "encode_mvectors_per_s": 2 * len(units) * ctx / enc_s / 1e6,
-        "encode_sample": f"{2 * len(units) * ctx} vectors (K 4-bit + V 2-bit) in {enc_s:.1f} s",
+        "encode": {
+            "workload": "the whole encode step: 4 heads x 8192 tokens fp16, K 4-bit + V 2-bit (65,536 vectors)",
+            "mvectors_per_s": n_enc / enc_s / 1e6,
+            "mvectors_per_s_1_thread": n_enc / enc_1t_s / 1e6,
+            "seconds": enc_s,
+            "seconds_1_thread": enc_1t_s,
+        },
+        "tiny": {
+            "workload": "512 keys/values d=128, 3-bit K (MSE-only and QJL m=128) and V, 8 queries: encode + attention",
+            "seconds_1_thread": tiny_s,
+        },
+        "search": {
+            "sample": f"{n_qs} of 1024 queries over {n_rows} of 2^20 rows (3-bit + QJL m=256, d=256, top-10)",
+            "sample_seconds": s_search,
+            "db_encode_mvectors_per_s": n_rows / s_enc / 1e6,
+            "extrapolated_ms_per_call": full * 1e3,
+            "extrapolated": "linearly in queries x rows to 1024 queries over 2^20 rows",
+        },
+        "long": {
+            "sample": f"1 of 8 kv heads x {lt} of 2^20 tokens, K3/V3, its 8 query heads (bf16)",
+            "gbs": lt * 100 / long_s / 1e9,
+            "seconds": long_s,
+        },
     }
 
 
-def read_ceiling(torch, reps=50):
-    """Context for the roofline: what plain library streaming kernels reach on
-    the box, timed with events on the current stream -- torch's sum over a
-    1 GiB fp32 tensor (read only) and a 512 MiB device copy (512 MiB read +
-    512 MiB written), both well beyond the 256 MB Infinity Cache.  The faster
-    of the two is reported as the practical ceiling; the roofline peak stays
-    the published 8 TB/s."""
-    def timed(fn):
-        for _ in range(5):
-            fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+class _Null:
+    def __enter__(self):
+        return self
 
-    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    ms_sum = timed(lambda: x.sum())
-    del x
-    src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    ms_copy = timed(lambda: dst.copy_(src))
-    del src, dst
-    sum_gbs = (1 << 30) / (ms_sum * 1e-3) / 1e9
-    copy_gbs = (1 << 30) / (ms_copy * 1e-3) / 1e9
-    return {"sum_1gib_gbs": sum_gbs, "copy_512mib_gbs": copy_gbs, "gbs": max(sum_gbs, copy_gbs),
-            "kernels": "torch.sum over 1 GiB fp32; torch copy_ of 512 MiB (bytes read + written)"}
+    def __exit__(self, *a):
+        return False
+
+
+def read_ceiling(tq, torch, reps=30):
+    """The practical read ceiling: the library's read-only streaming kernel
+    (tq_stream_read, 16-byte loads, nothing written) over a 1 GiB buffer, far
+    beyond the 256 MB Infinity Cache, timed with events on the launch stream
+    around each launch.  The roofline peak stays the published 8 TB/s."""
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(5):
+        tq.tq_stream_read(src, sink)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        tq.tq_stream_read(src, sink)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+    del src
+    return {"gbs": nbytes / (ms * 1e-3) / 1e9, "ms_per_launch": ms, "bytes": nbytes,
+            "kernel": "tq_stream_read: 16-byte loads over a 1 GiB buffer, read only"}
 
 
 def main():
@@ -567,7 +665,7 @@ def main():
         res["quality"] = quality_leg(tq, torch, synth)
         log(f"quality: {res['quality']}")
     if "decode" in legs and not args.calib_copy:  # counter runs keep the calibration copies the only large ones
-        res["read_ceiling"] = read_ceiling(torch)
+        res["read_ceiling"] = read_ceiling(tq, torch)
         log(f"streaming-read reference: {res['read_ceiling']['gbs']:.0f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
@@ -587,7 +685,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16 operands (K scores hi/lo split, fp32-accurate), f32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": "decode attention over a packed K4/V2 cache: batch 16, 28 query heads / 4 kv heads (7:1), "

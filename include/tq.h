@@ -387,6 +387,19 @@ size_t tq_search_workspace_bytes(const tq_codec *c, int n_q, int64_t n_db, int k
 size_t tq_packed_bytes(int d, int bits, int qjl_m);
 
 /*
+ * tq_stream_read -- read `bytes` of device memory at `src` with 16-byte loads,
+ * keeping only a running XOR (nothing is written except, with negligible
+ * probability, one word at *sink).  A measurement helper: decode is bound by
+ * memory bandwidth ([P1] v1.8.0 "성능 특성": decode reads its operands from
+ * memory every token), and the decode scan is itself a read-only stream, so
+ * this kernel's rate is the practical read ceiling the scan is compared with.
+ *   src   16-byte aligned; bytes a multiple of 16 (0 launches nothing).
+ *   sink  one uint32 on the device, 4-byte aligned.
+ * Errors: TQ_EINVAL for NULL or misaligned pointers or a bad size.
+ */
+int tq_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
+/*
  * Static description of an error code (never NULL).  [P1] v1.2.0 ("입력 검증")
  * handles invalid K/V type combinations by silently falling back; this
  * library reports them as TQ_EUNSUPPORTED and leaves the policy to the caller.

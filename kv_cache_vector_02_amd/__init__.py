@@ -24,7 +24,7 @@ _DTYPES = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16
 EXPORTS = (
     "tq_codebook", "tq_encode", "tq_encode_kv", "tq_prefill", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
     "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes", "tq_workspace_bytes",
-    "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror",
+    "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror", "tq_stream_read",
 )
 TQ_OP_ATTN_DECODE, TQ_OP_ATTN_DECODE_RW, TQ_OP_IP_SEARCH = 1, 2, 3
 
@@ -90,6 +90,7 @@ def _load():
         "tq_search_workspace_bytes": (SZ, [CP, I, I64, I]),
         "tq_packed_bytes": (SZ, [I, I, I]),
         "tq_strerror": (ctypes.c_char_p, [I]),
+        "tq_stream_read": (I, [P, SZ, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -424,6 +425,15 @@ def tq_ip_search(codec: tq_codec, q: torch.Tensor, codes: torch.Tensor, norms: t
                              _ptr(qjl_gamma), _ptr(qjl_S), n_db, k, _ptr(out_scores), _ptr(out_ids),
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q)),
            "tq_ip_search")
+
+
+def tq_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read all of `src` (contiguous device tensor) with 16-byte loads; `sink`
+    is a device tensor of at least 4 bytes (almost never written)."""
+    if not src.is_contiguous() or sink.numel() * sink.element_size() < 4:
+        raise ValueError("src must be contiguous and sink hold at least 4 bytes")
+    _check(_lib.tq_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream, src)),
+           "tq_stream_read")
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

@@ -278,19 +278,19 @@ __device__ __forceinline__ void fetch_k(uint32_t (&rk)[4 * C::GW], const uint8_t
         if constexpr (C::GW % 4 == 0) {
 #pragma unroll
             for (int w = 0; w < C::GW / 4; ++w) {
-                const uint4 v = reinterpret_cast<const uint4*>(p)[w];
+                const uint4 v = ld_stream4(p + 4 * w);
                 rk[j * C::GW + 4 * w] = v.x; rk[j * C::GW + 4 * w + 1] = v.y;
                 rk[j * C::GW + 4 * w + 2] = v.z; rk[j * C::GW + 4 * w + 3] = v.w;
             }
         } else if constexpr (C::GW % 2 == 0) {
 #pragma unroll
             for (int w = 0; w < C::GW / 2; ++w) {
-                const uint2 v = reinterpret_cast<const uint2*>(p)[w];
+                const uint2 v = ld_stream2(p + 2 * w);
                 rk[j * C::GW + 2 * w] = v.x; rk[j * C::GW + 2 * w + 1] = v.y;
             }
         } else {
 #pragma unroll
-            for (int w = 0; w < C::GW; ++w) rk[j * C::GW + w] = p[w];
+            for (int w = 0; w < C::GW; ++w) rk[j * C::GW + w] = ld_stream1(p + w);
         }
     }
 }
@@ -305,12 +305,11 @@ __device__ __forceinline__ void fetch_v(uint32_t (&rv)[C::VTW], uint32_t& rn, ui
     const uint4* vp = reinterpret_cast<const uint4*>(vcodes + tl * C::RBV);
 #pragma unroll
     for (int w = 0; w < C::RBV / 16; ++w) {
-        const uint4 v = vp[w];
+        const uint4 v = ld_stream4(vp + w);
         rv[4 * w] = v.x; rv[4 * w + 1] = v.y; rv[4 * w + 2] = v.z; rv[4 * w + 3] = v.w;
     }
-    rn = (uint32_t)*reinterpret_cast<const uint16_t*>(knb + 2u * tl) |
-         ((uint32_t)*reinterpret_cast<const uint16_t*>(vnb + 2u * tl) << 16);
-    if constexpr (QJL) rg = *reinterpret_cast<const uint16_t*>(gmb + 2u * tl);
+    rn = ld_stream_u16(knb + 2u * tl) | (ld_stream_u16(vnb + 2u * tl) << 16);
+    if constexpr (QJL) rg = ld_stream_u16(gmb + 2u * tl);
 }
 
 template <int D, int KB, int VB, int G, bool QJL>

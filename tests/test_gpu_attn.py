@@ -235,3 +235,17 @@ def test_long_context_full_size_sampled_heads(tq):
     rel = parity.rel_rows(got[0, kh * g:(kh + 1) * g], ref)
     assert rel.max() <= parity.ATTN_TOL, rel.max()
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("splits", ["1", "2", "5", "plan", "max"])
+def test_split_count_invariance(tq, splits, monkeypatch):
+    """The split-K merge does not change the result: one split, a few, the
+    planned count and one split per 64-token tile (with empty trailing splits
+    for the shorter sequence) all match the oracle at a ragged context."""
+    if splits == "max":
+        monkeypatch.setenv("TQ_ATTN_SPLITS", "100000")
+    elif splits != "plan":
+        monkeypatch.setenv("TQ_ATTN_SPLITS", splits)
+    else:
+        monkeypatch.delenv("TQ_ATTN_SPLITS", raising=False)
+    run_case(tq, B=2, Hkv=2, g=7, cap=1000, ctx_len=[1000, 317], kbits=4, vbits=2, seed=31)

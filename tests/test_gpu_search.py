@@ -76,6 +76,14 @@ def test_search_tails(tq):
     check_search(tq, n_db=300, n_q=1, d=256, bits=1, m=0, k=1, seed=3)
 
 
+def test_search_long_lists(tq):
+    """k above 32 takes the 64-entry list variant: k = 33 and the largest, 64,
+    over ragged tiles, and fewer rows than k."""
+    check_search(tq, n_db=4097, n_q=40, d=128, bits=3, m=32, k=64, seed=4)
+    check_search(tq, n_db=3000, n_q=33, d=256, bits=2, m=256, k=33, seed=5)
+    check_search(tq, n_db=50, n_q=2, d=128, bits=4, m=0, k=64, seed=6)
+
+
 def test_search_full_size_sampled_queries(tq):
     """2^20 x 256 database, 3-bit + QJL m=256, 1024 queries, k=10; the oracle
     checks 8 sampled queries against all 2^20 estimates."""
