@@ -45,7 +45,8 @@ enum {
     TQ_EINVAL = -1,        /* null pointer, bad size, stride or alignment      */
     TQ_EUNSUPPORTED = -2,  /* d, bits, qjl_m, k or head ratio outside support  */
     TQ_EWORKSPACE = -3,    /* workspace missing or smaller than required       */
-    TQ_EDEVICE = -4        /* the HIP runtime reported a launch failure        */
+    TQ_EDEVICE = -4,       /* the HIP runtime reported a launch failure        */
+    TQ_ESCRATCH = -5       /* needs more than the no-alloc entry point's static scratch */
 };
 
 enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 };
@@ -250,6 +251,33 @@ int tq_attn_decode(const tq_codec *kc, const tq_codec *vc,
                    const uint8_t *v_codes, const uint16_t *v_norms,
                    float scale, float *out, void *workspace, size_t workspace_bytes,
                    void *stream);
+
+/*
+ * tq_attn_decode_noalloc -- tq_attn_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same computation and arguments without the
+ * workspace, which comes from a static device array of the library instead.
+ *
+ * The array holds TQ_NOALLOC_SCRATCH_BYTES (16 MiB) per device, for as long as
+ * the process runs; its device address is looked up once per device on the
+ * first call made there.  A call needing more scratch than that
+ * (tq_attn_workspace_bytes(...) > TQ_NOALLOC_SCRATCH_BYTES) returns
+ * TQ_ESCRATCH and launches nothing.  Nothing in the scratch has to start at
+ * zero: every value the kernels read is written earlier in the same call.
+ * Every call on one device shares its array: calls that overlap on one device
+ * (concurrent streams, or threads without ordering) race and give undefined
+ * results; order them on one stream.  The call allocates and frees nothing.
+ * Errors: those of tq_attn_decode, TQ_ESCRATCH, and TQ_EDEVICE when the
+ * scratch address cannot be looked up.
+ */
+#define TQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int tq_attn_decode_noalloc(const tq_codec *kc, const tq_codec *vc,
+                           const void *q, int q_dtype, int batch, int n_q_heads, int n_kv_heads,
+                           const int32_t *ctx_len, int64_t ctx_cap,
+                           const uint8_t *k_codes, const uint16_t *k_norms,
+                           const uint8_t *k_qjl, const uint16_t *k_gamma, const float *qjl_S,
+                           const uint8_t *v_codes, const uint16_t *v_norms,
+                           float scale, float *out, void *stream);
 
 /*
  * The three launches of tq_attn_decode as separate calls (same arguments, same

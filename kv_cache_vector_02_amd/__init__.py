@@ -16,7 +16,8 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
-TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EWORKSPACE, TQ_EDEVICE = 0, -1, -2, -3, -4
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EWORKSPACE, TQ_EDEVICE, TQ_ESCRATCH = 0, -1, -2, -3, -4, -5
+TQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 
 _DTYPES = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16}
@@ -25,6 +26,7 @@ EXPORTS = (
     "tq_codebook", "tq_encode", "tq_encode_kv", "tq_prefill", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
     "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes", "tq_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror", "tq_stream_read",
+    "tq_attn_decode_noalloc",
 )
 TQ_OP_ATTN_DECODE, TQ_OP_ATTN_DECODE_RW, TQ_OP_IP_SEARCH = 1, 2, 3
 
@@ -91,6 +93,7 @@ def _load():
         "tq_packed_bytes": (SZ, [I, I, I]),
         "tq_strerror": (ctypes.c_char_p, [I]),
         "tq_stream_read": (I, [P, SZ, P, P]),
+        "tq_attn_decode_noalloc": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -348,6 +351,22 @@ def tq_attn_decode(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.T
     """q [B][Hq][d]; caches [B][Hkv][ctx_cap][...] contiguous; out [B][Hq][d] fp32."""
     _attn("tq_attn_decode", kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, scale, out, workspace,
           k_qjl, k_gamma, qjl_S, stream)
+
+
+def tq_attn_decode_noalloc(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.Tensor,
+                           k_codes: torch.Tensor, k_norms: torch.Tensor, v_codes: torch.Tensor,
+                           v_norms: torch.Tensor, scale: float, out: torch.Tensor,
+                           k_qjl: torch.Tensor | None = None, k_gamma: torch.Tensor | None = None,
+                           qjl_S: torch.Tensor | None = None, stream=None) -> None:
+    """tq_attn_decode without a workspace: the library's static per-device
+    scratch (TQ_NOALLOC_SCRATCH_BYTES) is used; nothing is allocated.  Calls
+    that overlap on one device race on that scratch."""
+    B, Hq, Hkv, cap = _check_cache(kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, out, k_qjl, k_gamma,
+                                   qjl_S)
+    _check(_lib.tq_attn_decode_noalloc(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _DTYPES[q.dtype], B, Hq, Hkv,
+                                       _ptr(ctx_len), cap, _ptr(k_codes), _ptr(k_norms), _ptr(k_qjl), _ptr(k_gamma),
+                                       _ptr(qjl_S), _ptr(v_codes), _ptr(v_norms), ctypes.c_float(scale), _ptr(out),
+                                       _stream(stream, q)), "tq_attn_decode_noalloc")
 
 
 def tq_attn_decode_rw(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.Tensor,

@@ -5,6 +5,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "tq.h"
 #include "tq_internal.h"
 
@@ -134,6 +137,7 @@ const char* tq_strerror(int code) {
         case TQ_EUNSUPPORTED: return "unsupported configuration (d, bits, qjl_m, k or head ratio)";
         case TQ_EWORKSPACE: return "workspace missing or too small";
         case TQ_EDEVICE: return "HIP launch failed";
+        case TQ_ESCRATCH: return "request exceeds the static scratch of the no-alloc entry point";
         default: return "unknown error code";
     }
 }
@@ -376,6 +380,55 @@ TQ_ATTN_ENTRY(tq_attn_decode, tqi::ATTN_ALL)
 TQ_ATTN_ENTRY(tq_attn_prepare, tqi::ATTN_PREPARE)
 TQ_ATTN_ENTRY(tq_attn_scan, tqi::ATTN_SCAN)
 TQ_ATTN_ENTRY(tq_attn_combine, tqi::ATTN_COMBINE)
+
+// Scratch of tq_attn_decode_noalloc: a static device array (one copy per
+// device the library runs on), holding the split partials and QJL query
+// projections between the launches of one call.  In host code `scratch` names
+// a host-side stand-in, not the device array: only the address from
+// hipGetSymbolAddress, taken once per device with that device current, is
+// passed to kernels.
+static __device__ __align__(256) uint8_t scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch (nullptr on failure).
+void* scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+        g_scratch_ptr[dev].store(addr, std::memory_order_release);
+        p = addr;
+    }
+    return p;
+}
+}  // namespace
+
+int tq_attn_decode_noalloc(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch,
+                           int n_q_heads, int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap,
+                           const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl,
+                           const uint16_t* k_gamma, const float* qjl_S, const uint8_t* v_codes,
+                           const uint16_t* v_norms, float scale, float* out, void* stream) {
+    const size_t need = tq_attn_workspace_bytes(kc, vc, batch, n_q_heads, n_kv_heads, ctx_cap);
+    if (need > TQ_NOALLOC_SCRATCH_BYTES) return TQ_ESCRATCH;
+    void* ws = need > 0 ? scratch_address() : nullptr;
+    if (need > 0 && !ws) return TQ_EDEVICE;
+    // need == 0 means the sizes are invalid: attn_setup reports why
+    tqi::AttnArgs a;
+    const int rc = attn_setup(kc, vc, q, q_dtype, batch, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes, k_norms,
+                              k_qjl, k_gamma, qjl_S, v_codes, v_norms, nullptr, nullptr, 0, nullptr, 0, scale, out,
+                              ws ? ws : (void*)nullptr, ws ? (size_t)TQ_NOALLOC_SCRATCH_BYTES : 0, &a);
+    if (rc != TQ_OK) return rc;
+    return finish(tqi::launch_attn(a, tqi::ATTN_ALL, (hipStream_t)stream));
+}
 
 int tq_attn_decode_rw(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch, int n_q_heads,
                       int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap, const uint8_t* k_codes,

@@ -308,3 +308,20 @@ def test_binding_rejects_mismatched_planes():
         tq.tq_ip_search(sc, _cpu(4, 256, dtype=torch.float32), _cpu(100, 96), _cpu(100, dtype=torch.float16),
                         _cpu(100, 32), _cpu(100, dtype=torch.float16), _cpu(256, 256, dtype=torch.float32), 10,
                         _cpu(4, 10, dtype=torch.float32), _cpu(4, 10, dtype=torch.int32), _cpu(1 << 16))
+
+
+def test_noalloc_rejects_requests_beyond_its_scratch():
+    """tq_attn_decode_noalloc refuses, on the host, sizes whose workspace would
+    exceed its static scratch, and validates arguments like tq_attn_decode."""
+    kc, vc = tq.tq_codebook(4, 128, 0), tq.tq_codebook(2, 128, 0)
+    P = FAKE
+
+    def call(B, Hq, Hkv, cap, q=P):
+        return tq.raw_call("tq_attn_decode_noalloc", ctypes.byref(kc), ctypes.byref(vc), q, 1, B, Hq, Hkv, P, cap,
+                           P, P, None, None, None, P, P, ctypes.c_float(0.1), P, None)
+
+    assert tq.tq_attn_workspace_bytes(kc, vc, 512, 64, 8, 4096) > tq.TQ_NOALLOC_SCRATCH_BYTES
+    assert call(512, 64, 8, 4096) == tq.TQ_ESCRATCH
+    assert call(2, 14, 3, 1000) == tq.TQ_EUNSUPPORTED  # 14 % 3
+    assert call(2, 14, 2, 0) == tq.TQ_EINVAL
+    assert "scratch" in tq.strerror(tq.TQ_ESCRATCH)
