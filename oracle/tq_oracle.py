@@ -425,6 +425,37 @@ def gqa_attention(q, ctx_len, k_codes, k_norms, v_codes, v_norms, kc, vc, scale,
     return out
 
 
+def mq_attention(q, ctx_len, k_codes, k_norms, v_codes, v_norms, kc, vc, scale,
+                 k_qjl=None, k_gamma=None, S=None, cols=None):
+    """Multi-query decode over the packed cache: q [B][C][Hq][d] holds the last C
+    query tokens (columns) of each sequence, whose keys and values are already
+    in the cache ([P1] v1.1.0 "버그 수정": prompt evaluation runs ncols = 2 query
+    columns through the same attention kernel; [P1] v1.4.2 "MMA Tensor Core 가속"
+    serves several columns at once).  Column c of sequence b sits at position
+    ctx_len[b] - C + c and attends causally: over the first
+    max(0, ctx_len[b] - (C - 1 - c)) tokens of its cache, with everything else
+    as in gqa_attention.
+
+    ``cols`` optionally restricts the computation to a list of (b, c, h)
+    triples; the result then has one row per triple.  Returns [B*C*Hq][d] in
+    (b, c, h) order otherwise.
+    """
+    B, C, Hq, d = q.shape
+    Hkv = k_codes.shape[1]
+    g = Hq // Hkv
+    trip = cols if cols is not None else [(b, c, h) for b in range(B) for c in range(C) for h in range(Hq)]
+    out = np.zeros((len(trip), vc.d))
+    for row, (b, c, h) in enumerate(trip):
+        kh = h // g
+        n = max(0, int(ctx_len[b]) - (C - 1 - c))
+        args = {}
+        if kc.qjl_m:
+            args = dict(k_qjl=k_qjl[b, kh, :n], k_gamma=k_gamma[b, kh, :n], S=S)
+        out[row] = attention(np.asarray(q[b, c, h], dtype=np.float64)[None, :], k_codes[b, kh, :n],
+                             k_norms[b, kh, :n], v_codes[b, kh, :n], v_norms[b, kh, :n], kc, vc, scale, **args)[0]
+    return out
+
+
 def ip_scores(q: np.ndarray, codes, norms16, qjl_packed, gamma16, S, codec: Codec) -> np.ndarray:
     """Unbiased inner-product estimates <q, x_t> for all (query, database row) pairs.
 

@@ -339,6 +339,76 @@ def test_gqa_head_mapping():
         np.testing.assert_allclose(out[row], want, rtol=1e-14)
 
 
+def _mq_cache(rng, B, Hkv, cap, d, kc, vc, keys=None):
+    K = keys if keys is not None else rng.standard_normal((B * Hkv * cap, d)) * 3
+    ek = o.encode(K, kc)
+    ev = o.encode(rng.standard_normal((B * Hkv * cap, d)), vc)
+    return (ek["codes"].reshape(B, Hkv, cap, -1), ek["norms"].reshape(B, Hkv, cap),
+            ev["codes"].reshape(B, Hkv, cap, -1), ev["norms"].reshape(B, Hkv, cap))
+
+
+def test_mq_causal_closed_forms():
+    """Multi-query decode, closed forms: with ctx_len = C, column c sees tokens
+    0..c, so column 0 returns V_hat_0 exactly; with identical keys column c
+    returns the mean of V_hat_0..V_hat_c; the last column equals single-query
+    decode over the whole context."""
+    d, C, cap = 64, 4, 4
+    kc, vc = o.Codec(3, d, 3), o.Codec(2, d, 3)
+    rng = np.random.default_rng(21)
+    kcodes, kn, vcodes, vn = _mq_cache(rng, 1, 1, cap, d, kc, vc)
+    V = o.decode(vcodes[0, 0], vn[0, 0], vc)
+    q = rng.standard_normal((1, C, 2, d))
+    out = o.mq_attention(q, [C], kcodes, kn, vcodes, vn, kc, vc, 0.3).reshape(C, 2, d)
+    np.testing.assert_allclose(out[0], np.repeat(V[:1], 2, axis=0), rtol=1e-13)
+    # identical keys: uniform weights over the visible prefix
+    same = np.repeat(rng.standard_normal((1, d)), cap, axis=0) * 5
+    kcodes2, kn2, _, _ = _mq_cache(rng, 1, 1, cap, d, kc, vc, keys=same)
+    out2 = o.mq_attention(q, [C], kcodes2, kn2, vcodes, vn, kc, vc, 0.3).reshape(C, 2, d)
+    for c in range(C):
+        np.testing.assert_allclose(out2[c], np.repeat(V[:c + 1].mean(0, keepdims=True), 2, axis=0),
+                                   rtol=1e-12, atol=1e-14)
+    # last column = plain decode over everything
+    full = o.gqa_attention(q[:, C - 1], [C], kcodes, kn, vcodes, vn, kc, vc, 0.3)
+    np.testing.assert_allclose(out[C - 1], full, rtol=1e-14)
+
+
+def test_mq_is_causal():
+    """Column c ignores every token at or after its own position + 1: changing
+    those keys and values leaves it unchanged and changes the later columns."""
+    d, B, Hkv, g, C, cap = 64, 2, 2, 3, 3, 20
+    kc, vc = o.Codec(4, d, 5), o.Codec(3, d, 5)
+    rng = np.random.default_rng(22)
+    kcodes, kn, vcodes, vn = _mq_cache(rng, B, Hkv, cap, d, kc, vc)
+    ctx = np.array([20, 9])
+    q = rng.standard_normal((B, C, Hkv * g, d))
+    base = o.mq_attention(q, ctx, kcodes, kn, vcodes, vn, kc, vc, 0.2).reshape(B, C, Hkv * g, d)
+    # overwrite the last token of sequence 1 (position ctx-1, seen only by column C-1)
+    k2, n2, v2, vn2 = kcodes.copy(), kn.copy(), vcodes.copy(), vn.copy()
+    k2[1, :, ctx[1] - 1] = kcodes[0, :, 0]
+    v2[1, :, ctx[1] - 1] = vcodes[0, :, 0]
+    n2[1, :, ctx[1] - 1] = kn[0, :, 0]
+    vn2[1, :, ctx[1] - 1] = vn[0, :, 0]
+    moved = o.mq_attention(q, ctx, k2, n2, v2, vn2, kc, vc, 0.2).reshape(B, C, Hkv * g, d)
+    assert np.array_equal(moved[0], base[0])
+    assert np.array_equal(moved[1, :C - 1], base[1, :C - 1])
+    assert np.abs(moved[1, C - 1] - base[1, C - 1]).max() > 1e-6
+    # a context shorter than the columns: early columns see no token -> zero
+    short = o.mq_attention(q, [2, 1], kcodes, kn, vcodes, vn, kc, vc, 0.2).reshape(B, C, Hkv * g, d)
+    assert np.all(short[0, 0] == 0) and np.all(short[1, :2] == 0)
+    assert np.all(np.linalg.norm(short[0, 1:], axis=-1) > 0)
+
+
+def test_mq_single_column_is_decode():
+    d, B, Hkv, g, cap = 128, 2, 2, 4, 30
+    kc, vc = o.Codec(4, d, 6), o.Codec(2, d, 6)
+    rng = np.random.default_rng(23)
+    kcodes, kn, vcodes, vn = _mq_cache(rng, B, Hkv, cap, d, kc, vc)
+    q = rng.standard_normal((B, 1, Hkv * g, d))
+    ctx = [30, 17]
+    np.testing.assert_array_equal(o.mq_attention(q, ctx, kcodes, kn, vcodes, vn, kc, vc, 0.1),
+                                  o.gqa_attention(q[:, 0], ctx, kcodes, kn, vcodes, vn, kc, vc, 0.1))
+
+
 def test_window_is_concatenation():
     """Tokens moved from the packed cache into the residual window (as their
     decoded values) leave the output unchanged: the window joins the same softmax."""
