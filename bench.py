@@ -206,6 +206,20 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
 
     ms_append = timed_loop(append, steps, max(warmup // 4, 1), torch)
     ms_append_attend = timed_loop(append_attend, steps, max(warmup // 4, 1), torch)
+
+    # multi-query decode (speculative verification of 3 draft tokens + 1): 4
+    # causal query columns per sequence in one tq_attn_decode_mq call
+    C = 4
+    q_mq = synth.normal((B, C, Hq, d), seed=synth.SEED_DECODE_Q + 1, dtype=torch.float16, device="cuda")
+    out_mq = torch.empty(B, C, Hq, d, device="cuda")
+    ws_mq = tq.workspace(tq.tq_workspace_bytes(tq.TQ_OP_ATTN_DECODE_MQ, kc, vc, B, Hq, Hkv, ctx, n_q=C))
+
+    def mq(i, ev=None):
+        c = caches[i % replicas]
+        tq.tq_attn_decode_mq(kc, vc, q_mq, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], scale,
+                             out_mq, ws_mq)
+
+    ms_mq = timed_loop(mq, steps, max(warmup // 4, 1), torch)
     token_heads = B * Hkv * ctx
     per_token_head = (kc.code_bytes + 2) + (vc.code_bytes + 2)  # 100 B
     cache_bytes = token_heads * per_token_head
@@ -228,6 +242,15 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
             "gbs": (cache_bytes + win_bytes + q.numel() * 2 + out.numel() * 4) / (ms_rw * 1e-3) / 1e9,
             "window_bytes": win_bytes,
             "extra_ms_vs_packed_only": ms_rw - ms,
+        },
+        "multi_query": {
+            "workload": "4 causal query columns per sequence (speculative verification of 3 draft tokens + 1) in one "
+                        "tq_attn_decode_mq call over the same caches",
+            "columns": C,
+            "ms_per_call": ms_mq,
+            "ms_per_column": ms_mq / C,
+            "single_column_ms_per_step": ms,
+            "gbs_cache_bytes": cache_bytes / (ms_mq * 1e-3) / 1e9,
         },
         "append": {
             "workload": "one new token per (sequence, kv head) appended to the K4 and V2 caches (one tq_append call)",

@@ -280,6 +280,39 @@ int tq_attn_decode_noalloc(const tq_codec *kc, const tq_codec *vc,
                            float scale, float *out, void *stream);
 
 /*
+ * tq_attn_decode_mq -- multi-query decode over the packed cache: n_cols query
+ * tokens per sequence in one call, each attending causally.  [P1] runs several
+ * query columns through its attention kernel at once (v1.1.0 "버그 수정": the
+ * ncols = 2 prompt-evaluation path; v1.4.2 "MMA Tensor Core 가속"), the shape
+ * of chunked-prefill attention and of speculative verification.
+ *
+ * The n_cols columns are the last n_cols tokens of each sequence, and their
+ * keys and values are already in the cache (append or prefill first): column c
+ * of sequence b sits at position ctx_len[b] - n_cols + c and attends over the
+ * first max(0, ctx_len[b] - (n_cols - 1 - c)) tokens, exactly as
+ * tq_attn_decode would with that context length.  A column that sees no token
+ * gives a zero row.
+ *
+ *   q    [batch][n_cols][n_q_heads][d] of q_dtype, contiguous, 16-byte aligned.
+ *   out  [batch][n_cols][n_q_heads][d] float32.
+ *   workspace  >= tq_workspace_bytes(TQ_OP_ATTN_DECODE_MQ, ..., n_q = n_cols, ...).
+ * Every other argument and error is that of tq_attn_decode; 1 <= n_cols <=
+ * TQ_MAX_QUERY_COLS.  The query rows of one kv head (its g heads in each
+ * column) share the scan of its cache in blocks of up to 8 rows, so with
+ * g * n_cols <= 8 the cache is read once for all columns.  n_cols = 1 is
+ * tq_attn_decode.
+ */
+#define TQ_MAX_QUERY_COLS 64
+int tq_attn_decode_mq(const tq_codec *kc, const tq_codec *vc,
+                      const void *q, int q_dtype, int batch, int n_cols, int n_q_heads, int n_kv_heads,
+                      const int32_t *ctx_len, int64_t ctx_cap,
+                      const uint8_t *k_codes, const uint16_t *k_norms,
+                      const uint8_t *k_qjl, const uint16_t *k_gamma, const float *qjl_S,
+                      const uint8_t *v_codes, const uint16_t *v_norms,
+                      float scale, float *out, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
  * The three launches of tq_attn_decode as separate calls (same arguments, same
  * checks, same workspace, which carries the state between them), for callers
  * that time or schedule the stages themselves:
@@ -366,14 +399,16 @@ int tq_attn_decode_rw(const tq_codec *kc, const tq_codec *vc,
  *   TQ_OP_ATTN_DECODE, TQ_OP_ATTN_DECODE_RW: kc, vc, batch, n_q_heads,
  *       n_kv_heads, ctx_cap as for tq_attn_decode (n_q, n_db, k unused);
  *   TQ_OP_IP_SEARCH: kc is the search codec (vc may be NULL), n_q, n_db, k as
- *       for tq_ip_search (batch, heads and ctx_cap unused).
+ *       for tq_ip_search (batch, heads and ctx_cap unused);
+ *   TQ_OP_ATTN_DECODE_MQ: as TQ_OP_ATTN_DECODE with n_q = n_cols, the query
+ *       columns per sequence of tq_attn_decode_mq.
  * The codecs are arguments because the sizes depend on d, the bit widths
  * (through the split plan) and the QJL width m.  The size depends on the
  * current device (its compute-unit count sets the split count).
  * tq_attn_workspace_bytes and tq_search_workspace_bytes are the same sizes for
  * one operation each.
  */
-enum { TQ_OP_ATTN_DECODE = 1, TQ_OP_ATTN_DECODE_RW = 2, TQ_OP_IP_SEARCH = 3 };
+enum { TQ_OP_ATTN_DECODE = 1, TQ_OP_ATTN_DECODE_RW = 2, TQ_OP_IP_SEARCH = 3, TQ_OP_ATTN_DECODE_MQ = 4 };
 size_t tq_workspace_bytes(int op, const tq_codec *kc, const tq_codec *vc, int batch, int n_q_heads,
                           int n_kv_heads, int64_t ctx_cap, int n_q, int64_t n_db, int k);
 

@@ -26,9 +26,10 @@ EXPORTS = (
     "tq_codebook", "tq_encode", "tq_encode_kv", "tq_prefill", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
     "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes", "tq_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror", "tq_stream_read",
-    "tq_attn_decode_noalloc",
+    "tq_attn_decode_noalloc", "tq_attn_decode_mq",
 )
-TQ_OP_ATTN_DECODE, TQ_OP_ATTN_DECODE_RW, TQ_OP_IP_SEARCH = 1, 2, 3
+TQ_OP_ATTN_DECODE, TQ_OP_ATTN_DECODE_RW, TQ_OP_IP_SEARCH, TQ_OP_ATTN_DECODE_MQ = 1, 2, 3, 4
+TQ_MAX_QUERY_COLS = 64
 
 
 class tq_codec(ctypes.Structure):
@@ -94,6 +95,7 @@ def _load():
         "tq_strerror": (ctypes.c_char_p, [I]),
         "tq_stream_read": (I, [P, SZ, P, P]),
         "tq_attn_decode_noalloc": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P]),
+        "tq_attn_decode_mq": (I, [CP, CP, P, I, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -351,6 +353,26 @@ def tq_attn_decode(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.T
     """q [B][Hq][d]; caches [B][Hkv][ctx_cap][...] contiguous; out [B][Hq][d] fp32."""
     _attn("tq_attn_decode", kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, scale, out, workspace,
           k_qjl, k_gamma, qjl_S, stream)
+
+
+def tq_attn_decode_mq(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.Tensor,
+                      k_codes: torch.Tensor, k_norms: torch.Tensor, v_codes: torch.Tensor, v_norms: torch.Tensor,
+                      scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                      k_qjl: torch.Tensor | None = None, k_gamma: torch.Tensor | None = None,
+                      qjl_S: torch.Tensor | None = None, stream=None) -> None:
+    """Multi-query causal decode: q and out [B][C][Hq][d] (the last C tokens of
+    each sequence, already in the cache); caches [B][Hkv][ctx_cap][...]."""
+    if q.dim() != 4 or out.dim() != 4:
+        raise ValueError("q and out must be [B][C][Hq][d]")
+    B, C, Hq, d = q.shape
+    _check_cache(kc, vc, q.view(B, C * Hq, d), ctx_len, k_codes, k_norms, v_codes, v_norms, out.view(B, C * Hq, -1),
+                 k_qjl, k_gamma, qjl_S)
+    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
+    _check(_lib.tq_attn_decode_mq(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _DTYPES[q.dtype], B, C, Hq, Hkv,
+                                  _ptr(ctx_len), cap, _ptr(k_codes), _ptr(k_norms), _ptr(k_qjl), _ptr(k_gamma),
+                                  _ptr(qjl_S), _ptr(v_codes), _ptr(v_norms), ctypes.c_float(scale), _ptr(out),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q)),
+           "tq_attn_decode_mq")
 
 
 def tq_attn_decode_noalloc(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.Tensor,

@@ -272,33 +272,39 @@ int tq_decode(const tq_codec* c, const uint8_t* codes, int64_t code_row_stride, 
     return finish(tqi::launch_decode(a, (hipStream_t)stream));
 }
 
-static int attn_check(const tq_codec* kc, const tq_codec* vc, int batch, int n_q_heads, int n_kv_heads,
+static int attn_check(const tq_codec* kc, const tq_codec* vc, int batch, int ncols, int n_q_heads, int n_kv_heads,
                       int64_t ctx_cap, int* splits, int64_t* split_tokens, int* G) {
     if (!kc || !vc) return TQ_EINVAL;
     if (!valid_codec(kc) || !valid_codec(vc)) return TQ_EUNSUPPORTED;
     if (kc->d != vc->d || (kc->d != 128 && kc->d != 256) || vc->qjl_m != 0) return TQ_EUNSUPPORTED;
-    if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || ctx_cap <= 0 || batch > 65535) return TQ_EINVAL;
-    if (n_q_heads % n_kv_heads != 0) return TQ_EUNSUPPORTED;
+    if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || ctx_cap <= 0 || batch > 65535 || ncols <= 0)
+        return TQ_EINVAL;
+    if (n_q_heads % n_kv_heads != 0 || ncols > TQ_MAX_QUERY_COLS) return TQ_EUNSUPPORTED;
     // one (batch, kv head) plane of any cache array must be addressable with 31-bit offsets
     const int64_t row_max = kc->d * (kc->bits > vc->bits ? kc->bits : vc->bits) / 8 + kc->qjl_m / 8;
     if (ctx_cap > (((int64_t)1 << 31) - 1) / (row_max > 2 ? row_max : 2)) return TQ_EUNSUPPORTED;
-    const int g = n_q_heads / n_kv_heads;
-    tqi::attn_plan(batch, n_kv_heads, g, ctx_cap, kc->d, kc->bits, vc->bits, kc->qjl_m > 0, splits, split_tokens, G);
-    if ((int64_t)n_kv_heads * (g / *G) > 65535) return TQ_EUNSUPPORTED;
+    const int gv = n_q_heads / n_kv_heads * ncols;  // query rows per kv head
+    tqi::attn_plan(batch, n_kv_heads, gv, ctx_cap, kc->d, kc->bits, vc->bits, kc->qjl_m > 0, splits, split_tokens, G);
+    if ((int64_t)n_kv_heads * (gv / *G) > 65535) return TQ_EUNSUPPORTED;
     return TQ_OK;
+}
+
+static size_t attn_ws_bytes(const tq_codec* kc, const tq_codec* vc, int batch, int ncols, int n_q_heads,
+                            int n_kv_heads, int64_t ctx_cap) {
+    int splits, G;
+    int64_t per;
+    if (attn_check(kc, vc, batch, ncols, n_q_heads, n_kv_heads, ctx_cap, &splits, &per, &G) != TQ_OK) return 0;
+    return tqi::attn_workspace(batch * ncols, n_q_heads, kc->d, kc->qjl_m, splits);
 }
 
 size_t tq_attn_workspace_bytes(const tq_codec* kc, const tq_codec* vc, int batch, int n_q_heads, int n_kv_heads,
                                int64_t ctx_cap) {
-    int splits, G;
-    int64_t per;
-    if (attn_check(kc, vc, batch, n_q_heads, n_kv_heads, ctx_cap, &splits, &per, &G) != TQ_OK) return 0;
-    return tqi::attn_workspace(batch, n_q_heads, kc->d, kc->qjl_m, splits);
+    return attn_ws_bytes(kc, vc, batch, 1, n_q_heads, n_kv_heads, ctx_cap);
 }
 
 // Validates every argument of the decode-attention entry points and fills the
 // launch description; nothing is launched here.
-static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch,
+static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch, int ncols,
                       int n_q_heads, int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap,
                       const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl, const uint16_t* k_gamma,
                       const float* qjl_S, const uint8_t* v_codes, const uint16_t* v_norms, const void* k_win,
@@ -306,8 +312,9 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
                       void* workspace, size_t workspace_bytes, tqi::AttnArgs* a) {
     int splits, G;
     int64_t per;
-    const int rc = attn_check(kc, vc, batch, n_q_heads, n_kv_heads, ctx_cap, &splits, &per, &G);
+    const int rc = attn_check(kc, vc, batch, ncols, n_q_heads, n_kv_heads, ctx_cap, &splits, &per, &G);
     if (rc != TQ_OK) return rc;
+    if (ncols > 1 && win_cap > 0) return TQ_EUNSUPPORTED;  // the residual window serves one query column
     if (q_dtype != TQ_F32 && q_dtype != TQ_F16 && q_dtype != TQ_BF16) return TQ_EINVAL;
     if (!q || !ctx_len || !k_codes || !k_norms || !v_codes || !v_norms || !out) return TQ_EINVAL;
     if (!aligned(q, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(out, 16) ||
@@ -323,7 +330,7 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
             return TQ_EINVAL;
     }
     const int d = kc->d, m = kc->qjl_m;
-    const size_t need = tqi::attn_workspace(batch, n_q_heads, d, m, splits);
+    const size_t need = tqi::attn_workspace(batch * ncols, n_q_heads, d, m, splits);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return TQ_EWORKSPACE;
 
     tqi::fill_codec_args(kc, &a->kc);
@@ -334,8 +341,9 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
     a->hq = n_q_heads;
     a->hkv = n_kv_heads;
     a->g = n_q_heads / n_kv_heads;
+    a->ncols = ncols;
     a->heads_per_chunk = G;
-    a->chunks = a->g / G;
+    a->chunks = a->g * ncols / G;
     a->ctx_len = ctx_len;
     a->ctx_cap = ctx_cap;
     a->k_codes = k_codes;
@@ -347,7 +355,7 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
     a->v_norms = v_norms;
     a->scale = scale;
     a->out = out;
-    const size_t heads = (size_t)batch * n_q_heads;
+    const size_t heads = (size_t)batch * ncols * n_q_heads;
     float* ws = (float*)workspace;
     auto al = [](size_t n) { return (n + 63) & ~(size_t)63; };
     a->qproj = ws;
@@ -369,7 +377,7 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
              const uint8_t* v_codes, const uint16_t* v_norms, float scale, float* out, void* workspace,        \
              size_t workspace_bytes, void* stream) {                                                          \
         tqi::AttnArgs a;                                                                                      \
-        const int rc = attn_setup(kc, vc, q, q_dtype, batch, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes, \
+        const int rc = attn_setup(kc, vc, q, q_dtype, batch, 1, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes, \
                                   k_norms, k_qjl, k_gamma, qjl_S, v_codes, v_norms, nullptr, nullptr, 0,       \
                                   nullptr, 0, scale, out, workspace, workspace_bytes, &a);                   \
         if (rc != TQ_OK) return rc;                                                                           \
@@ -423,7 +431,7 @@ int tq_attn_decode_noalloc(const tq_codec* kc, const tq_codec* vc, const void* q
     if (need > 0 && !ws) return TQ_EDEVICE;
     // need == 0 means the sizes are invalid: attn_setup reports why
     tqi::AttnArgs a;
-    const int rc = attn_setup(kc, vc, q, q_dtype, batch, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes, k_norms,
+    const int rc = attn_setup(kc, vc, q, q_dtype, batch, 1, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes, k_norms,
                               k_qjl, k_gamma, qjl_S, v_codes, v_norms, nullptr, nullptr, 0, nullptr, 0, scale, out,
                               ws ? ws : (void*)nullptr, ws ? (size_t)TQ_NOALLOC_SCRATCH_BYTES : 0, &a);
     if (rc != TQ_OK) return rc;
@@ -437,11 +445,24 @@ int tq_attn_decode_rw(const tq_codec* kc, const tq_codec* vc, const void* q, int
                       int win_dtype, const int32_t* win_len, int win_cap, float scale, float* out, void* workspace,
                       size_t workspace_bytes, void* stream) {
     tqi::AttnArgs a;
-    const int rc = attn_setup(kc, vc, q, q_dtype, batch, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes, k_norms,
+    const int rc = attn_setup(kc, vc, q, q_dtype, batch, 1, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes, k_norms,
                               k_qjl, k_gamma, qjl_S, v_codes, v_norms, k_win, v_win, win_dtype, win_len, win_cap,
                               scale, out, workspace, workspace_bytes, &a);
     if (rc != TQ_OK) return rc;
     return finish(tqi::launch_attn(a, tqi::ATTN_ALL | tqi::ATTN_WINDOW, (hipStream_t)stream));
+}
+
+int tq_attn_decode_mq(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch, int n_cols,
+                      int n_q_heads, int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap, const uint8_t* k_codes,
+                      const uint16_t* k_norms, const uint8_t* k_qjl, const uint16_t* k_gamma, const float* qjl_S,
+                      const uint8_t* v_codes, const uint16_t* v_norms, float scale, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    tqi::AttnArgs a;
+    const int rc = attn_setup(kc, vc, q, q_dtype, batch, n_cols, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes,
+                              k_norms, k_qjl, k_gamma, qjl_S, v_codes, v_norms, nullptr, nullptr, 0, nullptr, 0, scale,
+                              out, workspace, workspace_bytes, &a);
+    if (rc != TQ_OK) return rc;
+    return finish(tqi::launch_attn(a, tqi::ATTN_ALL, (hipStream_t)stream));
 }
 
 static int search_check(const tq_codec* c, int n_q, int64_t n_db, int k) {
@@ -468,6 +489,7 @@ size_t tq_workspace_bytes(int op, const tq_codec* kc, const tq_codec* vc, int ba
         case TQ_OP_ATTN_DECODE:
         case TQ_OP_ATTN_DECODE_RW: return tq_attn_workspace_bytes(kc, vc, batch, n_q_heads, n_kv_heads, ctx_cap);
         case TQ_OP_IP_SEARCH: return tq_search_workspace_bytes(kc, n_q, n_db, k);
+        case TQ_OP_ATTN_DECODE_MQ: return attn_ws_bytes(kc, vc, batch, n_q, n_q_heads, n_kv_heads, ctx_cap);
         default: return 0;
     }
 }

@@ -52,25 +52,26 @@ static int device_cus() {
     return n;
 }
 
-// Query heads of one kv group are processed in chunks of G <= 8 heads (the
-// largest divisor of g not above 8).  The context is cut into splits of a
+// The query rows of one kv head (g heads in each of the ncols query columns,
+// gv = g * ncols rows) are processed in chunks of G <= 8 rows (the largest
+// divisor of gv not above 8).  The context is cut into splits of a
 // multiple of 64 tokens.  With S resident block slots on the device (compute
 // units x blocks per unit for this variant), a grid of B blocks runs in
 // ceil(B / S) rounds and a block costs about (tiles per wave + 2) tile times
 // (the 2 covers its table setup and merge); the split count minimising
 // rounds x block cost is taken, among the largest split counts that fit 1..8
 // rounds.  The plan depends on the current device.
-void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int d, int kb, int vb, bool qjl, int* splits,
+void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int vb, bool qjl, int* splits,
                int64_t* split_tokens, int* heads_per_chunk) {
     int G = 1;
     for (int c = 8; c >= 1; --c) {
-        if (g % c == 0) {
+        if (gv % c == 0) {
             G = c;
             break;
         }
     }
     *heads_per_chunk = G;
-    const int64_t units = (int64_t)batch * hkv * (g / G);
+    const int64_t units = (int64_t)batch * hkv * (gv / G);
     const int64_t slots = (int64_t)device_cus() * split_blocks_any(d, kb, vb, G, qjl);
     const int64_t max_splits = ctx_cap > 0 ? (ctx_cap + 63) / 64 : 1;
     int64_t best_sp = 1, best_per = ((ctx_cap > 0 ? ctx_cap : 1) + 63) & ~(int64_t)63;
@@ -121,7 +122,7 @@ template <int D>
 static hipError_t launch_qprep_combine(const AttnArgs& a, hipStream_t s, bool prep) {
     if (prep) {
         constexpr int VPW = 64 / (D / 8);
-        const int heads = a.batch * a.hq;
+        const int heads = a.batch * a.ncols * a.hq;
         const int grid = (heads + VPW - 1) / VPW;
         switch (a.q_dtype) {
             case TQ_F32: hipLaunchKernelGGL((attn::qprep_kernel<D, 0>), dim3(grid), dim3(64), 0, s, a); break;
@@ -130,7 +131,7 @@ static hipError_t launch_qprep_combine(const AttnArgs& a, hipStream_t s, bool pr
         }
     } else {
         constexpr int HPB = 256 / (D / 8);  // heads per combine block
-        hipLaunchKernelGGL((attn::combine_kernel<D>), dim3((a.batch * a.hq + HPB - 1) / HPB), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((attn::combine_kernel<D>), dim3((a.batch * a.ncols * a.hq + HPB - 1) / HPB), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
     __shared__ float rot[VPW][D];
     const int lane = threadIdx.x;
     const int gl = lane & (LPV - 1), grp = lane / LPV;
-    const int heads = a.batch * a.hq;
+    const int heads = a.batch * a.ncols * a.hq;
     const int head = blockIdx.x * VPW + grp;
     const bool valid = head < heads;
     const uint32_t sbits = (a.kc.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
@@ -312,6 +312,17 @@ __device__ __forceinline__ void fetch_v(uint32_t (&rv)[C::VTW], uint32_t& rn, ui
     if constexpr (QJL) rg = ld_stream_u16(gmb + 2u * tl);
 }
 
+// Query rows.  A sequence carries ncols query columns (its last ncols tokens,
+// already in the cache) of hq heads; the rows of kv head kvh are its g heads
+// in each column, vl = c * g + j for column c and head kvh * g + j, and a
+// block takes G consecutive rows vl.  Row (b, c, h) is stored at index
+// (b * ncols + c) * hq + h of the query, workspace and output arrays, and
+// column c attends over the first ctx - (ncols - 1 - c) tokens (causal).
+__device__ __forceinline__ int64_t query_row(const AttnArgs& a, int b, int kvh, int vl) {
+    const int c = vl / a.g;
+    return ((int64_t)b * a.ncols + c) * a.hq + kvh * a.g + (vl - c * a.g);
+}
+
 template <int D, int KB, int VB, int G, bool QJL>
 __global__ __launch_bounds__(64 * split_waves(D, KB, VB, QJL))
 __attribute__((amdgpu_waves_per_eu(split_waves(D, KB, VB, QJL) / 4)))
@@ -335,7 +346,9 @@ void split_kernel(AttnArgs a) {
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
     const int t_beg = split * (int)a.split_tokens;
     const int t_end = (t_beg + (int)a.split_tokens < ctx) ? t_beg + (int)a.split_tokens : ctx;
-    const int h0 = kvh * a.g + chunk * G;
+    const int vl0 = chunk * G;  // first row of this block (see query_row)
+    // tokens a row may see: ctx for the last column, fewer for earlier ones
+    const int ctx_min = ctx - (a.ncols - 1 - vl0 / a.g);  // the block's first row sees the fewest
     const int64_t kvrow = ((int64_t)b * a.hkv + kvh) * a.ctx_cap;
     const uint8_t* kcodes = a.k_codes + kvrow * C::RBK;
     const uint8_t* vcodes = a.v_codes + kvrow * C::RBV;
@@ -344,9 +357,9 @@ void split_kernel(AttnArgs a) {
     const uint8_t* gmb = QJL ? reinterpret_cast<const uint8_t*>(a.k_gamma + kvrow) : nullptr;
     const uint32_t last = t_end > 0 ? (uint32_t)(t_end - 1) : 0u;
 
-    // This chunk's query heads are rotated here (the Q-side transform): lane
+    // This chunk's query rows are rotated here (the Q-side transform): lane
     // group hl = wave * QVPW + lane / QLPV of the first waves holds dims
-    // [8 gl, 8 gl + 8) of head h0 + hl.  Their loads go out first, so the
+    // [8 gl, 8 gl + 8) of row vl0 + hl.  Their loads go out first, so the
     // transform waits for them alone, then the first tile's loads.
     constexpr int QLPV = D / 8, QVPW = 64 / QLPV;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -355,7 +368,7 @@ void split_kernel(AttnArgs a) {
     float qx[8];
     if (qwave) {
         if (qhl < G) {
-            const int64_t e0 = ((int64_t)b * a.hq + h0 + qhl) * D + qgl * 8;
+            const int64_t e0 = query_row(a, b, kvh, vl0 + qhl) * D + qgl * 8;
             if (a.q_dtype == TQ_F32) load8<0>(static_cast<const float*>(a.q) + e0, qx);
             else if (a.q_dtype == TQ_F16) load8<1>(static_cast<const uint16_t*>(a.q) + e0, qx);
             else load8<2>(static_cast<const uint16_t*>(a.q) + e0, qx);
@@ -448,6 +461,7 @@ void split_kernel(AttnArgs a) {
     // KE = 4: d0 d1 d2 d3 d0 d1 d2 d3); likewise the QJL projection
     const int hh = n & 7;
     const bool lo_col = n >= 8, head_ok = hh < G;
+    const int ctx_row = ctx - (a.ncols - 1 - (vl0 + hh) / a.g);  // tokens row hh may see
     half8_t bq[C::KSTEPS];
     float qinv;
     {
@@ -462,11 +476,11 @@ void split_kernel(AttnArgs a) {
                 qv[ks][i] = head_ok ? x : 0.0f;
                 amax = fmaxf(amax, fabsf(qv[ks][i]));
             }
-        const float* qp = a.qproj + ((int64_t)b * a.hq + h0) * m;
+        const float* qp = a.qproj + query_row(a, b, kvh, vl0 + (head_ok ? hh : 0)) * m;
         if constexpr (QJL) {
             for (int ks = 0; ks < (m >> 5); ++ks)
                 for (int j = 0; j < 8; ++j)
-                    amax = fmaxf(amax, head_ok ? fabsf(qp[hh * m + grp * (m >> 2) + 8 * ks + j]) : 0.0f);
+                    amax = fmaxf(amax, head_ok ? fabsf(qp[grp * (m >> 2) + 8 * ks + j]) : 0.0f);
         }
         amax = wave_max(amax);
         float sc = 1.0f;
@@ -500,7 +514,7 @@ void split_kernel(AttnArgs a) {
                     half8_t x8;
                     for (int j = 0; j < 8; ++j) {
                         // the sign operand carries 16*gamma, so scale by sc only
-                        const float v = (head_ok ? qp[hh * m + grp * (m >> 2) + 8 * ks + j] : 0.0f) * sc;
+                        const float v = (head_ok ? qp[grp * (m >> 2) + 8 * ks + j] : 0.0f) * sc;
                         const _Float16 hi = (_Float16)v;
                         x8[j] = lo_col ? (_Float16)(v - (float)hi) : hi;
                     }
@@ -623,6 +637,8 @@ void split_kernel(AttnArgs a) {
         const int rem = t_end - t0;
         float dsc[4][4];
         float lmax = -INFINITY;
+        // this lane's row sees tokens below row_end; every row of the block
+        // sees the whole tile unless it reaches past ctx_min or t_end
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float4 kq = *reinterpret_cast<const float4*>(knq + 16 * j + 4 * grp);
@@ -631,8 +647,9 @@ void split_kernel(AttnArgs a) {
             dsc[j][2] = fmaf(sacc[j][2], kq.z, -m_ref);
             dsc[j][3] = fmaf(sacc[j][3], kq.w, -m_ref);
         }
-        int lim = rem - 4 * grp;  // token 16j + 4grp + v is valid iff 16j + v < lim
-        if (rem < 64) {
+        const int row_end = ctx_row < t_end ? ctx_row : t_end;
+        int lim = row_end - t0 - 4 * grp;  // token 16j + 4grp + v is valid iff 16j + v < lim
+        if ((ctx_min < t_end ? ctx_min : t_end) - t0 < 64) {
             // keeps the compares inside this (last-tile) branch
             asm volatile("" : "+v"(lim));
 #pragma unroll
@@ -673,14 +690,17 @@ void split_kernel(AttnArgs a) {
             }
             tmax = fmaxf(tmax, xor_lane<16>(tmax));
             tmax = fmaxf(tmax, xor_lane<32>(tmax));
+            // a row that has seen no token yet (an early column of a
+            // multi-query block) keeps max -inf and weight zero
             const float mnew = fmaxf(m_ref, tmax);
-            const float alpha = fast_exp2(m_ref - mnew);
+            const bool none = mnew == -INFINITY;
+            const float alpha = none ? 1.0f : fast_exp2(m_ref - mnew);
             m_ref = mnew;
             l_lane *= alpha;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) dsc[j][v] = sv[j][v] - mnew;
+                for (int v = 0; v < 4; ++v) dsc[j][v] = none ? -INFINITY : sv[j][v] - mnew;
             if (grp == 0) hfac[n] = alpha * vfac;
             wave_sync();
             const float4 f4 = *reinterpret_cast<const float4*>(hfac + 4 * grp);
@@ -854,8 +874,6 @@ void split_kernel(AttnArgs a) {
         }
     }
     __syncthreads();
-    float* part = a.part + (((int64_t)b * a.hq + h0) * a.splits + split) * (D + 2);
-    const int64_t hstride = (int64_t)a.splits * (D + 2);
     for (int e = tid; e < G * (D + 2); e += C::NT) {
         const int h = e / (D + 2), i = e - h * (D + 2);
         float mx = -INFINITY;
@@ -874,7 +892,7 @@ void split_kernel(AttnArgs a) {
                 val = fmaf(mrg[(w * G + h) * (D + 2) + i], exp2f(mw - mx), val);
             }
         }
-        part[h * hstride + i] = val;
+        a.part[(query_row(a, b, kvh, vl0 + h) * a.splits + split) * (D + 2) + i] = val;
     }
 }
 
@@ -947,7 +965,7 @@ template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     constexpr int LPV = D / 8, HPB = 256 / LPV;  // lanes per head, heads per block
     const int tid = threadIdx.x, gl = tid & (LPV - 1);
-    const int heads = a.batch * a.hq;
+    const int heads = a.batch * a.ncols * a.hq;
     const int bh = blockIdx.x * HPB + tid / LPV;
     const bool valid = bh < heads;  // uniform inside a lane group
     float x[8];

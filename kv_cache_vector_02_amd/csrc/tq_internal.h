@@ -54,8 +54,9 @@ struct AttnArgs {
     const void* q;
     int q_dtype;
     int batch, hq, hkv, g;   // g = hq / hkv
-    int heads_per_chunk;     // G: query heads handled by one block
-    int chunks;              // g / G
+    int ncols;               // query columns per sequence (1: single-token decode)
+    int heads_per_chunk;     // G: query rows (of the g * ncols of a kv head) per block
+    int chunks;              // g * ncols / G
     const int32_t* ctx_len;
     int64_t ctx_cap;
     const uint8_t* k_codes;
@@ -89,7 +90,7 @@ hipError_t launch_encode_pair(const EncodeArgs& k, const EncodeArgs& v, int dtyp
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 enum AttnStage { ATTN_PREPARE = 1, ATTN_SCAN = 2, ATTN_COMBINE = 4, ATTN_ALL = 7, ATTN_WINDOW = 8 };
 hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s);
-void attn_plan(int batch, int hkv, int g, int64_t ctx_cap, int d, int kb, int vb, bool qjl, int* splits,
+void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int vb, bool qjl, int* splits,
                int64_t* split_tokens, int* heads_per_chunk);
 template <int D, int KB>
 hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s);
