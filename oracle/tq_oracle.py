@@ -356,8 +356,37 @@ def qjl_term(q: np.ndarray, qjl_packed: np.ndarray, norms16: np.ndarray,
     return (qhat @ sgn.T) * coef[None, :]
 
 
+SCORE_PLAIN, SCORE_SHARPEN, SCORE_SOFTEN = 0, 1, 2
+
+
+def score_factor(mode: int, n_tokens: int, sqnr: float, n0: int = 2048) -> float:
+    """The factor alpha(N) multiplying every attention score of a query that
+    attends over N tokens ([P1] v1.5.2 "핵심 변경" item 3 and "Attention
+    Sharpening — 이론 & 동적 α 공식": quantisation noise in K flattens the
+    softmax; the dynamic factor compensates, with N the current KV token count
+    and N0 = 2048 the reference context):
+
+      sharpen: alpha = 1 + c sqrt(ln N),  c = 1 / (2 SQNR_eff sqrt(ln N0));
+      soften (item 11, the MMSE softening used at head_dim 64):
+               alpha = SQNR / (SQNR + sqrt(ln N / ln N0));
+      plain:   alpha = 1.
+    N <= 1 gives ln N <= 0, read as 0 (alpha = 1): a single token's weight is 1
+    whatever the factor.  The pages do not print SQNR_eff per cache type, so it
+    is the caller's parameter.
+    """
+    if mode == SCORE_PLAIN or n_tokens <= 1:
+        return 1.0
+    ln_n, ln_n0 = math.log(n_tokens), math.log(n0)
+    if mode == SCORE_SHARPEN:
+        return 1.0 + math.sqrt(ln_n) / (2.0 * sqnr * math.sqrt(ln_n0))
+    if mode == SCORE_SOFTEN:
+        return sqnr / (sqnr + math.sqrt(ln_n / ln_n0))
+    raise ValueError("unknown score mode")
+
+
 def attention(q: np.ndarray, k_codes, k_norms, v_codes, v_norms, kc: Codec, vc: Codec,
-              scale: float, k_qjl=None, k_gamma=None, S=None, k_win=None, v_win=None) -> np.ndarray:
+              scale: float, k_qjl=None, k_gamma=None, S=None, k_win=None, v_win=None,
+              alpha: float = 1.0, sparse_v: float = 0.0) -> np.ndarray:
     """Exact softmax attention of one query group over one decoded cache.
 
     Decompress-then-attend ([P3] "결과 — 피크 VRAM" describes the reference
@@ -369,6 +398,13 @@ def attention(q: np.ndarray, k_codes, k_norms, v_codes, v_norms, kc: Codec, vc: 
     tokens are kept uncompressed and appended to the decompressed ones before
     attention): k_win, v_win [w][d] are exact keys and values that join the
     softmax after the decoded tokens, with s = scale <q, k_win_t> (no QJL term).
+
+    Score factor: every score (QJL part included) is multiplied by alpha
+    (see score_factor).  Sparse V (the sparse V dequantisation of [P3] "왜 이걸
+    보게 됐나": value rows whose softmax weight is below 1e-6 are not
+    dequantised): with sparse_v = tau > 0 a token whose weight relative to the
+    largest one, exp(s_t - max_u s_u), is below tau adds nothing to the output,
+    while the softmax denominator keeps every token.
 
     q [n_q][d]; caches [ctx][...]; returns [n_q][d] float64.  With no token at
     all the output is zero.
@@ -389,12 +425,12 @@ def attention(q: np.ndarray, k_codes, k_norms, v_codes, v_norms, kc: Codec, vc: 
     if w:
         parts_s.append(scale * (q @ np.asarray(k_win, dtype=np.float64).T))
         parts_v.append(np.asarray(v_win, dtype=np.float64))
-    s = np.concatenate(parts_s, axis=1)
+    s = alpha * np.concatenate(parts_s, axis=1)
     V = np.concatenate(parts_v, axis=0)
     s = s - s.max(axis=1, keepdims=True)
-    p = np.exp(s)
-    p /= p.sum(axis=1, keepdims=True)
-    return p @ V
+    e = np.exp(s)
+    w = np.where(e < sparse_v, 0.0, e) if sparse_v > 0 else e
+    return (w / e.sum(axis=1, keepdims=True)) @ V
 
 
 def gqa_attention(q, ctx_len, k_codes, k_norms, v_codes, v_norms, kc, vc, scale,
@@ -426,7 +462,8 @@ def gqa_attention(q, ctx_len, k_codes, k_norms, v_codes, v_norms, kc, vc, scale,
 
 
 def mq_attention(q, ctx_len, k_codes, k_norms, v_codes, v_norms, kc, vc, scale,
-                 k_qjl=None, k_gamma=None, S=None, cols=None):
+                 k_qjl=None, k_gamma=None, S=None, cols=None, score_mode=SCORE_PLAIN, sqnr=1.0,
+                 n0=2048, sparse_v=0.0):
     """Multi-query decode over the packed cache: q [B][C][Hq][d] holds the last C
     query tokens (columns) of each sequence, whose keys and values are already
     in the cache ([P1] v1.1.0 "버그 수정": prompt evaluation runs ncols = 2 query
@@ -438,7 +475,9 @@ def mq_attention(q, ctx_len, k_codes, k_norms, v_codes, v_norms, kc, vc, scale,
 
     ``cols`` optionally restricts the computation to a list of (b, c, h)
     triples; the result then has one row per triple.  Returns [B*C*Hq][d] in
-    (b, c, h) order otherwise.
+    (b, c, h) order otherwise.  score_mode / sqnr / n0 select the score factor
+    alpha(N) of each column, N being the tokens it attends over; sparse_v is
+    attention()'s threshold.
     """
     B, C, Hq, d = q.shape
     Hkv = k_codes.shape[1]
@@ -452,7 +491,8 @@ def mq_attention(q, ctx_len, k_codes, k_norms, v_codes, v_norms, kc, vc, scale,
         if kc.qjl_m:
             args = dict(k_qjl=k_qjl[b, kh, :n], k_gamma=k_gamma[b, kh, :n], S=S)
         out[row] = attention(np.asarray(q[b, c, h], dtype=np.float64)[None, :], k_codes[b, kh, :n],
-                             k_norms[b, kh, :n], v_codes[b, kh, :n], v_norms[b, kh, :n], kc, vc, scale, **args)[0]
+                             k_norms[b, kh, :n], v_codes[b, kh, :n], v_norms[b, kh, :n], kc, vc, scale,
+                             alpha=score_factor(score_mode, n, sqnr, n0), sparse_v=sparse_v, **args)[0]
     return out
 
 

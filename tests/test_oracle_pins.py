@@ -409,6 +409,100 @@ def test_mq_single_column_is_decode():
                                   o.gqa_attention(q[:, 0], ctx, kcodes, kn, vcodes, vn, kc, vc, 0.1))
 
 
+def test_score_factor_closed_forms(golden_dir):
+    """alpha(N): sharpening gives 1 + 1/(2 SQNR) at N = N0 and grows as
+    sqrt(ln N / ln N0) above 1; softening gives SQNR/(SQNR + 1) at N0 and
+    shrinks; both are 1 for N <= 1 and tend to 1 as SQNR grows."""
+    n0 = int(_pages(golden_dir)["sharpen_n0"])
+    for sq in (2.0, 11.6, 30.0):
+        assert o.score_factor(o.SCORE_SHARPEN, n0, sq) == pytest.approx(1 + 1 / (2 * sq), rel=1e-15)
+        assert o.score_factor(o.SCORE_SOFTEN, n0, sq) == pytest.approx(sq / (sq + 1), rel=1e-15)
+        for n in (3, 100, 262144, 1 << 20):
+            ratio = (o.score_factor(o.SCORE_SHARPEN, n, sq) - 1) / (1 / (2 * sq))
+            assert ratio == pytest.approx(math.sqrt(math.log(n) / math.log(n0)), rel=1e-13)
+        for n in (0, 1):
+            assert o.score_factor(o.SCORE_SHARPEN, n, sq) == 1.0 == o.score_factor(o.SCORE_SOFTEN, n, sq)
+        ns = [2, 64, 2048, 65536, 1 << 20]
+        sh = [o.score_factor(o.SCORE_SHARPEN, n, sq) for n in ns]
+        so = [o.score_factor(o.SCORE_SOFTEN, n, sq) for n in ns]
+        assert all(a < b for a, b in zip(sh, sh[1:])) and all(a > b for a, b in zip(so, so[1:]))
+    assert o.score_factor(o.SCORE_SHARPEN, 5000, 1e12) == pytest.approx(1.0, abs=1e-11)
+    assert o.score_factor(o.SCORE_PLAIN, 5000, 3.0) == 1.0
+
+
+def test_sharpening_matches_the_pages_range(golden_dir):
+    """The page's figures: over 2048 -> 262144 tokens the factor moves by about
+    0.012 while staying in 1.007-1.048.  With the top of that range reached at
+    262144 tokens, the sqrt(ln N) law gives a move of 0.0105; a law linear in
+    ln N would give 0.019, outside 'about 0.012'."""
+    pages = _pages(golden_dir)
+    lo, hi = (float(v) for v in pages["sharpen_alpha_range"].split())
+    delta = float(pages["sharpen_delta_2048_262144"])
+    growth = math.sqrt(math.log(262144) / math.log(2048))
+    sq = growth / (2 * (hi - 1))  # SQNR_eff with alpha(262144) = 1.048
+    a0, a1 = o.score_factor(o.SCORE_SHARPEN, 2048, sq), o.score_factor(o.SCORE_SHARPEN, 262144, sq)
+    assert a1 == pytest.approx(hi, rel=1e-12)
+    assert lo <= a0 < a1 <= hi
+    assert abs((a1 - a0) - delta) < 0.003
+    linear = (hi - 1) * (1 - math.log(2048) / math.log(262144))
+    assert abs(linear - delta) > 0.005
+
+
+def _sharpen_case(seed=24, d=64, n=30):
+    kc, vc = o.Codec(3, d, 9), o.Codec(3, d, 9)
+    rng = np.random.default_rng(seed)
+    ek, ev = o.encode(rng.standard_normal((n, d)) * 4, kc), o.encode(rng.standard_normal((n, d)), vc)
+    q = rng.standard_normal((2, d))
+    return kc, vc, ek, ev, q
+
+
+def test_score_factor_enters_as_a_scale():
+    """attention(alpha = a) is plain attention at scale a * scale; in
+    mq_attention every column uses alpha of the tokens it sees."""
+    kc, vc, ek, ev, q = _sharpen_case()
+    a = 1.37
+    np.testing.assert_allclose(
+        o.attention(q, ek["codes"], ek["norms"], ev["codes"], ev["norms"], kc, vc, 0.2, alpha=a),
+        o.attention(q, ek["codes"], ek["norms"], ev["codes"], ev["norms"], kc, vc, 0.2 * a), rtol=1e-13)
+    C, n, sq = 3, 30, 4.0
+    qq = np.random.default_rng(25).standard_normal((1, C, 2, kc.d))
+    kcodes, kn = ek["codes"][None, None], ek["norms"][None, None]
+    vcodes, vn = ev["codes"][None, None], ev["norms"][None, None]
+    got = o.mq_attention(qq, [n], kcodes, kn, vcodes, vn, kc, vc, 0.2, score_mode=o.SCORE_SHARPEN,
+                         sqnr=sq).reshape(C, 2, -1)
+    for c in range(C):
+        nc = n - (C - 1 - c)
+        want = o.attention(qq[0, c], ek["codes"][:nc], ek["norms"][:nc], ev["codes"][:nc], ev["norms"][:nc], kc,
+                           vc, 0.2 * (1 + math.sqrt(math.log(nc)) / (2 * sq * math.sqrt(math.log(2048)))))
+        np.testing.assert_allclose(got[c], want, rtol=1e-12)
+    # sharpening concentrates the weights: the output moves toward the top value
+    plain = o.mq_attention(qq, [n], kcodes, kn, vcodes, vn, kc, vc, 0.2).reshape(C, 2, -1)
+    assert np.abs(got - plain).max() > 1e-4
+
+
+def test_sparse_v_closed_forms(golden_dir):
+    """Sparse V: tau = 0 is plain attention; tau = 1 keeps only the top token
+    (o = V_top / sum_t exp(s_t - s_top)); in general the output moves by at
+    most the dropped weight times the dropped values' norms."""
+    kc, vc, ek, ev, q = _sharpen_case(seed=26, n=40)
+    args = (ek["codes"], ek["norms"], ev["codes"], ev["norms"], kc, vc, 0.5)
+    plain = o.attention(q, *args)
+    np.testing.assert_array_equal(o.attention(q, *args, sparse_v=0.0), plain)
+    K, V = o.decode(ek["codes"], ek["norms"], kc), o.decode(ev["codes"], ev["norms"], vc)
+    s = 0.5 * q @ K.T
+    top = np.argmax(s, axis=1)
+    want = V[top] / np.exp(s - s.max(axis=1, keepdims=True)).sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(o.attention(q, *args, sparse_v=1.0), want, rtol=1e-13)
+    tau = float(_pages(golden_dir)["sparse_v_threshold"])
+    for t in (tau, 1e-3, 0.05):
+        got = o.attention(q, *args, sparse_v=t)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        bound = np.where(e < t, p, 0.0) @ np.linalg.norm(V, axis=1)
+        assert np.all(np.linalg.norm(got - plain, axis=1) <= bound + 1e-15)
+    assert np.abs(o.attention(q, *args, sparse_v=0.05) - plain).max() > 1e-6
+
+
 def test_window_is_concatenation():
     """Tokens moved from the packed cache into the residual window (as their
     decoded values) leave the output unchanged: the window joins the same softmax."""
