@@ -220,6 +220,23 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
                              out_mq, ws_mq)
 
     ms_mq = timed_loop(mq, steps, max(warmup // 4, 1), torch)
+
+    # the softmax-side switches on the same step (tq_attn_decode_ex): sparse V
+    # at the pages' 1e-6, and dynamic sharpening (SQNR_eff 11.6)
+    q1 = q.view(B, 1, Hq, d)
+    out1 = out.view(B, 1, Hq, d)
+    sparse_opts = tq.tq_attn_opts(tq.TQ_SCORE_PLAIN, 0.0, 0, 1e-6)
+    sharp_opts = tq.tq_attn_opts(tq.TQ_SCORE_SHARPEN, 11.6, 0, 0.0)
+
+    def step_ex(opts):
+        def f(i, ev=None):
+            c = caches[i % replicas]
+            tq.tq_attn_decode_ex(kc, vc, q1, ctx_len, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], scale,
+                                 out1, ws, opts)
+        return f
+
+    ms_sparse = timed_loop(step_ex(sparse_opts), steps, max(warmup // 4, 1), torch)
+    ms_sharp = timed_loop(step_ex(sharp_opts), steps, max(warmup // 4, 1), torch)
     token_heads = B * Hkv * ctx
     per_token_head = (kc.code_bytes + 2) + (vc.code_bytes + 2)  # 100 B
     cache_bytes = token_heads * per_token_head
@@ -251,6 +268,12 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
             "ms_per_column": ms_mq / C,
             "single_column_ms_per_step": ms,
             "gbs_cache_bytes": cache_bytes / (ms_mq * 1e-3) / 1e9,
+        },
+        "switches": {
+            "workload": "the same step through tq_attn_decode_ex with one softmax-side switch on",
+            "sparse_v_1e-6_ms_per_step": ms_sparse,
+            "sharpen_sqnr_11.6_ms_per_step": ms_sharp,
+            "plain_ms_per_step": ms,
         },
         "append": {
             "workload": "one new token per (sequence, kv head) appended to the K4 and V2 caches (one tq_append call)",

@@ -313,6 +313,55 @@ int tq_attn_decode_mq(const tq_codec *kc, const tq_codec *vc,
                       void *stream);
 
 /*
+ * Optional softmax-side switches of decode attention, all off in a zeroed
+ * struct (tq_attn_decode_ex with opts == NULL is tq_attn_decode_mq).
+ *
+ *   score_mode  TQ_SCORE_PLAIN: scores as in tq_attn_decode.
+ *               TQ_SCORE_SHARPEN: every score of a query row that attends over
+ *               N tokens is multiplied by alpha(N) = 1 + c sqrt(ln N),
+ *               c = 1 / (2 sqnr sqrt(ln N0)) -- the dynamic attention
+ *               sharpening of [P1] v1.5.2 ("핵심 변경" item 3, "Attention
+ *               Sharpening — 이론 & 동적 α 공식"), which offsets the flattening
+ *               of the softmax by K quantisation noise.
+ *               TQ_SCORE_SOFTEN: alpha(N) = sqnr / (sqnr + sqrt(ln N / ln N0)),
+ *               the MMSE softening of [P1] v1.5.2 item 11.
+ *               alpha = 1 for N <= 1.  N counts the row's own tokens (its
+ *               column's causal limit in multi-query calls).
+ *   sqnr        SQNR_eff > 0 of the key cache (the pages print no value per
+ *               type; the caller picks it); ignored when plain.
+ *   ref_tokens  N0 >= 2; 0 means 2048 (the pages' reference context).
+ *   sparse_v    0 = off; tau in (0, 1]: a token whose softmax weight relative to
+ *               the largest weight is below tau adds nothing to the output, the
+ *               denominator still counting it -- the sparse V dequantisation of
+ *               [P3] "왜 이걸 보게 됐나" (weights below 1e-6 skip their V).  The
+ *               kernels compare against their running maximum, which never
+ *               exceeds the true one, so they drop a subset of those tokens; a
+ *               32-token step whose weights are all dropped skips its V work.
+ */
+enum { TQ_SCORE_PLAIN = 0, TQ_SCORE_SHARPEN = 1, TQ_SCORE_SOFTEN = 2 };
+typedef struct {
+    int32_t score_mode;
+    float sqnr;
+    int32_t ref_tokens;
+    float sparse_v;
+} tq_attn_opts;
+
+/*
+ * tq_attn_decode_ex -- tq_attn_decode_mq with the switches above (opts may be
+ * NULL).  Errors: those of tq_attn_decode_mq, and TQ_EINVAL for an unknown
+ * score_mode, sqnr not finite and positive when used, ref_tokens of 1 or
+ * negative, or sparse_v outside [0, 1].  Workspace: as tq_attn_decode_mq.
+ */
+int tq_attn_decode_ex(const tq_codec *kc, const tq_codec *vc,
+                      const void *q, int q_dtype, int batch, int n_cols, int n_q_heads, int n_kv_heads,
+                      const int32_t *ctx_len, int64_t ctx_cap,
+                      const uint8_t *k_codes, const uint16_t *k_norms,
+                      const uint8_t *k_qjl, const uint16_t *k_gamma, const float *qjl_S,
+                      const uint8_t *v_codes, const uint16_t *v_norms,
+                      float scale, const tq_attn_opts *opts, float *out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The three launches of tq_attn_decode as separate calls (same arguments, same
  * checks, same workspace, which carries the state between them), for callers
  * that time or schedule the stages themselves:

@@ -26,7 +26,7 @@ EXPORTS = (
     "tq_codebook", "tq_encode", "tq_encode_kv", "tq_prefill", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
     "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes", "tq_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror", "tq_stream_read",
-    "tq_attn_decode_noalloc", "tq_attn_decode_mq",
+    "tq_attn_decode_noalloc", "tq_attn_decode_mq", "tq_attn_decode_ex",
 )
 TQ_OP_ATTN_DECODE, TQ_OP_ATTN_DECODE_RW, TQ_OP_IP_SEARCH, TQ_OP_ATTN_DECODE_MQ = 1, 2, 3, 4
 TQ_MAX_QUERY_COLS = 64
@@ -63,6 +63,20 @@ class tq_codec(ctypes.Structure):
         return [-1.0 if (self.sign_mask[i >> 5] >> (i & 31)) & 1 else 1.0 for i in range(self.d)]
 
 
+TQ_SCORE_PLAIN, TQ_SCORE_SHARPEN, TQ_SCORE_SOFTEN = 0, 1, 2
+
+
+class tq_attn_opts(ctypes.Structure):
+    """Mirror of the C struct tq_attn_opts (softmax-side switches, all off when zero)."""
+
+    _fields_ = [
+        ("score_mode", ctypes.c_int32),
+        ("sqnr", ctypes.c_float),
+        ("ref_tokens", ctypes.c_int32),
+        ("sparse_v", ctypes.c_float),
+    ]
+
+
 class TQError(RuntimeError):
     def __init__(self, code: int, where: str):
         super().__init__(f"{where}: {strerror(code)} ({code})")
@@ -96,6 +110,8 @@ def _load():
         "tq_stream_read": (I, [P, SZ, P, P]),
         "tq_attn_decode_noalloc": (I, [CP, CP, P, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P]),
         "tq_attn_decode_mq": (I, [CP, CP, P, I, I, I, I, I, P, I64, P, P, P, P, P, P, P, F, P, P, SZ, P]),
+        "tq_attn_decode_ex": (I, [CP, CP, P, I, I, I, I, I, P, I64, P, P, P, P, P, P, P, F,
+                                  ctypes.POINTER(tq_attn_opts), P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -373,6 +389,27 @@ def tq_attn_decode_mq(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torc
                                   _ptr(qjl_S), _ptr(v_codes), _ptr(v_norms), ctypes.c_float(scale), _ptr(out),
                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q)),
            "tq_attn_decode_mq")
+
+
+def tq_attn_decode_ex(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.Tensor,
+                      k_codes: torch.Tensor, k_norms: torch.Tensor, v_codes: torch.Tensor, v_norms: torch.Tensor,
+                      scale: float, out: torch.Tensor, workspace: torch.Tensor, opts: tq_attn_opts | None = None,
+                      k_qjl: torch.Tensor | None = None, k_gamma: torch.Tensor | None = None,
+                      qjl_S: torch.Tensor | None = None, stream=None) -> None:
+    """tq_attn_decode_mq with softmax-side switches (tq_attn_opts; None = off):
+    q and out [B][C][Hq][d]."""
+    if q.dim() != 4 or out.dim() != 4:
+        raise ValueError("q and out must be [B][C][Hq][d]")
+    B, C, Hq, d = q.shape
+    _check_cache(kc, vc, q.view(B, C * Hq, d), ctx_len, k_codes, k_norms, v_codes, v_norms, out.view(B, C * Hq, -1),
+                 k_qjl, k_gamma, qjl_S)
+    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
+    _check(_lib.tq_attn_decode_ex(ctypes.byref(kc), ctypes.byref(vc), _ptr(q), _DTYPES[q.dtype], B, C, Hq, Hkv,
+                                  _ptr(ctx_len), cap, _ptr(k_codes), _ptr(k_norms), _ptr(k_qjl), _ptr(k_gamma),
+                                  _ptr(qjl_S), _ptr(v_codes), _ptr(v_norms), ctypes.c_float(scale),
+                                  ctypes.byref(opts) if opts is not None else None, _ptr(out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream, q)),
+           "tq_attn_decode_ex")
 
 
 def tq_attn_decode_noalloc(kc: tq_codec, vc: tq_codec, q: torch.Tensor, ctx_len: torch.Tensor,

@@ -309,7 +309,7 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
                       const uint8_t* k_codes, const uint16_t* k_norms, const uint8_t* k_qjl, const uint16_t* k_gamma,
                       const float* qjl_S, const uint8_t* v_codes, const uint16_t* v_norms, const void* k_win,
                       const void* v_win, int win_dtype, const int32_t* win_len, int win_cap, float scale, float* out,
-                      void* workspace, size_t workspace_bytes, tqi::AttnArgs* a) {
+                      void* workspace, size_t workspace_bytes, tqi::AttnArgs* a, const tq_attn_opts* opts = nullptr) {
     int splits, G;
     int64_t per;
     const int rc = attn_check(kc, vc, batch, ncols, n_q_heads, n_kv_heads, ctx_cap, &splits, &per, &G);
@@ -323,6 +323,13 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
     if (kc->qjl_m > 0 && (!k_qjl || !k_gamma || !qjl_S || !aligned(k_qjl, 4) || !aligned(k_gamma, 2)))
         return TQ_EINVAL;
     if (!isfinite(scale)) return TQ_EINVAL;
+    if (opts) {
+        if (opts->score_mode < TQ_SCORE_PLAIN || opts->score_mode > TQ_SCORE_SOFTEN) return TQ_EINVAL;
+        if (opts->score_mode != TQ_SCORE_PLAIN && !(isfinite(opts->sqnr) && opts->sqnr > 0.0f)) return TQ_EINVAL;
+        if (opts->ref_tokens != 0 && opts->ref_tokens < 2) return TQ_EINVAL;
+        if (!(opts->sparse_v >= 0.0f && opts->sparse_v <= 1.0f)) return TQ_EINVAL;
+        if (win_cap > 0 && (opts->score_mode != TQ_SCORE_PLAIN || opts->sparse_v > 0.0f)) return TQ_EUNSUPPORTED;
+    }
     if (win_cap < 0) return TQ_EINVAL;
     if (win_cap > 0) {
         if (win_dtype != TQ_F32 && win_dtype != TQ_F16 && win_dtype != TQ_BF16) return TQ_EINVAL;
@@ -354,6 +361,14 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
     a->v_codes = v_codes;
     a->v_norms = v_norms;
     a->scale = scale;
+    a->score_mode = opts ? opts->score_mode : TQ_SCORE_PLAIN;
+    a->sqnr = opts ? opts->sqnr : 1.0f;
+    {
+        const double n0 = opts && opts->ref_tokens ? opts->ref_tokens : 2048.0;
+        a->inv_ln_n0 = (float)(1.0 / log(n0));
+        a->sharp_c = (float)(1.0 / (2.0 * (double)a->sqnr * sqrt(log(n0))));
+    }
+    a->sparse_log2 = opts && opts->sparse_v > 0.0f ? (float)log2((double)opts->sparse_v) : -INFINITY;
     a->out = out;
     const size_t heads = (size_t)batch * ncols * n_q_heads;
     float* ws = (float*)workspace;
@@ -450,6 +465,19 @@ int tq_attn_decode_rw(const tq_codec* kc, const tq_codec* vc, const void* q, int
                               scale, out, workspace, workspace_bytes, &a);
     if (rc != TQ_OK) return rc;
     return finish(tqi::launch_attn(a, tqi::ATTN_ALL | tqi::ATTN_WINDOW, (hipStream_t)stream));
+}
+
+int tq_attn_decode_ex(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch, int n_cols,
+                      int n_q_heads, int n_kv_heads, const int32_t* ctx_len, int64_t ctx_cap, const uint8_t* k_codes,
+                      const uint16_t* k_norms, const uint8_t* k_qjl, const uint16_t* k_gamma, const float* qjl_S,
+                      const uint8_t* v_codes, const uint16_t* v_norms, float scale, const tq_attn_opts* opts,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    tqi::AttnArgs a;
+    const int rc = attn_setup(kc, vc, q, q_dtype, batch, n_cols, n_q_heads, n_kv_heads, ctx_len, ctx_cap, k_codes,
+                              k_norms, k_qjl, k_gamma, qjl_S, v_codes, v_norms, nullptr, nullptr, 0, nullptr, 0, scale,
+                              out, workspace, workspace_bytes, &a, opts);
+    if (rc != TQ_OK) return rc;
+    return finish(tqi::launch_attn(a, tqi::ATTN_ALL, (hipStream_t)stream));
 }
 
 int tq_attn_decode_mq(const tq_codec* kc, const tq_codec* vc, const void* q, int q_dtype, int batch, int n_cols,

@@ -49,6 +49,28 @@ __device__ __forceinline__ void static_for(F&& f) {
 constexpr float kLog2e = 1.4426950408889634f;
 
 
+// Score factor alpha(N) of a query row that attends over n tokens (1 when the
+// mode is plain or n <= 1): the dynamic sharpening and MMSE softening of the
+// llama.cpp fork's README ("TurboQuant KV 캐시 압축 for llama.cpp", v1.5.2
+// "Attention Sharpening — 이론 & 동적 α 공식" and "핵심 변경" item 11).
+__device__ __forceinline__ float score_factor(const AttnArgs& a, int n) {
+    if (a.score_mode == 0 || n <= 1) return 1.0f;
+    const float ln_n = logf((float)n);
+    if (a.score_mode == 1) return 1.0f + a.sharp_c * sqrtf(ln_n);
+    return a.sqnr / (a.sqnr + sqrtf(ln_n * a.inv_ln_n0));
+}
+
+// Tokens query row `row` ((b * ncols + c) * hq + h) attends over.
+__device__ __forceinline__ int row_tokens(const AttnArgs& a, int64_t row) {
+    const int64_t bc = row / a.hq;
+    const int b = (int)(bc / a.ncols), c = (int)(bc - (int64_t)b * a.ncols);
+    const int cap = (int)a.ctx_cap;
+    int ctx = a.ctx_len[b];
+    ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+    const int n = ctx - (a.ncols - 1 - c);
+    return n > 0 ? n : 0;
+}
+
 // ----------------------------------------------------------------- qprep ----
 // QJL keys only: per query head, the projection S H(D_K q) / sqrt(d) of the
 // rotated query (the Q_wht2 side of the fused query pass), pre-scaled by
@@ -79,7 +101,8 @@ __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) rot[grp][gl * 8 + e] = v[e];
     __syncthreads();
-    const float ps = a.scale * kLog2e * sqrtf(1.57079632679489662f) / ((float)m * sqrtf((float)D));
+    const float ps = a.scale * kLog2e * sqrtf(1.57079632679489662f) / ((float)m * sqrtf((float)D)) *
+                     (valid ? score_factor(a, row_tokens(a, head)) : 1.0f);
     for (int j = gl; j < m; j += LPV) {
         const float* srow = a.S + (int64_t)j * D;
         float acc = 0.0f;
@@ -401,7 +424,11 @@ void split_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qx[e] = as_f(as_u(qx[e]) ^ (((sbits >> e) & 1u) << 31));
         fwht<QLPV>(qx, qgl);
-        const float qs = a.scale * kLog2e / (float)D;
+        float qs = a.scale * kLog2e / (float)D;
+        if (a.score_mode != 0 && qhl < G) {
+            const int nr = ctx - (a.ncols - 1 - (vl0 + qhl) / a.g);  // tokens this row attends over
+            qs *= score_factor(a, nr > 0 ? nr : 0);
+        }
         if (qhl < G) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) qr[qhl * D + qgl * 8 + e] = qx[e] * qs;
@@ -535,6 +562,7 @@ void split_kernel(AttnArgs a) {
     const uint32_t koff = (uint32_t)(lane % C::KSL) * C::KENT;
     const uint32_t voff = C::VOFF0 + (uint32_t)(lane % C::VSL) * C::VENT;
 
+    const bool sparse = a.sparse_log2 > -INFINITY;  // uniform: sparse V on
     float m_ref = -INFINITY, l_lane = 0.0f;  // head n's reference max / this lane's partial sum
     // V sums D[nb][i]: head 4*grp + i, dim NB*n + nb, in units of 2^wsh
     floatx4_t vacc[C::NB];
@@ -723,6 +751,19 @@ void split_kernel(AttnArgs a) {
             wa[j >> 1][2 * (j & 1) + 1] = pack_half2(p2 * vq.z, p3 * vq.w);
         }
         l_lane += psum;
+        if (sparse) {
+            // sparse V: weights below 2^sparse_log2 of the reference max keep
+            // their place in the sum above but add nothing to the V sums (the
+            // reference max never exceeds the true one, so only weights below
+            // the threshold of the true max are dropped)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t k0 = (dsc[j][0] < a.sparse_log2 ? 0u : 0xFFFFu) | (dsc[j][1] < a.sparse_log2 ? 0u : 0xFFFF0000u);
+                const uint32_t k1 = (dsc[j][2] < a.sparse_log2 ? 0u : 0xFFFFu) | (dsc[j][3] < a.sparse_log2 ? 0u : 0xFFFF0000u);
+                wa[j >> 1][2 * (j & 1)] &= k0;
+                wa[j >> 1][2 * (j & 1) + 1] &= k1;
+            }
+        }
         // rows of heads >= G and the repeated rows 8..15 carry zero weights (they
         // are never read; zero operands cost the matrix cores less energy)
         if (n >= G) {
@@ -773,6 +814,9 @@ void split_kernel(AttnArgs a) {
         __attribute__((always_inline)) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
+            // sparse V: a 32-token step whose weights are all dropped is skipped
+            // (its table lookups and matrix-core ops)
+            if (sparse && !__builtin_amdgcn_ballot_w64((wa[s2][0] | wa[s2][1] | wa[s2][2] | wa[s2][3]) != 0u)) continue;
             const half8_t aw = as_half8(make_uint4(wa[s2][0], wa[s2][1], wa[s2][2], wa[s2][3]));
 #pragma unroll
             for (int k = 0; k < C::VLK; ++k) {

@@ -67,6 +67,13 @@ struct AttnArgs {
     const uint8_t* v_codes;
     const uint16_t* v_norms;
     float scale;
+    // score factor alpha(N) of a row attending over N tokens: mode 0 plain,
+    // 1 sharpen 1 + sharp_c sqrt(ln N), 2 soften sqnr / (sqnr + sqrt(ln N * inv_ln_n0))
+    int score_mode;
+    float sharp_c, sqnr, inv_ln_n0;
+    // sparse V: softmax weights below 2^sparse_log2 (relative to the reference
+    // max) add nothing to the V sums; -INFINITY when off
+    float sparse_log2;
     float* out;
     float* qproj;     // [batch][hq][m]  scale*log2e*sqrt(pi/2)/m * S H(D_K q)/sqrt(d)
     float* part;      // [batch][hq][splits][d + 2]

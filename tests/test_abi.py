@@ -325,3 +325,27 @@ def test_noalloc_rejects_requests_beyond_its_scratch():
     assert call(2, 14, 3, 1000) == tq.TQ_EUNSUPPORTED  # 14 % 3
     assert call(2, 14, 2, 0) == tq.TQ_EINVAL
     assert "scratch" in tq.strerror(tq.TQ_ESCRATCH)
+
+
+def test_attention_switch_argument_errors():
+    """tq_attn_decode_ex validates its switches on the host."""
+    kc, vc = tq.tq_codebook(4, 128, 0), tq.tq_codebook(2, 128, 0)
+    P = FAKE
+    ws = tq.tq_workspace_bytes(tq.TQ_OP_ATTN_DECODE_MQ, kc, vc, 2, 14, 2, 1000, n_q=3)
+    assert ws > 0
+
+    def call(mode=0, sqnr=0.0, n0=0, sparse=0.0, cols=3, opts=True):
+        o_ = tq.tq_attn_opts(mode, sqnr, n0, sparse)
+        return tq.raw_call("tq_attn_decode_ex", ctypes.byref(kc), ctypes.byref(vc), P, 1, 2, cols, 14, 2, P, 1000,
+                           P, P, None, None, None, P, P, ctypes.c_float(0.1), ctypes.byref(o_) if opts else None,
+                           P, P, ws, None)
+
+    assert call(mode=3) == tq.TQ_EINVAL
+    assert call(mode=tq.TQ_SCORE_SHARPEN, sqnr=0.0) == tq.TQ_EINVAL
+    assert call(mode=tq.TQ_SCORE_SOFTEN, sqnr=float("inf")) == tq.TQ_EINVAL
+    assert call(n0=1) == tq.TQ_EINVAL
+    assert call(sparse=-0.5) == tq.TQ_EINVAL
+    assert call(sparse=1.5) == tq.TQ_EINVAL
+    assert call(sparse=float("nan")) == tq.TQ_EINVAL
+    assert call(cols=0) == tq.TQ_EINVAL
+    assert call(cols=tq.TQ_MAX_QUERY_COLS + 1) == tq.TQ_EUNSUPPORTED
