@@ -32,6 +32,7 @@ pages print, closed forms, textbook routines or brute force.
 """
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -140,35 +141,90 @@ def sign_vector(seed: int, d: int) -> np.ndarray:
     return np.array([-1.0 if (v >> 63) & 1 else 1.0 for v in splitmix64(seed, d)])
 
 
+@functools.lru_cache(maxsize=None)
 def hadamard(d: int) -> np.ndarray:
-    """Sylvester Hadamard matrix of order d from its definition (-1)^popcount(i&j)."""
+    """Sylvester Hadamard matrix of order d from its definition (-1)^popcount(i&j).
+    (Cached per d and returned read-only: it is a constant.)"""
     if d < 1 or d & (d - 1):
         raise ValueError("d must be a power of two")
     i = np.arange(d)
     pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
-    return np.where(pc % 2 == 0, 1.0, -1.0)
+    h = np.where(pc % 2 == 0, 1.0, -1.0)
+    h.setflags(write=False)
+    return h
 
 
 # --------------------------------------------------------------------------
 # Codec
 # --------------------------------------------------------------------------
+RES_NONE, RES_QJL, RES_SRHT, RES_SIGN = 0, 1, 2, 3
+
+
+def second_sign_vector(seed: int, d: int) -> np.ndarray:
+    """Second sign basis ("signs2" of [P1] v1.4.2 "MMA Tensor Core 가속" item 2,
+    the SRHT QJL's own random signs): sign i is -1 when bit 63 of SplitMix64
+    output 257 + i for the seed is set (outputs 1..256 belong to the first
+    sign vector, whatever d)."""
+    return np.array([-1.0 if (v >> 63) & 1 else 1.0 for v in splitmix64(seed, 256 + d)[256:]])
+
+
 class Codec:
-    """What one encoder/decoder needs: d, bits, QJL width, signs, codebook.
+    """What one encoder/decoder needs: d, bits, residual kind and width,
+    signs, codebook.
 
     The float64 Lloyd-Max values are rounded to float32 once; those float32
     centroids and thresholds define the quantiser.
+
+    Residual kinds (one bit per projection, m of them, plus a half scale):
+      RES_QJL   Gaussian projections S [m][d] given by the caller ([P1] "QJL
+                보정 효과": the paper's TurboQuant_prod);
+      RES_SRHT  the structured projection S = H diag(signs2), m = d: a second
+                sign flip and Walsh-Hadamard transform ([P1] v1.3.0: QJL is
+                SRHT-based in the original paper; v1.4.2 item 2: its second
+                sign basis signs2);
+      RES_SIGN  Direct Sign, m = d: the signs of the residual itself with
+                their mean magnitude as the scale ([P1] v1.1.0 "Direct Sign —
+                논문 QJL 대비 4.3배 낮은 분산").
     """
 
-    def __init__(self, bits: int, d: int, seed: int, qjl_m: int = 0):
+    def __init__(self, bits: int, d: int, seed: int, qjl_m: int = 0, residual: int | None = None):
         self.bits = int(bits)
         self.d = int(d)
         self.seed = int(seed)
+        if residual is None:
+            residual = RES_QJL if qjl_m else RES_NONE
+        if residual in (RES_SRHT, RES_SIGN):
+            qjl_m = self.d
+        if residual == RES_NONE:
+            qjl_m = 0
+        self.residual = int(residual)
         self.qjl_m = int(qjl_m)
         c64, t64 = lloyd_max_gaussian(self.bits)
         self.centroid = c64.astype(np.float32)
         self.threshold = t64.astype(np.float32)
         self.signs = sign_vector(self.seed, self.d)
+        self.signs2 = second_sign_vector(self.seed, self.d)
         self.H = hadamard(self.d)
+
+    def projection(self, S=None) -> np.ndarray:
+        """The [m][d] projection of the residual: S (QJL), H diag(signs2)
+        (SRHT) or the identity (Direct Sign)."""
+        if self.residual == RES_QJL:
+            if S is None or np.shape(S) != (self.qjl_m, self.d):
+                raise ValueError("QJL needs S of shape [m][d]")
+            return np.asarray(S, dtype=np.float64)
+        if self.residual == RES_SRHT:
+            return self.H * self.signs2[None, :]
+        if self.residual == RES_SIGN:
+            return np.eye(self.d)
+        raise ValueError("codec has no residual")
+
+    @property
+    def residual_coef(self) -> float:
+        """Estimator constant: sqrt(pi/2)/m for the projected signs (from
+        E[sign(s.r)(s.a)] = sqrt(2/pi) <a, r>/||r||), 1 for Direct Sign (the
+        scale is already the mean magnitude)."""
+        return 1.0 if self.residual == RES_SIGN else math.sqrt(math.pi / 2) / self.qjl_m
 
     @property
     def code_bytes(self) -> int:
@@ -263,12 +319,14 @@ def encode(x: np.ndarray, codec: Codec, S: np.ndarray | None = None):
         "norm": norm,
     }
     if codec.qjl_m:
-        if S is None or S.shape != (codec.qjl_m, codec.d):
-            raise ValueError("QJL needs S of shape [m][d]")
+        P = codec.projection(S)
         c = codec.centroid.astype(np.float64)
         r = (z - c[idx]) / math.sqrt(codec.d)
-        gamma = np.sqrt(np.sum(r * r, axis=1))
-        u = r @ np.asarray(S, dtype=np.float64).T
+        if codec.residual == RES_SIGN:
+            gamma = np.sum(np.abs(r), axis=1) / codec.d  # mean magnitude: the best scale for fixed signs
+        else:
+            gamma = np.sqrt(np.sum(r * r, axis=1))
+        u = r @ P.T
         out["qjl"] = pack_signs(u >= 0.0)
         out["gamma"] = to_half(gamma)
         out["gamma64"] = gamma
@@ -346,13 +404,17 @@ def qjl_term(q: np.ndarray, qjl_packed: np.ndarray, norms16: np.ndarray,
     estimated by n * gamma * sqrt(pi/2)/m * <S a / sqrt(d), sign(S r)>, which is
     unbiased over S because E[sign(s.r) (s.a)] = sqrt(2/pi) <a, r>/||r|| for
     s ~ N(0, I).  ([P1] "Attention Sharpening" describes the same scalar
-    correction d_qjl * sum(Q_wht2[i] * sign[i]).)  Returns [n_q][n_rows].
+    correction d_qjl * sum(Q_wht2[i] * sign[i]).)  The SRHT kind uses
+    S = H diag(signs2) (rows of +-1, nearly Gaussian projections); Direct Sign
+    uses S = I and the constant 1: n * gamma * <a / sqrt(d), sign(r)> with gamma
+    the mean |r_i|, the residual rebuilt as gamma * sign(r).  Returns
+    [n_q][n_rows].
     """
     m = codec.qjl_m
     a = rotate(np.atleast_2d(q), codec)
-    qhat = (a / math.sqrt(codec.d)) @ np.asarray(S, dtype=np.float64).T  # [n_q][m]
+    qhat = (a / math.sqrt(codec.d)) @ codec.projection(S).T  # [n_q][m]
     sgn = 2.0 * unpack_signs(qjl_packed, m).astype(np.float64) - 1.0  # [n][m]
-    coef = np.asarray(norms16, np.float64) * np.asarray(gamma16, np.float64) * math.sqrt(math.pi / 2) / m
+    coef = np.asarray(norms16, np.float64) * np.asarray(gamma16, np.float64) * codec.residual_coef
     return (qhat @ sgn.T) * coef[None, :]
 
 

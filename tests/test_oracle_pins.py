@@ -759,6 +759,96 @@ def test_qjl_attention_logit_unbiased():
     assert abs(resid) > 10 * se
 
 
+def test_second_sign_vector_reads_outputs_257_on():
+    """signs2: bit 63 of SplitMix64 outputs 257.. (outputs 1..256 belong to
+    the first sign vector, pinned by the published test vector)."""
+    for seed, d in ((0, 64), (12345, 128), (2**63 + 5, 256)):
+        outs = o.splitmix64(seed, 256 + d)
+        want = np.array([-1.0 if (v >> 63) & 1 else 1.0 for v in outs[256:]])
+        assert np.array_equal(o.second_sign_vector(seed, d), want)
+        assert not np.array_equal(o.second_sign_vector(seed, d), o.sign_vector(seed, d))
+        c = o.Codec(3, d, seed, residual=o.RES_SRHT)
+        assert c.qjl_m == d and np.array_equal(c.signs2, want)
+
+
+def test_srht_projection_is_an_orthogonal_sign_matrix():
+    c = o.Codec(3, 128, 9, residual=o.RES_SRHT)
+    P = c.projection()
+    assert np.all(np.abs(P) == 1.0)
+    np.testing.assert_array_equal(P @ P.T, 128 * np.eye(128))
+    # u = S r is the second sign flip then the transform: H (signs2 * r)
+    r = np.random.default_rng(30).standard_normal((3, 128))
+    np.testing.assert_allclose(r @ P.T, o.rotate(r * c.signs2[None, :] * c.signs[None, :], c), rtol=1e-12, atol=1e-12)
+
+
+def test_srht_estimator_nearly_unbiased():
+    """Over random seeds (so random signs2), the SRHT residual term corrects the
+    MSE estimate like the Gaussian QJL: the mean error of the full estimate is
+    within 4 standard errors plus a 3% allowance for the bias of +-1
+    projections, while the MSE-only estimate is clearly biased."""
+    d = 256
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((1, d))
+    q = x + 0.5 * rng.standard_normal((1, d))  # correlated, so the MSE error has a sign
+    truth = float(q[0] @ x[0])
+    err, err_mse = [], []
+    for seed in range(400):
+        c = o.Codec(1, d, 1000 + seed, residual=o.RES_SRHT)
+        e = o.encode(x, c)
+        est = o.ip_scores(q, e["codes"], e["norm"], e["qjl"], e["gamma64"], None, c)[0, 0]
+        mse = o.ip_scores(q, e["codes"], e["norm"], None, None, None, o.Codec(1, d, 1000 + seed))[0, 0]
+        err.append(est - truth)
+        err_mse.append(mse - truth)
+    err, err_mse = np.array(err), np.array(err_mse)
+    se = err.std() / math.sqrt(len(err))
+    assert abs(err.mean()) < 4 * se + 0.03 * abs(err_mse.mean())
+    assert abs(err_mse.mean()) > 10 * se
+
+
+def test_direct_sign_variance_ratio(golden_dir):
+    """Direct Sign against the paper's QJL (Gaussian, m = d) on Gaussian
+    residuals: the error variance of the inner-product correction is
+    (1 - 2/pi)/(pi/2) = 0.2313 of QJL's, the printed 0.23 (4.3x lower)."""
+    pages = _pages(golden_dir)
+    d, n = 128, 400
+    rng = np.random.default_rng(32)
+    cs = o.Codec(2, d, 3, residual=o.RES_SIGN)
+    e_ds, e_qjl = [], []
+    for trial in range(25):
+        r = rng.standard_normal((n, d)) * 0.2  # residuals in unit-vector units
+        q = rng.standard_normal((1, d))
+        a = o.rotate(q, cs)[0]
+        truth = r @ a / math.sqrt(d)  # the residual part n <a/sqrt(d), r> at n = 1
+        ones = np.ones(n)
+        ds = o.qjl_term(q, o.pack_signs(r >= 0), ones, np.abs(r).mean(axis=1), None, cs)[0]
+        S = rng.standard_normal((d, d))
+        cq = o.Codec(2, d, 3, qjl_m=d)
+        qj = o.qjl_term(q, o.pack_signs(r @ S.T >= 0), ones, np.linalg.norm(r, axis=1), S, cq)[0]
+        e_ds.append(ds - truth)
+        e_qjl.append(qj - truth)
+    ratio = np.mean(np.concatenate(e_ds) ** 2) / np.mean(np.concatenate(e_qjl) ** 2)
+    assert ratio == pytest.approx((1 - 2 / math.pi) / (math.pi / 2), rel=0.06)
+    assert ratio == pytest.approx(float(pages["direct_sign_variance_ratio"]), abs=0.02)
+    assert 1 / ratio == pytest.approx(float(pages["direct_sign_variance_reduction"]), rel=0.07)
+
+
+def test_direct_sign_bits_and_scale():
+    d = 128
+    c = o.Codec(3, d, 4, residual=o.RES_SIGN)
+    x = np.random.default_rng(33).standard_normal((10, d))
+    e = o.encode(x, c)
+    rho = e["z"] - c.centroid.astype(np.float64)[e["idx"]]
+    assert np.array_equal(o.unpack_signs(e["qjl"], d), (rho >= 0).astype(np.uint8))
+    np.testing.assert_allclose(e["gamma64"], np.abs(rho).sum(axis=1) / d / math.sqrt(d), rtol=1e-13)
+    # the corrected estimate equals <q, x_hat + rebuilt residual>
+    q = np.random.default_rng(34).standard_normal((2, d))
+    est = o.ip_scores(q, e["codes"], e["norm"], e["qjl"], e["gamma64"], None, c)
+    # rotated unit domain: centroid plus the rebuilt residual gamma*sqrt(d)*sign
+    rebuilt = c.centroid.astype(np.float64)[e["idx"]] + e["gamma64"][:, None] * math.sqrt(d) * (2.0 * (rho >= 0) - 1.0)
+    xr = e["norm"][:, None] * ((rebuilt @ c.H.T) / d) * c.signs[None, :]  # back through D H / d
+    np.testing.assert_allclose(est, q @ xr.T, rtol=1e-11, atol=1e-11)
+
+
 def test_qjl_bits_and_gamma():
     d, m = 128, 128
     rng = np.random.default_rng(14)
