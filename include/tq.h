@@ -58,23 +58,39 @@ enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 };
  *
  *   d           head dimension: 32, 64, 128 or 256 (attention: 128 or 256).
  *   bits        1..4 bits per coordinate (L = 2^bits centroids).
- *   qjl_m       0, or the number of QJL projections (multiple of 32, <= 256).
+ *   qjl_m       0, or the number of residual sign bits m (multiple of 32,
+ *               <= 256; m = d for TQ_RES_SRHT and TQ_RES_SIGN).
+ *   residual    TQ_RES_NONE (qjl_m = 0), or how the m residual bits are
+ *               formed (K caches and search only):
+ *                 TQ_RES_QJL   signs of S r for a caller-drawn Gaussian S
+ *                              [m][d] ([P1] "QJL 보정 효과": TurboQuant_prod);
+ *                 TQ_RES_SRHT  signs of H(D2 r), the structured projection
+ *                              with the second sign basis D2 = sign_mask2
+ *                              ([P1] v1.3.0: QJL is SRHT-based in the paper;
+ *                              v1.4.2 item 2: its signs2);
+ *                 TQ_RES_SIGN  Direct Sign: the signs of r itself, with the
+ *                              mean |r_i| as the scale ([P1] v1.1.0 "Direct
+ *                              Sign — 논문 QJL 대비 4.3배 낮은 분산").
  *   sign_mask   bit i (word i/32, bit i%32) set means D_ii = -1: the seeded
  *               random sign flip applied before the Walsh-Hadamard transform
  *               ([P1] v1.7.0 "핵심 설계 결정" item 4, "tbq_signs").
  *   centroid    L float32 Lloyd-Max centroids of N(0,1), ascending, exactly
  *               symmetric; entries >= L are 0.
  *   threshold   L-1 float32 midpoints; the middle one is exactly 0.
+ *   sign_mask2  the second sign basis D2 of TQ_RES_SRHT (filled for every
+ *               codec; bit i set means D2_ii = -1).
  */
+enum { TQ_RES_NONE = 0, TQ_RES_QJL = 1, TQ_RES_SRHT = 2, TQ_RES_SIGN = 3 };
 typedef struct {
     int32_t d;
     int32_t bits;
     int32_t qjl_m;
-    int32_t reserved;
+    int32_t residual;
     uint64_t seed;
     uint32_t sign_mask[8];
     float centroid[16];
     float threshold[15];
+    uint32_t sign_mask2[8];
 } tq_codec;
 
 /*
@@ -87,12 +103,21 @@ typedef struct {
  * double precision by the Lloyd fixed-point iteration (centroid = conditional
  * mean of its cell, threshold = midpoint) on the positive half, mirrored, then
  * rounded to float32.  Signs: D_ii = -1 when bit 63 of the (i+1)-th SplitMix64
- * output from state `seed` is set.
+ * output from state `seed` is set; D2_ii likewise from output 257 + i.
+ * The residual kind is TQ_RES_QJL when qjl_m > 0, else TQ_RES_NONE.
  *
  * Errors: TQ_EINVAL if out is NULL; TQ_EUNSUPPORTED for d not in {32,64,128,256},
  * bits not in 1..4, qjl_m not a multiple of 32 in 0..256.
  */
 int tq_codebook(int bits, int d, uint64_t seed, int qjl_m, tq_codec *out);
+
+/*
+ * tq_codebook_ex -- tq_codebook with an explicit residual kind (TQ_RES_*).
+ * TQ_RES_SRHT and TQ_RES_SIGN use m = d bits (qjl_m must be 0 or d);
+ * TQ_RES_QJL needs qjl_m > 0; TQ_RES_NONE needs qjl_m = 0.  Errors as
+ * tq_codebook, plus TQ_EUNSUPPORTED for an unknown kind or a mismatched qjl_m.
+ */
+int tq_codebook_ex(int bits, int d, uint64_t seed, int residual, int qjl_m, tq_codec *out);
 
 /*
  * tq_encode -- quantise n vectors ([P1] v1.7.0 "핵심 설계 결정" item 4: sign flip +
@@ -103,8 +128,10 @@ int tq_codebook(int bits, int d, uint64_t seed, int qjl_m, tq_codec *out);
  *   n = ||x||_2;  z = H(D x)/n (z = 0 when n = 0);  idx_i = #{j : z_i > t_j};
  *   codes = packed idx;  norms = half(n).
  * With codec->qjl_m = m > 0 (the paper's TurboQuant_prod residual correction,
- * [P1] "QJL 보정 효과", K caches only):
- *   r = (z - c[idx]) / sqrt(d);  gamma = half(||r||);  qjl bit j = [(S r)_j >= 0].
+ * [P1] "QJL 보정 효과", K caches only), r = (z - c[idx]) / sqrt(d) and
+ *   TQ_RES_QJL:  gamma = half(||r||);  bit j = [(S r)_j >= 0];
+ *   TQ_RES_SRHT: gamma = half(||r||);  bit j = [(H D2 r)_j >= 0];
+ *   TQ_RES_SIGN: gamma = half(sum_i |r_i| / d);  bit i = [r_i >= 0].
  *
  *   c              codec (host pointer).
  *   x              [n][x_row_stride] elements; 16-byte aligned; x_row_stride*elem
@@ -112,8 +139,8 @@ int tq_codebook(int bits, int d, uint64_t seed, int qjl_m, tq_codec *out);
  *   codes          row i at codes + i*code_row_stride; code_row_stride >= d*bits/8,
  *                  multiple of 4; codes 4-byte aligned.
  *   norms_f16      [n] halves.
- *   qjl_S          [m][d] float32 row-major (N(0,1) draws made by the caller);
- *                  NULL when m = 0.
+ *   qjl_S          [m][d] float32 row-major (N(0,1) draws made by the caller)
+ *                  for TQ_RES_QJL; NULL (unused) for the other kinds.
  *   qjl_bits       [n][m/8] bytes, 4-byte aligned; NULL when m = 0.
  *   qjl_gamma_f16  [n] halves; NULL when m = 0.
  * n = 0 is valid and launches nothing.  Vectors whose squared norm underflows
@@ -215,7 +242,9 @@ int tq_decode(const tq_codec *c, const uint8_t *codes, int64_t code_row_stride,
  *           on the Q side, so the rotation cancels by Parseval);
  *   s_t   = scale * n_t/d * <q_rot, c_K[idx_t]>
  *           (+ with QJL: scale * n_t * gamma_t * sqrt(pi/2)/m * <S q_rot/sqrt(d), 2 bit_t - 1>,
- *            [P1] "Attention Sharpening": d_qjl * sum(Q_wht2[i] * sign[i]));
+ *            [P1] "Attention Sharpening": d_qjl * sum(Q_wht2[i] * sign[i]); with
+ *            TQ_RES_SRHT S = H D2; with TQ_RES_SIGN S = I and the constant
+ *            sqrt(pi/2)/m is replaced by 1);
  *   p     = softmax(s) over t < ctx_len[b] (exact, float32 accumulation,
  *           [P1] v1.5.2 "핵심 변경" item 1: float, not half2);
  *   o     = D_V H( sum_t p_t nV_t c_V[vidx_t] ) / d  (V accumulated in the rotated
@@ -229,7 +258,7 @@ int tq_decode(const tq_codec *c, const uint8_t *codes, int64_t code_row_stride,
  *   k_codes         [batch][n_kv_heads][ctx_cap][d*kbits/8]   contiguous, 16-B aligned
  *   k_norms         [batch][n_kv_heads][ctx_cap] halves
  *   k_qjl, k_gamma  [batch][n_kv_heads][ctx_cap][m/8], [..][ctx_cap] halves; NULL if m = 0
- *   qjl_S           [m][d] float32; NULL if m = 0
+ *   qjl_S           [m][d] float32 for TQ_RES_QJL keys; NULL otherwise
  *   v_codes, v_norms as k_codes / k_norms with vbits
  *   out             [batch][n_q_heads][d] float32; a sequence with ctx_len 0 gives 0.
  *   workspace       device scratch of at least tq_attn_workspace_bytes(...) bytes,
@@ -471,9 +500,11 @@ size_t tq_attn_workspace_bytes(const tq_codec *kc, const tq_codec *vc, int batch
  *
  *   est(q, t) = n_t ( <H(Dq), c[idx_t]>/d
  *                     + gamma_t sqrt(pi/2)/m <S H(Dq)/sqrt(d), 2 bit_t - 1> )
- * then the k largest estimates per query, ordered by (estimate desc, id asc).
+ * (S = H D2 for TQ_RES_SRHT; S = I and constant 1 for TQ_RES_SIGN), then the
+ * k largest estimates per query, ordered by (estimate desc, id asc).
  *
- *   c            codec (host) with qjl_m = m (0 = MSE-only estimate).
+ *   c            codec (host) with qjl_m = m (0 = MSE-only estimate); qjl_S
+ *                [m][d] for TQ_RES_QJL, NULL for the other kinds.
  *   q            [n_q][d] float32, 16-byte aligned.
  *   codes, norms [n_db][d*bits/8], [n_db]; qjl_bits [n_db][m/8]; qjl_gamma [n_db].
  *   out_scores   [n_q][k] float32;  out_ids [n_q][k] int64.  If n_db < k the tail

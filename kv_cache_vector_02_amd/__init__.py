@@ -17,13 +17,14 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EWORKSPACE, TQ_EDEVICE, TQ_ESCRATCH = 0, -1, -2, -3, -4, -5
+TQ_RES_NONE, TQ_RES_QJL, TQ_RES_SRHT, TQ_RES_SIGN = 0, 1, 2, 3
 TQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 
 _DTYPES = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16}
 
 EXPORTS = (
-    "tq_codebook", "tq_encode", "tq_encode_kv", "tq_prefill", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
+    "tq_codebook", "tq_codebook_ex", "tq_encode", "tq_encode_kv", "tq_prefill", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
     "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes", "tq_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror", "tq_stream_read",
     "tq_attn_decode_noalloc", "tq_attn_decode_mq", "tq_attn_decode_ex",
@@ -39,11 +40,12 @@ class tq_codec(ctypes.Structure):
         ("d", ctypes.c_int32),
         ("bits", ctypes.c_int32),
         ("qjl_m", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("residual", ctypes.c_int32),
         ("seed", ctypes.c_uint64),
         ("sign_mask", ctypes.c_uint32 * 8),
         ("centroid", ctypes.c_float * 16),
         ("threshold", ctypes.c_float * 15),
+        ("sign_mask2", ctypes.c_uint32 * 8),
     ]
 
     @property
@@ -61,6 +63,10 @@ class tq_codec(ctypes.Structure):
     @property
     def signs(self) -> list[float]:
         return [-1.0 if (self.sign_mask[i >> 5] >> (i & 31)) & 1 else 1.0 for i in range(self.d)]
+
+    @property
+    def signs2(self) -> list[float]:
+        return [-1.0 if (self.sign_mask2[i >> 5] >> (i & 31)) & 1 else 1.0 for i in range(self.d)]
 
 
 TQ_SCORE_PLAIN, TQ_SCORE_SHARPEN, TQ_SCORE_SOFTEN = 0, 1, 2
@@ -91,6 +97,7 @@ def _load():
     CP = ctypes.POINTER(tq_codec)
     sig = {
         "tq_codebook": (I, [I, I, ctypes.c_uint64, I, CP]),
+        "tq_codebook_ex": (I, [I, I, ctypes.c_uint64, I, I, CP]),
         "tq_encode": (I, [CP, P, I, I64, I64, P, I64, P, P, P, P, P]),
         "tq_encode_kv": (I, [CP, CP, P, P, I, I64, I64, P, I64, P, P, I64, P, P, P, P, P]),
         "tq_prefill": (I, [CP, CP, P, P, I, I, I64, I64, I64, P, P, P, P, P, P, P, P]),
@@ -180,7 +187,8 @@ def _qjl_rows(codec, n, qjl_S, qjl_bits, qjl_gamma, names=("qjl_S", "qjl_bits", 
     m = codec.qjl_m
     if not m:
         return
-    _shape(qjl_S, (m, codec.d), names[0], torch.float32)
+    if codec.residual == TQ_RES_QJL:
+        _shape(qjl_S, (m, codec.d), names[0], torch.float32)
     if qjl_bits is None or qjl_bits.numel() != n * (m // 8) or qjl_bits.dtype != torch.uint8 \
             or not qjl_bits.is_contiguous() or qjl_bits.shape[-1] != m // 8:
         raise ValueError(f"{names[1]} must be contiguous uint8 [{n}][{m // 8}]")
@@ -201,6 +209,14 @@ def tq_codebook(bits: int, d: int, seed: int, qjl_m: int = 0) -> tq_codec:
     """Host-only: codec with the Lloyd-Max codebook and the seeded sign mask."""
     c = tq_codec()
     _check(_lib.tq_codebook(bits, d, ctypes.c_uint64(seed & (2**64 - 1)), qjl_m, ctypes.byref(c)), "tq_codebook")
+    return c
+
+
+def tq_codebook_ex(bits: int, d: int, seed: int, residual: int, qjl_m: int = 0) -> tq_codec:
+    """Host-only: codec with an explicit residual kind (TQ_RES_*)."""
+    c = tq_codec()
+    _check(_lib.tq_codebook_ex(bits, d, ctypes.c_uint64(seed & (2**64 - 1)), residual, qjl_m, ctypes.byref(c)),
+           "tq_codebook_ex")
     return c
 
 

@@ -81,9 +81,20 @@ uint64_t splitmix64_at(uint64_t seed, uint64_t index) {
 bool valid_d(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
 bool valid_codec(const tq_codec* c) {
-    return c && valid_d(c->d) && c->bits >= 1 && c->bits <= 4 && c->qjl_m >= 0 && c->qjl_m <= 256 &&
-           c->qjl_m % 32 == 0;
+    if (!(c && valid_d(c->d) && c->bits >= 1 && c->bits <= 4 && c->qjl_m >= 0 && c->qjl_m <= 256 &&
+          c->qjl_m % 32 == 0))
+        return false;
+    switch (c->residual) {
+        case TQ_RES_NONE: return c->qjl_m == 0;
+        case TQ_RES_QJL: return c->qjl_m > 0;
+        case TQ_RES_SRHT:
+        case TQ_RES_SIGN: return c->qjl_m == c->d;
+        default: return false;
+    }
 }
+
+// The residual needs the caller's Gaussian projection S.
+bool needs_S(const tq_codec* c) { return c->residual == TQ_RES_QJL; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -99,28 +110,46 @@ void fill_codec_args(const tq_codec* c, CodecArgs* a) {
     a->d = c->d;
     a->bits = c->bits;
     a->qjl_m = c->qjl_m;
+    a->residual = c->residual;
+    memcpy(a->sign_mask2, c->sign_mask2, sizeof(a->sign_mask2));
 }
 }  // namespace tqi
 
 extern "C" {
 
-int tq_codebook(int bits, int d, uint64_t seed, int qjl_m, tq_codec* out) {
+int tq_codebook_ex(int bits, int d, uint64_t seed, int residual, int qjl_m, tq_codec* out) {
     if (!out) return TQ_EINVAL;
     if (!valid_d(d) || bits < 1 || bits > 4 || qjl_m < 0 || qjl_m > 256 || qjl_m % 32 != 0)
         return TQ_EUNSUPPORTED;
+    if (residual == TQ_RES_SRHT || residual == TQ_RES_SIGN) {
+        if (qjl_m != 0 && qjl_m != d) return TQ_EUNSUPPORTED;
+        qjl_m = d;
+    } else if (residual == TQ_RES_QJL) {
+        if (qjl_m == 0) return TQ_EUNSUPPORTED;
+    } else if (residual != TQ_RES_NONE || qjl_m != 0) {
+        return TQ_EUNSUPPORTED;
+    }
     memset(out, 0, sizeof(*out));
     out->d = d;
     out->bits = bits;
     out->qjl_m = qjl_m;
+    out->residual = residual;
     out->seed = seed;
-    for (int i = 0; i < d; ++i)
+    for (int i = 0; i < d; ++i) {
         if (splitmix64_at(seed, (uint64_t)i + 1) >> 63) out->sign_mask[i >> 5] |= 1u << (i & 31);
+        // the second sign basis: outputs 257.. (1..256 belong to the first, whatever d)
+        if (splitmix64_at(seed, (uint64_t)i + 257) >> 63) out->sign_mask2[i >> 5] |= 1u << (i & 31);
+    }
     double c[16], t[15];
     lloyd_max(bits, c, t);
     const int L = 1 << bits;
     for (int k = 0; k < L; ++k) out->centroid[k] = (float)c[k];
     for (int k = 0; k < L - 1; ++k) out->threshold[k] = (float)t[k];
     return TQ_OK;
+}
+
+int tq_codebook(int bits, int d, uint64_t seed, int qjl_m, tq_codec* out) {
+    return tq_codebook_ex(bits, d, seed, qjl_m > 0 ? TQ_RES_QJL : TQ_RES_NONE, qjl_m, out);
 }
 
 size_t tq_packed_bytes(int d, int bits, int qjl_m) {
@@ -157,9 +186,8 @@ static int encode_setup(const tq_codec* c, const void* x, int x_dtype, int64_t n
         if (x_row_stride < c->d || (x_row_stride * esz) % 16 != 0) return TQ_EINVAL;
         if (code_row_stride < c->d * c->bits / 8 || code_row_stride % 4 != 0) return TQ_EINVAL;
         if (c->qjl_m > 0) {
-            if (!qjl_S || !qjl_bits || !qjl_gamma_f16 || !aligned(qjl_bits, 4) || !aligned(qjl_gamma_f16, 2) ||
-                !aligned(qjl_S, 4))
-                return TQ_EINVAL;
+            if (!qjl_bits || !qjl_gamma_f16 || !aligned(qjl_bits, 4) || !aligned(qjl_gamma_f16, 2)) return TQ_EINVAL;
+            if (needs_S(c) && (!qjl_S || !aligned(qjl_S, 4))) return TQ_EINVAL;
         }
     }
     tqi::fill_codec_args(c, &a->c);
@@ -320,7 +348,8 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
     if (!aligned(q, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(out, 16) ||
         !aligned(k_norms, 2) || !aligned(v_norms, 2) || !aligned(ctx_len, 4))
         return TQ_EINVAL;
-    if (kc->qjl_m > 0 && (!k_qjl || !k_gamma || !qjl_S || !aligned(k_qjl, 4) || !aligned(k_gamma, 2)))
+    if (kc->qjl_m > 0 && (!k_qjl || !k_gamma || (needs_S(kc) && !qjl_S) || !aligned(k_qjl, 4) ||
+                          !aligned(k_gamma, 2)))
         return TQ_EINVAL;
     if (!isfinite(scale)) return TQ_EINVAL;
     if (opts) {
@@ -529,9 +558,8 @@ int tq_ip_search(const tq_codec* c, const float* q, int n_q, const uint8_t* code
     if (rc != TQ_OK) return rc;
     if (!q || !out_scores || !out_ids || !aligned(q, 16)) return TQ_EINVAL;
     if (n_db > 0 && (!codes || !norms || !aligned(codes, 4) || !aligned(norms, 2))) return TQ_EINVAL;
-    if (c->qjl_m > 0 && n_db > 0 && (!qjl_bits || !qjl_gamma || !qjl_S || !aligned(qjl_bits, 4)))
-        return TQ_EINVAL;
-    if (c->qjl_m > 0 && !qjl_S) return TQ_EINVAL;
+    if (c->qjl_m > 0 && n_db > 0 && (!qjl_bits || !qjl_gamma || !aligned(qjl_bits, 4))) return TQ_EINVAL;
+    if (needs_S(c) && !qjl_S) return TQ_EINVAL;
     int nb;
     int64_t rows;
     tqi::search_plan(n_q, n_db, k, &nb, &rows);

@@ -72,9 +72,11 @@ __device__ __forceinline__ int row_tokens(const AttnArgs& a, int64_t row) {
 }
 
 // ----------------------------------------------------------------- qprep ----
-// QJL keys only: per query head, the projection S H(D_K q) / sqrt(d) of the
-// rotated query (the Q_wht2 side of the fused query pass), pre-scaled by
-// scale * log2(e) * sqrt(pi/2) / m.  The scan rotates its queries itself.
+// Keys with residual bits only: per query row, the projection S H(D_K q) /
+// sqrt(d) of the rotated query (the Q_wht2 side of the fused query pass),
+// pre-scaled by scale * log2(e) * sqrt(pi/2) / m (S = H D2 for the SRHT kind;
+// S = I and the constant 1 for Direct Sign).  The scan rotates its queries
+// itself.
 template <int D, int DT>
 __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
     constexpr int LPV = D / 8;
@@ -98,11 +100,29 @@ __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) v[e] = as_f(as_u(v[e]) ^ (((sbits >> e) & 1u) << 31));
     fwht<LPV>(v, gl);
     const int m = a.kc.qjl_m;
+    const float alpha = valid ? score_factor(a, row_tokens(a, head)) : 1.0f;
+    if (a.kc.residual != TQ_RES_QJL) {
+        // m = D: the structured SRHT projection H(D2 q_rot) (second sign flip
+        // and transform in registers), or Direct Sign's q_rot itself with the
+        // constant 1 in place of sqrt(pi/2)/m
+        float ps = a.scale * kLog2e / sqrtf((float)D) * alpha;
+        if (a.kc.residual == TQ_RES_SRHT) {
+            const uint32_t sbits2 = (a.kc.sign_mask2[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = as_f(as_u(v[e]) ^ (((sbits2 >> e) & 1u) << 31));
+            fwht<LPV>(v, gl);
+            ps *= sqrtf(1.57079632679489662f) / (float)m;
+        }
+        if (valid) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a.qproj[(int64_t)head * m + gl * 8 + e] = v[e] * ps;
+        }
+        return;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) rot[grp][gl * 8 + e] = v[e];
     __syncthreads();
-    const float ps = a.scale * kLog2e * sqrtf(1.57079632679489662f) / ((float)m * sqrtf((float)D)) *
-                     (valid ? score_factor(a, row_tokens(a, head)) : 1.0f);
+    const float ps = a.scale * kLog2e * sqrtf(1.57079632679489662f) / ((float)m * sqrtf((float)D)) * alpha;
     for (int j = gl; j < m; j += LPV) {
         const float* srow = a.S + (int64_t)j * D;
         float acc = 0.0f;

@@ -270,6 +270,61 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
     }
 }
 
+// Residual signs without a dense projection (one vector per lane group, in
+// registers): the structured SRHT QJL, bits = signs of H(D2 r) with the second
+// sign basis D2 and gamma = ||r|| ("TurboQuant KV 캐시 압축 for llama.cpp",
+// v1.3.0 and v1.4.2 item 2: the paper's QJL is SRHT-based, with its own signs2),
+// or Direct Sign, bits = signs of r with gamma = mean |r_i| (v1.1.0 "Direct
+// Sign").  r = (z - c[idx]) / sqrt(d) as for the Gaussian QJL.
+template <int D, int BITS, int DT, int KIND>
+__global__ __launch_bounds__(256) void encode_sign_kernel(EncodeArgs a) {
+    constexpr int LPV = D / 8;
+    constexpr int VPW = 64 / LPV;
+    __shared__ float cent[16];
+    if (threadIdx.x < 16) cent[threadIdx.x] = a.c.centroid[threadIdx.x];
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int gl = lane & (LPV - 1);
+    const uint32_t sbits = (a.c.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+    const uint32_t sbits2 = (a.c.sign_mask2[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+    const float rsd = 1.0f / sqrtf((float)D);
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    for (int64_t base = wave * VPW; base < a.n; base += nwaves * VPW) {
+        const int64_t row = base + lane / LPV;
+        const bool valid = row < a.n;
+        VecState st;
+        load_rotate<D, DT>(a, row, valid, gl, sbits, st);
+        uint32_t idx[8];
+        const uint32_t packed = pack_lane<BITS>(st, a.c, idx);
+        bool keep = true;
+        const int64_t orow = valid ? out_row(a, row, keep) : 0;
+        store_codes<BITS>(reinterpret_cast<uint32_t*>(a.codes + orow * a.code_stride), gl, packed, valid && keep);
+        const float inv = st.nrm > 0.0f ? 1.0f / st.nrm : 0.0f;
+        float r[8], acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            r[e] = (st.v[e] * inv - cent[idx[e]]) * rsd;
+            acc += KIND == TQ_RES_SIGN ? fabsf(r[e]) : r[e] * r[e];
+        }
+        acc = group_sum<LPV>(acc);
+        const float gamma = KIND == TQ_RES_SIGN ? acc * (1.0f / (float)D) : sqrtf(acc);
+        if constexpr (KIND == TQ_RES_SRHT) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r[e] = as_f(as_u(r[e]) ^ (((sbits2 >> e) & 1u) << 31));
+            fwht<LPV>(r, gl);
+        }
+        uint32_t sb = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sb |= (r[e] >= 0.0f ? 1u : 0u) << e;
+        store_codes<1>(reinterpret_cast<uint32_t*>(a.qjl + orow * (D / 8)), gl, sb, valid && keep);
+        if (valid && keep && gl == 0) {
+            a.norms[orow] = norm_to_half(st.nrm);
+            a.gamma[orow] = norm_to_half(gamma);
+        }
+    }
+}
+
 template <int D, int BITS>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     constexpr int LPV = D / 8;
@@ -307,7 +362,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
 template <int D, int BITS, int DT>
 hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t s) {
-    if (a.c.qjl_m > 0) {
+    if (a.c.residual == TQ_RES_SRHT || a.c.residual == TQ_RES_SIGN) {
+        constexpr int VPB = 4 * (64 / (D / 8));
+        const int64_t need = (a.n + VPB - 1) / VPB;
+        const int grid = (int)(need < 16384 ? need : 16384);
+        if (a.c.residual == TQ_RES_SRHT)
+            hipLaunchKernelGGL((encode_sign_kernel<D, BITS, DT, TQ_RES_SRHT>), dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((encode_sign_kernel<D, BITS, DT, TQ_RES_SIGN>), dim3(grid), dim3(256), 0, s, a);
+    } else if (a.c.qjl_m > 0) {
         const int64_t tiles = (a.n + QJL_TILE - 1) / QJL_TILE;
         const int grid = (int)(tiles < 8192 ? tiles : 8192);
         hipLaunchKernelGGL((encode_qjl_kernel<D, BITS, DT>), dim3(grid), dim3(256), 0, s, a);

@@ -14,6 +14,8 @@ struct CodecArgs {
     float centroid[16];
     float threshold[15];
     int32_t d, bits, qjl_m;
+    int32_t residual;        // TQ_RES_*
+    uint32_t sign_mask2[8];  // second sign basis (TQ_RES_SRHT)
 };
 
 struct EncodeArgs {

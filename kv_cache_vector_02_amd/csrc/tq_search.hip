@@ -50,7 +50,22 @@ __global__ __launch_bounds__(64) void search_qprep_kernel(SearchArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) a.qrot[(int64_t)(gl * 8 + e) * a.n_q + qi] = v[e] * (1.0f / (float)D);
     }
-    if (m > 0) {
+    if (m > 0 && a.c.residual != TQ_RES_QJL) {
+        // m = D: the SRHT projection H(D2 q_rot) in registers, or Direct
+        // Sign's q_rot itself with the constant 1 in place of sqrt(pi/2)/m
+        float ps = 1.0f / sqrtf((float)D);
+        if (a.c.residual == TQ_RES_SRHT) {
+            const uint32_t sbits2 = (a.c.sign_mask2[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = as_f(as_u(v[e]) ^ (((sbits2 >> e) & 1u) << 31));
+            fwht<LPV>(v, gl);
+            ps *= sqrtf(1.57079632679489662f) / (float)m;
+        }
+        if (valid) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a.qrot[(int64_t)(D + gl * 8 + e) * a.n_q + qi] = v[e] * ps;
+        }
+    } else if (m > 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) rot[grp][gl * 8 + e] = v[e];
         __syncthreads();

@@ -349,3 +349,42 @@ def test_attention_switch_argument_errors():
     assert call(sparse=float("nan")) == tq.TQ_EINVAL
     assert call(cols=0) == tq.TQ_EINVAL
     assert call(cols=tq.TQ_MAX_QUERY_COLS + 1) == tq.TQ_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+def test_codebook_ex_residual_kinds(d):
+    """tq_codebook_ex: the second sign basis and the residual widths agree with
+    the oracle; inconsistent kinds and widths are refused."""
+    for kind in (tq.TQ_RES_SRHT, tq.TQ_RES_SIGN):
+        c = tq.tq_codebook_ex(3, d, 77 + d, kind)
+        ref = o.Codec(3, d, 77 + d, residual=kind)
+        assert c.residual == kind and c.qjl_m == d == ref.qjl_m
+        assert np.array_equal(np.array(c.signs2), ref.signs2)
+        assert np.array_equal(np.array(c.signs), ref.signs)
+    plain = tq.tq_codebook(3, d, 1, 0)
+    assert plain.residual == tq.TQ_RES_NONE and np.array_equal(np.array(plain.signs2), o.Codec(3, d, 1).signs2)
+    assert tq.tq_codebook(3, d, 1, 32).residual == tq.TQ_RES_QJL
+    out = tq.tq_codec()
+    ex = lambda *a: tq.raw_call("tq_codebook_ex", 3, d, ctypes.c_uint64(0), *a, ctypes.byref(out))  # noqa: E731
+    assert ex(tq.TQ_RES_SRHT, d) == tq.TQ_OK
+    assert ex(tq.TQ_RES_SRHT, 32 if d != 32 else 64) == tq.TQ_EUNSUPPORTED
+    assert ex(tq.TQ_RES_QJL, 0) == tq.TQ_EUNSUPPORTED
+    assert ex(tq.TQ_RES_NONE, 32) == tq.TQ_EUNSUPPORTED
+    assert ex(7, 0) == tq.TQ_EUNSUPPORTED
+
+
+def test_structured_residuals_need_no_projection():
+    """SRHT and Direct Sign keys pass the argument checks without S: with a
+    too-small workspace the call fails at the workspace check that follows
+    (nothing is launched), while QJL keys without S fail before it."""
+    P = FAKE
+    vc = tq.tq_codebook(2, 128, 0)
+
+    def call(kc):
+        ws = tq.tq_attn_workspace_bytes(kc, vc, 2, 14, 2, 1000)
+        return tq.raw_call("tq_attn_decode", ctypes.byref(kc), ctypes.byref(vc), P, 1, 2, 14, 2, P, 1000,
+                           P, P, P, P, None, P, P, ctypes.c_float(0.1), P, P, ws - 1, None)
+
+    assert call(tq.tq_codebook_ex(3, 128, 0, tq.TQ_RES_SRHT)) == tq.TQ_EWORKSPACE
+    assert call(tq.tq_codebook_ex(3, 128, 0, tq.TQ_RES_SIGN)) == tq.TQ_EWORKSPACE
+    assert call(tq.tq_codebook(3, 128, 0, 128)) == tq.TQ_EINVAL

@@ -67,7 +67,7 @@ def gpu_attn(tq, kc, vc, q, ctx_len, dev, scale, S=None):
 
 
 def run_case(tq, B, Hkv, g, cap, ctx_len, kbits, vbits, d=128, qdtype=torch.float16, m=0, seed=0,
-             keys=None, values=None):
+             keys=None, values=None, residual=None):
     Hq = Hkv * g
     if keys is None:
         kk = torch.stack([synth.kv_block(Hkv, cap, d, seed + b, dtype=torch.float32)[0] for b in range(B)])
@@ -77,9 +77,12 @@ def run_case(tq, B, Hkv, g, cap, ctx_len, kbits, vbits, d=128, qdtype=torch.floa
     K = kk.numpy().astype(np.float64)
     V = vv.numpy().astype(np.float64)
     q = synth.normal((B, Hq, d), seed=seed + 99, dtype=qdtype)
-    S = synth.qjl_projection(m, d, seed=seed + 7) if m else None
-    kc_r, vc_r = o.Codec(kbits, d, seed + 1, m), o.Codec(vbits, d, seed + 1)
-    kc, vc = tq.tq_codebook(kbits, d, seed + 1, m), tq.tq_codebook(vbits, d, seed + 1)
+    S = synth.qjl_projection(m, d, seed=seed + 7) if m and residual in (None, o.RES_QJL) else None
+    if residual in (o.RES_SRHT, o.RES_SIGN):
+        kc_r, kc = o.Codec(kbits, d, seed + 1, residual=residual), tq.tq_codebook_ex(kbits, d, seed + 1, residual)
+    else:
+        kc_r, kc = o.Codec(kbits, d, seed + 1, m), tq.tq_codebook(kbits, d, seed + 1, m)
+    vc_r, vc = o.Codec(vbits, d, seed + 1), tq.tq_codebook(vbits, d, seed + 1)
     cache = oracle_cache(K, V, kc_r, vc_r, None if S is None else S.numpy().astype(np.float64))
     scale = 1.0 / math.sqrt(d)
     got = gpu_attn(tq, kc, vc, q.cuda(), ctx_len, to_dev(cache), scale, None if S is None else S.cuda())
@@ -249,3 +252,12 @@ def test_split_count_invariance(tq, splits, monkeypatch):
     else:
         monkeypatch.delenv("TQ_ATTN_SPLITS", raising=False)
     run_case(tq, B=2, Hkv=2, g=7, cap=1000, ctx_len=[1000, 317], kbits=4, vbits=2, seed=31)
+
+
+@pytest.mark.parametrize("residual", [o.RES_SRHT, o.RES_SIGN])
+@pytest.mark.parametrize("d", [128, 256])
+def test_structured_residual_keys(tq, residual, d):
+    """Keys with SRHT QJL or Direct Sign residual bits: the scan's residual
+    term uses the structured projection of the query."""
+    run_case(tq, B=2, Hkv=1, g=3, cap=800, ctx_len=[800, 217], kbits=3, vbits=2, d=d, qdtype=torch.float32,
+             seed=50 + d + residual, residual=residual)

@@ -185,3 +185,23 @@ def test_encode_kv_matches_two_encodes_and_oracle(tq, kbits, vbits, m, dtype, n)
             parity.compare_halves(pl["gamma"].cpu().numpy().view(np.uint16), ref["gamma64"], ref["gamma"],
                                   skip=bad_rows)
             parity.compare_qjl(pl["qjl"].cpu().numpy(), ref, S_side.numpy(), ref_codec, bad_rows)
+
+
+@pytest.mark.parametrize("kind", [o.RES_SRHT, o.RES_SIGN])
+@pytest.mark.parametrize("d,bits,dtype", [(32, 2, torch.float32), (64, 3, torch.float16), (128, 3, torch.bfloat16),
+                                          (256, 4, torch.float16)])
+def test_structured_residuals(tq, kind, d, bits, dtype):
+    """SRHT QJL (signs of H(D2 r)) and Direct Sign (signs of r, mean |r|):
+    codes, norms, residual bits (band rule against the oracle's projection)
+    and gamma against the oracle, over ragged row counts."""
+    x = synth.normal((777, d), seed=40 + d + kind, dtype=torch.float32) * 3
+    codec = tq.tq_codebook_ex(bits, d, 5 + d, kind)
+    ref_codec = o.Codec(bits, d, 5 + d, residual=kind)
+    assert codec.qjl_m == d == ref_codec.qjl_m
+    xs = x.to(dtype)
+    g = gpu_encode(tq, codec, xs.cuda())
+    ref = o.encode(xs.float().numpy().astype(np.float64), ref_codec)
+    _, bad_rows = parity.compare_codes(g["codes"], ref, ref_codec)
+    parity.compare_halves(g["norms"], ref["norm"], ref["norms"])
+    parity.compare_halves(g["gamma"], ref["gamma64"], ref["gamma"], skip=bad_rows)
+    parity.compare_qjl(g["qjl"], ref, ref_codec.projection(), ref_codec, bad_rows)

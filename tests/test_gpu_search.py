@@ -37,17 +37,20 @@ def gpu_search(tq, codec, q, enc, S, k):
     ids = torch.empty(n_q, k, dtype=torch.int64, device="cuda")
     m = codec.qjl_m
     tq.tq_ip_search(codec, q.cuda(), dev["codes"], dev["norms"], dev["qjl"] if m else None,
-                    dev["gamma"] if m else None, S.cuda() if m else None, k, scores, ids, ws)
+                    dev["gamma"] if m else None, S.cuda() if S is not None else None, k, scores, ids, ws)
     torch.cuda.synchronize()
     return scores.cpu().numpy(), ids.cpu().numpy()
 
 
-def check_search(tq, n_db, n_q, d, bits, m, k, seed):
+def check_search(tq, n_db, n_q, d, bits, m, k, seed, residual=None):
     db, q, S = synth.search_inputs(n_db, n_q, d, max(m, 32), seed=seed)
-    S = S[:m] if m else None
-    codec = tq.tq_codebook(bits, d, seed, m)
-    codec_r = o.Codec(bits, d, seed, m)
-    S64 = S.numpy().astype(np.float64) if m else None
+    S = S[:m] if m and residual in (None, o.RES_QJL) else None
+    if residual in (o.RES_SRHT, o.RES_SIGN):
+        codec, codec_r = tq.tq_codebook_ex(bits, d, seed, residual), o.Codec(bits, d, seed, residual=residual)
+        m = d
+    else:
+        codec, codec_r = tq.tq_codebook(bits, d, seed, m), o.Codec(bits, d, seed, m)
+    S64 = S.numpy().astype(np.float64) if S is not None else None
     enc = oracle_db(db.numpy().astype(np.float64), codec_r, S64)
     g_s, g_i = gpu_search(tq, codec, q, enc, S, k)
     est = o.ip_scores(q.numpy().astype(np.float64), enc["codes"], enc["norms"], enc["qjl"], enc["gamma"], S64, codec_r)
@@ -100,3 +103,9 @@ def test_search_full_size_sampled_queries(tq):
     for j, i in enumerate(rows):
         assert np.all(np.abs(g_s[i] - est[j, g_i[i]]) <= parity.SEARCH_TOL)
     parity.assert_topk_ids(g_i[rows], est, k)
+
+
+@pytest.mark.parametrize("residual", [o.RES_SRHT, o.RES_SIGN])
+def test_search_structured_residuals(tq, residual):
+    check_search(tq, n_db=3000, n_q=40, d=256, bits=3, m=0, k=10, seed=7 + residual, residual=residual)
+    check_search(tq, n_db=1000, n_q=17, d=128, bits=2, m=0, k=5, seed=9 + residual, residual=residual)
