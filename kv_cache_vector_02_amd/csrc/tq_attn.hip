@@ -14,24 +14,24 @@
 namespace tqi {
 
 // Resident split blocks per compute unit for this variant (cached).
-static int split_blocks_any(int d, int kb, int vb, int G, bool qjl) {
-    static std::atomic<int> cache[2][4][4][8][2];
-    std::atomic<int>& c = cache[d == 128 ? 0 : 1][kb - 1][vb - 1][G - 1][qjl ? 1 : 0];
+static int split_blocks_any(int d, int kb, int vb, bool qjl) {
+    static std::atomic<int> cache[2][4][4][2];
+    std::atomic<int>& c = cache[d == 128 ? 0 : 1][kb - 1][vb - 1][qjl ? 1 : 0];
     int nb = c.load(std::memory_order_relaxed);
     if (nb > 0) return nb;
     if (d == 128) {
         switch (kb) {
-            case 1: nb = split_blocks_dk<128, 1>(vb, G, qjl); break;
-            case 2: nb = split_blocks_dk<128, 2>(vb, G, qjl); break;
-            case 3: nb = split_blocks_dk<128, 3>(vb, G, qjl); break;
-            default: nb = split_blocks_dk<128, 4>(vb, G, qjl); break;
+            case 1: nb = split_blocks_dk<128, 1>(vb, qjl); break;
+            case 2: nb = split_blocks_dk<128, 2>(vb, qjl); break;
+            case 3: nb = split_blocks_dk<128, 3>(vb, qjl); break;
+            default: nb = split_blocks_dk<128, 4>(vb, qjl); break;
         }
     } else {
         switch (kb) {
-            case 1: nb = split_blocks_dk<256, 1>(vb, G, qjl); break;
-            case 2: nb = split_blocks_dk<256, 2>(vb, G, qjl); break;
-            case 3: nb = split_blocks_dk<256, 3>(vb, G, qjl); break;
-            default: nb = split_blocks_dk<256, 4>(vb, G, qjl); break;
+            case 1: nb = split_blocks_dk<256, 1>(vb, qjl); break;
+            case 2: nb = split_blocks_dk<256, 2>(vb, qjl); break;
+            case 3: nb = split_blocks_dk<256, 3>(vb, qjl); break;
+            default: nb = split_blocks_dk<256, 4>(vb, qjl); break;
         }
     }
     if (nb <= 0) return 1;  // occupancy unknown (no device): not cached
@@ -72,7 +72,7 @@ void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int v
     }
     *heads_per_chunk = G;
     const int64_t units = (int64_t)batch * hkv * (gv / G);
-    const int64_t slots = (int64_t)device_cus() * split_blocks_any(d, kb, vb, G, qjl);
+    const int64_t slots = (int64_t)device_cus() * split_blocks_any(d, kb, vb, qjl);
     const int64_t max_splits = ctx_cap > 0 ? (ctx_cap + 63) / 64 : 1;
     int64_t best_sp = 1, best_per = ((ctx_cap > 0 ? ctx_cap : 1) + 63) & ~(int64_t)63;
     double best_cost = -1.0;

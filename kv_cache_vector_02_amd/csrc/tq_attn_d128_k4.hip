@@ -1,5 +1,5 @@
 // Split-K decode attention kernels for d=128, 4-bit keys (all value widths
-// and head-chunk sizes).  One translation unit per (d, key bits) keeps the
+// and switch variants).  One translation unit per (d, key bits) keeps the
 // template instantiations compiling in parallel.
 #include "tq_attn_kernels.h"
 
@@ -9,7 +9,7 @@ hipError_t launch_split_dk<128, 4>(const AttnArgs& a, hipStream_t s) {
     return attn::launch_split_dk<128, 4>(a, s);
 }
 template <>
-int split_blocks_dk<128, 4>(int vb, int G, bool qjl) {
-    return attn::split_blocks_dk<128, 4>(vb, G, qjl);
+int split_blocks_dk<128, 4>(int vb, bool qjl) {
+    return attn::split_blocks_dk<128, 4>(vb, qjl);
 }
 }  // namespace tqi

@@ -214,9 +214,9 @@ constexpr bool split_tables(int d, int kb, int vb, bool qjl) {
     return !qjl && split_fits(d, kb, vb, qjl, split_waves(d, kb, vb, qjl));
 }
 
-template <int D, int KB, int VB, int G, bool QJL>
+template <int D, int KB, int VB, bool QJL>
 struct Cfg {
-    static_assert(G >= 1 && G <= 8, "at most eight query heads per block");
+    static constexpr int GMAX = 8;                  // query rows per block (at most)
     static constexpr int NW = split_waves(D, KB, VB, QJL);  // waves per block
     static constexpr int NT = 64 * NW;              // threads per block
     // K side
@@ -257,10 +257,10 @@ struct Cfg {
     static constexpr int WAVE_DW = wave_dw(D, VB);
     static constexpr int QJL_DW = qjl_dw(QJL);      // QJL B operands + sign table
     static constexpr int LOOP_DW = TABB / 4 + NW * WAVE_DW + QJL_DW;
-    static constexpr int MERGE_DW = NW * G * (D + 2);
+    static constexpr int MERGE_DW = NW * GMAX * (D + 2);
     static constexpr int SMEM_DW = LOOP_DW > MERGE_DW ? LOOP_DW : MERGE_DW;
     static_assert(4 * SMEM_DW <= kLdsBytes, "split kernel exceeds LDS");
-    static_assert(G * D <= NW * WAVE_DW, "rotated queries exceed the wave areas");
+    static_assert(GMAX * D <= NW * WAVE_DW, "rotated queries exceed the wave areas");
     // K codes double-buffered (loaded a whole tile ahead) where the register
     // budget of two waves per SIMD leaves room
     static constexpr bool KDB = NW <= 8 && !QJL;
@@ -361,16 +361,24 @@ __device__ __forceinline__ void fetch_v(uint32_t (&rv)[C::VTW], uint32_t& rn, ui
 // block takes G consecutive rows vl.  Row (b, c, h) is stored at index
 // (b * ncols + c) * hq + h of the query, workspace and output arrays, and
 // column c attends over the first ctx - (ncols - 1 - c) tokens (causal).
+template <bool MQ>
 __device__ __forceinline__ int64_t query_row(const AttnArgs& a, int b, int kvh, int vl) {
+    if constexpr (!MQ) return (int64_t)b * a.hq + kvh * a.g + vl;  // one column
     const int c = vl / a.g;
     return ((int64_t)b * a.ncols + c) * a.hq + kvh * a.g + (vl - c * a.g);
 }
 
-template <int D, int KB, int VB, int G, bool QJL>
+// One instance per (D, KB, VB, QJL) and switch set: SPARSE = the sparse-V
+// switch, MQ = more than one query column, G8 = eight query rows per block.
+// Other row counts G (< 8) are a runtime value (the matrix-core columns are
+// fixed at 8 rows); the full block gets its own instance because a
+// compile-time G keeps the 12-wave variants free of register spills.
+template <int D, int KB, int VB, bool QJL, bool SPARSE, bool MQ, bool G8>
 __global__ __launch_bounds__(64 * split_waves(D, KB, VB, QJL))
 __attribute__((amdgpu_waves_per_eu(split_waves(D, KB, VB, QJL) / 4)))
 void split_kernel(AttnArgs a) {
-    using C = Cfg<D, KB, VB, G, QJL>;
+    using C = Cfg<D, KB, VB, QJL>;
+    const int G = G8 ? 8 : a.heads_per_chunk;
     __shared__ __attribute__((aligned(16))) uint32_t smem[C::SMEM_DW];
     uint8_t* tab = reinterpret_cast<uint8_t*>(smem);
     uint32_t* waves_lds = smem + C::TABB / 4;
@@ -391,7 +399,7 @@ void split_kernel(AttnArgs a) {
     const int t_end = (t_beg + (int)a.split_tokens < ctx) ? t_beg + (int)a.split_tokens : ctx;
     const int vl0 = chunk * G;  // first row of this block (see query_row)
     // tokens a row may see: ctx for the last column, fewer for earlier ones
-    const int ctx_min = ctx - (a.ncols - 1 - vl0 / a.g);  // the block's first row sees the fewest
+    const int ctx_min = MQ ? ctx - (a.ncols - 1 - vl0 / a.g) : ctx;  // the block's first row sees the fewest
     const int64_t kvrow = ((int64_t)b * a.hkv + kvh) * a.ctx_cap;
     const uint8_t* kcodes = a.k_codes + kvrow * C::RBK;
     const uint8_t* vcodes = a.v_codes + kvrow * C::RBV;
@@ -411,7 +419,7 @@ void split_kernel(AttnArgs a) {
     float qx[8];
     if (qwave) {
         if (qhl < G) {
-            const int64_t e0 = query_row(a, b, kvh, vl0 + qhl) * D + qgl * 8;
+            const int64_t e0 = query_row<MQ>(a, b, kvh, vl0 + qhl) * D + qgl * 8;
             if (a.q_dtype == TQ_F32) load8<0>(static_cast<const float*>(a.q) + e0, qx);
             else if (a.q_dtype == TQ_F16) load8<1>(static_cast<const uint16_t*>(a.q) + e0, qx);
             else load8<2>(static_cast<const uint16_t*>(a.q) + e0, qx);
@@ -446,7 +454,7 @@ void split_kernel(AttnArgs a) {
         fwht<QLPV>(qx, qgl);
         float qs = a.scale * kLog2e / (float)D;
         if (a.score_mode != 0 && qhl < G) {
-            const int nr = ctx - (a.ncols - 1 - (vl0 + qhl) / a.g);  // tokens this row attends over
+            const int nr = MQ ? ctx - (a.ncols - 1 - (vl0 + qhl) / a.g) : ctx;  // tokens this row attends over
             qs *= score_factor(a, nr > 0 ? nr : 0);
         }
         if (qhl < G) {
@@ -508,7 +516,7 @@ void split_kernel(AttnArgs a) {
     // KE = 4: d0 d1 d2 d3 d0 d1 d2 d3); likewise the QJL projection
     const int hh = n & 7;
     const bool lo_col = n >= 8, head_ok = hh < G;
-    const int ctx_row = ctx - (a.ncols - 1 - (vl0 + hh) / a.g);  // tokens row hh may see
+    const int ctx_row = MQ ? ctx - (a.ncols - 1 - (vl0 + hh) / a.g) : ctx;  // tokens row hh may see
     half8_t bq[C::KSTEPS];
     float qinv;
     {
@@ -523,7 +531,7 @@ void split_kernel(AttnArgs a) {
                 qv[ks][i] = head_ok ? x : 0.0f;
                 amax = fmaxf(amax, fabsf(qv[ks][i]));
             }
-        const float* qp = a.qproj + query_row(a, b, kvh, vl0 + (head_ok ? hh : 0)) * m;
+        const float* qp = a.qproj + query_row<MQ>(a, b, kvh, vl0 + (head_ok ? hh : 0)) * m;
         if constexpr (QJL) {
             for (int ks = 0; ks < (m >> 5); ++ks)
                 for (int j = 0; j < 8; ++j)
@@ -582,7 +590,7 @@ void split_kernel(AttnArgs a) {
     const uint32_t koff = (uint32_t)(lane % C::KSL) * C::KENT;
     const uint32_t voff = C::VOFF0 + (uint32_t)(lane % C::VSL) * C::VENT;
 
-    const bool sparse = a.sparse_log2 > -INFINITY;  // uniform: sparse V on
+    constexpr bool sparse = SPARSE;
     float m_ref = -INFINITY, l_lane = 0.0f;  // head n's reference max / this lane's partial sum
     // V sums D[nb][i]: head 4*grp + i, dim NB*n + nb, in units of 2^wsh
     floatx4_t vacc[C::NB];
@@ -695,9 +703,18 @@ void split_kernel(AttnArgs a) {
             dsc[j][2] = fmaf(sacc[j][2], kq.z, -m_ref);
             dsc[j][3] = fmaf(sacc[j][3], kq.w, -m_ref);
         }
-        const int row_end = ctx_row < t_end ? ctx_row : t_end;
-        int lim = row_end - t0 - 4 * grp;  // token 16j + 4grp + v is valid iff 16j + v < lim
-        if ((ctx_min < t_end ? ctx_min : t_end) - t0 < 64) {
+        // token 16j + 4grp + v is valid iff 16j + v < lim
+        int lim;
+        bool partial;
+        if constexpr (MQ) {
+            const int row_end = ctx_row < t_end ? ctx_row : t_end;
+            lim = row_end - t0 - 4 * grp;
+            partial = (ctx_min < t_end ? ctx_min : t_end) - t0 < 64;
+        } else {
+            lim = rem - 4 * grp;
+            partial = rem < 64;
+        }
+        if (partial) {
             // keeps the compares inside this (last-tile) branch
             asm volatile("" : "+v"(lim));
 #pragma unroll
@@ -956,7 +973,7 @@ void split_kernel(AttnArgs a) {
                 val = fmaf(mrg[(w * G + h) * (D + 2) + i], exp2f(mw - mx), val);
             }
         }
-        a.part[(query_row(a, b, kvh, vl0 + h) * a.splits + split) * (D + 2) + i] = val;
+        a.part[(query_row<MQ>(a, b, kvh, vl0 + h) * a.splits + split) * (D + 2) + i] = val;
     }
 }
 
@@ -1194,71 +1211,63 @@ __global__ __launch_bounds__(256) void window_kernel(AttnArgs a) {
     combine_head<D>(a, bh, gl, tg == 0, m, l, y);
 }
 
-template <int D, int KB, int VB, int G>
-hipError_t launch_split(const AttnArgs& a, hipStream_t s) {
-    dim3 grid(a.splits, a.hkv * a.chunks, a.batch);
-    if (a.kc.qjl_m > 0)
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, G, true>), grid, dim3(64 * split_waves(D, KB, VB, true)), 0, s, a);
+template <int D, int KB, int VB, bool QJL, bool G8>
+void launch_split_g(const AttnArgs& a, hipStream_t s) {
+    const dim3 grid(a.splits, a.hkv * a.chunks, a.batch);
+    const dim3 block(64 * split_waves(D, KB, VB, QJL));
+    const bool sparse = a.sparse_log2 > -INFINITY, mq = a.ncols > 1;
+    if (sparse && mq)
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, true, true, G8>), grid, block, 0, s, a);
+    else if (sparse)
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, true, false, G8>), grid, block, 0, s, a);
+    else if (mq)
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, false, true, G8>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, G, false>), grid, dim3(64 * split_waves(D, KB, VB, false)), 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, false, false, G8>), grid, block, 0, s, a);
+}
+
+template <int D, int KB, int VB, bool QJL>
+hipError_t launch_split_q(const AttnArgs& a, hipStream_t s) {
+    if (a.heads_per_chunk == 8) launch_split_g<D, KB, VB, QJL, true>(a, s);
+    else launch_split_g<D, KB, VB, QJL, false>(a, s);
     return hipGetLastError();
 }
 
-// Resident split blocks per compute unit for one split-kernel variant.
-template <int D, int KB, int VB, int G>
+template <int D, int KB, int VB>
+hipError_t launch_split(const AttnArgs& a, hipStream_t s) {
+    return a.kc.qjl_m > 0 ? launch_split_q<D, KB, VB, true>(a, s) : launch_split_q<D, KB, VB, false>(a, s);
+}
+
+// Resident split blocks per compute unit for one split-kernel variant (the
+// switch variants use the same LDS and launch bounds).
+template <int D, int KB, int VB>
 int split_blocks(bool qjl) {
     int nb = 0;
     const hipError_t e =
-        qjl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, G, true>, 64 * split_waves(D, KB, VB, true), 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, G, false>, 64 * split_waves(D, KB, VB, false), 0);
+        qjl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, true, false, false, true>,
+                                                          64 * split_waves(D, KB, VB, true), 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, false, false, false, true>,
+                                                          64 * split_waves(D, KB, VB, false), 0);
     return e == hipSuccess && nb > 0 ? nb : 0;
-}
-
-template <int D, int KB, int VB>
-hipError_t launch_split_g(const AttnArgs& a, hipStream_t s) {
-    switch (a.heads_per_chunk) {
-        case 1: return launch_split<D, KB, VB, 1>(a, s);
-        case 2: return launch_split<D, KB, VB, 2>(a, s);
-        case 3: return launch_split<D, KB, VB, 3>(a, s);
-        case 4: return launch_split<D, KB, VB, 4>(a, s);
-        case 5: return launch_split<D, KB, VB, 5>(a, s);
-        case 6: return launch_split<D, KB, VB, 6>(a, s);
-        case 7: return launch_split<D, KB, VB, 7>(a, s);
-        default: return launch_split<D, KB, VB, 8>(a, s);
-    }
-}
-
-template <int D, int KB, int VB>
-int split_blocks_g(int G, bool qjl) {
-    switch (G) {
-        case 1: return split_blocks<D, KB, VB, 1>(qjl);
-        case 2: return split_blocks<D, KB, VB, 2>(qjl);
-        case 3: return split_blocks<D, KB, VB, 3>(qjl);
-        case 4: return split_blocks<D, KB, VB, 4>(qjl);
-        case 5: return split_blocks<D, KB, VB, 5>(qjl);
-        case 6: return split_blocks<D, KB, VB, 6>(qjl);
-        case 7: return split_blocks<D, KB, VB, 7>(qjl);
-        default: return split_blocks<D, KB, VB, 8>(qjl);
-    }
 }
 
 template <int D, int KB>
 hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s) {
     switch (a.vc.bits) {
-        case 1: return launch_split_g<D, KB, 1>(a, s);
-        case 2: return launch_split_g<D, KB, 2>(a, s);
-        case 3: return launch_split_g<D, KB, 3>(a, s);
-        default: return launch_split_g<D, KB, 4>(a, s);
+        case 1: return launch_split<D, KB, 1>(a, s);
+        case 2: return launch_split<D, KB, 2>(a, s);
+        case 3: return launch_split<D, KB, 3>(a, s);
+        default: return launch_split<D, KB, 4>(a, s);
     }
 }
 
 template <int D, int KB>
-int split_blocks_dk(int vb, int G, bool qjl) {
+int split_blocks_dk(int vb, bool qjl) {
     switch (vb) {
-        case 1: return split_blocks_g<D, KB, 1>(G, qjl);
-        case 2: return split_blocks_g<D, KB, 2>(G, qjl);
-        case 3: return split_blocks_g<D, KB, 3>(G, qjl);
-        default: return split_blocks_g<D, KB, 4>(G, qjl);
+        case 1: return split_blocks<D, KB, 1>(qjl);
+        case 2: return split_blocks<D, KB, 2>(qjl);
+        case 3: return split_blocks<D, KB, 3>(qjl);
+        default: return split_blocks<D, KB, 4>(qjl);
     }
 }
 
@@ -1268,6 +1277,6 @@ int split_blocks_dk(int vb, int G, bool qjl) {
 template <int D, int KB>
 hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s);
 template <int D, int KB>
-int split_blocks_dk(int vb, int G, bool qjl);
+int split_blocks_dk(int vb, bool qjl);
 
 }  // namespace tqi

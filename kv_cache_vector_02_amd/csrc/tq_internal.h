@@ -104,7 +104,7 @@ void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int v
 template <int D, int KB>
 hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s);
 template <int D, int KB>
-int split_blocks_dk(int vb, int G, bool qjl);
+int split_blocks_dk(int vb, bool qjl);
 size_t attn_workspace(int batch, int hq, int d, int m, int splits);
 
 struct SearchArgs {
