@@ -2,6 +2,8 @@
 // argument validation, workspace sizing and kernel dispatch.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include <math.h>
 #include <string.h>
 
@@ -103,6 +105,91 @@ int finish(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EDEVICE; }
 }  // namespace
 
 namespace tqi {
+// Bin table of the encoder's quantizer.  The index of z = w / n is the number
+// of thresholds below it; with bins b = floor(z * s + off) that each hold at
+// most one threshold, every value away from the bin edges needs the count
+// below its bin and one compare with the bin's threshold.  The plan puts no
+// threshold within 1/64 of a bin edge, far beyond the rounding of z * s + off
+// in float32, so a value whose bin is misjudged lies away from any threshold
+// and the count and compare still give its exact index.  Bins cover
+// |z| <= sqrt(d) (the largest |w| / n) with margin; qt_n = 0 leaves the
+// encoder to count the thresholds one by one.  The search starts at the
+// smallest scale whose bins are narrower than the closest pair of thresholds,
+// and plans are cached per (d, bits, thresholds): every call fills the
+// launch arguments.
+struct QtabPlan {
+    float scale, off, inv_scale;
+    int32_t n;
+};
+
+static QtabPlan search_qtab(int d, int nt, const float* th) {
+    QtabPlan p{0.0f, 0.0f, 0.0f, 0};
+    double gap = INFINITY;
+    for (int j = 0; j < nt; ++j) {
+        if (!std::isfinite(th[j]) || (j > 0 && !(th[j] > th[j - 1]))) return p;
+        if (j > 0) gap = std::fmin(gap, (double)th[j] - (double)th[j - 1]);
+    }
+    const double zmax = std::sqrt((double)d) * 1.001 + 0.5;
+    const double edge = 1.0 / 64.0;
+    const int si0 = nt > 1 ? (int)std::ceil((1.0 / gap - 1.0) * 8.0) : 0;
+    for (int si = si0 < 0 ? 0 : si0; si <= 504; ++si) {
+        const double s = 1.0 + 0.125 * si;  // bins per unit of z, exact in float32
+        for (int fi = 0; fi < 64; ++fi) {
+            const double off = std::ceil(zmax * s) + 1.0 + fi / 64.0;
+            const int nb = (int)std::floor(zmax * s + off) + 2;
+            if (nb > kQTabMax) return p;  // larger scales need more bins still
+            bool ok = true;
+            double prev = -1.0;
+            for (int j = 0; j < nt && ok; ++j) {
+                const double x = (double)th[j] * s + off, b = std::floor(x), fr = x - b;
+                ok = fr >= edge && fr <= 1.0 - edge && b > prev;
+                prev = b;
+            }
+            if (ok) return QtabPlan{(float)s, (float)off, (float)(1.0 / s), nb};
+        }
+    }
+    return p;
+}
+
+static void plan_qtab(const tq_codec* c, CodecArgs* a) {
+    struct Entry {
+        int d, bits;
+        float th[15];
+        QtabPlan plan;
+    };
+    static std::mutex mu;
+    static Entry cache[16];
+    static int used = 0, next = 0;
+    const int nt = (1 << c->bits) - 1;
+    QtabPlan plan;
+    bool hit = false;
+    {
+        std::lock_guard<std::mutex> g(mu);
+        for (int i = 0; i < used && !hit; ++i) {
+            const Entry& e = cache[i];
+            if (e.d == c->d && e.bits == c->bits && memcmp(e.th, c->threshold, nt * sizeof(float)) == 0) {
+                plan = e.plan;
+                hit = true;
+            }
+        }
+    }
+    if (!hit) {
+        plan = search_qtab(c->d, nt, c->threshold);
+        std::lock_guard<std::mutex> g(mu);
+        Entry& e = cache[next];
+        e.d = c->d;
+        e.bits = c->bits;
+        memcpy(e.th, c->threshold, nt * sizeof(float));
+        e.plan = plan;
+        next = (next + 1) % 16;
+        used = used < 16 ? used + 1 : 16;
+    }
+    a->qt_scale = plan.scale;
+    a->qt_off = plan.off;
+    a->qt_inv_scale = plan.inv_scale;
+    a->qt_n = plan.n;
+}
+
 void fill_codec_args(const tq_codec* c, CodecArgs* a) {
     memcpy(a->sign_mask, c->sign_mask, sizeof(a->sign_mask));
     memcpy(a->centroid, c->centroid, sizeof(a->centroid));
@@ -112,6 +199,7 @@ void fill_codec_args(const tq_codec* c, CodecArgs* a) {
     a->qjl_m = c->qjl_m;
     a->residual = c->residual;
     memcpy(a->sign_mask2, c->sign_mask2, sizeof(a->sign_mask2));
+    plan_qtab(c, a);
 }
 }  // namespace tqi
 

@@ -120,6 +120,85 @@ __device__ __forceinline__ void fwht(float (&v)[8], int gl) {
 }
 
 // ---------------------------------------------------------------------------
+// The same transform with every cross-lane stage as one fused DPP
+// multiply-add, y_l = x_l + c_l * x_{l ^ v} (v_fmac_f32 with the partner read
+// through DPP), for the encoder, whose cost is its VALU instruction count.
+// Partners l ^ 1, l ^ 2 (quad_perm), l ^ 7 (row_half_mirror), l ^ 8
+// (row_ror:8) and l ^ 16 (ds_swizzle), with c_l = (-1)^popcount(l & w) for
+// w = 5, 6, 4, 8, 16.  Every stage keeps a + b in one lane of a pair and
+// b - a (not a - b) in the other, and the partners are not the unit steps of
+// the plain butterfly; the network still equals H, applied to the lane blocks
+// in a fixed order: lane gl must hold the input elements of lane
+// fwht_src_lane(gl) (their 8 elements in place) to receive H x in Sylvester
+// order.  (Both facts are exact identities of the +-1 matrices, checked for
+// every d by multiplying the stages out.)
+// ---------------------------------------------------------------------------
+template <int LPV>
+__device__ __forceinline__ int fwht_src_lane(int gl) {
+    static_assert(LPV == 4 || LPV == 8 || LPV == 16 || LPV == 32, "lane group of 4..32 lanes");
+    if constexpr (LPV == 4) return gl ^ 3;
+    // lanes 0..7 of each block of 8 read 7 2 1 4 0 5 6 3 (affine in the lane
+    // bits); the blocks of 8 come in reverse order
+    const int lo = (int)((0x36504127u >> (4 * (gl & 7))) & 7u);
+    return lo | ((~gl) & (LPV - 1) & ~7);
+}
+
+template <int W>
+__device__ __forceinline__ float parity_sign(int gl) {
+    return (__builtin_popcount(gl & W) & 1) ? -1.0f : 1.0f;
+}
+
+// x[e] += c * x[e] of the DPP partner lane, for the 8 elements, as
+// v_fmac_f32_dpp (one instruction each).  The compiler does not fold a DPP
+// move into a multiply-add that overwrites the moved register, hence the asm;
+// the leading s_nop 1 gives the two wait states a DPP read needs after a VALU
+// write of its source (inside the block every source was written eight
+// instructions earlier).  All lanes of the wave are active where it is used.
+#define TQ_FMAC_DPP8(x, c, DPP)                                                                          \
+    asm("s_nop 1\n"                                                                                      \
+        "v_fmac_f32_dpp %0, %0, %8 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"                    \
+        "v_fmac_f32_dpp %1, %1, %8 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"                    \
+        "v_fmac_f32_dpp %2, %2, %8 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"                    \
+        "v_fmac_f32_dpp %3, %3, %8 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"                    \
+        "v_fmac_f32_dpp %4, %4, %8 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"                    \
+        "v_fmac_f32_dpp %5, %5, %8 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"                    \
+        "v_fmac_f32_dpp %6, %6, %8 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"                    \
+        "v_fmac_f32_dpp %7, %7, %8 " DPP " row_mask:0xf bank_mask:0xf bound_ctrl:1"                      \
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]) \
+        : "v"(c))
+
+template <int LPV>
+__device__ __forceinline__ void fwht_fused(float (&v)[8], int gl) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if ((e & h) == 0) {
+                const float a = v[e], b = v[e + h];
+                v[e] = a + b;
+                v[e + h] = a - b;
+            }
+        }
+    }
+    const float c1 = parity_sign<5 & (LPV - 1)>(gl), c2 = parity_sign<6 & (LPV - 1)>(gl);
+    TQ_FMAC_DPP8(v, c1, "quad_perm:[1,0,3,2]");  // l ^ 1
+    TQ_FMAC_DPP8(v, c2, "quad_perm:[2,3,0,1]");  // l ^ 2
+    if constexpr (LPV >= 8) {
+        const float c3 = parity_sign<4>(gl);
+        TQ_FMAC_DPP8(v, c3, "row_half_mirror");  // l ^ 7
+    }
+    if constexpr (LPV >= 16) {
+        const float c4 = parity_sign<8>(gl);
+        TQ_FMAC_DPP8(v, c4, "row_ror:8");  // l ^ 8
+    }
+    if constexpr (LPV >= 32) {
+        const float c5 = parity_sign<16>(gl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fmaf(xor_lane<16>(v[e]), c5, v[e]);  // l ^ 16
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Element loads: 8 consecutive elements of type DT (0 f32, 1 f16, 2 bf16).
 // `p` must be 16-byte aligned.
 // ---------------------------------------------------------------------------
@@ -131,16 +210,19 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
 }
 
+// The raw bits of 8 elements: two 16-byte words for f32, one for f16/bf16.
 template <int DT>
-__device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
+struct Raw8 {
+    uint4 w[DT == 0 ? 2 : 1];
+};
+
+template <int DT>
+__device__ __forceinline__ void unpack8(const Raw8<DT>& r, float (&v)[8]) {
     if constexpr (DT == 0) {
-        const float4* q = reinterpret_cast<const float4*>(p);
-        const float4 a = q[0], b = q[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        v[0] = as_f(r.w[0].x); v[1] = as_f(r.w[0].y); v[2] = as_f(r.w[0].z); v[3] = as_f(r.w[0].w);
+        v[4] = as_f(r.w[1].x); v[5] = as_f(r.w[1].y); v[6] = as_f(r.w[1].z); v[7] = as_f(r.w[1].w);
     } else {
-        const uint4 r = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+        const uint32_t w[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if constexpr (DT == 1) {
@@ -152,6 +234,14 @@ __device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
             }
         }
     }
+}
+
+template <int DT>
+__device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
+    Raw8<DT> r;
+#pragma unroll
+    for (int k = 0; k < (DT == 0 ? 2 : 1); ++k) r.w[k] = reinterpret_cast<const uint4*>(p)[k];
+    unpack8<DT>(r, v);
 }
 
 template <int DT>
@@ -182,6 +272,13 @@ __device__ __forceinline__ uint32_t ld_stream1(const void* p) {
 
 __device__ __forceinline__ uint32_t ld_stream_u16(const void* p) {
     return (uint32_t)__builtin_nontemporal_load(static_cast<const uint16_t*>(p));
+}
+
+// 8 elements of type DT read once (non-temporal); `p` 16-byte aligned.
+template <int DT>
+__device__ __forceinline__ void ld_stream8(const void* p, Raw8<DT>& r) {
+#pragma unroll
+    for (int k = 0; k < (DT == 0 ? 2 : 1); ++k) r.w[k] = ld_stream4(static_cast<const uint4*>(p) + k);
 }
 
 // Half norm: clamp to the largest finite half, then round to nearest even.

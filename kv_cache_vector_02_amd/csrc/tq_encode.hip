@@ -13,6 +13,8 @@
 // write-up on idea.jsleekr.com ("핵심 발견 3": bit-shift packing).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -64,38 +66,94 @@ struct VecState {
     float nrm;
 };
 
-// Load row `row` (or zeros), compute the norm, sign flip and transform.
-template <int D, int DT>
-__device__ __forceinline__ void load_rotate(const EncodeArgs& a, int64_t row, bool valid, int gl,
-                                            uint32_t sbits, VecState& st) {
+// Input elements lane gl of a group loads: those of lane fwht_src_lane(gl)
+// (the order the fused transform takes), and the sign bits of D for them.
+template <int D>
+__device__ __forceinline__ int enc_src_lane(int gl) { return fwht_src_lane<D / 8>(gl); }
+
+__device__ __forceinline__ uint32_t enc_sign_bits(const uint32_t (&mask)[8], int sl) {
+    return (mask[sl >> 2] >> ((sl & 3) * 8)) & 0xFFu;
+}
+
+// Norm, sign flip and transform of the 8 elements a lane holds (st.v, loaded
+// from lane enc_src_lane(gl)); afterwards lane gl holds elements
+// [8 gl, 8 gl + 8) of H(D x).  v_sqrt_f32 (1 ulp) gives the norm: both the
+// half norm and the code decisions already allow 1e-6 relative.
+template <int D>
+__device__ __forceinline__ void rotate(VecState& st, int gl, uint32_t sbits) {
     constexpr int LPV = D / 8;
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(st.v[e], st.v[e], ss);
+    ss = group_sum<LPV>(ss);
+    st.nrm = __builtin_amdgcn_sqrtf(ss);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.v[e] = as_f(as_u(st.v[e]) ^ (((sbits >> e) & 1u) << 31));
+    fwht_fused<LPV>(st.v, gl);
+}
+
+// The same from the raw 16-byte words of 16-bit input: the D sign flip as
+// four XORs on the packed halves (flip = the per-lane masks of
+// half_sign_masks), the squared norm by v_dot2_f32_f16 / v_dot2_f32_bf16
+// (the products of two 16-bit values are exact in float32), then unpack.
+__device__ __forceinline__ void half_sign_masks(uint32_t sbits, uint32_t (&flip)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) flip[k] = (((sbits >> (2 * k)) & 1u) << 15) | (((sbits >> (2 * k + 1)) & 1u) << 31);
+}
+
+template <int D, int DT>
+__device__ __forceinline__ void rotate_raw16(Raw8<DT>& r, const uint32_t (&flip)[4], int gl, VecState& st) {
+    static_assert(DT != 0, "16-bit input");
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+    constexpr int LPV = D / 8;
+    uint32_t w[4] = {r.w[0].x ^ flip[0], r.w[0].y ^ flip[1], r.w[0].z ^ flip[2], r.w[0].w ^ flip[3]};
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if constexpr (DT == 1) {
+            const h2_t h = __builtin_bit_cast(h2_t, w[k]);
+            ss = __builtin_amdgcn_fdot2(h, h, ss, false);
+        } else {
+            const b2_t h = __builtin_bit_cast(b2_t, w[k]);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss, false);
+        }
+    }
+    r.w[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    unpack8<DT>(r, st.v);
+    ss = group_sum<LPV>(ss);
+    st.nrm = __builtin_amdgcn_sqrtf(ss);
+    fwht_fused<LPV>(st.v, gl);
+}
+
+// Load row `row` (or zeros) from lane sl's elements, compute the norm, sign
+// flip and transform.
+template <int D, int DT>
+__device__ __forceinline__ void load_rotate(const EncodeArgs& a, int64_t row, bool valid, int gl, int sl,
+                                            uint32_t sbits, VecState& st) {
     if (valid) {
-        const char* base = static_cast<const char*>(a.x) + (row * a.x_stride + gl * 8) * elem_bytes<DT>();
+        const char* base = static_cast<const char*>(a.x) + (row * a.x_stride + sl * 8) * elem_bytes<DT>();
         load8<DT>(base, st.v);
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) st.v[e] = 0.0f;
     }
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(st.v[e], st.v[e], ss);
-    ss = group_sum<LPV>(ss);
-    st.nrm = sqrtf(ss);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.v[e] = as_f(as_u(st.v[e]) ^ (((sbits >> e) & 1u) << 31));
-    fwht<LPV>(st.v, gl);
+    rotate<D>(st, gl, sbits);
 }
 
 // Output row of input row `row` (see EncodeArgs: plain, append or prefill
 // mapping); keep = false when an append position lies outside the cache.
+// Row counts below 2^32 (every call that fits a device) take 32-bit division.
 __device__ __forceinline__ int64_t out_row(const EncodeArgs& a, int64_t row, bool& keep) {
     keep = true;
     if (!a.pos) {
         if (a.grp_rows <= 0) return row;
-        const int64_t g = row / a.grp_rows;
+        int64_t g;
+        if (a.n <= 0xFFFFFFFFll) g = (uint32_t)row / (uint32_t)a.grp_rows;
+        else g = row / a.grp_rows;
         return g * a.cap + a.grp_off + (row - g * a.grp_rows);
     }
-    const int p = a.pos[row / a.seq_heads];
+    const int p = a.pos[(uint32_t)row / (uint32_t)a.seq_heads];
     keep = p >= 0 && (int64_t)p < a.cap;
     return row * a.cap + (keep ? p : 0);
 }
@@ -117,48 +175,134 @@ __device__ __forceinline__ uint32_t pack_lane(const VecState& st, const CodecArg
     return packed;
 }
 
-template <int D, int BITS, int DT>
-__device__ __forceinline__ void encode_rows(const EncodeArgs& a, int64_t block, int64_t nblocks) {
+// The bin table of the codec's quantizer (plan_qtab on the host): entry b =
+// (#thresholds below bin b, bits of the bin's threshold or +inf).  Built by
+// the whole block (the threshold loop unrolled, so the thresholds stay in
+// scalar registers); returns after the barrier.  The bin edges come from the
+// host's reciprocal of the scale: the plan keeps every threshold 1/32 of a bin
+// from an edge, far beyond that rounding.
+template <int BITS>
+__device__ __forceinline__ void build_qtab(const CodecArgs& c, uint2* qtab) {
+    constexpr int NT = (1 << BITS) - 1;
+    for (int b = threadIdx.x; b < c.qt_n; b += blockDim.x) {
+        const float z0 = ((float)b - c.qt_off) * c.qt_inv_scale;
+        const float z1 = ((float)b + 1.0f - c.qt_off) * c.qt_inv_scale;
+        uint32_t below = 0;
+        float t = INFINITY;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const float tj = c.threshold[j];
+            below += tj < z0 ? 1u : 0u;
+            t = (tj >= z0 && tj < z1) ? tj : t;
+        }
+        qtab[b] = make_uint2(below, as_u(t));
+    }
+    __syncthreads();
+}
+
+// Packed indices of the lane's 8 values by the bin table: the count below the
+// value's bin plus one compare w > t * n with the bin's threshold (the same
+// float32 comparison as the threshold count, so the same indices).
+template <int BITS>
+__device__ __forceinline__ uint32_t pack_lane_tab(const VecState& st, const CodecArgs& c, const uint2* qtab) {
+    const float sc = st.nrm > 0.0f ? st.nrm : 1.0f;
+    const float sn = c.qt_scale / sc;
+    const float topf = (float)(c.qt_n - 1);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float w = st.v[e];
+        // bin of w / n, clamped into the table (v_med3 under IEEE min/max
+        // rules: a NaN lands in bin 0)
+        const float u = __builtin_amdgcn_fmed3f(fmaf(w, sn, c.qt_off), 0.0f, topf);
+        const uint2 ent = qtab[(uint32_t)u];
+        const uint32_t idx = ent.x + (w > as_f(ent.y) * sc ? 1u : 0u);
+        packed |= idx << (BITS * e);
+    }
+    return packed;
+}
+
+// Vectors per lane group per pass of the plain encoder: the loads of all of
+// them go out before the first is transformed, so a wave keeps kEncBatch
+// 16-byte loads per lane in flight (twice that for f32 input).  One vector's
+// loads at a time left the encoder waiting on memory.
+constexpr int kEncBatch = 2;
+
+// TAB: the codec has a bin table (qt_n > 0), else the thresholds are counted.
+template <int D, int BITS, int DT, bool TAB>
+__device__ __forceinline__ void encode_rows(const EncodeArgs& a, const uint2* qtab, int64_t block, int64_t nblocks) {
     constexpr int LPV = D / 8;
     constexpr int VPW = 64 / LPV;
+    constexpr int U = kEncBatch;
     const int lane = threadIdx.x & 63;
-    const int gl = lane & (LPV - 1);
-    const uint32_t sbits = (a.c.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+    const int gl = lane & (LPV - 1), sl = enc_src_lane<D>(gl);
+    const uint32_t sbits = enc_sign_bits(a.c.sign_mask, sl);
+    uint32_t flip[4];
+    half_sign_masks(sbits, flip);
     const int64_t wave = (block * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = (nblocks * blockDim.x) >> 6;
-    for (int64_t base = wave * VPW; base < a.n; base += nwaves * VPW) {
-        const int64_t row = base + lane / LPV;
-        const bool valid = row < a.n;
-        VecState st;
-        load_rotate<D, DT>(a, row, valid, gl, sbits, st);
-        uint32_t idx[8];
-        const uint32_t packed = pack_lane<BITS>(st, a.c, idx);
-        bool keep = true;
-        const int64_t orow = valid ? out_row(a, row, keep) : 0;
-        uint32_t* rowp = reinterpret_cast<uint32_t*>(a.codes + orow * a.code_stride);
-        store_codes<BITS>(rowp, gl, packed, valid && keep);
-        if (valid && keep && gl == 0) a.norms[orow] = norm_to_half(st.nrm);
+    for (int64_t base = wave * VPW * U; base < a.n; base += nwaves * VPW * U) {
+        Raw8<DT> raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // rows past the end re-read the last row (never stored)
+            int64_t row = base + u * VPW + lane / LPV;
+            row = row < a.n ? row : a.n - 1;
+            ld_stream8<DT>(static_cast<const char*>(a.x) + (row * a.x_stride + sl * 8) * elem_bytes<DT>(), raw[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = base + u * VPW + lane / LPV;
+            const bool valid = row < a.n;
+            VecState st;
+            if constexpr (DT == 0) {
+                unpack8<DT>(raw[u], st.v);
+                rotate<D>(st, gl, sbits);
+            } else {
+                rotate_raw16<D, DT>(raw[u], flip, gl, st);
+            }
+            uint32_t packed;
+            if constexpr (TAB) {
+                packed = pack_lane_tab<BITS>(st, a.c, qtab);
+            } else {
+                uint32_t idx[8];
+                packed = pack_lane<BITS>(st, a.c, idx);
+            }
+            bool keep = true;
+            const int64_t orow = valid ? out_row(a, row, keep) : 0;
+            uint32_t* rowp = reinterpret_cast<uint32_t*>(a.codes + orow * a.code_stride);
+            store_codes<BITS>(rowp, gl, packed, valid && keep);
+            if (valid && keep && gl == 0) a.norms[orow] = norm_to_half(st.nrm);
+        }
     }
 }
 
-template <int D, int BITS, int DT>
+template <int D, int BITS, int DT, bool TAB>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
-    encode_rows<D, BITS, DT>(a, blockIdx.x, gridDim.x);
+    __shared__ uint2 qtab[TAB ? kQTabMax : 1];
+    if constexpr (TAB) build_qtab<BITS>(a.c, qtab);
+    encode_rows<D, BITS, DT, TAB>(a, qtab, blockIdx.x, gridDim.x);
 }
 
 // Two encodes in one launch (a layer's K and V): blocks [0, kblocks) run job
 // k, the rest job v; each block switches on its codec's bit width (uniform
 // per block).  Neither job uses QJL.
-template <int D, int DT>
+template <int D, int DT, bool TAB>
 __global__ __launch_bounds__(256) void encode_pair_kernel(EncodeArgs k, EncodeArgs v, int kblocks) {
     // each branch reads its own argument directly (selecting a reference to
     // one of the two would copy them to scratch)
-    auto run = [](const EncodeArgs& a, int64_t block, int64_t nblocks) __attribute__((always_inline)) {
+    __shared__ uint2 qtab[TAB ? kQTabMax : 1];
+    auto run = [&](const EncodeArgs& a, int64_t block, int64_t nblocks) __attribute__((always_inline)) {
+        auto one = [&](auto bc) __attribute__((always_inline)) {
+            constexpr int B = decltype(bc)::value;
+            if constexpr (TAB) build_qtab<B>(a.c, qtab);
+            encode_rows<D, B, DT, TAB>(a, qtab, block, nblocks);
+        };
         switch (a.c.bits) {
-            case 1: encode_rows<D, 1, DT>(a, block, nblocks); break;
-            case 2: encode_rows<D, 2, DT>(a, block, nblocks); break;
-            case 3: encode_rows<D, 3, DT>(a, block, nblocks); break;
-            default: encode_rows<D, 4, DT>(a, block, nblocks); break;
+            case 1: one(std::integral_constant<int, 1>{}); break;
+            case 2: one(std::integral_constant<int, 2>{}); break;
+            case 3: one(std::integral_constant<int, 3>{}); break;
+            default: one(std::integral_constant<int, 4>{}); break;
         }
     };
     if ((int)blockIdx.x < kblocks) run(k, blockIdx.x, kblocks);
@@ -180,8 +324,8 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int gl = lane & (LPV - 1);
-    const uint32_t sbits = (a.c.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+    const int gl = lane & (LPV - 1), sl = enc_src_lane<D>(gl);
+    const uint32_t sbits = enc_sign_bits(a.c.sign_mask, sl);
     const int m = a.c.qjl_m;
     const float rsd = 1.0f / sqrtf((float)D);
     if (tid < 16) cent[tid] = a.c.centroid[tid];
@@ -194,7 +338,7 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
             const int64_t row = tile0 + vloc;
             const bool valid = row < a.n;
             VecState st;
-            load_rotate<D, DT>(a, row, valid, gl, sbits, st);
+            load_rotate<D, DT>(a, row, valid, gl, sl, sbits, st);
             uint32_t idx[8];
             const uint32_t packed = pack_lane<BITS>(st, a.c, idx);
             bool keep = true;
@@ -284,8 +428,8 @@ __global__ __launch_bounds__(256) void encode_sign_kernel(EncodeArgs a) {
     if (threadIdx.x < 16) cent[threadIdx.x] = a.c.centroid[threadIdx.x];
     __syncthreads();
     const int lane = threadIdx.x & 63;
-    const int gl = lane & (LPV - 1);
-    const uint32_t sbits = (a.c.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+    const int gl = lane & (LPV - 1), sl = enc_src_lane<D>(gl);
+    const uint32_t sbits = enc_sign_bits(a.c.sign_mask, sl);
     const uint32_t sbits2 = (a.c.sign_mask2[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
     const float rsd = 1.0f / sqrtf((float)D);
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -294,7 +438,7 @@ __global__ __launch_bounds__(256) void encode_sign_kernel(EncodeArgs a) {
         const int64_t row = base + lane / LPV;
         const bool valid = row < a.n;
         VecState st;
-        load_rotate<D, DT>(a, row, valid, gl, sbits, st);
+        load_rotate<D, DT>(a, row, valid, gl, sl, sbits, st);
         uint32_t idx[8];
         const uint32_t packed = pack_lane<BITS>(st, a.c, idx);
         bool keep = true;
@@ -360,6 +504,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
 }
 
+// Blocks of the plain encoder for n rows at d: 4 waves, each taking
+// kEncBatch * 64/(d/8) rows per pass; at most 4096 blocks (16 per compute
+// unit), the rows loop inside.
+int encode_blocks(int64_t n, int d) {
+    const int64_t vpb = 4 * kEncBatch * (64 / (d / 8));
+    const int64_t need = (n + vpb - 1) / vpb;
+    return (int)(need < 4096 ? need : 4096);
+}
+
 template <int D, int BITS, int DT>
 hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t s) {
     if (a.c.residual == TQ_RES_SRHT || a.c.residual == TQ_RES_SIGN) {
@@ -375,10 +528,10 @@ hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t s) {
         const int grid = (int)(tiles < 8192 ? tiles : 8192);
         hipLaunchKernelGGL((encode_qjl_kernel<D, BITS, DT>), dim3(grid), dim3(256), 0, s, a);
     } else {
-        constexpr int VPB = 4 * (64 / (D / 8));  // vectors per block per iteration
-        const int64_t need = (a.n + VPB - 1) / VPB;
-        const int grid = (int)(need < 16384 ? need : 16384);
-        hipLaunchKernelGGL((encode_kernel<D, BITS, DT>), dim3(grid), dim3(256), 0, s, a);
+        if (a.c.qt_n > 0)
+            hipLaunchKernelGGL((encode_kernel<D, BITS, DT, true>), dim3(encode_blocks(a.n, D)), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((encode_kernel<D, BITS, DT, false>), dim3(encode_blocks(a.n, D)), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }
@@ -419,18 +572,13 @@ hipError_t launch_decode_b(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Blocks of the plain encoder for n rows at d (4 waves of 64/(d/8) vectors per
-// iteration, at most 16384 blocks; the rows loop inside).
-static int encode_blocks(int64_t n, int d) {
-    const int64_t vpb = 4 * (64 / (d / 8));
-    const int64_t need = (n + vpb - 1) / vpb;
-    return (int)(need < 16384 ? need : 16384);
-}
-
 template <int D, int DT>
 static hipError_t launch_pair_d(const EncodeArgs& k, const EncodeArgs& v, hipStream_t s) {
     const int kb = encode_blocks(k.n, D), vb = encode_blocks(v.n, D);
-    hipLaunchKernelGGL((encode_pair_kernel<D, DT>), dim3(kb + vb), dim3(256), 0, s, k, v, kb);
+    if (k.c.qt_n > 0 && v.c.qt_n > 0)
+        hipLaunchKernelGGL((encode_pair_kernel<D, DT, true>), dim3(kb + vb), dim3(256), 0, s, k, v, kb);
+    else
+        hipLaunchKernelGGL((encode_pair_kernel<D, DT, false>), dim3(kb + vb), dim3(256), 0, s, k, v, kb);
     return hipGetLastError();
 }
 

@@ -16,7 +16,14 @@ struct CodecArgs {
     int32_t d, bits, qjl_m;
     int32_t residual;        // TQ_RES_*
     uint32_t sign_mask2[8];  // second sign basis (TQ_RES_SRHT)
+    // the encoder's bin table (see plan_qtab): bin b = floor(z * qt_scale +
+    // qt_off) of z = w / n holds at most one threshold; qt_n bins, 0 = none
+    float qt_scale, qt_off, qt_inv_scale;
+    int32_t qt_n;
 };
+
+// Bins of the encoder's quantizer table at most (8 bytes each in LDS).
+constexpr int kQTabMax = 512;
 
 struct EncodeArgs {
     CodecArgs c;
