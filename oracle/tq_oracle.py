@@ -168,6 +168,17 @@ def second_sign_vector(seed: int, d: int) -> np.ndarray:
     return np.array([-1.0 if (v >> 63) & 1 else 1.0 for v in splitmix64(seed, 256 + d)[256:]])
 
 
+ROT_WHT, ROT_DOUBLE = 0, 1
+
+
+def third_sign_vector(seed: int, d: int) -> np.ndarray:
+    """Sign flip S2 of the double transform S1 -> WHT -> S2 -> WHT ([P1] v1.5.3
+    "핵심 변경" item 1, head_dim 64): sign i is -1 when bit 63 of SplitMix64
+    output 513 + i for the seed is set (outputs 1..512 belong to the first sign
+    vector at any d up to 512, outputs 257.. to the SRHT basis)."""
+    return np.array([-1.0 if (v >> 63) & 1 else 1.0 for v in splitmix64(seed, 512 + d)[512:]])
+
+
 class Codec:
     """What one encoder/decoder needs: d, bits, residual kind and width,
     signs, codebook.
@@ -185,9 +196,26 @@ class Codec:
       RES_SIGN  Direct Sign, m = d: the signs of the residual itself with
                 their mean magnitude as the scale ([P1] v1.1.0 "Direct Sign —
                 논문 QJL 대비 4.3배 낮은 분산").
+
+    Rotation R (the transform after the sign flip D):
+      ROT_WHT     R = H, the Sylvester Hadamard matrix;
+      ROT_DOUBLE  R = H diag(signs3) H / sqrt(d): S1 -> WHT -> S2 -> WHT per head
+                  ([P1] v1.5.3 "핵심 변경" item 1 and v1.5.2 item 9, head_dim 64,
+                  where one transform leaves the coordinates too far from
+                  Gaussian).  The 1/sqrt(d) keeps R R = d I, as for H, so z keeps
+                  unit variance and decoding divides by d as before.
+    Both R are symmetric.
+
+    Norm blocks B ([P1] v1.5.2 "핵심 변경" item 5, d = 512: after the 512-point
+    transform each 256-half gets its own norm; codecs with a residual keep the
+    single norm): with y = R D x split into B blocks y_h of d/B coordinates,
+    nu_h = ||y_h|| / sqrt(d) (the norm of that block of the orthonormally
+    rotated vector, so sum_h nu_h^2 = ||x||^2), z_h = y_h / (nu_h sqrt(B)) and
+    half(nu_h) is stored; B = 1 is the usual norm ||x||.
     """
 
-    def __init__(self, bits: int, d: int, seed: int, qjl_m: int = 0, residual: int | None = None):
+    def __init__(self, bits: int, d: int, seed: int, qjl_m: int = 0, residual: int | None = None,
+                 rotation: int = ROT_WHT, norm_blocks: int = 1):
         self.bits = int(bits)
         self.d = int(d)
         self.seed = int(seed)
@@ -204,7 +232,23 @@ class Codec:
         self.threshold = t64.astype(np.float32)
         self.signs = sign_vector(self.seed, self.d)
         self.signs2 = second_sign_vector(self.seed, self.d)
+        self.signs3 = third_sign_vector(self.seed, self.d)
         self.H = hadamard(self.d)
+        self.rotation = int(rotation)
+        if self.rotation == ROT_WHT:
+            self.R = self.H
+        elif self.rotation == ROT_DOUBLE:
+            self.R = (self.H * self.signs3[None, :]) @ self.H / math.sqrt(self.d)
+        else:
+            raise ValueError("unknown rotation")
+        self.norm_blocks = int(norm_blocks)
+        if self.norm_blocks not in (1, 2) or (self.norm_blocks > 1 and self.qjl_m):
+            raise ValueError("norm blocks: 1, or 2 without a residual")
+
+    @property
+    def norm_shape_tail(self) -> tuple:
+        """Trailing shape of one vector's stored norms: () or (B,)."""
+        return () if self.norm_blocks == 1 else (self.norm_blocks,)
 
     def projection(self, S=None) -> np.ndarray:
         """The [m][d] projection of the residual: S (QJL), H diag(signs2)
@@ -280,10 +324,11 @@ def unpack_signs(packed: np.ndarray, m: int) -> np.ndarray:
 
 
 def rotate(x: np.ndarray, codec: Codec) -> np.ndarray:
-    """H (D x) per row: sign flip then Walsh-Hadamard transform ([P1] v1.7.0
-    "핵심 설계 결정" item 4: internal sign flip + butterfly WHT), as a dense product."""
+    """R (D x) per row: sign flip then the codec's transform R ([P1] v1.7.0
+    "핵심 설계 결정" item 4: internal sign flip + butterfly WHT; R = H, or the
+    double transform of v1.5.3), as a dense product."""
     x = np.asarray(x, dtype=np.float64)
-    return (x * codec.signs[None, :]) @ codec.H.T
+    return (x * codec.signs[None, :]) @ codec.R.T
 
 
 def quantize(z: np.ndarray, codec: Codec) -> np.ndarray:
@@ -306,10 +351,18 @@ def encode(x: np.ndarray, codec: Codec, S: np.ndarray | None = None):
     """
     x = np.asarray(x, dtype=np.float64)
     n_rows = x.shape[0]
-    norm = np.sqrt(np.sum(x * x, axis=1))
     y = rotate(x, codec)
-    safe = np.where(norm > 0, norm, 1.0)
-    z = np.where(norm[:, None] > 0, y / safe[:, None], 0.0)
+    if codec.norm_blocks == 1:
+        norm = np.sqrt(np.sum(x * x, axis=1))
+        safe = np.where(norm > 0, norm, 1.0)
+        z = np.where(norm[:, None] > 0, y / safe[:, None], 0.0)
+    else:
+        # one norm per block of the rotated vector ([P1] v1.5.2 item 5)
+        B = codec.norm_blocks
+        yb = y.reshape(n_rows, B, codec.d // B)
+        norm = np.sqrt(np.sum(yb * yb, axis=2)) / math.sqrt(codec.d)  # [n][B]
+        safe = np.where(norm > 0, norm, 1.0) * math.sqrt(B)
+        z = np.where(norm[:, :, None] > 0, yb / safe[:, :, None], 0.0).reshape(n_rows, codec.d)
     idx = quantize(z, codec)
     out = {
         "codes": pack_indices(idx, codec.bits),
@@ -339,11 +392,16 @@ def encode(x: np.ndarray, codec: Codec, S: np.ndarray | None = None):
 
 
 def decode(codes: np.ndarray, norms16: np.ndarray, codec: Codec) -> np.ndarray:
-    """x_hat = n16 * D * H(c[idx]) / d (H H = d I, D D = I)."""
+    """x_hat = n16 * D * R(c[idx]) / d (R R = d I with R symmetric, D D = I);
+    with norm blocks each block of c[idx] is scaled by half(nu_h) sqrt(B) first."""
     idx = unpack_indices(codes, codec.d, codec.bits)
     c = codec.centroid.astype(np.float64)[idx]
-    w = c @ codec.H.T / codec.d
-    return np.asarray(norms16, dtype=np.float64)[:, None] * w * codec.signs[None, :]
+    n16 = np.asarray(norms16, dtype=np.float64)
+    if codec.norm_blocks == 1:
+        return n16[:, None] * (c @ codec.R.T / codec.d) * codec.signs[None, :]
+    B = codec.norm_blocks
+    yb = c.reshape(c.shape[0], B, codec.d // B) * (n16.reshape(-1, B)[:, :, None] * math.sqrt(B))
+    return (yb.reshape(c.shape[0], codec.d) @ codec.R.T / codec.d) * codec.signs[None, :]
 
 
 def append(codes, norms16, x_new, pos, codec: Codec, S=None, qjl=None, gamma16=None):
