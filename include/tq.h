@@ -56,7 +56,9 @@ enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 };
  * Host struct, filled by tq_codebook and passed by pointer; the library copies
  * it by value into kernel arguments.
  *
- *   d           head dimension: 32, 64, 128 or 256 (attention: 128 or 256).
+ *   d           head dimension: 32, 64, 128, 256 or 512 (512: no residual).
+ *               Attention: 128 and 256; 64 with 2- or 4-bit keys and 2..4-bit
+ *               values.
  *   bits        1..4 bits per coordinate (L = 2^bits centroids).
  *   qjl_m       0, or the number of residual sign bits m (multiple of 32,
  *               <= 256; m = d for TQ_RES_SRHT and TQ_RES_SIGN).
@@ -78,9 +80,25 @@ enum { TQ_F32 = 0, TQ_F16 = 1, TQ_BF16 = 2 };
  *               symmetric; entries >= L are 0.
  *   threshold   L-1 float32 midpoints; the middle one is exactly 0.
  *   sign_mask2  the second sign basis D2 of TQ_RES_SRHT (filled for every
- *               codec; bit i set means D2_ii = -1).
+ *               codec with d <= 256; bit i set means D2_ii = -1).
+ *   rotation    the transform R after the sign flip D:
+ *                 TQ_ROT_WHT     R = H, the Sylvester Walsh-Hadamard matrix;
+ *                 TQ_ROT_DOUBLE  R = H D3 H / sqrt(d) with the sign flip
+ *                                D3 = sign_mask3: S1 -> WHT -> S2 -> WHT per
+ *                                head ([P1] v1.5.3 "핵심 변경" item 1, head_dim
+ *                                64 only).  R R = d I as for H.
+ *   norm_blocks 1: one norm per vector, ||x||.  2: one norm per half of the
+ *               rotated vector y = R D x ([P1] v1.5.2 "핵심 변경" item 5: after
+ *               the 512-point transform each 256-half has its own norm):
+ *               nu_h = ||y_h|| / sqrt(d) (so nu_0^2 + nu_1^2 = ||x||^2) and
+ *               z_h = y_h / (nu_h sqrt(2)).  d = 256 or 512, no residual.
+ *   sign_mask3  D3 of TQ_ROT_DOUBLE (filled for every codec with d <= 256):
+ *               bit i set when bit 63 of SplitMix64 output 513 + i is set.
+ *   sign_mask_hi  D for dims 256..511 of a d = 512 codec (bit i of the array
+ *               = dim 256 + i).
  */
 enum { TQ_RES_NONE = 0, TQ_RES_QJL = 1, TQ_RES_SRHT = 2, TQ_RES_SIGN = 3 };
+enum { TQ_ROT_WHT = 0, TQ_ROT_DOUBLE = 1 };
 typedef struct {
     int32_t d;
     int32_t bits;
@@ -91,6 +109,10 @@ typedef struct {
     float centroid[16];
     float threshold[15];
     uint32_t sign_mask2[8];
+    int32_t rotation;
+    int32_t norm_blocks;
+    uint32_t sign_mask3[8];
+    uint32_t sign_mask_hi[8];
 } tq_codec;
 
 /*
@@ -118,6 +140,18 @@ int tq_codebook(int bits, int d, uint64_t seed, int qjl_m, tq_codec *out);
  * tq_codebook, plus TQ_EUNSUPPORTED for an unknown kind or a mismatched qjl_m.
  */
 int tq_codebook_ex(int bits, int d, uint64_t seed, int residual, int qjl_m, tq_codec *out);
+
+/*
+ * tq_codebook_opts -- tq_codebook_ex with the rotation (TQ_ROT_*) and the
+ * number of norm blocks (1 or 2) explicit; tq_codebook and tq_codebook_ex use
+ * TQ_ROT_WHT and one norm.  Errors as tq_codebook_ex, plus TQ_EUNSUPPORTED for
+ * TQ_ROT_DOUBLE at d != 64 ([P1] v1.5.3 uses it at head_dim 64 only), for
+ * norm_blocks not 1 or 2, and for two norm blocks at d < 256 or with a
+ * residual kind (the pages keep one norm for the residual codecs, [P1]
+ * v1.5.2 item 5).
+ */
+int tq_codebook_opts(int bits, int d, uint64_t seed, int residual, int qjl_m, int rotation, int norm_blocks,
+                     tq_codec *out);
 
 /*
  * tq_encode -- quantise n vectors ([P1] v1.7.0 "핵심 설계 결정" item 4: sign flip +

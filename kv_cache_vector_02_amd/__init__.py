@@ -18,13 +18,14 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EWORKSPACE, TQ_EDEVICE, TQ_ESCRATCH = 0, -1, -2, -3, -4, -5
 TQ_RES_NONE, TQ_RES_QJL, TQ_RES_SRHT, TQ_RES_SIGN = 0, 1, 2, 3
+TQ_ROT_WHT, TQ_ROT_DOUBLE = 0, 1
 TQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 TQ_F32, TQ_F16, TQ_BF16 = 0, 1, 2
 
 _DTYPES = {torch.float32: TQ_F32, torch.float16: TQ_F16, torch.bfloat16: TQ_BF16}
 
 EXPORTS = (
-    "tq_codebook", "tq_codebook_ex", "tq_encode", "tq_encode_kv", "tq_prefill", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
+    "tq_codebook", "tq_codebook_ex", "tq_codebook_opts", "tq_encode", "tq_encode_kv", "tq_prefill", "tq_append", "tq_decode", "tq_attn_decode", "tq_attn_prepare", "tq_attn_scan",
     "tq_attn_combine", "tq_attn_decode_rw", "tq_attn_workspace_bytes", "tq_workspace_bytes",
     "tq_ip_search", "tq_search_workspace_bytes", "tq_packed_bytes", "tq_strerror", "tq_stream_read",
     "tq_attn_decode_noalloc", "tq_attn_decode_mq", "tq_attn_decode_ex",
@@ -46,6 +47,10 @@ class tq_codec(ctypes.Structure):
         ("centroid", ctypes.c_float * 16),
         ("threshold", ctypes.c_float * 15),
         ("sign_mask2", ctypes.c_uint32 * 8),
+        ("rotation", ctypes.c_int32),
+        ("norm_blocks", ctypes.c_int32),
+        ("sign_mask3", ctypes.c_uint32 * 8),
+        ("sign_mask_hi", ctypes.c_uint32 * 8),
     ]
 
     @property
@@ -62,7 +67,14 @@ class tq_codec(ctypes.Structure):
 
     @property
     def signs(self) -> list[float]:
-        return [-1.0 if (self.sign_mask[i >> 5] >> (i & 31)) & 1 else 1.0 for i in range(self.d)]
+        def bit(i):
+            return (self.sign_mask[i >> 5] >> (i & 31)) & 1 if i < 256 else \
+                (self.sign_mask_hi[(i - 256) >> 5] >> (i & 31)) & 1
+        return [-1.0 if bit(i) else 1.0 for i in range(self.d)]
+
+    @property
+    def signs3(self) -> list[float]:
+        return [-1.0 if (self.sign_mask3[i >> 5] >> (i & 31)) & 1 else 1.0 for i in range(min(self.d, 256))]
 
     @property
     def signs2(self) -> list[float]:
@@ -98,6 +110,7 @@ def _load():
     sig = {
         "tq_codebook": (I, [I, I, ctypes.c_uint64, I, CP]),
         "tq_codebook_ex": (I, [I, I, ctypes.c_uint64, I, I, CP]),
+        "tq_codebook_opts": (I, [I, I, ctypes.c_uint64, I, I, I, I, CP]),
         "tq_encode": (I, [CP, P, I, I64, I64, P, I64, P, P, P, P, P]),
         "tq_encode_kv": (I, [CP, CP, P, P, I, I64, I64, P, I64, P, P, I64, P, P, P, P, P]),
         "tq_prefill": (I, [CP, CP, P, P, I, I, I64, I64, I64, P, P, P, P, P, P, P, P]),
@@ -220,6 +233,21 @@ def tq_codebook_ex(bits: int, d: int, seed: int, residual: int, qjl_m: int = 0) 
     return c
 
 
+def tq_codebook_opts(bits: int, d: int, seed: int, residual: int = TQ_RES_NONE, qjl_m: int = 0,
+                     rotation: int = TQ_ROT_WHT, norm_blocks: int = 1) -> tq_codec:
+    """Host-only: codec with the rotation (TQ_ROT_*) and norm blocks (1 or 2)."""
+    c = tq_codec()
+    _check(_lib.tq_codebook_opts(bits, d, ctypes.c_uint64(seed & (2**64 - 1)), residual, qjl_m, rotation,
+                                 norm_blocks, ctypes.byref(c)), "tq_codebook_opts")
+    return c
+
+
+def _nshape(codec, shape):
+    """Shape of a norms plane: `shape`, with a trailing block axis for a codec
+    with two norm blocks."""
+    return tuple(shape) + ((codec.norm_blocks,) if codec.norm_blocks > 1 else ())
+
+
 def tq_packed_bytes(d: int, bits: int, qjl_m: int = 0) -> int:
     return _lib.tq_packed_bytes(d, bits, qjl_m)
 
@@ -234,7 +262,7 @@ def tq_encode(codec: tq_codec, x: torch.Tensor, codes: torch.Tensor, norms: torc
     n = x.shape[0]
     _rows(x, n, codec.d, "x")
     _rows(codes, n, codec.code_bytes, "codes", torch.uint8)
-    _vec(norms, n, "norms")
+    _vec(norms, n * codec.norm_blocks, "norms")
     _qjl_rows(codec, n, qjl_S, qjl_bits, qjl_gamma)
     _check(_lib.tq_encode(ctypes.byref(codec), _ptr(x), _DTYPES[x.dtype], n, x.stride(0), _ptr(codes),
                           codes.stride(0), _ptr(norms), _ptr(qjl_S), _ptr(qjl_bits), _ptr(qjl_gamma),
@@ -256,8 +284,8 @@ def tq_encode_kv(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, k
     _rows(k, n, kc.d, "k")
     _rows(k_codes, n, kc.code_bytes, "k_codes", torch.uint8)
     _rows(v_codes, n, vc.code_bytes, "v_codes", torch.uint8)
-    _vec(k_norms, n, "k_norms")
-    _vec(v_norms, n, "v_norms")
+    _vec(k_norms, n * kc.norm_blocks, "k_norms")
+    _vec(v_norms, n * vc.norm_blocks, "v_norms")
     _qjl_rows(kc, n, qjl_S, k_qjl_bits, k_qjl_gamma, ("qjl_S", "k_qjl_bits", "k_qjl_gamma"))
     _check(_lib.tq_encode_kv(ctypes.byref(kc), ctypes.byref(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], k.shape[0],
                              k.stride(0), _ptr(k_codes), k_codes.stride(0), _ptr(k_norms), _ptr(v_codes),
@@ -284,8 +312,8 @@ def tq_prefill(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, t0:
     _shape(k, (H, T, kc.d), "k")
     _shape(k_codes, (H, cap, kc.code_bytes), "k_codes", torch.uint8)
     _shape(v_codes, (H, cap, vc.code_bytes), "v_codes", torch.uint8)
-    _shape(k_norms, (H, cap), "k_norms", elem=2)
-    _shape(v_norms, (H, cap), "v_norms", elem=2)
+    _shape(k_norms, _nshape(kc, (H, cap)), "k_norms", elem=2)
+    _shape(v_norms, _nshape(vc, (H, cap)), "v_norms", elem=2)
     if kc.qjl_m:
         _qjl_rows(kc, H * cap, qjl_S, k_qjl_bits, k_qjl_gamma, ("qjl_S", "k_qjl_bits", "k_qjl_gamma"))
         _shape(k_qjl_bits, (H, cap, kc.qjl_m // 8), "k_qjl_bits", torch.uint8)
@@ -314,8 +342,8 @@ def tq_append(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, pos:
     _shape(pos, (B,), "pos", torch.int32)
     _shape(k_codes, (B, H, cap, kc.code_bytes), "k_codes", torch.uint8)
     _shape(v_codes, (B, H, cap, vc.code_bytes), "v_codes", torch.uint8)
-    _shape(k_norms, (B, H, cap), "k_norms", elem=2)
-    _shape(v_norms, (B, H, cap), "v_norms", elem=2)
+    _shape(k_norms, _nshape(kc, (B, H, cap)), "k_norms", elem=2)
+    _shape(v_norms, _nshape(vc, (B, H, cap)), "v_norms", elem=2)
     if kc.qjl_m:
         _qjl_rows(kc, B * H * cap, qjl_S, k_qjl_bits, k_qjl_gamma, ("qjl_S", "k_qjl_bits", "k_qjl_gamma"))
         _shape(k_qjl_bits, (B, H, cap, kc.qjl_m // 8), "k_qjl_bits", torch.uint8)
@@ -329,7 +357,7 @@ def tq_decode(codec: tq_codec, codes: torch.Tensor, norms: torch.Tensor, x_hat: 
         raise ValueError("codes must be 2-D with contiguous rows")
     n = codes.shape[0]
     _rows(codes, n, codec.code_bytes, "codes", torch.uint8)
-    _vec(norms, n, "norms")
+    _vec(norms, n * codec.norm_blocks, "norms")
     _shape(x_hat, (n, codec.d), "x_hat", torch.float32)
     if not x_hat.is_contiguous():
         raise ValueError("x_hat must be contiguous")

@@ -80,12 +80,15 @@ uint64_t splitmix64_at(uint64_t seed, uint64_t index) {
     return z ^ (z >> 31);
 }
 
-bool valid_d(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+bool valid_d(int d) { return d == 32 || d == 64 || d == 128 || d == 256 || d == 512; }
 
 bool valid_codec(const tq_codec* c) {
     if (!(c && valid_d(c->d) && c->bits >= 1 && c->bits <= 4 && c->qjl_m >= 0 && c->qjl_m <= 256 &&
           c->qjl_m % 32 == 0))
         return false;
+    if (c->rotation != TQ_ROT_WHT && !(c->rotation == TQ_ROT_DOUBLE && c->d == 64)) return false;
+    if (c->norm_blocks != 1 && !(c->norm_blocks == 2 && c->d >= 256 && c->residual == TQ_RES_NONE)) return false;
+    if (c->d == 512 && c->residual != TQ_RES_NONE) return false;
     switch (c->residual) {
         case TQ_RES_NONE: return c->qjl_m == 0;
         case TQ_RES_QJL: return c->qjl_m > 0;
@@ -191,7 +194,8 @@ static void plan_qtab(const tq_codec* c, CodecArgs* a) {
 }
 
 void fill_codec_args(const tq_codec* c, CodecArgs* a) {
-    memcpy(a->sign_mask, c->sign_mask, sizeof(a->sign_mask));
+    memcpy(a->sign_mask, c->sign_mask, sizeof(c->sign_mask));
+    memcpy(a->sign_mask + 8, c->sign_mask_hi, sizeof(c->sign_mask_hi));
     memcpy(a->centroid, c->centroid, sizeof(a->centroid));
     memcpy(a->threshold, c->threshold, sizeof(a->threshold));
     a->d = c->d;
@@ -199,16 +203,23 @@ void fill_codec_args(const tq_codec* c, CodecArgs* a) {
     a->qjl_m = c->qjl_m;
     a->residual = c->residual;
     memcpy(a->sign_mask2, c->sign_mask2, sizeof(a->sign_mask2));
+    a->rotation = c->rotation;
+    a->norm_blocks = c->norm_blocks;
+    memcpy(a->sign_mask3, c->sign_mask3, sizeof(a->sign_mask3));
     plan_qtab(c, a);
 }
 }  // namespace tqi
 
 extern "C" {
 
-int tq_codebook_ex(int bits, int d, uint64_t seed, int residual, int qjl_m, tq_codec* out) {
+int tq_codebook_opts(int bits, int d, uint64_t seed, int residual, int qjl_m, int rotation, int norm_blocks,
+                     tq_codec* out) {
     if (!out) return TQ_EINVAL;
     if (!valid_d(d) || bits < 1 || bits > 4 || qjl_m < 0 || qjl_m > 256 || qjl_m % 32 != 0)
         return TQ_EUNSUPPORTED;
+    if (rotation != TQ_ROT_WHT && !(rotation == TQ_ROT_DOUBLE && d == 64)) return TQ_EUNSUPPORTED;
+    if (norm_blocks != 1 && !(norm_blocks == 2 && d >= 256 && residual == TQ_RES_NONE)) return TQ_EUNSUPPORTED;
+    if (d == 512 && residual != TQ_RES_NONE) return TQ_EUNSUPPORTED;
     if (residual == TQ_RES_SRHT || residual == TQ_RES_SIGN) {
         if (qjl_m != 0 && qjl_m != d) return TQ_EUNSUPPORTED;
         qjl_m = d;
@@ -223,10 +234,18 @@ int tq_codebook_ex(int bits, int d, uint64_t seed, int residual, int qjl_m, tq_c
     out->qjl_m = qjl_m;
     out->residual = residual;
     out->seed = seed;
+    out->rotation = rotation;
+    out->norm_blocks = norm_blocks;
     for (int i = 0; i < d; ++i) {
-        if (splitmix64_at(seed, (uint64_t)i + 1) >> 63) out->sign_mask[i >> 5] |= 1u << (i & 31);
-        // the second sign basis: outputs 257.. (1..256 belong to the first, whatever d)
+        if (splitmix64_at(seed, (uint64_t)i + 1) >> 63) {
+            if (i < 256) out->sign_mask[i >> 5] |= 1u << (i & 31);
+            else out->sign_mask_hi[(i - 256) >> 5] |= 1u << (i & 31);
+        }
+        if (i >= 256) continue;
+        // the second sign basis: outputs 257.. (1..256 belong to the first at d <= 256);
+        // the double transform's second flip: outputs 513..
         if (splitmix64_at(seed, (uint64_t)i + 257) >> 63) out->sign_mask2[i >> 5] |= 1u << (i & 31);
+        if (splitmix64_at(seed, (uint64_t)i + 513) >> 63) out->sign_mask3[i >> 5] |= 1u << (i & 31);
     }
     double c[16], t[15];
     lloyd_max(bits, c, t);
@@ -234,6 +253,10 @@ int tq_codebook_ex(int bits, int d, uint64_t seed, int residual, int qjl_m, tq_c
     for (int k = 0; k < L; ++k) out->centroid[k] = (float)c[k];
     for (int k = 0; k < L - 1; ++k) out->threshold[k] = (float)t[k];
     return TQ_OK;
+}
+
+int tq_codebook_ex(int bits, int d, uint64_t seed, int residual, int qjl_m, tq_codec* out) {
+    return tq_codebook_opts(bits, d, seed, residual, qjl_m, TQ_ROT_WHT, 1, out);
 }
 
 int tq_codebook(int bits, int d, uint64_t seed, int qjl_m, tq_codec* out) {
@@ -392,7 +415,16 @@ static int attn_check(const tq_codec* kc, const tq_codec* vc, int batch, int nco
                       int64_t ctx_cap, int* splits, int64_t* split_tokens, int* G) {
     if (!kc || !vc) return TQ_EINVAL;
     if (!valid_codec(kc) || !valid_codec(vc)) return TQ_EUNSUPPORTED;
-    if (kc->d != vc->d || (kc->d != 128 && kc->d != 256) || vc->qjl_m != 0) return TQ_EUNSUPPORTED;
+    if (kc->d != vc->d || vc->qjl_m != 0) return TQ_EUNSUPPORTED;
+    // the scan's lane layout: d = 128 and 256 at every width; d = 64 with key
+    // bytes a whole number of dwords per lane group (2 or 4 bits) and 2..4-bit
+    // values; one norm per token
+    if (kc->d == 64) {
+        if ((kc->bits != 2 && kc->bits != 4) || vc->bits < 2) return TQ_EUNSUPPORTED;
+    } else if (kc->d != 128 && kc->d != 256) {
+        return TQ_EUNSUPPORTED;
+    }
+    if (kc->norm_blocks != 1 || vc->norm_blocks != 1) return TQ_EUNSUPPORTED;
     if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || ctx_cap <= 0 || batch > 65535 || ncols <= 0)
         return TQ_EINVAL;
     if (n_q_heads % n_kv_heads != 0 || ncols > TQ_MAX_QUERY_COLS) return TQ_EUNSUPPORTED;
@@ -613,7 +645,7 @@ int tq_attn_decode_mq(const tq_codec* kc, const tq_codec* vc, const void* q, int
 static int search_check(const tq_codec* c, int n_q, int64_t n_db, int k) {
     if (!c) return TQ_EINVAL;
     if (!valid_codec(c)) return TQ_EUNSUPPORTED;
-    if (c->d != 128 && c->d != 256) return TQ_EUNSUPPORTED;
+    if ((c->d != 128 && c->d != 256) || c->norm_blocks != 1) return TQ_EUNSUPPORTED;
     if (k < 1 || k > 64) return TQ_EUNSUPPORTED;
     if (n_q <= 0 || n_db < 0 || n_q > 65535 * 32) return TQ_EINVAL;  // 32 queries per block row of the grid
     if (n_db > ((int64_t)1 << 31) - 1) return TQ_EUNSUPPORTED;

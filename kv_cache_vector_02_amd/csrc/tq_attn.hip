@@ -15,11 +15,13 @@ namespace tqi {
 
 // Resident split blocks per compute unit for this variant (cached).
 static int split_blocks_any(int d, int kb, int vb, bool qjl) {
-    static std::atomic<int> cache[2][4][4][2];
-    std::atomic<int>& c = cache[d == 128 ? 0 : 1][kb - 1][vb - 1][qjl ? 1 : 0];
+    static std::atomic<int> cache[3][4][4][2];
+    std::atomic<int>& c = cache[d == 64 ? 2 : (d == 128 ? 0 : 1)][kb - 1][vb - 1][qjl ? 1 : 0];
     int nb = c.load(std::memory_order_relaxed);
     if (nb > 0) return nb;
-    if (d == 128) {
+    if (d == 64) {
+        nb = kb == 2 ? split_blocks_dk<64, 2>(vb, qjl) : split_blocks_dk<64, 4>(vb, qjl);
+    } else if (d == 128) {
         switch (kb) {
             case 1: nb = split_blocks_dk<128, 1>(vb, qjl); break;
             case 2: nb = split_blocks_dk<128, 2>(vb, qjl); break;
@@ -146,6 +148,7 @@ static void launch_window(const AttnArgs& a, int grid, hipStream_t s) {
 }
 
 static hipError_t launch_split_any(const AttnArgs& a, hipStream_t s) {
+    if (a.kc.d == 64) return a.kc.bits == 2 ? launch_split_dk<64, 2>(a, s) : launch_split_dk<64, 4>(a, s);
     if (a.kc.d == 128) {
         switch (a.kc.bits) {
             case 1: return launch_split_dk<128, 1>(a, s);
@@ -162,12 +165,19 @@ static hipError_t launch_split_any(const AttnArgs& a, hipStream_t s) {
     }
 }
 
+static hipError_t launch_qprep_combine_any(const AttnArgs& a, hipStream_t s, bool prep) {
+    switch (a.kc.d) {
+        case 64: return launch_qprep_combine<64>(a, s, prep);
+        case 128: return launch_qprep_combine<128>(a, s, prep);
+        default: return launch_qprep_combine<256>(a, s, prep);
+    }
+}
+
 hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s) {
-    const bool d128 = a.kc.d == 128;
     hipError_t e = hipSuccess;
     // without QJL the scan rotates its queries itself and there is nothing to prepare
     if ((stages & ATTN_PREPARE) && a.kc.qjl_m > 0) {
-        e = d128 ? launch_qprep_combine<128>(a, s, true) : launch_qprep_combine<256>(a, s, true);
+        e = launch_qprep_combine_any(a, s, true);
         if (e != hipSuccess) return e;
     }
     if (stages & ATTN_SCAN) {
@@ -178,11 +188,14 @@ hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s) {
         // the window kernel also merges the splits and writes the output:
         // one block per (batch, query head), heads of one kv head on one XCD
         const int grid = ((a.batch * a.hkv + 7) & ~7) * a.g;
-        if (d128) launch_window<128>(a, grid, s);
-        else launch_window<256>(a, grid, s);
+        switch (a.kc.d) {
+            case 64: launch_window<64>(a, grid, s); break;
+            case 128: launch_window<128>(a, grid, s); break;
+            default: launch_window<256>(a, grid, s); break;
+        }
         return hipGetLastError();
     }
-    if (stages & ATTN_COMBINE) e = d128 ? launch_qprep_combine<128>(a, s, false) : launch_qprep_combine<256>(a, s, false);
+    if (stages & ATTN_COMBINE) e = launch_qprep_combine_any(a, s, false);
     return e;
 }
 

@@ -99,6 +99,9 @@ __global__ __launch_bounds__(64) void qprep_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = as_f(as_u(v[e]) ^ (((sbits >> e) & 1u) << 31));
     fwht<LPV>(v, gl);
+    if constexpr (D == 64) {
+        if (a.kc.rotation == TQ_ROT_DOUBLE) second_pass<LPV>(v, gl, a.kc.sign_mask3);
+    }
     const int m = a.kc.qjl_m;
     const float alpha = valid ? score_factor(a, row_tokens(a, head)) : 1.0f;
     if (a.kc.residual != TQ_RES_QJL) {
@@ -345,11 +348,22 @@ __device__ __forceinline__ void fetch_v(uint32_t (&rv)[C::VTW], uint32_t& rn, ui
                                         uint32_t last, int lane) {
     uint32_t tl = t0 + lane;
     tl = tl < last ? tl : last;
-    const uint4* vp = reinterpret_cast<const uint4*>(vcodes + tl * C::RBV);
+    if constexpr (C::RBV % 16 == 0) {
+        const uint4* vp = reinterpret_cast<const uint4*>(vcodes + tl * C::RBV);
 #pragma unroll
-    for (int w = 0; w < C::RBV / 16; ++w) {
-        const uint4 v = ld_stream4(vp + w);
-        rv[4 * w] = v.x; rv[4 * w + 1] = v.y; rv[4 * w + 2] = v.z; rv[4 * w + 3] = v.w;
+        for (int w = 0; w < C::RBV / 16; ++w) {
+            const uint4 v = ld_stream4(vp + w);
+            rv[4 * w] = v.x; rv[4 * w + 1] = v.y; rv[4 * w + 2] = v.z; rv[4 * w + 3] = v.w;
+        }
+    } else {
+        // 24-byte rows (3-bit values at d = 64): 8-byte loads keep every load aligned
+        static_assert(C::RBV % 8 == 0, "V rows of whole 8-byte words");
+        const uint2* vp = reinterpret_cast<const uint2*>(vcodes + tl * C::RBV);
+#pragma unroll
+        for (int w = 0; w < C::RBV / 8; ++w) {
+            const uint2 v = ld_stream2(vp + w);
+            rv[2 * w] = v.x; rv[2 * w + 1] = v.y;
+        }
     }
     rn = ld_stream_u16(knb + 2u * tl) | (ld_stream_u16(vnb + 2u * tl) << 16);
     if constexpr (QJL) rg = ld_stream_u16(gmb + 2u * tl);
@@ -452,6 +466,9 @@ void split_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qx[e] = as_f(as_u(qx[e]) ^ (((sbits >> e) & 1u) << 31));
         fwht<QLPV>(qx, qgl);
+        if constexpr (D == 64) {
+            if (a.kc.rotation == TQ_ROT_DOUBLE) second_pass<QLPV>(qx, qgl, a.kc.sign_mask3);
+        }
         float qs = a.scale * kLog2e / (float)D;
         if (a.score_mode != 0 && qhl < G) {
             const int nr = MQ ? ctx - (a.ncols - 1 - (vl0 + qhl) / a.g) : ctx;  // tokens this row attends over
@@ -1030,8 +1047,11 @@ __device__ __forceinline__ void combine_head(const AttnArgs& a, int64_t bh, int 
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = L > 0.0f ? x[e] / L : 0.0f;
-    // inverse rotation: D_V H(x) / d
+    // inverse rotation: D_V R(x) / d (R = H, or H D3 H / sqrt(d))
     fwht<LPV>(x, gl);
+    if constexpr (D == 64) {
+        if (a.vc.rotation == TQ_ROT_DOUBLE) second_pass<LPV>(x, gl, a.vc.sign_mask3);
+    }
     const uint32_t sbits = (a.vc.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = as_f(as_u(x[e] * (1.0f / (float)D)) ^ (((sbits >> e) & 1u) << 31));
@@ -1180,6 +1200,7 @@ __global__ __launch_bounds__(256) void window_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) yo[e] = xor_lane<M>(y[e]);
         join(mo, lo, yo);
     };
+    if constexpr (TPW >= 8) merge_lanes(std::integral_constant<int, 8>{});
     if constexpr (TPW >= 4) merge_lanes(std::integral_constant<int, 16>{});
     merge_lanes(std::integral_constant<int, 32>{});
     // the 4 waves, through LDS
@@ -1200,7 +1221,7 @@ __global__ __launch_bounds__(256) void window_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) yo[e] = mrg[w][2 + 8 * gl + e];
         join(mrg[w][0], mrg[w][1], yo);
     }
-    // the window's share in the rotated domain, x = H(D_V y), then the merge
+    // the window's share in the rotated domain, x = R(D_V y), then the merge
     // with the head's split partials and the output (every lane group of wave
     // 0 holds the merged state, up to the rounding order of its merges; group
     // 0's is the one stored)
@@ -1208,6 +1229,9 @@ __global__ __launch_bounds__(256) void window_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = as_f(as_u(y[e]) ^ (((sbits >> e) & 1u) << 31));
     fwht<LPV>(y, gl);
+    if constexpr (D == 64) {
+        if (a.vc.rotation == TQ_ROT_DOUBLE) second_pass<LPV>(y, gl, a.vc.sign_mask3);
+    }
     combine_head<D>(a, bh, gl, tg == 0, m, l, y);
 }
 
@@ -1251,23 +1275,39 @@ int split_blocks(bool qjl) {
     return e == hipSuccess && nb > 0 ? nb : 0;
 }
 
+// Value widths of the scan at d: every width at d >= 128; at d = 64 a lane
+// group's V piece needs 2 to 4 bits (and the keys 2 or 4, see tq_attn.hip).
+constexpr bool scan_vb_ok(int d, int vb) { return d >= 128 || vb >= 2; }
+
+template <int D, int KB, int VB>
+hipError_t launch_split_v(const AttnArgs& a, hipStream_t s) {
+    if constexpr (scan_vb_ok(D, VB)) return launch_split<D, KB, VB>(a, s);
+    else return hipErrorInvalidValue;
+}
+
 template <int D, int KB>
 hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s) {
     switch (a.vc.bits) {
-        case 1: return launch_split<D, KB, 1>(a, s);
-        case 2: return launch_split<D, KB, 2>(a, s);
-        case 3: return launch_split<D, KB, 3>(a, s);
-        default: return launch_split<D, KB, 4>(a, s);
+        case 1: return launch_split_v<D, KB, 1>(a, s);
+        case 2: return launch_split_v<D, KB, 2>(a, s);
+        case 3: return launch_split_v<D, KB, 3>(a, s);
+        default: return launch_split_v<D, KB, 4>(a, s);
     }
+}
+
+template <int D, int KB, int VB>
+int split_blocks_v(bool qjl) {
+    if constexpr (scan_vb_ok(D, VB)) return split_blocks<D, KB, VB>(qjl);
+    else return 0;
 }
 
 template <int D, int KB>
 int split_blocks_dk(int vb, bool qjl) {
     switch (vb) {
-        case 1: return split_blocks<D, KB, 1>(qjl);
-        case 2: return split_blocks<D, KB, 2>(qjl);
-        case 3: return split_blocks<D, KB, 3>(qjl);
-        default: return split_blocks<D, KB, 4>(qjl);
+        case 1: return split_blocks_v<D, KB, 1>(qjl);
+        case 2: return split_blocks_v<D, KB, 2>(qjl);
+        case 3: return split_blocks_v<D, KB, 3>(qjl);
+        default: return split_blocks_v<D, KB, 4>(qjl);
     }
 }
 

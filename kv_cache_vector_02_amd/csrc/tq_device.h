@@ -117,6 +117,23 @@ __device__ __forceinline__ void fwht(float (&v)[8], int gl) {
     if constexpr (LPV >= 8) cross_stage<4>(v, gl);
     if constexpr (LPV >= 16) cross_stage<8>(v, gl);
     if constexpr (LPV >= 32) cross_stage<16>(v, gl);
+    if constexpr (LPV >= 64) cross_stage<32>(v, gl);
+}
+
+// Second pass of the double transform S1 -> WHT -> S2 -> WHT ("TurboQuant KV
+// 캐시 압축 for llama.cpp", v1.5.3 "핵심 변경" item 1) on a vector in the
+// natural layout: v <- H(D3 v) / sqrt(d), D3 given by its sign bits (bit i =
+// dim i).  After the first transform H(D x) this gives R D x with
+// R = H D3 H / sqrt(d); R is symmetric, so the same pass after H also inverts.
+template <int LPV>
+__device__ __forceinline__ void second_pass(float (&v)[8], int gl, const uint32_t* mask3) {
+    const uint32_t s3 = (mask3[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = as_f(as_u(v[e]) ^ (((s3 >> e) & 1u) << 31));
+    fwht<LPV>(v, gl);
+    const float r = 1.0f / __builtin_sqrtf((float)(8 * LPV));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= r;
 }
 
 // ---------------------------------------------------------------------------
@@ -124,8 +141,9 @@ __device__ __forceinline__ void fwht(float (&v)[8], int gl) {
 // multiply-add, y_l = x_l + c_l * x_{l ^ v} (v_fmac_f32 with the partner read
 // through DPP), for the encoder, whose cost is its VALU instruction count.
 // Partners l ^ 1, l ^ 2 (quad_perm), l ^ 7 (row_half_mirror), l ^ 8
-// (row_ror:8) and l ^ 16 (ds_swizzle), with c_l = (-1)^popcount(l & w) for
-// w = 5, 6, 4, 8, 16.  Every stage keeps a + b in one lane of a pair and
+// (row_ror:8), l ^ 16 (ds_swizzle) and l ^ 32 (ds_bpermute), with
+// c_l = (-1)^popcount(l & w) for
+// w = 5, 6, 4, 8, 16, 32.  Every stage keeps a + b in one lane of a pair and
 // b - a (not a - b) in the other, and the partners are not the unit steps of
 // the plain butterfly; the network still equals H, applied to the lane blocks
 // in a fixed order: lane gl must hold the input elements of lane
@@ -135,7 +153,7 @@ __device__ __forceinline__ void fwht(float (&v)[8], int gl) {
 // ---------------------------------------------------------------------------
 template <int LPV>
 __device__ __forceinline__ int fwht_src_lane(int gl) {
-    static_assert(LPV == 4 || LPV == 8 || LPV == 16 || LPV == 32, "lane group of 4..32 lanes");
+    static_assert(LPV == 4 || LPV == 8 || LPV == 16 || LPV == 32 || LPV == 64, "lane group of 4..64 lanes");
     if constexpr (LPV == 4) return gl ^ 3;
     // lanes 0..7 of each block of 8 read 7 2 1 4 0 5 6 3 (affine in the lane
     // bits); the blocks of 8 come in reverse order
@@ -195,6 +213,11 @@ __device__ __forceinline__ void fwht_fused(float (&v)[8], int gl) {
         const float c5 = parity_sign<16>(gl);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = fmaf(xor_lane<16>(v[e]), c5, v[e]);  // l ^ 16
+    }
+    if constexpr (LPV >= 64) {
+        const float c6 = parity_sign<32>(gl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = fmaf(xor_lane<32>(v[e]), c6, v[e]);  // l ^ 32
     }
 }
 

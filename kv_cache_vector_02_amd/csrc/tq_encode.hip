@@ -63,15 +63,50 @@ __device__ __forceinline__ void store_codes(uint32_t* rowp, int gl, uint32_t pac
 
 struct VecState {
     float v[8];
-    float nrm;
+    float nrm;   // threshold scale: z = w / nrm (the norm, or nu_h sqrt(2) with two norm blocks)
+    float keep;  // the norm stored for the lane's block
 };
+
+// After the first transform: the second pass of the double transform (d = 64)
+// and the scales of the norm blocks (two blocks at d >= 256: lane gl holds
+// rotated dims [8 gl, 8 gl + 8), so the lanes below LPV/2 hold the first half).
+// ss = ||x||^2 of the input.
+template <int D>
+__device__ __forceinline__ void finish_rotation(VecState& st, int gl, const CodecArgs& c, float ss) {
+    constexpr int LPV = D / 8;
+    if constexpr (D == 64) {
+        if (c.rotation == TQ_ROT_DOUBLE) second_pass<LPV>(st.v, gl, c.sign_mask3);
+    }
+    if constexpr (D >= 256) {
+        if (c.norm_blocks == 2) {
+            float sh = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sh = fmaf(st.v[e], st.v[e], sh);
+            sh = group_sum<LPV / 2>(sh);  // ||y_h||^2 of the lane's half
+            st.keep = __builtin_amdgcn_sqrtf(sh * (1.0f / (float)D));
+            st.nrm = __builtin_amdgcn_sqrtf(sh * (2.0f / (float)D));
+            return;
+        }
+    }
+    st.nrm = st.keep = __builtin_amdgcn_sqrtf(ss);
+}
+
+// Norms of one vector in its norms row (norm_blocks halves) by the lanes
+// that start a block.
+template <int D>
+__device__ __forceinline__ void store_norms(const EncodeArgs& a, int64_t orow, int gl, const VecState& st, bool ok) {
+    constexpr int LPV = D / 8;
+    const int nb = D >= 256 ? a.c.norm_blocks : 1;
+    const int per = LPV / nb;
+    if (ok && (gl & (per - 1)) == 0) a.norms[orow * nb + gl / per] = norm_to_half(st.keep);
+}
 
 // Input elements lane gl of a group loads: those of lane fwht_src_lane(gl)
 // (the order the fused transform takes), and the sign bits of D for them.
 template <int D>
 __device__ __forceinline__ int enc_src_lane(int gl) { return fwht_src_lane<D / 8>(gl); }
 
-__device__ __forceinline__ uint32_t enc_sign_bits(const uint32_t (&mask)[8], int sl) {
+__device__ __forceinline__ uint32_t enc_sign_bits(const uint32_t* mask, int sl) {
     return (mask[sl >> 2] >> ((sl & 3) * 8)) & 0xFFu;
 }
 
@@ -80,16 +115,16 @@ __device__ __forceinline__ uint32_t enc_sign_bits(const uint32_t (&mask)[8], int
 // [8 gl, 8 gl + 8) of H(D x).  v_sqrt_f32 (1 ulp) gives the norm: both the
 // half norm and the code decisions already allow 1e-6 relative.
 template <int D>
-__device__ __forceinline__ void rotate(VecState& st, int gl, uint32_t sbits) {
+__device__ __forceinline__ void rotate(VecState& st, int gl, uint32_t sbits, const CodecArgs& c) {
     constexpr int LPV = D / 8;
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(st.v[e], st.v[e], ss);
     ss = group_sum<LPV>(ss);
-    st.nrm = __builtin_amdgcn_sqrtf(ss);
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.v[e] = as_f(as_u(st.v[e]) ^ (((sbits >> e) & 1u) << 31));
     fwht_fused<LPV>(st.v, gl);
+    finish_rotation<D>(st, gl, c, ss);
 }
 
 // The same from the raw 16-byte words of 16-bit input: the D sign flip as
@@ -102,7 +137,8 @@ __device__ __forceinline__ void half_sign_masks(uint32_t sbits, uint32_t (&flip)
 }
 
 template <int D, int DT>
-__device__ __forceinline__ void rotate_raw16(Raw8<DT>& r, const uint32_t (&flip)[4], int gl, VecState& st) {
+__device__ __forceinline__ void rotate_raw16(Raw8<DT>& r, const uint32_t (&flip)[4], int gl, const CodecArgs& c,
+                                             VecState& st) {
     static_assert(DT != 0, "16-bit input");
     typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
     typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
@@ -122,8 +158,8 @@ __device__ __forceinline__ void rotate_raw16(Raw8<DT>& r, const uint32_t (&flip)
     r.w[0] = make_uint4(w[0], w[1], w[2], w[3]);
     unpack8<DT>(r, st.v);
     ss = group_sum<LPV>(ss);
-    st.nrm = __builtin_amdgcn_sqrtf(ss);
     fwht_fused<LPV>(st.v, gl);
+    finish_rotation<D>(st, gl, c, ss);
 }
 
 // Load row `row` (or zeros) from lane sl's elements, compute the norm, sign
@@ -138,7 +174,7 @@ __device__ __forceinline__ void load_rotate(const EncodeArgs& a, int64_t row, bo
 #pragma unroll
         for (int e = 0; e < 8; ++e) st.v[e] = 0.0f;
     }
-    rotate<D>(st, gl, sbits);
+    rotate<D>(st, gl, sbits, a.c);
 }
 
 // Output row of input row `row` (see EncodeArgs: plain, append or prefill
@@ -257,9 +293,9 @@ __device__ __forceinline__ void encode_rows(const EncodeArgs& a, const uint2* qt
             VecState st;
             if constexpr (DT == 0) {
                 unpack8<DT>(raw[u], st.v);
-                rotate<D>(st, gl, sbits);
+                rotate<D>(st, gl, sbits, a.c);
             } else {
-                rotate_raw16<D, DT>(raw[u], flip, gl, st);
+                rotate_raw16<D, DT>(raw[u], flip, gl, a.c, st);
             }
             uint32_t packed;
             if constexpr (TAB) {
@@ -272,7 +308,7 @@ __device__ __forceinline__ void encode_rows(const EncodeArgs& a, const uint2* qt
             const int64_t orow = valid ? out_row(a, row, keep) : 0;
             uint32_t* rowp = reinterpret_cast<uint32_t*>(a.codes + orow * a.code_stride);
             store_codes<BITS>(rowp, gl, packed, valid && keep);
-            if (valid && keep && gl == 0) a.norms[orow] = norm_to_half(st.nrm);
+            store_norms<D>(a, orow, gl, st, valid && keep);
         }
     }
 }
@@ -479,6 +515,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63;
     const int gl = lane & (LPV - 1);
     const uint32_t sbits = (a.c.sign_mask[gl >> 2] >> ((gl & 3) * 8)) & 0xFFu;
+    const int nb = D >= 256 ? a.c.norm_blocks : 1;
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
     for (int64_t base = wave * VPW; base < a.n; base += nwaves * VPW) {
@@ -492,8 +529,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = cent[(packed >> (BITS * e)) & ((1u << BITS) - 1u)];
+        // x_hat = D R(y_hat) / d with y_hat = n c (one norm) or nu_h sqrt(2) c on
+        // block h (two norms); R = H, or H D3 H / sqrt(d) (the same pass after H)
+        float sc;
+        if (nb == 2) {
+            const float nu = half_bits_to_float(a.norms[r * 2 + (gl >= LPV / 2 ? 1 : 0)]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] *= nu * 1.41421356237309505f;
+            sc = 1.0f / (float)D;
+        } else {
+            sc = half_bits_to_float(a.norms[r]) * (1.0f / (float)D);
+        }
         fwht<LPV>(v, gl);
-        const float sc = half_bits_to_float(a.norms[r]) * (1.0f / (float)D);
+        if constexpr (D == 64) {
+            if (a.c.rotation == TQ_ROT_DOUBLE) second_pass<LPV>(v, gl, a.c.sign_mask3);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = as_f(as_u(v[e] * sc) ^ (((sbits >> e) & 1u) << 31));
         if (valid) {
@@ -515,7 +565,9 @@ int encode_blocks(int64_t n, int d) {
 
 template <int D, int BITS, int DT>
 hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t s) {
-    if (a.c.residual == TQ_RES_SRHT || a.c.residual == TQ_RES_SIGN) {
+    if constexpr (D > 256) {
+        // d = 512 codecs have no residual (checked on the host)
+    } else if (a.c.residual == TQ_RES_SRHT || a.c.residual == TQ_RES_SIGN) {
         constexpr int VPB = 4 * (64 / (D / 8));
         const int64_t need = (a.n + VPB - 1) / VPB;
         const int grid = (int)(need < 16384 ? need : 16384);
@@ -527,7 +579,8 @@ hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t s) {
         const int64_t tiles = (a.n + QJL_TILE - 1) / QJL_TILE;
         const int grid = (int)(tiles < 8192 ? tiles : 8192);
         hipLaunchKernelGGL((encode_qjl_kernel<D, BITS, DT>), dim3(grid), dim3(256), 0, s, a);
-    } else {
+    }
+    if (a.c.qjl_m == 0) {
         if (a.c.qt_n > 0)
             hipLaunchKernelGGL((encode_kernel<D, BITS, DT, true>), dim3(encode_blocks(a.n, D)), dim3(256), 0, s, a);
         else
@@ -552,7 +605,8 @@ hipError_t launch_encode_d(const EncodeArgs& a, hipStream_t s) {
         case 32: return launch_encode_b<32, DT>(a, s);
         case 64: return launch_encode_b<64, DT>(a, s);
         case 128: return launch_encode_b<128, DT>(a, s);
-        default: return launch_encode_b<256, DT>(a, s);
+        case 256: return launch_encode_b<256, DT>(a, s);
+        default: return launch_encode_b<512, DT>(a, s);
     }
 }
 
@@ -588,7 +642,8 @@ static hipError_t launch_pair_t(const EncodeArgs& k, const EncodeArgs& v, hipStr
         case 32: return launch_pair_d<32, DT>(k, v, s);
         case 64: return launch_pair_d<64, DT>(k, v, s);
         case 128: return launch_pair_d<128, DT>(k, v, s);
-        default: return launch_pair_d<256, DT>(k, v, s);
+        case 256: return launch_pair_d<256, DT>(k, v, s);
+        default: return launch_pair_d<512, DT>(k, v, s);
     }
 }
 
@@ -619,7 +674,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
         case 32: return launch_decode_b<32>(a, s);
         case 64: return launch_decode_b<64>(a, s);
         case 128: return launch_decode_b<128>(a, s);
-        default: return launch_decode_b<256>(a, s);
+        case 256: return launch_decode_b<256>(a, s);
+        default: return launch_decode_b<512>(a, s);
     }
 }
 

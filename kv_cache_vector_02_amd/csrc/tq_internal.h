@@ -10,12 +10,15 @@ namespace tqi {
 
 // Everything one encode/decode launch needs, passed by value as a kernel argument.
 struct CodecArgs {
-    uint32_t sign_mask[8];
+    uint32_t sign_mask[16];  // D for dims 0..511 (words 8.. only at d = 512)
     float centroid[16];
     float threshold[15];
     int32_t d, bits, qjl_m;
     int32_t residual;        // TQ_RES_*
     uint32_t sign_mask2[8];  // second sign basis (TQ_RES_SRHT)
+    int32_t rotation;        // TQ_ROT_*
+    int32_t norm_blocks;     // 1 or 2
+    uint32_t sign_mask3[8];  // D3 of TQ_ROT_DOUBLE
     // the encoder's bin table (see plan_qtab): bin b = floor(z * qt_scale +
     // qt_off) of z = w / n holds at most one threshold; qt_n bins, 0 = none
     float qt_scale, qt_off, qt_inv_scale;

@@ -84,12 +84,21 @@ def test_attention_argument_errors():
     vc = tq.tq_codebook(2, 128, 0)
     vq = tq.tq_codebook(2, 128, 0, 64)
     k64 = tq.tq_codebook(4, 64, 0)
+    k64_3, v64_1 = tq.tq_codebook(3, 64, 0), tq.tq_codebook(1, 64, 0)
+    k32 = tq.tq_codebook(4, 32, 0)
+    kb2 = tq.tq_codebook_opts(3, 256, 0, norm_blocks=2)
+    k512 = tq.tq_codebook(3, 512, 0)
     P = FAKE
     ws = tq.tq_attn_workspace_bytes(kc, vc, 2, 14, 2, 1000)
     assert ws > 0
     assert tq.tq_attn_workspace_bytes(kc, vc, 2, 14, 3, 1000) == 0  # 14 % 3
     assert tq.tq_attn_workspace_bytes(kc, vq, 2, 14, 2, 1000) == 0  # QJL on V
-    assert tq.tq_attn_workspace_bytes(k64, k64, 2, 14, 2, 1000) == 0  # d = 64
+    assert tq.tq_attn_workspace_bytes(k64, k64, 2, 14, 2, 1000) > 0  # d = 64: 4-bit keys
+    assert tq.tq_attn_workspace_bytes(k64_3, k64, 2, 14, 2, 1000) == 0  # d = 64: 3-bit keys
+    assert tq.tq_attn_workspace_bytes(k64, v64_1, 2, 14, 2, 1000) == 0  # d = 64: 1-bit values
+    assert tq.tq_attn_workspace_bytes(k32, k32, 2, 14, 2, 1000) == 0  # d = 32
+    assert tq.tq_attn_workspace_bytes(kb2, kb2, 2, 14, 2, 1000) == 0  # two norm blocks
+    assert tq.tq_attn_workspace_bytes(k512, k512, 2, 14, 2, 1000) == 0  # d = 512
 
     def call(kc_, vc_, hq=14, hkv=2, cap=1000, q=P, wsb=ws, scale=0.1):
         return tq.raw_call("tq_attn_decode", ctypes.byref(kc_), ctypes.byref(vc_), q, 1, 2, hq, hkv, P, cap,
@@ -97,7 +106,8 @@ def test_attention_argument_errors():
 
     assert call(kc, vc, hkv=3) == tq.TQ_EUNSUPPORTED
     assert call(kc, vq) == tq.TQ_EUNSUPPORTED
-    assert call(k64, k64) == tq.TQ_EUNSUPPORTED
+    assert call(k64_3, k64) == tq.TQ_EUNSUPPORTED
+    assert call(kb2, kb2) == tq.TQ_EUNSUPPORTED
     assert call(kc, vc, cap=0) == tq.TQ_EINVAL
     assert call(kc, vc, q=None) == tq.TQ_EINVAL
     assert call(kc, vc, wsb=ws - 1) == tq.TQ_EWORKSPACE
@@ -388,3 +398,40 @@ def test_structured_residuals_need_no_projection():
     assert call(tq.tq_codebook_ex(3, 128, 0, tq.TQ_RES_SRHT)) == tq.TQ_EWORKSPACE
     assert call(tq.tq_codebook_ex(3, 128, 0, tq.TQ_RES_SIGN)) == tq.TQ_EWORKSPACE
     assert call(tq.tq_codebook(3, 128, 0, 128)) == tq.TQ_EINVAL
+
+
+def test_codebook_opts_matches_oracle():
+    """tq_codebook_opts: the double transform's D3 (SplitMix64 outputs 513..),
+    the d = 512 signs across sign_mask and sign_mask_hi, the rotation and norm
+    block fields; the shorter entry points fill the plain transform and one
+    norm."""
+    from oracle import tq_oracle as o
+    for seed in (0, 9, 2**63 + 7):
+        c = tq.tq_codebook_opts(3, 64, seed, tq.TQ_RES_NONE, 0, tq.TQ_ROT_DOUBLE, 1)
+        assert c.rotation == tq.TQ_ROT_DOUBLE and c.norm_blocks == 1
+        assert np.array_equal(np.array(c.signs3), o.third_sign_vector(seed, 64))
+        assert np.array_equal(np.array(c.signs), o.sign_vector(seed, 64))
+        w = tq.tq_codebook_opts(3, 512, seed, tq.TQ_RES_NONE, 0, tq.TQ_ROT_WHT, 2)
+        assert w.norm_blocks == 2 and np.array_equal(np.array(w.signs), o.sign_vector(seed, 512))
+    p = tq.tq_codebook(3, 128, 5)
+    assert p.rotation == tq.TQ_ROT_WHT and p.norm_blocks == 1
+
+
+def test_codebook_opts_errors():
+    bad = [
+        (3, 128, tq.TQ_RES_NONE, 0, tq.TQ_ROT_DOUBLE, 1),  # double transform: head_dim 64 only
+        (3, 128, tq.TQ_RES_NONE, 0, tq.TQ_ROT_WHT, 2),     # two norm blocks: d >= 256
+        (3, 256, tq.TQ_RES_QJL, 64, tq.TQ_ROT_WHT, 2),     # ... and no residual
+        (3, 512, tq.TQ_RES_QJL, 64, tq.TQ_ROT_WHT, 1),     # d = 512: no residual
+        (3, 256, tq.TQ_RES_NONE, 0, tq.TQ_ROT_WHT, 3),     # one or two blocks
+        (3, 64, tq.TQ_RES_NONE, 0, 2, 1),                  # unknown rotation
+    ]
+    for bits, d, res, m, rot, nb in bad:
+        c = tq.tq_codec()
+        rc = tq.raw_call("tq_codebook_opts", bits, d, ctypes.c_uint64(1), res, m, rot, nb, ctypes.byref(c))
+        assert rc == tq.TQ_EUNSUPPORTED, (bits, d, res, m, rot, nb)
+    # a codec edited into an unsupported combination is refused by every call
+    c = tq.tq_codebook(3, 128, 0)
+    c.rotation = tq.TQ_ROT_DOUBLE
+    assert tq.raw_call("tq_encode", ctypes.byref(c), FAKE, 0, 4, 128, FAKE, 48, FAKE, None, None, None,
+                       None) == tq.TQ_EUNSUPPORTED

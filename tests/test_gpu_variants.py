@@ -1,0 +1,183 @@
+"""GPU parity of the rotation and norm variants against the oracle: the double
+transform S1 -> WHT -> S2 -> WHT at head_dim 64 (encode, decode, attention,
+including residual keys, the window and multi-query decode) and per-block norms
+(two norm blocks at d = 256 and 512: encode and decode), with the d = 64 scan
+itself also checked under the plain transform."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import tq_oracle as o
+from tests import parity
+from tests.test_gpu_attn import gpu_attn, oracle_cache, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_vector_02_amd as lib
+    return lib
+
+
+def codecs(tq, bits, d, seed, rotation=0, norm_blocks=1, residual=o.RES_NONE, m=0):
+    ref = o.Codec(bits, d, seed, qjl_m=m, residual=residual, rotation=rotation, norm_blocks=norm_blocks)
+    lib = tq.tq_codebook_opts(bits, d, seed, residual, m, rotation, norm_blocks)
+    return ref, lib
+
+
+def gpu_encode(tq, codec, nb, x, S=None):
+    n = x.shape[0]
+    codes = torch.full((n, codec.d * codec.bits // 8), 0xA5, dtype=torch.uint8, device="cuda")
+    norms = torch.empty((n, nb) if nb > 1 else (n,), dtype=torch.float16, device="cuda")
+    qjl = gamma = None
+    if codec.qjl_m:
+        qjl = torch.empty(n, codec.qjl_m // 8, dtype=torch.uint8, device="cuda")
+        gamma = torch.empty(n, dtype=torch.float16, device="cuda")
+    tq.tq_encode(codec, x, codes, norms, S, qjl, gamma)
+    torch.cuda.synchronize()
+    out = {"codes": codes.cpu().numpy(), "norms": norms.cpu().numpy().view(np.uint16)}
+    if codec.qjl_m:
+        out["qjl"], out["gamma"] = qjl.cpu().numpy(), gamma.cpu().numpy().view(np.uint16)
+    return out
+
+
+def check_encode_decode(tq, x_cpu, bits, seed, dtype, rotation=0, norm_blocks=1, residual=o.RES_NONE, m=0,
+                        S_cpu=None):
+    n, d = x_cpu.shape
+    ref_c, lib_c = codecs(tq, bits, d, seed, rotation, norm_blocks, residual, m)
+    xs = x_cpu.to(dtype)
+    S = S_cpu.cuda() if S_cpu is not None else None
+    g = gpu_encode(tq, lib_c, norm_blocks, xs.cuda(), S)
+    S64 = None if S_cpu is None else S_cpu.numpy().astype(np.float64)
+    ref = o.encode(xs.float().numpy().astype(np.float64), ref_c, S64)
+    n_bad, bad_rows = parity.compare_codes(g["codes"], ref, ref_c)
+    parity.compare_halves(g["norms"].reshape(-1), np.asarray(ref["norm"]).reshape(-1),
+                          np.asarray(ref["norms"]).reshape(-1))
+    if m:
+        parity.compare_halves(g["gamma"], ref["gamma64"], ref["gamma"], skip=bad_rows)
+        Sref = S64 if S64 is not None else ref_c.projection()
+        parity.compare_qjl(g["qjl"], ref, Sref, ref_c, bad_rows)
+    # decode the oracle's bytes on the GPU
+    codes = torch.from_numpy(ref["codes"]).cuda()
+    norms = torch.from_numpy(np.ascontiguousarray(ref["norms"])).cuda()
+    xh = torch.empty(n, d, device="cuda")
+    tq.tq_decode(lib_c, codes, norms, xh)
+    torch.cuda.synchronize()
+    want = o.decode(ref["codes"], ref["norms"], ref_c)
+    n16 = np.asarray(ref["norms"], np.float64).reshape(n, -1).max(axis=1)
+    assert np.all(np.abs(xh.cpu().numpy() - want) <= parity.RECON_TOL * np.maximum(n16, 1e-30)[:, None] + 1e-30)
+    return n_bad
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+def test_double_transform_encode_decode(tq, bits, dtype):
+    """d = 64 with S1 -> WHT -> S2 -> WHT: codes (band rule), half norms,
+    reconstructions; ragged n (not a multiple of the vectors per wave)."""
+    x = synth.normal((3001, 64), seed=500 + bits)
+    x[:, :4] *= 20.0  # a few outlier channels
+    check_encode_decode(tq, x, bits, 31 + bits, dtype, rotation=o.ROT_DOUBLE)
+
+
+@pytest.mark.parametrize("residual", [o.RES_QJL, o.RES_SRHT, o.RES_SIGN])
+def test_double_transform_residual_encode(tq, residual):
+    """[P1] v1.5.3 item 2: head_dim-64 keys keep the 1-bit residual (2-bit
+    codes + residual signs with the double transform)."""
+    x = synth.normal((1500, 64), seed=520 + residual)
+    m = 64
+    S = synth.qjl_projection(m, 64, seed=521) if residual == o.RES_QJL else None
+    check_encode_decode(tq, x, 2, 41, torch.float16, rotation=o.ROT_DOUBLE, residual=residual, m=m, S_cpu=S)
+
+
+@pytest.mark.parametrize("d,nb", [(256, 2), (512, 1), (512, 2)])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_block_norms_encode_decode(tq, d, nb, bits):
+    """Two norm blocks ([P1] v1.5.2 item 5) at d = 256 and 512, and one norm at
+    d = 512; halves of different size so the two block norms differ."""
+    x = synth.normal((777, d), seed=600 + d + bits)
+    x[:, : d // 3] *= 4.0
+    check_encode_decode(tq, x, bits, 51, torch.bfloat16 if bits == 3 else torch.float32, norm_blocks=nb)
+
+
+def attn_case(tq, B, Hkv, g, cap, ctx_len, kbits, vbits, rotation, residual=o.RES_NONE, m=0, seed=0,
+              qdtype=torch.float16):
+    d = 64
+    Hq = Hkv * g
+    kk = torch.stack([synth.kv_block(Hkv, cap, d, seed + b, dtype=torch.float32)[0] for b in range(B)])
+    vv = torch.stack([synth.kv_block(Hkv, cap, d, seed + b, dtype=torch.float32)[1] for b in range(B)])
+    q = synth.normal((B, Hq, d), seed=seed + 99, dtype=qdtype)
+    S = synth.qjl_projection(m, d, seed=seed + 7) if residual == o.RES_QJL else None
+    kc_r, kc = codecs(tq, kbits, d, seed + 1, rotation, 1, residual, m)
+    vc_r, vc = codecs(tq, vbits, d, seed + 2, rotation)
+    S64 = None if S is None else S.numpy().astype(np.float64)
+    cache = oracle_cache(kk.numpy().astype(np.float64), vv.numpy().astype(np.float64), kc_r, vc_r, S64)
+    scale = 1.0 / math.sqrt(d)
+    got = gpu_attn(tq, kc, vc, q.cuda(), ctx_len, to_dev(cache), scale, None if S is None else S.cuda())
+    ref = o.gqa_attention(q.float().numpy().astype(np.float64), ctx_len, cache["k_codes"], cache["k_norms"],
+                          cache["v_codes"], cache["v_norms"], kc_r, vc_r, scale, cache.get("k_qjl"),
+                          cache.get("k_gamma"), S64)
+    got = got.reshape(-1, d)
+    assert np.all(np.isfinite(got))
+    rel = parity.rel_rows(got, ref)
+    assert rel.max() <= parity.ATTN_TOL, f"max rel {rel.max():.3e}"
+    return cache, q, kc, vc, kc_r, vc_r
+
+
+@pytest.mark.parametrize("kbits,vbits", [(4, 3), (4, 2), (2, 4), (2, 3)])
+@pytest.mark.parametrize("rotation", [o.ROT_WHT, o.ROT_DOUBLE])
+def test_d64_attention(tq, kbits, vbits, rotation):
+    """The d = 64 scan (64-token tiles over 16-dim lane groups), ragged
+    contexts over several tiles and splits, both transforms."""
+    attn_case(tq, B=2, Hkv=2, g=4, cap=2500, ctx_len=[2500, 1377], kbits=kbits, vbits=vbits, rotation=rotation,
+              seed=10 * kbits + vbits)
+
+
+@pytest.mark.parametrize("residual", [o.RES_QJL, o.RES_SRHT, o.RES_SIGN])
+def test_d64_double_attention_residual_keys(tq, residual):
+    """2-bit keys + 1-bit residual + double transform ([P1] v1.5.2 item 10,
+    TBQP3_3) with 3-bit values."""
+    attn_case(tq, B=1, Hkv=2, g=8, cap=1300, ctx_len=[1300], kbits=2, vbits=3, rotation=o.ROT_DOUBLE,
+              residual=residual, m=64, seed=70 + residual)
+
+
+def test_d64_double_window_and_multi_query(tq):
+    """The window kernel and multi-query decode at d = 64 with the double
+    transform (the window's value sum re-enters the rotated domain)."""
+    d, B, Hkv, g, cap, rw = 64, 2, 2, 3, 700, 40
+    ctx_len = [700, 333]
+    cache, q, kc, vc, kc_r, vc_r = attn_case(tq, B, Hkv, g, cap, ctx_len, 4, 3, o.ROT_DOUBLE, seed=90)
+    Hq = Hkv * g
+    dev = to_dev(cache)
+    # window
+    kw, vw = synth.kv_block(B * Hkv, rw, d, 95, dtype=torch.float16)
+    kw, vw = kw.view(B, Hkv, rw, d).contiguous(), vw.view(B, Hkv, rw, d).contiguous()
+    wl = [rw, 17]
+    ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, B, Hq, Hkv, cap))
+    out = torch.full((B, Hq, d), float("nan"), device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    tq.tq_attn_decode_rw(kc, vc, q.cuda(), torch.tensor(ctx_len, dtype=torch.int32, device="cuda"),
+                         dev["k_codes"], dev["k_norms"], dev["v_codes"], dev["v_norms"], kw.cuda(), vw.cuda(),
+                         torch.tensor(wl, dtype=torch.int32, device="cuda"), scale, out, ws)
+    torch.cuda.synchronize()
+    ref = o.gqa_attention(q.float().numpy().astype(np.float64), ctx_len, cache["k_codes"], cache["k_norms"],
+                          cache["v_codes"], cache["v_norms"], kc_r, vc_r, scale,
+                          k_win=kw.float().numpy().astype(np.float64), v_win=vw.float().numpy().astype(np.float64),
+                          win_len=wl)
+    assert parity.rel_rows(out.cpu().numpy().reshape(-1, d), ref).max() <= parity.ATTN_TOL
+    # multi-query: 3 causal columns
+    C = 3
+    qm = synth.normal((B, C, Hq, d), seed=96, dtype=torch.float16)
+    wsm = tq.workspace(tq.tq_workspace_bytes(tq.TQ_OP_ATTN_DECODE_MQ, kc, vc, B, Hq, Hkv, cap, n_q=C))
+    outm = torch.full((B, C, Hq, d), float("nan"), device="cuda")
+    tq.tq_attn_decode_mq(kc, vc, qm.cuda(), torch.tensor(ctx_len, dtype=torch.int32, device="cuda"),
+                         dev["k_codes"], dev["k_norms"], dev["v_codes"], dev["v_norms"], scale, outm, wsm)
+    torch.cuda.synchronize()
+    refm = o.mq_attention(qm.float().numpy().astype(np.float64), ctx_len, cache["k_codes"], cache["k_norms"],
+                          cache["v_codes"], cache["v_norms"], kc_r, vc_r, scale)
+    assert parity.rel_rows(outm.cpu().numpy().reshape(-1, d), refm).max() <= parity.ATTN_TOL
