@@ -385,8 +385,8 @@ def _check_cache(kc, vc, q, ctx_len, k_codes, k_norms, v_codes, v_norms, out, k_
     _shape(ctx_len, (B,), "ctx_len", torch.int32)
     _shape(k_codes, (B, Hkv, cap, kc.code_bytes), "k_codes", torch.uint8)
     _shape(v_codes, (B, Hkv, cap, vc.code_bytes), "v_codes", torch.uint8)
-    _shape(k_norms, (B, Hkv, cap), "k_norms", elem=2)
-    _shape(v_norms, (B, Hkv, cap), "v_norms", elem=2)
+    _shape(k_norms, _nshape(kc, (B, Hkv, cap)), "k_norms", elem=2)
+    _shape(v_norms, _nshape(vc, (B, Hkv, cap)), "v_norms", elem=2)
     _shape(out, (B, Hq, vc.d), "out", torch.float32)
     if kc.qjl_m:
         _qjl_rows(kc, B * Hkv * cap, qjl_S, k_qjl, k_gamma, ("qjl_S", "k_qjl", "k_gamma"))

@@ -416,15 +416,18 @@ static int attn_check(const tq_codec* kc, const tq_codec* vc, int batch, int nco
     if (!kc || !vc) return TQ_EINVAL;
     if (!valid_codec(kc) || !valid_codec(vc)) return TQ_EUNSUPPORTED;
     if (kc->d != vc->d || vc->qjl_m != 0) return TQ_EUNSUPPORTED;
-    // the scan's lane layout: d = 128 and 256 at every width; d = 64 with key
-    // bytes a whole number of dwords per lane group (2 or 4 bits) and 2..4-bit
-    // values; one norm per token
-    if (kc->d == 64) {
+    const bool wide = tqi::attn_wide(kc->d, kc->norm_blocks, vc->norm_blocks);
+    if (wide) {
+        // d = 512 or two norm blocks: the vector-ALU kernel, one query column,
+        // keys without a residual
+        if ((kc->d != 256 && kc->d != 512) || kc->qjl_m != 0 || ncols != 1) return TQ_EUNSUPPORTED;
+    } else if (kc->d == 64) {
+        // the scan's lane layout: key bytes a whole number of dwords per lane
+        // group (2 or 4 bits) and 2..4-bit values
         if ((kc->bits != 2 && kc->bits != 4) || vc->bits < 2) return TQ_EUNSUPPORTED;
     } else if (kc->d != 128 && kc->d != 256) {
         return TQ_EUNSUPPORTED;
     }
-    if (kc->norm_blocks != 1 || vc->norm_blocks != 1) return TQ_EUNSUPPORTED;
     if (batch <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || ctx_cap <= 0 || batch > 65535 || ncols <= 0)
         return TQ_EINVAL;
     if (n_q_heads % n_kv_heads != 0 || ncols > TQ_MAX_QUERY_COLS) return TQ_EUNSUPPORTED;
@@ -432,7 +435,8 @@ static int attn_check(const tq_codec* kc, const tq_codec* vc, int batch, int nco
     const int64_t row_max = kc->d * (kc->bits > vc->bits ? kc->bits : vc->bits) / 8 + kc->qjl_m / 8;
     if (ctx_cap > (((int64_t)1 << 31) - 1) / (row_max > 2 ? row_max : 2)) return TQ_EUNSUPPORTED;
     const int gv = n_q_heads / n_kv_heads * ncols;  // query rows per kv head
-    tqi::attn_plan(batch, n_kv_heads, gv, ctx_cap, kc->d, kc->bits, vc->bits, kc->qjl_m > 0, splits, split_tokens, G);
+    if (wide) tqi::wide_plan(batch, n_kv_heads, gv, ctx_cap, splits, split_tokens, G);
+    else tqi::attn_plan(batch, n_kv_heads, gv, ctx_cap, kc->d, kc->bits, vc->bits, kc->qjl_m > 0, splits, split_tokens, G);
     if ((int64_t)n_kv_heads * (gv / *G) > 65535) return TQ_EUNSUPPORTED;
     return TQ_OK;
 }
@@ -463,6 +467,11 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
     const int rc = attn_check(kc, vc, batch, ncols, n_q_heads, n_kv_heads, ctx_cap, &splits, &per, &G);
     if (rc != TQ_OK) return rc;
     if (ncols > 1 && win_cap > 0) return TQ_EUNSUPPORTED;  // the residual window serves one query column
+    if (tqi::attn_wide(kc->d, kc->norm_blocks, vc->norm_blocks)) {
+        // the vector-ALU kernel: no residual window and no softmax switches
+        if (win_cap > 0) return TQ_EUNSUPPORTED;
+        if (opts && (opts->score_mode != TQ_SCORE_PLAIN || opts->sparse_v > 0.0f)) return TQ_EUNSUPPORTED;
+    }
     if (q_dtype != TQ_F32 && q_dtype != TQ_F16 && q_dtype != TQ_BF16) return TQ_EINVAL;
     if (!q || !ctx_len || !k_codes || !k_norms || !v_codes || !v_norms || !out) return TQ_EINVAL;
     if (!aligned(q, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(out, 16) ||

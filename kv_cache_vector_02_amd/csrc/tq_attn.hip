@@ -112,6 +112,38 @@ void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int v
     *split_tokens = best_per;
 }
 
+bool attn_wide(int d, int k_blocks, int v_blocks) { return d == 512 || k_blocks != 1 || v_blocks != 1; }
+
+// Plan of the vector-ALU kernel: query rows in chunks of G <= 8 as above;
+// block splits of a multiple of 256 tokens (4 waves x 64), as many as give
+// about four blocks per compute unit; every block split yields 4 partials.
+void wide_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t* split_tokens, int* heads_per_chunk) {
+    int G = 1;
+    for (int c = 8; c >= 1; --c) {
+        if (g % c == 0) {
+            G = c;
+            break;
+        }
+    }
+    *heads_per_chunk = G;
+    const int64_t units = (int64_t)batch * hkv * (g / G);
+    const int64_t max_splits = ctx_cap > 0 ? (ctx_cap + 255) / 256 : 1;
+    int64_t sp = (4 * (int64_t)device_cus() + units - 1) / units;
+    sp = sp < 1 ? 1 : (sp > max_splits ? max_splits : sp);
+    int64_t per = ctx_cap > 0 ? (ctx_cap + sp - 1) / sp : 256;
+    per = (per + 255) & ~(int64_t)255;
+    if (const char* env = getenv("TQ_ATTN_SPLITS")) {  // test hook, as for the scan
+        const long want = strtol(env, nullptr, 10);
+        if (want > 0 && ctx_cap > 0) {
+            const int64_t w = want < max_splits ? (int64_t)want : max_splits;
+            per = ((ctx_cap + w - 1) / w + 255) & ~(int64_t)255;
+        }
+    }
+    sp = ctx_cap > 0 ? (ctx_cap + per - 1) / per : 1;
+    *splits = (int)(4 * sp);
+    *split_tokens = per;
+}
+
 static size_t align_floats(size_t n) { return (n + 63) & ~(size_t)63; }
 
 size_t attn_workspace(int batch, int hq, int d, int m, int splits) {
@@ -169,7 +201,15 @@ static hipError_t launch_qprep_combine_any(const AttnArgs& a, hipStream_t s, boo
     switch (a.kc.d) {
         case 64: return launch_qprep_combine<64>(a, s, prep);
         case 128: return launch_qprep_combine<128>(a, s, prep);
-        default: return launch_qprep_combine<256>(a, s, prep);
+        case 256: return launch_qprep_combine<256>(a, s, prep);
+        default: {
+            // d = 512 (no residual, so nothing to prepare): the combine only
+            if (prep) return hipSuccess;
+            constexpr int HPB = 256 / 64;
+            hipLaunchKernelGGL((attn::combine_kernel<512>), dim3((a.batch * a.ncols * a.hq + HPB - 1) / HPB),
+                               dim3(256), 0, s, a);
+            return hipGetLastError();
+        }
     }
 }
 
@@ -181,7 +221,7 @@ hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (stages & ATTN_SCAN) {
-        e = launch_split_any(a, s);
+        e = attn_wide(a.kc.d, a.kc.norm_blocks, a.vc.norm_blocks) ? launch_wide(a, s) : launch_split_any(a, s);
         if (e != hipSuccess) return e;
     }
     if ((stages & ATTN_WINDOW) && a.win_cap > 0) {

@@ -97,8 +97,11 @@ def test_attention_argument_errors():
     assert tq.tq_attn_workspace_bytes(k64_3, k64, 2, 14, 2, 1000) == 0  # d = 64: 3-bit keys
     assert tq.tq_attn_workspace_bytes(k64, v64_1, 2, 14, 2, 1000) == 0  # d = 64: 1-bit values
     assert tq.tq_attn_workspace_bytes(k32, k32, 2, 14, 2, 1000) == 0  # d = 32
-    assert tq.tq_attn_workspace_bytes(kb2, kb2, 2, 14, 2, 1000) == 0  # two norm blocks
-    assert tq.tq_attn_workspace_bytes(k512, k512, 2, 14, 2, 1000) == 0  # d = 512
+    # d = 512 and two norm blocks: the vector-ALU kernel, one query column only
+    assert tq.tq_attn_workspace_bytes(kb2, kb2, 2, 14, 2, 1000) > 0
+    assert tq.tq_attn_workspace_bytes(k512, k512, 2, 14, 2, 1000) > 0
+    assert tq.tq_workspace_bytes(tq.TQ_OP_ATTN_DECODE_MQ, k512, k512, 2, 14, 2, 1000, 2, 0, 0) == 0
+    assert tq.tq_workspace_bytes(tq.TQ_OP_ATTN_DECODE_MQ, k512, k512, 2, 14, 2, 1000, 1, 0, 0) > 0
 
     def call(kc_, vc_, hq=14, hkv=2, cap=1000, q=P, wsb=ws, scale=0.1):
         return tq.raw_call("tq_attn_decode", ctypes.byref(kc_), ctypes.byref(vc_), q, 1, 2, hq, hkv, P, cap,
@@ -107,7 +110,7 @@ def test_attention_argument_errors():
     assert call(kc, vc, hkv=3) == tq.TQ_EUNSUPPORTED
     assert call(kc, vq) == tq.TQ_EUNSUPPORTED
     assert call(k64_3, k64) == tq.TQ_EUNSUPPORTED
-    assert call(kb2, kb2) == tq.TQ_EUNSUPPORTED
+    assert call(kb2, k64) == tq.TQ_EUNSUPPORTED  # d mismatch
     assert call(kc, vc, cap=0) == tq.TQ_EINVAL
     assert call(kc, vc, q=None) == tq.TQ_EINVAL
     assert call(kc, vc, wsb=ws - 1) == tq.TQ_EWORKSPACE

@@ -181,3 +181,61 @@ def test_d64_double_window_and_multi_query(tq):
     refm = o.mq_attention(qm.float().numpy().astype(np.float64), ctx_len, cache["k_codes"], cache["k_norms"],
                           cache["v_codes"], cache["v_norms"], kc_r, vc_r, scale)
     assert parity.rel_rows(outm.cpu().numpy().reshape(-1, d), refm).max() <= parity.ATTN_TOL
+
+
+def oracle_cache_blocks(K, V, kc, vc):
+    """Packed oracle cache [B][Hkv][cap][...] whose norm planes keep a trailing
+    block axis for codecs with two norm blocks."""
+    B, H, cap, d = K.shape
+    ek = o.encode(K.reshape(-1, d), kc)
+    ev = o.encode(V.reshape(-1, d), vc)
+    return {"k_codes": ek["codes"].reshape(B, H, cap, -1),
+            "k_norms": ek["norms"].reshape((B, H, cap) + kc.norm_shape_tail),
+            "v_codes": ev["codes"].reshape(B, H, cap, -1),
+            "v_norms": ev["norms"].reshape((B, H, cap) + vc.norm_shape_tail)}
+
+
+def wide_case(tq, d, kbits, vbits, nb, B, Hkv, g, cap, ctx_len, seed, qdtype=torch.bfloat16, splits=None,
+              monkeypatch=None):
+    Hq = Hkv * g
+    kk = torch.stack([synth.kv_block(Hkv, cap, d, seed + b, dtype=torch.float32)[0] for b in range(B)])
+    vv = torch.stack([synth.kv_block(Hkv, cap, d, seed + b, dtype=torch.float32)[1] for b in range(B)])
+    q = synth.normal((B, Hq, d), seed=seed + 99, dtype=qdtype)
+    kc_r, kc = codecs(tq, kbits, d, seed + 1, norm_blocks=nb)
+    vc_r, vc = codecs(tq, vbits, d, seed + 2, norm_blocks=nb)
+    cache = oracle_cache_blocks(kk.numpy().astype(np.float64), vv.numpy().astype(np.float64), kc_r, vc_r)
+    if splits is not None:
+        monkeypatch.setenv("TQ_ATTN_SPLITS", str(splits))
+    scale = 1.0 / math.sqrt(d)
+    got = gpu_attn(tq, kc, vc, q.cuda(), ctx_len, to_dev(cache), scale)
+    ref = o.gqa_attention(q.float().numpy().astype(np.float64), ctx_len, cache["k_codes"], cache["k_norms"],
+                          cache["v_codes"], cache["v_norms"], kc_r, vc_r, scale)
+    got = got.reshape(-1, d)
+    assert np.all(np.isfinite(got))
+    zero_rows = np.linalg.norm(ref, axis=1) == 0
+    assert np.all(got[zero_rows] == 0)
+    rel = parity.rel_rows(got, ref)
+    assert rel.max() <= parity.ATTN_TOL, f"max rel {rel.max():.3e}"
+    return got
+
+
+@pytest.mark.parametrize("d,nb", [(512, 2), (512, 1), (256, 2)])
+@pytest.mark.parametrize("kbits,vbits", [(3, 3), (4, 2), (2, 4), (1, 1)])
+def test_wide_attention(tq, d, nb, kbits, vbits):
+    """Attention over two-norm-block caches ([P1] v1.5.2 item 5) and over
+    d = 512: ragged contexts across several 256-token block splits, an empty
+    sequence, GQA 4:1."""
+    wide_case(tq, d, kbits, vbits, nb, B=3, Hkv=2, g=4, cap=1500, ctx_len=[1500, 700, 0], seed=d + 10 * kbits + vbits)
+
+
+@pytest.mark.parametrize("g", [1, 8, 16])
+def test_wide_attention_head_groups(tq, g):
+    """One to sixteen query heads per kv head (16 = two blocks of 8 rows)."""
+    wide_case(tq, 512, 3, 3, 2, B=1, Hkv=2, g=g, cap=900, ctx_len=[777], seed=300 + g, qdtype=torch.float16)
+
+
+def test_wide_attention_split_invariance(tq, monkeypatch):
+    outs = [wide_case(tq, 512, 3, 3, 2, B=1, Hkv=1, g=8, cap=3000, ctx_len=[2999], seed=400, splits=s,
+                      monkeypatch=monkeypatch) for s in (1, 3, 12)]
+    for o2 in outs[1:]:
+        assert parity.rel_rows(o2, outs[0]).max() <= 1e-5
