@@ -16,7 +16,9 @@ tokens, fp16, K 4-bit + V 2-bit per step, over a 1 GiB rotating input pool),
 long-context decode (8 kv heads x 2^20 tokens, K3/V3, 64 bf16 query heads) and
 inner-product search (2^20 x 256 database, 3-bit + QJL m=256, 1024 queries,
 top-10; useful estimator TFLOP/s, and the matrix-core work issued against the
-dense fp16 peak).  `roofline` is the scan kernel's algorithmic bytes per launch over its
+dense fp16 peak), and decode over the caches of the rotation / norm variants
+(head_dim 64 with the double transform on the scan; head_dim 512 with one norm
+per 256-half on the vector-ALU kernel).  `roofline` is the scan kernel's algorithmic bytes per launch over its
 mean launch time, measured with HIP events recorded on the launch stream around
 the scan launch of every timed step (so the scan time is part of, and never
 longer than, the step time); `traffic` is the HBM bytes per scan launch from the
@@ -33,7 +35,7 @@ the GPU reach its sustained clock: a decode loop run straight from idle is
 timed while the clocks still ramp, which reads about 20% slower than the steady
 state a serving loop runs in.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs decode,encode,long,search,quality]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs decode,encode,long,search,variants,quality]
 """
 from __future__ import annotations
 
@@ -61,7 +63,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=2000)
-    ap.add_argument("--legs", default="decode,encode,long,search,quality")
+    ap.add_argument("--legs", default="decode,encode,long,search,variants,quality")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
@@ -383,6 +385,60 @@ def long_leg(tq, torch, synth, steps, warmup):
         "prefill_encode_ms": enc_ms,
         "prefill_encode_mvectors_per_s": 2 * Hkv * cap / (enc_ms * 1e-3) / 1e6,
     }
+
+
+# ---------------------------------------------------------------- variants ----
+def variants_leg(tq, torch, synth, steps, warmup):
+    """Decode over the caches of the rotation and norm variants, packed bytes
+    per second with 2 cache replicas (beyond the 256 MB Infinity Cache):
+      * head_dim 64 with the double transform S1 -> WHT -> S2 -> WHT, K4/V3
+        (the head_dim-64 recommendation of [P1] v1.5.3), 8:1 GQA on the scan;
+      * head_dim 512 with one norm per 256-half, K3/V3, 4:1 GQA, on the
+        vector-ALU kernel."""
+    out = {}
+    cases = (
+        ("double_wht_d64", dict(B=16, Hkv=8, g=8, ctx=32768, d=64, kb=4, vb=3, rot=tq.TQ_ROT_DOUBLE, nb=1),
+         "decode, batch 16, 64 query heads / 8 kv heads, d=64, context 32768, K4/V3, double transform"),
+        ("block_norm_d512", dict(B=4, Hkv=4, g=4, ctx=32768, d=512, kb=3, vb=3, rot=tq.TQ_ROT_WHT, nb=2),
+         "decode, batch 4, 16 query heads / 4 kv heads, d=512, context 32768, K3/V3, two norm blocks"),
+    )
+    for name, c, desc in cases:
+        B, Hkv, g, ctx, d = c["B"], c["Hkv"], c["g"], c["ctx"], c["d"]
+        kc = tq.tq_codebook_opts(c["kb"], d, 5, tq.TQ_RES_NONE, 0, c["rot"], c["nb"])
+        vc = tq.tq_codebook_opts(c["vb"], d, 5, tq.TQ_RES_NONE, 0, c["rot"], c["nb"])
+        nt = (c["nb"],) if c["nb"] > 1 else ()
+        caches = []
+        for r in range(2):
+            cc = {"k_codes": torch.empty(B, Hkv, ctx, kc.code_bytes, dtype=torch.uint8, device="cuda"),
+                  "k_norms": torch.empty((B, Hkv, ctx) + nt, dtype=torch.float16, device="cuda"),
+                  "v_codes": torch.empty(B, Hkv, ctx, vc.code_bytes, dtype=torch.uint8, device="cuda"),
+                  "v_norms": torch.empty((B, Hkv, ctx) + nt, dtype=torch.float16, device="cuda")}
+            for b in range(B):
+                k, v = synth.kv_block(Hkv, ctx, d, 7000 + 100 * r + b, device="cuda", dtype=torch.float16)
+                tq.tq_encode_kv(kc, vc, k.view(-1, d), v.view(-1, d), cc["k_codes"][b].view(-1, kc.code_bytes),
+                                cc["k_norms"][b].reshape(-1), cc["v_codes"][b].view(-1, vc.code_bytes),
+                                cc["v_norms"][b].reshape(-1))
+            caches.append(cc)
+        q = synth.normal((B, Hkv * g, d), seed=7500, dtype=torch.float16, device="cuda")
+        ctx_len = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+        o_ = torch.empty(B, Hkv * g, d, device="cuda")
+        ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, B, Hkv * g, Hkv, ctx))
+        scale = 1.0 / math.sqrt(d)
+
+        def step(i, ev=None, caches=caches, kc=kc, vc=vc, q=q, ctx_len=ctx_len, o_=o_, ws=ws, scale=scale):
+            cc = caches[i % 2]
+            tq.tq_attn_decode(kc, vc, q, ctx_len, cc["k_codes"], cc["k_norms"], cc["v_codes"], cc["v_norms"],
+                              scale, o_, ws)
+
+        ms = timed_loop(step, steps, max(warmup // 4, 1), torch)
+        per = (kc.code_bytes + 2 * c["nb"]) + (vc.code_bytes + 2 * c["nb"])
+        cache_bytes = B * Hkv * ctx * per
+        out[name] = {"workload": desc, "ms_per_step": ms, "bytes_per_token_head": per, "cache_bytes": cache_bytes,
+                     "gbs": cache_bytes / (ms * 1e-3) / 1e9,
+                     "pct_hbm_peak": 100.0 * cache_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del caches
+        torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------------ search ----
@@ -707,6 +763,10 @@ def main():
         log("search leg (2^20 x 256, 1024 queries)")
         res["search"] = search_leg(tq, torch, synth, args.steps, args.warmup)
         log(f"search: {res['search']['ms_per_call']:.2f} ms/call, {res['search']['tflops']:.1f} TFLOP/s")
+    if "variants" in legs:
+        log("variants leg (d=64 double transform, d=512 block norms)")
+        res["variants"] = variants_leg(tq, torch, synth, args.steps, args.warmup)
+        log("variants: " + ", ".join(f"{k} {v['gbs']:.0f} GB/s" for k, v in res["variants"].items()))
     if "quality" in legs:
         res["quality"] = quality_leg(tq, torch, synth)
         log(f"quality: {res['quality']}")
@@ -764,7 +824,7 @@ def main():
             line["read_ceiling"] = rc
     if cpu:
         line["cpu_baseline"] = cpu
-    for k in ("encode", "long", "search", "quality"):
+    for k in ("encode", "long", "search", "variants", "quality"):
         if k in res:
             line[k] = res[k]
     if "encode" in res:

@@ -13,11 +13,12 @@
 //     the block's rotated queries in LDS (broadcast reads),
 //     one float32 sum per head and norm block, scaled by the block's norm;
 //   * online softmax per head across the wave in log2 units;
-//   * value sums, lane = 8 (d = 512) or 4 (d = 256) dims: the tile's tokens
-//     one at a time, each token's V row read by the whole wave at once (one
-//     contiguous row per load), weights and V norms broadcast from the lane
-//     that scored the token; sums stay in the rotated domain (one inverse
-//     transform per output row in the combine).
+//   * value sums, lane = 8 (d = 512) or 4 (d = 256) dims: the tile's V rows
+//     (loaded by their token's lane at the start of the tile, in flight during
+//     the scores) staged in the wave's LDS tile, then the tokens one at a
+//     time, weights and V norms broadcast from the lane that scored the
+//     token; sums stay in the rotated domain (one inverse transform per output
+//     row in the combine).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -74,7 +75,10 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
     constexpr int DPL = D / 64;         // value dims per lane
     constexpr int PBITS = DPL * VB;     // a lane's value bits of one token (<= 32)
     static_assert(RBK % 4 == 0 && RBV % 8 == 0 && PBITS <= 32, "row layout");
+    constexpr int VW = RBV / 4;          // dwords of a V row
+    constexpr int VSTR = VW + 1;         // padded stride of the staged rows (odd: no bank conflicts)
     __shared__ __attribute__((aligned(16))) float qr[kWideRows * D];
+    __shared__ uint32_t vtile[4][64 * VSTR];
     __shared__ float cent[32];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -136,10 +140,23 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
         for (int e = 0; e < DPL; ++e) acc[h][e] = 0.0f;
     }
 
+    uint32_t* vt = vtile[wave];
     for (int t0 = t_beg + wave * 64; t0 < t_end; t0 += 256) {
         const int t = t0 + lane;
         const bool valid = t < t_end;
         const int tl = valid ? t : t_end - 1;
+        // this token's V row: loads out now, into the wave's LDS tile after
+        // the scores (the value loop then reads every token's row from LDS)
+        uint32_t vrow[VW];
+        {
+            const uint2* vp = reinterpret_cast<const uint2*>(vcodes + (int64_t)tl * RBV);
+#pragma unroll
+            for (int u = 0; u < VW / 2; ++u) {
+                const uint2 v = ld_stream2(vp + u);
+                vrow[2 * u] = v.x;
+                vrow[2 * u + 1] = v.y;
+            }
+        }
         // ---- scores (lane = token), one sum per head and norm block.  The
         // token's K row is read in groups of 32 codes (KB dwords); inside a
         // group the code fields sit at compile-time bit offsets.
@@ -223,14 +240,19 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
             }
         }
         // ---- value sums (lane = dims), the tile's tokens in order
+        // (the wave's previous tile is consumed: its rows can be replaced)
+#pragma unroll
+        for (int w = 0; w < VW; ++w) vt[lane * VSTR + w] = vrow[w];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int nt = t_end - t0 < 64 ? t_end - t0 : 64;
+        const int wi = pbit >> 5, sh = pbit & 31;
         for (int j = 0; j < nt; ++j) {
-            // the lane's PBITS bits of token j's row: a dword pair from one
-            // contiguous row read by the whole wave
-            const uint32_t* rp = reinterpret_cast<const uint32_t*>(vcodes + (int64_t)(t0 + j) * RBV);
-            const int wi = pbit >> 5, sh = pbit & 31;
-            const uint32_t lo = ld_stream1(rp + wi);
-            const uint32_t hi = (sh + PBITS > 32) ? ld_stream1(rp + wi + 1) : 0u;
+            // the lane's PBITS bits of token j's row (one staged row read by
+            // the whole wave: consecutive dwords, no bank conflicts)
+            const uint32_t lo = vt[j * VSTR + wi];
+            const uint32_t hi = (sh + PBITS > 32) ? vt[j * VSTR + wi + 1] : 0u;
             const uint32_t bits = sh ? __builtin_amdgcn_alignbit(hi, lo, sh) : lo;
             // token j's norm of this lane's block: both broadcast, then chosen
             const float v0j = bcast(vs0, j), v1j = bcast(vs1, j);
@@ -247,6 +269,10 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
                 }
             }
         }
+        // every lane has read the tile before any lane overwrites it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     // ---- this wave's partial: (max, sum, acc[D]) per row in split 4*split + wave
