@@ -315,6 +315,7 @@ def encode_leg(tq, torch, synth, steps, warmup):
         tq.tq_encode_kv(kc, vc, pool_k[li], pool_v[li], out_k[li], nk[li], out_v[li], nv[li])
 
     ms_kv = timed_loop(step_kv, max(steps, 512), max(warmup // 4, 1), torch)
+
     # single-call latency (one K+V layer), median of 20
     lat = []
     for i in range(20):
@@ -325,6 +326,24 @@ def encode_leg(tq, torch, synth, steps, warmup):
         torch.cuda.synchronize()
         lat.append(a.elapsed_time(b))
     lat.sort()
+
+    # one large launch: 2^19 keys (fp16, 4-bit) per tq_encode call over 4
+    # rotating inputs (512 MiB), where the per-launch cost no longer hides the
+    # kernel's own rate
+    big_n = 1 << 19
+    del pool_k, pool_v
+    torch.cuda.empty_cache()
+    big = [synth.kv_block(4, big_n // 4, d, synth.SEED_ENCODE + 100 + r, device="cuda", dtype=torch.float16)[0]
+           .reshape(big_n, d) for r in range(4)]
+    big_codes = torch.empty(big_n, kc.code_bytes, dtype=torch.uint8, device="cuda")
+    big_norms = torch.empty(big_n, dtype=torch.float16, device="cuda")
+
+    def step_big(i, ev=None):
+        tq.tq_encode(kc, big[i % 4], big_codes, big_norms)
+
+    ms_big = timed_loop(step_big, max(steps // 4, 20), max(warmup // 20, 5), torch)
+    big_bytes = big_n * (d * 2 + kc.code_bytes + 2)
+    del big
     vecs = 2 * n
     bytes_step = vecs * d * 2 + n * (kc.code_bytes + 2) + n * (vc.code_bytes + 2)
     return {
@@ -340,6 +359,13 @@ def encode_leg(tq, torch, synth, steps, warmup):
             "mvectors_per_s": vecs / (ms_kv * 1e-3) / 1e6,
             "ms_per_step": ms_kv,
             "gbs": bytes_step / (ms_kv * 1e-3) / 1e9,
+        },
+        "large_launch": {
+            "call": "tq_encode of 2^19 fp16 keys (4-bit) per launch, 4 rotating inputs",
+            "mvectors_per_s": big_n / (ms_big * 1e-3) / 1e6,
+            "ms_per_launch": ms_big,
+            "gbs": big_bytes / (ms_big * 1e-3) / 1e9,
+            "bytes_per_launch": big_bytes,
         },
     }
 

@@ -115,8 +115,8 @@ void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int v
 bool attn_wide(int d, int k_blocks, int v_blocks) { return d == 512 || k_blocks != 1 || v_blocks != 1; }
 
 // Plan of the vector-ALU kernel: query rows in chunks of G <= 8 as above;
-// block splits of a multiple of 256 tokens (4 waves x 64), as many as give
-// about four blocks per compute unit; every block split yields 4 partials.
+// splits of a multiple of 256 tokens (4 waves x 64), as many as give about two
+// blocks per compute unit (its registers and LDS hold two).
 void wide_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t* split_tokens, int* heads_per_chunk) {
     int G = 1;
     for (int c = 8; c >= 1; --c) {
@@ -128,7 +128,7 @@ void wide_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t*
     *heads_per_chunk = G;
     const int64_t units = (int64_t)batch * hkv * (g / G);
     const int64_t max_splits = ctx_cap > 0 ? (ctx_cap + 255) / 256 : 1;
-    int64_t sp = (4 * (int64_t)device_cus() + units - 1) / units;
+    int64_t sp = (2 * (int64_t)device_cus() + units - 1) / units;
     sp = sp < 1 ? 1 : (sp > max_splits ? max_splits : sp);
     int64_t per = ctx_cap > 0 ? (ctx_cap + sp - 1) / sp : 256;
     per = (per + 255) & ~(int64_t)255;
@@ -140,7 +140,7 @@ void wide_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t*
         }
     }
     sp = ctx_cap > 0 ? (ctx_cap + per - 1) / per : 1;
-    *splits = (int)(4 * sp);
+    *splits = (int)sp;
     *split_tokens = per;
 }
 

@@ -5,9 +5,10 @@
 // operations sum the dims of all four quarters of a token in one instruction,
 // so a norm per half cannot enter there; this kernel runs on the vector ALUs.
 //
-// Grid (block splits, kv head x head chunk, batch), 4 waves per block, and
-// every wave writes its own split partial (max, sum, acc[d]) in the layout the
-// combine kernel merges: the combine sees 4 x block splits partials per row.
+// Grid (splits, kv head x head chunk, batch), 4 waves per block taking the
+// split's 64-token tiles in turn; the waves merge their states through LDS and
+// the block writes one partial (max, sum, acc[d]) per row in the layout the
+// combine kernel merges.
 // Per 64-token tile of a wave:
 //   * scores, lane = token: the token's K codes (32 codes per load) against
 //     the block's rotated queries in LDS (broadcast reads),
@@ -77,9 +78,15 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
     static_assert(RBK % 4 == 0 && RBV % 8 == 0 && PBITS <= 32, "row layout");
     constexpr int VW = RBV / 4;          // dwords of a V row
     constexpr int VSTR = VW + 1;         // padded stride of the staged rows (odd: no bank conflicts)
-    __shared__ __attribute__((aligned(16))) float qr[kWideRows * D];
-    __shared__ uint32_t vtile[4][64 * VSTR];
+    // LDS: rotated queries, then the 4 waves' V tiles; after the token loop the
+    // same space holds the states of two waves for the block merge
+    constexpr int LOOP_DW = kWideRows * D + 4 * 64 * VSTR;
+    constexpr int MERGE_DW = 2 * kWideRows * (D + 2);
+    static_assert(MERGE_DW <= LOOP_DW, "merge area exceeds the loop space");
+    __shared__ __attribute__((aligned(16))) uint32_t smem[LOOP_DW];
     __shared__ float cent[32];
+    float* qr = reinterpret_cast<float*>(smem);
+    uint32_t* vtile = smem + kWideRows * D;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int split = blockIdx.x;
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
         for (int e = 0; e < DPL; ++e) acc[h][e] = 0.0f;
     }
 
-    uint32_t* vt = vtile[wave];
+    uint32_t* vt = vtile + wave * 64 * VSTR;
     for (int t0 = t_beg + wave * 64; t0 < t_end; t0 += 256) {
         const int t = t0 + lane;
         const bool valid = t < t_end;
@@ -275,22 +282,63 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // ---- this wave's partial: (max, sum, acc[D]) per row in split 4*split + wave
-    const int part_split = 4 * split + wave;
+    // ---- block merge of the 4 waves' (max, sum, acc) in two pairwise rounds
+    // through LDS (waves 2, 3 into 0, 1; then 1 into 0), then one partial per
+    // row of the block split: (max, sum, acc[D]) in the combine's layout
 #pragma unroll
     for (int h = 0; h < kWideRows; ++h) {
-        if (h >= G) break;
         float lh = l[h];
         lh += xor_lane<1>(lh);
         lh += xor_lane<2>(lh);
         lh += xor_lane<4>(lh);
         lh += xor_lane<8>(lh);
         lh += xor_lane<16>(lh);
-        lh += xor_lane<32>(lh);
-        float* pr = a.part + (((int64_t)b * a.hq + row0 + h) * a.splits + part_split) * (D + 2);
+        l[h] = lh + xor_lane<32>(lh);
+    }
+    float* mrg = reinterpret_cast<float*>(smem);  // [2][kWideRows][D + 2]
+    auto put = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < kWideRows; ++h) {
+            float* st = mrg + (slot * kWideRows + h) * (D + 2);
+            if (lane == 0) {
+                st[0] = m[h];
+                st[1] = l[h];
+            }
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) st[2 + DPL * lane + e] = acc[h][e];
+        }
+    };
+    auto take = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < kWideRows; ++h) {
+            const float* st = mrg + (slot * kWideRows + h) * (D + 2);
+            const float mo = st[0], lo = st[1];
+            const float mn = fmaxf(m[h], mo);
+            if (mn != -INFINITY) {
+                const float f = exp2f(m[h] - mn), fo = exp2f(mo - mn);
+                l[h] = l[h] * f + lo * fo;
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) acc[h][e] = acc[h][e] * f + st[2 + DPL * lane + e] * fo;
+                m[h] = mn;
+            }
+        }
+    };
+    __syncthreads();  // every wave is done with the queries and its tile
+    if (wave >= 2) put(wave - 2);
+    __syncthreads();
+    if (wave < 2) take(wave);
+    __syncthreads();
+    if (wave == 1) put(0);
+    __syncthreads();
+    if (wave != 0) return;
+    take(0);
+#pragma unroll
+    for (int h = 0; h < kWideRows; ++h) {
+        if (h >= G) break;
+        float* pr = a.part + (((int64_t)b * a.hq + row0 + h) * a.splits + split) * (D + 2);
         if (lane == 0) {
             pr[0] = m[h];
-            pr[1] = lh;
+            pr[1] = l[h];
         }
 #pragma unroll
         for (int e = 0; e < DPL; ++e) pr[2 + DPL * lane + e] = acc[h][e];
@@ -299,7 +347,7 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
 
 template <int D, int KB>
 hipError_t launch_wide_k(const AttnArgs& a, hipStream_t s) {
-    const dim3 grid(a.splits / 4, a.hkv * a.chunks, a.batch);
+    const dim3 grid(a.splits, a.hkv * a.chunks, a.batch);
     switch (a.vc.bits) {
         case 1: hipLaunchKernelGGL((wide_kernel<D, KB, 1>), grid, dim3(256), 0, s, a); break;
         case 2: hipLaunchKernelGGL((wide_kernel<D, KB, 2>), grid, dim3(256), 0, s, a); break;

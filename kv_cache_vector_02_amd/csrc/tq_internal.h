@@ -112,8 +112,7 @@ hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s);
 void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int vb, bool qjl, int* splits,
                int64_t* split_tokens, int* heads_per_chunk);
 // Head dimension 512 and two-norm-block caches: the vector-ALU kernel
-// (tq_attn_wide.hip) in place of the matrix-core scan; its plan counts four
-// partials (one per wave) per block split.
+// (tq_attn_wide.hip) in place of the matrix-core scan, with its own plan.
 bool attn_wide(int d, int k_blocks, int v_blocks);
 void wide_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t* split_tokens, int* heads_per_chunk);
 hipError_t launch_wide(const AttnArgs& a, hipStream_t s);
