@@ -540,7 +540,8 @@ size_t tq_attn_workspace_bytes(const tq_codec *kc, const tq_codec *vc, int batch
  *   c            codec (host) with qjl_m = m (0 = MSE-only estimate); qjl_S
  *                [m][d] for TQ_RES_QJL, NULL for the other kinds.
  *   q            [n_q][d] float32, 16-byte aligned.
- *   codes, norms [n_db][d*bits/8], [n_db]; qjl_bits [n_db][m/8]; qjl_gamma [n_db].
+ *   codes, norms [n_db][d*bits/8] (16-byte aligned), [n_db]; qjl_bits [n_db][m/8]
+ *                (4-byte aligned); qjl_gamma [n_db].
  *   out_scores   [n_q][k] float32;  out_ids [n_q][k] int64.  If n_db < k the tail
  *                is filled with -inf and id -1.
  *   workspace    >= tq_search_workspace_bytes(...) bytes, 16-byte aligned.

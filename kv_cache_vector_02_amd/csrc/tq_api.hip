@@ -686,7 +686,7 @@ int tq_ip_search(const tq_codec* c, const float* q, int n_q, const uint8_t* code
     const int rc = search_check(c, n_q, n_db, k);
     if (rc != TQ_OK) return rc;
     if (!q || !out_scores || !out_ids || !aligned(q, 16)) return TQ_EINVAL;
-    if (n_db > 0 && (!codes || !norms || !aligned(codes, 4) || !aligned(norms, 2))) return TQ_EINVAL;
+    if (n_db > 0 && (!codes || !norms || !aligned(codes, 16) || !aligned(norms, 2))) return TQ_EINVAL;
     if (c->qjl_m > 0 && n_db > 0 && (!qjl_bits || !qjl_gamma || !aligned(qjl_bits, 4))) return TQ_EINVAL;
     if (needs_S(c) && !qjl_S) return TQ_EINVAL;
     int nb;

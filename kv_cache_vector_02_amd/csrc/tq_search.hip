@@ -97,9 +97,12 @@ __global__ __launch_bounds__(64) void search_qprep_kernel(SearchArgs a) {
 // part is a normal half; the scale comes off the float32 result.
 //
 // A block of 4 waves takes 32 queries (8 per wave, their operands kept in
-// registers) and a range of database rows in tiles of 64 staged through LDS;
-// each wave scores all 64 rows of a tile for its queries and inserts them into
-// its queries' exact top-k lists, so after staging the waves run independently.
+// registers) and a range of database rows in tiles of 64 staged through LDS
+// (rows padded so that the 16 rows a step reads sit on distinct banks); each
+// wave scores the tile's rows 16 at a time for its queries.  A lane keeps its
+// query's k-th best score in a register, so a group of 16 rows costs one
+// compare per score and a wave vote, and only rows above that score go
+// through the query's exact top-k list in LDS.
 typedef _Float16 sh8_t __attribute__((ext_vector_type(8)));
 typedef float sf4_t __attribute__((ext_vector_type(4)));
 
@@ -131,9 +134,19 @@ __device__ __forceinline__ float wmax64(float v) {
 }
 
 template <int D, int BITS, int KM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void search_mfma_kernel(SearchArgs a) {
-    constexpr int RB = D * BITS / 8;   // code bytes per row
+// Three waves per SIMD (168 registers) where the kernel fits them without
+// spilling; at d = 256 only the 3-bit variant does, the others take two.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 && BITS != 3 ? 2 : 3))) void search_mfma_kernel(
+    SearchArgs a) {
+    constexpr int RB = D * BITS / 8;   // code bytes per row (a multiple of 16)
     constexpr int RW = RB / 4;         // ... dwords
+    // LDS row stride of the staged codes: RW + 2 = 2 x odd, so the 16 rows a
+    // sub-tile reads at once start on distinct even banks
+    constexpr int RWP = RW + 2;
+    constexpr int RV = RB / 16;        // 16-byte pieces per row
+    constexpr int NV = MT * RV;        // ... per tile
+    constexpr int BWP = 9;             // LDS row stride of the sign bits (<= 8 dwords used), dwords
+    constexpr int KP = KM + 1;         // list stride: the 8 lists of a wave on distinct banks
     constexpr int DG = D / 4;          // dims per lane group
     constexpr int KS = DG / 4;         // centroid k steps
     constexpr int GW = DG * BITS / 32; // code dwords per lane group and row
@@ -143,17 +156,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     // entries (at 4 bits 8 copies keep the table at 16 KB)
     constexpr int TS = BITS <= 3 ? 32 : 8;
     const int m = a.c.qjl_m;
-    const int JS = m >> 5;             // QJL k steps (<= 8)
-    const int MW = m >> 5;             // sign dwords per row
+    // QJL k steps (<= 8); also the sign bytes of a lane group's m/4 projections
+    // and the sign dwords of a row
+    const int JS = m >> 5;
     const int k = a.k;
     __shared__ __attribute__((aligned(16))) uint2 tab[TE * TS];  // two codes: hi a, hi b | lo a, lo b (of 16 c)
     __shared__ __attribute__((aligned(16))) uint2 sgn[16 * 32];  // nibble -> 4 halves of +-16, 32 copies
-    __shared__ __attribute__((aligned(16))) uint32_t rcode[MT * RW];
-    __shared__ __attribute__((aligned(16))) uint32_t rbits[MT * 8];
-    __shared__ float rn[MT], rg[MT];
-    __shared__ float es[MQ][MT + 1];
-    __shared__ float lst_s[MQ][KM];
-    __shared__ int32_t lst_i[MQ][KM];
+    __shared__ __attribute__((aligned(16))) uint32_t rcode[MT * RWP];
+    __shared__ __attribute__((aligned(16))) uint32_t rbits[MT * BWP];
+    __shared__ __attribute__((aligned(16))) float rn[MT];
+    __shared__ __attribute__((aligned(16))) float rg[MT];
+    __shared__ float es[MQ][17];       // candidate scores of one sub-tile (16 rows)
+    __shared__ float lst_s[MQ * KP];
+    __shared__ int32_t lst_i[MQ * KP];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, grp = lane >> 4;
@@ -173,10 +188,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
         auto sg = [&](int b) { return ((x >> b) & 1) ? 16.0f : -16.0f; };
         sgn[i] = make_uint2(pack_h2(sg(0), sg(1)), pack_h2(sg(2), sg(3)));
     }
-    const int tsl = lane % TS, ssl = lane & 31;  // this lane's table copies
-    for (int e = tid; e < MQ * KM; e += 256) {
-        lst_s[e / KM][e % KM] = -INFINITY;
-        lst_i[e / KM][e % KM] = -1;
+    const uint2* tabl = tab + lane % TS;  // this lane's table copies
+    const uint2* sgnl = sgn + (lane & 31);
+    for (int e = tid; e < MQ * KP; e += 256) {
+        lst_s[e] = -INFINITY;
+        lst_i[e] = -1;
     }
 
     // this wave's query operands: column n <-> query q0 + 8 wave + (n & 7), hi (n < 8) or lo
@@ -226,96 +242,151 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
         }
     }
 
+    // k-th best score so far of this lane's query (n & 7); only larger scores
+    // can enter its list
+    float thr = -INFINITY;
+    const int ql = 8 * wave + (n & 7);
     for (int64_t t0 = r_beg; t0 < r_end; t0 += MT) {
         const int nt = (int)((r_end - t0) < MT ? (r_end - t0) : MT);
         __syncthreads();  // the previous tile's rows are no longer read
-        for (int e = tid; e < MT * RW; e += 256) {
-            const int r = e / RW;
-            rcode[e] = r < nt ? reinterpret_cast<const uint32_t*>(a.codes + (t0 + r) * RB)[e % RW] : 0u;
+        {
+            // the tile's code rows are contiguous in memory: 16-byte pieces
+            // into rows of RWP dwords
+            const uint4* src = reinterpret_cast<const uint4*>(a.codes + t0 * RB);
+            const int nv = nt * RV;
+#pragma unroll
+            for (int i = 0; i < (NV + 255) / 256; ++i) {
+                const int e = tid + 256 * i;
+                if (NV % 256 == 0 || e < NV) {
+                    const uint4 v = e < nv ? src[e] : make_uint4(0u, 0u, 0u, 0u);
+                    const int row = e / RV, c = e - row * RV;
+                    uint2* dst = reinterpret_cast<uint2*>(rcode + row * RWP + 4 * c);
+                    dst[0] = make_uint2(v.x, v.y);
+                    dst[1] = make_uint2(v.z, v.w);
+                }
+            }
         }
-        for (int e = tid; e < MT * MW; e += 256) {
-            const int r = e / MW;
-            rbits[r * 8 + e % MW] = r < nt ? reinterpret_cast<const uint32_t*>(a.qjl + (t0 + r) * (m >> 3))[e % MW] : 0u;
+        if (JS > 0) {
+            // four threads per row, sign dwords w and w + 4
+            const int row = tid >> 2;
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(a.qjl + (t0 + row) * (int64_t)(m >> 3));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int w = (tid & 3) + 4 * h;
+                if (w < JS) rbits[row * BWP + w] = row < nt ? src[w] : 0u;
+            }
         }
         if (tid < MT) {
             rn[tid] = tid < nt ? half_bits_to_float(a.norms[t0 + tid]) : 0.0f;
-            rg[tid] = (tid < nt && m > 0) ? half_bits_to_float(a.gamma[t0 + tid]) : 0.0f;
+        } else if (tid < 2 * MT) {
+            const int r = tid - MT;
+            rg[r] = (r < nt && m > 0) ? half_bits_to_float(a.gamma[t0 + r]) : 0.0f;
         }
         __syncthreads();
 #pragma unroll 1
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4 && 16 * j < nt; ++j) {
             const int r = 16 * j + n;  // this lane's row of the A side
             uint32_t cw[GW];
 #pragma unroll
-            for (int w = 0; w < GW; ++w) cw[w] = rcode[r * RW + grp * GW + w];
-            sf4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint2 e0 = tab[bits_at<2 * BITS>(cw, 4 * ks * BITS) * TS + tsl];
-                const uint2 e1 = tab[bits_at<2 * BITS>(cw, (4 * ks + 2) * BITS) * TS + tsl];
+            for (int w = 0; w < GW; ++w) cw[w] = rcode[r * RWP + grp * GW + w];
+            // two centroid accumulators (even and odd k steps) and the QJL one:
+            // independent matrix-core chains.  The QJL part takes A = 16 (+-1):
+            // the row's gamma multiplies its float32 result instead of the
+            // operands.  Step js takes the projections of sign byte
+            // grp * JS + js of the row.
+            sf4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0, accq = acc0;
+            auto centroid_step = [&](int ks, sf4_t& acc) {
+                const uint2 e0 = tabl[bits_at<2 * BITS>(cw, 4 * ks * BITS) * TS];
+                const uint2 e1 = tabl[bits_at<2 * BITS>(cw, (4 * ks + 2) * BITS) * TS];
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_sh8(make_uint4(e0.x, e0.y, e1.x, e1.y)), bq[ks], acc, 0, 0, 0);
-            }
-            // the QJL part in its own accumulator with A = 16 (+-1): the row's
-            // gamma multiplies the float32 result instead of the operands
-            sf4_t accq = {0.0f, 0.0f, 0.0f, 0.0f};
+            };
+            auto qjl_step = [&](int js, uint32_t lo4, uint32_t hi4) {
+                const uint2 lo = sgnl[lo4 * 32], hi = sgnl[hi4 * 32];
+                accq = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_sh8(make_uint4(lo.x, lo.y, hi.x, hi.y)), bj[js], accq, 0, 0, 0);
+            };
+            if (JS == 8) {
+                // all eight steps, with no branch: the lane's 8 sign bytes in two
+                // dwords, steps interleaved with the centroid ones
+                const uint32_t sw[2] = {rbits[r * BWP + 2 * grp], rbits[r * BWP + 2 * grp + 1]};
+                auto full_qjl = [&](int js) {
+                    const uint32_t w = sw[js >> 2];
+                    const int sh = 8 * (js & 3);
+                    qjl_step(js, (w >> sh) & 15u, (w >> (sh + 4)) & 15u);
+                };
 #pragma unroll
-            for (int js = 0; js < 8; ++js) {
-                if (js < JS) {
-                    const int j0 = grp * (m >> 2) + 8 * js;
-                    const uint32_t byte = (rbits[r * 8 + (j0 >> 5)] >> (j0 & 31)) & 0xFFu;
-                    const uint2 lo = sgn[(byte & 15u) * 32 + ssl], hi = sgn[(byte >> 4) * 32 + ssl];
-                    accq = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_sh8(make_uint4(lo.x, lo.y, hi.x, hi.y)), bj[js],
-                                                                 accq, 0, 0, 0);
+                for (int ks = 0; ks < KS; ++ks) {
+                    centroid_step(ks, (ks & 1) ? acc1 : acc0);
+                    if ((ks & 1) && (ks >> 1) < 8) full_qjl(ks >> 1);
+                }
+#pragma unroll
+                for (int js = KS / 2; js < 8; ++js) full_qjl(js);
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) centroid_step(ks, (ks & 1) ? acc1 : acc0);
+                const uint8_t* sb = reinterpret_cast<const uint8_t*>(rbits + r * BWP) + grp * JS;
+#pragma unroll
+                for (int js = 0; js < 8; ++js) {
+                    if (js < JS) {
+                        const uint32_t byte = sb[js];
+                        qjl_step(js, byte & 15u, byte >> 4);
+                    }
                 }
             }
+            sf4_t acc = acc0 + acc1;
             // column n + 8 holds the q_lo part of query n: add the two halves
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 acc[v] += xor_lane<8>(acc[v]);
                 accq[v] += xor_lane<8>(accq[v]);
             }
-            if (n < 8) {
+            // lanes n < 8: estimates of rows 16 j + 4 grp + v for query n
+            const float4 n4 = *reinterpret_cast<const float4*>(rn + 16 * j + 4 * grp);
+            const float4 g4 = *reinterpret_cast<const float4*>(rg + 16 * j + 4 * grp);
+            const float nv4[4] = {n4.x, n4.y, n4.z, n4.w}, gv4[4] = {g4.x, g4.y, g4.z, g4.w};
+            float s[4];
+            uint32_t f = 0;  // bit v: row 4 grp + v beats the list's k-th score
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int row = 16 * j + 4 * grp + v;
-                    es[8 * wave + n][row] = row < nt ? rn[row] * (fmaf(rg[row], accq[v], acc[v]) * qinv) : -INFINITY;
-                }
+            for (int v = 0; v < 4; ++v) {
+                const int row = 16 * j + 4 * grp + v;
+                s[v] = (n < 8 && row < nt) ? nv4[v] * (fmaf(gv4[v], accq[v], acc[v]) * qinv) : -INFINITY;
+                f |= (s[v] > thr ? 1u : 0u) << v;
             }
-        }
-        // this wave's queries: exact top-k insertion (score desc, id asc; ids
-        // grow along the scan, so an equal score never displaces an entry)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < 8) {
-            const int ql = 8 * wave + lane;
-            float* ls = lst_s[ql];
-            int32_t* li = lst_i[ql];
-            float thr = ls[k - 1];  // the list's k-th score: only larger scores enter
-            for (int tb = 0; tb < nt; tb += 8) {
-                float sv[8], mx = -INFINITY;
+            if (__builtin_amdgcn_ballot_w64(f != 0) == 0) continue;  // no candidate in the wave: the common case
+            // exact top-k insertion of the candidates, in row order (score
+            // desc, id asc; ids grow along the scan, so an equal score never
+            // displaces an entry)
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {  // 8 independent loads, then one compare in the common case
-                    sv[u] = tb + u < nt ? es[ql][tb + u] : -INFINITY;
-                    mx = fmaxf(mx, sv[u]);
-                }
-                if (mx > thr) {
-                    for (int u = 0; u < 8; ++u) {
-                        const float sc = sv[u];
-                        if (sc > ls[k - 1]) {
-                            int pos = k - 1;
-                            while (pos > 0 && ls[pos - 1] < sc) {
-                                ls[pos] = ls[pos - 1];
-                                li[pos] = li[pos - 1];
-                                --pos;
-                            }
-                            ls[pos] = sc;
-                            li[pos] = (int32_t)(t0 + tb + u);
+            for (int v = 0; v < 4; ++v)
+                if ((f >> v) & 1u) es[ql][4 * grp + v] = s[v];
+            // candidate rows of query n (bit 4 grp + v) gathered from lanes n + 16 grp
+            uint32_t mk = f | (xor_lane_u<16>(f) << 4);
+            mk |= xor_lane_u<32>(mk) << 8;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float kth = -INFINITY;
+            if (lane < 8) {
+                float* ls = lst_s + ql * KP;
+                int32_t* li = lst_i + ql * KP;
+                while (mk != 0) {
+                    const int i = __builtin_ctz(mk);
+                    mk &= mk - 1u;
+                    const float sc = es[ql][i];
+                    if (sc > ls[k - 1]) {
+                        int pos = k - 1;
+                        while (pos > 0 && ls[pos - 1] < sc) {
+                            ls[pos] = ls[pos - 1];
+                            li[pos] = li[pos - 1];
+                            --pos;
                         }
+                        ls[pos] = sc;
+                        li[pos] = (int32_t)(t0 + 16 * j + i);
                     }
-                    thr = ls[k - 1];
                 }
+                kth = ls[k - 1];
             }
+            // every lane of query n takes its new k-th score from lane n & 7
+            thr = __int_as_float(__builtin_amdgcn_ds_bpermute((n & 7) << 2, __float_as_int(kth)));
         }
     }
     __syncthreads();
@@ -323,8 +394,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
         const int q = e / k, jj = e % k;
         if (q0 + q < a.n_q) {
             const int64_t o = ((int64_t)(q0 + q) * a.n_blocks + blockIdx.x) * k + jj;
-            a.cand_s[o] = lst_s[q][jj];
-            a.cand_i[o] = lst_i[q][jj];
+            a.cand_s[o] = lst_s[q * KP + jj];
+            a.cand_i[o] = lst_i[q * KP + jj];
         }
     }
 }

@@ -205,9 +205,10 @@ def test_search_argument_errors():
     assert tq.tq_search_workspace_bytes(c, 16, 1000, 65) == 0
     assert tq.tq_search_workspace_bytes(tq.tq_codebook(3, 64, 0), 16, 1000, 10) == 0
 
-    def call(k=10, wsb=ws, S=P, nq=16):
-        return tq.raw_call("tq_ip_search", ctypes.byref(c), P, nq, P, P, P, P, S, 1000, k, P, P, P, wsb, None)
+    def call(k=10, wsb=ws, S=P, nq=16, codes=P):
+        return tq.raw_call("tq_ip_search", ctypes.byref(c), P, nq, codes, P, P, P, S, 1000, k, P, P, P, wsb, None)
 
+    assert call(codes=ctypes.c_void_p((1 << 20) + 4)) == tq.TQ_EINVAL  # codes not 16-byte aligned
     assert call(k=0) == tq.TQ_EUNSUPPORTED
     assert call(k=65) == tq.TQ_EUNSUPPORTED
     assert call(wsb=ws - 16) == tq.TQ_EWORKSPACE
