@@ -665,7 +665,7 @@ size_t tq_search_workspace_bytes(const tq_codec* c, int n_q, int64_t n_db, int k
     if (search_check(c, n_q, n_db, k) != TQ_OK) return 0;
     int nb;
     int64_t rows;
-    tqi::search_plan(n_q, n_db, k, &nb, &rows);
+    tqi::search_plan(n_q, n_db, k, c->d, c->bits, &nb, &rows);
     return tqi::search_workspace(n_q, c->d, c->qjl_m, k, nb);
 }
 
@@ -691,7 +691,7 @@ int tq_ip_search(const tq_codec* c, const float* q, int n_q, const uint8_t* code
     if (needs_S(c) && !qjl_S) return TQ_EINVAL;
     int nb;
     int64_t rows;
-    tqi::search_plan(n_q, n_db, k, &nb, &rows);
+    tqi::search_plan(n_q, n_db, k, c->d, c->bits, &nb, &rows);
     const size_t need = tqi::search_workspace(n_q, c->d, c->qjl_m, k, nb);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return TQ_EWORKSPACE;
     tqi::SearchArgs a;

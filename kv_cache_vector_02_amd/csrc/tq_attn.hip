@@ -42,7 +42,7 @@ static int split_blocks_any(int d, int kb, int vb, bool qjl) {
 }
 
 // Compute units of the current device (cached per device).
-static int device_cus() {
+int device_cus() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;

@@ -121,6 +121,8 @@ hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s);
 template <int D, int KB>
 int split_blocks_dk(int vb, bool qjl);
 size_t attn_workspace(int batch, int hq, int d, int m, int splits);
+// Compute units of the current device (cached per device; 1 without one).
+int device_cus();
 
 struct SearchArgs {
     CodecArgs c;
@@ -143,7 +145,7 @@ struct SearchArgs {
     int64_t block_rows;
 };
 hipError_t launch_search(const SearchArgs& a, hipStream_t s);
-void search_plan(int n_q, int64_t n_db, int k, int* n_blocks, int64_t* block_rows);
+void search_plan(int n_q, int64_t n_db, int k, int d, int bits, int* n_blocks, int64_t* block_rows);
 size_t search_workspace(int n_q, int d, int m, int k, int n_blocks);
 
 }  // namespace tqi

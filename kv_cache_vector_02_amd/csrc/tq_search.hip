@@ -14,6 +14,10 @@
 // lists, ordered by estimate descending then id ascending).
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
+
+#include <atomic>
+#include <type_traits>
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -473,19 +477,76 @@ hipError_t launch_scan_b(const SearchArgs& a, hipStream_t s) {
 
 }  // namespace
 
-void search_plan(int n_q, int64_t n_db, int k, int* n_blocks, int64_t* block_rows) {
-    // DB chunks of a multiple of 64 rows, about 4096 rows, at most ~4096
-    // candidates per query for the merge.
-    (void)n_q;
-    int64_t rows = 4096;
-    int64_t nb = (n_db + rows - 1) / rows;
-    const int64_t max_nb = 4096 / (k > 0 ? k : 1);
-    if (nb > max_nb) {
-        nb = max_nb;
-        rows = ((n_db + nb - 1) / nb + 63) & ~(int64_t)63;
-        nb = (n_db + rows - 1) / rows;
+// Resident scan blocks per compute unit for this variant (cached; 0 without a device).
+static int search_blocks(int d, int bits, int k) {
+    static std::atomic<int> cache[2][4][2];
+    std::atomic<int>& c = cache[d == 256 ? 1 : 0][bits - 1][k <= 32 ? 0 : 1];
+    int nb = c.load(std::memory_order_relaxed);
+    if (nb > 0) return nb;
+    const void* f = nullptr;
+    auto pick = [&](auto dk) {
+        constexpr int D = decltype(dk)::value;
+        if (k <= 32) {
+            switch (bits) {
+                case 1: f = (const void*)search_mfma_kernel<D, 1, 32>; break;
+                case 2: f = (const void*)search_mfma_kernel<D, 2, 32>; break;
+                case 3: f = (const void*)search_mfma_kernel<D, 3, 32>; break;
+                default: f = (const void*)search_mfma_kernel<D, 4, 32>; break;
+            }
+        } else {
+            switch (bits) {
+                case 1: f = (const void*)search_mfma_kernel<D, 1, KMAX>; break;
+                case 2: f = (const void*)search_mfma_kernel<D, 2, KMAX>; break;
+                case 3: f = (const void*)search_mfma_kernel<D, 3, KMAX>; break;
+                default: f = (const void*)search_mfma_kernel<D, 4, KMAX>; break;
+            }
+        }
+    };
+    if (d == 256) pick(std::integral_constant<int, 256>{});
+    else pick(std::integral_constant<int, 128>{});
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, 256, 0) != hipSuccess || nb <= 0) {
+        (void)hipGetLastError();
+        return 0;
     }
+    c.store(nb, std::memory_order_relaxed);
+    return nb;
+}
+
+// Database rows per block: a multiple of 64, as many as give one round of
+// blocks over the device's resident block slots (compute units x blocks per
+// unit for this variant) across the ceil(n_q / 32) query tiles.  A block's
+// fixed costs (its query operands, list setup and write-out, and the early
+// insertions while its lists fill) shrink per row as the block grows, so the
+// fewest blocks that still occupy every slot are the fastest (measured on the
+// 2^20 x 256 database with 1024 queries: 4096 rows per block 7.4 ms, two
+// rounds 5.2 ms, one round 4.9 ms).  At most 4096 / k blocks, so the merge
+// sees at most 4096 candidates per query.  The plan depends on the current
+// device.
+void search_plan(int n_q, int64_t n_db, int k, int d, int bits, int* n_blocks, int64_t* block_rows) {
+    const int64_t qt = ((int64_t)(n_q > 0 ? n_q : 1) + MQ - 1) / MQ;
+    const int per_cu = search_blocks(d, bits, k);
+    const int64_t slots = (int64_t)device_cus() * (per_cu > 0 ? per_cu : 1);
+    const int64_t max_nb = 4096 / (k > 0 ? k : 1);
+    int64_t nb = (slots + qt - 1) / qt;
+    nb = nb < 1 ? 1 : (nb > max_nb ? max_nb : nb);
+    int64_t rows = ((n_db + nb - 1) / nb + 63) & ~(int64_t)63;
+    if (rows < 64) rows = 64;
+    nb = (n_db + rows - 1) / rows;
     if (nb < 1) nb = 1;
+    // A positive TQ_SEARCH_ROWS in the environment replaces the rows per block
+    // (rounded up to a multiple of 64, within the candidate bound above); read
+    // per call, so the workspace query and the call that follows agree.
+    if (const char* env = getenv("TQ_SEARCH_ROWS")) {
+        const long want = strtol(env, nullptr, 10);
+        if (want > 0) {
+            const int64_t r = ((int64_t)want + 63) & ~(int64_t)63;
+            const int64_t b2 = (n_db + r - 1) / r;
+            if (b2 <= max_nb) {
+                rows = r;
+                nb = b2 < 1 ? 1 : b2;
+            }
+        }
+    }
     *n_blocks = (int)nb;
     *block_rows = rows;
 }
