@@ -109,3 +109,18 @@ def test_search_full_size_sampled_queries(tq):
 def test_search_structured_residuals(tq, residual):
     check_search(tq, n_db=3000, n_q=40, d=256, bits=3, m=0, k=10, seed=7 + residual, residual=residual)
     check_search(tq, n_db=1000, n_q=17, d=128, bits=2, m=0, k=5, seed=9 + residual, residual=residual)
+
+
+def test_search_block_rows_invariance(tq, monkeypatch):
+    """The result does not depend on how the database is cut into blocks: the
+    plan's rows per block against one-tile blocks, ragged blocks and one block."""
+    db, q, S = synth.search_inputs(5000, 40, 128, 64, seed=11)
+    codec = tq.tq_codebook(3, 128, 11, 64)
+    codec_r = o.Codec(3, 128, 11, 64)
+    enc = oracle_db(db.numpy().astype(np.float64), codec_r, S.numpy().astype(np.float64))
+    base_s, base_i = gpu_search(tq, codec, q, enc, S, 10)
+    for rows in ("64", "1000", "5000"):
+        monkeypatch.setenv("TQ_SEARCH_ROWS", rows)
+        g_s, g_i = gpu_search(tq, codec, q, enc, S, 10)
+        assert np.array_equal(g_i, base_i), rows
+        assert np.array_equal(g_s, base_s), rows
