@@ -35,7 +35,12 @@ the GPU reach its sustained clock: a decode loop run straight from idle is
 timed while the clocks still ramp, which reads about 20% slower than the steady
 state a serving loop runs in.
 
+With --power the decode leg also samples board power and GFX clock (amd-smi)
+while the scan alone, and then a read-only stream, run back to back, after a
+reading of the idle board ("power" under "decode").
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs decode,encode,long,search,variants,quality]
+                       [--power]
 """
 from __future__ import annotations
 
@@ -65,6 +70,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--legs", default="decode,encode,long,search,variants,quality")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power", action="store_true",
+                    help="decode leg: board power and GFX clock (amd-smi) while the scan, and then a read-only "
+                         "stream, run back to back; idle power first")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration for --pmc runs)")
@@ -147,8 +155,67 @@ def attn_step(tq, args, ev):
     tq.tq_attn_combine(*args)
 
 
+def _smi_sample():
+    """One amd-smi reading: board power (W) and the mean GFX clock (MHz) of GPU 0."""
+    import re
+    import subprocess
+
+    r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-g", "0"], capture_output=True, text=True, timeout=20)
+    pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", r.stdout)
+    clk = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", r.stdout)]
+    return (float(pw.group(1)) if pw else None), (sum(clk) / len(clk) if clk else None)
+
+
+def power_probe(fn, seconds, torch):
+    """Runs fn(i) back to back for about `seconds` while a thread samples
+    amd-smi; the first third of the samples (clock and power ramp) is dropped.
+    fn=None samples the idle board."""
+    import threading
+    import time
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                samples.append(_smi_sample())
+            except Exception:  # noqa: BLE001 -- a failed reading is skipped
+                pass
+            time.sleep(0.25)
+
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler)
+    th.start()
+    n, t0 = 0, time.time()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    while time.time() - t0 < seconds:
+        if fn is None:
+            time.sleep(0.1)
+            continue
+        for _ in range(100):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    b.record()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    steady = samples[len(samples) // 3:]
+    pw = [p for p, _ in steady if p is not None]
+    ck = [c for _, c in steady if c is not None]
+    out = {"samples": len(steady), "power_w": sum(pw) / len(pw) if pw else None,
+           "power_w_max": max(pw) if pw else None, "gfx_mhz": sum(ck) / len(ck) if ck else None}
+    if fn is not None:
+        out["launches"] = n
+        out["ms_per_launch"] = a.elapsed_time(b) / n
+        if pw:
+            out["energy_mj_per_launch"] = out["power_w"] * out["ms_per_launch"]
+    return out
+
+
 # ------------------------------------------------------------------ decode ----
-def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
+def decode_leg(tq, torch, synth, steps, warmup, replicas=4, power=False):
     B, Hkv, g, ctx, d, kb, vb = 16, 4, 7, 32768, 128, 4, 2
     Hq = Hkv * g
     kc, vc = tq.tq_codebook(kb, d, 42), tq.tq_codebook(vb, d, 42)
@@ -239,6 +306,26 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
 
     ms_sparse = timed_loop(step_ex(sparse_opts), steps, max(warmup // 4, 1), torch)
     ms_sharp = timed_loop(step_ex(sharp_opts), steps, max(warmup // 4, 1), torch)
+
+    pwr = None
+    if power:
+        import shutil
+
+        if shutil.which("amd-smi") is None:
+            pwr = {"error": "amd-smi not found"}
+        else:
+            # idle board, the scan alone back to back over the rotating
+            # caches, and a read-only stream of 1 GiB for comparison
+            src = torch.ones((1 << 30) // 4, dtype=torch.int32, device="cuda")
+            sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+            pwr = {
+                "method": "amd-smi metric -p -c -g 0 every 0.25 s (SOCKET_POWER, mean of GFX_0..7 CLK); "
+                          "first third of each run's samples dropped",
+                "idle": power_probe(None, 3.0, torch),
+                "scan": power_probe(lambda i: tq.tq_attn_scan(*args_of(i)), 6.0, torch),
+                "stream_read_1gib": power_probe(lambda i: tq.tq_stream_read(src, sink), 6.0, torch),
+            }
+            del src
     token_heads = B * Hkv * ctx
     per_token_head = (kc.code_bytes + 2) + (vc.code_bytes + 2)  # 100 B
     cache_bytes = token_heads * per_token_head
@@ -283,6 +370,7 @@ def decode_leg(tq, torch, synth, steps, warmup, replicas=4):
             "ms_per_append": ms_append,
             "ms_per_append_and_attend": ms_append_attend,
         },
+        **({"power": pwr} if pwr is not None else {}),
     }, (kc, vc, caches[0], q)
 
 
@@ -775,7 +863,7 @@ def main():
         log("calibration copy: 3 launches, each 256 MiB read + 256 MiB written")
     if "decode" in legs:
         log("decode leg: batch 16, 28/4 heads, 32768 tokens, K4/V2")
-        res["decode"], _ = decode_leg(tq, torch, synth, args.steps, args.warmup)
+        res["decode"], _ = decode_leg(tq, torch, synth, args.steps, args.warmup, power=args.power)
         log(f"decode: {res['decode']['ms_per_step']:.3f} ms/step, {res['decode']['gbs']:.0f} GB/s")
     if "encode" in legs:
         log("encode leg")
