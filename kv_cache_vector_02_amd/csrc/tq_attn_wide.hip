@@ -67,7 +67,9 @@ __device__ __forceinline__ uint32_t field(const uint32_t* w, int bit0) {
     return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & ((1u << BITS) - 1u);
 }
 
-template <int D, int KB, int VB>
+// GR (4 or 8) query rows are computed, rows G..GR-1 with zero queries: no
+// per-row branch inside the token loops, so their loads and FMAs pipeline.
+template <int D, int KB, int VB, int GR>
 __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
     constexpr int LPV = D / 8;          // lanes of one query row in the rotation
     constexpr int RPW = 64 / LPV;       // query rows per wave pass of the rotation
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
     if (tid < 16) cent[tid] = a.kc.centroid[tid];
     else if (tid < 32) cent[tid] = a.vc.centroid[tid - 16];
     // rotated queries qr[r][i] = (scale log2(e) / d) H(D_K q_r)
-    for (int r0 = wave * RPW; r0 < G; r0 += 4 * RPW) {
+    for (int r0 = wave * RPW; r0 < GR; r0 += 4 * RPW) {
         const int r = r0 + lane / LPV, gl = lane & (LPV - 1);
         float x[8];
         if (r < G) {
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) x[e] = as_f(as_u(x[e]) ^ (((sb >> e) & 1u) << 31));
         fwht<LPV>(x, gl);
         const float qs = a.scale * kLog2eW / (float)D;
-        if (r < G) {
+        if (r < GR) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) qr[r * D + 8 * gl + e] = x[e] * qs;
         }
@@ -138,9 +140,9 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
     const int vblk = (nbv == 2 && lane >= 32) ? 1 : 0;  // norm block of this lane's value dims
     const int pbit = PBITS * lane;                      // this lane's value bits in a row
 
-    float m[kWideRows], l[kWideRows], acc[kWideRows][DPL];
+    float m[GR], l[GR], acc[GR][DPL];
 #pragma unroll
-    for (int h = 0; h < kWideRows; ++h) {
+    for (int h = 0; h < GR; ++h) {
         m[h] = -INFINITY;
         l[h] = 0.0f;
 #pragma unroll
@@ -167,9 +169,9 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
         // ---- scores (lane = token), one sum per head and norm block.  The
         // token's K row is read in groups of 32 codes (KB dwords); inside a
         // group the code fields sit at compile-time bit offsets.
-        float s0[kWideRows], s1[kWideRows];
+        float s0[GR], s1[GR];
 #pragma unroll
-        for (int h = 0; h < kWideRows; ++h) s0[h] = s1[h] = 0.0f;
+        for (int h = 0; h < GR; ++h) s0[h] = s1[h] = 0.0f;
         const uint32_t* kp = reinterpret_cast<const uint32_t*>(kcodes + (int64_t)tl * RBK);
         for (int grp = 0; grp < D / 32; ++grp) {
             uint32_t w[KB];
@@ -183,9 +185,9 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
 #pragma unroll
                 for (int u = 0; u < KB; ++u) w[u] = ld_stream1(kp + KB * grp + u);
             }
-            float part[kWideRows];
+            float part[GR];
 #pragma unroll
-            for (int h = 0; h < kWideRows; ++h) part[h] = 0.0f;
+            for (int h = 0; h < GR; ++h) part[h] = 0.0f;
             const float* qg = qr + 32 * grp;
             static_for<8>([&](auto fc) __attribute__((always_inline)) {
                 constexpr int f = decltype(fc)::value;  // four codes 4f .. 4f + 3
@@ -193,21 +195,19 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) c[k] = cent[field<KB>(w, KB * (4 * f + k))];
 #pragma unroll
-                for (int h = 0; h < kWideRows; ++h) {
-                    if (h < G) {
-                        const float4 q4 = *reinterpret_cast<const float4*>(qg + h * D + 4 * f);
-                        float ph = part[h];
-                        ph = fmaf(q4.x, c[0], ph);
-                        ph = fmaf(q4.y, c[1], ph);
-                        ph = fmaf(q4.z, c[2], ph);
-                        ph = fmaf(q4.w, c[3], ph);
-                        part[h] = ph;
-                    }
+                for (int h = 0; h < GR; ++h) {
+                    const float4 q4 = *reinterpret_cast<const float4*>(qg + h * D + 4 * f);
+                    float ph = part[h];
+                    ph = fmaf(q4.x, c[0], ph);
+                    ph = fmaf(q4.y, c[1], ph);
+                    ph = fmaf(q4.z, c[2], ph);
+                    ph = fmaf(q4.w, c[3], ph);
+                    part[h] = ph;
                 }
             });
             const bool second = grp >= D / 64;  // the group's norm block (uniform)
 #pragma unroll
-            for (int h = 0; h < kWideRows; ++h) {
+            for (int h = 0; h < GR; ++h) {
                 s0[h] += second ? 0.0f : part[h];
                 s1[h] += second ? part[h] : 0.0f;
             }
@@ -228,22 +228,20 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
             vs0 = vs1 = half_bits_to_float(vn[tl]);
         }
         // ---- online softmax per head across the wave
-        float p[kWideRows];
+        float p[GR];
 #pragma unroll
-        for (int h = 0; h < kWideRows; ++h) {
+        for (int h = 0; h < GR; ++h) {
             p[h] = 0.0f;
-            if (h < G) {
-                const float sc = valid ? fmaf(s0[h], n0, s1[h] * n1) : -INFINITY;
-                const float mn = fmaxf(m[h], wave_max64(sc));
-                if (mn != -INFINITY) {
-                    const float f = exp2f(m[h] - mn);  // 0 when m was -inf
-                    l[h] *= f;
+            const float sc = valid ? fmaf(s0[h], n0, s1[h] * n1) : -INFINITY;
+            const float mn = fmaxf(m[h], wave_max64(sc));
+            if (mn != -INFINITY) {
+                const float f = exp2f(m[h] - mn);  // 0 when m was -inf
+                l[h] *= f;
 #pragma unroll
-                    for (int e = 0; e < DPL; ++e) acc[h][e] *= f;
-                    p[h] = valid ? exp2f(sc - mn) : 0.0f;
-                    l[h] += p[h];
-                    m[h] = mn;
-                }
+                for (int e = 0; e < DPL; ++e) acc[h][e] *= f;
+                p[h] = valid ? exp2f(sc - mn) : 0.0f;
+                l[h] += p[h];
+                m[h] = mn;
             }
         }
         // ---- value sums (lane = dims), the tile's tokens in order
@@ -268,12 +266,10 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < DPL; ++e) vv[e] = cent[16 + ((bits >> (VB * e)) & ((1u << VB) - 1u))] * vsj;
 #pragma unroll
-            for (int h = 0; h < kWideRows; ++h) {
-                if (h < G) {
-                    const float pj = bcast(p[h], j);
+            for (int h = 0; h < GR; ++h) {
+                const float pj = bcast(p[h], j);
 #pragma unroll
-                    for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pj, vv[e], acc[h][e]);
-                }
+                for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(pj, vv[e], acc[h][e]);
             }
         }
         // every lane has read the tile before any lane overwrites it
@@ -286,7 +282,7 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
     // through LDS (waves 2, 3 into 0, 1; then 1 into 0), then one partial per
     // row of the block split: (max, sum, acc[D]) in the combine's layout
 #pragma unroll
-    for (int h = 0; h < kWideRows; ++h) {
+    for (int h = 0; h < GR; ++h) {
         float lh = l[h];
         lh += xor_lane<1>(lh);
         lh += xor_lane<2>(lh);
@@ -298,7 +294,7 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
     float* mrg = reinterpret_cast<float*>(smem);  // [2][kWideRows][D + 2]
     auto put = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < kWideRows; ++h) {
+        for (int h = 0; h < GR; ++h) {
             float* st = mrg + (slot * kWideRows + h) * (D + 2);
             if (lane == 0) {
                 st[0] = m[h];
@@ -310,7 +306,7 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
     };
     auto take = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < kWideRows; ++h) {
+        for (int h = 0; h < GR; ++h) {
             const float* st = mrg + (slot * kWideRows + h) * (D + 2);
             const float mo = st[0], lo = st[1];
             const float mn = fmaxf(m[h], mo);
@@ -333,7 +329,7 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
     if (wave != 0) return;
     take(0);
 #pragma unroll
-    for (int h = 0; h < kWideRows; ++h) {
+    for (int h = 0; h < GR; ++h) {
         if (h >= G) break;
         float* pr = a.part + (((int64_t)b * a.hq + row0 + h) * a.splits + split) * (D + 2);
         if (lane == 0) {
@@ -345,15 +341,22 @@ __global__ __launch_bounds__(256) void wide_kernel(AttnArgs a) {
     }
 }
 
-template <int D, int KB>
-hipError_t launch_wide_k(const AttnArgs& a, hipStream_t s) {
+template <int D, int KB, int GR>
+void launch_wide_g(const AttnArgs& a, hipStream_t s) {
     const dim3 grid(a.splits, a.hkv * a.chunks, a.batch);
     switch (a.vc.bits) {
-        case 1: hipLaunchKernelGGL((wide_kernel<D, KB, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((wide_kernel<D, KB, 2>), grid, dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((wide_kernel<D, KB, 3>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((wide_kernel<D, KB, 4>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((wide_kernel<D, KB, 1, GR>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((wide_kernel<D, KB, 2, GR>), grid, dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((wide_kernel<D, KB, 3, GR>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((wide_kernel<D, KB, 4, GR>), grid, dim3(256), 0, s, a); break;
     }
+}
+
+// rows computed per block: 4 for chunks of up to 4 query heads, else 8
+template <int D, int KB>
+hipError_t launch_wide_k(const AttnArgs& a, hipStream_t s) {
+    if (a.heads_per_chunk <= 4) launch_wide_g<D, KB, 4>(a, s);
+    else launch_wide_g<D, KB, kWideRows>(a, s);
     return hipGetLastError();
 }
 
