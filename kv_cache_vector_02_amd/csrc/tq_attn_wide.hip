@@ -1,7 +1,7 @@
-// Decode attention over caches the matrix-core scan does not serve: head
-// dimension 512 and caches with two norm blocks (one norm per half of the
+// Decode attention over caches with two norm blocks at head dimension 256,
+// which the matrix-core scan does not serve (one norm per half of the
 // rotated vector, "TurboQuant KV 캐시 압축 for llama.cpp", v1.5.2 "핵심 변경" item
-// 5; v1.5.0 and v1.5.1 for the 512-point transform).  The scan's matrix-core
+// 5).  The kernel is generic in D (256 and 512).  The scan's matrix-core
 // operations sum the dims of all four quarters of a token in one instruction,
 // so a norm per half cannot enter there; this kernel runs on the vector ALUs.
 //
@@ -372,8 +372,10 @@ hipError_t launch_wide_d(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// d = 512 runs on the matrix cores (tq_attn_wide_mc.hip); this kernel serves
+// d = 256 caches with two norm blocks
 hipError_t launch_wide(const AttnArgs& a, hipStream_t s) {
-    return a.kc.d == 512 ? launch_wide_d<512>(a, s) : launch_wide_d<256>(a, s);
+    return a.kc.d == 512 ? launch_wide_mc(a, s) : launch_wide_d<256>(a, s);
 }
 
 }  // namespace tqi

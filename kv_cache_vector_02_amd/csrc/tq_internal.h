@@ -116,6 +116,8 @@ void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int v
 bool attn_wide(int d, int k_blocks, int v_blocks);
 void wide_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t* split_tokens, int* heads_per_chunk);
 hipError_t launch_wide(const AttnArgs& a, hipStream_t s);
+// the d = 512 kernel on the matrix cores (tq_attn_wide_mc.hip)
+hipError_t launch_wide_mc(const AttnArgs& a, hipStream_t s);
 template <int D, int KB>
 hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s);
 template <int D, int KB>

@@ -234,8 +234,14 @@ def test_wide_attention_head_groups(tq, g):
     wide_case(tq, 512, 3, 3, 2, B=1, Hkv=2, g=g, cap=900, ctx_len=[777], seed=300 + g, qdtype=torch.float16)
 
 
-def test_wide_attention_split_invariance(tq, monkeypatch):
-    outs = [wide_case(tq, 512, 3, 3, 2, B=1, Hkv=1, g=8, cap=3000, ctx_len=[2999], seed=400, splits=s,
+@pytest.mark.parametrize("d,tol", [(512, 5e-4), (256, 1e-5)])
+def test_wide_attention_split_invariance(tq, monkeypatch, d, tol):
+    """Every split count matches the oracle, and the split counts agree with
+    each other to the kernels' own rounding: the d = 512 matrix-core kernel
+    forms its value weights p |v| as halves (relative rounding 2^-11 per
+    weight, and splits with different running maxima round differently); the
+    d = 256 vector-ALU kernel keeps them in float32."""
+    outs = [wide_case(tq, d, 3, 3, 2, B=1, Hkv=1, g=8, cap=3000, ctx_len=[2999], seed=400, splits=s,
                       monkeypatch=monkeypatch) for s in (1, 3, 12)]
     for o2 in outs[1:]:
-        assert parity.rel_rows(o2, outs[0]).max() <= 1e-5
+        assert parity.rel_rows(o2, outs[0]).max() <= tol
