@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float qr[kMcRows * D];
     __shared__ __attribute__((aligned(16))) float psc[2 * PB];
     __shared__ __attribute__((aligned(16))) uint32_t vst[4 * 64 * VSTR];
+    __shared__ __attribute__((aligned(16))) float nrms[4 * 128];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, grp = lane >> 4;
@@ -192,34 +193,56 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
     for (int nb = 0; nb < NB; ++nb) vacc[nb] = mf4_t{0.0f, 0.0f, 0.0f, 0.0f};
     float m = -INFINITY, l = 0.0f;  // of head hq
 
-    int par = 0;
-    for (int t0 = t_beg; t0 < t_end; t0 += 64, par ^= 1) {
-        // this lane's token's value quarter: loads out now, staged after the scores
+    // a tile's global inputs, requested one tile ahead: the lane's key codes of
+    // tokens 16 tb + n (its lane group's 32 codes), its token's value quarter
+    // and its token's norms of this wave's halves (tokens clamped to the split)
+    struct TileIn {
+        uint32_t cw[4][KB];
         uint4 vq[VB];
-        {
-            const int tv = (t0 + lane < t_end) ? t0 + lane : t_end - 1;
-            const uint4* vp = reinterpret_cast<const uint4*>(vcodes + (int64_t)tv * RBV + wave * SEGV);
-#pragma unroll
-            for (int u = 0; u < VB; ++u) vq[u] = ld_stream4(vp + u);
-        }
-        // ---- partial scores of the wave's quarter
-        float* pw = psc + par * PB + wave * kMcRows * kPStride;
+        uint32_t nk, nv;
+    };
+    auto fetch = [&](TileIn& in, int t0) __attribute__((always_inline)) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             const int tok = t0 + 16 * tb + n;
             const int tk = tok < t_end ? tok : t_end - 1;
             const uint32_t* kp = reinterpret_cast<const uint32_t*>(kcodes + (int64_t)tk * RBK) + (4 * wave + grp) * KB;
-            uint32_t cw[KB];
             if constexpr (KB == 4) {
                 const uint4 v = ld_stream4(kp);
-                cw[0] = v.x; cw[1] = v.y; cw[2] = v.z; cw[3] = v.w;
+                in.cw[tb][0] = v.x; in.cw[tb][1] = v.y; in.cw[tb][2] = v.z; in.cw[tb][3] = v.w;
             } else if constexpr (KB == 2) {
                 const uint2 v = ld_stream2(kp);
-                cw[0] = v.x; cw[1] = v.y;
+                in.cw[tb][0] = v.x; in.cw[tb][1] = v.y;
             } else {
 #pragma unroll
-                for (int u = 0; u < KB; ++u) cw[u] = ld_stream1(kp + u);
+                for (int u = 0; u < KB; ++u) in.cw[tb][u] = ld_stream1(kp + u);
             }
+        }
+        const int tv = (t0 + lane < t_end) ? t0 + lane : t_end - 1;
+        const uint4* vp = reinterpret_cast<const uint4*>(vcodes + (int64_t)tv * RBV + wave * SEGV);
+#pragma unroll
+        for (int u = 0; u < VB; ++u) in.vq[u] = ld_stream4(vp + u);
+        in.nk = kn[(int64_t)tv * nbk];
+        in.nv = vn[(int64_t)tv * nbv];
+    };
+    float* nrm = nrms + wave * 128;  // this wave's K norms [64] then V norms [64] of the tile
+
+    TileIn cur;
+    if (t_beg < t_end) fetch(cur, t_beg);
+    int par = 0;
+    for (int t0 = t_beg; t0 < t_end; t0 += 64, par ^= 1) {
+        TileIn nxt;
+        fetch(nxt, t0 + 64 < t_end ? t0 + 64 : t0);  // the next tile's loads go out now
+        // the tile's norms of this wave's halves, one token per lane (the
+        // previous tile's reads of this area are done)
+        nrm[lane] = half_bits_to_float(cur.nk) * bs_k;
+        nrm[64 + lane] = half_bits_to_float(cur.nv);
+        wave_order();
+        // ---- partial scores of the wave's quarter
+        float* pw = psc + par * PB + wave * kMcRows * kPStride;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const uint32_t* cw = cur.cw[tb];
             mf4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -230,14 +253,11 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
             }
             // column n + 8 holds the q_lo part of head n: add the two halves;
             // lanes n < 8 then hold tokens 16 tb + 4 grp + v of head n
+            const float4 nk4 = *reinterpret_cast<const float4*>(nrm + 16 * tb + 4 * grp);
+            const float nkv[4] = {nk4.x, nk4.y, nk4.z, nk4.w};
             float sv[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float s = acc[v] + xor_lane<8>(acc[v]);
-                const int t = t0 + 16 * tb + 4 * grp + v;
-                const int tc = t < t_end ? t : t_end - 1;
-                sv[v] = s * qinv * (half_bits_to_float(kn[(int64_t)tc * nbk]) * bs_k);
-            }
+            for (int v = 0; v < 4; ++v) sv[v] = (acc[v] + xor_lane<8>(acc[v])) * qinv * nkv[v];
             if (n < 8)
                 *reinterpret_cast<float4*>(pw + n * kPStride + 16 * tb + 4 * grp) = make_float4(sv[0], sv[1], sv[2], sv[3]);
         }
@@ -275,14 +295,15 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
         uint32_t wa[2][4];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
+            const float4 va = *reinterpret_cast<const float4*>(nrm + 64 + 32 * s2 + 8 * grp);
+            const float4 vb = *reinterpret_cast<const float4*>(nrm + 64 + 32 * s2 + 8 * grp + 4);
+            const float nv8[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
             float pe[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int t = t0 + 32 * s2 + 8 * grp + e;
-                const int tc = t < t_end ? t : t_end - 1;
                 const float p = live_row ? exp2f(s[s2][e] - mn) : 0.0f;  // 0 past the end (s = -inf)
                 psum += p;
-                pe[e] = p * half_bits_to_float(vn[(int64_t)tc * nbv]);
+                pe[e] = p * nv8[e];
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) wa[s2][j] = pack_halves(pe[2 * j], pe[2 * j + 1]);
@@ -304,10 +325,10 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
         // reads of this wave's area are done
 #pragma unroll
         for (int u = 0; u < VB; ++u) {
-            vs[lane * VSTR + 4 * u] = vq[u].x;
-            vs[lane * VSTR + 4 * u + 1] = vq[u].y;
-            vs[lane * VSTR + 4 * u + 2] = vq[u].z;
-            vs[lane * VSTR + 4 * u + 3] = vq[u].w;
+            vs[lane * VSTR + 4 * u] = cur.vq[u].x;
+            vs[lane * VSTR + 4 * u + 1] = cur.vq[u].y;
+            vs[lane * VSTR + 4 * u + 2] = cur.vq[u].z;
+            vs[lane * VSTR + 4 * u + 3] = cur.vq[u].w;
         }
         wave_order();
         // ---- value sums: k step s2 covers tokens 32 s2 + 8 grp + e, column n'
@@ -342,6 +363,7 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
             }
         }
         wave_order();  // every lane has read the staged quarters before the next tile
+        cur = nxt;
     }
 
     // one partial per query row of the block split: (max, sum, acc[D]); the
