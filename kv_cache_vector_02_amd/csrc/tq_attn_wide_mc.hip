@@ -184,7 +184,8 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
     const uint8_t* kcodes = a.k_codes + kvrow * RBK;
     const uint8_t* vcodes = a.v_codes + kvrow * RBV;
     const uint2* ktl = ktab + lane % KTS;
-    const uint32_t* vtl = vtab + lane % VTS;
+    constexpr int VLOG = VTS == 32 ? 7 : 5;       // log2 of the V table's row stride in bytes
+    const uint32_t vlane = (uint32_t)(lane % VTS) * 4u;  // this lane's copy in a row
     uint32_t* vs = vst + wave * 64 * VSTR;
     const bool live_row = n < 8 && hq < G;  // A rows of the value sums that carry a head
 
@@ -238,26 +239,31 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
         nrm[lane] = half_bits_to_float(cur.nk) * bs_k;
         nrm[64 + lane] = half_bits_to_float(cur.nv);
         wave_order();
-        // ---- partial scores of the wave's quarter
+        // ---- partial scores of the wave's quarter: the four 16-token blocks'
+        // matrix-core chains interleaved step by step
         float* pw = psc + par * PB + wave * kMcRows * kPStride;
+        mf4_t kacc[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) kacc[tb] = mf4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const uint2 e0 = ktl[bits_from<2 * KB>(cur.cw[tb], 4 * ks * KB) * KTS];
+                const uint2 e1 = ktl[bits_from<2 * KB>(cur.cw[tb], (4 * ks + 2) * KB) * KTS];
+                kacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_mh8(make_uint4(e0.x, e0.y, e1.x, e1.y)), bq[ks],
+                                                                 kacc[tb], 0, 0, 0);
+            }
+        }
+        // column n + 8 holds the q_lo part of head n: add the two halves; lanes
+        // n < 8 then hold tokens 16 tb + 4 grp + v of head n
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-            const uint32_t* cw = cur.cw[tb];
-            mf4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint2 e0 = ktl[bits_from<2 * KB>(cw, 4 * ks * KB) * KTS];
-                const uint2 e1 = ktl[bits_from<2 * KB>(cw, (4 * ks + 2) * KB) * KTS];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_mh8(make_uint4(e0.x, e0.y, e1.x, e1.y)), bq[ks], acc, 0,
-                                                            0, 0);
-            }
-            // column n + 8 holds the q_lo part of head n: add the two halves;
-            // lanes n < 8 then hold tokens 16 tb + 4 grp + v of head n
             const float4 nk4 = *reinterpret_cast<const float4*>(nrm + 16 * tb + 4 * grp);
             const float nkv[4] = {nk4.x, nk4.y, nk4.z, nk4.w};
             float sv[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sv[v] = (acc[v] + xor_lane<8>(acc[v])) * qinv * nkv[v];
+            for (int v = 0; v < 4; ++v) sv[v] = (kacc[tb][v] + xor_lane<8>(kacc[tb][v])) * qinv * nkv[v];
             if (n < 8)
                 *reinterpret_cast<float4*>(pw + n * kPStride + 16 * tb + 4 * grp) = make_float4(sv[0], sv[1], sv[2], sv[3]);
         }
@@ -278,19 +284,20 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
                 s[s2][4] += u1.x; s[s2][5] += u1.y; s[s2][6] += u1.z; s[s2][7] += u1.w;
             }
         }
+        const bool full = t0 + 64 <= t_end;  // uniform: no token past the split's end
         float tmax = -INFINITY;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (t0 + 32 * s2 + 8 * grp + e >= t_end) s[s2][e] = -INFINITY;
+                if (!full) s[s2][e] = (t0 + 32 * s2 + 8 * grp + e < t_end) ? s[s2][e] : -INFINITY;
                 tmax = fmaxf(tmax, s[s2][e]);
             }
         }
         tmax = fmaxf(tmax, xor_lane<16>(tmax));
         tmax = fmaxf(tmax, xor_lane<32>(tmax));
         const float mn = fmaxf(m, tmax);  // finite: the tile holds a token
-        const float f = exp2f(m - mn);    // 0 on the first tile
+        const float f = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile (m = -inf)
         float psum = 0.0f;
         uint32_t wa[2][4];
 #pragma unroll
@@ -301,7 +308,8 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
             float pe[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float p = live_row ? exp2f(s[s2][e] - mn) : 0.0f;  // 0 past the end (s = -inf)
+                // exp2 of a value <= 0 (-inf past the end gives 0)
+                const float p = live_row ? __builtin_amdgcn_exp2f(s[s2][e] - mn) : 0.0f;
                 psum += p;
                 pe[e] = p * nv8[e];
             }
@@ -312,13 +320,16 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
         psum += xor_lane<32>(psum);
         l = l * f + psum;
         m = mn;
-        // rescale the value sums: rows 4 grp + i hold head 4 grp + i (rows 8..15
-        // are unused), whose factor sits in lane 4 grp + i
+        // rescale the value sums when some head's max rose: rows 4 grp + i hold
+        // head 4 grp + i (rows 8..15 are unused), whose factor sits in lane
+        // 4 grp + i
+        if (__builtin_amdgcn_ballot_w64(f != 1.0f) != 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float fi = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * grp + i) << 2, __float_as_int(f)));
+            for (int i = 0; i < 4; ++i) {
+                const float fi = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * grp + i) << 2, __float_as_int(f)));
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) vacc[nb][i] *= fi;
+                for (int nb = 0; nb < NB; ++nb) vacc[nb][i] *= fi;
+            }
         }
 
         // ---- stage the value quarters (lane = token); the previous tile's
@@ -334,22 +345,29 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
         // ---- value sums: k step s2 covers tokens 32 s2 + 8 grp + e, column n'
         // stands for dim 8 n' + nb of the quarter
         const int bit0 = PIECE * n, wi = bit0 >> 5, sh = bit0 & 31;
+        // V pair table entry of the 2 VB bits at bit fb of a piece: the index
+        // lands on the table's row stride with one shift and one and-or
+        auto vlook = [&](uint32_t pcv, int fb) __attribute__((always_inline)) {
+            const uint32_t sl = fb <= VLOG ? (pcv << (VLOG - fb)) : (pcv >> (fb - VLOG));
+            const uint32_t off = (sl & ((VTE - 1u) << VLOG)) | vlane;
+            return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(vtab) + off);
+        };
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             uint32_t pc[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                // dword wi + 1 is at most the row's padding dword; its bits only
+                // enter when the piece crosses into it
                 const uint32_t* row = vs + (32 * s2 + 8 * grp + e) * VSTR;
-                const uint32_t lo = row[wi];
-                const uint32_t hi = (sh + PIECE > 32) ? row[wi + 1] : 0u;
-                pc[e] = sh ? __builtin_amdgcn_alignbit(hi, lo, sh) : lo;
+                pc[e] = __builtin_amdgcn_alignbit(row[wi + 1], row[wi], sh);
             }
             const mh8_t aw = as_mh8(make_uint4(wa[s2][0], wa[s2][1], wa[s2][2], wa[s2][3]));
 #pragma unroll
             for (int pp = 0; pp < NB / 2; ++pp) {
                 uint32_t ent[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ent[e] = vtl[((pc[e] >> (2 * pp * VB)) & (VTE - 1u)) * VTS];
+                for (int e = 0; e < 8; ++e) ent[e] = vlook(pc[e], 2 * pp * VB);
                 const uint4 blo = make_uint4(__builtin_amdgcn_perm(ent[1], ent[0], 0x05040100u),
                                              __builtin_amdgcn_perm(ent[3], ent[2], 0x05040100u),
                                              __builtin_amdgcn_perm(ent[5], ent[4], 0x05040100u),
