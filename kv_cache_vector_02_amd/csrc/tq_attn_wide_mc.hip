@@ -73,14 +73,21 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
     constexpr int VSTR = SEGW + 1;      // padded LDS stride of the staged quarters
     constexpr int PIECE = 8 * VB;       // bits of a lane's 8 dims of one token
     constexpr int KTE = 1 << (2 * KB), KTS = KB <= 3 ? 32 : 8;  // K pair table: entries, copies
-    constexpr int VTE = 1 << (2 * VB), VTS = VB <= 3 ? 32 : 8;  // V pair table
+    // V pair table: one copy per lane of the wave (16 at 4 bits), so the 64
+    // four-byte reads of a lookup fall on distinct banks
+    constexpr int VTE = 1 << (2 * VB), VTS = VB <= 3 ? 64 : 16;
     constexpr int PB = 4 * kMcRows * kPStride;                  // floats of one partial buffer
     static_assert(NB == 8 && KS == 8 && PIECE <= 32, "layout");
     __shared__ __attribute__((aligned(16))) uint2 ktab[KTE * KTS];   // (c_hi a, c_hi b), (c_lo a, c_lo b) of 16 c
     __shared__ __attribute__((aligned(16))) uint32_t vtab[VTE * VTS];  // (c a, c b) halves
-    __shared__ __attribute__((aligned(16))) float qr[kMcRows * D];
-    __shared__ __attribute__((aligned(16))) float psc[2 * PB];
-    __shared__ __attribute__((aligned(16))) uint32_t vst[4 * 64 * VSTR];
+    // the rotated queries are read only before the tile loop: the loop's
+    // partial scores and staged value quarters reuse their space
+    constexpr int LOOP_DW = 2 * PB + 4 * 64 * VSTR;
+    constexpr int AREA_DW = LOOP_DW > kMcRows * D ? LOOP_DW : kMcRows * D;
+    __shared__ __attribute__((aligned(16))) uint32_t area[AREA_DW];
+    float* qr = reinterpret_cast<float*>(area);
+    float* psc = reinterpret_cast<float*>(area);
+    uint32_t* vst = area + 2 * PB;
     __shared__ __attribute__((aligned(16))) float nrms[4 * 128];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -173,6 +180,7 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
             }
         }
     }
+    __syncthreads();  // every wave has its query operands: the area is the loop's now
 
     const int nbk = a.kc.norm_blocks, nbv = a.vc.norm_blocks;
     const float bs_k = nbk == 2 ? 1.41421356237309505f : 1.0f;  // sqrt(B)
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(256) void wide_mc_kernel(AttnArgs a) {
     const uint8_t* kcodes = a.k_codes + kvrow * RBK;
     const uint8_t* vcodes = a.v_codes + kvrow * RBV;
     const uint2* ktl = ktab + lane % KTS;
-    constexpr int VLOG = VTS == 32 ? 7 : 5;       // log2 of the V table's row stride in bytes
+    constexpr int VLOG = VTS == 64 ? 8 : 6;       // log2 of the V table's row stride in bytes
     const uint32_t vlane = (uint32_t)(lane % VTS) * 4u;  // this lane's copy in a row
     uint32_t* vs = vst + wave * 64 * VSTR;
     const bool live_row = n < 8 && hq < G;  // A rows of the value sums that carry a head
