@@ -565,11 +565,13 @@ def search_leg(tq, torch, synth, steps, warmup):
     bits = torch.empty(n_db, m // 8, dtype=torch.uint8, device="cuda")
     gamma = torch.empty(n_db, dtype=torch.float16, device="cuda")
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tq.tq_encode(codec, db, codes, norms, S, bits, gamma)  # first call untimed (code object load)
     a.record()
-    tq.tq_encode(codec, db, codes, norms, S, bits, gamma)
+    for _ in range(3):
+        tq.tq_encode(codec, db, codes, norms, S, bits, gamma)
     b.record()
     torch.cuda.synchronize()
-    enc_ms = a.elapsed_time(b)
+    enc_ms = a.elapsed_time(b) / 3
     del db
     ws = tq.workspace(tq.tq_search_workspace_bytes(codec, n_q, n_db, k))
     scores = torch.empty(n_q, k, device="cuda")

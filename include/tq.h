@@ -173,8 +173,8 @@ int tq_codebook_opts(int bits, int d, uint64_t seed, int residual, int qjl_m, in
  *   codes          row i at codes + i*code_row_stride; code_row_stride >= d*bits/8,
  *                  multiple of 4; codes 4-byte aligned.
  *   norms_f16      [n] halves.
- *   qjl_S          [m][d] float32 row-major (N(0,1) draws made by the caller)
- *                  for TQ_RES_QJL; NULL (unused) for the other kinds.
+ *   qjl_S          [m][d] float32 row-major, 16-byte aligned (N(0,1) draws made by
+ *                  the caller) for TQ_RES_QJL; NULL (unused) for the other kinds.
  *   qjl_bits       [n][m/8] bytes, 4-byte aligned; NULL when m = 0.
  *   qjl_gamma_f16  [n] halves; NULL when m = 0.
  * n = 0 is valid and launches nothing.  Vectors whose squared norm underflows

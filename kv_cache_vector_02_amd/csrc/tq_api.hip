@@ -298,7 +298,7 @@ static int encode_setup(const tq_codec* c, const void* x, int x_dtype, int64_t n
         if (code_row_stride < c->d * c->bits / 8 || code_row_stride % 4 != 0) return TQ_EINVAL;
         if (c->qjl_m > 0) {
             if (!qjl_bits || !qjl_gamma_f16 || !aligned(qjl_bits, 4) || !aligned(qjl_gamma_f16, 2)) return TQ_EINVAL;
-            if (needs_S(c) && (!qjl_S || !aligned(qjl_S, 4))) return TQ_EINVAL;
+            if (needs_S(c) && (!qjl_S || !aligned(qjl_S, 16))) return TQ_EINVAL;
         }
     }
     tqi::fill_codec_args(c, &a->c);

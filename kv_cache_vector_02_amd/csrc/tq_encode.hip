@@ -347,15 +347,24 @@ __global__ __launch_bounds__(256) void encode_pair_kernel(EncodeArgs k, EncodeAr
 
 // QJL variant: a block of 256 threads encodes a tile of 32 vectors.
 constexpr int QJL_TILE = 32;
-constexpr int QJL_ICHUNK = 16;
+
+typedef _Float16 sh8v_t __attribute__((ext_vector_type(8)));
+typedef float sf4v_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ sh8v_t as_sh8v(uint4 u) { return __builtin_bit_cast(sh8v_t, u); }
+__device__ __forceinline__ uint32_t pack_h2f(float a, float b) {
+    const _Float16 x = (_Float16)a, y = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
 
 template <int D, int BITS, int DT>
 __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
     constexpr int LPV = D / 8;
     constexpr int VPW = 64 / LPV;
     constexpr int RS = D + 1;  // padded row of r in LDS
+    constexpr int KS = D / 16;  // projection k steps (16 dims each)
     __shared__ float r_lds[QJL_TILE * RS];
-    __shared__ float s_lds[QJL_ICHUNK * 256];
+    // S operands of two projection blocks (double buffer): [block][ks][lane]
+    __shared__ __attribute__((aligned(16))) uint4 sa[2 * KS * 64];
     __shared__ float cent[16];
 
     const int tid = threadIdx.x;
@@ -397,56 +406,90 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
             }
         }
         __syncthreads();
-        // phase 2: U = R S^T, thread (tv, tj): vectors tv + 8*vv, projections tj + 32*jj
-        const int tv = tid >> 5, tj = tid & 31;
-        float acc[4][8];
+        // phase 2: U = R S^T on the matrix cores (v_mfma_f32_16x16x32_f16), 16
+        // projections x 8 vectors per step with the hi/lo fold of the decode
+        // scan: lane (n, grp) holds in its k slots dims 16 ks + 4 grp + [0, 4)
+        // as (s_hi, s_hi, s_lo, s_lo) pairs of projection 16 jb + n (A), and
+        // columns 0-7 / 8-15 hold r_hi / r_lo of the wave's 8 vectors (B, zero
+        // on the s_lo slots); D[j][v] + D[j][v + 8] is (S r)_j without the
+        // s_lo r_lo term (below 2^-21 of the sum of |s_i r_i|).  S is scaled by
+        // 16 and r by 2^15 (|r_i| < 1), so every lo part is a normal half; the
+        // signs do not depend on the scale.  The blocks' S operands are built
+        // once per block into LDS, the next block's while this one's run.
+        const int n = lane & 15, grp = lane >> 4;
+        const int vv = 8 * wave + (n & 7);  // this lane's vector of the tile (B columns)
+        const bool lo_col = n >= 8;
+        sh8v_t bq[KS];
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv)
+        for (int ks = 0; ks < KS; ++ks) {
+            float x[4];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) acc[vv][jj] = 0.0f;
-        const int nj = m >> 5;
-        for (int i0 = 0; i0 < D; i0 += QJL_ICHUNK) {
-            // stage S[:, i0:i0+16] transposed: s_lds[ii][j]
-            for (int e = tid; e < QJL_ICHUNK * m; e += 256) {
-                const int j = e / QJL_ICHUNK, ii = e % QJL_ICHUNK;
-                s_lds[ii * 256 + j] = a.S[(int64_t)j * D + i0 + ii];
+            for (int i = 0; i < 4; ++i) {
+                const float v = r_lds[vv * RS + 16 * ks + 4 * grp + i] * 32768.0f;
+                const float h = (float)(_Float16)v;
+                x[i] = lo_col ? v - h : h;
             }
-            __syncthreads();
-#pragma unroll 4
-            for (int ii = 0; ii < QJL_ICHUNK; ++ii) {
-                float rv[4];
-#pragma unroll
-                for (int vv = 0; vv < 4; ++vv) rv[vv] = r_lds[(tv + 8 * vv) * RS + i0 + ii];
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    if (jj < nj) {
-                        const float sv = s_lds[ii * 256 + tj + 32 * jj];
-#pragma unroll
-                        for (int vv = 0; vv < 4; ++vv) acc[vv][jj] = fmaf(rv[vv], sv, acc[vv][jj]);
-                    }
-                }
-            }
-            __syncthreads();
+            bq[ks] = lo_col ? as_sh8v(make_uint4(pack_h2f(x[0], x[1]), 0u, pack_h2f(x[2], x[3]), 0u))
+                            : as_sh8v(make_uint4(pack_h2f(x[0], x[1]), pack_h2f(x[0], x[1]), pack_h2f(x[2], x[3]),
+                                                 pack_h2f(x[2], x[3])));
         }
-        // sign bits: one ballot per (vector, 32 projections); lanes 0..31 and
-        // 32..63 of a wave hold two different vectors.
+        constexpr int NE = KS * 64;              // S operands of one projection block
+        constexpr int BPT = (NE + 255) / 256;    // ... each thread builds
+        const int jbs = m >> 4;             // projection blocks
+        float4 sv[BPT];
+        auto s_load = [&](int jb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-            const int vloc = tv + 8 * vv;
-            const int64_t row = tile0 + vloc;
-            bool keep = true;
-            const int64_t orow = row < a.n ? out_row(a, row, keep) : 0;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                if (jj < nj) {
-                    const uint64_t mask = __ballot(acc[vv][jj] >= 0.0f);
-                    const uint32_t word = (lane < 32) ? (uint32_t)mask : (uint32_t)(mask >> 32);
-                    if ((lane & 31) == 0 && row < a.n && keep)
-                        reinterpret_cast<uint32_t*>(a.qjl + orow * (m >> 3))[jj] = word;
-                }
+            for (int u = 0; u < BPT; ++u) {
+                const int e = tid + 256 * u, ks = e >> 6, l = e & 63;
+                if (NE % 256 == 0 || e < NE)
+                    sv[u] = *reinterpret_cast<const float4*>(a.S + (int64_t)(16 * jb + (l & 15)) * D + 16 * ks +
+                                                             4 * (l >> 4));
             }
-        }
+        };
+        auto s_store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < BPT; ++u) {
+                if (!(NE % 256 == 0 || tid + 256 * u < NE)) continue;
+                const float x[4] = {16.0f * sv[u].x, 16.0f * sv[u].y, 16.0f * sv[u].z, 16.0f * sv[u].w};
+                float h[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) h[i] = (float)(_Float16)x[i];
+                sa[buf * KS * 64 + tid + 256 * u] = make_uint4(pack_h2f(h[0], h[1]), pack_h2f(x[0] - h[0], x[1] - h[1]),
+                                                               pack_h2f(h[2], h[3]), pack_h2f(x[2] - h[2], x[3] - h[3]));
+            }
+        };
+        // this lane's output row (lanes n < 8 of lane group 0 write their vector's signs)
+        bool keep = true;
+        const int64_t vrow = tile0 + vv;
+        const int64_t orow = vrow < a.n ? out_row(a, vrow, keep) : 0;
+        const bool writer = n < 8 && grp == 0 && vrow < a.n && keep;
+        uint32_t* qrow = reinterpret_cast<uint32_t*>(a.qjl + orow * (m >> 3));
+        s_load(0);
+        s_store(0);
         __syncthreads();
+        uint32_t word = 0;
+        for (int jb = 0; jb < jbs; ++jb) {
+            const int cur = jb & 1;
+            if (jb + 1 < jbs) s_load(jb + 1);  // uniform; the loads run under the matrix-core steps
+            const uint4* sc = sa + cur * KS * 64 + lane;
+            sf4v_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_sh8v(sc[ks * 64]), bq[ks], acc, 0, 0, 0);
+            // lanes n < 8: projections 16 jb + 4 grp + i of vector vv; bit = [u >= 0]
+            uint32_t f = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f |= ((acc[i] + xor_lane<8>(acc[i])) >= 0.0f ? 1u : 0u) << i;
+            f |= xor_lane_u<16>(f) << 4;  // lane group 0 gathers the 16 projections
+            f |= xor_lane_u<32>(f) << 8;
+            word |= (f & 0xFFFFu) << (16 * (jb & 1));
+            if (jb & 1) {
+                if (writer) qrow[jb >> 1] = word;
+                word = 0;
+            }
+            if (jb + 1 < jbs) s_store(cur ^ 1);
+            __syncthreads();  // the next block's operands are in; this block's are free
+        }
     }
 }
 
