@@ -345,8 +345,8 @@ __global__ __launch_bounds__(256) void encode_pair_kernel(EncodeArgs k, EncodeAr
     else run(v, (int64_t)blockIdx.x - kblocks, (int64_t)gridDim.x - kblocks);
 }
 
-// QJL variant: a block of 256 threads encodes a tile of 32 vectors.
-constexpr int QJL_TILE = 32;
+// QJL variant: a block of 256 threads encodes a tile of 64 vectors.
+constexpr int QJL_TILE = 64;
 
 typedef _Float16 sh8v_t __attribute__((ext_vector_type(8)));
 typedef float sf4v_t __attribute__((ext_vector_type(4)));
@@ -362,9 +362,13 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
     constexpr int VPW = 64 / LPV;
     constexpr int RS = D + 1;  // padded row of r in LDS
     constexpr int KS = D / 16;  // projection k steps (16 dims each)
-    __shared__ float r_lds[QJL_TILE * RS];
-    // S operands of two projection blocks (double buffer): [block][ks][lane]
-    __shared__ __attribute__((aligned(16))) uint4 sa[2 * KS * 64];
+    // the tile's residuals r (phase 1), then, once every wave holds its
+    // operands, the S operands of two projection blocks (double buffer:
+    // [block][ks][lane])
+    constexpr int R_U4 = (QJL_TILE * RS + 3) / 4, SA_U4 = 2 * KS * 64;
+    __shared__ __attribute__((aligned(16))) uint4 qarea[R_U4 > SA_U4 ? R_U4 : SA_U4];
+    float* r_lds = reinterpret_cast<float*>(qarea);
+    uint4* sa = qarea;
     __shared__ float cent[16];
 
     const int tid = threadIdx.x;
@@ -410,29 +414,35 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
         // projections x 8 vectors per step with the hi/lo fold of the decode
         // scan: lane (n, grp) holds in its k slots dims 16 ks + 4 grp + [0, 4)
         // as (s_hi, s_hi, s_lo, s_lo) pairs of projection 16 jb + n (A), and
-        // columns 0-7 / 8-15 hold r_hi / r_lo of the wave's 8 vectors (B, zero
-        // on the s_lo slots); D[j][v] + D[j][v + 8] is (S r)_j without the
-        // s_lo r_lo term (below 2^-21 of the sum of |s_i r_i|).  S is scaled by
-        // 16 and r by 2^15 (|r_i| < 1), so every lo part is a normal half; the
-        // signs do not depend on the scale.  The blocks' S operands are built
-        // once per block into LDS, the next block's while this one's run.
+        // columns 0-7 / 8-15 hold r_hi / r_lo of 8 vectors (B, zero on the
+        // s_lo slots); D[j][v] + D[j][v + 8] is (S r)_j without the s_lo r_lo
+        // term (below 2^-21 of the sum of |s_i r_i|).  S is scaled by 16 and r
+        // by 2^15 (|r_i| < 1), so every lo part is a normal half; the signs do
+        // not depend on the scale.  A wave takes 16 vectors as two column sets,
+        // so each S operand read from LDS feeds two steps.  The projection
+        // blocks' S operands are built once per block into LDS, the next
+        // block's while this one's run.
         const int n = lane & 15, grp = lane >> 4;
-        const int vv = 8 * wave + (n & 7);  // this lane's vector of the tile (B columns)
         const bool lo_col = n >= 8;
-        sh8v_t bq[KS];
+        sh8v_t bq[2][KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            float x[4];
+        for (int c = 0; c < 2; ++c) {
+            const int vv = 16 * wave + 8 * c + (n & 7);  // column set c's vector of the tile
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = r_lds[vv * RS + 16 * ks + 4 * grp + i] * 32768.0f;
-                const float h = (float)(_Float16)v;
-                x[i] = lo_col ? v - h : h;
+            for (int ks = 0; ks < KS; ++ks) {
+                float x[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = r_lds[vv * RS + 16 * ks + 4 * grp + i] * 32768.0f;
+                    const float h = (float)(_Float16)v;
+                    x[i] = lo_col ? v - h : h;
+                }
+                bq[c][ks] = lo_col ? as_sh8v(make_uint4(pack_h2f(x[0], x[1]), 0u, pack_h2f(x[2], x[3]), 0u))
+                                   : as_sh8v(make_uint4(pack_h2f(x[0], x[1]), pack_h2f(x[0], x[1]),
+                                                        pack_h2f(x[2], x[3]), pack_h2f(x[2], x[3])));
             }
-            bq[ks] = lo_col ? as_sh8v(make_uint4(pack_h2f(x[0], x[1]), 0u, pack_h2f(x[2], x[3]), 0u))
-                            : as_sh8v(make_uint4(pack_h2f(x[0], x[1]), pack_h2f(x[0], x[1]), pack_h2f(x[2], x[3]),
-                                                 pack_h2f(x[2], x[3])));
         }
+        __syncthreads();  // every wave holds its operands: r's space takes the S operands
         constexpr int NE = KS * 64;              // S operands of one projection block
         constexpr int BPT = (NE + 255) / 256;    // ... each thread builds
         const int jbs = m >> 4;             // projection blocks
@@ -458,34 +468,46 @@ __global__ __launch_bounds__(256) void encode_qjl_kernel(EncodeArgs a) {
                                                                pack_h2f(h[2], h[3]), pack_h2f(x[2] - h[2], x[3] - h[3]));
             }
         };
-        // this lane's output row (lanes n < 8 of lane group 0 write their vector's signs)
-        bool keep = true;
-        const int64_t vrow = tile0 + vv;
-        const int64_t orow = vrow < a.n ? out_row(a, vrow, keep) : 0;
-        const bool writer = n < 8 && grp == 0 && vrow < a.n && keep;
-        uint32_t* qrow = reinterpret_cast<uint32_t*>(a.qjl + orow * (m >> 3));
+        // the output rows of this lane's two vectors (lanes n < 8 of lane
+        // group 0 write their vectors' signs)
+        bool writer[2];
+        uint32_t* qrow[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            bool keep = true;
+            const int64_t vrow = tile0 + 16 * wave + 8 * c + (n & 7);
+            const int64_t orow = vrow < a.n ? out_row(a, vrow, keep) : 0;
+            writer[c] = n < 8 && grp == 0 && vrow < a.n && keep;
+            qrow[c] = reinterpret_cast<uint32_t*>(a.qjl + orow * (m >> 3));
+        }
         s_load(0);
         s_store(0);
         __syncthreads();
-        uint32_t word = 0;
+        uint32_t word[2] = {0u, 0u};
         for (int jb = 0; jb < jbs; ++jb) {
             const int cur = jb & 1;
             if (jb + 1 < jbs) s_load(jb + 1);  // uniform; the loads run under the matrix-core steps
             const uint4* sc = sa + cur * KS * 64 + lane;
-            sf4v_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            sf4v_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_sh8v(sc[ks * 64]), bq[ks], acc, 0, 0, 0);
-            // lanes n < 8: projections 16 jb + 4 grp + i of vector vv; bit = [u >= 0]
-            uint32_t f = 0;
+            for (int ks = 0; ks < KS; ++ks) {
+                const sh8v_t sop = as_sh8v(sc[ks * 64]);
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sop, bq[0][ks], acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sop, bq[1][ks], acc[1], 0, 0, 0);
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) f |= ((acc[i] + xor_lane<8>(acc[i])) >= 0.0f ? 1u : 0u) << i;
-            f |= xor_lane_u<16>(f) << 4;  // lane group 0 gathers the 16 projections
-            f |= xor_lane_u<32>(f) << 8;
-            word |= (f & 0xFFFFu) << (16 * (jb & 1));
-            if (jb & 1) {
-                if (writer) qrow[jb >> 1] = word;
-                word = 0;
+            for (int c = 0; c < 2; ++c) {
+                // lanes n < 8: projections 16 jb + 4 grp + i of the set's vector; bit = [u >= 0]
+                uint32_t f = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) f |= ((acc[c][i] + xor_lane<8>(acc[c][i])) >= 0.0f ? 1u : 0u) << i;
+                f |= xor_lane_u<16>(f) << 4;  // lane group 0 gathers the 16 projections
+                f |= xor_lane_u<32>(f) << 8;
+                word[c] |= (f & 0xFFFFu) << (16 * (jb & 1));
+                if (jb & 1) {
+                    if (writer[c]) qrow[c][jb >> 1] = word[c];
+                    word[c] = 0;
+                }
             }
             if (jb + 1 < jbs) s_store(cur ^ 1);
             __syncthreads();  // the next block's operands are in; this block's are free
