@@ -1,0 +1,77 @@
+"""tq_encode / tq_encode_kv captured in a HIP graph: every replay, with the
+program's own eager work and synchronisations between replays, writes the
+bytes that eager calls write on the same inputs."""
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_vector_02_amd as lib
+    return lib
+
+
+def _planes(codec, n, layers):
+    return {"codes": torch.full((layers, n, codec.d * codec.bits // 8), 0xA5, dtype=torch.uint8, device="cuda"),
+            "norms": torch.zeros(layers, n, dtype=torch.float16, device="cuda")}
+
+
+@pytest.mark.parametrize("kbits,vbits,n", [(4, 2, 8192), (3, 3, 1000)])
+def test_encode_graph_replays_match_eager(tq, kbits, vbits, n):
+    d, layers = 128, 4
+    kc, vc = tq.tq_codebook(kbits, d, 5), tq.tq_codebook(vbits, d, 5)
+    k_in = torch.empty(layers, n, d, dtype=torch.float16, device="cuda")
+    v_in = torch.empty_like(k_in)
+    gk, gv = _planes(kc, n, layers), _planes(vc, n, layers)  # the graph's outputs
+    ek, ev = _planes(kc, n, layers), _planes(vc, n, layers)  # eager outputs
+    two_k, two_v = _planes(kc, n, layers), _planes(vc, n, layers)  # the graph's two-call outputs
+
+    def fill(seed):
+        for li in range(layers):
+            k, v = synth.kv_block(1, n, d, seed=seed * 16 + li, dtype=torch.float16)
+            k_in[li].copy_(k[0])
+            v_in[li].copy_(v[0])
+
+    def run(pk, pv, fused):
+        for li in range(layers):
+            if fused:
+                tq.tq_encode_kv(kc, vc, k_in[li], v_in[li], pk["codes"][li], pk["norms"][li],
+                                pv["codes"][li], pv["norms"][li])
+            else:
+                tq.tq_encode(kc, k_in[li], pk["codes"][li], pk["norms"][li])
+                tq.tq_encode(vc, v_in[li], pv["codes"][li], pv["norms"][li])
+
+    fill(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm the library (plans, codebook upload) outside capture
+        run(gk, gv, True)
+        run(two_k, two_v, False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(gk, gv, True)
+        run(two_k, two_v, False)
+
+    for rep in range(4):
+        fill(rep + 1)  # eager work between replays: new inputs, poisoned outputs
+        for p in (gk, gv, two_k, two_v):
+            p["codes"].fill_(0xA5)
+            p["norms"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        run(ek, ev, True)
+        torch.cuda.synchronize()
+        for got_k, got_v in ((gk, gv), (two_k, two_v)):
+            for got, want in ((got_k, ek), (got_v, ev)):
+                for key in ("codes", "norms"):
+                    assert torch.equal(got[key].view(torch.uint8), want[key].view(torch.uint8)), (rep, key)
+    del g
