@@ -204,14 +204,16 @@ constexpr bool split_fits(int d, int kb, int vb, bool qjl, int nw) {
     return split_tab_bytes(kb, vb) + 4 * (nw * wave_dw(d, vb) + qjl_dw(qjl)) <= kLdsBytes;
 }
 // Waves of one split block (the block owns a compute unit: one resident block
-// per CU, its waves sharing the tables): split tables with the most waves that
-// fit (12 or 8 at d = 128, 8 at d = 256), else the shared table.  The QJL
-// variant, whose extra operands already press on the registers, keeps the
-// shared table.
+// per CU, its waves sharing the tables): 8 up to d = 128 (two waves per SIMD,
+// 256 registers each), 4 at d = 256 (one wave per SIMD: the twice longer query
+// operands and V sums need up to 512 registers).  Every variant then compiles
+// without register spills; with 12 waves (168 registers) most d = 128 variants
+// spilled and ran up to 1.7x slower, with 8 waves at d = 256 up to 2.3x.  The
+// split tables are used where they fit beside the wave areas, else the shared
+// table; the QJL variant, whose extra operands take LDS, keeps the shared one.
 constexpr int split_waves(int d, int kb, int vb, bool qjl) {
-    if (!qjl && d == 128 && split_fits(d, kb, vb, qjl, 12)) return 12;
-    if (!qjl && split_fits(d, kb, vb, qjl, 8)) return 8;
-    return d == 128 ? 12 : 8;
+    (void)kb, (void)vb, (void)qjl;
+    return d >= 256 ? 4 : 8;
 }
 constexpr bool split_tables(int d, int kb, int vb, bool qjl) {
     return !qjl && split_fits(d, kb, vb, qjl, split_waves(d, kb, vb, qjl));
@@ -385,8 +387,8 @@ __device__ __forceinline__ int64_t query_row(const AttnArgs& a, int b, int kvh, 
 // One instance per (D, KB, VB, QJL) and switch set: SPARSE = the sparse-V
 // switch, MQ = more than one query column, G8 = eight query rows per block.
 // Other row counts G (< 8) are a runtime value (the matrix-core columns are
-// fixed at 8 rows); the full block gets its own instance because a
-// compile-time G keeps the 12-wave variants free of register spills.
+// fixed at 8 rows); the full block gets its own instance, whose compile-time G
+// drops the per-row checks.
 template <int D, int KB, int VB, bool QJL, bool SPARSE, bool MQ, bool G8>
 __global__ __launch_bounds__(64 * split_waves(D, KB, VB, QJL))
 __attribute__((amdgpu_waves_per_eu(split_waves(D, KB, VB, QJL) / 4)))
