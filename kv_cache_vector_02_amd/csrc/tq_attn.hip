@@ -55,8 +55,9 @@ int device_cus() {
 }
 
 // The query rows of one kv head (g heads in each of the ncols query columns,
-// gv = g * ncols rows) are processed in chunks of G <= 8 rows (the largest
-// divisor of gv not above 8).  The context is cut into splits of a
+// gv = g * ncols rows) are processed in chunks of G rows, the largest divisor
+// of gv not above 16 where the scan has 16-row blocks (no QJL, d <= 128), else
+// not above 8.  The context is cut into splits of a
 // multiple of 64 tokens.  With S resident block slots on the device (compute
 // units x blocks per unit for this variant), a grid of B blocks runs in
 // ceil(B / S) rounds and a block costs about (tiles per wave + 2) tile times
@@ -66,7 +67,7 @@ int device_cus() {
 void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int vb, bool qjl, int* splits,
                int64_t* split_tokens, int* heads_per_chunk) {
     int G = 1;
-    for (int c = 8; c >= 1; --c) {
+    for (int c = attn::split_rows16(d, qjl) ? 16 : 8; c >= 1; --c) {
         if (gv % c == 0) {
             G = c;
             break;
@@ -114,7 +115,7 @@ void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int v
 
 bool attn_wide(int d, int k_blocks, int v_blocks) { return d == 512 || k_blocks != 1 || v_blocks != 1; }
 
-// Plan of the vector-ALU kernel: query rows in chunks of G <= 8 as above;
+// Plan of the wide kernels: query rows in chunks of G <= 8 (the largest divisor of g);
 // splits of a multiple of 256 tokens (4 waves x 64), as many as give about two
 // blocks per compute unit (its registers and LDS hold two).
 void wide_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t* split_tokens, int* heads_per_chunk) {

@@ -218,10 +218,13 @@ constexpr int split_waves(int d, int kb, int vb, bool qjl) {
 constexpr bool split_tables(int d, int kb, int vb, bool qjl) {
     return !qjl && split_fits(d, kb, vb, qjl, split_waves(d, kb, vb, qjl));
 }
+// Blocks of up to 16 query rows (see split_kernel): without QJL and up to
+// d = 128, where the 16 rotated query rows fit the wave areas.
+constexpr bool split_rows16(int d, bool qjl) { return !qjl && d <= 128; }
 
 template <int D, int KB, int VB, bool QJL>
 struct Cfg {
-    static constexpr int GMAX = 8;                  // query rows per block (at most)
+    static constexpr int GMAX = split_rows16(D, QJL) ? 16 : 8;  // query rows per block (at most)
     static constexpr int NW = split_waves(D, KB, VB, QJL);  // waves per block
     static constexpr int NT = 64 * NW;              // threads per block
     // K side
@@ -385,16 +388,24 @@ __device__ __forceinline__ int64_t query_row(const AttnArgs& a, int b, int kvh, 
 }
 
 // One instance per (D, KB, VB, QJL) and switch set: SPARSE = the sparse-V
-// switch, MQ = more than one query column, G8 = eight query rows per block.
-// Other row counts G (< 8) are a runtime value (the matrix-core columns are
-// fixed at 8 rows); the full block gets its own instance, whose compile-time G
-// drops the per-row checks.
-template <int D, int KB, int VB, bool QJL, bool SPARSE, bool MQ, bool G8>
+// switch, MQ = more than one query column, GM = the row mode of the block:
+//   GM = 8: eight query rows;
+//   GM = 0: G < 8 rows (a runtime value).  In both, the 16 matrix-core
+//           columns of a K step hold q_hi (columns 0..7) and q_lo (8..15) of
+//           the same 8 rows, folded after the scores;
+//   GM = 16: 9 to 16 rows (runtime G), one row per column: each K step runs
+//           twice on the same looked-up operands, once against q_hi and once
+//           against q_lo, into the same scores, so the lookups, softmax and V
+//           sums of a tile serve twice the rows for 1.67x the matrix-core
+//           work (2 x 32 K steps + 16 V steps against 32 + 16 per 8 rows).
+template <int D, int KB, int VB, bool QJL, bool SPARSE, bool MQ, int GM>
 __global__ __launch_bounds__(64 * split_waves(D, KB, VB, QJL))
 __attribute__((amdgpu_waves_per_eu(split_waves(D, KB, VB, QJL) / 4)))
 void split_kernel(AttnArgs a) {
     using C = Cfg<D, KB, VB, QJL>;
-    const int G = G8 ? 8 : a.heads_per_chunk;
+    constexpr bool R16 = GM == 16;
+    static_assert(!R16 || split_rows16(D, QJL), "16-row blocks need d <= 128 and no QJL");
+    const int G = GM == 8 ? 8 : a.heads_per_chunk;
     __shared__ __attribute__((aligned(16))) uint32_t smem[C::SMEM_DW];
     uint8_t* tab = reinterpret_cast<uint8_t*>(smem);
     uint32_t* waves_lds = smem + C::TABB / 4;
@@ -532,11 +543,13 @@ void split_kernel(AttnArgs a) {
     // K-side B operands: column n holds q_hi (n < 8) or q_lo (n >= 8) of head
     // n % 8 (zero beyond G), all heads scaled by one power of two, with the dims
     // of K step ks in the order of the A entries (KE = 2: d0 d1 d0 d1 d2 d3 d2 d3;
-    // KE = 4: d0 d1 d2 d3 d0 d1 d2 d3); likewise the QJL projection
-    const int hh = n & 7;
-    const bool lo_col = n >= 8, head_ok = hh < G;
+    // KE = 4: d0 d1 d2 d3 d0 d1 d2 d3); likewise the QJL projection.  With 16
+    // rows, column n is head n: q_hi in bq, q_lo in bql.
+    const int hh = R16 ? n : (n & 7);
+    const bool lo_col = !R16 && n >= 8, head_ok = hh < G;
     const int ctx_row = MQ ? ctx - (a.ncols - 1 - (vl0 + hh) / a.g) : ctx;  // tokens row hh may see
     half8_t bq[C::KSTEPS];
+    half8_t bql[R16 ? C::KSTEPS : 1];
     float qinv;
     {
         float qv[C::KSTEPS][4];
@@ -566,20 +579,23 @@ void split_kernel(AttnArgs a) {
         qinv = 1.0f / (16.0f * sc);
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            _Float16 x[4];
+            _Float16 x[4], xl[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float v = qv[ks][i] * sc;
                 const _Float16 hi = (_Float16)v;
-                x[i] = lo_col ? (_Float16)(v - (float)hi) : hi;
+                xl[i] = (_Float16)(v - (float)hi);
+                x[i] = lo_col ? xl[i] : hi;
             }
 #pragma unroll
-            // the q_lo columns are zero on the c_lo slots: the c_lo * q_lo product
+            // the q_lo operands are zero on the c_lo slots: the c_lo * q_lo product
             // (below 2^-22 of the score) is left out, and zero operands cost the
             // matrix cores less energy
             for (int e = 0; e < 8; ++e) {
                 const bool lo_slot = C::KE == 2 ? (e & 2) != 0 : (e & 4) != 0;
-                bq[ks][e] = (lo_col && lo_slot) ? (_Float16)0.0f : (C::KE == 2 ? x[(e >> 2) * 2 + (e & 1)] : x[e & 3]);
+                const int di = C::KE == 2 ? (e >> 2) * 2 + (e & 1) : e & 3;
+                bq[ks][e] = (lo_col && lo_slot) ? (_Float16)0.0f : x[di];
+                if constexpr (R16) bql[ks][e] = lo_slot ? (_Float16)0.0f : xl[di];
             }
         }
         if constexpr (QJL) {
@@ -679,8 +695,9 @@ void split_kernel(AttnArgs a) {
             constexpr int s = decltype(sc)::value, j = s / C::KSTEPS, ks = s % C::KSTEPS;
             if constexpr (s + kKLookahead < NS) look(std::integral_constant<int, s + kKLookahead>{});
             __builtin_amdgcn_sched_barrier(0);
-            sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(make_uint4(aw[s][0], aw[s][1], aw[s][2], aw[s][3])),
-                                                             bq[ks], sacc[j], 0, 0, 0);
+            const half8_t ak = as_half8(make_uint4(aw[s][0], aw[s][1], aw[s][2], aw[s][3]));
+            sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bq[ks], sacc[j], 0, 0, 0);
+            if constexpr (R16) sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bql[ks], sacc[j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr (!KDB) fetch_k<C>(rk[cur], kcodes, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
@@ -699,10 +716,12 @@ void split_kernel(AttnArgs a) {
             }
         }
         // column h + 8 holds the q_lo part of head h: add the two halves of each row
+        if constexpr (!R16) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sacc[j][v] += xor_lane<8>(sacc[j][v]);
+                for (int v = 0; v < 4; ++v) sacc[j][v] += xor_lane<8>(sacc[j][v]);
+        }
     };
     // scores of tile t0 relative to the reference max, the rare rescale, and the
     // V-side A operands: half weights p * |v| * 2^wsh (K order: sub-tile pairs
@@ -820,8 +839,9 @@ void split_kernel(AttnArgs a) {
                 wa[j >> 1][2 * (j & 1) + 1] &= k1;
             }
         }
-        // rows of heads >= G and the repeated rows 8..15 carry zero weights (they
-        // are never read; zero operands cost the matrix cores less energy)
+        // rows of heads >= G (with G <= 8 also the repeated rows 8..15) carry
+        // zero weights (they are never read; zero operands cost the matrix
+        // cores less energy)
         if (n >= G) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
@@ -1237,25 +1257,31 @@ __global__ __launch_bounds__(256) void window_kernel(AttnArgs a) {
     combine_head<D>(a, bh, gl, tg == 0, m, l, y);
 }
 
-template <int D, int KB, int VB, bool QJL, bool G8>
+template <int D, int KB, int VB, bool QJL, int GM>
 void launch_split_g(const AttnArgs& a, hipStream_t s) {
     const dim3 grid(a.splits, a.hkv * a.chunks, a.batch);
     const dim3 block(64 * split_waves(D, KB, VB, QJL));
     const bool sparse = a.sparse_log2 > -INFINITY, mq = a.ncols > 1;
     if (sparse && mq)
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, true, true, G8>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, true, true, GM>), grid, block, 0, s, a);
     else if (sparse)
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, true, false, G8>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, true, false, GM>), grid, block, 0, s, a);
     else if (mq)
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, false, true, G8>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, false, true, GM>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, false, false, G8>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, false, false, GM>), grid, block, 0, s, a);
 }
 
 template <int D, int KB, int VB, bool QJL>
 hipError_t launch_split_q(const AttnArgs& a, hipStream_t s) {
-    if (a.heads_per_chunk == 8) launch_split_g<D, KB, VB, QJL, true>(a, s);
-    else launch_split_g<D, KB, VB, QJL, false>(a, s);
+    if (a.heads_per_chunk > 8) {
+        if constexpr (split_rows16(D, QJL)) launch_split_g<D, KB, VB, QJL, 16>(a, s);
+        else return hipErrorInvalidValue;  // the plan gives such chunks only where they exist
+    } else if (a.heads_per_chunk == 8) {
+        launch_split_g<D, KB, VB, QJL, 8>(a, s);
+    } else {
+        launch_split_g<D, KB, VB, QJL, 0>(a, s);
+    }
     return hipGetLastError();
 }
 
@@ -1270,9 +1296,9 @@ template <int D, int KB, int VB>
 int split_blocks(bool qjl) {
     int nb = 0;
     const hipError_t e =
-        qjl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, true, false, false, true>,
+        qjl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, true, false, false, 8>,
                                                           64 * split_waves(D, KB, VB, true), 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, false, false, false, true>,
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, false, false, false, 8>,
                                                           64 * split_waves(D, KB, VB, false), 0);
     return e == hipSuccess && nb > 0 ? nb : 0;
 }

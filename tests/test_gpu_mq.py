@@ -61,8 +61,10 @@ def run_mq(tq, B, Hkv, g, C, cap, ctx_len, kbits, vbits, d=128, m=0, seed=0, qdt
 
 @pytest.mark.parametrize("g,C", [(7, 2), (4, 2), (1, 8), (8, 4), (6, 4), (3, 5), (7, 3)])
 def test_mq_groups_and_columns(tq, g, C):
-    """Rows of a kv head (g heads x C columns) in blocks of up to 8, including
-    blocks whose rows straddle two columns (g = 6, C = 4; g = 3, C = 5)."""
+    """Rows of a kv head (g heads x C columns) in blocks of up to 16 (8 with
+    the q_hi/q_lo column fold, 9..16 one row per column: 14 for (7, 2), 16
+    for (8, 4), 12 for (6, 4), 15 for (3, 5)), including blocks whose rows
+    straddle columns (g = 6, C = 4; g = 3, C = 5)."""
     run_mq(tq, B=2, Hkv=2, g=g, C=C, cap=700, ctx_len=[700, 333], kbits=4, vbits=2, seed=10 * g + C)
 
 
@@ -70,6 +72,11 @@ def test_mq_context_edges(tq):
     """Contexts shorter than the columns (early columns see nothing), and
     causal limits across the 64-token tile boundary."""
     run_mq(tq, B=9, Hkv=1, g=2, C=3, cap=200, ctx_len=[0, 1, 2, 3, 63, 64, 65, 66, 200], kbits=3, vbits=3, seed=3)
+
+
+def test_mq_context_edges_16_rows(tq):
+    """The same edges with 12 rows per block (g = 4, C = 3)."""
+    run_mq(tq, B=9, Hkv=1, g=4, C=3, cap=200, ctx_len=[0, 1, 2, 3, 63, 64, 65, 66, 200], kbits=4, vbits=2, seed=4)
 
 
 def test_mq_qjl_d256(tq):
@@ -82,10 +89,16 @@ def test_mq_bit_widths(tq):
         run_mq(tq, B=1, Hkv=2, g=2, C=4, cap=300, ctx_len=[290], kbits=kb, vbits=vb, seed=kb * 4 + vb)
 
 
+def test_mq_bit_widths_16_rows(tq):
+    for kb, vb in ((1, 4), (2, 1), (3, 3), (4, 4)):
+        run_mq(tq, B=1, Hkv=2, g=4, C=4, cap=300, ctx_len=[290], kbits=kb, vbits=vb, seed=kb * 4 + vb + 50)
+
+
 @pytest.mark.parametrize("splits", ["1", "3", "100000"])
-def test_mq_split_invariance(tq, splits, monkeypatch):
+@pytest.mark.parametrize("g,C", [(4, 2), (8, 2)])
+def test_mq_split_invariance(tq, splits, g, C, monkeypatch):
     monkeypatch.setenv("TQ_ATTN_SPLITS", splits)
-    run_mq(tq, B=2, Hkv=1, g=4, C=2, cap=1000, ctx_len=[1000, 129], kbits=4, vbits=2, seed=8)
+    run_mq(tq, B=2, Hkv=1, g=g, C=C, cap=1000, ctx_len=[1000, 129], kbits=4, vbits=2, seed=8)
 
 
 def test_mq_one_column_is_decode(tq):

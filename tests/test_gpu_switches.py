@@ -62,11 +62,11 @@ def test_score_factor_parity(tq, mode, sqnr, C, m):
     assert parity.rel_rows(plain, ref).max() > 10 * parity.ATTN_TOL
 
 
-def _sparse_case(tq, tau, seed=70):
+def _sparse_case(tq, tau, seed=70, g=2):
     """Keys whose 64-token tiles all open with the same dominant key, so every
     wave's running maximum is the true maximum from its first tile on and the
     kernels drop exactly the tokens the oracle drops."""
-    B, Hkv, g, cap, d = 1, 2, 2, 1500, 128
+    B, Hkv, cap, d = 1, 2, 1500, 128
     rng = np.random.default_rng(seed)
     qv = rng.standard_normal(d)
     qv /= np.linalg.norm(qv)
@@ -88,8 +88,10 @@ def _sparse_case(tq, tau, seed=70):
     return got, o.mq_attention(*args, sparse_v=tau), o.mq_attention(*args)
 
 
-def test_sparse_v_drops_what_the_oracle_drops(tq):
-    got, ref, plain = _sparse_case(tq, 0.02)
+@pytest.mark.parametrize("g", [2, 16])
+def test_sparse_v_drops_what_the_oracle_drops(tq, g):
+    """g = 16 runs blocks of 16 query rows."""
+    got, ref, plain = _sparse_case(tq, 0.02, g=g)
     assert np.all(np.isfinite(got))
     assert parity.rel_rows(got, ref).max() <= parity.ATTN_TOL
     assert parity.rel_rows(plain, ref).max() > 10 * parity.ATTN_TOL  # the switch matters here
