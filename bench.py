@@ -543,18 +543,29 @@ def long_leg(tq, torch, synth, steps, warmup):
 
 # ---------------------------------------------------------------- variants ----
 def variants_leg(tq, torch, synth, steps, warmup):
-    """Decode over the caches of the rotation and norm variants, packed bytes
-    per second with 2 cache replicas (beyond the 256 MB Infinity Cache):
+    """Decode over the caches of the rotation, norm and head-shape variants,
+    packed bytes per second with 2 cache replicas (beyond the 256 MB Infinity
+    Cache):
       * head_dim 64 with the double transform S1 -> WHT -> S2 -> WHT, K4/V3
         (the head_dim-64 recommendation of [P1] v1.5.3), 8:1 GQA on the scan;
       * head_dim 512 with one norm per 256-half, K3/V3, 4:1 GQA, on the
-        vector-ALU kernel."""
+        matrix-core wide kernel;
+      * head_dim 256 with one norm per 128-half, K3/V3, 7:1 GQA, on the
+        vector-ALU wide kernel;
+      * head_dim 256 with one norm, K4/V3, 7:1 GQA, on the scan (4-wave blocks);
+      * head_dim 128, K4/V2, 16:1 GQA, on the scan's 16-row blocks."""
     out = {}
     cases = (
         ("double_wht_d64", dict(B=16, Hkv=8, g=8, ctx=32768, d=64, kb=4, vb=3, rot=tq.TQ_ROT_DOUBLE, nb=1),
          "decode, batch 16, 64 query heads / 8 kv heads, d=64, context 32768, K4/V3, double transform"),
         ("block_norm_d512", dict(B=4, Hkv=4, g=4, ctx=32768, d=512, kb=3, vb=3, rot=tq.TQ_ROT_WHT, nb=2),
          "decode, batch 4, 16 query heads / 4 kv heads, d=512, context 32768, K3/V3, two norm blocks"),
+        ("block_norm_d256", dict(B=16, Hkv=4, g=7, ctx=16384, d=256, kb=3, vb=3, rot=tq.TQ_ROT_WHT, nb=2),
+         "decode, batch 16, 28 query heads / 4 kv heads, d=256, context 16384, K3/V3, two norm blocks"),
+        ("d256", dict(B=16, Hkv=4, g=7, ctx=16384, d=256, kb=4, vb=3, rot=tq.TQ_ROT_WHT, nb=1),
+         "decode, batch 16, 28 query heads / 4 kv heads, d=256, context 16384, K4/V3"),
+        ("gqa16_d128", dict(B=16, Hkv=4, g=16, ctx=32768, d=128, kb=4, vb=2, rot=tq.TQ_ROT_WHT, nb=1),
+         "decode, batch 16, 64 query heads / 4 kv heads (16:1), d=128, context 32768, K4/V2"),
     )
     for name, c, desc in cases:
         B, Hkv, g, ctx, d = c["B"], c["Hkv"], c["g"], c["ctx"], c["d"]
@@ -920,7 +931,7 @@ def main():
         res["search"] = search_leg(tq, torch, synth, args.steps, args.warmup)
         log(f"search: {res['search']['ms_per_call']:.2f} ms/call, {res['search']['tflops']:.1f} TFLOP/s")
     if "variants" in legs:
-        log("variants leg (d=64 double transform, d=512 block norms)")
+        log("variants leg (d=64 double transform, block norms at d=512 and 256, d=256, 16:1 GQA)")
         res["variants"] = variants_leg(tq, torch, synth, args.steps, args.warmup)
         log("variants: " + ", ".join(f"{k} {v['gbs']:.0f} GB/s" for k, v in res["variants"].items()))
     if "quality" in legs:

@@ -416,11 +416,10 @@ static int attn_check(const tq_codec* kc, const tq_codec* vc, int batch, int nco
     if (!kc || !vc) return TQ_EINVAL;
     if (!valid_codec(kc) || !valid_codec(vc)) return TQ_EUNSUPPORTED;
     if (kc->d != vc->d || vc->qjl_m != 0) return TQ_EUNSUPPORTED;
-    const bool wide = tqi::attn_wide(kc->d, kc->norm_blocks, vc->norm_blocks);
+    const bool wide = tqi::attn_wide(kc->d);
     if (wide) {
-        // d = 512 or two norm blocks: the vector-ALU kernel, one query column,
-        // keys without a residual
-        if ((kc->d != 256 && kc->d != 512) || kc->qjl_m != 0 || ncols != 1) return TQ_EUNSUPPORTED;
+        // d = 512: the wide kernel, one query column, keys without a residual
+        if (kc->qjl_m != 0 || ncols != 1) return TQ_EUNSUPPORTED;
     } else if (kc->d == 64) {
         // the scan's lane layout: key bytes a whole number of dwords per lane
         // group (2 or 4 bits) and 2..4-bit values
@@ -467,8 +466,8 @@ static int attn_setup(const tq_codec* kc, const tq_codec* vc, const void* q, int
     const int rc = attn_check(kc, vc, batch, ncols, n_q_heads, n_kv_heads, ctx_cap, &splits, &per, &G);
     if (rc != TQ_OK) return rc;
     if (ncols > 1 && win_cap > 0) return TQ_EUNSUPPORTED;  // the residual window serves one query column
-    if (tqi::attn_wide(kc->d, kc->norm_blocks, vc->norm_blocks)) {
-        // the vector-ALU kernel: no residual window and no softmax switches
+    if (tqi::attn_wide(kc->d)) {
+        // the d = 512 kernel: no residual window and no softmax switches
         if (win_cap > 0) return TQ_EUNSUPPORTED;
         if (opts && (opts->score_mode != TQ_SCORE_PLAIN || opts->sparse_v > 0.0f)) return TQ_EUNSUPPORTED;
     }

@@ -113,7 +113,7 @@ void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int v
     *split_tokens = best_per;
 }
 
-bool attn_wide(int d, int k_blocks, int v_blocks) { return d == 512 || k_blocks != 1 || v_blocks != 1; }
+bool attn_wide(int d) { return d == 512; }
 
 // Plan of the wide kernels: query rows in chunks of G <= 8 (the largest divisor of g);
 // splits of a multiple of 256 tokens (4 waves x 64), as many as give about two
@@ -222,7 +222,7 @@ hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (stages & ATTN_SCAN) {
-        e = attn_wide(a.kc.d, a.kc.norm_blocks, a.vc.norm_blocks) ? launch_wide(a, s) : launch_split_any(a, s);
+        e = attn_wide(a.kc.d) ? launch_wide(a, s) : launch_split_any(a, s);
         if (e != hipSuccess) return e;
     }
     if ((stages & ATTN_WINDOW) && a.win_cap > 0) {

@@ -194,7 +194,7 @@ constexpr int kLdsBytes = 160 * 1024;
 constexpr int kVStride = 68;                        // padded dword stride of the V staging rows
 constexpr int k_codes(int kb) { return kb >= 3 ? 2 : 4; }  // codes per K lookup
 constexpr int v_codes(int vb) { return vb == 1 ? 8 : (vb == 2 ? 4 : 2); }  // codes per V lookup
-constexpr int wave_dw(int d, int vb) { return (d * vb / 32 + 1) * kVStride + 16 + 3 * 64; }
+constexpr int wave_dw(int d, int vb) { return (d * vb / 32 + 1) * kVStride + 16 + 3 * 64 + (d == 256 ? 2 * 64 : 0); }
 constexpr int qjl_dw(bool qjl) { return qjl ? 8 * 64 * 4 + 256 * 4 : 0; }
 constexpr int k_rows(int kb) { return 1 << (k_codes(kb) * kb); }
 constexpr int v_rows(int vb) { return 1 << (v_codes(vb) * vb); }
@@ -222,8 +222,9 @@ constexpr bool split_tables(int d, int kb, int vb, bool qjl) {
 // d = 128, where the 16 rotated query rows fit the wave areas.
 constexpr bool split_rows16(int d, bool qjl) { return !qjl && d <= 128; }
 
-template <int D, int KB, int VB, bool QJL>
+template <int D, int KB, int VB, bool QJL, bool TWO = false>
 struct Cfg {
+    static_assert(!TWO || (D == 256 && !QJL), "the per-half layout is for d = 256 without QJL");
     static constexpr int GMAX = split_rows16(D, QJL) ? 16 : 8;  // query rows per block (at most)
     static constexpr int NW = split_waves(D, KB, VB, QJL);  // waves per block
     static constexpr int NT = 64 * NW;              // threads per block
@@ -247,6 +248,10 @@ struct Cfg {
     static constexpr int VENT = 2 * VT;             // bytes per V entry
     static constexpr int VENTW = VENT / 4;          // ... in dwords
     static constexpr int VLK = NB / VT;             // V lookups per token
+    // caches with two norm blocks (d = 256): every K step and every V sum
+    // covers dims of one half of the rotated vector only (see fetch_k and the V
+    // pieces), so a norm per half can scale each half's products
+    static constexpr bool HALVES = TWO;
     // tables (see above): slices per row, table bytes, byte offset of V row 0
     // split into the part above 64 KiB (carried by the lane offset) and the
     // rest (an instruction offset)
@@ -317,6 +322,9 @@ __device__ __forceinline__ void lds_read(uint32_t* dst, const uint8_t* p) {
 }
 
 // K codes of sub-tiles 0..3 in MFMA A layout: token t0 + 16j + n, bytes grp*GB.
+// With HALVES the lane group's dims are [32 grp, 32 grp + 32) of each half:
+// the GB/2 bytes at grp*GB/2 and at RBK/2 + grp*GB/2, one after the other in
+// the registers (so K step ks < KSTEPS/2 reads the first half's dims).
 // Token indices are clamped into [t0, t_end) so every address is valid.
 template <class C>
 __device__ __forceinline__ void fetch_k(uint32_t (&rk)[4 * C::GW], const uint8_t* kcodes, uint32_t t0, uint32_t last,
@@ -325,6 +333,32 @@ __device__ __forceinline__ void fetch_k(uint32_t (&rk)[4 * C::GW], const uint8_t
     for (int j = 0; j < 4; ++j) {
         uint32_t t = t0 + 16 * j + n;
         t = t < last ? t : last;
+        if constexpr (C::HALVES) {
+            constexpr int HW = C::GW / 2;  // dwords per half
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(kcodes + (t * C::RBK + hf * (C::RBK / 2) +
+                                                                                  grp * (C::GB / 2)));
+                uint32_t* r = rk + j * C::GW + hf * HW;
+                if constexpr (HW % 4 == 0) {
+#pragma unroll
+                    for (int w = 0; w < HW / 4; ++w) {
+                        const uint4 v = ld_stream4(p + 4 * w);
+                        r[4 * w] = v.x; r[4 * w + 1] = v.y; r[4 * w + 2] = v.z; r[4 * w + 3] = v.w;
+                    }
+                } else if constexpr (HW % 2 == 0) {
+#pragma unroll
+                    for (int w = 0; w < HW / 2; ++w) {
+                        const uint2 v = ld_stream2(p + 2 * w);
+                        r[2 * w] = v.x; r[2 * w + 1] = v.y;
+                    }
+                } else {
+#pragma unroll
+                    for (int w = 0; w < HW; ++w) r[w] = ld_stream1(p + w);
+                }
+            }
+            continue;
+        }
         const uint32_t* p = reinterpret_cast<const uint32_t*>(kcodes + (t * C::RBK + grp * C::GB));
         if constexpr (C::GW % 4 == 0) {
 #pragma unroll
@@ -348,9 +382,9 @@ __device__ __forceinline__ void fetch_k(uint32_t (&rk)[4 * C::GW], const uint8_t
 
 // V row, norms (and QJL gamma) of token t0 + lane (clamped like fetch_k).
 template <class C, bool QJL>
-__device__ __forceinline__ void fetch_v(uint32_t (&rv)[C::VTW], uint32_t& rn, uint32_t& rg, const uint8_t* vcodes,
-                                        const uint8_t* knb, const uint8_t* vnb, const uint8_t* gmb, uint32_t t0,
-                                        uint32_t last, int lane) {
+__device__ __forceinline__ void fetch_v(uint32_t (&rv)[C::VTW], uint32_t& rn, uint32_t& rg, uint32_t& rv2,
+                                        const uint8_t* vcodes, const uint8_t* knb, const uint8_t* vnb,
+                                        const uint8_t* gmb, uint32_t t0, uint32_t last, int lane, int nbk, int nbv) {
     uint32_t tl = t0 + lane;
     tl = tl < last ? tl : last;
     if constexpr (C::RBV % 16 == 0) {
@@ -369,6 +403,19 @@ __device__ __forceinline__ void fetch_v(uint32_t (&rv)[C::VTW], uint32_t& rn, ui
             const uint2 v = ld_stream2(vp + w);
             rv[2 * w] = v.x; rv[2 * w + 1] = v.y;
         }
+    }
+    if constexpr (C::HALVES) {
+        // rn: the K norms of the two halves, rg: the V norms (the one norm twice
+        // for a cache with one norm block); no QJL with two norm blocks
+        // (the norm arrays are only 2-byte aligned: two 16-bit loads per pair)
+        const uint32_t k = nbk == 2 ? ld_stream_u16(knb + 4u * tl) | (ld_stream_u16(knb + 4u * tl + 2u) << 16)
+                                    : ld_stream_u16(knb + 2u * tl) * 0x10001u;
+        const uint32_t v = nbv == 2 ? ld_stream_u16(vnb + 4u * tl) | (ld_stream_u16(vnb + 4u * tl + 2u) << 16)
+                                    : ld_stream_u16(vnb + 2u * tl) * 0x10001u;
+        rn = k;
+        rv2 = v;
+        if constexpr (QJL) rg = ld_stream_u16(gmb + 2u * tl);
+        return;
     }
     rn = ld_stream_u16(knb + 2u * tl) | (ld_stream_u16(vnb + 2u * tl) << 16);
     if constexpr (QJL) rg = ld_stream_u16(gmb + 2u * tl);
@@ -398,11 +445,13 @@ __device__ __forceinline__ int64_t query_row(const AttnArgs& a, int b, int kvh, 
 //           against q_lo, into the same scores, so the lookups, softmax and V
 //           sums of a tile serve twice the rows for 1.67x the matrix-core
 //           work (2 x 32 K steps + 16 V steps against 32 + 16 per 8 rows).
-template <int D, int KB, int VB, bool QJL, bool SPARSE, bool MQ, int GM>
+// TWO: a cache with two norm blocks on either side (d = 256, the per-half
+// layout of Cfg::HALVES; a side with one norm uses it for both halves).
+template <int D, int KB, int VB, bool QJL, bool SPARSE, bool MQ, int GM, bool TWO>
 __global__ __launch_bounds__(64 * split_waves(D, KB, VB, QJL))
 __attribute__((amdgpu_waves_per_eu(split_waves(D, KB, VB, QJL) / 4)))
 void split_kernel(AttnArgs a) {
-    using C = Cfg<D, KB, VB, QJL>;
+    using C = Cfg<D, KB, VB, QJL, TWO>;
     constexpr bool R16 = GM == 16;
     static_assert(!R16 || split_rows16(D, QJL), "16-row blocks need d <= 128 and no QJL");
     const int G = GM == 8 ? 8 : a.heads_per_chunk;
@@ -430,8 +479,11 @@ void split_kernel(AttnArgs a) {
     const int64_t kvrow = ((int64_t)b * a.hkv + kvh) * a.ctx_cap;
     const uint8_t* kcodes = a.k_codes + kvrow * C::RBK;
     const uint8_t* vcodes = a.v_codes + kvrow * C::RBV;
-    const uint8_t* knb = reinterpret_cast<const uint8_t*>(a.k_norms + kvrow);
-    const uint8_t* vnb = reinterpret_cast<const uint8_t*>(a.v_norms + kvrow);
+    // norm blocks per vector (two only with HALVES), their scale sqrt(blocks)
+    const int nbk = C::HALVES ? a.kc.norm_blocks : 1, nbv = C::HALVES ? a.vc.norm_blocks : 1;
+    const float bsk = nbk == 2 ? 1.41421356237309505f : 1.0f, bsv = nbv == 2 ? 1.41421356237309505f : 1.0f;
+    const uint8_t* knb = reinterpret_cast<const uint8_t*>(a.k_norms + kvrow * nbk);
+    const uint8_t* vnb = reinterpret_cast<const uint8_t*>(a.v_norms + kvrow * nbv);
     const uint8_t* gmb = QJL ? reinterpret_cast<const uint8_t*>(a.k_gamma + kvrow) : nullptr;
     const uint32_t last = t_end > 0 ? (uint32_t)(t_end - 1) : 0u;
 
@@ -460,10 +512,10 @@ void split_kernel(AttnArgs a) {
     constexpr bool KDB = C::KDB;
     constexpr int KBUF = KDB ? 2 : 1;  // K code buffers: with two, a tile's K codes are loaded one tile ahead
     uint32_t rk[KBUF][4 * C::GW];
-    uint32_t rv[C::VTW], rn = 0, rg = 0;
+    uint32_t rv[C::VTW], rn = 0, rg = 0, rv2 = 0;
     if (t0 < t_end) {
         fetch_k<C>(rk[0], kcodes, (uint32_t)t0, last, n, grp);
-        fetch_v<C, QJL>(rv, rn, rg, vcodes, knb, vnb, gmb, (uint32_t)t0, last, lane);
+        fetch_v<C, QJL>(rv, rn, rg, rv2, vcodes, knb, vnb, gmb, (uint32_t)t0, last, lane, nbk, nbv);
     }
 
     // centroids once into LDS, then every table row is written as 16-byte
@@ -558,7 +610,8 @@ void split_kernel(AttnArgs a) {
         for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int dim = grp * C::DG + 4 * ks + i;
+                const int dim = C::HALVES ? (ks < C::KSTEPS / 2 ? 0 : D / 2) + grp * (C::DG / 2) + 4 * (ks % (C::KSTEPS / 2)) + i
+                                          : grp * C::DG + 4 * ks + i;
                 const float x = qr[(head_ok ? hh : 0) * D + dim];
                 qv[ks][i] = head_ok ? x : 0.0f;
                 amax = fmaxf(amax, fabsf(qv[ks][i]));
@@ -618,6 +671,8 @@ void split_kernel(AttnArgs a) {
     float* knq = hfac + 16;                                             // [64] K norm * query scale
     float* vnl = knq + 64;                                              // [64] V norm * weight scale
     float* gml = vnl + 64;                                              // [64] QJL gamma
+    float* knq1 = gml + 64;                                             // HALVES: [64] second-half K norm * query scale
+    float* vnl1 = knq1 + 64;                                            // HALVES: [64] second-half V norm * weight scale
     __syncthreads();  // every wave has read qr before the wave areas are reused
     vt[C::VTW * C::VSTR + lane] = 0u;
     __syncthreads();
@@ -631,6 +686,11 @@ void split_kernel(AttnArgs a) {
     floatx4_t vacc[C::NB];
 #pragma unroll
     for (int q = 0; q < C::NB; ++q) vacc[q] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // HALVES: the second half's K sums of the tile, its V norm (scaled like
+    // vnf) and its V-side A operands
+    floatx4_t sacc1[4];
+    float vn1f = 0.0f;
+    uint32_t wa1[2][4];
     int vref = -200;                 // reference V-norm exponent: norms < 2^vref
     float vlim = 0.0f, vsc = 0.0f;   // 2^vref, 2^wsh with wsh = 15 - kTauLog2 - vref
     const int pbit = C::PIECE * n;   // this lane's V field inside a row
@@ -653,15 +713,26 @@ void split_kernel(AttnArgs a) {
         const bool lane_valid = lane < rem;
 #pragma unroll
         for (int w = 0; w < C::VTW; ++w) vt[w * C::VSTR + lane] = rv[w];
-        vnf = half_bits_to_float(rn >> 16);
-        knq[lane] = half_bits_to_float(rn & 0xFFFFu) * qinv;
+        float vmx;  // the larger V norm of the token
+        if constexpr (C::HALVES) {
+            knq[lane] = half_bits_to_float(rn & 0xFFFFu) * (qinv * bsk);
+            knq1[lane] = half_bits_to_float(rn >> 16) * (qinv * bsk);
+            vnf = half_bits_to_float(rv2 & 0xFFFFu) * bsv;
+            vn1f = half_bits_to_float(rv2 >> 16) * bsv;
+            vnl1[lane] = vn1f * vsc;
+            vmx = fmaxf(vnf, vn1f);
+        } else {
+            vnf = half_bits_to_float(rn >> 16);
+            knq[lane] = half_bits_to_float(rn & 0xFFFFu) * qinv;
+            vmx = vnf;
+        }
         if constexpr (QJL) gml[lane] = half_bits_to_float(rg);
         vnl[lane] = vnf * vsc;
         // prefetch (clamped to the split: past its end this re-reads the last token)
-        fetch_v<C, QJL>(rv, rn, rg, vcodes, knb, vnb, gmb, (uint32_t)(t0 + 64 * C::NW), last, lane);
+        fetch_v<C, QJL>(rv, rn, rg, rv2, vcodes, knb, vnb, gmb, (uint32_t)(t0 + 64 * C::NW), last, lane, nbk, nbv);
         if constexpr (KDB) fetch_k<C>(rk[nxt], kcodes, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
         // a V norm at or above the reference is handled by the rare rescale
-        return __builtin_amdgcn_ballot_w64(lane_valid && vnf >= vlim) != 0;
+        return __builtin_amdgcn_ballot_w64(lane_valid && vmx >= vlim) != 0;
     };
     // K scores of tile t0 (16 tokens x 16 columns per sub-tile), then prefetch the next tile's K codes
     // (K codes from buffer cur; with one buffer the next tile's codes are loaded after the lookups)
@@ -669,6 +740,10 @@ void split_kernel(AttnArgs a) {
         constexpr int cur = decltype(curc)::value % KBUF;
 #pragma unroll
         for (int j = 0; j < 4; ++j) sacc[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (C::HALVES) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sacc1[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
         // step s = (sub-tile j, K step ks); the table lookups of step
         // s + kKLookahead are issued before the matrix-core op of step s, and
         // scheduling barriers keep that order
@@ -696,8 +771,10 @@ void split_kernel(AttnArgs a) {
             if constexpr (s + kKLookahead < NS) look(std::integral_constant<int, s + kKLookahead>{});
             __builtin_amdgcn_sched_barrier(0);
             const half8_t ak = as_half8(make_uint4(aw[s][0], aw[s][1], aw[s][2], aw[s][3]));
-            sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bq[ks], sacc[j], 0, 0, 0);
-            if constexpr (R16) sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bql[ks], sacc[j], 0, 0, 0);
+            // the K steps of the second half accumulate apart (HALVES)
+            floatx4_t& acc = (C::HALVES && ks >= C::KSTEPS / 2) ? sacc1[j] : sacc[j];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bq[ks], acc, 0, 0, 0);
+            if constexpr (R16) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, bql[ks], acc, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr (!KDB) fetch_k<C>(rk[cur], kcodes, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
@@ -721,6 +798,12 @@ void split_kernel(AttnArgs a) {
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) sacc[j][v] += xor_lane<8>(sacc[j][v]);
+            if constexpr (C::HALVES) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) sacc1[j][v] += xor_lane<8>(sacc1[j][v]);
+            }
         }
     };
     // scores of tile t0 relative to the reference max, the rare rescale, and the
@@ -740,6 +823,13 @@ void split_kernel(AttnArgs a) {
             dsc[j][1] = fmaf(sacc[j][1], kq.y, -m_ref);
             dsc[j][2] = fmaf(sacc[j][2], kq.z, -m_ref);
             dsc[j][3] = fmaf(sacc[j][3], kq.w, -m_ref);
+            if constexpr (C::HALVES) {
+                const float4 kq1 = *reinterpret_cast<const float4*>(knq1 + 16 * j + 4 * grp);
+                dsc[j][0] = fmaf(sacc1[j][0], kq1.x, dsc[j][0]);
+                dsc[j][1] = fmaf(sacc1[j][1], kq1.y, dsc[j][1]);
+                dsc[j][2] = fmaf(sacc1[j][2], kq1.z, dsc[j][2]);
+                dsc[j][3] = fmaf(sacc1[j][3], kq1.w, dsc[j][3]);
+            }
         }
         // token 16j + 4grp + v is valid iff 16j + v < lim
         int lim;
@@ -770,7 +860,7 @@ void split_kernel(AttnArgs a) {
             // head (to its tile max), rescaling the running sums
             float vfac = 1.0f;
             if (vraise) {
-                const float vm = wave_max(lane < rem ? vnf : 0.0f);
+                const float vm = wave_max(lane < rem ? (C::HALVES ? fmaxf(vnf, vn1f) : vnf) : 0.0f);
                 int e;
                 frexpf(vm, &e);
                 const int vnew = e + kVHeadroom;
@@ -779,15 +869,22 @@ void split_kernel(AttnArgs a) {
                 vlim = ldexpf(1.0f, vref);
                 vsc = ldexpf(1.0f, 15 - (int)kTauLog2 - vref);
                 vnl[lane] = vnf * vsc;
+                if constexpr (C::HALVES) vnl1[lane] = vn1f * vsc;
             }
             float sv[4][4], tmax = -INFINITY;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float4 kq = *reinterpret_cast<const float4*>(knq + 16 * j + 4 * grp);
                 const float kv[4] = {kq.x, kq.y, kq.z, kq.w};
+                float kv1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (C::HALVES) {
+                    const float4 kq1 = *reinterpret_cast<const float4*>(knq1 + 16 * j + 4 * grp);
+                    kv1[0] = kq1.x; kv1[1] = kq1.y; kv1[2] = kq1.z; kv1[3] = kq1.w;
+                }
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    sv[j][v] = (16 * j + v < lim) ? sacc[j][v] * kv[v] : -INFINITY;
+                    const float sk = C::HALVES ? fmaf(sacc1[j][v], kv1[v], sacc[j][v] * kv[v]) : sacc[j][v] * kv[v];
+                    sv[j][v] = (16 * j + v < lim) ? sk : -INFINITY;
                     tmax = fmaxf(tmax, sv[j][v]);
                 }
             }
@@ -824,6 +921,11 @@ void split_kernel(AttnArgs a) {
             psum += (p0 + p1) + (p2 + p3);
             wa[j >> 1][2 * (j & 1)] = pack_half2(p0 * vq.x, p1 * vq.y);
             wa[j >> 1][2 * (j & 1) + 1] = pack_half2(p2 * vq.z, p3 * vq.w);
+            if constexpr (C::HALVES) {
+                const float4 vq1 = *reinterpret_cast<const float4*>(vnl1 + 16 * j + 4 * grp);
+                wa1[j >> 1][2 * (j & 1)] = pack_half2(p0 * vq1.x, p1 * vq1.y);
+                wa1[j >> 1][2 * (j & 1) + 1] = pack_half2(p2 * vq1.z, p3 * vq1.w);
+            }
         }
         l_lane += psum;
         if (sparse) {
@@ -837,6 +939,10 @@ void split_kernel(AttnArgs a) {
                 const uint32_t k1 = (dsc[j][2] < a.sparse_log2 ? 0u : 0xFFFFu) | (dsc[j][3] < a.sparse_log2 ? 0u : 0xFFFF0000u);
                 wa[j >> 1][2 * (j & 1)] &= k0;
                 wa[j >> 1][2 * (j & 1) + 1] &= k1;
+                if constexpr (C::HALVES) {
+                    wa1[j >> 1][2 * (j & 1)] &= k0;
+                    wa1[j >> 1][2 * (j & 1) + 1] &= k1;
+                }
             }
         }
         // rows of heads >= G (with G <= 8 also the repeated rows 8..15) carry
@@ -846,7 +952,10 @@ void split_kernel(AttnArgs a) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                for (int w = 0; w < 4; ++w) wa[s2][w] = 0u;
+                for (int w = 0; w < 4; ++w) {
+                    wa[s2][w] = 0u;
+                    if constexpr (C::HALVES) wa1[s2][w] = 0u;
+                }
         }
     };
     // this lane's PIECE-bit field of the staged tile's tokens e = 4 jj + v (token
@@ -861,6 +970,49 @@ void split_kernel(AttnArgs a) {
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const int tok = 32 * s2 + 16 * jj + 4 * grp;
+                if constexpr (C::HALVES) {
+                    // the lane's dims are [NB/2 n, NB/2 n + NB/2) of each half: two
+                    // HB-bit fields, the first half's in the low bits of the piece
+                    constexpr int HB = C::PIECE / 2;
+                    constexpr uint32_t HM = HB == 32 ? 0xFFFFFFFFu : (1u << HB) - 1u;
+                    const int b0 = HB * n, b1 = (D / 2) * VB + HB * n;
+                    const uint4 x0 = *reinterpret_cast<const uint4*>(vt + (b0 >> 5) * C::VSTR + tok);
+                    const uint4 x1 = *reinterpret_cast<const uint4*>(vt + (b1 >> 5) * C::VSTR + tok);
+                    const uint32_t l0[4] = {x0.x, x0.y, x0.z, x0.w}, l1[4] = {x1.x, x1.y, x1.z, x1.w};
+                    uint32_t h0[4], h1[4];
+                    if constexpr (32 % HB != 0) {
+                        // a field may cross into the next dword (the tile's last row is zero)
+                        const uint4 y0 = *reinterpret_cast<const uint4*>(vt + ((b0 >> 5) + 1) * C::VSTR + tok);
+                        const uint4 y1 = *reinterpret_cast<const uint4*>(vt + ((b1 >> 5) + 1) * C::VSTR + tok);
+                        const uint32_t u0[4] = {y0.x, y0.y, y0.z, y0.w}, u1[4] = {y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            h0[v] = __builtin_amdgcn_alignbit(u0[v], l0[v], b0 & 31) & HM;
+                            h1[v] = __builtin_amdgcn_alignbit(u1[v], l1[v], b1 & 31) & HM;
+                        }
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            h0[v] = (l0[v] >> (b0 & 31)) & HM;
+                            h1[v] = (l1[v] >> (b1 & 31)) & HM;
+                        }
+                    }
+                    if constexpr (PK == 2) {
+                        pc[s2][2 * jj] = (h0[0] | (h1[0] << HB)) | ((h0[1] | (h1[1] << HB)) << 16);
+                        pc[s2][2 * jj + 1] = (h0[2] | (h1[2] << HB)) | ((h0[3] | (h1[3] << HB)) << 16);
+                    } else if constexpr (C::PIECE == 32) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) pc[s2][4 * jj + v] = h0[v] | (h1[v] << HB);
+                    } else {
+                        static_assert(C::PIECE > 32 && C::PIECE <= 64, "V piece of 33..64 bits");
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            pc[s2][4 * jj + v] = HB == 32 ? h0[v] : (h0[v] | (h1[v] << HB));
+                            ph[s2][4 * jj + v] = HB == 32 ? h1[v] : (h1[v] >> (32 - HB));
+                        }
+                    }
+                    continue;
+                }
                 const uint4 x = *reinterpret_cast<const uint4*>(vt + pw0 * C::VSTR + tok);
                 const uint32_t lo[4] = {x.x, x.y, x.z, x.w};
                 if constexpr (PK == 2) {
@@ -892,8 +1044,12 @@ void split_kernel(AttnArgs a) {
         for (int s2 = 0; s2 < 2; ++s2) {
             // sparse V: a 32-token step whose weights are all dropped is skipped
             // (its table lookups and matrix-core ops)
-            if (sparse && !__builtin_amdgcn_ballot_w64((wa[s2][0] | wa[s2][1] | wa[s2][2] | wa[s2][3]) != 0u)) continue;
-            const half8_t aw = as_half8(make_uint4(wa[s2][0], wa[s2][1], wa[s2][2], wa[s2][3]));
+            if (sparse && !__builtin_amdgcn_ballot_w64((wa[s2][0] | wa[s2][1] | wa[s2][2] | wa[s2][3] |
+                                                        (C::HALVES ? wa1[s2][0] | wa1[s2][1] | wa1[s2][2] | wa1[s2][3]
+                                                                   : 0u)) != 0u))
+                continue;
+            const half8_t aw0 = as_half8(make_uint4(wa[s2][0], wa[s2][1], wa[s2][2], wa[s2][3]));
+            const half8_t aw1 = C::HALVES ? as_half8(make_uint4(wa1[s2][0], wa1[s2][1], wa1[s2][2], wa1[s2][3])) : aw0;
 #pragma unroll
             for (int k = 0; k < C::VLK; ++k) {
                 const int bit = k * C::VLB;
@@ -928,6 +1084,8 @@ void split_kernel(AttnArgs a) {
                                                 __builtin_amdgcn_perm(ent[5][h >> 1], ent[4][h >> 1], sel),
                                                 __builtin_amdgcn_perm(ent[7][h >> 1], ent[6][h >> 1], sel));
                     const int nb = k * C::VT + h;
+                    // with HALVES, columns nb >= NB/2 are second-half dims (their own V norms)
+                    const half8_t aw = (C::HALVES && nb >= C::NB / 2) ? aw1 : aw0;
                     vacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, as_half8(bq), vacc[nb], 0, 0, 0);
                 }
             }
@@ -988,9 +1146,14 @@ void split_kernel(AttnArgs a) {
     for (int i = 0; i < 4; ++i) {
         const int h = 4 * grp + i;
         if (h < G) {
-            float* rr = mrg + (wave * G + h) * (D + 2) + 2 + C::NB * n;
+            float* rr = mrg + (wave * G + h) * (D + 2) + 2;
 #pragma unroll
-            for (int q = 0; q < C::NB; ++q) rr[q] = vacc[q][i] * wunit;
+            for (int q = 0; q < C::NB; ++q) {
+                // the dim of column n of V sum q (see the V pieces)
+                const int dim = C::HALVES ? (q < C::NB / 2 ? 0 : D / 2) + (C::NB / 2) * n + (q % (C::NB / 2))
+                                          : C::NB * n + q;
+                rr[dim] = vacc[q][i] * wunit;
+            }
         }
     }
     __syncthreads();
@@ -1257,30 +1420,38 @@ __global__ __launch_bounds__(256) void window_kernel(AttnArgs a) {
     combine_head<D>(a, bh, gl, tg == 0, m, l, y);
 }
 
-template <int D, int KB, int VB, bool QJL, int GM>
+template <int D, int KB, int VB, bool QJL, int GM, bool TWO>
 void launch_split_g(const AttnArgs& a, hipStream_t s) {
     const dim3 grid(a.splits, a.hkv * a.chunks, a.batch);
     const dim3 block(64 * split_waves(D, KB, VB, QJL));
     const bool sparse = a.sparse_log2 > -INFINITY, mq = a.ncols > 1;
     if (sparse && mq)
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, true, true, GM>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, true, true, GM, TWO>), grid, block, 0, s, a);
     else if (sparse)
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, true, false, GM>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, true, false, GM, TWO>), grid, block, 0, s, a);
     else if (mq)
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, false, true, GM>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, false, true, GM, TWO>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, false, false, GM>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((split_kernel<D, KB, VB, QJL, false, false, GM, TWO>), grid, block, 0, s, a);
 }
 
 template <int D, int KB, int VB, bool QJL>
 hipError_t launch_split_q(const AttnArgs& a, hipStream_t s) {
-    if (a.heads_per_chunk > 8) {
-        if constexpr (split_rows16(D, QJL)) launch_split_g<D, KB, VB, QJL, 16>(a, s);
+    if (a.kc.norm_blocks == 2 || a.vc.norm_blocks == 2) {
+        // two norm blocks: d = 256, no QJL, at most 8 rows per block (the plan's G)
+        if constexpr (D == 256 && !QJL) {
+            if (a.heads_per_chunk == 8) launch_split_g<D, KB, VB, QJL, 8, true>(a, s);
+            else launch_split_g<D, KB, VB, QJL, 0, true>(a, s);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if (a.heads_per_chunk > 8) {
+        if constexpr (split_rows16(D, QJL)) launch_split_g<D, KB, VB, QJL, 16, false>(a, s);
         else return hipErrorInvalidValue;  // the plan gives such chunks only where they exist
     } else if (a.heads_per_chunk == 8) {
-        launch_split_g<D, KB, VB, QJL, 8>(a, s);
+        launch_split_g<D, KB, VB, QJL, 8, false>(a, s);
     } else {
-        launch_split_g<D, KB, VB, QJL, 0>(a, s);
+        launch_split_g<D, KB, VB, QJL, 0, false>(a, s);
     }
     return hipGetLastError();
 }
@@ -1296,9 +1467,9 @@ template <int D, int KB, int VB>
 int split_blocks(bool qjl) {
     int nb = 0;
     const hipError_t e =
-        qjl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, true, false, false, 8>,
+        qjl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, true, false, false, 8, false>,
                                                           64 * split_waves(D, KB, VB, true), 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, false, false, false, 8>,
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, split_kernel<D, KB, VB, false, false, false, 8, false>,
                                                           64 * split_waves(D, KB, VB, false), 0);
     return e == hipSuccess && nb > 0 ? nb : 0;
 }

@@ -425,7 +425,7 @@ void launch_mc_k(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_wide_mc(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_wide(const AttnArgs& a, hipStream_t s) {
     switch (a.kc.bits) {
         case 1: launch_mc_k<1>(a, s); break;
         case 2: launch_mc_k<2>(a, s); break;

@@ -111,13 +111,11 @@ enum AttnStage { ATTN_PREPARE = 1, ATTN_SCAN = 2, ATTN_COMBINE = 4, ATTN_ALL = 7
 hipError_t launch_attn(const AttnArgs& a, int stages, hipStream_t s);
 void attn_plan(int batch, int hkv, int gv, int64_t ctx_cap, int d, int kb, int vb, bool qjl, int* splits,
                int64_t* split_tokens, int* heads_per_chunk);
-// Head dimension 512 and two-norm-block caches: the vector-ALU kernel
-// (tq_attn_wide.hip) in place of the matrix-core scan, with its own plan.
-bool attn_wide(int d, int k_blocks, int v_blocks);
+// Head dimension 512: the wide kernel (tq_attn_wide_mc.hip, the dims split
+// across a block's waves) in place of the scan, with its own plan.
+bool attn_wide(int d);
 void wide_plan(int batch, int hkv, int g, int64_t ctx_cap, int* splits, int64_t* split_tokens, int* heads_per_chunk);
 hipError_t launch_wide(const AttnArgs& a, hipStream_t s);
-// the d = 512 kernel on the matrix cores (tq_attn_wide_mc.hip)
-hipError_t launch_wide_mc(const AttnArgs& a, hipStream_t s);
 template <int D, int KB>
 hipError_t launch_split_dk(const AttnArgs& a, hipStream_t s);
 template <int D, int KB>

@@ -97,8 +97,10 @@ def test_attention_argument_errors():
     assert tq.tq_attn_workspace_bytes(k64_3, k64, 2, 14, 2, 1000) == 0  # d = 64: 3-bit keys
     assert tq.tq_attn_workspace_bytes(k64, v64_1, 2, 14, 2, 1000) == 0  # d = 64: 1-bit values
     assert tq.tq_attn_workspace_bytes(k32, k32, 2, 14, 2, 1000) == 0  # d = 32
-    # d = 512 and two norm blocks: the vector-ALU kernel, one query column only
+    # two norm blocks at d = 256 run on the scan (any number of query columns);
+    # d = 512 runs on the wide kernel, one query column only
     assert tq.tq_attn_workspace_bytes(kb2, kb2, 2, 14, 2, 1000) > 0
+    assert tq.tq_workspace_bytes(tq.TQ_OP_ATTN_DECODE_MQ, kb2, kb2, 2, 14, 2, 1000, 3, 0, 0) > 0
     assert tq.tq_attn_workspace_bytes(k512, k512, 2, 14, 2, 1000) > 0
     assert tq.tq_workspace_bytes(tq.TQ_OP_ATTN_DECODE_MQ, k512, k512, 2, 14, 2, 1000, 2, 0, 0) == 0
     assert tq.tq_workspace_bytes(tq.TQ_OP_ATTN_DECODE_MQ, k512, k512, 2, 14, 2, 1000, 1, 0, 0) > 0
