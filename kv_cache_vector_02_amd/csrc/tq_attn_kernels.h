@@ -206,8 +206,8 @@ constexpr bool split_fits(int d, int kb, int vb, bool qjl, int nw) {
 // Waves of one split block (the block owns a compute unit: one resident block
 // per CU, its waves sharing the tables): 8 up to d = 128 (two waves per SIMD,
 // 256 registers each), 4 at d = 256 (one wave per SIMD: the twice longer query
-// operands and V sums need up to 512 registers).  Every variant then compiles
-// without register spills; with 12 waves (168 registers) most d = 128 variants
+// operands and V sums need up to 512 registers).  No variant then spills in
+// its tile loop; with 12 waves (168 registers) most d = 128 variants
 // spilled and ran up to 1.7x slower, with 8 waves at d = 256 up to 2.3x.  The
 // split tables are used where they fit beside the wave areas, else the shared
 // table; the QJL variant, whose extra operands take LDS, keeps the shared one.
