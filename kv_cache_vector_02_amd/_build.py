@@ -29,9 +29,15 @@ CFLAGS = [
 ]
 
 
+# Per-file code generation options: the encoder's matrix-core transform keeps
+# its accumulators in ordinary vector registers (no moves out of the
+# accumulation registers before the quantizer reads them).
+FILE_FLAGS = {"tq_encode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> tuple[str, str]:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

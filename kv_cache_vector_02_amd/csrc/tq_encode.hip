@@ -13,6 +13,7 @@
 // write-up on idea.jsleekr.com ("핵심 발견 3": bit-shift packing).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "tq_device.h"
@@ -313,26 +314,239 @@ __device__ __forceinline__ void encode_rows(const EncodeArgs& a, const uint2* qt
     }
 }
 
-template <int D, int BITS, int DT, bool TAB>
+// ---------------------------------------------------------------------------
+// 16-bit input with the transform on the matrix cores (d = 128 and 256, one
+// norm, the plain transform): y = H D x is a dense contraction of each vector
+// with the +-1 matrix H, exact in its products for fp16 and bf16 input, so a
+// wave runs it as v_mfma_f32_16x16x32_{f16,bf16} with its 16 vectors as the
+// 16 columns.
+//   * Loads: lane l (vector n = l % 16, quarter q = l / 16) reads dims
+//     32 s + 8 q .. + 7 of its vector for K step s: the B operand of step s
+//     as it comes from memory; the D sign flip is an XOR on the halves.
+//   * A operands: H[16 r + m][32 s + k] = (-1)^popcount((16 r + m) & (32 s + k)),
+//     and with m < 16, k < 32 the exponent splits into popcount(m & k & 15),
+//     (r & 1) * (k >> 4) and popcount((r >> 1) & s).  For the lane holding
+//     A row m, k = 8 (l / 16) + e, so one base operand, its copy signed by
+//     (-1)^(l / 32) (odd r), and the negations of both (the uniform sign
+//     of (r >> 1) & s) cover every (r, s): 4 registers sets instead of
+//     D/16 x D/32.
+//   * Output: lane l holds y[16 r + 4 q + j] of vector n (D layout), which the
+//     bin-table quantizer codes in place; 4 codes per r make one piece of
+//     4 BITS bits.  The pieces go through the wave's LDS area and come back as
+//     dims [D/4 q, D/4 (q + 1)) per lane, which for 2 and 4 bits are already
+//     the packed code words.
+// Fewer vector instructions per vector than the register transform (two
+// matrix-core ops per vector at d = 128 replace 56 lane adds and DPP moves).
+// ---------------------------------------------------------------------------
+typedef float sf4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 mc_h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 mc_b2_t __attribute__((ext_vector_type(2)));
+
+template <int DT>
+struct McTypes;
+template <>
+struct McTypes<1> {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    static constexpr uint32_t one = 0x3C00u;  // 1.0 as fp16
+    static __device__ __forceinline__ sf4_t mfma(v8 a, v8 b, sf4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct McTypes<2> {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    static constexpr uint32_t one = 0x3F80u;  // 1.0 as bf16
+    static __device__ __forceinline__ sf4_t mfma(v8 a, v8 b, sf4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+constexpr int kMcVectors = 16;  // vectors per wave pass (one MFMA column each)
+// staged piece bytes (1 for BITS <= 2, else 2) and the padded row of a vector
+constexpr int mc_piece_bytes(int bits) { return bits <= 2 ? 1 : 2; }
+constexpr int mc_row_bytes(int d, int bits) { return d / 4 * mc_piece_bytes(bits) + 16; }
+constexpr int mc_stage_dw(int d, int bits) { return kMcVectors * mc_row_bytes(d, bits) / 4; }
+
+template <int D, int BITS, int DT>
+__device__ __forceinline__ void encode_rows_mc(const EncodeArgs& a, const uint2* qtab, uint32_t* stage_all,
+                                               int64_t block, int64_t nblocks) {
+    static_assert(D == 128 || D == 256, "matrix-core transform at d = 128 and 256");
+    static_assert(DT == 1 || DT == 2, "16-bit input");
+    using T = McTypes<DT>;
+    typedef typename T::v8 v8;
+    constexpr int NS = D / 32;                   // K steps
+    constexpr int NR = D / 16;                   // output row blocks
+    constexpr int PB = mc_piece_bytes(BITS);     // staged bytes per piece (4 codes)
+    constexpr int RB = mc_row_bytes(D, BITS);    // staged row of one vector
+    constexpr int QP = D / 16;                   // pieces per lane after the exchange
+    constexpr int QW = D / 4 * BITS / 32;        // code dwords per lane
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    uint8_t* stage = reinterpret_cast<uint8_t*>(stage_all + (threadIdx.x >> 6) * mc_stage_dw(D, BITS));
+
+    // A operands (see above): base[e] = (-1)^popcount(m & (8 (q & 1) + e)) for
+    // A row m = n; the odd-r copy is signed by (-1)^(q >> 1)
+    uint32_t ae[4], ao[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = 8 * (q & 1) + 2 * e2 + h;
+            const uint32_t neg = (uint32_t)(__builtin_popcount(n & k) & 1);
+            w |= (T::one | (neg << 15)) << (16 * h);
+        }
+        ae[e2] = w;
+        ao[e2] = w ^ ((q >> 1) ? 0x80008000u : 0u);
+    }
+    const v8 A[4] = {__builtin_bit_cast(v8, make_uint4(ae[0], ae[1], ae[2], ae[3])),
+                     __builtin_bit_cast(v8, make_uint4(ae[0] ^ 0x80008000u, ae[1] ^ 0x80008000u,
+                                                       ae[2] ^ 0x80008000u, ae[3] ^ 0x80008000u)),
+                     __builtin_bit_cast(v8, make_uint4(ao[0], ao[1], ao[2], ao[3])),
+                     __builtin_bit_cast(v8, make_uint4(ao[0] ^ 0x80008000u, ao[1] ^ 0x80008000u,
+                                                       ao[2] ^ 0x80008000u, ao[3] ^ 0x80008000u))};
+    // the D sign flip of this lane's dims 32 s + 8 q .. + 7, per step
+    uint32_t flip[NS][4];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) half_sign_masks((a.c.sign_mask[st] >> (8 * q)) & 0xFFu, flip[st]);
+    const int64_t wave = (block * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = (nblocks * blockDim.x) >> 6;
+    // the 16-byte pieces of this lane for the pass at `base` (rows past the
+    // end re-read the last one and are never stored)
+    auto load = [&](int64_t base, uint4 (&x)[NS]) __attribute__((always_inline)) {
+        int64_t rl = base + n;
+        rl = rl < a.n ? rl : a.n - 1;
+        const char* src = static_cast<const char*>(a.x) + (rl * a.x_stride + 8 * q) * 2;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) x[st] = ld_stream4(src + 64 * st);
+    };
+    uint4 x[NS];
+    if (wave * kMcVectors < a.n) load(wave * kMcVectors, x);
+    for (int64_t base = wave * kMcVectors; base < a.n; base += nwaves * kMcVectors) {
+        const int64_t row = base + n;
+        const bool valid = row < a.n;
+        // the next pass's loads go out before this pass's work
+        uint4 xn[NS];
+        const int64_t next = base + nwaves * kMcVectors;
+        if (next < a.n) load(next, xn);
+        float ss = 0.0f;
+        sf4_t acc[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r] = sf4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const uint32_t w[4] = {x[st].x ^ flip[st][0], x[st].y ^ flip[st][1], x[st].z ^ flip[st][2],
+                                   x[st].w ^ flip[st][3]};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (DT == 1) {
+                    const mc_h2_t h = __builtin_bit_cast(mc_h2_t, w[k]);
+                    ss = __builtin_amdgcn_fdot2(h, h, ss, false);
+                } else {
+                    const mc_b2_t h = __builtin_bit_cast(mc_b2_t, w[k]);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss, false);
+                }
+            }
+            const v8 b = __builtin_bit_cast(v8, make_uint4(w[0], w[1], w[2], w[3]));
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const int ai = 2 * (r & 1) + (__builtin_popcount((r >> 1) & st) & 1);
+                acc[r] = T::mfma(A[ai], b, acc[r]);
+            }
+        }
+        // ||x||^2 of vector n: its four quarters are lanes n + 16 q
+        ss += xor_lane<16>(ss);
+        ss += xor_lane<32>(ss);
+        const float nrm = __builtin_amdgcn_sqrtf(ss);
+        bool keep = true;
+        const int64_t orow = valid ? out_row(a, row, keep) : 0;
+        if (q == 0 && valid && keep) a.norms[orow] = norm_to_half(nrm);
+        // codes of y[16 r + 4 q + j], one piece of 4 codes per r, staged.  The
+        // bin coordinate takes 1/sc by v_rcp_f32 (1 ulp): it only picks the
+        // table bin, and every threshold lies 1/32 of a bin from a bin edge
+        const float sc = nrm > 0.0f ? nrm : 1.0f;
+        const float sn = a.c.qt_scale * __builtin_amdgcn_rcpf(sc);
+        const float topf = (float)(a.c.qt_n - 1);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            uint32_t piece = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float w = acc[r][j];
+                const float u = __builtin_amdgcn_fmed3f(fmaf(w, sn, a.c.qt_off), 0.0f, topf);
+                const uint2 ent = qtab[(uint32_t)u];
+                const uint32_t idx = ent.x + (w > as_f(ent.y) * sc ? 1u : 0u);
+                piece |= idx << (BITS * j);
+            }
+            uint8_t* dst = stage + n * RB + (4 * r + q) * PB;
+            if constexpr (PB == 1) *dst = (uint8_t)piece;
+            else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)piece;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // pieces QP q .. QP q + QP - 1 of vector n: its dims [D/4 q, D/4 (q + 1))
+        const uint8_t* srcp = stage + n * RB + QP * q * PB;
+        uint32_t cw[QW];
+        if constexpr (BITS == 4 || BITS == 2) {
+            // pieces of 16 (8) bits side by side are the packed code words
+#pragma unroll
+            for (int i = 0; i < QW; i += 2) {
+                const uint2 v = *reinterpret_cast<const uint2*>(srcp + 4 * i);
+                cw[i] = v.x;
+                cw[i + 1] = v.y;
+            }
+        } else {
+            // 4-bit pieces in bytes (1 bit) or 12-bit pieces in halfwords (3 bits)
+            constexpr int PBITS = 4 * BITS;
+#pragma unroll
+            for (int i = 0; i < QW; ++i) cw[i] = 0u;
+#pragma unroll
+            for (int p = 0; p < QP; ++p) {
+                const uint32_t v = PB == 1 ? (uint32_t)srcp[p] : (uint32_t)reinterpret_cast<const uint16_t*>(srcp)[p];
+                const int bit = PBITS * p;
+                cw[bit >> 5] |= v << (bit & 31);
+                if ((bit & 31) + PBITS > 32) cw[(bit >> 5) + 1] |= v >> (32 - (bit & 31));
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (valid && keep) {
+            uint32_t* rowp = reinterpret_cast<uint32_t*>(a.codes + orow * a.code_stride) + QW * q;
+#pragma unroll
+            for (int i = 0; i < QW; ++i) rowp[i] = cw[i];
+        }
+#pragma unroll
+        for (int st = 0; st < NS; ++st) x[st] = xn[st];
+    }
+}
+
+// MC: the matrix-core transform (encode_rows_mc; 16-bit input, d = 128 or 256,
+// one norm, the plain transform, a bin table), else the register transform.
+template <int D, int BITS, int DT, bool TAB, bool MC>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     __shared__ uint2 qtab[TAB ? kQTabMax : 1];
+    __shared__ uint32_t stage[MC ? 4 * mc_stage_dw(D, BITS) : 1];
     if constexpr (TAB) build_qtab<BITS>(a.c, qtab);
-    encode_rows<D, BITS, DT, TAB>(a, qtab, blockIdx.x, gridDim.x);
+    if constexpr (MC) encode_rows_mc<D, BITS, DT>(a, qtab, stage, blockIdx.x, gridDim.x);
+    else encode_rows<D, BITS, DT, TAB>(a, qtab, blockIdx.x, gridDim.x);
 }
 
 // Two encodes in one launch (a layer's K and V): blocks [0, kblocks) run job
 // k, the rest job v; each block switches on its codec's bit width (uniform
 // per block).  Neither job uses QJL.
-template <int D, int DT, bool TAB>
+template <int D, int DT, bool TAB, bool MC>
 __global__ __launch_bounds__(256) void encode_pair_kernel(EncodeArgs k, EncodeArgs v, int kblocks) {
     // each branch reads its own argument directly (selecting a reference to
     // one of the two would copy them to scratch)
     __shared__ uint2 qtab[TAB ? kQTabMax : 1];
+    __shared__ uint32_t stage[MC ? 4 * mc_stage_dw(D, 4) : 1];  // 4 bits need the most
     auto run = [&](const EncodeArgs& a, int64_t block, int64_t nblocks) __attribute__((always_inline)) {
         auto one = [&](auto bc) __attribute__((always_inline)) {
             constexpr int B = decltype(bc)::value;
             if constexpr (TAB) build_qtab<B>(a.c, qtab);
-            encode_rows<D, B, DT, TAB>(a, qtab, block, nblocks);
+            if constexpr (MC) encode_rows_mc<D, B, DT>(a, qtab, stage, block, nblocks);
+            else encode_rows<D, B, DT, TAB>(a, qtab, block, nblocks);
         };
         switch (a.c.bits) {
             case 1: one(std::integral_constant<int, 1>{}); break;
@@ -628,6 +842,26 @@ int encode_blocks(int64_t n, int d) {
     return (int)(need < 4096 ? need : 4096);
 }
 
+// The matrix-core encoder: shapes it is built for, codecs it serves, and its
+// blocks (4 waves of 16 vectors per pass, at most 4096 blocks).
+constexpr bool mc_dims(int d, int dt) { return (d == 128 || d == 256) && dt != 0; }
+bool mc_codec(const CodecArgs& c) { return c.rotation == TQ_ROT_WHT && c.norm_blocks == 1 && c.qt_n > 0; }
+// One resident round of blocks (compute units x resident blocks of the
+// kernel, cached per kernel): each wave then loops over several passes and
+// its next pass's loads overlap this pass's work.
+template <auto Kernel>
+int mc_blocks(int64_t n) {
+    static std::atomic<int> per_cu{0};
+    int pc = per_cu.load(std::memory_order_relaxed);
+    if (pc <= 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, Kernel, 256, 0) != hipSuccess || pc <= 0) pc = 4;
+        per_cu.store(pc, std::memory_order_relaxed);
+    }
+    const int64_t need = (n + 4 * kMcVectors - 1) / (4 * kMcVectors);
+    const int64_t cap = (int64_t)device_cus() * pc;
+    return (int)(need < cap ? need : cap);
+}
+
 template <int D, int BITS, int DT>
 hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t s) {
     if constexpr (D > 256) {
@@ -646,10 +880,19 @@ hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((encode_qjl_kernel<D, BITS, DT>), dim3(grid), dim3(256), 0, s, a);
     }
     if (a.c.qjl_m == 0) {
+        if constexpr (mc_dims(D, DT)) {
+            if (mc_codec(a.c)) {
+                constexpr auto kern = encode_kernel<D, BITS, DT, true, true>;
+                hipLaunchKernelGGL(kern, dim3(mc_blocks<kern>(a.n)), dim3(256), 0, s, a);
+                return hipGetLastError();
+            }
+        }
         if (a.c.qt_n > 0)
-            hipLaunchKernelGGL((encode_kernel<D, BITS, DT, true>), dim3(encode_blocks(a.n, D)), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((encode_kernel<D, BITS, DT, true, false>), dim3(encode_blocks(a.n, D)), dim3(256), 0, s,
+                               a);
         else
-            hipLaunchKernelGGL((encode_kernel<D, BITS, DT, false>), dim3(encode_blocks(a.n, D)), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((encode_kernel<D, BITS, DT, false, false>), dim3(encode_blocks(a.n, D)), dim3(256), 0,
+                               s, a);
     }
     return hipGetLastError();
 }
@@ -693,11 +936,23 @@ hipError_t launch_decode_b(const DecodeArgs& a, hipStream_t s) {
 
 template <int D, int DT>
 static hipError_t launch_pair_d(const EncodeArgs& k, const EncodeArgs& v, hipStream_t s) {
+    if constexpr (mc_dims(D, DT)) {
+        if (mc_codec(k.c) && mc_codec(v.c)) {
+            // the K and V jobs share one resident round in proportion to their rows
+            constexpr auto kern = encode_pair_kernel<D, DT, true, true>;
+            int all = mc_blocks<kern>(k.n + v.n);
+            all = all < 2 ? 2 : all;
+            int kb = (int)((int64_t)all * k.n / (k.n + v.n));
+            kb = kb < 1 ? 1 : (kb > all - 1 ? all - 1 : kb);  // each job gets at least one block
+            hipLaunchKernelGGL(kern, dim3(all), dim3(256), 0, s, k, v, kb);
+            return hipGetLastError();
+        }
+    }
     const int kb = encode_blocks(k.n, D), vb = encode_blocks(v.n, D);
     if (k.c.qt_n > 0 && v.c.qt_n > 0)
-        hipLaunchKernelGGL((encode_pair_kernel<D, DT, true>), dim3(kb + vb), dim3(256), 0, s, k, v, kb);
+        hipLaunchKernelGGL((encode_pair_kernel<D, DT, true, false>), dim3(kb + vb), dim3(256), 0, s, k, v, kb);
     else
-        hipLaunchKernelGGL((encode_pair_kernel<D, DT, false>), dim3(kb + vb), dim3(256), 0, s, k, v, kb);
+        hipLaunchKernelGGL((encode_pair_kernel<D, DT, false, false>), dim3(kb + vb), dim3(256), 0, s, k, v, kb);
     return hipGetLastError();
 }
 
