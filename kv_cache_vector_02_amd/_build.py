@@ -2,7 +2,9 @@
 
 Every .hip file under csrc/ is compiled to an object with hipcc (in parallel),
 then linked into kv_cache_vector_02_amd/libtq.so.  Packed-FP32 instruction
-selection is disabled for all device code.
+selection is disabled for all device code.  csrc/tq_pycall.c, the CPython
+argument marshalling of the per-step calls, is built with gcc into the
+package's _tqcall extension module.
 """
 from __future__ import annotations
 
@@ -11,6 +13,7 @@ import glob
 import os
 import subprocess
 import sys
+import sysconfig
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -18,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
+PYCALL_SRC = os.path.join(CSRC, "tq_pycall.c")
+PYCALL = os.path.join(PKG, "_tqcall" + (sysconfig.get_config_var("EXT_SUFFIX") or ".so"))
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -64,7 +69,20 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_pycall()
     return LIB
+
+
+def build_pycall() -> str:
+    """The _tqcall extension (plain C against the CPython API; it does not link libtq)."""
+    tmp = PYCALL + ".tmp"
+    cmd = [os.environ.get("CC", "gcc"), "-O2", "-std=c11", "-Wall", "-Werror", "-shared", "-fPIC",
+           f"-I{sysconfig.get_paths()['include']}", f"-I{INCLUDE}", PYCALL_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building {os.path.basename(PYCALL)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PYCALL)
+    return PYCALL
 
 
 if __name__ == "__main__":

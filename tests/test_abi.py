@@ -441,3 +441,49 @@ def test_codebook_opts_errors():
     c.rotation = tq.TQ_ROT_DOUBLE
     assert tq.raw_call("tq_encode", ctypes.byref(c), FAKE, 0, 4, 128, FAKE, 48, FAKE, None, None, None,
                        None) == tq.TQ_EUNSUPPORTED
+
+
+def test_fast_marshalling_returns_the_library_codes():
+    """The _tqcall module is built and bound to the loaded library, and its
+    per-step calls return what the same calls through ctypes return, for
+    arguments the library rejects (or accepts with nothing to launch) before
+    any device work."""
+    assert tq._tqcall is not None, "the _tqcall extension is not built"
+    assert tq._fast_lib is tq._lib
+    f = tq._tqcall
+    c, cq = tq.tq_codebook(3, 128, 0), tq.tq_codebook(3, 128, 0, 128)
+    ca, cqa = ctypes.addressof(c), ctypes.addressof(cq)
+    P = FAKE.value
+    enc_cases = [
+        (0, P, 0, 4, 128, P, 48, P, None, None, None, None),          # NULL codec
+        (ca, P, 7, 4, 128, P, 48, P, None, None, None, None),         # dtype
+        (ca, P, 0, -1, 128, P, 48, P, None, None, None, None),        # n < 0
+        (ca, P, 0, 0, 128, P, 48, P, None, None, None, None),         # n = 0
+        (ca, P + 4, 0, 4, 128, P, 48, P, None, None, None, None),     # misaligned rows
+        (ca, P, 0, 4, 128, P, 46, P, None, None, None, None),         # code stride
+        (cqa, P, 0, 4, 128, P, 48, P, None, P, P, None),              # QJL without S
+    ]
+    refs = {0: None, ca: ctypes.byref(c), cqa: ctypes.byref(cq)}
+    for a in enc_cases:
+        want = tq.raw_call("tq_encode", refs[a[0]], *a[1:])
+        assert f.encode(*a) == want, a
+    c4 = tq.tq_codebook(4, 128, 0)
+    c4a = ctypes.addressof(c4)
+    kv_cases = [(-1, 128, 64), (0, 128, 64), (10, 100, 64), (10, 128, 60)]
+    for n, stride, kcs in kv_cases:
+        a = (c4a, c4a, P, P, 1, n, stride, P, kcs, P, P, 64, P, None, None, None, None)
+        want = tq.raw_call("tq_encode_kv", ctypes.byref(c4), ctypes.byref(c4), *a[2:])
+        assert f.encode_kv(*a) == want, (n, stride, kcs)
+    kc, vc = tq.tq_codebook(4, 128, 0), tq.tq_codebook(2, 128, 0)
+    ws = tq.tq_attn_workspace_bytes(kc, vc, 2, 14, 2, 1000)
+    for hq, hkv, cap, wsb in ((14, 3, 1000, ws), (14, 2, 0, ws), (14, 2, 1000, ws - 1)):
+        a = (ctypes.addressof(kc), ctypes.addressof(vc), P, 1, 2, hq, hkv, P, cap, P, P, None, None, None, P, P, 0.1,
+             P, P, wsb, None)
+        want = tq.raw_call("tq_attn_decode", ctypes.byref(kc), ctypes.byref(vc), *a[2:16], ctypes.c_float(0.1),
+                           *a[17:])
+        assert want != tq.TQ_OK
+        assert f.attn_decode(*a) == want, (hq, hkv, cap, wsb)
+    with pytest.raises(TypeError):
+        f.encode(ca, P)  # wrong argument count
+    with pytest.raises(OverflowError):
+        f.encode(ca, P, 1 << 40, 4, 128, P, 48, P, None, None, None, None)  # dtype beyond a C int
