@@ -421,6 +421,35 @@ __device__ __forceinline__ void fetch_v(uint32_t (&rv)[C::VTW], uint32_t& rn, ui
     if constexpr (QJL) rg = ld_stream_u16(gmb + 2u * tl);
 }
 
+// QJL sign bytes of sub-tiles 0..3: token t0 + 16 j + n, the m/32 bytes of
+// lane group grp (projections [m/4 grp, m/4 (grp + 1))), clamped like
+// fetch_k.  Rows of m/8 bytes are only 4-byte aligned: dword loads at most.
+__device__ __forceinline__ void fetch_q(uint32_t (&rq)[4][2], const uint8_t* qb, int m, uint32_t t0, uint32_t last,
+                                        int n, int grp) {
+    const uint32_t gbytes = (uint32_t)m >> 5, row = (uint32_t)m >> 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t t = t0 + 16 * j + n;
+        t = t < last ? t : last;
+        const uint8_t* p = qb + t * row + grp * gbytes;
+        if (gbytes == 8 || gbytes == 4) {
+            rq[j][0] = ld_stream1(p);
+            rq[j][1] = gbytes == 8 ? ld_stream1(p + 4) : 0u;
+        } else if (gbytes == 2) {
+            rq[j][0] = ld_stream_u16(p);
+            rq[j][1] = 0u;
+        } else {
+            // 1, 3, 5, 6 or 7 bytes (m = 32 or an odd multiple of 32): byte loads
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int b = 0; b < 7; ++b)
+                if ((uint32_t)b < gbytes) w[b >> 2] |= (uint32_t)__builtin_nontemporal_load(p + b) << (8 * (b & 3));
+            rq[j][0] = w[0];
+            rq[j][1] = w[1];
+        }
+    }
+}
+
 // Query rows.  A sequence carries ncols query columns (its last ncols tokens,
 // already in the cache) of hq heads; the rows of kv head kvh are its g heads
 // in each column, vl = c * g + j for column c and head kvh * g + j, and a
@@ -513,9 +542,13 @@ void split_kernel(AttnArgs a) {
     constexpr int KBUF = KDB ? 2 : 1;  // K code buffers: with two, a tile's K codes are loaded one tile ahead
     uint32_t rk[KBUF][4 * C::GW];
     uint32_t rv[C::VTW], rn = 0, rg = 0, rv2 = 0;
+    // QJL: the sign bytes of a tile, loaded a whole tile ahead (see kphase)
+    uint32_t rq[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
+    const uint8_t* qjb = QJL ? a.k_qjl + kvrow * (m >> 3) : nullptr;
     if (t0 < t_end) {
         fetch_k<C>(rk[0], kcodes, (uint32_t)t0, last, n, grp);
         fetch_v<C, QJL>(rv, rn, rg, rv2, vcodes, knb, vnb, gmb, (uint32_t)t0, last, lane, nbk, nbv);
+        if constexpr (QJL) fetch_q(rq, qjb, m, (uint32_t)t0, last, n, grp);
     }
 
     // centroids once into LDS, then every table row is written as 16-byte
@@ -779,18 +812,24 @@ void split_kernel(AttnArgs a) {
         });
         if constexpr (!KDB) fetch_k<C>(rk[cur], kcodes, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
         if constexpr (QJL) {
-            // A = 16*gamma*(+-1) of token 16j + n (exact in half); same accumulators
-            const int gbytes = m >> 5;
+            // A = 16*gamma*(+-1) of token 16j + n (exact in half); same
+            // accumulators.  The sign bytes came with the previous tile; the
+            // next tile's go out once these are used.
+            const int nks = m >> 5;
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
-                int t = t0 + 16 * j + n;
-                t = t < t_end - 1 ? t : t_end - 1;
                 const _Float16 g16 = (_Float16)(16.0f * gml[16 * j + n]);
-                const uint8_t* sp = a.k_qjl + (kvrow + t) * (m >> 3) + grp * gbytes;
-                for (int ks = 0; ks < (m >> 5); ++ks) {
-                    const half8_t asg = as_half8(sigt[sp[ks]]) * g16;
-                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asg, as_half8(qjlb[ks * 64 + lane]), sacc[j], 0, 0, 0);
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) {
+                    if (ks < nks) {
+                        const uint32_t byte = (rq[j][ks >> 2] >> (8 * (ks & 3))) & 0xFFu;
+                        const half8_t asg = as_half8(sigt[byte]) * g16;
+                        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asg, as_half8(qjlb[ks * 64 + lane]), sacc[j],
+                                                                         0, 0, 0);
+                    }
                 }
             }
+            fetch_q(rq, qjb, m, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
         }
         // column h + 8 holds the q_lo part of head h: add the two halves of each row
         if constexpr (!R16) {
