@@ -558,7 +558,8 @@ def variants_leg(tq, torch, synth, steps, warmup):
       * head_dim 256 with one norm per 128-half, K3/V3, 7:1 GQA, on the
         vector-ALU wide kernel;
       * head_dim 256 with one norm, K4/V3, 7:1 GQA, on the scan (4-wave blocks);
-      * head_dim 128, K4/V2, 16:1 GQA, on the scan's 16-row blocks."""
+      * head_dim 128, K4/V2, 16:1 GQA, on the scan's 16-row blocks;
+      * head_dim 128, K3 with Gaussian QJL signs (m = 128) / V3, 7:1 GQA."""
     out = {}
     cases = (
         ("double_wht_d64", dict(B=16, Hkv=8, g=8, ctx=32768, d=64, kb=4, vb=3, rot=tq.TQ_ROT_DOUBLE, nb=1),
@@ -571,10 +572,14 @@ def variants_leg(tq, torch, synth, steps, warmup):
          "decode, batch 16, 28 query heads / 4 kv heads, d=256, context 16384, K4/V3"),
         ("gqa16_d128", dict(B=16, Hkv=4, g=16, ctx=32768, d=128, kb=4, vb=2, rot=tq.TQ_ROT_WHT, nb=1),
          "decode, batch 16, 64 query heads / 4 kv heads (16:1), d=128, context 32768, K4/V2"),
+        ("qjl_d128", dict(B=16, Hkv=4, g=7, ctx=32768, d=128, kb=3, vb=3, rot=tq.TQ_ROT_WHT, nb=1, m=128),
+         "decode, batch 16, 28 query heads / 4 kv heads, d=128, context 32768, K3 + QJL signs (m=128) / V3"),
     )
     for name, c, desc in cases:
         B, Hkv, g, ctx, d = c["B"], c["Hkv"], c["g"], c["ctx"], c["d"]
-        kc = tq.tq_codebook_opts(c["kb"], d, 5, tq.TQ_RES_NONE, 0, c["rot"], c["nb"])
+        m = c.get("m", 0)
+        S = synth.qjl_projection(m, d, seed=8).cuda() if m else None
+        kc = tq.tq_codebook_opts(c["kb"], d, 5, tq.TQ_RES_QJL if m else tq.TQ_RES_NONE, m, c["rot"], c["nb"])
         vc = tq.tq_codebook_opts(c["vb"], d, 5, tq.TQ_RES_NONE, 0, c["rot"], c["nb"])
         nt = (c["nb"],) if c["nb"] > 1 else ()
         caches = []
@@ -583,11 +588,16 @@ def variants_leg(tq, torch, synth, steps, warmup):
                   "k_norms": torch.empty((B, Hkv, ctx) + nt, dtype=torch.float16, device="cuda"),
                   "v_codes": torch.empty(B, Hkv, ctx, vc.code_bytes, dtype=torch.uint8, device="cuda"),
                   "v_norms": torch.empty((B, Hkv, ctx) + nt, dtype=torch.float16, device="cuda")}
+            if m:
+                cc["k_qjl"] = torch.empty(B, Hkv, ctx, m // 8, dtype=torch.uint8, device="cuda")
+                cc["k_gamma"] = torch.empty(B, Hkv, ctx, dtype=torch.float16, device="cuda")
             for b in range(B):
                 k, v = synth.kv_block(Hkv, ctx, d, 7000 + 100 * r + b, device="cuda", dtype=torch.float16)
                 tq.tq_encode_kv(kc, vc, k.view(-1, d), v.view(-1, d), cc["k_codes"][b].view(-1, kc.code_bytes),
                                 cc["k_norms"][b].reshape(-1), cc["v_codes"][b].view(-1, vc.code_bytes),
-                                cc["v_norms"][b].reshape(-1))
+                                cc["v_norms"][b].reshape(-1), S,
+                                cc["k_qjl"][b].view(-1, m // 8) if m else None,
+                                cc["k_gamma"][b].reshape(-1) if m else None)
             caches.append(cc)
         q = synth.normal((B, Hkv * g, d), seed=7500, dtype=torch.float16, device="cuda")
         ctx_len = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
@@ -595,13 +605,13 @@ def variants_leg(tq, torch, synth, steps, warmup):
         ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, B, Hkv * g, Hkv, ctx))
         scale = 1.0 / math.sqrt(d)
 
-        def step(i, ev=None, caches=caches, kc=kc, vc=vc, q=q, ctx_len=ctx_len, o_=o_, ws=ws, scale=scale):
+        def step(i, ev=None, caches=caches, kc=kc, vc=vc, q=q, ctx_len=ctx_len, o_=o_, ws=ws, scale=scale, S=S):
             cc = caches[i % 2]
             tq.tq_attn_decode(kc, vc, q, ctx_len, cc["k_codes"], cc["k_norms"], cc["v_codes"], cc["v_norms"],
-                              scale, o_, ws)
+                              scale, o_, ws, cc.get("k_qjl"), cc.get("k_gamma"), S)
 
         ms = timed_loop(step, steps, max(warmup // 4, 1), torch)
-        per = (kc.code_bytes + 2 * c["nb"]) + (vc.code_bytes + 2 * c["nb"])
+        per = (kc.code_bytes + 2 * c["nb"]) + (vc.code_bytes + 2 * c["nb"]) + (m // 8 + 2 if m else 0)
         cache_bytes = B * Hkv * ctx * per
         out[name] = {"workload": desc, "ms_per_step": ms, "bytes_per_token_head": per, "cache_bytes": cache_bytes,
                      "gbs": cache_bytes / (ms * 1e-3) / 1e9,
@@ -936,7 +946,7 @@ def main():
         res["search"] = search_leg(tq, torch, synth, args.steps, args.warmup)
         log(f"search: {res['search']['ms_per_call']:.2f} ms/call, {res['search']['tflops']:.1f} TFLOP/s")
     if "variants" in legs:
-        log("variants leg (d=64 double transform, block norms at d=512 and 256, d=256, 16:1 GQA)")
+        log("variants leg (d=64 double transform, block norms at d=512 and 256, d=256, 16:1 GQA, QJL keys)")
         res["variants"] = variants_leg(tq, torch, synth, args.steps, args.warmup)
         log("variants: " + ", ".join(f"{k} {v['gbs']:.0f} GB/s" for k, v in res["variants"].items()))
     if "quality" in legs:
