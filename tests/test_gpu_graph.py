@@ -1,6 +1,7 @@
-"""tq_encode / tq_encode_kv captured in a HIP graph: every replay, with the
-program's own eager work and synchronisations between replays, writes the
-bytes that eager calls write on the same inputs."""
+"""tq_encode / tq_encode_kv and tq_attn_decode / tq_attn_decode_noalloc
+captured in a HIP graph: every replay, with the program's own eager work and
+synchronisations between replays, writes the bytes that eager calls write on
+the same inputs."""
 import pytest
 import torch
 
@@ -75,3 +76,51 @@ def test_encode_graph_replays_match_eager(tq, kbits, vbits, n):
                 for key in ("codes", "norms"):
                     assert torch.equal(got[key].view(torch.uint8), want[key].view(torch.uint8)), (rep, key)
     del g
+
+
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_decode_graph_replays_match_eager(tq, noalloc):
+    """tq_attn_decode (with a workspace) and tq_attn_decode_noalloc (the
+    library's static scratch) captured in a HIP graph: every replay, after new
+    queries are written eagerly, gives the bytes of an eager call."""
+    from tests.test_gpu_attn import _fill_gpu_cache
+    B, Hkv, g, cap, d = 2, 2, 7, 3000, 128
+    Hq = Hkv * g
+    kc, vc = tq.tq_codebook(4, d, 2), tq.tq_codebook(2, d, 2)
+    K, V = synth.decode_cache_inputs(B, Hkv, cap, d, device="cuda", seed_base=91)
+    dev = _fill_gpu_cache(tq, kc, vc, K, V)
+    del K, V
+    q = torch.empty(B, Hq, d, dtype=torch.float16, device="cuda")
+    ctx = torch.tensor([cap, 1777], dtype=torch.int32, device="cuda")
+    ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, B, Hq, Hkv, cap))
+    out_g = torch.empty(B, Hq, d, device="cuda")
+    out_e = torch.empty(B, Hq, d, device="cuda")
+
+    def run(out):
+        args = (kc, vc, q, ctx, dev["k_codes"], dev["k_norms"], dev["v_codes"], dev["v_norms"], 0.09, out)
+        if noalloc:
+            tq.tq_attn_decode_noalloc(*args)
+        else:
+            tq.tq_attn_decode(*args, ws)
+
+    q.copy_(synth.normal((B, Hq, d), seed=1, dtype=torch.float16))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # first calls (launch plan, scratch address) outside capture
+        run(out_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        run(out_g)
+    for rep in range(4):
+        q.copy_(synth.normal((B, Hq, d), seed=10 + rep, dtype=torch.float16))  # eager work between replays
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        run(out_e)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out_g).all(), rep
+        assert torch.equal(out_g, out_e), rep
+    del gr
