@@ -315,8 +315,8 @@ __device__ __forceinline__ void encode_rows(const EncodeArgs& a, const uint2* qt
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit input with the transform on the matrix cores (d = 128 and 256, one
-// norm, the plain transform): y = H D x is a dense contraction of each vector
+// 16-bit input with the transform on the matrix cores (d = 128 and 256, the
+// plain transform; one norm, or two at d = 256): y = H D x is a dense contraction of each vector
 // with the +-1 matrix H, exact in its products for fp16 and bf16 input, so a
 // wave runs it as v_mfma_f32_16x16x32_{f16,bf16} with its 16 vectors as the
 // 16 columns.
@@ -456,18 +456,43 @@ __device__ __forceinline__ void encode_rows_mc(const EncodeArgs& a, const uint2*
         // ||x||^2 of vector n: its four quarters are lanes n + 16 q
         ss += xor_lane<16>(ss);
         ss += xor_lane<32>(ss);
-        const float nrm = __builtin_amdgcn_sqrtf(ss);
         bool keep = true;
         const int64_t orow = valid ? out_row(a, row, keep) : 0;
-        if (q == 0 && valid && keep) a.norms[orow] = norm_to_half(nrm);
+        // the threshold scale of each half of y (rows r < NR/2 and r >= NR/2)
+        // and the norms stored: one norm, ||x||, or with two norm blocks
+        // (d = 256) per half h the stored sqrt(||y_h||^2 / d) and the scale
+        // sqrt(2 ||y_h||^2 / d)
+        float scl[2];
+        if (D == 256 && a.c.norm_blocks == 2) {
+            float sh[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sh[r / (NR / 2)] = fmaf(acc[r][j], acc[r][j], sh[r / (NR / 2)]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                sh[h] += xor_lane<16>(sh[h]);
+                sh[h] += xor_lane<32>(sh[h]);
+                scl[h] = __builtin_amdgcn_sqrtf(sh[h] * (2.0f / (float)D));
+            }
+            if (q < 2 && valid && keep) a.norms[orow * 2 + q] = norm_to_half(__builtin_amdgcn_sqrtf(sh[q] * (1.0f / (float)D)));
+        } else {
+            scl[0] = scl[1] = __builtin_amdgcn_sqrtf(ss);
+            if (q == 0 && valid && keep) a.norms[orow] = norm_to_half(scl[0]);
+        }
         // codes of y[16 r + 4 q + j], one piece of 4 codes per r, staged.  The
         // bin coordinate takes 1/sc by v_rcp_f32 (1 ulp): it only picks the
         // table bin, and every threshold lies 1/32 of a bin from a bin edge
-        const float sc = nrm > 0.0f ? nrm : 1.0f;
-        const float sn = a.c.qt_scale * __builtin_amdgcn_rcpf(sc);
+        float scs[2], sns[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            scs[h] = scl[h] > 0.0f ? scl[h] : 1.0f;
+            sns[h] = a.c.qt_scale * __builtin_amdgcn_rcpf(scs[h]);
+        }
         const float topf = (float)(a.c.qt_n - 1);
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
+            const float sc = scs[r / (NR / 2)], sn = sns[r / (NR / 2)];
             uint32_t piece = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -522,7 +547,7 @@ __device__ __forceinline__ void encode_rows_mc(const EncodeArgs& a, const uint2*
 }
 
 // MC: the matrix-core transform (encode_rows_mc; 16-bit input, d = 128 or 256,
-// one norm, the plain transform, a bin table), else the register transform.
+// the plain transform, a bin table), else the register transform.
 template <int D, int BITS, int DT, bool TAB, bool MC>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     __shared__ uint2 qtab[TAB ? kQTabMax : 1];
@@ -845,7 +870,9 @@ int encode_blocks(int64_t n, int d) {
 // The matrix-core encoder: shapes it is built for, codecs it serves, and its
 // blocks (4 waves of 16 vectors per pass, at most 4096 blocks).
 constexpr bool mc_dims(int d, int dt) { return (d == 128 || d == 256) && dt != 0; }
-bool mc_codec(const CodecArgs& c) { return c.rotation == TQ_ROT_WHT && c.norm_blocks == 1 && c.qt_n > 0; }
+bool mc_codec(const CodecArgs& c) {
+    return c.rotation == TQ_ROT_WHT && (c.norm_blocks == 1 || c.d == 256) && c.qt_n > 0;
+}
 // One resident round of blocks (compute units x resident blocks of the
 // kernel, cached per kernel): each wave then loops over several passes and
 // its next pass's loads overlap this pass's work.

@@ -105,6 +105,37 @@ def test_block_norms_encode_decode(tq, d, nb, bits):
     check_encode_decode(tq, x, bits, 51, torch.bfloat16 if bits == 3 else torch.float32, norm_blocks=nb)
 
 
+@pytest.mark.parametrize("bits", [1, 2, 4])
+def test_block_norms_encode_16bit_input(tq, bits):
+    """Two norm blocks at d = 256 from fp16 input (the matrix-core transform:
+    per-half norms from the rotated vector it holds), ragged row count."""
+    x = synth.normal((1001, 256), seed=640 + bits)
+    x[:, 200:] *= 3.0
+    check_encode_decode(tq, x, bits, 53, torch.float16, norm_blocks=2)
+
+
+def test_block_norms_encode_kv_matches_two_encodes(tq):
+    """tq_encode_kv with two-norm-block codecs (K 4-bit, V 2-bit, d = 256,
+    bf16) writes the bytes of tq_encode on K and on V."""
+    n, d = 2500, 256
+    k, v = synth.kv_block(1, n, d, seed=650, dtype=torch.bfloat16)
+    k, v = k[0].cuda(), v[0].cuda()
+    _, kc = codecs(tq, 4, d, 54, norm_blocks=2)
+    _, vc = codecs(tq, 2, d, 54, norm_blocks=2)
+
+    def planes(c):
+        return (torch.full((n, c.code_bytes), 0xA5, dtype=torch.uint8, device="cuda"),
+                torch.zeros(n, 2, dtype=torch.float16, device="cuda"))
+
+    (fkc, fkn), (fvc, fvn), (skc, skn), (svc, svn) = planes(kc), planes(vc), planes(kc), planes(vc)
+    tq.tq_encode_kv(kc, vc, k, v, fkc, fkn.view(-1), fvc, fvn.view(-1))
+    tq.tq_encode(kc, k, skc, skn.view(-1))
+    tq.tq_encode(vc, v, svc, svn.view(-1))
+    torch.cuda.synchronize()
+    for a_, b_ in ((fkc, skc), (fvc, svc), (fkn, skn), (fvn, svn)):
+        assert torch.equal(a_.view(torch.uint8), b_.view(torch.uint8))
+
+
 def attn_case(tq, B, Hkv, g, cap, ctx_len, kbits, vbits, rotation, residual=o.RES_NONE, m=0, seed=0,
               qdtype=torch.float16):
     d = 64
