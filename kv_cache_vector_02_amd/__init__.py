@@ -164,7 +164,7 @@ def _bind_fast(lib) -> bool:
     def addr(name):
         return ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
-    _tqcall.bind(addr("tq_encode"), addr("tq_encode_kv"), addr("tq_attn_decode"))
+    _tqcall.bind(addr("tq_encode"), addr("tq_encode_kv"), addr("tq_attn_decode"), addr("tq_append"))
     _fast_lib = lib
     return True
 
@@ -237,6 +237,43 @@ def _qjl_rows(codec, n, qjl_S, qjl_bits, qjl_gamma, names=("qjl_S", "qjl_bits", 
 
 
 _raw_stream = torch._C._cuda_getCurrentRawStream
+_TWO_BYTE = (torch.float16, torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _mat(t, n, min_width, name, dtype=None):
+    """_rows of a per-step tensor in one pass over its shape and strides:
+    returns (address, row stride in elements); the caller checks the device
+    (_on_device) once every shape has been checked."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    shp, st = t.shape, t.stride()
+    if len(shp) != 2 or st[1] != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    if shp[0] != n or shp[1] < min_width:
+        raise ValueError(f"{name} must be [{n}][>= {min_width}], got {tuple(shp)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr(), st[0]
+
+
+def _halves(t, n, name):
+    """_vec of a norms plane (n contiguous 2-byte values): returns its address."""
+    if not isinstance(t, torch.Tensor) or t.dtype not in _TWO_BYTE:
+        raise ValueError(f"{name} must hold {n} contiguous 2-byte values")
+    shp = t.shape
+    if len(shp) == 1:
+        ok = shp[0] == n and (n <= 1 or t.stride(0) == 1)
+    else:
+        ok = t.numel() == n and t.is_contiguous()
+    if not ok:
+        raise ValueError(f"{name} must hold {n} contiguous 2-byte values")
+    return t.data_ptr()
+
+
+def _on_device(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("device tensor expected")
 
 
 def _stream(stream=None, like=None):
@@ -285,22 +322,29 @@ def tq_encode(codec: tq_codec, x: torch.Tensor, codes: torch.Tensor, norms: torc
               qjl_gamma: torch.Tensor | None = None, stream=None) -> None:
     """x [n][>=d] (fp32/fp16/bf16, last dim contiguous); codes [n][>= d*bits/8] uint8;
     norms [n] (2-byte dtype, half bits).  Row strides are taken from the tensors."""
-    if x.dim() != 2:
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be 2-D with contiguous rows")
     n = x.shape[0]
-    _rows(x, n, codec.d, "x")
-    _rows(codes, n, codec.code_bytes, "codes", torch.uint8)
-    _vec(norms, n * codec.norm_blocks, "norms")
-    _qjl_rows(codec, n, qjl_S, qjl_bits, qjl_gamma)
-    if _lib is _fast_lib:
-        rc = _tqcall.encode(ctypes.addressof(codec), _ptr(x), _DTYPES[x.dtype], n, x.stride(0), _ptr(codes),
-                            codes.stride(0), _ptr(norms), _ptr(qjl_S), _ptr(qjl_bits), _ptr(qjl_gamma),
-                            _stream(stream, x))
+    xp, xs = _mat(x, n, codec.d, "x")
+    cp, cs = _mat(codes, n, codec.code_bytes, "codes", torch.uint8)
+    npp = _halves(norms, n * codec.norm_blocks, "norms")
+    if codec.qjl_m:
+        _qjl_rows(codec, n, qjl_S, qjl_bits, qjl_gamma)
+    dt = _DTYPES.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"x must be float32, float16 or bfloat16, got {x.dtype}")
+    _on_device(x, codes, norms)
+    if codec.qjl_m:
+        qs, qb, qg = _ptr(qjl_S), _ptr(qjl_bits), _ptr(qjl_gamma)
     else:
-        rc = _lib.tq_encode(ctypes.byref(codec), _ptr(x), _DTYPES[x.dtype], n, x.stride(0), _ptr(codes),
-                            codes.stride(0), _ptr(norms), _ptr(qjl_S), _ptr(qjl_bits), _ptr(qjl_gamma),
-                            _stream(stream, x))
-    _check(rc, "tq_encode")
+        qs = qb = qg = None
+    st = _stream(stream, x)
+    if _lib is _fast_lib:
+        rc = _tqcall.encode(ctypes.addressof(codec), xp, dt, n, xs, cp, cs, npp, qs, qb, qg, st)
+    else:
+        rc = _lib.tq_encode(ctypes.byref(codec), xp, dt, n, xs, cp, cs, npp, qs, qb, qg, st)
+    if rc:
+        _check(rc, "tq_encode")
 
 
 def tq_encode_kv(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, k_codes: torch.Tensor,
@@ -309,28 +353,36 @@ def tq_encode_kv(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, k
                  k_qjl_gamma: torch.Tensor | None = None, stream=None) -> None:
     """tq_encode of keys and values in one call: k, v [n][>=d] of one dtype and
     row stride (last dim contiguous); codes [n][>= d*bits/8] uint8; norms [n]."""
-    if k.dim() != 2:
+    if not isinstance(k, torch.Tensor) or not isinstance(v, torch.Tensor) or k.dim() != 2:
         raise ValueError("k, v and the code planes must be 2-D with contiguous rows")
     if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
         raise ValueError("k and v must share shape, strides and dtype")
     n = k.shape[0]
-    _rows(k, n, kc.d, "k")
-    _rows(k_codes, n, kc.code_bytes, "k_codes", torch.uint8)
-    _rows(v_codes, n, vc.code_bytes, "v_codes", torch.uint8)
-    _vec(k_norms, n * kc.norm_blocks, "k_norms")
-    _vec(v_norms, n * vc.norm_blocks, "v_norms")
-    _qjl_rows(kc, n, qjl_S, k_qjl_bits, k_qjl_gamma, ("qjl_S", "k_qjl_bits", "k_qjl_gamma"))
-    if _lib is _fast_lib:
-        rc = _tqcall.encode_kv(ctypes.addressof(kc), ctypes.addressof(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], n,
-                               k.stride(0), _ptr(k_codes), k_codes.stride(0), _ptr(k_norms), _ptr(v_codes),
-                               v_codes.stride(0), _ptr(v_norms), _ptr(qjl_S), _ptr(k_qjl_bits), _ptr(k_qjl_gamma),
-                               _stream(stream, k))
+    kp, xs = _mat(k, n, kc.d, "k")
+    vp, _ = _mat(v, n, kc.d, "v")
+    kcp, kcs = _mat(k_codes, n, kc.code_bytes, "k_codes", torch.uint8)
+    vcp, vcs = _mat(v_codes, n, vc.code_bytes, "v_codes", torch.uint8)
+    knp = _halves(k_norms, n * kc.norm_blocks, "k_norms")
+    vnp = _halves(v_norms, n * vc.norm_blocks, "v_norms")
+    if kc.qjl_m:
+        _qjl_rows(kc, n, qjl_S, k_qjl_bits, k_qjl_gamma, ("qjl_S", "k_qjl_bits", "k_qjl_gamma"))
+    dt = _DTYPES.get(k.dtype)
+    if dt is None:
+        raise ValueError(f"k and v must be float32, float16 or bfloat16, got {k.dtype}")
+    _on_device(k, v, k_codes, k_norms, v_codes, v_norms)
+    if kc.qjl_m:
+        qs, qb, qg = _ptr(qjl_S), _ptr(k_qjl_bits), _ptr(k_qjl_gamma)
     else:
-        rc = _lib.tq_encode_kv(ctypes.byref(kc), ctypes.byref(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], n,
-                               k.stride(0), _ptr(k_codes), k_codes.stride(0), _ptr(k_norms), _ptr(v_codes),
-                               v_codes.stride(0), _ptr(v_norms), _ptr(qjl_S), _ptr(k_qjl_bits), _ptr(k_qjl_gamma),
-                               _stream(stream, k))
-    _check(rc, "tq_encode_kv")
+        qs = qb = qg = None
+    st = _stream(stream, k)
+    if _lib is _fast_lib:
+        rc = _tqcall.encode_kv(ctypes.addressof(kc), ctypes.addressof(vc), kp, vp, dt, n, xs, kcp, kcs, knp, vcp, vcs,
+                               vnp, qs, qb, qg, st)
+    else:
+        rc = _lib.tq_encode_kv(ctypes.byref(kc), ctypes.byref(vc), kp, vp, dt, n, xs, kcp, kcs, knp, vcp, vcs, vnp,
+                               qs, qb, qg, st)
+    if rc:
+        _check(rc, "tq_encode_kv")
 
 
 def tq_prefill(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, t0: int, k_codes: torch.Tensor,
@@ -370,26 +422,43 @@ def tq_append(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, pos:
     (device); cache planes [B][H][cap][d*bits/8] uint8 and norms [B][H][cap]
     (2-byte dtype), contiguous."""
     for t in (k, v, pos, k_codes, k_norms, v_codes, v_norms):
-        if not t.is_contiguous():
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous():
             raise ValueError("append tensors must be contiguous")
-    if k.dim() != 3 or k.shape != v.shape or k.dtype != v.dtype:
+    ks, kcs = k.shape, k_codes.shape
+    if len(ks) != 3 or ks != v.shape or k.dtype != v.dtype:
         raise ValueError("k and v must be [B][H][d] of one dtype")
-    if k_codes.dim() != 4 or k_codes.shape[:2] != k.shape[:2] or v_codes.shape[:3] != k_codes.shape[:3]:
+    if len(kcs) != 4 or kcs[:2] != ks[:2] or v_codes.shape[:3] != kcs[:3]:
         raise ValueError("cache planes must be [B][H][cap][row] matching k")
-    B, H = k.shape[0], k.shape[1]
-    cap = k_codes.shape[2]
-    _shape(k, (B, H, kc.d), "k")
+    B, H, cap = kcs[0], kcs[1], kcs[2]
+    if ks[2] != kc.d:
+        raise ValueError(f"k must have shape {(B, H, kc.d)}, got {tuple(ks)}")
     _shape(pos, (B,), "pos", torch.int32)
-    _shape(k_codes, (B, H, cap, kc.code_bytes), "k_codes", torch.uint8)
-    _shape(v_codes, (B, H, cap, vc.code_bytes), "v_codes", torch.uint8)
-    _shape(k_norms, _nshape(kc, (B, H, cap)), "k_norms", elem=2)
-    _shape(v_norms, _nshape(vc, (B, H, cap)), "v_norms", elem=2)
+    if kcs[3] != kc.code_bytes or k_codes.dtype != torch.uint8:
+        _shape(k_codes, (B, H, cap, kc.code_bytes), "k_codes", torch.uint8)
+    if v_codes.shape[3] != vc.code_bytes or v_codes.dtype != torch.uint8:
+        _shape(v_codes, (B, H, cap, vc.code_bytes), "v_codes", torch.uint8)
+    for t, c, name in ((k_norms, kc, "k_norms"), (v_norms, vc, "v_norms")):
+        if t.shape != _nshape(c, (B, H, cap)) or t.dtype not in _TWO_BYTE:
+            _shape(t, _nshape(c, (B, H, cap)), name, elem=2)
     if kc.qjl_m:
         _qjl_rows(kc, B * H * cap, qjl_S, k_qjl_bits, k_qjl_gamma, ("qjl_S", "k_qjl_bits", "k_qjl_gamma"))
         _shape(k_qjl_bits, (B, H, cap, kc.qjl_m // 8), "k_qjl_bits", torch.uint8)
-    _check(_lib.tq_append(ctypes.byref(kc), ctypes.byref(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], B, H, _ptr(pos),
-                          k_codes.shape[2], _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), _ptr(qjl_S),
-                          _ptr(k_qjl_bits), _ptr(k_qjl_gamma), _stream(stream, k)), "tq_append")
+    dt = _DTYPES.get(k.dtype)
+    if dt is None:
+        raise ValueError(f"k and v must be float32, float16 or bfloat16, got {k.dtype}")
+    _on_device(k, v, pos, k_codes, k_norms, v_codes, v_norms)
+    if kc.qjl_m:
+        qs, qb, qg = _ptr(qjl_S), _ptr(k_qjl_bits), _ptr(k_qjl_gamma)
+    else:
+        qs = qb = qg = None
+    args = (k.data_ptr(), v.data_ptr(), dt, B, H, pos.data_ptr(), cap, k_codes.data_ptr(), k_norms.data_ptr(),
+            v_codes.data_ptr(), v_norms.data_ptr(), qs, qb, qg, _stream(stream, k))
+    if _lib is _fast_lib:
+        rc = _tqcall.append(ctypes.addressof(kc), ctypes.addressof(vc), *args)
+    else:
+        rc = _lib.tq_append(ctypes.byref(kc), ctypes.byref(vc), *args)
+    if rc:
+        _check(rc, "tq_append")
 
 
 def tq_decode(codec: tq_codec, codes: torch.Tensor, norms: torch.Tensor, x_hat: torch.Tensor, stream=None) -> None:

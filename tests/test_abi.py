@@ -474,6 +474,21 @@ def test_fast_marshalling_returns_the_library_codes():
         a = (c4a, c4a, P, P, 1, n, stride, P, kcs, P, P, 64, P, None, None, None, None)
         want = tq.raw_call("tq_encode_kv", ctypes.byref(c4), ctypes.byref(c4), *a[2:])
         assert f.encode_kv(*a) == want, (n, stride, kcs)
+    c64 = tq.tq_codebook(2, 64, 0)
+    app_cases = [
+        (0, c4a, 0, 2, 4, P, 100),                          # NULL codec
+        (c4a, ctypes.addressof(c64), 0, 2, 4, P, 100),      # K and V head sizes differ
+        (c4a, c4a, 0, 0, 4, P, 100),                        # batch 0
+        (c4a, c4a, 0, 2, 4, P + 2, 100),                    # misaligned positions
+        (c4a, c4a, 0, 2, 4, P, 0),                          # no capacity
+        (c4a, c4a, 9, 2, 4, P, 100),                        # dtype
+    ]
+    refs4 = {0: None, c4a: ctypes.byref(c4), ctypes.addressof(c64): ctypes.byref(c64)}
+    for kca, vca, dt, B, H, pos, cap in app_cases:
+        a = (kca, vca, P, P, dt, B, H, pos, cap, P, P, P, P, None, None, None, None)
+        want = tq.raw_call("tq_append", refs4[kca], refs4[vca], *a[2:])
+        assert want != tq.TQ_OK
+        assert f.append(*a) == want, a
     kc, vc = tq.tq_codebook(4, 128, 0), tq.tq_codebook(2, 128, 0)
     ws = tq.tq_attn_workspace_bytes(kc, vc, 2, 14, 2, 1000)
     for hq, hkv, cap, wsb in ((14, 3, 1000, ws), (14, 2, 0, ws), (14, 2, 1000, ws - 1)):
