@@ -143,7 +143,7 @@ def _load():
 _lib = _load()
 LIB_PATH = _LIB_PATH
 
-# The per-step calls (tq_encode, tq_encode_kv, tq_attn_decode) go through the
+# The per-step calls (tq_encode, tq_encode_kv, tq_append, tq_attn_decode) go through the
 # _tqcall extension when it is built and bound to _lib: the same entry points,
 # with their arguments converted in C instead of by ctypes (about 0.5 us of
 # host time per call saved, 7-9 % of a small encode).  Without it ctypes
@@ -164,7 +164,10 @@ def _bind_fast(lib) -> bool:
     def addr(name):
         return ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
-    _tqcall.bind(addr("tq_encode"), addr("tq_encode_kv"), addr("tq_attn_decode"), addr("tq_append"))
+    try:
+        _tqcall.bind(addr("tq_encode"), addr("tq_encode_kv"), addr("tq_attn_decode"), addr("tq_append"))
+    except TypeError:  # a _tqcall built from older sources: keep ctypes
+        return False
     _fast_lib = lib
     return True
 
