@@ -240,7 +240,7 @@ def _qjl_rows(codec, n, qjl_S, qjl_bits, qjl_gamma, names=("qjl_S", "qjl_bits", 
 
 
 _raw_stream = torch._C._cuda_getCurrentRawStream
-_TWO_BYTE = (torch.float16, torch.bfloat16, torch.int16, torch.uint16)
+_TWO_BYTE = frozenset((torch.float16, torch.bfloat16, torch.int16, torch.uint16))
 
 
 def _mat(t, n, min_width, name, dtype=None):
@@ -265,7 +265,7 @@ def _halves(t, n, name):
         raise ValueError(f"{name} must hold {n} contiguous 2-byte values")
     shp = t.shape
     if len(shp) == 1:
-        ok = shp[0] == n and (n <= 1 or t.stride(0) == 1)
+        ok = shp[0] == n and t.is_contiguous()
     else:
         ok = t.numel() == n and t.is_contiguous()
     if not ok:
