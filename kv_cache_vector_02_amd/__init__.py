@@ -143,7 +143,8 @@ def _load():
 _lib = _load()
 LIB_PATH = _LIB_PATH
 
-# The per-step calls (tq_encode, tq_encode_kv, tq_append, tq_attn_decode) go through the
+# The per-step calls (tq_encode, tq_encode_kv, tq_prefill, tq_append,
+# tq_attn_decode) go through the
 # _tqcall extension when it is built and bound to _lib: the same entry points,
 # with their arguments converted in C instead of by ctypes (about 0.5 us of
 # host time per call saved, 7-9 % of a small encode).  Without it ctypes
@@ -165,7 +166,8 @@ def _bind_fast(lib) -> bool:
         return ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
     try:
-        _tqcall.bind(addr("tq_encode"), addr("tq_encode_kv"), addr("tq_attn_decode"), addr("tq_append"))
+        _tqcall.bind(addr("tq_encode"), addr("tq_encode_kv"), addr("tq_attn_decode"), addr("tq_append"),
+                     addr("tq_prefill"))
     except TypeError:  # a _tqcall built from older sources: keep ctypes
         return False
     _fast_lib = lib
@@ -396,25 +398,42 @@ def tq_prefill(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, t0:
     [H][cap][d*bits/8] uint8 and norms [H][cap] (2-byte dtype), contiguous (a
     slice [b] of a batched cache is); writes slots [t0, t0 + T) of every head."""
     for t in (k, v, k_codes, k_norms, v_codes, v_norms):
-        if not t.is_contiguous():
+        if not isinstance(t, torch.Tensor) or not t.is_contiguous():
             raise ValueError("prefill tensors must be contiguous")
-    if k.dim() != 3 or k.shape != v.shape or k.dtype != v.dtype:
+    ks, kcs = k.shape, k_codes.shape
+    if len(ks) != 3 or ks != v.shape or k.dtype != v.dtype:
         raise ValueError("k and v must be [H][T][d] of one dtype")
-    if k_codes.dim() != 3 or k_codes.shape[0] != k.shape[0] or v_codes.shape[:2] != k_codes.shape[:2]:
+    if len(kcs) != 3 or kcs[0] != ks[0] or v_codes.shape[:2] != kcs[:2]:
         raise ValueError("cache planes must be [H][cap][row] matching k")
-    H, T = k.shape[0], k.shape[1]
-    cap = k_codes.shape[1]
-    _shape(k, (H, T, kc.d), "k")
-    _shape(k_codes, (H, cap, kc.code_bytes), "k_codes", torch.uint8)
-    _shape(v_codes, (H, cap, vc.code_bytes), "v_codes", torch.uint8)
-    _shape(k_norms, _nshape(kc, (H, cap)), "k_norms", elem=2)
-    _shape(v_norms, _nshape(vc, (H, cap)), "v_norms", elem=2)
+    H, T, cap = ks[0], ks[1], kcs[1]
+    if ks[2] != kc.d:
+        raise ValueError(f"k must have shape {(H, T, kc.d)}, got {tuple(ks)}")
+    if kcs[2] != kc.code_bytes or k_codes.dtype != torch.uint8:
+        _shape(k_codes, (H, cap, kc.code_bytes), "k_codes", torch.uint8)
+    if v_codes.shape[2] != vc.code_bytes or v_codes.dtype != torch.uint8:
+        _shape(v_codes, (H, cap, vc.code_bytes), "v_codes", torch.uint8)
+    for t, c, name in ((k_norms, kc, "k_norms"), (v_norms, vc, "v_norms")):
+        if t.shape != _nshape(c, (H, cap)) or t.dtype not in _TWO_BYTE:
+            _shape(t, _nshape(c, (H, cap)), name, elem=2)
     if kc.qjl_m:
         _qjl_rows(kc, H * cap, qjl_S, k_qjl_bits, k_qjl_gamma, ("qjl_S", "k_qjl_bits", "k_qjl_gamma"))
         _shape(k_qjl_bits, (H, cap, kc.qjl_m // 8), "k_qjl_bits", torch.uint8)
-    _check(_lib.tq_prefill(ctypes.byref(kc), ctypes.byref(vc), _ptr(k), _ptr(v), _DTYPES[k.dtype], H, T, t0,
-                           k_codes.shape[1], _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), _ptr(qjl_S),
-                           _ptr(k_qjl_bits), _ptr(k_qjl_gamma), _stream(stream, k)), "tq_prefill")
+    dt = _DTYPES.get(k.dtype)
+    if dt is None:
+        raise ValueError(f"k and v must be float32, float16 or bfloat16, got {k.dtype}")
+    _on_device(k, v, k_codes, k_norms, v_codes, v_norms)
+    if kc.qjl_m:
+        qs, qb, qg = _ptr(qjl_S), _ptr(k_qjl_bits), _ptr(k_qjl_gamma)
+    else:
+        qs = qb = qg = None
+    args = (k.data_ptr(), v.data_ptr(), dt, H, T, t0, cap, k_codes.data_ptr(), k_norms.data_ptr(), v_codes.data_ptr(),
+            v_norms.data_ptr(), qs, qb, qg, _stream(stream, k))
+    if _lib is _fast_lib:
+        rc = _tqcall.prefill(ctypes.addressof(kc), ctypes.addressof(vc), *args)
+    else:
+        rc = _lib.tq_prefill(ctypes.byref(kc), ctypes.byref(vc), *args)
+    if rc:
+        _check(rc, "tq_prefill")
 
 
 def tq_append(kc: tq_codec, vc: tq_codec, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor,

@@ -1,7 +1,7 @@
 /*
  * Argument marshalling from Python to the C ABI of libtq (include/tq.h) for
  * the calls a decode or prefill loop makes every step: tq_encode, tq_encode_kv,
- * tq_append and tq_attn_decode.  Plain integers (device addresses, sizes,
+ * tq_prefill, tq_append and tq_attn_decode.  Plain integers (device addresses, sizes,
  * strides), one float and None (a NULL pointer) in, the library's return code
  * out; no arithmetic.  ctypes spends about 0.5 us more per call converting
  * their 12 to 21 arguments, 7-9 % of the host time of a small encode.
@@ -20,11 +20,13 @@ typedef __typeof__(tq_encode) encode_fn;
 typedef __typeof__(tq_encode_kv) encode_kv_fn;
 typedef __typeof__(tq_attn_decode) attn_decode_fn;
 typedef __typeof__(tq_append) append_fn;
+typedef __typeof__(tq_prefill) prefill_fn;
 
 static encode_fn *p_encode;
 static encode_kv_fn *p_encode_kv;
 static attn_decode_fn *p_attn_decode;
 static append_fn *p_append;
+static prefill_fn *p_prefill;
 
 /* an address argument: a Python int, or None for NULL */
 static int arg_ptr(PyObject *o, void **out) {
@@ -65,12 +67,13 @@ static PyObject *unbound(const char *name) {
     return NULL;
 }
 
-/* bind(addr_tq_encode, addr_tq_encode_kv, addr_tq_attn_decode, addr_tq_append) */
+/* bind(addr_tq_encode, addr_tq_encode_kv, addr_tq_attn_decode, addr_tq_append,
+ *      addr_tq_prefill) */
 static PyObject *py_bind(PyObject *self, PyObject *args) {
-    unsigned long long a, b, c, d;
+    unsigned long long a, b, c, d, e;
     (void)self;
-    if (!PyArg_ParseTuple(args, "KKKK", &a, &b, &c, &d)) return NULL;
-    if (!a || !b || !c || !d) {
+    if (!PyArg_ParseTuple(args, "KKKKK", &a, &b, &c, &d, &e)) return NULL;
+    if (!a || !b || !c || !d || !e) {
         PyErr_SetString(PyExc_ValueError, "null entry point");
         return NULL;
     }
@@ -78,6 +81,7 @@ static PyObject *py_bind(PyObject *self, PyObject *args) {
     p_encode_kv = (encode_kv_fn *)(uintptr_t)b;
     p_attn_decode = (attn_decode_fn *)(uintptr_t)c;
     p_append = (append_fn *)(uintptr_t)d;
+    p_prefill = (prefill_fn *)(uintptr_t)e;
     Py_RETURN_NONE;
 }
 
@@ -141,6 +145,27 @@ static PyObject *py_append(PyObject *self, PyObject *const *a, Py_ssize_t nargs)
     return PyLong_FromLong(rc);
 }
 
+/* prefill(kc, vc, k, v, x_dtype, n_heads, tokens, t0, ctx_cap, k_codes,
+ *         k_norms, v_codes, v_norms, qjl_S, k_qjl_bits, k_qjl_gamma, stream):
+ * tq_prefill's arguments in order */
+static PyObject *py_prefill(PyObject *self, PyObject *const *a, Py_ssize_t nargs) {
+    void *kc, *vc, *k, *v, *kcodes, *knorms, *vcodes, *vnorms, *S, *bits, *gamma, *stream;
+    int dtype, heads;
+    int64_t tokens, t0, cap;
+    (void)self;
+    if (!p_prefill) return unbound("prefill");
+    if (check_nargs(nargs, 17, "prefill") || arg_ptr(a[0], &kc) || arg_ptr(a[1], &vc) || arg_ptr(a[2], &k) ||
+        arg_ptr(a[3], &v) || arg_int(a[4], &dtype) || arg_int(a[5], &heads) || arg_i64(a[6], &tokens) ||
+        arg_i64(a[7], &t0) || arg_i64(a[8], &cap) || arg_ptr(a[9], &kcodes) || arg_ptr(a[10], &knorms) ||
+        arg_ptr(a[11], &vcodes) || arg_ptr(a[12], &vnorms) || arg_ptr(a[13], &S) || arg_ptr(a[14], &bits) ||
+        arg_ptr(a[15], &gamma) || arg_ptr(a[16], &stream))
+        return NULL;
+    const int rc = p_prefill((const tq_codec *)kc, (const tq_codec *)vc, k, v, dtype, heads, tokens, t0, cap,
+                             (uint8_t *)kcodes, (uint16_t *)knorms, (uint8_t *)vcodes, (uint16_t *)vnorms,
+                             (const float *)S, (uint8_t *)bits, (uint16_t *)gamma, stream);
+    return PyLong_FromLong(rc);
+}
+
 /* attn_decode(kc, vc, q, q_dtype, batch, n_q_heads, n_kv_heads, ctx_len,
  *             ctx_cap, k_codes, k_norms, k_qjl, k_gamma, qjl_S, v_codes,
  *             v_norms, scale, out, workspace, workspace_bytes, stream):
@@ -174,10 +199,11 @@ static PyObject *py_attn_decode(PyObject *self, PyObject *const *a, Py_ssize_t n
 
 static PyMethodDef methods[] = {
     {"bind", py_bind, METH_VARARGS,
-     "bind(tq_encode, tq_encode_kv, tq_attn_decode, tq_append): entry point addresses"},
+     "bind(tq_encode, tq_encode_kv, tq_attn_decode, tq_append, tq_prefill): entry point addresses"},
     {"encode", (PyCFunction)(void (*)(void))py_encode, METH_FASTCALL, "tq_encode with its C arguments"},
     {"encode_kv", (PyCFunction)(void (*)(void))py_encode_kv, METH_FASTCALL, "tq_encode_kv with its C arguments"},
     {"append", (PyCFunction)(void (*)(void))py_append, METH_FASTCALL, "tq_append with its C arguments"},
+    {"prefill", (PyCFunction)(void (*)(void))py_prefill, METH_FASTCALL, "tq_prefill with its C arguments"},
     {"attn_decode", (PyCFunction)(void (*)(void))py_attn_decode, METH_FASTCALL,
      "tq_attn_decode with its C arguments"},
     {NULL, NULL, 0, NULL},

@@ -489,6 +489,19 @@ def test_fast_marshalling_returns_the_library_codes():
         want = tq.raw_call("tq_append", refs4[kca], refs4[vca], *a[2:])
         assert want != tq.TQ_OK
         assert f.append(*a) == want, a
+    pre_cases = [
+        (0, c4a, 0, 4, 100, 0, 1000),                       # NULL codec
+        (c4a, ctypes.addressof(c64), 0, 4, 100, 0, 1000),   # K and V head sizes differ
+        (c4a, c4a, 0, 0, 100, 0, 1000),                     # no heads
+        (c4a, c4a, 0, 4, 100, 950, 1000),                   # chunk past the capacity
+        (c4a, c4a, 0, 4, 100, -1, 1000),                    # negative start
+        (c4a, c4a, 9, 4, 100, 0, 1000),                     # dtype
+    ]
+    for kca, vca, dt, H, T, t0, cap in pre_cases:
+        a = (kca, vca, P, P, dt, H, T, t0, cap, P, P, P, P, None, None, None, None)
+        want = tq.raw_call("tq_prefill", refs4[kca], refs4[vca], *a[2:])
+        assert want != tq.TQ_OK
+        assert f.prefill(*a) == want, a
     kc, vc = tq.tq_codebook(4, 128, 0), tq.tq_codebook(2, 128, 0)
     ws = tq.tq_attn_workspace_bytes(kc, vc, 2, 14, 2, 1000)
     for hq, hkv, cap, wsb in ((14, 3, 1000, ws), (14, 2, 0, ws), (14, 2, 1000, ws - 1)):
