@@ -124,3 +124,66 @@ def test_decode_graph_replays_match_eager(tq, noalloc):
         assert torch.isfinite(out_g).all(), rep
         assert torch.equal(out_g, out_e), rep
     del gr
+
+
+def test_append_and_decode_graph_replays_match_eager(tq):
+    """One decode step (tq_append of the new token's K and V at each
+    sequence's device-side position, then tq_attn_decode over the grown
+    context) captured in a HIP graph.  Between replays the program writes the
+    next positions, context lengths, tokens and queries eagerly; every replay
+    must leave the caches and the output with the bytes of the same eager
+    calls on a separate copy of the caches."""
+    from tests.test_gpu_attn import _fill_gpu_cache
+    B, Hkv, g, cap, d = 2, 2, 7, 2048, 128
+    Hq = Hkv * g
+    kc, vc = tq.tq_codebook(4, d, 12), tq.tq_codebook(2, d, 12)
+    K, V = synth.decode_cache_inputs(B, Hkv, cap, d, device="cuda", seed_base=131)
+    graph_cache = _fill_gpu_cache(tq, kc, vc, K, V)
+    del K, V
+    eager_cache = {key: t.clone() for key, t in graph_cache.items()}
+    pos = torch.empty(B, dtype=torch.int32, device="cuda")
+    ctx = torch.empty(B, dtype=torch.int32, device="cuda")
+    k_new = torch.empty(B, Hkv, d, dtype=torch.float16, device="cuda")
+    v_new = torch.empty_like(k_new)
+    q = torch.empty(B, Hq, d, dtype=torch.float16, device="cuda")
+    ws = tq.workspace(tq.tq_attn_workspace_bytes(kc, vc, B, Hq, Hkv, cap))
+    out_g = torch.empty(B, Hq, d, device="cuda")
+    out_e = torch.empty(B, Hq, d, device="cuda")
+
+    def step(c, out):
+        tq.tq_append(kc, vc, k_new, v_new, pos, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"])
+        tq.tq_attn_decode(kc, vc, q, ctx, c["k_codes"], c["k_norms"], c["v_codes"], c["v_norms"], 0.09, out, ws)
+
+    def set_inputs(r):
+        base = torch.tensor([1000 + r, 1500 + 3 * r], dtype=torch.int32)  # ragged, growing contexts
+        pos.copy_(base)
+        ctx.copy_(base + 1)
+        k, v = synth.kv_block(B * Hkv, 1, d, seed=700 + r, dtype=torch.float16)
+        k_new.copy_(k.view(B, Hkv, d))
+        v_new.copy_(v.view(B, Hkv, d))
+        q.copy_(synth.normal((B, Hq, d), seed=800 + r, dtype=torch.float16))
+
+    set_inputs(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # first calls (plans, code objects) outside capture
+        step(graph_cache, out_g)
+        step(eager_cache, out_e)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step(graph_cache, out_g)
+    for rep in range(1, 5):
+        set_inputs(rep)
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        step(eager_cache, out_e)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out_g).all(), rep
+        assert torch.equal(out_g, out_e), rep
+        for key in graph_cache:
+            assert torch.equal(graph_cache[key].view(torch.uint8), eager_cache[key].view(torch.uint8)), (rep, key)
+    del gr
