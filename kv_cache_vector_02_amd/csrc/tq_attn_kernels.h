@@ -815,17 +815,22 @@ void split_kernel(AttnArgs a) {
             // A = 16*gamma*(+-1) of token 16j + n (exact in half); same
             // accumulators.  The sign bytes came with the previous tile; the
             // next tile's go out once these are used.
+            // step ks outer (one uniform branch and one read of the projected
+            // query per step), the four sub-tiles' independent chains inner;
+            // each accumulator still takes its steps in order ks = 0, 1, ...
             const int nks = m >> 5;
+            _Float16 g16[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const _Float16 g16 = (_Float16)(16.0f * gml[16 * j + n]);
+            for (int j = 0; j < 4; ++j) g16[j] = (_Float16)(16.0f * gml[16 * j + n]);
 #pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    if (ks < nks) {
+            for (int ks = 0; ks < 8; ++ks) {
+                if (ks < nks) {
+                    const half8_t bqj = as_half8(qjlb[ks * 64 + lane]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
                         const uint32_t byte = (rq[j][ks >> 2] >> (8 * (ks & 3))) & 0xFFu;
-                        const half8_t asg = as_half8(sigt[byte]) * g16;
-                        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asg, as_half8(qjlb[ks * 64 + lane]), sacc[j],
-                                                                         0, 0, 0);
+                        const half8_t asg = as_half8(sigt[byte]) * g16[j];
+                        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asg, bqj, sacc[j], 0, 0, 0);
                     }
                 }
             }
