@@ -578,21 +578,24 @@ void split_kernel(AttnArgs a) {
         }
     }
     __syncthreads();
-    constexpr int NCH = C::SPLIT ? (C::KROWS + C::VROWS) * 16 : C::TABB / 16;  // 16-byte chunks
-    for (int i = tid; i < NCH; i += C::NT) {
-        // split: K rows then V rows, 16 chunks each; shared: row u, chunks 0..7
-        // repeat the K entry of u and chunks 8..15 the V entry
+    // one item per (row, table): its entry is computed once and written as the
+    // row's NCI 16-byte chunks, chunk (c + tid) % NCI in step c, so the 16
+    // lanes of a write pass (distinct rows) fall on distinct banks.  Split: K
+    // rows then V rows, 16 chunks each; shared: row u's chunks 0..7 repeat the
+    // K entry of u and chunks 8..15 the V entry.
+    constexpr int NCI = C::SPLIT ? 16 : 8;  // chunks per item
+    constexpr int NITEMS = C::SPLIT ? C::KROWS + C::VROWS : 2 * (C::TABB / 256);
+    for (int i = tid; i < NITEMS; i += C::NT) {
         bool is_k;
         int u, dst;
         if constexpr (C::SPLIT) {
-            is_k = i < C::KROWS * 16;
-            const int r = is_k ? i : i - C::KROWS * 16;
-            u = r >> 4;
-            dst = (is_k ? 0 : C::VBASE) + 16 * r;
+            is_k = i < C::KROWS;
+            u = is_k ? i : i - C::KROWS;
+            dst = (is_k ? 0 : C::VBASE) + 256 * u;
         } else {
-            u = i >> 4;
-            is_k = (i & 15) < 8;
-            dst = 16 * i;
+            u = i >> 1;
+            is_k = (i & 1) == 0;
+            dst = 256 * u + (is_k ? 0 : 128);
         }
         uint32_t w[4] = {0u, 0u, 0u, 0u};  // one entry (K: hi halves then lo halves; V: halves)
         bool live;
@@ -618,7 +621,11 @@ void split_kernel(AttnArgs a) {
         if (eb == 4) v = make_uint4(w[0], w[0], w[0], w[0]);
         else if (eb == 8) v = make_uint4(w[0], w[1], w[0], w[1]);
         else v = make_uint4(w[0], w[1], w[2], w[3]);
-        if (live) *reinterpret_cast<uint4*>(tab + dst) = v;
+        if (live) {
+#pragma unroll
+            for (int c = 0; c < NCI; ++c)
+                *reinterpret_cast<uint4*>(tab + dst + 16 * ((c + tid) & (NCI - 1))) = v;
+        }
     }
     if constexpr (QJL) {
         _Float16* st = reinterpret_cast<_Float16*>(sigt);
