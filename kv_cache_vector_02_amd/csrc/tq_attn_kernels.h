@@ -270,7 +270,7 @@ struct Cfg {
     static constexpr int WAVE_DW = wave_dw(D, VB);
     static constexpr int QJL_DW = qjl_dw(QJL);      // QJL B operands + sign table
     static constexpr int LOOP_DW = TABB / 4 + NW * WAVE_DW + QJL_DW;
-    static constexpr int MERGE_DW = NW * GMAX * (D + 2);
+    static constexpr int MERGE_DW = NW * GMAX * (D + 2) + GMAX * (NW + 1);  // partials, then merge factors
     static constexpr int SMEM_DW = LOOP_DW > MERGE_DW ? LOOP_DW : MERGE_DW;
     static_assert(4 * SMEM_DW <= kLdsBytes, "split kernel exceeds LDS");
     static_assert(GMAX * D <= NW * WAVE_DW, "rotated queries exceed the wave areas");
@@ -1208,23 +1208,30 @@ void split_kernel(AttnArgs a) {
         }
     }
     __syncthreads();
-    for (int e = tid; e < G * (D + 2); e += C::NT) {
-        const int h = e / (D + 2), i = e - h * (D + 2);
+    // per head: the block max and each wave's factor 2^(m_w - max) (0 for a
+    // head no wave has seen), once, then every value of the head
+    float* fac = mrg + C::NW * G * (D + 2);  // [G][NW + 1]: factors, then the max
+    if (tid < G) {
+        const int h = tid;
         float mx = -INFINITY;
 #pragma unroll
         for (int w = 0; w < C::NW; ++w) mx = fmaxf(mx, mrg[(w * G + h) * (D + 2)]);
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w)
+            fac[h * (C::NW + 1) + w] = mx == -INFINITY ? 0.0f : exp2f(mrg[(w * G + h) * (D + 2)] - mx);
+        fac[h * (C::NW + 1) + C::NW] = mx;
+    }
+    __syncthreads();
+    for (int e = tid; e < G * (D + 2); e += C::NT) {
+        const int h = e / (D + 2), i = e - h * (D + 2);
+        const float* fh = fac + h * (C::NW + 1);
         float val;
         if (i == 0) {
-            val = mx;
-        } else if (mx == -INFINITY) {
-            val = 0.0f;
+            val = fh[C::NW];
         } else {
             val = 0.0f;
 #pragma unroll
-            for (int w = 0; w < C::NW; ++w) {
-                const float mw = mrg[(w * G + h) * (D + 2)];
-                val = fmaf(mrg[(w * G + h) * (D + 2) + i], exp2f(mw - mx), val);
-            }
+            for (int w = 0; w < C::NW; ++w) val = fmaf(mrg[(w * G + h) * (D + 2) + i], fh[w], val);
         }
         a.part[(query_row<MQ>(a, b, kvh, vl0 + h) * a.splits + split) * (D + 2) + i] = val;
     }
