@@ -696,7 +696,7 @@ void split_kernel(AttnArgs a) {
                 for (int ks = 0; ks < (m >> 5); ++ks) {
                     half8_t x8;
                     for (int j = 0; j < 8; ++j) {
-                        // the sign operand carries 16*gamma, so scale by sc only
+                        // the sign products are scaled by 16*gamma later, so by sc only
                         const float v = (head_ok ? qp[grp * (m >> 2) + 8 * ks + j] : 0.0f) * sc;
                         const _Float16 hi = (_Float16)v;
                         x8[j] = lo_col ? (_Float16)(v - (float)hi) : hi;
@@ -766,7 +766,7 @@ void split_kernel(AttnArgs a) {
             knq[lane] = half_bits_to_float(rn & 0xFFFFu) * qinv;
             vmx = vnf;
         }
-        if constexpr (QJL) gml[lane] = half_bits_to_float(rg);
+        if constexpr (QJL) gml[lane] = 16.0f * half_bits_to_float(rg);
         vnl[lane] = vnf * vsc;
         // prefetch (clamped to the split: past its end this re-reads the last token)
         fetch_v<C, QJL>(rv, rn, rg, rv2, vcodes, knb, vnb, gmb, (uint32_t)(t0 + 64 * C::NW), last, lane, nbk, nbv);
@@ -819,16 +819,16 @@ void split_kernel(AttnArgs a) {
         });
         if constexpr (!KDB) fetch_k<C>(rk[cur], kcodes, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
         if constexpr (QJL) {
-            // A = 16*gamma*(+-1) of token 16j + n (exact in half); same
-            // accumulators.  The sign bytes came with the previous tile; the
-            // next tile's go out once these are used.
-            // step ks outer (one uniform branch and one read of the projected
-            // query per step), the four sub-tiles' independent chains inner;
-            // each accumulator still takes its steps in order ks = 0, 1, ...
+            // A = the +-1 signs of token 16j + n, accumulated apart and scaled
+            // by the token's 16*gamma in float32 before joining the scores.
+            // The sign bytes came with the previous tile; the next tile's go
+            // out once these are used.  Step ks outer (one uniform branch and
+            // one read of the projected query per step), the four sub-tiles'
+            // independent chains inner.
             const int nks = m >> 5;
-            _Float16 g16[4];
+            floatx4_t qacc[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) g16[j] = (_Float16)(16.0f * gml[16 * j + n]);
+            for (int j = 0; j < 4; ++j) qacc[j] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
                 if (ks < nks) {
@@ -836,10 +836,18 @@ void split_kernel(AttnArgs a) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const uint32_t byte = (rq[j][ks >> 2] >> (8 * (ks & 3))) & 0xFFu;
-                        const half8_t asg = as_half8(sigt[byte]) * g16[j];
-                        sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(asg, bqj, sacc[j], 0, 0, 0);
+                        qacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(sigt[byte]), bqj, qacc[j], 0, 0, 0);
                     }
                 }
+            }
+            // row v of sub-tile j's result is token 16j + 4grp + v
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 g4 = *reinterpret_cast<const float4*>(gml + 16 * j + 4 * grp);
+                sacc[j][0] = fmaf(qacc[j][0], g4.x, sacc[j][0]);
+                sacc[j][1] = fmaf(qacc[j][1], g4.y, sacc[j][1]);
+                sacc[j][2] = fmaf(qacc[j][2], g4.z, sacc[j][2]);
+                sacc[j][3] = fmaf(qacc[j][3], g4.w, sacc[j][3]);
             }
             fetch_q(rq, qjb, m, (uint32_t)(t0 + 64 * C::NW), last, n, grp);
         }
